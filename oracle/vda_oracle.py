@@ -1,0 +1,231 @@
+"""fp64 CPU oracle for the Video Delta Attention (VDA) forward pass.
+
+TEST INFRASTRUCTURE ONLY.  This file is the plain, slow, obviously-correct
+statement of what the VDA forward pass computes.  Only the tests, the smoke
+check and the bench's CPU-baseline leg may import it; the library never calls it
+and shares no code with it.
+
+Every function follows "Video DeltaNet: A Video-Native Hybrid Attention for
+Livestream Video Generation" (arXiv 2609.20744), cited below as [VDN] with the
+section or equation it restates.  All arithmetic is numpy fp64; a library
+routine (matmul, dense solve, inverse) serves as a single step, with no blocking,
+fusion or reordering beyond what the cited definition states.
+
+Notation: one "unit" is one (batch, head) pair; all units are independent.
+F latent frames of U tokens each; keys k in R^{d_k}, values v in R^{d_v};
+states S in R^{d_v x d_k}; chunk length C (5 in [VDN] Sec. 2.1); window radius r
+in chunks (1 in [VDN] Sec. 2.1); n = ceil(F / C) chunks; T text tokens.
+
+Readings taken where the pages leave a step open (each is also listed in the
+design notes):
+  * decay alpha = 1 (no channel-wise decay, hence no decay bridge in Eq. (A.4));
+  * no boundary anchors: every frame enters both scans;
+  * text seed, mode 0 (default): S_T is ONE frame-wise update from S = 0 over all
+    T text tokens (the prompt "as a leading virtual frame", [VDN] Sec. 5) and each
+    scan starts at S_T / 2 ([VDN] Eq. (1b)).  Mode 1: the text tokens are written
+    from S = 0 at beta / 2 ("written at beta/2" reading);
+  * chunk j = frames [C j, min(C j + C, F)); a short last chunk is allowed;
+  * the forward state a query in chunk c reads ends before chunk c - r, the
+    reverse state starts after chunk c + r (the window's outside, [VDN] Sec. 2.2
+    and Eq. (A.4)); a missing side reads the text seed;
+  * RMSNorm over the d_v channels of one (unit, frame, token) row with weight
+    w in R^{d_v} and epsilon eps, then an element-wise sigmoid gate
+    ([VDN] Eq. (1c)).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+__all__ = [
+    "frame_statistics", "frame_update", "transition", "text_state", "chunk_bounds",
+    "directional_states", "gather", "rms_norm", "sigmoid", "readout", "forward_unit",
+    "forward",
+]
+
+f64 = np.float64
+
+
+def frame_statistics(K, V, beta):
+    """Frame statistics, [VDN] Sec. 3.1 Eq. (3b).
+
+    A = sum_u beta_u k_u k_u^T = K^T Diag(beta) K   (d_k x d_k)
+    B = sum_u beta_u v_u k_u^T = V^T Diag(beta) K   (d_v x d_k)
+    K: U x d_k, V: U x d_v, beta: U (beta >= 0, [VDN] Sec. 3.1).
+    """
+    K = np.asarray(K, f64)
+    V = np.asarray(V, f64)
+    beta = np.asarray(beta, f64)
+    if np.any(beta < 0):
+        raise ValueError("write strengths must be non-negative")
+    DK = beta[:, None] * K  # Diag(beta) K: row u of K scaled by beta_u
+    A = K.T @ DK
+    B = V.T @ DK
+    return A, B
+
+
+def frame_update(S_bar, A, B):
+    """Frame-wise delta rule, [VDN] Sec. 3.2 Eq. (5).
+
+    The new state solves the normal equation S (I + A) = S_bar + B; it is
+    obtained with a dense solve (no explicit inverse).  S_bar is the inherited
+    state (alpha = 1: S_bar = S_{t-1}).
+    """
+    S_bar = np.asarray(S_bar, f64)
+    G = np.eye(A.shape[0]) + A
+    # S G = R  <=>  G^T S^T = R^T
+    return np.linalg.solve(G.T, (S_bar + B).T).T
+
+
+def transition(A):
+    """Inherited-state transition with alpha = 1, [VDN] App. A.1 Eq. (A.1): M = (I + A)^{-1}."""
+    return np.linalg.inv(np.eye(A.shape[0]) + A)
+
+
+def text_state(text_k, text_v, text_beta, d_k, d_v, seed_mode=0):
+    """Initial state of each directional scan, [VDN] Sec. 2.2 Eq. (1b).
+
+    mode 0: S_T = one frame-wise update (Eq. (5)) from S = 0 over all text
+            tokens; the seed is S_T / 2, so that the forward and reverse seeds
+            together read S_T q exactly once.
+    mode 1: the text tokens are written from S = 0 at half write strength.
+    No text tokens gives a zero seed.
+    """
+    text_k = np.asarray(text_k, f64).reshape(-1, d_k)
+    text_v = np.asarray(text_v, f64).reshape(-1, d_v)
+    text_beta = np.asarray(text_beta, f64).reshape(-1)
+    zero = np.zeros((d_v, d_k))
+    if text_k.shape[0] == 0:
+        return zero
+    if seed_mode == 0:
+        A, B = frame_statistics(text_k, text_v, text_beta)
+        return 0.5 * frame_update(zero, A, B)
+    if seed_mode == 1:
+        A, B = frame_statistics(text_k, text_v, 0.5 * text_beta)
+        return frame_update(zero, A, B)
+    raise ValueError("seed_mode must be 0 or 1")
+
+
+def chunk_bounds(F, C):
+    """Chunks of C consecutive latent frames from frame 0 ([VDN] Sec. 2.1); the last may be short."""
+    return [(s, min(s + C, F)) for s in range(0, F, C)]
+
+
+def directional_states(stats, seed, C):
+    """Both directional scans of [VDN] Sec. 2.2 / App. A.3 (alpha = 1, no anchors).
+
+    stats: list of (A_f, B_f) for f = 0..F-1.
+    Forward: start at the seed and apply Eq. (5) to frames 0, 1, ..., F-1;
+      P[0] = seed, P[j+1] = the state after the last frame of chunk j.
+    Reverse: start at the seed and apply Eq. (5) to frames F-1, ..., 0;
+      R[n] = seed, R[j] = the state after the first frame of chunk j.
+    Returns (P, R), each of shape (n + 1, d_v, d_k).
+    """
+    F = len(stats)
+    bounds = chunk_bounds(F, C)
+    n = len(bounds)
+    P = np.zeros((n + 1,) + seed.shape)
+    R = np.zeros((n + 1,) + seed.shape)
+    S = seed.copy()
+    P[0] = S
+    for j, (lo, hi) in enumerate(bounds):
+        for f in range(lo, hi):
+            S = frame_update(S, *stats[f])
+        P[j + 1] = S
+    S = seed.copy()
+    R[n] = S
+    for j in range(n - 1, -1, -1):
+        lo, hi = bounds[j]
+        for f in range(hi - 1, lo - 1, -1):
+            S = frame_update(S, *stats[f])
+        R[j] = S
+    return P, R
+
+
+def gather(P, R, c, radius):
+    """State read by queries of chunk c, [VDN] Eq. (A.4) with alpha = 1 and no anchors.
+
+    The forward state covers the chunks before the window [c - r, c + r], the
+    reverse state those after it; an empty side reads the seed (P[0] or R[n]).
+    """
+    n = P.shape[0] - 1
+    return P[max(c - radius, 0)] + R[min(c + radius + 1, n)]
+
+
+def rms_norm(O, w, eps):
+    """RMSNorm of each row of O over its d_v channels, scaled by w ([VDN] Eq. (1c))."""
+    O = np.asarray(O, f64)
+    ms = np.mean(O * O, axis=-1, keepdims=True)
+    return np.asarray(w, f64) * O / np.sqrt(ms + eps)
+
+
+def sigmoid(x):
+    return 1.0 / (1.0 + np.exp(-np.asarray(x, f64)))
+
+
+def readout(S_tilde, Q, G, w, eps):
+    """Linear-branch readout of [VDN] Eq. (1a), (A.4) and (1c).
+
+    o = S_tilde q for every query row q of Q (tokens x d_k); the output row is
+    sigmoid(g) * RMSNorm(o).
+    """
+    O = np.asarray(Q, f64) @ np.asarray(S_tilde, f64).T
+    return sigmoid(G) * rms_norm(O, w, eps)
+
+
+def forward_unit(q, k, v, beta, gate, text_k, text_v, text_beta, rms_weight,
+                 chunk=5, radius=1, eps=1e-6, seed_mode=0, taps=False):
+    """VDA forward for one unit.
+
+    q: F x U x d_k, k: F x U x d_k, v: F x U x d_v, beta: F x U,
+    gate: F x U x d_v (gate logits), text_k: T x d_k, text_v: T x d_v,
+    text_beta: T, rms_weight: d_v.  Returns out (F x U x d_v), plus a dict of
+    intermediates when taps=True: A, B (per frame), M (per frame, Eq. (A.1)),
+    seed, P, R.
+    """
+    q = np.asarray(q, f64)
+    k = np.asarray(k, f64)
+    v = np.asarray(v, f64)
+    beta = np.asarray(beta, f64)
+    F, U, d_k = k.shape
+    d_v = v.shape[-1]
+    seed = text_state(text_k, text_v, text_beta, d_k, d_v, seed_mode)
+    stats = [frame_statistics(k[f], v[f], beta[f]) for f in range(F)]
+    P, R = directional_states(stats, seed, chunk)
+    out = np.zeros((F, U, d_v))
+    for c, (lo, hi) in enumerate(chunk_bounds(F, chunk)):
+        S_tilde = gather(P, R, c, radius)
+        for f in range(lo, hi):
+            out[f] = readout(S_tilde, q[f], gate[f], rms_weight, eps)
+    if not taps:
+        return out
+    tap = {
+        "A": np.array([s[0] for s in stats]).reshape(F, d_k, d_k),
+        "B": np.array([s[1] for s in stats]).reshape(F, d_v, d_k),
+        "M": np.array([transition(s[0]) for s in stats]).reshape(F, d_k, d_k),
+        "seed": seed, "P": P, "R": R,
+    }
+    return out, tap
+
+
+def forward(q, k, v, beta, gate, text_k, text_v, text_beta, rms_weight,
+            chunk=5, radius=1, eps=1e-6, seed_mode=0, taps=False, units=None):
+    """VDA forward over all units (leading axis of every per-unit tensor).
+
+    ``units`` restricts the work to a subset of unit indices; the result then
+    holds only those units, in that order.
+    """
+    idx = range(np.shape(k)[0]) if units is None else list(units)
+    outs, tapl = [], []
+    for u in idx:
+        r = forward_unit(q[u], k[u], v[u], beta[u], gate[u], text_k[u], text_v[u],
+                         text_beta[u], rms_weight, chunk, radius, eps, seed_mode, taps)
+        if taps:
+            outs.append(r[0])
+            tapl.append(r[1])
+        else:
+            outs.append(r)
+    out = np.stack(outs) if outs else np.zeros((0,))
+    if not taps:
+        return out
+    merged = {key: np.stack([t[key] for t in tapl]) for key in tapl[0]} if tapl else {}
+    return out, merged

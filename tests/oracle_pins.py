@@ -1,0 +1,527 @@
+"""Pins of the fp64 oracle against what the pages and the mathematics fix.
+
+Each ``pin_*`` function takes the oracle module, raises AssertionError when the
+oracle disagrees with the fact it checks, and returns nothing otherwise.  The
+facts come from "Video DeltaNet" (arXiv 2609.20744), cited as [VDN]:
+
+  * Eq. (3b): the frame statistics are sums of per-token outer products;
+  * Eq. (4)-(5): the update is the unique minimiser of a strictly convex
+    objective, so its gradient vanishes and an independent least-squares solver
+    finds the same state;
+  * the classical one-token delta rule ([VDN] Eq. (2)) is the single-key case of
+    Eq. (5) with write strength beta / (1 + beta ||k||^2) (Sherman-Morrison);
+  * App. A.2 Eq. (A.3): repeated keys get the saturating weight U b / (1 + U b),
+    orthogonal keys b / (1 + b) each;
+  * Prop. 1 / App. A.1: ||(I + A)^{-1}||_2 <= 1 and state differences never grow;
+  * Eq. (1b): the two seeds together read the text state exactly once;
+  * Sec. 2.2 and Eq. (A.4): forward and reverse regions are disjoint from the
+    local window and from each other;
+  * Eq. (1c): RMSNorm then an element-wise sigmoid gate.
+
+None of these re-types the oracle's own formula: gradients and objectives are
+evaluated token by token, least squares goes through numpy's SVD-based solver,
+and the scan wiring is checked through symmetries (time reversal, a one-frame
+probe) rather than re-implemented.
+"""
+from __future__ import annotations
+
+import json
+import os
+from fractions import Fraction
+
+import numpy as np
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _rng(seed):
+    return np.random.default_rng(seed)
+
+
+def _unit(x):
+    return x / np.linalg.norm(x, axis=-1, keepdims=True)
+
+
+def _frame(rng, U=7, dk=5, dv=3, unit_keys=False):
+    K = rng.standard_normal((U, dk))
+    if unit_keys:
+        K = _unit(K)
+    V = rng.standard_normal((U, dv))
+    beta = 1.0 / (1.0 + np.exp(-rng.standard_normal(U)))
+    S_bar = rng.standard_normal((dv, dk))
+    return S_bar, K, V, beta
+
+
+def _update(o, S_bar, K, V, beta):
+    A, B = o.frame_statistics(K, V, beta)
+    return o.frame_update(S_bar, A, B)
+
+
+def _objective(S, S_bar, K, V, beta):
+    """[VDN] Eq. (4), evaluated token by token."""
+    val = 0.5 * np.sum((S - S_bar) ** 2)
+    for u in range(K.shape[0]):
+        r = S @ K[u] - V[u]
+        val += 0.5 * beta[u] * float(r @ r)
+    return val
+
+
+def _gradient(S, S_bar, K, V, beta):
+    """Gradient of Eq. (4) w.r.t. S, token by token."""
+    G = S - S_bar
+    for u in range(K.shape[0]):
+        G = G + beta[u] * np.outer(S @ K[u] - V[u], K[u])
+    return G
+
+
+# ----------------------------------------------------------------------------- a2: stats
+def pin_stats_hand_loop(o):
+    """Eq. (3b) entry by entry with plain Python loops."""
+    rng = _rng(1)
+    U, dk, dv = 6, 4, 3
+    K = rng.standard_normal((U, dk))
+    V = rng.standard_normal((U, dv))
+    beta = rng.uniform(0, 1, U)
+    A, B = o.frame_statistics(K, V, beta)
+    assert A.shape == (dk, dk) and B.shape == (dv, dk)
+    for i in range(dk):
+        for j in range(dk):
+            s = 0.0
+            for u in range(U):
+                s += beta[u] * K[u, i] * K[u, j]
+            assert abs(A[i, j] - s) <= 1e-13 * max(1.0, abs(s)), (i, j)
+    for i in range(dv):
+        for j in range(dk):
+            s = 0.0
+            for u in range(U):
+                s += beta[u] * V[u, i] * K[u, j]
+            assert abs(B[i, j] - s) <= 1e-13 * max(1.0, abs(s)), (i, j)
+
+
+def pin_stats_invariants(o):
+    """A is symmetric PSD, tr A = sum_u beta_u ||k_u||^2 ([VDN] App. A.2), and
+    standard-basis keys give A = Diag(beta), B = V^T Diag(beta) columns."""
+    rng = _rng(2)
+    S_bar, K, V, beta = _frame(rng, U=9, dk=6, dv=4)
+    A, B = o.frame_statistics(K, V, beta)
+    assert np.allclose(A, A.T, atol=1e-14, rtol=0)
+    assert np.min(np.linalg.eigvalsh(A)) > -1e-12
+    assert abs(np.trace(A) - sum(beta[u] * K[u] @ K[u] for u in range(9))) < 1e-12
+    dk = 5
+    Ke = np.eye(dk)
+    Ve = rng.standard_normal((dk, 3))
+    be = rng.uniform(0.1, 1, dk)
+    A, B = o.frame_statistics(Ke, Ve, be)
+    assert np.allclose(A, np.diag(be), atol=1e-15, rtol=0)
+    assert np.allclose(B, (Ve * be[:, None]).T, atol=1e-15, rtol=0)
+
+
+# ----------------------------------------------------------------------------- a3: update
+def pin_gradient_zero(o):
+    """Eq. (4)-(5): the update zeroes the gradient of the frame objective."""
+    rng = _rng(3)
+    for trial in range(5):
+        S_bar, K, V, beta = _frame(rng, U=7 + trial, dk=5, dv=3)
+        S = _update(o, S_bar, K, V, beta)
+        G = _gradient(S, S_bar, K, V, beta)
+        A, B = o.frame_statistics(K, V, beta)
+        assert np.linalg.norm(G) <= 1e-12 * np.linalg.norm(S_bar + B), trial
+        # strictly convex: any perturbation raises the objective
+        f0 = _objective(S, S_bar, K, V, beta)
+        for _ in range(3):
+            D = rng.standard_normal(S.shape) * 1e-3
+            assert _objective(S + D, S_bar, K, V, beta) > f0
+
+
+def pin_lstsq_bruteforce(o):
+    """Eq. (4) as stacked least squares per state row, solved by numpy's SVD solver."""
+    rng = _rng(4)
+    for U, dk, dv in ((1, 3, 2), (5, 4, 4), (16, 16, 16), (3, 8, 2)):
+        S_bar, K, V, beta = _frame(rng, U=U, dk=dk, dv=dv)
+        S = _update(o, S_bar, K, V, beta)
+        sb = np.sqrt(beta)[:, None]
+        Mtx = np.vstack([np.eye(dk), sb * K])
+        for i in range(dv):
+            rhs = np.concatenate([S_bar[i], sb[:, 0] * V[:, i]])
+            x = np.linalg.lstsq(Mtx, rhs, rcond=None)[0]
+            assert np.max(np.abs(x - S[i])) <= 1e-10 * max(1.0, np.max(np.abs(x))), (U, dk, dv, i)
+
+
+def pin_sherman_morrison(o):
+    """One token: S = S_bar + b' (v - S_bar k) k^T with b' = beta / (1 + beta ||k||^2),
+    i.e. the classical delta rule of [VDN] Eq. (2) with an effective strength."""
+    rng = _rng(5)
+    for trial in range(5):
+        dk, dv = 6, 4
+        k = rng.standard_normal(dk) * (0.5 + trial)   # not unit on purpose
+        v = rng.standard_normal(dv)
+        beta = rng.uniform(0.05, 2.0)
+        S_bar = rng.standard_normal((dv, dk))
+        S = _update(o, S_bar, k[None, :], v[None, :], np.array([beta]))
+        bprime = beta / (1.0 + beta * (k @ k))
+        expect = S_bar + bprime * np.outer(v - S_bar @ k, k)
+        assert np.max(np.abs(S - expect)) <= 1e-12 * max(1.0, np.max(np.abs(expect))), trial
+
+
+def pin_repeated_keys(o):
+    """[VDN] Eq. (A.3): U copies of a unit key k with common beta give
+    S k = s / (1 + U beta) + U beta / (1 + U beta) * mean(v); the weight rises
+    with U towards, but never reaches, 1."""
+    rng = _rng(6)
+    dk, dv = 8, 5
+    k = _unit(rng.standard_normal(dk))
+    S_bar = rng.standard_normal((dv, dk))
+    beta = 0.37
+    prev = 0.0
+    for U in (1, 2, 3, 7, 64, 4032):
+        V = rng.standard_normal((U, dv))
+        K = np.repeat(k[None, :], U, axis=0)
+        S = _update(o, S_bar, K, V, np.full(U, beta))
+        w = U * beta / (1.0 + U * beta)
+        expect = (S_bar @ k) / (1.0 + U * beta) + w * V.mean(axis=0)
+        assert np.max(np.abs(S @ k - expect)) <= 1e-12 * max(1.0, np.max(np.abs(expect))), U
+        # directions orthogonal to k keep the inherited state; fp64 rounding of the
+        # U-term sum in A leaves O(eps ||A||) off the k direction, ||A|| = U beta
+        x = rng.standard_normal(dk)
+        x -= (x @ k) * k
+        A, B = o.frame_statistics(K, V, np.full(U, beta))
+        tol = 1e-14 * dk * (1.0 + U * beta) * max(1.0, np.max(np.abs(S_bar + B)))
+        assert np.max(np.abs(S @ x - S_bar @ x)) <= tol, U
+        assert prev < w < 1.0
+        prev = w
+
+
+def pin_orthonormal_keys(o):
+    """[VDN] App. A.2: orthonormal keys are written independently, each with
+    weight beta_u / (1 + beta_u)."""
+    rng = _rng(7)
+    dk, dv, U = 9, 4, 6
+    Qm, _ = np.linalg.qr(rng.standard_normal((dk, dk)))
+    K = Qm[:, :U].T
+    V = rng.standard_normal((U, dv))
+    beta = rng.uniform(0.1, 3.0, U)
+    S_bar = rng.standard_normal((dv, dk))
+    S = _update(o, S_bar, K, V, beta)
+    for u in range(U):
+        expect = (S_bar @ K[u] + beta[u] * V[u]) / (1.0 + beta[u])
+        assert np.max(np.abs(S @ K[u] - expect)) <= 1e-12, u
+    for x in Qm[:, U:].T:
+        assert np.max(np.abs(S @ x - S_bar @ x)) <= 1e-12
+
+
+def pin_beta_zero(o):
+    """beta = 0 writes nothing: A = B = 0 and S = S_bar exactly."""
+    rng = _rng(8)
+    S_bar, K, V, _ = _frame(rng, U=11, dk=6, dv=5)
+    S = _update(o, S_bar, K, V, np.zeros(11))
+    assert np.array_equal(S, S_bar)
+
+
+def pin_non_expansive(o):
+    """[VDN] Prop. 1 (App. A.1, Eq. (A.2)) with alpha = 1: the transition
+    (I + A)^{-1} has spectral norm <= 1, also when lambda_max(A) > 2 (aligned
+    keys, App. A.2), and the difference of two entering states never grows."""
+    rng = _rng(9)
+    for trial in range(4):
+        dk, dv, U = 8, 4, 50
+        K = _unit(rng.standard_normal((U, dk)))
+        if trial % 2:
+            K = _unit(np.ones((U, dk)) + 0.05 * rng.standard_normal((U, dk)))
+        beta = 1.0 / (1.0 + np.exp(-rng.standard_normal(U)))
+        V = rng.standard_normal((U, dv))
+        A, B = o.frame_statistics(K, V, beta)
+        if trial % 2:
+            assert np.max(np.linalg.eigvalsh(A)) > 2.0
+        M = o.transition(A)
+        ev = np.linalg.eigvalsh((M + M.T) / 2)
+        assert np.max(np.abs(M - M.T)) <= 1e-12
+        assert 0.0 < np.min(ev) and np.max(ev) <= 1.0 + 1e-12
+        assert np.linalg.norm(M, 2) <= 1.0 + 1e-12
+        S1 = rng.standard_normal((dv, dk))
+        S2 = rng.standard_normal((dv, dk))
+        d0 = np.linalg.norm(S1 - S2)
+        d1 = np.linalg.norm(o.frame_update(S1, A, B) - o.frame_update(S2, A, B))
+        assert d1 <= d0 * (1.0 + 1e-12)
+        # the carried contribution is exactly Delta S M (Eq. (A.1))
+        D = o.frame_update(S1, A, B) - o.frame_update(S2, A, B)
+        assert np.max(np.abs(D - (S1 - S2) @ M)) <= 1e-12
+
+
+def pin_scalar_case(o):
+    """d_k = d_v = 1: Eq. (5) is s_t = (s_{t-1} + b_t) / (1 + a_t); checked against
+    the hand-derived fractions in golden/scalar_two_frames.json."""
+    with open(os.path.join(GOLDEN, "scalar_two_frames.json")) as fh:
+        g = json.load(fh)
+    s = np.zeros((1, 1))
+    for fr, want in zip(g["frames"], g["states"]):
+        K = np.array(fr["k"], float)[:, None]
+        V = np.array(fr["v"], float)[:, None]
+        beta = np.array([float(Fraction(b)) for b in fr["beta"]])
+        A, B = o.frame_statistics(K, V, beta)
+        s = o.frame_update(s, A, B)
+        assert abs(s[0, 0] - float(Fraction(want))) <= 1e-15, want
+
+
+def pin_orthonormal_golden(o):
+    """golden/orthonormal_d2.json: a 2x2 frame worked by hand (App. A.2)."""
+    with open(os.path.join(GOLDEN, "orthonormal_d2.json")) as fh:
+        g = json.load(fh)
+    fr = lambda m: np.array([[float(Fraction(x)) for x in row] for row in m])  # noqa: E731
+    S_bar = fr(g["S_bar"])
+    K = fr(g["k"])
+    V = fr(g["v"])
+    beta = np.array([float(Fraction(b)) for b in g["beta"]])
+    S = _update(o, S_bar, K, V, beta)
+    assert np.max(np.abs(S - fr(g["S"]))) <= 1e-15
+
+
+# ----------------------------------------------------------------------------- a1: seed
+def pin_exactly_once(o):
+    """[VDN] Eq. (1b): P[0] + R[n] equals the text state S_T, found here by
+    least squares over the text tokens (mode 0)."""
+    rng = _rng(10)
+    dk, dv, T = 6, 5, 9
+    tk = _unit(rng.standard_normal((T, dk)))
+    tv = rng.standard_normal((T, dv))
+    tb = rng.uniform(0.1, 1, T)
+    F, U = 6, 4
+    q = rng.standard_normal((F, U, dk))
+    k = _unit(rng.standard_normal((F, U, dk)))
+    v = rng.standard_normal((F, U, dv))
+    beta = rng.uniform(0, 1, (F, U))
+    g = rng.standard_normal((F, U, dv))
+    _, tap = o.forward_unit(q, k, v, beta, g, tk, tv, tb, np.ones(dv), chunk=2, radius=1,
+                            taps=True)
+    sb = np.sqrt(tb)[:, None]
+    Mtx = np.vstack([np.eye(dk), sb * tk])
+    S_T = np.stack([np.linalg.lstsq(Mtx, np.concatenate([np.zeros(dk), sb[:, 0] * tv[:, i]]),
+                                    rcond=None)[0] for i in range(dv)])
+    P, R = tap["P"], tap["R"]
+    n = P.shape[0] - 1
+    assert np.max(np.abs(P[0] + R[n] - S_T)) <= 1e-13
+    assert np.max(np.abs(P[0] - R[n])) == 0.0
+    # mode 1: the text written from zero at half strength (least squares with beta/2)
+    _, tap1 = o.forward_unit(q, k, v, beta, g, tk, tv, tb, np.ones(dv), chunk=2, radius=1,
+                             seed_mode=1, taps=True)
+    sb = np.sqrt(0.5 * tb)[:, None]
+    Mtx = np.vstack([np.eye(dk), sb * tk])
+    S_h = np.stack([np.linalg.lstsq(Mtx, np.concatenate([np.zeros(dk), sb[:, 0] * tv[:, i]]),
+                                    rcond=None)[0] for i in range(dv)])
+    assert np.max(np.abs(tap1["P"][0] - S_h)) <= 1e-13
+    # no text tokens: zero seed
+    _, tap0 = o.forward_unit(q, k, v, beta, g, tk[:0], tv[:0], tb[:0], np.ones(dv), chunk=2,
+                             radius=1, taps=True)
+    assert np.array_equal(tap0["P"][0], np.zeros((dv, dk)))
+
+
+# ----------------------------------------------------------------------------- a4-a6: scans
+def _random_unit(rng, F, U, dk, dv, T):
+    return dict(
+        q=rng.standard_normal((F, U, dk)), k=_unit(rng.standard_normal((F, U, dk))),
+        v=rng.standard_normal((F, U, dv)), beta=rng.uniform(0, 1, (F, U)),
+        gate=rng.standard_normal((F, U, dv)), text_k=_unit(rng.standard_normal((T, dk))),
+        text_v=rng.standard_normal((T, dv)), text_beta=rng.uniform(0, 1, T),
+        rms_weight=rng.uniform(0.5, 1.5, dv))
+
+
+def _call(o, x, **kw):
+    return o.forward_unit(x["q"], x["k"], x["v"], x["beta"], x["gate"], x["text_k"],
+                          x["text_v"], x["text_beta"], x["rms_weight"], **kw)
+
+
+def pin_time_reversal(o):
+    """[VDN] Sec. 2.2: the two scans are mirror images.  Reversing the frame order
+    (F a multiple of C) maps the output of frame f to frame F-1-f."""
+    rng = _rng(11)
+    for C, r, F in ((5, 1, 20), (2, 1, 8), (3, 2, 15), (1, 1, 6)):
+        x = _random_unit(rng, F, 4, 5, 3, 3)
+        out = _call(o, x, chunk=C, radius=r)
+        xr = dict(x)
+        for key in ("q", "k", "v", "beta", "gate"):
+            xr[key] = x[key][::-1].copy()
+        out_r = _call(o, xr, chunk=C, radius=r)
+        assert np.max(np.abs(out_r[::-1] - out)) <= 1e-12, (C, r, F)
+
+
+def pin_disjointness(o):
+    """[VDN] Sec. 2.2 / Eq. (A.4): with a single writing frame f* and no text, a
+    query in chunk c sees f* iff chunk(f*) lies outside the window [c-r, c+r];
+    otherwise its state and output are exactly zero."""
+    rng = _rng(12)
+    for C, r, F in ((5, 1, 30), (5, 1, 27), (2, 2, 13), (3, 0, 9)):
+        n = -(-F // C)
+        for fstar in range(F):
+            x = _random_unit(rng, F, 3, 4, 3, 0)
+            x["beta"][:] = 0.0
+            x["beta"][fstar] = rng.uniform(0.3, 1.0, 3)
+            out = _call(o, x, chunk=C, radius=r)
+            cs = fstar // C
+            for c in range(n):
+                frames = range(c * C, min(c * C + C, F))
+                seen = not (c - r <= cs <= c + r)
+                for f in frames:
+                    if seen:
+                        assert np.all(np.abs(out[f]).max(axis=-1) > 0), (C, r, F, fstar, c)
+                    else:
+                        assert np.all(out[f] == 0.0), (C, r, F, fstar, c)
+
+
+def pin_forward_reverse_regions(o):
+    """The forward state read by chunk c depends only on frames before chunk c-r and
+    the reverse state only on frames after chunk c+r: changing any other frame's
+    inputs leaves P[max(c-r,0)] and R[min(c+r+1,n)] unchanged."""
+    rng = _rng(13)
+    C, r, F = 3, 1, 14
+    n = -(-F // C)
+    x = _random_unit(rng, F, 3, 4, 3, 2)
+    _, t0 = _call(o, x, chunk=C, radius=r, taps=True)
+    for f in range(F):
+        y = {key: val.copy() for key, val in x.items()}
+        y["v"][f] += 1.0
+        _, t1 = _call(o, y, chunk=C, radius=r, taps=True)
+        for j in range(n + 1):
+            p_dep = f < j * C                 # P[j] covers frames [0, jC)
+            r_dep = f >= j * C                # R[j] covers frames [jC, F)
+            assert (np.max(np.abs(t1["P"][j] - t0["P"][j])) > 0) == p_dep, (f, j)
+            assert (np.max(np.abs(t1["R"][j] - t0["R"][j])) > 0) == r_dep, (f, j)
+
+
+def pin_chunk_composition(o):
+    """[VDN] Sec. 5 and Eq. (A.1): per-frame maps S -> S M_t + J_t compose per
+    chunk into one affine map; applying the chunk maps reproduces the per-frame
+    scan, and the reverse chunk transition is the transpose of the forward one
+    because each M_t is symmetric when alpha = 1."""
+    rng = _rng(14)
+    F, C, U, dk, dv = 13, 5, 6, 5, 4
+    x = _random_unit(rng, F, U, dk, dv, 3)
+    _, tap = _call(o, x, chunk=C, radius=1, taps=True)
+    n = -(-F // C)
+    I = np.eye(dk)
+    Ms = [np.linalg.inv(I + tap["A"][f]) for f in range(F)]
+    Js = [tap["B"][f] @ Ms[f] for f in range(F)]
+    P = [tap["P"][0]]
+    R = [None] * (n + 1)
+    R[n] = tap["R"][n]
+    chunks = [(s, min(s + C, F)) for s in range(0, F, C)]
+    maps = []
+    for lo, hi in chunks:
+        Mf, Jf = I.copy(), np.zeros((dv, dk))
+        for f in range(lo, hi):
+            Mf, Jf = Mf @ Ms[f], Jf @ Ms[f] + Js[f]
+        Mr, Jr = I.copy(), np.zeros((dv, dk))
+        for f in range(hi - 1, lo - 1, -1):
+            Mr, Jr = Mr @ Ms[f], Jr @ Ms[f] + Js[f]
+        assert np.max(np.abs(Mr - Mf.T)) <= 1e-12
+        maps.append((Mf, Jf, Mr, Jr))
+    for j in range(n):
+        P.append(P[j] @ maps[j][0] + maps[j][1])
+    for j in range(n - 1, -1, -1):
+        R[j] = R[j + 1] @ maps[j][2] + maps[j][3]
+    assert np.max(np.abs(np.array(P) - tap["P"])) <= 1e-12
+    assert np.max(np.abs(np.array(R) - tap["R"])) <= 1e-12
+    # M per frame matches the oracle's tap
+    assert np.max(np.abs(np.array(Ms) - tap["M"])) <= 1e-12
+
+
+def pin_golden_scan(o):
+    """golden/scan_scalar.json: d_k = d_v = 1, chunk 1, radius 1, four frames and one
+    text token, worked by hand (states P, R and the gathered states)."""
+    with open(os.path.join(GOLDEN, "scan_scalar.json")) as fh:
+        g = json.load(fh)
+    fr = lambda xs: np.array([float(Fraction(v)) for v in xs])  # noqa: E731
+    F = len(g["beta"])
+    k = np.ones((F, 1, 1))
+    v = fr(g["v"]).reshape(F, 1, 1)
+    beta = fr(g["beta"]).reshape(F, 1)
+    q = np.ones((F, 1, 1))
+    gate = np.zeros((F, 1, 1))
+    _, tap = o.forward_unit(q, k, v, beta, gate, np.ones((1, 1)), fr(g["text_v"]).reshape(1, 1),
+                            fr(g["text_beta"]), np.ones(1), chunk=1, radius=1, taps=True)
+    assert np.max(np.abs(tap["seed"].ravel() - float(Fraction(g["seed"])))) <= 1e-15
+    assert np.max(np.abs(tap["P"].ravel() - fr(g["P"]))) <= 1e-15
+    assert np.max(np.abs(tap["R"].ravel() - fr(g["R"]))) <= 1e-15
+    for c, want in enumerate(g["gathered"]):
+        St = o.gather(tap["P"], tap["R"], c, 1)
+        assert abs(St[0, 0] - float(Fraction(want))) <= 1e-15, c
+
+
+def pin_token_permutation(o):
+    """Frame-wise writes have no token order ([VDN] Sec. 3.1): permuting the tokens
+    of every frame permutes the output rows and leaves every state unchanged."""
+    rng = _rng(15)
+    F, U = 10, 8
+    x = _random_unit(rng, F, U, 5, 4, 3)
+    out, t0 = _call(o, x, chunk=5, radius=1, taps=True)
+    y = {key: val.copy() for key, val in x.items()}
+    perms = [rng.permutation(U) for _ in range(F)]
+    for f in range(F):
+        for key in ("q", "k", "v", "beta", "gate"):
+            y[key][f] = x[key][f][perms[f]]
+    out2, t1 = _call(o, y, chunk=5, radius=1, taps=True)
+    assert np.max(np.abs(t1["P"] - t0["P"])) <= 1e-12
+    assert np.max(np.abs(t1["R"] - t0["R"])) <= 1e-12
+    for f in range(F):
+        assert np.max(np.abs(out2[f] - out[f][perms[f]])) <= 1e-12
+
+
+def pin_all_beta_zero(o):
+    """No video writes: every state stays the seed exactly, so every chunk reads
+    seed + seed = S_T (Eq. (1b)); equal query rows in different chunks give
+    equal outputs."""
+    rng = _rng(16)
+    F, U, dk, dv = 12, 5, 4, 6
+    x = _random_unit(rng, F, U, dk, dv, 4)
+    x["beta"][:] = 0.0
+    x["q"][:] = x["q"][0]
+    x["gate"][:] = x["gate"][0]
+    out, tap = _call(o, x, chunk=5, radius=1, taps=True)
+    for j in range(tap["P"].shape[0]):
+        assert np.array_equal(tap["P"][j], tap["seed"])
+        assert np.array_equal(tap["R"][j], tap["seed"])
+    for f in range(1, F):
+        assert np.max(np.abs(out[f] - out[0])) <= 1e-14
+
+
+# ----------------------------------------------------------------------------- a7: epilogue
+def pin_rmsnorm_gate(o):
+    """Eq. (1c): RMSNorm makes each row's mean square ms/(ms + eps) (~1), is
+    invariant to rescaling the row (exactly with eps = 0), and sigmoid(0) = 1/2."""
+    rng = _rng(17)
+    Oq = rng.standard_normal((7, 12)) * 3.0
+    w = np.ones(12)
+    y = o.rms_norm(Oq, w, 0.0)
+    assert np.max(np.abs(np.mean(y * y, axis=-1) - 1.0)) <= 1e-13
+    assert np.max(np.abs(o.rms_norm(5.5 * Oq, w, 0.0) - y)) <= 1e-13
+    ye = o.rms_norm(Oq, w, 1e-6)
+    ms = np.mean(Oq * Oq, axis=-1)
+    assert np.max(np.abs(np.mean(ye * ye, axis=-1) - ms / (ms + 1e-6))) <= 1e-13
+    w2 = rng.uniform(0.5, 2.0, 12)
+    assert np.max(np.abs(o.rms_norm(Oq, w2, 0.0) - w2 * y)) <= 1e-13
+    assert abs(o.sigmoid(0.0) - 0.5) == 0.0
+    assert abs(o.sigmoid(np.log(3.0)) - 0.75) <= 1e-15
+    # readout: o = S q (hand loop); a saturated gate (sigmoid(40) == 1 in fp64)
+    # leaves the normalised o, a zero gate halves it.  A square, non-symmetric
+    # state makes a transposed operand visible.
+    for dv, dk in ((12, 5), (6, 6)):
+        S = rng.standard_normal((dv, dk))
+        Q = rng.standard_normal((7, dk))
+        O = np.zeros((7, dv))
+        for t in range(7):
+            for i in range(dv):
+                O[t, i] = sum(S[i, kk] * Q[t, kk] for kk in range(dk))
+        full = o.readout(S, Q, np.full((7, dv), 40.0), np.ones(dv), 0.0)
+        assert np.max(np.abs(np.mean(full * full, axis=-1) - 1.0)) <= 1e-13
+        for t in range(7):
+            cos = full[t] @ O[t] / (np.linalg.norm(full[t]) * np.linalg.norm(O[t]))
+            assert abs(cos - 1.0) <= 1e-13
+        half = o.readout(S, Q, np.zeros((7, dv)), np.ones(dv), 0.0)
+        assert np.max(np.abs(half - 0.5 * full)) <= 1e-13
+
+
+ALL_PINS = [
+    pin_stats_hand_loop, pin_stats_invariants, pin_gradient_zero, pin_lstsq_bruteforce,
+    pin_sherman_morrison, pin_repeated_keys, pin_orthonormal_keys, pin_beta_zero,
+    pin_non_expansive, pin_scalar_case, pin_orthonormal_golden, pin_exactly_once,
+    pin_time_reversal, pin_disjointness, pin_forward_reverse_regions, pin_chunk_composition,
+    pin_golden_scan, pin_token_permutation, pin_all_beta_zero, pin_rmsnorm_gate,
+]

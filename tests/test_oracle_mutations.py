@@ -1,0 +1,213 @@
+"""Planted mistakes in a private copy of the oracle must each break a pin.
+
+Every mutation below is a plausible slip (a dropped term, a wrong sign, an
+off-by-one index, a transposed operand, a swapped direction).  The test loads a
+fresh copy of the oracle module, plants one mistake in it (CPU only), runs the
+pin suite and requires at least one pin to fail.  The real oracle is untouched.
+"""
+import importlib.util
+import os
+
+import numpy as np
+import pytest
+
+import oracle_pins
+
+ORACLE_FILE = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                           "oracle", "vda_oracle.py")
+
+
+def fresh_oracle():
+    spec = importlib.util.spec_from_file_location("vda_oracle_mutant", ORACLE_FILE)
+    m = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(m)
+    return m
+
+
+def _stats_no_beta(m):
+    def frame_statistics(K, V, beta):
+        K = np.asarray(K, float)
+        V = np.asarray(V, float)
+        return K.T @ K, V.T @ K
+    m.frame_statistics = frame_statistics
+
+
+def _stats_beta_squared(m):
+    orig = m.frame_statistics
+
+    def frame_statistics(K, V, beta):
+        return orig(K, V, np.asarray(beta, float) ** 2)
+    m.frame_statistics = frame_statistics
+
+
+def _stats_b_swapped(m):
+    def frame_statistics(K, V, beta):
+        K = np.asarray(K, float)
+        V = np.asarray(V, float)
+        b = np.asarray(beta, float)
+        A = K.T @ (b[:, None] * K)
+        Bt = K.T @ (b[:, None] * V)
+        return A, Bt.T if Bt.shape[0] != Bt.shape[1] else Bt
+    m.frame_statistics = frame_statistics
+
+
+def _update_minus(m):
+    def frame_update(S_bar, A, B):
+        G = np.eye(A.shape[0]) - A
+        return np.linalg.solve(G.T, (S_bar + B).T).T
+    m.frame_update = frame_update
+
+
+def _update_no_identity(m):
+    def frame_update(S_bar, A, B):
+        G = A + 1e-3 * np.eye(A.shape[0])
+        return np.linalg.solve(G.T, (S_bar + B).T).T
+    m.frame_update = frame_update
+
+
+def _update_drops_inherited(m):
+    def frame_update(S_bar, A, B):
+        G = np.eye(A.shape[0]) + A
+        return S_bar + np.linalg.solve(G.T, B.T).T
+    m.frame_update = frame_update
+
+
+def _update_frozen_state(m):
+    # the additive rule S_bar (I - A) + B ([VDN] Eq. (3c)) instead of the joint solve
+    def frame_update(S_bar, A, B):
+        return S_bar @ (np.eye(A.shape[0]) - A) + B
+    m.frame_update = frame_update
+
+
+def _update_left_multiplied(m):
+    def frame_update(S_bar, A, B):
+        G = np.eye(A.shape[0]) + A
+        R = S_bar + B
+        if R.shape[0] == G.shape[0]:
+            return np.linalg.solve(G, R)
+        return np.linalg.solve(G.T, R.T).T @ G @ G  # still wrong when not square
+    m.frame_update = frame_update
+
+
+def _seed_not_halved(m):
+    orig = m.text_state
+
+    def text_state(*a, **kw):
+        return 2.0 * orig(*a, **kw)
+    m.text_state = text_state
+
+
+def _gather_fwd_off_by_one(m):
+    def gather(P, R, c, radius):
+        n = P.shape[0] - 1
+        return P[min(max(c - radius + 1, 0), n)] + R[min(c + radius + 1, n)]
+    m.gather = gather
+
+
+def _gather_rev_off_by_one(m):
+    def gather(P, R, c, radius):
+        n = P.shape[0] - 1
+        return P[max(c - radius, 0)] + R[min(c + radius, n)]
+    m.gather = gather
+
+
+def _gather_swapped(m):
+    def gather(P, R, c, radius):
+        n = P.shape[0] - 1
+        return R[max(c - radius, 0)] + P[min(c + radius + 1, n)]
+    m.gather = gather
+
+
+def _reverse_scan_store_late(m):
+    orig = m.directional_states
+
+    def directional_states(stats, seed, C):
+        P, R = orig(stats, seed, C)
+        R2 = R.copy()
+        R2[:-1] = R[1:]   # R[j] := state after chunk j+1
+        return P, R2
+    m.directional_states = directional_states
+
+
+def _forward_scan_skips_last_frame(m):
+    def directional_states(stats, seed, C):
+        F = len(stats)
+        bounds = m.chunk_bounds(F, C)
+        n = len(bounds)
+        P = np.zeros((n + 1,) + seed.shape)
+        R = np.zeros((n + 1,) + seed.shape)
+        S = seed.copy()
+        P[0] = S
+        for j, (lo, hi) in enumerate(bounds):
+            for f in range(lo, hi - 1):
+                S = m.frame_update(S, *stats[f])
+            P[j + 1] = S
+        S = seed.copy()
+        R[n] = S
+        for j in range(n - 1, -1, -1):
+            lo, hi = bounds[j]
+            for f in range(hi - 1, lo - 1, -1):
+                S = m.frame_update(S, *stats[f])
+            R[j] = S
+        return P, R
+    m.directional_states = directional_states
+
+
+def _rms_sum_not_mean(m):
+    def rms_norm(O, w, eps):
+        O = np.asarray(O, float)
+        return np.asarray(w, float) * O / np.sqrt(np.sum(O * O, axis=-1, keepdims=True) + eps)
+    m.rms_norm = rms_norm
+
+
+def _rms_wrong_axis(m):
+    def rms_norm(O, w, eps):
+        O = np.asarray(O, float)
+        ax = 0 if O.ndim > 1 else -1
+        return np.asarray(w, float) * O / np.sqrt(np.mean(O * O, axis=ax, keepdims=True) + eps)
+    m.rms_norm = rms_norm
+
+
+def _sigmoid_sign(m):
+    m.sigmoid = lambda x: 1.0 / (1.0 + np.exp(np.asarray(x, float)))
+
+
+def _readout_transposed(m):
+    def readout(S_tilde, Q, G, w, eps):
+        S = np.asarray(S_tilde, float)
+        O = np.asarray(Q, float) @ (S if S.shape[0] == S.shape[1] else S.T)
+        return m.sigmoid(G) * m.rms_norm(O, w, eps)
+    m.readout = readout
+
+
+def _transition_wrong(m):
+    m.transition = lambda A: np.eye(A.shape[0]) - A
+
+
+MUTATIONS = {f.__name__.lstrip("_"): f for f in [
+    _stats_no_beta, _stats_beta_squared, _stats_b_swapped, _update_minus, _update_no_identity,
+    _update_drops_inherited, _update_frozen_state, _update_left_multiplied, _seed_not_halved,
+    _gather_fwd_off_by_one, _gather_rev_off_by_one, _gather_swapped, _reverse_scan_store_late,
+    _forward_scan_skips_last_frame, _rms_sum_not_mean, _rms_wrong_axis, _sigmoid_sign,
+    _readout_transposed, _transition_wrong,
+]}
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_mutation_is_caught(name):
+    m = fresh_oracle()
+    MUTATIONS[name](m)
+    failed = []
+    for pin in oracle_pins.ALL_PINS:
+        try:
+            with np.errstate(all="ignore"):
+                pin(m)
+        except Exception:  # AssertionError, or a shape error from the planted slip
+            failed.append(pin.__name__)
+    assert failed, f"no pin caught the planted mistake {name}"
+
+
+def test_unmutated_copy_passes():
+    m = fresh_oracle()
+    for pin in oracle_pins.ALL_PINS:
+        pin(m)
