@@ -1,0 +1,226 @@
+#!/usr/bin/env python3
+"""Throughput of the VDA forward pass on one MI355X.
+
+One step = one vda_forward call (statistics, Cholesky solve, chunk composition,
+bidirectional boundary scan, fused readout) over the whole workload, inputs
+already resident in HBM.  Default workload: the 768p-shaped one-GPU head share
+(16 heads x 90 latent frames x 4032 tokens, d_k = d_v = 128, 512 text tokens,
+bf16 features, fp32 state), synthetic seeded inputs.
+
+Prints ONE JSON line: token-heads/s, the roofline of the dominant kernel
+(timed with HIP events recorded by the library on the launch stream), the
+MFMA fraction the metric asks for, and the fp64 CPU oracle timed on a bounded
+sample of the same workload on the host cores.
+
+  python bench.py [--steps K] [--warmup W] [--config 4] [--cpu-seconds S]
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "VDA fwd tokens/sec per head-layer on 1 MI355X; % MFMA peak"
+HBM_PEAK = 8.0e12          # MI355X HBM3E, bytes/s
+BF16_PEAK = 2.5166e15      # MI355X dense bf16 MFMA, flop/s
+PROFILES = os.path.join(ROOT, "profiles")
+STAGES = ("stats", "solve", "compose", "scan", "readout")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def algorithmic(cfg):
+    """Algorithmic HBM bytes and bf16 MFMA flops per launch of each streaming kernel."""
+    eb = 2 if cfg.dtype == "bf16" else 4
+    th = cfg.units * cfg.frames * cfg.tokens        # token-heads
+    tt = cfg.units * cfg.text_tokens
+    dk, dv, n = cfg.d_k, cfg.d_v, cfg.n_chunks
+    stats_bytes = ((th + tt) * ((dk + dv) * eb + 4)                     # k, v, beta read
+                   + cfg.units * (cfg.frames + 1) * (dk + dv) * dk * 4)  # A, B written
+    readout_bytes = (th * (dk + 2 * dv) * eb                           # q, gate read; out written
+                     + cfg.units * n * 2 * dv * dk * 4 + dv * 4)        # two states per chunk
+    stats_flops = 2 * (th + tt) * (dk + dv) * dk     # [K|V]^T (beta K), full Gram
+    readout_flops = 2 * th * dk * dv                 # S~ q
+    return {"stats": (stats_bytes, stats_flops), "readout": (readout_bytes, readout_flops)}
+
+
+def source_digest(kernel):
+    path = os.path.join(ROOT, "frame_wise_delta_gram_amd", "csrc",
+                        {"stats": "k_stats.hip", "readout": "k_readout.hip"}[kernel])
+    with open(path, "rb") as fh:
+        return hashlib.sha256(fh.read()).hexdigest()
+
+
+def measured_traffic(kernel, workload):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or None
+    when there is none or the kernel source changed since it was taken."""
+    path = os.path.join(PROFILES, f"traffic_{kernel}_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        rec = json.load(fh)
+    if rec.get("source_sha256") != source_digest(kernel):
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(d, cfg, budget_s):
+    """The fp64 oracle on whole units of the same inputs until ~budget_s of CPU time."""
+    import numpy as np
+    import oracle
+    import workloads as W
+    from threadpoolctl import threadpool_info
+
+    feats = ("q", "k", "v", "gate", "text_k", "text_v")
+    done = 0
+    elapsed = 0.0
+    for u in range(cfg.units):
+        x = {}
+        for name, t in d.items():
+            a = W.tensor_to_host(t if name == "rms_weight" else t[u:u + 1])
+            x[name] = W.to_f64(a, cfg.dtype) if name in feats else a.astype(np.float64)
+        t0 = time.perf_counter()
+        oracle.forward(x["q"], x["k"], x["v"], x["beta"], x["gate"], x["text_k"], x["text_v"],
+                       x["text_beta"], x["rms_weight"], chunk=cfg.chunk, radius=cfg.radius,
+                       eps=cfg.rms_eps)
+        elapsed += time.perf_counter() - t0
+        done += 1
+        log(f"[bench] oracle unit {u}: {elapsed:.1f} s total")
+        if elapsed >= budget_s:
+            break
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    th = done * cfg.frames * cfg.tokens
+    return {"value": th / elapsed, "unit": "token-heads/s", "cores": threads, "kind": "oracle",
+            "sample": f"{done} of {cfg.units} units of the same inputs (all {cfg.frames} frames "
+                      f"x {cfg.tokens} tokens each), fp64 numpy, {elapsed:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", type=int, default=4, help="workload id (4 = 768p-bf16)")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="CPU budget of the oracle baseline (0 disables it)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the VDA forward shards by head with no "
+              "communication inside the op, and this build runs on a single MI355X. "
+              "Run it with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import frame_wise_delta_gram_amd as vda
+    import workloads as W
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    vda.load_library()
+    cfg = W.CONFIGS[args.config]
+    log(f"[bench] generating {cfg.name} inputs on the device")
+    d = W.device_inputs(cfg)
+    torch.cuda.synchronize()
+    desc = vda.make_desc(cfg.units, cfg.frames, cfg.tokens, cfg.text_tokens, cfg.d_k, cfg.d_v,
+                         cfg.chunk, cfg.radius, cfg.rms_eps, 0,
+                         vda.VDA_DTYPE_BF16 if cfg.dtype == "bf16" else vda.VDA_DTYPE_F32)
+    ws = torch.empty(max(vda.vda_workspace_bytes(desc), 1), dtype=torch.uint8, device="cuda")
+    out = torch.empty((cfg.units, cfg.frames, cfg.tokens, cfg.d_v), device="cuda",
+                      dtype=d["q"].dtype)
+    stream = torch.cuda.current_stream()
+    args_fw = (desc, d["q"], d["k"], d["v"], d["beta"], d["gate"], d["text_k"], d["text_v"],
+               d["text_beta"], d["rms_weight"], out, ws)
+
+    hip = ctypes.CDLL(os.path.join(os.path.dirname(torch.__file__), "lib", "libamdhip64.so"))
+    hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+    hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+    hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                        ctypes.c_void_p]
+    events = []
+    for _ in range(args.steps):
+        row = []
+        for _ in range(6):
+            e = ctypes.c_void_p()
+            if hip.hipEventCreate(ctypes.byref(e)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+            row.append(e.value)
+        events.append(row)
+
+    log(f"[bench] warmup {args.warmup}")
+    for _ in range(args.warmup):
+        vda.vda_forward(*args_fw, stream=stream)
+    torch.cuda.synchronize()
+    log(f"[bench] timing {args.steps} steps")
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        vda.vda_forward_timed(*args_fw, events[i], stream=stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    elapsed = t1 - t0
+
+    stage_ms = {s: [] for s in STAGES}
+    for row in events:
+        for j, s in enumerate(STAGES):
+            ms = ctypes.c_float()
+            if hip.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(row[j]),
+                                       ctypes.c_void_p(row[j + 1])) != 0:
+                raise RuntimeError("hipEventElapsedTime failed")
+            stage_ms[s].append(ms.value)
+    for row in events:
+        for e in row:
+            hip.hipEventDestroy(ctypes.c_void_p(e))
+    avg_ms = {s: sum(v) / len(v) for s, v in stage_ms.items()}
+
+    th = cfg.token_heads
+    ms_per_step = elapsed * 1e3 / args.steps
+    value = th * args.steps / elapsed
+    alg = algorithmic(cfg)
+    dominant = max(("stats", "readout"), key=lambda s: avg_ms[s])
+    bytes_, flops = alg[dominant]
+    achieved = bytes_ / (avg_ms[dominant] * 1e-3)
+    workload = cfg.name
+    roofline = {"bound": "hbm", "kernel": dominant, "achieved": achieved / 1e9,
+                "peak": HBM_PEAK / 1e9, "unit": "GB/s", "frac": achieved / HBM_PEAK,
+                "traffic": measured_traffic(dominant, workload),
+                "algorithmic_bytes_per_launch": bytes_, "avg_launch_ms": avg_ms[dominant]}
+    whole_flops = alg["stats"][1] + alg["readout"][1]
+    mfma = {
+        "whole_op": whole_flops / (ms_per_step * 1e-3) / BF16_PEAK,
+        "stats": alg["stats"][1] / (avg_ms["stats"] * 1e-3) / BF16_PEAK,
+        "readout": alg["readout"][1] / (avg_ms["readout"] * 1e-3) / BF16_PEAK,
+    }
+    hbm_whole = (alg["stats"][0] + alg["readout"][0]) / (ms_per_step * 1e-3) / HBM_PEAK
+    line = {
+        "metric": METRIC, "value": value, "unit": "token-heads/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": cfg.dtype, "data": "synthetic",
+        "config": {"workload": workload, "units": cfg.units, "frames": cfg.frames,
+                   "tokens_per_frame": cfg.tokens, "d_k": cfg.d_k, "d_v": cfg.d_v,
+                   "text_tokens": cfg.text_tokens, "chunk": cfg.chunk, "radius": cfg.radius,
+                   "state": "fp32", "parallelism": "single GPU"},
+        "roofline": roofline,
+        "mfma_frac": mfma,
+        "hbm_frac_whole_op": hbm_whole,
+        "stage_ms": avg_ms,
+    }
+    if args.cpu_seconds > 0:
+        log("[bench] CPU oracle baseline")
+        line["cpu_baseline"] = cpu_baseline(d, cfg, args.cpu_seconds)
+    else:
+        line["cpu_baseline"] = None
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,254 @@
+"""ctypes binding of libvda.so (Video Delta Attention forward on MI355X).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of libvda.so.  The functions mirror the C ABI in include/vda.h and
+have the same names; tensors are torch tensors on the GPU (their data_ptr() is
+passed), and the stream defaults to torch's current stream.  There is no CPU
+fallback: when the library is missing or no GPU is present these functions
+raise.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libvda.so")
+
+VDA_OK = 0
+VDA_ERR_INVALID_ARG = -1
+VDA_ERR_BAD_DTYPE = -2
+VDA_ERR_WORKSPACE_TOO_SMALL = -3
+VDA_ERR_MISALIGNED = -4
+VDA_ERR_HIP = -5
+VDA_DTYPE_F32 = 0
+VDA_DTYPE_BF16 = 1
+
+EXPORTED = ("vda_workspace_bytes", "vda_check_desc", "vda_forward", "vda_forward_timed",
+            "vda_debug_stats",
+            "vda_debug_solve", "vda_debug_chunks", "vda_debug_states", "vda_status_string")
+
+
+class VdaDesc(ctypes.Structure):
+    """vda_desc_t of include/vda.h."""
+    _fields_ = [
+        ("units", ctypes.c_int32), ("frames", ctypes.c_int32), ("tokens", ctypes.c_int32),
+        ("text_tokens", ctypes.c_int32), ("d_k", ctypes.c_int32), ("d_v", ctypes.c_int32),
+        ("chunk", ctypes.c_int32), ("radius", ctypes.c_int32), ("rms_eps", ctypes.c_float),
+        ("seed_mode", ctypes.c_int32), ("in_dtype", ctypes.c_int32), ("out_dtype", ctypes.c_int32),
+    ]
+
+    @property
+    def n_chunks(self):
+        return -(-self.frames // self.chunk) if self.frames > 0 else 0
+
+
+class VdaError(RuntimeError):
+    def __init__(self, status, fn):
+        self.status = status
+        super().__init__("%s failed: %s (%d)" % (fn, vda_status_string(status), status))
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH):
+    """Load libvda.so (once).  Raises when it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError("libvda.so is not built (%s); run `python -m "
+                           "frame_wise_delta_gram_amd.build`" % path)
+    try:  # bind to the HIP runtime torch already uses (one runtime per process)
+        import torch  # noqa: F401
+    except ImportError:
+        pass
+    lib = ctypes.CDLL(path)
+    P = ctypes.c_void_p
+    D = ctypes.POINTER(VdaDesc)
+    lib.vda_workspace_bytes.argtypes = [D]
+    lib.vda_workspace_bytes.restype = ctypes.c_size_t
+    lib.vda_check_desc.argtypes = [D]
+    lib.vda_check_desc.restype = ctypes.c_int
+    lib.vda_forward.argtypes = [D] + [P] * 11 + [ctypes.c_size_t, P]
+    lib.vda_forward.restype = ctypes.c_int
+    lib.vda_forward_timed.argtypes = [D] + [P] * 11 + [ctypes.c_size_t, P,
+                                                      ctypes.POINTER(ctypes.c_void_p), ctypes.c_int]
+    lib.vda_forward_timed.restype = ctypes.c_int
+    lib.vda_debug_stats.argtypes = [D] + [P] * 9 + [ctypes.c_size_t, P]
+    lib.vda_debug_stats.restype = ctypes.c_int
+    lib.vda_debug_solve.argtypes = [D] + [P] * 9 + [ctypes.c_size_t, P]
+    lib.vda_debug_solve.restype = ctypes.c_int
+    lib.vda_debug_chunks.argtypes = [D] + [P] * 10 + [ctypes.c_size_t, P]
+    lib.vda_debug_chunks.restype = ctypes.c_int
+    lib.vda_debug_states.argtypes = [D] + [P] * 9 + [ctypes.c_size_t, P]
+    lib.vda_debug_states.restype = ctypes.c_int
+    lib.vda_status_string.argtypes = [ctypes.c_int]
+    lib.vda_status_string.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def vda_status_string(status: int) -> str:
+    return load_library().vda_status_string(int(status)).decode()
+
+
+def make_desc(units, frames, tokens, text_tokens, d_k, d_v, chunk=5, radius=1, rms_eps=1e-6,
+              seed_mode=0, dtype=VDA_DTYPE_BF16) -> VdaDesc:
+    return VdaDesc(units, frames, tokens, text_tokens, d_k, d_v, chunk, radius, rms_eps,
+                   seed_mode, dtype, dtype)
+
+
+def vda_workspace_bytes(desc: VdaDesc) -> int:
+    return int(load_library().vda_workspace_bytes(ctypes.byref(desc)))
+
+
+def vda_check_desc(desc: VdaDesc) -> int:
+    return int(load_library().vda_check_desc(ctypes.byref(desc)))
+
+
+def _ptr(x):
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return x.data_ptr() if x.numel() > 0 else None
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check(status, fn):
+    if status != VDA_OK:
+        raise VdaError(status, fn)
+
+
+def vda_forward(desc, q, k, v, beta, gate, text_k, text_v, text_beta, rms_weight, out,
+                workspace, workspace_bytes=None, stream=None):
+    """C vda_forward: enqueue the forward pass on `stream` (torch's current by default)."""
+    if workspace_bytes is None:
+        workspace_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = load_library().vda_forward(
+        ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(gate), _ptr(text_k),
+        _ptr(text_v), _ptr(text_beta), _ptr(rms_weight), _ptr(out), _ptr(workspace),
+        workspace_bytes, _stream(stream))
+    _check(st, "vda_forward")
+
+
+def vda_forward_timed(desc, q, k, v, beta, gate, text_k, text_v, text_beta, rms_weight, out,
+                      workspace, stage_events, workspace_bytes=None, stream=None):
+    """C vda_forward_timed: as vda_forward, recording the six caller-created
+    hipEvent_t handles (ints) in ``stage_events`` at the stage boundaries."""
+    ev = (ctypes.c_void_p * 6)(*[int(e) for e in stage_events])
+    st = load_library().vda_forward_timed(
+        ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(gate), _ptr(text_k),
+        _ptr(text_v), _ptr(text_beta), _ptr(rms_weight), _ptr(out), _ptr(workspace),
+        _ws_bytes(workspace, workspace_bytes), _stream(stream), ev, len(stage_events))
+    _check(st, "vda_forward_timed")
+
+
+def _ws_bytes(workspace, workspace_bytes):
+    if workspace_bytes is not None:
+        return workspace_bytes
+    return workspace.numel() * workspace.element_size() if workspace is not None else 0
+
+
+def vda_debug_stats(desc, k, v, beta, text_k, text_v, text_beta, A_out, B_out, workspace,
+                    workspace_bytes=None, stream=None):
+    st = load_library().vda_debug_stats(
+        ctypes.byref(desc), _ptr(k), _ptr(v), _ptr(beta), _ptr(text_k), _ptr(text_v),
+        _ptr(text_beta), _ptr(A_out), _ptr(B_out), _ptr(workspace),
+        _ws_bytes(workspace, workspace_bytes), _stream(stream))
+    _check(st, "vda_debug_stats")
+
+
+def vda_debug_solve(desc, k, v, beta, text_k, text_v, text_beta, M_out, seed_out, workspace,
+                    workspace_bytes=None, stream=None):
+    st = load_library().vda_debug_solve(
+        ctypes.byref(desc), _ptr(k), _ptr(v), _ptr(beta), _ptr(text_k), _ptr(text_v),
+        _ptr(text_beta), _ptr(M_out), _ptr(seed_out), _ptr(workspace),
+        _ws_bytes(workspace, workspace_bytes), _stream(stream))
+    _check(st, "vda_debug_solve")
+
+
+def vda_debug_chunks(desc, k, v, beta, text_k, text_v, text_beta, Mc_out, Jf_out, Jr_out,
+                     workspace, workspace_bytes=None, stream=None):
+    st = load_library().vda_debug_chunks(
+        ctypes.byref(desc), _ptr(k), _ptr(v), _ptr(beta), _ptr(text_k), _ptr(text_v),
+        _ptr(text_beta), _ptr(Mc_out), _ptr(Jf_out), _ptr(Jr_out), _ptr(workspace),
+        _ws_bytes(workspace, workspace_bytes), _stream(stream))
+    _check(st, "vda_debug_chunks")
+
+
+def vda_debug_states(desc, k, v, beta, text_k, text_v, text_beta, P_out, R_out, workspace,
+                     workspace_bytes=None, stream=None):
+    st = load_library().vda_debug_states(
+        ctypes.byref(desc), _ptr(k), _ptr(v), _ptr(beta), _ptr(text_k), _ptr(text_v),
+        _ptr(text_beta), _ptr(P_out), _ptr(R_out), _ptr(workspace),
+        _ws_bytes(workspace, workspace_bytes), _stream(stream))
+    _check(st, "vda_debug_states")
+
+
+# ----------------------------------------------------------------------------- torch helpers
+def desc_from_tensors(q, k, v, text_k, chunk=5, radius=1, eps=1e-6, seed_mode=0) -> VdaDesc:
+    """Descriptor from tensor shapes: q/k [units, F, U, d_k], v [units, F, U, d_v],
+    text_k [units, T, d_k]."""
+    import torch
+    units, F, U, dk = k.shape
+    dv = v.shape[-1]
+    T = text_k.shape[1] if text_k is not None else 0
+    if k.dtype == torch.bfloat16:
+        dt = VDA_DTYPE_BF16
+    elif k.dtype == torch.float32:
+        dt = VDA_DTYPE_F32
+    else:
+        raise TypeError("features must be bfloat16 or float32, got %s" % k.dtype)
+    return make_desc(units, F, U, T, dk, dv, chunk, radius, eps, seed_mode, dt)
+
+
+def _check_tensor(name, x, dtype, shape):
+    if x.dtype != dtype:
+        raise TypeError("%s: expected %s, got %s" % (name, dtype, x.dtype))
+    if tuple(x.shape) != tuple(shape):
+        raise ValueError("%s: expected shape %s, got %s" % (name, tuple(shape), tuple(x.shape)))
+    if x.numel() > 0 and (not x.is_cuda or not x.is_contiguous()):
+        raise ValueError("%s must be a contiguous GPU tensor" % name)
+
+
+def forward(q, k, v, beta, gate, text_k, text_v, text_beta, rms_weight, chunk=5, radius=1,
+            eps=1e-6, seed_mode=0, out=None, workspace=None, stream=None):
+    """VDA forward on torch GPU tensors; allocates `out` and the workspace when absent.
+
+    Shapes: q, k [units, F, U, d_k]; v, gate [units, F, U, d_v]; beta [units, F, U]
+    (float32); text_k [units, T, d_k]; text_v [units, T, d_v]; text_beta
+    [units, T] (float32); rms_weight [d_v] (float32).  Returns out
+    [units, F, U, d_v] in the features' dtype.
+    """
+    import torch
+    desc = desc_from_tensors(q, k, v, text_k, chunk, radius, eps, seed_mode)
+    units, F, U, dk = k.shape
+    dv = v.shape[-1]
+    T = desc.text_tokens
+    fdt = k.dtype
+    for name, x, shp in (("q", q, (units, F, U, dk)), ("v", v, (units, F, U, dv)),
+                         ("gate", gate, (units, F, U, dv)), ("text_k", text_k, (units, T, dk)),
+                         ("text_v", text_v, (units, T, dv))):
+        _check_tensor(name, x, fdt, shp)
+    _check_tensor("beta", beta, torch.float32, (units, F, U))
+    _check_tensor("text_beta", text_beta, torch.float32, (units, T))
+    _check_tensor("rms_weight", rms_weight, torch.float32, (dv,))
+    if out is None:
+        out = torch.empty((units, F, U, dv), dtype=fdt, device=k.device)
+    nbytes = vda_workspace_bytes(desc)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=k.device)
+    vda_forward(desc, q, k, v, beta, gate, text_k, text_v, text_beta, rms_weight, out,
+                workspace, stream=stream)
+    return out

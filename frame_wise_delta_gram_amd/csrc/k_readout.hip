@@ -1,0 +1,265 @@
+// Readout of the bidirectional linear memory ("Video DeltaNet", arXiv
+// 2609.20744, Sec. 2.2 Eq. (1a), App. A.3 Eq. (A.4) with alpha = 1, Sec. 2.3
+// Eq. (1c)), fused with the gather and the epilogue:
+//
+//   gather:  a query of chunk c reads S~ = P[max(c - r, 0)] + R[min(c + r + 1, n)]
+//            (forward state of the chunks before the window, reverse state of
+//            those after it; the two regions are disjoint)
+//   readout: o = S~ q                              (d_v outputs per token)
+//   epilogue: out = sigmoid(g) * w * o / sqrt(mean(o^2) + eps)
+//
+// bf16 path.  One workgroup per (unit, chunk, block of 1024 token rows); all
+// frames of a chunk share S~.  S~ is formed in fp32, split into a bf16 high
+// part and a bf16 residual (S~ = hi + lo to ~2^-17 relative) and kept in LDS,
+// so the readout is two bf16 MFMAs with fp32 accumulation and the HBM-bound
+// stream of q, gate and out never waits on a conversion.  The transposed
+// product O^T = S~ Q^T runs on v_mfma_f32_32x32x16_bf16 with q as the B
+// operand, loaded straight from HBM (lane l: token l % 32, half l / 32 of its
+// channels, 16-byte loads).  S~'s rows are stored in a permuted order such that
+// accumulator register r of tile T in lane l holds output channel
+//   (l / 32) * d_v' / 2 + 16 T + r,
+// i.e. each lane ends with one contiguous half-row of its token: the RMSNorm
+// reduction is a lane-local sum plus one cross-lane add, and gate loads and
+// output stores are 16-byte vectors.  Math in the epilogue is fp32; the output
+// is rounded to bf16 (nearest even).
+//
+// fp32 path: the same computation on the vector ALUs in fp32.
+#include "vda_device.h"
+#include "vda_internal.h"
+
+namespace vda {
+namespace {
+
+constexpr int kIters = 8;                 // 32-row blocks per wave
+constexpr int kRows = 4 * 32 * kIters;    // token rows per workgroup
+
+__global__ __launch_bounds__(256, 2) void readout_bf16_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ gate,
+    const float* __restrict__ wrms, uint16_t* __restrict__ out, const float* __restrict__ ST,
+    int dk, int dv, int F, int U, int C, int radius, int n, float eps) {
+  __shared__ __align__(16) uint16_t Shi[128 * 136];
+  __shared__ __align__(16) uint16_t Slo[128 * 136];
+
+  const int blk = blockIdx.x;
+  const int c = blockIdx.y;
+  const int u = blockIdx.z;
+  const int f0 = c * C;
+  const int f1 = min(f0 + C, F);
+  const long rows_total = (long)(f1 - f0) * U;
+  const long row0 = (long)blk * kRows;
+  if (row0 >= rows_total) return;
+
+  const int t = threadIdx.x;
+  const int lane = t & 63;
+  const int w = t >> 6;
+  const int Dvp = pad32(dv);
+  const int NT = Dvp >> 5;     // 32-channel output tiles
+  const int HALF = Dvp >> 1;   // output channels per lane
+  const int SROW = dk + 8;     // LDS row stride (bf16 elements)
+  const int halfk = dk >> 1;   // input channels per lane half
+  const int NKS = dk >> 4;     // k-steps of 16 channels
+
+  // gather S~ and split it into bf16 hi + lo, rows permuted (see header)
+  {
+    const size_t SS = (size_t)dv * dk;
+    const int pi = max(c - radius, 0);
+    const int ri = min(c + radius + 1, n);
+    const float* P = ST + ((size_t)(u * 2 + 0) * (n + 1) + pi) * SS;
+    const float* R = ST + ((size_t)(u * 2 + 1) * (n + 1) + ri) * SS;
+    const int k8n = dk >> 3;
+    for (int it = t; it < Dvp * k8n; it += 256) {
+      const int ch = it / k8n;
+      const int k8 = it - ch * k8n;
+      const int h = ch / HALF;
+      const int rem = ch - h * HALF;
+      const int T = rem >> 4;
+      const int rr = rem & 15;
+      const int lrow = 32 * T + 8 * (rr >> 2) + 4 * h + (rr & 3);
+      u32x4_t hi = {0u, 0u, 0u, 0u}, lo = {0u, 0u, 0u, 0u};
+      if (ch < dv) {
+        const f32x4_t* pp = reinterpret_cast<const f32x4_t*>(P + (size_t)ch * dk + 8 * k8);
+        const f32x4_t* rp = reinterpret_cast<const f32x4_t*>(R + (size_t)ch * dk + 8 * k8);
+        const f32x4_t p0 = pp[0], p1 = pp[1], r0 = rp[0], r1 = rp[1];
+        float x[8];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          x[e] = p0[e] + r0[e];
+          x[4 + e] = p1[e] + r1[e];
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t hp = pack_bf16(x[2 * e], x[2 * e + 1]);
+          hi[e] = hp;
+          lo[e] = pack_bf16(x[2 * e] - bf16_lo(hp), x[2 * e + 1] - bf16_hi(hp));
+        }
+      }
+      *reinterpret_cast<u32x4_t*>(Shi + lrow * SROW + 8 * k8) = hi;
+      *reinterpret_cast<u32x4_t*>(Slo + lrow * SROW + 8 * k8) = lo;
+    }
+  }
+  __syncthreads();
+
+  const int g = lane >> 5;      // half of the input channels (B operand k slots) and of the outputs
+  const int il = lane & 31;     // token within the 32-row block
+  const size_t chunk_row0 = ((size_t)u * F + f0) * U;
+  const float inv_dv = 1.0f / (float)dv;
+
+  for (int it = 0; it < kIters; ++it) {
+    const long rb = row0 + (long)(it * 4 + w) * 32;
+    if (rb >= rows_total) break;
+    const long myrow = rb + il;
+    const bool valid = myrow < rows_total;
+    const size_t grow = chunk_row0 + (size_t)myrow;
+
+    u32x4_t qr[8];
+    const uint16_t* qp = q + grow * dk + g * halfk;
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      const u32x4_t z = {0u, 0u, 0u, 0u};
+      qr[s] = (s < NKS && valid) ? *reinterpret_cast<const u32x4_t*>(qp + 8 * s) : z;
+    }
+    f32x16_t acc[4];
+#pragma unroll
+    for (int T = 0; T < 4; ++T) acc[T] = zero16();
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      if (s >= NKS) continue;
+#pragma unroll
+      for (int T = 0; T < 4; ++T) {
+        if (T >= NT) continue;
+        const int off = (32 * T + il) * SROW + g * halfk + 8 * s;
+        const u32x4_t ah = *reinterpret_cast<const u32x4_t*>(Shi + off);
+        const u32x4_t al = *reinterpret_cast<const u32x4_t*>(Slo + off);
+        acc[T] = mfma_bf16(ah, qr[s], acc[T]);
+        acc[T] = mfma_bf16(al, qr[s], acc[T]);
+      }
+    }
+
+    // RMSNorm over the token's d_v outputs: this lane's half plus lane ^ 32's
+    float ss = 0.0f;
+#pragma unroll
+    for (int T = 0; T < 4; ++T)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) ss = fmaf(acc[T][r], acc[T][r], ss);
+    ss += __shfl_xor(ss, 32);
+    const float inv = rsqrtf(ss * inv_dv + eps);
+
+    if (valid) {
+      const uint16_t* gp = gate + grow * dv + g * HALF;
+      uint16_t* op = out + grow * dv + g * HALF;
+      const float* wp = wrms + g * HALF;
+#pragma unroll
+      for (int m = 0; m < 8; ++m) {
+        if (8 * m >= HALF || g * HALF + 8 * m >= dv) continue;
+        const u32x4_t gv = *reinterpret_cast<const u32x4_t*>(gp + 8 * m);
+        const f32x4_t w0 = *reinterpret_cast<const f32x4_t*>(wp + 8 * m);
+        const f32x4_t w1 = *reinterpret_cast<const f32x4_t*>(wp + 8 * m + 4);
+        float y[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int idx = 8 * m + e;
+          const float o = acc[idx >> 4][idx & 15];
+          const float gl = (e & 1) ? bf16_hi(gv[e >> 1]) : bf16_lo(gv[e >> 1]);
+          const float ww = e < 4 ? w0[e] : w1[e - 4];
+          const float sig = 1.0f / (1.0f + __expf(-gl));
+          y[e] = o * inv * ww * sig;
+        }
+        u32x4_t ov;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ov[e] = pack_bf16(y[2 * e], y[2 * e + 1]);
+        *reinterpret_cast<u32x4_t*>(op + 8 * m) = ov;
+      }
+    }
+  }
+}
+
+// fp32 features: 64 token rows per workgroup, S~ and the rows' queries in LDS.
+constexpr int SG = 129;
+constexpr int kRowsF = 64;
+
+__global__ __launch_bounds__(256) void readout_f32_kernel(
+    const float* __restrict__ q, const float* __restrict__ gate, const float* __restrict__ wrms,
+    float* __restrict__ out, const float* __restrict__ ST, int dk, int dv, int F, int U, int C,
+    int radius, int n, float eps) {
+  __shared__ float Ss[128 * SG];
+  __shared__ float Qs[kRowsF * SG];
+  const int blk = blockIdx.x;
+  const int c = blockIdx.y;
+  const int u = blockIdx.z;
+  const int f0 = c * C;
+  const int f1 = min(f0 + C, F);
+  const long rows_total = (long)(f1 - f0) * U;
+  const long row0 = (long)blk * kRowsF;
+  if (row0 >= rows_total) return;
+  const int t = threadIdx.x;
+  const size_t SS = (size_t)dv * dk;
+  const int pi = max(c - radius, 0);
+  const int ri = min(c + radius + 1, n);
+  const float* P = ST + ((size_t)(u * 2 + 0) * (n + 1) + pi) * SS;
+  const float* R = ST + ((size_t)(u * 2 + 1) * (n + 1) + ri) * SS;
+  for (int idx = t; idx < dv * dk; idx += 256) {
+    const int i = idx / dk;
+    const int j = idx - i * dk;
+    Ss[i * SG + j] = P[idx] + R[idx];
+  }
+  const size_t chunk_row0 = ((size_t)u * F + f0) * U;
+  for (int idx = t; idx < kRowsF * dk; idx += 256) {
+    const int i = idx / dk;
+    const int j = idx - i * dk;
+    const long row = row0 + i;
+    Qs[i * SG + j] = row < rows_total ? q[(chunk_row0 + row) * dk + j] : 0.0f;
+  }
+  __syncthreads();
+  const int lr = t >> 2;
+  const int part = t & 3;
+  const long myrow = row0 + lr;
+  float o[32];
+  float ss = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 32; ++j) {
+    const int ch = part + 4 * j;
+    float a = 0.0f;
+    if (ch < dv)
+      for (int kx = 0; kx < dk; ++kx) a = fmaf(Ss[ch * SG + kx], Qs[lr * SG + kx], a);
+    o[j] = a;
+    ss = fmaf(a, a, ss);
+  }
+  ss += __shfl_xor(ss, 1);
+  ss += __shfl_xor(ss, 2);
+  const float inv = 1.0f / sqrtf(ss / (float)dv + eps);
+  if (myrow < rows_total) {
+    const size_t grow = chunk_row0 + (size_t)myrow;
+#pragma unroll
+    for (int j = 0; j < 32; ++j) {
+      const int ch = part + 4 * j;
+      if (ch < dv) {
+        const float gl = gate[grow * dv + ch];
+        out[grow * dv + ch] = wrms[ch] * o[j] * inv / (1.0f + expf(-gl));
+      }
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_readout(const Plan& p, const void* q, const void* gate, const float* rms_weight,
+                          void* out, const WsPtrs& w, hipStream_t s) {
+  const long max_rows = (long)p.C * p.U;
+  if (max_rows == 0) return hipSuccess;
+  if (p.dtype == VDA_DTYPE_BF16) {
+    const dim3 grid((unsigned)((max_rows + kRows - 1) / kRows), p.n, p.units);
+    hipLaunchKernelGGL(readout_bf16_kernel, grid, dim3(kThreads), 0, s,
+                       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(gate),
+                       rms_weight, static_cast<uint16_t*>(out), w.ST, p.dk, p.dv, p.F, p.U, p.C,
+                       p.r, p.n, p.eps);
+  } else {
+    const dim3 grid((unsigned)((max_rows + kRowsF - 1) / kRowsF), p.n, p.units);
+    hipLaunchKernelGGL(readout_f32_kernel, grid, dim3(kThreads), 0, s,
+                       static_cast<const float*>(q), static_cast<const float*>(gate), rms_weight,
+                       static_cast<float*>(out), w.ST, p.dk, p.dv, p.F, p.U, p.C, p.r, p.n,
+                       p.eps);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace vda

@@ -1,0 +1,198 @@
+// Chunk-wise scans of Video Delta Attention ("Video DeltaNet", arXiv
+// 2609.20744, Sec. 5 "Chunk-wise scans", App. A.1 Eq. (A.1), App. A.3).
+//
+// Each frame acts on the state as the affine map S -> (S + B_t) M_t
+// (= S M_t + J_t with J_t = B_t M_t, M_t = (I + A_t)^{-1}).  Attention reads
+// memory only at chunk boundaries, so
+//
+//   compose: per (unit, chunk) and independently of every other chunk,
+//     Mc = M_{f0} M_{f0+1} ... M_{f1-1}                 (forward transition)
+//     Jf = (((B_{f0}) M_{f0} + B_{f0+1}) M_{f0+1} + ...) M_{f1-1}
+//     Jr = (((B_{f1-1}) M_{f1-1} + B_{f1-2}) M_{f1-2} + ...) M_{f0}
+//   The reverse transition is M_{f1-1} ... M_{f0} = Mc^T because every M_t is
+//   symmetric (alpha = 1), so it is not stored.
+//
+//   scan: per (unit, direction, 32-row block of the state) -- the rows of S
+//   evolve independently --
+//     P[0] = seed, P[j+1] = P[j] Mc_j + Jf_j          (forward, chunks 0..n-1)
+//     R[n] = seed, R[j]   = R[j+1] Mc_j^T + Jr_j      (reverse, chunks n-1..0)
+//   Only these n + 1 boundary states per direction are ever written.
+//
+// All products are 32x32x32 fp32 MFMA block products with both operands in
+// LDS.  fp32 throughout ("the inverse and recurrent state updates remain in
+// FP32", Sec. 5).
+#include "vda_device.h"
+#include "vda_internal.h"
+
+namespace vda {
+namespace {
+
+constexpr int SG = 129;
+
+// rows x Dk block of a row-major (ld = dk) fp32 matrix into LDS, zero padded
+// to R32 x Dk; adds `add` (same layout) when given.
+__device__ __forceinline__ void load_rows(float* dst, const float* src, const float* add, int rows,
+                                          int R32, int dk, int Dk) {
+  for (int idx = threadIdx.x; idx < R32 * Dk; idx += 256) {
+    const int i = idx / Dk;
+    const int j = idx - i * Dk;
+    float x = 0.0f;
+    if (i < rows && j < dk) {
+      x = src[(size_t)i * dk + j];
+      if (add) x += add[(size_t)i * dk + j];
+    }
+    dst[i * SG + j] = x;
+  }
+}
+
+__global__ __launch_bounds__(256, 1) void compose_kernel(const float* __restrict__ Bw,
+                                                        const float* __restrict__ Mw,
+                                                        float* __restrict__ Mc,
+                                                        float* __restrict__ Jf,
+                                                        float* __restrict__ Jr, int dk, int dv,
+                                                        int F, int C, int n) {
+  __shared__ float Xs[128 * SG];
+  __shared__ float Ms[128 * SG];
+  const int c = blockIdx.x;
+  const int u = blockIdx.y;
+  const int chain = blockIdx.z;  // 0: Mc, 1: Jf, 2: Jr
+  const int t = threadIdx.x;
+  const int lane = t & 63;
+  const int w = t >> 6;
+  const int f0 = c * C;
+  const int f1 = min(f0 + C, F);
+  const int nf = f1 - f0;
+  const int rows = chain == 0 ? dk : dv;
+  const int R32 = pad32(rows);
+  const int nR = R32 >> 5;
+  const int Dk = pad32(dk);
+  const int nb = Dk >> 5;
+  const size_t Fp1 = (size_t)F + 1;
+  // workspace frame index f + 1 holds latent frame f (index 0 is the text frame)
+  auto frame = [&](int s) { return chain == 2 ? f1 - 1 - s : f0 + s; };
+  auto Mp = [&](int f) { return Mw + ((size_t)u * Fp1 + f + 1) * dk * dk; };
+  auto Bp = [&](int f) { return Bw + ((size_t)u * Fp1 + f + 1) * dv * dk; };
+
+  if (chain == 0) {
+    for (int idx = t; idx < R32 * Dk; idx += 256) {
+      const int i = idx / Dk;
+      const int j = idx - i * Dk;
+      Xs[i * SG + j] = (i == j) ? 1.0f : 0.0f;
+    }
+  } else {
+    load_rows(Xs, Bp(frame(0)), nullptr, dv, R32, dk, Dk);
+  }
+  load_rows(Ms, Mp(frame(0)), nullptr, dk, Dk, dk, Dk);
+  __syncthreads();
+
+  float* dst = chain == 0 ? Mc + ((size_t)u * n + c) * dk * dk
+                          : (chain == 1 ? Jf : Jr) + ((size_t)u * n + c) * dv * dk;
+  for (int s = 0; s < nf; ++s) {
+    f32x16_t acc[4];
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) acc[ct] = zero16();
+    if (w < nR) {
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct) {
+        if (ct >= nb) continue;
+        for (int kb = 0; kb < nb; ++kb)
+          acc[ct] = blk_mm32<false, false>(acc[ct], Xs + 32 * w * SG + 32 * kb, SG,
+                                           Ms + 32 * kb * SG + 32 * ct, SG);
+      }
+    }
+    __syncthreads();
+    const bool last = s == nf - 1;
+    const float* addB = (!last && chain != 0) ? Bp(frame(s + 1)) : nullptr;
+    if (w < nR) {
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct) {
+        if (ct >= nb) continue;
+        const int col = 32 * ct + (lane & 31);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = 32 * w + acc_row(r, lane);
+          float x = acc[ct][r];
+          if (last) {
+            if (row < rows && col < dk) dst[(size_t)row * dk + col] = x;
+          } else {
+            if (addB && row < rows && col < dk) x += addB[(size_t)row * dk + col];
+            Xs[row * SG + col] = x;
+          }
+        }
+      }
+    }
+    if (last) break;
+    load_rows(Ms, Mp(frame(s + 1)), nullptr, dk, Dk, dk, Dk);
+    __syncthreads();
+  }
+}
+
+__global__ __launch_bounds__(256) void scan_kernel(const float* __restrict__ Mc,
+                                                   const float* __restrict__ Jf,
+                                                   const float* __restrict__ Jr,
+                                                   float* __restrict__ ST, int dk, int dv, int n) {
+  __shared__ float Xs[32 * SG];
+  __shared__ float Ms[128 * SG];
+  const int rb = blockIdx.x;  // rows [32 rb, 32 rb + 32) of the state
+  const int u = blockIdx.y;
+  const int dir = blockIdx.z;  // 0: forward (P), 1: reverse (R)
+  const int t = threadIdx.x;
+  const int lane = t & 63;
+  const int w = t >> 6;
+  const int Dk = pad32(dk);
+  const int nb = Dk >> 5;
+  const size_t SS = (size_t)dv * dk;
+  float* S = ST + (size_t)(u * 2 + dir) * (n + 1) * SS;
+  const int r0 = 32 * rb;
+  const int nrows = min(32, dv - r0);
+
+  load_rows(Xs, S + (size_t)(dir == 0 ? 0 : n) * SS + (size_t)r0 * dk, nullptr, nrows, 32, dk, Dk);
+  for (int s = 0; s < n; ++s) {
+    const int j = dir == 0 ? s : n - 1 - s;
+    load_rows(Ms, Mc + ((size_t)u * n + j) * dk * dk, nullptr, dk, Dk, dk, Dk);
+    __syncthreads();
+    f32x16_t acc = zero16();
+    if (w < nb) {
+      for (int kb = 0; kb < nb; ++kb) {
+        if (dir == 0)
+          acc = blk_mm32<false, false>(acc, Xs + 32 * kb, SG, Ms + 32 * kb * SG + 32 * w, SG);
+        else
+          acc = blk_mm32<false, true>(acc, Xs + 32 * kb, SG, Ms + 32 * w * SG + 32 * kb, SG);
+      }
+    }
+    __syncthreads();
+    if (w < nb) {
+      const float* J = (dir == 0 ? Jf : Jr) + ((size_t)u * n + j) * SS;
+      float* dst = S + (size_t)(dir == 0 ? j + 1 : j) * SS;
+      const int col = 32 * w + (lane & 31);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = acc_row(r, lane);
+        float x = 0.0f;
+        if (row < nrows && col < dk) {
+          x = acc[r] + J[(size_t)(r0 + row) * dk + col];
+          dst[(size_t)(r0 + row) * dk + col] = x;
+        }
+        Xs[row * SG + col] = x;
+      }
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_compose(const Plan& p, const WsPtrs& w, hipStream_t s) {
+  const dim3 grid(p.n, p.units, 3);
+  hipLaunchKernelGGL(compose_kernel, grid, dim3(kThreads), 0, s, w.B, w.M, w.Mc, w.Jf, w.Jr, p.dk,
+                     p.dv, p.F, p.C, p.n);
+  return hipGetLastError();
+}
+
+hipError_t launch_scan(const Plan& p, const WsPtrs& w, hipStream_t s) {
+  const dim3 grid(pad32(p.dv) >> 5, p.units, 2);
+  hipLaunchKernelGGL(scan_kernel, grid, dim3(kThreads), 0, s, w.Mc, w.Jf, w.Jr, w.ST, p.dk, p.dv,
+                     p.n);
+  return hipGetLastError();
+}
+
+}  // namespace vda

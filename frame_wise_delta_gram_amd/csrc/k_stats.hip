@@ -1,0 +1,322 @@
+// Frame statistics of Video Delta Attention ("Video DeltaNet", arXiv 2609.20744,
+// Sec. 3.1 Eq. (3b)):
+//   A_t = K_t^T Diag(beta_t) K_t,   B_t = V_t^T Diag(beta_t) K_t
+// for every (unit, frame), with the text tokens as a leading virtual frame
+// (Sec. 5, "Chunk-wise scans").  Both statistics come from ONE contraction
+// over the frame's tokens,
+//   [A_t ; B_t] = [K_t | V_t]^T (Diag(beta_t) K_t),
+// so every K/V byte is read from HBM once ("in one pass, sharing input reads
+// and reduction work", Sec. 5).
+//
+// bf16 path: one workgroup (4 waves) per (unit, frame).  Tokens stream in
+// tiles of 64.  Each thread loads a 4-token x 8-channel block of K and of V
+// (16-byte coalesced loads: one wave instruction covers four whole 256-byte
+// rows), transposes it in registers to channel-major order, forms beta*K in
+// fp32 and rounds it to bf16, and writes the three channel-major tiles to LDS
+// with an XOR swizzle that keeps both the 8-byte staging writes and the
+// 16-byte MFMA operand reads free of bank conflicts.  The contraction runs on
+// v_mfma_f32_32x32x16_bf16 with fp32 accumulators held for the whole frame;
+// the next tile's global loads are in flight while the current one is
+// multiplied (two LDS stages).
+//
+// fp32 path: the same contraction in fp32 on the vector ALUs (exact fp32
+// products, fp32 accumulation) for fp32 features.
+#include "vda_device.h"
+#include "vda_internal.h"
+
+namespace vda {
+namespace {
+
+constexpr int kTok = 64;                  // tokens per tile
+constexpr int kRowBytes = kTok * 2;       // one LDS row: 64 bf16 tokens of one channel
+constexpr int kXRows = 256;               // K channels in rows [0,128), V channels in [128,256)
+constexpr int kBRows = 128;               // beta-scaled K channels
+constexpr int kStageBytes = (kXRows + kBRows) * kRowBytes;  // 48 KiB
+
+// Swizzle of a channel row: XOR applied to the 16-byte chunk index.  Rows r..r+7
+// (r a multiple of 8) get 8 distinct values (MFMA reads), and rows 8c+x for 8
+// consecutive c get 8 distinct values (staging writes).
+__device__ __forceinline__ uint32_t swz(uint32_t row) { return (row & 7) ^ ((row >> 3) & 7); }
+// byte offset of the 8-byte slot `slot` (tokens 4*slot..4*slot+3) of `row`
+__device__ __forceinline__ uint32_t off8(uint32_t row, uint32_t slot) {
+  return row * kRowBytes + ((slot ^ (swz(row) << 1)) << 3);
+}
+// byte offset of the 16-byte chunk `j` (tokens 8*j..8*j+7) of `row`
+__device__ __forceinline__ uint32_t off16(uint32_t row, uint32_t j) {
+  return row * kRowBytes + ((j ^ swz(row)) << 4);
+}
+
+__global__ __launch_bounds__(256, 1) void stats_bf16_kernel(
+    const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, const float* __restrict__ beta,
+    const uint16_t* __restrict__ tk, const uint16_t* __restrict__ tv,
+    const float* __restrict__ tb, float* __restrict__ Aout, float* __restrict__ Bout, int F, int U,
+    int T, int dk, int dv, float text_scale) {
+  __shared__ __align__(16) unsigned char smem[2 * kStageBytes];
+
+  const int fi = blockIdx.x;  // 0 = text frame, f + 1 = latent frame f
+  const int u = blockIdx.y;
+  const int t = threadIdx.x;
+  const int lane = t & 63;
+  const int w = t >> 6;
+
+  const uint16_t* sk;
+  const uint16_t* sv;
+  const float* sb;
+  int ntok;
+  float bscale;
+  if (fi == 0) {
+    sk = tk + (size_t)u * T * dk;
+    sv = tv + (size_t)u * T * dv;
+    sb = tb + (size_t)u * T;
+    ntok = T;
+    bscale = text_scale;
+  } else {
+    const size_t fr = (size_t)u * F + (fi - 1);
+    sk = k + fr * U * dk;
+    sv = v + fr * U * dv;
+    sb = beta + fr * U;
+    ntok = U;
+    bscale = 1.0f;
+  }
+
+  // staging role: token group tg (4 tokens) x channel group cg (8 channels)
+  const int tg = (t & 1) | ((t >> 5) << 1);
+  const int cg = (t >> 1) & 15;
+  const bool kact = cg * 8 < dk;
+  const bool vact = cg * 8 < dv;
+
+  u32x4_t kr[4], vr[4];
+  float bb[4];
+
+  auto load = [&](int tile) {
+    const int base = tile * kTok + 4 * tg;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const int tok = base + s;
+      const bool ok = tok < ntok;
+      const u32x4_t z = {0u, 0u, 0u, 0u};
+      kr[s] = (ok && kact) ? *reinterpret_cast<const u32x4_t*>(sk + (size_t)tok * dk + 8 * cg) : z;
+      vr[s] = (ok && vact) ? *reinterpret_cast<const u32x4_t*>(sv + (size_t)tok * dv + 8 * cg) : z;
+      bb[s] = ok ? sb[tok] * bscale : 0.0f;
+    }
+  };
+
+  auto write = [&](int stage) {
+    unsigned char* X = smem + stage * kStageBytes;
+    unsigned char* BK = X + kXRows * kRowBytes;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      const int p = c >> 1;
+      const bool hi = (c & 1) != 0;
+      if (kact) {
+        const uint32_t a0 = kr[0][p], a1 = kr[1][p], a2 = kr[2][p], a3 = kr[3][p];
+        u32x2_t d;
+        d[0] = hi ? ((a0 >> 16) | (a1 & 0xffff0000u)) : ((a0 & 0xffffu) | (a1 << 16));
+        d[1] = hi ? ((a2 >> 16) | (a3 & 0xffff0000u)) : ((a2 & 0xffffu) | (a3 << 16));
+        *reinterpret_cast<u32x2_t*>(X + off8(8 * cg + c, tg)) = d;
+        const float x0 = hi ? bf16_hi(a0) : bf16_lo(a0);
+        const float x1 = hi ? bf16_hi(a1) : bf16_lo(a1);
+        const float x2 = hi ? bf16_hi(a2) : bf16_lo(a2);
+        const float x3 = hi ? bf16_hi(a3) : bf16_lo(a3);
+        u32x2_t e;
+        e[0] = pack_bf16(x0 * bb[0], x1 * bb[1]);
+        e[1] = pack_bf16(x2 * bb[2], x3 * bb[3]);
+        *reinterpret_cast<u32x2_t*>(BK + off8(8 * cg + c, tg)) = e;
+      }
+      if (vact) {
+        const uint32_t a0 = vr[0][p], a1 = vr[1][p], a2 = vr[2][p], a3 = vr[3][p];
+        u32x2_t d;
+        d[0] = hi ? ((a0 >> 16) | (a1 & 0xffff0000u)) : ((a0 & 0xffffu) | (a1 << 16));
+        d[1] = hi ? ((a2 >> 16) | (a3 & 0xffff0000u)) : ((a2 & 0xffffu) | (a3 << 16));
+        *reinterpret_cast<u32x2_t*>(X + off8(128 + 8 * cg + c, tg)) = d;
+      }
+    }
+  };
+
+  // contraction role: this wave owns output row tiles w and w + 4 of [A; B]
+  const int nK = pad32(dk) >> 5;
+  const int nV = pad32(dv) >> 5;
+  const int nR = nK + nV;
+  bool ract[2];
+  int rbase[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int rt = w + 4 * i;
+    ract[i] = rt < nR;
+    rbase[i] = rt < nK ? 32 * rt : 128 + 32 * (rt - nK);
+  }
+  f32x16_t acc[2][4];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) acc[i][ct] = zero16();
+
+  auto compute = [&](int stage) {
+    const unsigned char* X = smem + stage * kStageBytes;
+    const unsigned char* BK = X + kXRows * kRowBytes;
+    const int il = lane & 31;
+    const int kh = lane >> 5;
+#pragma unroll
+    for (int kk = 0; kk < kTok / 16; ++kk) {
+      const int j = 2 * kk + kh;  // tokens 16 kk + 8 kh .. + 7
+      u32x4_t b[4];
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct)
+        if (ct < nK) b[ct] = *reinterpret_cast<const u32x4_t*>(BK + off16(32 * ct + il, j));
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        if (!ract[i]) continue;
+        const u32x4_t a = *reinterpret_cast<const u32x4_t*>(X + off16(rbase[i] + il, j));
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct)
+          if (ct < nK) acc[i][ct] = mfma_bf16(a, b[ct], acc[i][ct]);
+      }
+    }
+  };
+
+  const int ntiles = (ntok + kTok - 1) / kTok;
+  if (ntiles > 0) {
+    load(0);
+    write(0);
+  }
+  for (int it = 0; it < ntiles; ++it) {
+    if (it + 1 < ntiles) load(it + 1);
+    __syncthreads();
+    compute(it & 1);
+    if (it + 1 < ntiles) write((it + 1) & 1);
+  }
+
+  // results: rows of A (K tiles) or B (V tiles), columns are key channels
+  const size_t fr = (size_t)u * (F + 1) + fi;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    if (!ract[i]) continue;
+    const int rt = w + 4 * i;
+    const bool isA = rt < nK;
+    const int ch0 = isA ? 32 * rt : 32 * (rt - nK);
+    const int nrows = isA ? dk : dv;
+    float* dst = isA ? Aout + fr * dk * dk : Bout + fr * dv * dk;
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) {
+      if (ct >= nK) continue;
+      const int col = 32 * ct + (lane & 31);
+      if (col >= dk) continue;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = ch0 + acc_row(r, lane);
+        if (row < nrows) dst[(size_t)row * dk + col] = acc[i][ct][r];
+      }
+    }
+  }
+}
+
+// fp32 features: the same contraction on the vector ALUs.
+constexpr int kTokF = 32;
+constexpr int kXS = 257;  // LDS row stride (floats) of the token tile [K | V]
+constexpr int kBS = 129;
+
+__global__ __launch_bounds__(256) void stats_f32_kernel(
+    const float* __restrict__ k, const float* __restrict__ v, const float* __restrict__ beta,
+    const float* __restrict__ tk, const float* __restrict__ tv, const float* __restrict__ tb,
+    float* __restrict__ Aout, float* __restrict__ Bout, int F, int U, int T, int dk, int dv,
+    float text_scale) {
+  __shared__ float Xs[kTokF * kXS];
+  __shared__ float Bs[kTokF * kBS];
+
+  const int fi = blockIdx.x;
+  const int u = blockIdx.y;
+  const int t = threadIdx.x;
+  const float* sk;
+  const float* sv;
+  const float* sb;
+  int ntok;
+  float bscale;
+  if (fi == 0) {
+    sk = tk + (size_t)u * T * dk;
+    sv = tv + (size_t)u * T * dv;
+    sb = tb + (size_t)u * T;
+    ntok = T;
+    bscale = text_scale;
+  } else {
+    const size_t fr = (size_t)u * F + (fi - 1);
+    sk = k + fr * U * dk;
+    sv = v + fr * U * dv;
+    sb = beta + fr * U;
+    ntok = U;
+    bscale = 1.0f;
+  }
+  // thread t accumulates rows 16*(t/16) .. +15 of [K | V] channels x key columns 8*(t%16) .. +7
+  const int rb = t >> 4;
+  const int cb = t & 15;
+  float acc[16][8];
+#pragma unroll
+  for (int i = 0; i < 16; ++i)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[i][j] = 0.0f;
+
+  for (int base = 0; base < ntok; base += kTokF) {
+    for (int idx = t; idx < kTokF * 128; idx += 256) {
+      const int s = idx >> 7;
+      const int ch = idx & 127;
+      const int tok = base + s;
+      const bool ok = tok < ntok;
+      const float kv = (ok && ch < dk) ? sk[(size_t)tok * dk + ch] : 0.0f;
+      const float vv = (ok && ch < dv) ? sv[(size_t)tok * dv + ch] : 0.0f;
+      const float bv = ok ? sb[tok] * bscale : 0.0f;
+      Xs[s * kXS + ch] = kv;
+      Xs[s * kXS + 128 + ch] = vv;
+      Bs[s * kBS + ch] = kv * bv;
+    }
+    __syncthreads();
+    for (int s = 0; s < kTokF; ++s) {
+      float xv[16], bv[8];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) xv[i] = Xs[s * kXS + 16 * rb + i];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) bv[j] = Bs[s * kBS + 8 * cb + j];
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[i][j] = fmaf(xv[i], bv[j], acc[i][j]);
+    }
+    __syncthreads();
+  }
+  const size_t fr = (size_t)u * (F + 1) + fi;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int row = 16 * rb + i;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int col = 8 * cb + j;
+      if (col >= dk) continue;
+      if (row < 128) {
+        if (row < dk) Aout[fr * dk * dk + (size_t)row * dk + col] = acc[i][j];
+      } else if (row - 128 < dv) {
+        Bout[fr * dv * dk + (size_t)(row - 128) * dk + col] = acc[i][j];
+      }
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_stats(const Plan& p, const void* k, const void* v, const float* beta,
+                        const void* text_k, const void* text_v, const float* text_beta,
+                        const WsPtrs& w, hipStream_t s) {
+  const dim3 grid(p.F + 1, p.units);
+  const float ts = p.seed_mode == 1 ? 0.5f : 1.0f;
+  if (p.dtype == VDA_DTYPE_BF16) {
+    hipLaunchKernelGGL(stats_bf16_kernel, grid, dim3(kThreads), 0, s,
+                       static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), beta,
+                       static_cast<const uint16_t*>(text_k), static_cast<const uint16_t*>(text_v),
+                       text_beta, w.A, w.B, p.F, p.U, p.T, p.dk, p.dv, ts);
+  } else {
+    hipLaunchKernelGGL(stats_f32_kernel, grid, dim3(kThreads), 0, s,
+                       static_cast<const float*>(k), static_cast<const float*>(v), beta,
+                       static_cast<const float*>(text_k), static_cast<const float*>(text_v),
+                       text_beta, w.A, w.B, p.F, p.U, p.T, p.dk, p.dv, ts);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace vda

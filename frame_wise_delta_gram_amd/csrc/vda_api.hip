@@ -1,0 +1,300 @@
+// C ABI of the VDA forward library: argument checks, workspace carve-up and
+// the five-launch sequence on the caller's stream.  See include/vda.h for the
+// contract of every entry point.
+#include <math.h>
+#include <stdint.h>
+
+#include "vda_internal.h"
+
+namespace vda {
+namespace {
+
+constexpr int64_t kMaxGridYZ = 65535;
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+bool mul_ok(int64_t a, int64_t b, int64_t* out) {
+  if (a < 0 || b < 0) return false;
+  if (a != 0 && b > INT64_MAX / a) return false;
+  *out = a * b;
+  return true;
+}
+
+int make_plan(const vda_desc_t* d, Plan* p) {
+  if (!d) return VDA_ERR_INVALID_ARG;
+  if (d->in_dtype != VDA_DTYPE_F32 && d->in_dtype != VDA_DTYPE_BF16) return VDA_ERR_BAD_DTYPE;
+  if (d->out_dtype != d->in_dtype) return VDA_ERR_BAD_DTYPE;
+  if (d->units < 0 || d->frames < 0 || d->tokens < 0 || d->text_tokens < 0)
+    return VDA_ERR_INVALID_ARG;
+  if (d->d_k < 16 || d->d_k > 128 || d->d_k % 16) return VDA_ERR_INVALID_ARG;
+  if (d->d_v < 16 || d->d_v > 128 || d->d_v % 16) return VDA_ERR_INVALID_ARG;
+  if (d->chunk < 1 || d->radius < 0) return VDA_ERR_INVALID_ARG;
+  if (!(d->rms_eps >= 0.0f) || !isfinite(d->rms_eps)) return VDA_ERR_INVALID_ARG;
+  if (d->seed_mode != 0 && d->seed_mode != 1) return VDA_ERR_INVALID_ARG;
+  if (d->units > kMaxGridYZ) return VDA_ERR_INVALID_ARG;
+  const int64_t n = d->frames > 0 ? (d->frames + (int64_t)d->chunk - 1) / d->chunk : 0;
+  if (n > kMaxGridYZ) return VDA_ERR_INVALID_ARG;
+  // every element count must fit in int64 (and the kernels' size_t arithmetic)
+  int64_t rows, elems, x;
+  if (!mul_ok(d->units, d->frames, &rows) || !mul_ok(rows, d->tokens, &rows)) return VDA_ERR_INVALID_ARG;
+  if (!mul_ok(rows, 128, &elems)) return VDA_ERR_INVALID_ARG;
+  if (!mul_ok((int64_t)d->chunk, d->tokens, &x)) return VDA_ERR_INVALID_ARG;
+  if (!mul_ok(d->units, d->text_tokens, &x) || !mul_ok(x, 128, &x)) return VDA_ERR_INVALID_ARG;
+
+  p->units = d->units;
+  p->F = d->frames;
+  p->U = d->tokens;
+  p->T = d->text_tokens;
+  p->dk = d->d_k;
+  p->dv = d->d_v;
+  p->C = d->chunk;
+  p->r = d->radius;
+  p->n = (int)n;
+  p->eps = d->rms_eps;
+  p->seed_mode = d->seed_mode;
+  p->dtype = d->in_dtype;
+
+  const size_t U_ = (size_t)p->units, Fp1 = (size_t)p->F + 1, N = (size_t)p->n;
+  const size_t kk = (size_t)p->dk * p->dk * 4, vk = (size_t)p->dv * p->dk * 4;
+  size_t sz[7];
+  sz[0] = U_ * Fp1 * kk;          // A
+  sz[1] = U_ * Fp1 * vk;          // B
+  sz[2] = U_ * Fp1 * kk;          // M
+  sz[3] = U_ * N * kk;            // Mc
+  sz[4] = U_ * N * vk;            // Jf
+  sz[5] = U_ * N * vk;            // Jr
+  sz[6] = U_ * 2 * (N + 1) * vk;  // ST
+  if (p->units == 0 || p->F == 0)
+    for (size_t& s : sz) s = 0;
+  size_t off = 0;
+  for (int i = 0; i < 7; ++i) {
+    p->off[i] = off;
+    off += align256(sz[i]);
+  }
+  p->total = off;
+  return VDA_OK;
+}
+
+WsPtrs carve(const Plan& p, void* ws) {
+  char* b = static_cast<char*>(ws);
+  WsPtrs w;
+  w.A = reinterpret_cast<float*>(b + p.off[0]);
+  w.B = reinterpret_cast<float*>(b + p.off[1]);
+  w.M = reinterpret_cast<float*>(b + p.off[2]);
+  w.Mc = reinterpret_cast<float*>(b + p.off[3]);
+  w.Jf = reinterpret_cast<float*>(b + p.off[4]);
+  w.Jr = reinterpret_cast<float*>(b + p.off[5]);
+  w.ST = reinterpret_cast<float*>(b + p.off[6]);
+  return w;
+}
+
+bool aligned(const void* ptr, size_t a) { return (reinterpret_cast<uintptr_t>(ptr) % a) == 0; }
+
+// Checks shared by every entry point that runs the state pipeline.
+int check_state_inputs(const Plan& p, const void* k, const void* v, const float* beta,
+                       const void* tk, const void* tv, const float* tb, const void* ws,
+                       size_t ws_bytes) {
+  const bool video = (size_t)p.units * p.F * p.U > 0;
+  const bool text = (size_t)p.units * p.T > 0 && p.F > 0;
+  if (video && (!k || !v || !beta)) return VDA_ERR_INVALID_ARG;
+  if (text && (!tk || !tv || !tb)) return VDA_ERR_INVALID_ARG;
+  if (p.total > 0 && !ws) return VDA_ERR_INVALID_ARG;
+  if (ws_bytes < p.total) return VDA_ERR_WORKSPACE_TOO_SMALL;
+  if (video && (!aligned(k, 16) || !aligned(v, 16) || !aligned(beta, 4))) return VDA_ERR_MISALIGNED;
+  if (text && (!aligned(tk, 16) || !aligned(tv, 16) || !aligned(tb, 4))) return VDA_ERR_MISALIGNED;
+  if (ws && !aligned(ws, 256)) return VDA_ERR_MISALIGNED;
+  return VDA_OK;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? VDA_OK : VDA_ERR_HIP; }
+
+// stages: 1 stats, 2 solve, 3 compose, 4 scan.  events (optional): recorded
+// before each launched stage.
+int run_states(const Plan& p, const void* k, const void* v, const float* beta, const void* tk,
+               const void* tv, const float* tb, const WsPtrs& w, hipStream_t s, int upto,
+               hipEvent_t const* ev = nullptr) {
+  auto rec = [&](int i) { return ev ? hipEventRecord(ev[i], s) : hipSuccess; };
+  if (p.units == 0 || p.F == 0) {  // nothing to launch; keep the event sequence complete
+    for (int i = 0; i < upto; ++i)
+      if (rec(i) != hipSuccess) return VDA_ERR_HIP;
+    return VDA_OK;
+  }
+  if (upto >= 1 && (rec(0) != hipSuccess || launch_stats(p, k, v, beta, tk, tv, tb, w, s) != hipSuccess))
+    return VDA_ERR_HIP;
+  if (upto >= 2 && (rec(1) != hipSuccess || launch_solve(p, w, s) != hipSuccess)) return VDA_ERR_HIP;
+  if (upto >= 3 && (rec(2) != hipSuccess || launch_compose(p, w, s) != hipSuccess))
+    return VDA_ERR_HIP;
+  if (upto >= 4 && (rec(3) != hipSuccess || launch_scan(p, w, s) != hipSuccess)) return VDA_ERR_HIP;
+  return VDA_OK;
+}
+
+int forward_impl(const vda_desc_t* desc, const void* q, const void* k, const void* v,
+                 const float* beta, const void* gate, const void* text_k, const void* text_v,
+                 const float* text_beta, const float* rms_weight, void* out, void* workspace,
+                 size_t workspace_bytes, vda_stream_t stream, hipEvent_t const* ev) {
+  Plan p;
+  int st = make_plan(desc, &p);
+  if (st != VDA_OK) return st;
+  st = check_state_inputs(p, k, v, beta, text_k, text_v, text_beta, workspace, workspace_bytes);
+  if (st != VDA_OK) return st;
+  const bool video = (size_t)p.units * p.F * p.U > 0;
+  if (video && (!q || !gate || !out || !rms_weight)) return VDA_ERR_INVALID_ARG;
+  if (video && (!aligned(q, 16) || !aligned(gate, 16) || !aligned(out, 16) ||
+                !aligned(rms_weight, 16)))
+    return VDA_ERR_MISALIGNED;
+  const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const WsPtrs w = carve(p, workspace);
+  st = run_states(p, k, v, beta, text_k, text_v, text_beta, w, s, 4, ev);
+  if (st != VDA_OK) return st;
+  if (ev && hipEventRecord(ev[4], s) != hipSuccess) return VDA_ERR_HIP;
+  if (video && launch_readout(p, q, gate, rms_weight, out, w, s) != hipSuccess) return VDA_ERR_HIP;
+  if (ev && hipEventRecord(ev[5], s) != hipSuccess) return VDA_ERR_HIP;
+  return VDA_OK;
+}
+
+}  // namespace
+}  // namespace vda
+
+using vda::Plan;
+using vda::WsPtrs;
+
+extern "C" {
+
+size_t vda_workspace_bytes(const vda_desc_t* desc) {
+  Plan p;
+  if (vda::make_plan(desc, &p) != VDA_OK) return 0;
+  return p.total;
+}
+
+int vda_check_desc(const vda_desc_t* desc) {
+  Plan p;
+  return vda::make_plan(desc, &p);
+}
+
+int vda_forward(const vda_desc_t* desc, const void* q, const void* k, const void* v,
+                const float* beta, const void* gate, const void* text_k, const void* text_v,
+                const float* text_beta, const float* rms_weight, void* out, void* workspace,
+                size_t workspace_bytes, vda_stream_t stream) {
+  return vda::forward_impl(desc, q, k, v, beta, gate, text_k, text_v, text_beta, rms_weight, out,
+                           workspace, workspace_bytes, stream, nullptr);
+}
+
+int vda_forward_timed(const vda_desc_t* desc, const void* q, const void* k, const void* v,
+                      const float* beta, const void* gate, const void* text_k, const void* text_v,
+                      const float* text_beta, const float* rms_weight, void* out, void* workspace,
+                      size_t workspace_bytes, vda_stream_t stream, void* const* stage_events,
+                      int n_events) {
+  if (!stage_events || n_events != 6) return VDA_ERR_INVALID_ARG;
+  for (int i = 0; i < 6; ++i)
+    if (!stage_events[i]) return VDA_ERR_INVALID_ARG;
+  return vda::forward_impl(desc, q, k, v, beta, gate, text_k, text_v, text_beta, rms_weight, out,
+                           workspace, workspace_bytes, stream,
+                           reinterpret_cast<hipEvent_t const*>(stage_events));
+}
+
+int vda_debug_stats(const vda_desc_t* desc, const void* k, const void* v, const float* beta,
+                    const void* text_k, const void* text_v, const float* text_beta, float* A_out,
+                    float* B_out, void* workspace, size_t workspace_bytes, vda_stream_t stream) {
+  Plan p;
+  int st = vda::make_plan(desc, &p);
+  if (st != VDA_OK) return st;
+  st = vda::check_state_inputs(p, k, v, beta, text_k, text_v, text_beta, workspace,
+                               workspace_bytes);
+  if (st != VDA_OK) return st;
+  if (p.units == 0 || p.F == 0) return VDA_OK;
+  if (!A_out || !B_out) return VDA_ERR_INVALID_ARG;
+  const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const WsPtrs w = vda::carve(p, workspace);
+  st = vda::run_states(p, k, v, beta, text_k, text_v, text_beta, w, s, 1);
+  if (st != VDA_OK) return st;
+  const size_t fr = (size_t)p.units * (p.F + 1);
+  if (hipMemcpyAsync(A_out, w.A, fr * p.dk * p.dk * 4, hipMemcpyDeviceToDevice, s) != hipSuccess)
+    return VDA_ERR_HIP;
+  return vda::hip_status(
+      hipMemcpyAsync(B_out, w.B, fr * p.dv * p.dk * 4, hipMemcpyDeviceToDevice, s));
+}
+
+int vda_debug_solve(const vda_desc_t* desc, const void* k, const void* v, const float* beta,
+                    const void* text_k, const void* text_v, const float* text_beta, float* M_out,
+                    float* seed_out, void* workspace, size_t workspace_bytes, vda_stream_t stream) {
+  Plan p;
+  int st = vda::make_plan(desc, &p);
+  if (st != VDA_OK) return st;
+  st = vda::check_state_inputs(p, k, v, beta, text_k, text_v, text_beta, workspace,
+                               workspace_bytes);
+  if (st != VDA_OK) return st;
+  if (p.units == 0 || p.F == 0) return VDA_OK;
+  if (!M_out || !seed_out) return VDA_ERR_INVALID_ARG;
+  const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const WsPtrs w = vda::carve(p, workspace);
+  st = vda::run_states(p, k, v, beta, text_k, text_v, text_beta, w, s, 2);
+  if (st != VDA_OK) return st;
+  const size_t fr = (size_t)p.units * (p.F + 1);
+  if (hipMemcpyAsync(M_out, w.M, fr * p.dk * p.dk * 4, hipMemcpyDeviceToDevice, s) != hipSuccess)
+    return VDA_ERR_HIP;
+  const size_t SSb = (size_t)p.dv * p.dk * 4;
+  return vda::hip_status(hipMemcpy2DAsync(seed_out, SSb, w.ST, 2 * (p.n + 1) * SSb, SSb, p.units,
+                                          hipMemcpyDeviceToDevice, s));
+}
+
+int vda_debug_chunks(const vda_desc_t* desc, const void* k, const void* v, const float* beta,
+                     const void* text_k, const void* text_v, const float* text_beta, float* Mc_out,
+                     float* Jf_out, float* Jr_out, void* workspace, size_t workspace_bytes,
+                     vda_stream_t stream) {
+  Plan p;
+  int st = vda::make_plan(desc, &p);
+  if (st != VDA_OK) return st;
+  st = vda::check_state_inputs(p, k, v, beta, text_k, text_v, text_beta, workspace,
+                               workspace_bytes);
+  if (st != VDA_OK) return st;
+  if (p.units == 0 || p.F == 0) return VDA_OK;
+  if (!Mc_out || !Jf_out || !Jr_out) return VDA_ERR_INVALID_ARG;
+  const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const WsPtrs w = vda::carve(p, workspace);
+  st = vda::run_states(p, k, v, beta, text_k, text_v, text_beta, w, s, 3);
+  if (st != VDA_OK) return st;
+  const size_t nc = (size_t)p.units * p.n;
+  if (hipMemcpyAsync(Mc_out, w.Mc, nc * p.dk * p.dk * 4, hipMemcpyDeviceToDevice, s) != hipSuccess)
+    return VDA_ERR_HIP;
+  if (hipMemcpyAsync(Jf_out, w.Jf, nc * p.dv * p.dk * 4, hipMemcpyDeviceToDevice, s) != hipSuccess)
+    return VDA_ERR_HIP;
+  return vda::hip_status(
+      hipMemcpyAsync(Jr_out, w.Jr, nc * p.dv * p.dk * 4, hipMemcpyDeviceToDevice, s));
+}
+
+int vda_debug_states(const vda_desc_t* desc, const void* k, const void* v, const float* beta,
+                     const void* text_k, const void* text_v, const float* text_beta, float* P_out,
+                     float* R_out, void* workspace, size_t workspace_bytes, vda_stream_t stream) {
+  Plan p;
+  int st = vda::make_plan(desc, &p);
+  if (st != VDA_OK) return st;
+  st = vda::check_state_inputs(p, k, v, beta, text_k, text_v, text_beta, workspace,
+                               workspace_bytes);
+  if (st != VDA_OK) return st;
+  if (p.units == 0 || p.F == 0) return VDA_OK;
+  if (!P_out || !R_out) return VDA_ERR_INVALID_ARG;
+  const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const WsPtrs w = vda::carve(p, workspace);
+  st = vda::run_states(p, k, v, beta, text_k, text_v, text_beta, w, s, 4);
+  if (st != VDA_OK) return st;
+  const size_t dirb = (size_t)(p.n + 1) * p.dv * p.dk * 4;
+  if (hipMemcpy2DAsync(P_out, dirb, w.ST, 2 * dirb, dirb, p.units, hipMemcpyDeviceToDevice, s) !=
+      hipSuccess)
+    return VDA_ERR_HIP;
+  return vda::hip_status(hipMemcpy2DAsync(R_out, dirb, reinterpret_cast<char*>(w.ST) + dirb,
+                                          2 * dirb, dirb, p.units, hipMemcpyDeviceToDevice, s));
+}
+
+const char* vda_status_string(int status) {
+  switch (status) {
+    case VDA_OK: return "ok";
+    case VDA_ERR_INVALID_ARG: return "invalid argument";
+    case VDA_ERR_BAD_DTYPE: return "unsupported dtype";
+    case VDA_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case VDA_ERR_MISALIGNED: return "misaligned pointer";
+    case VDA_ERR_HIP: return "HIP launch or copy failed";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

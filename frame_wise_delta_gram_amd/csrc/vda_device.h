@@ -1,0 +1,105 @@
+// Device-side helpers shared by the VDA kernels (gfx950 / CDNA4).
+//
+// MFMA conventions used throughout (wave64):
+//   v_mfma_f32_32x32x16_bf16  C[32x32] += A[32x16] B[16x32]
+//     A operand: lane l holds A[i = l % 32][k = 8 (l / 32) .. + 7]   (8 bf16)
+//     B operand: lane l holds B[k = 8 (l / 32) .. + 7][j = l % 32]   (8 bf16)
+//   v_mfma_f32_32x32x2_f32    C[32x32] += A[32x2] B[2x32]
+//     A operand: lane l holds A[i = l % 32][k = l / 32]
+//     B operand: lane l holds B[k = l / 32][j = l % 32]
+//   accumulator (both): register r of lane l holds C[acc_row(r, l)][l % 32]
+//     with acc_row(r, l) = 8 (r / 4) + 4 (l / 32) + r % 4.
+// Which contraction index sits in which k slot is free as long as the A and B
+// operands of one instruction agree; the kernels use that freedom to keep
+// every operand a contiguous 16-byte load.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace vda {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+constexpr int kThreads = 256;  // every kernel: 4 waves of 64
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+__device__ __forceinline__ int wave_id() { return threadIdx.x >> 6; }
+
+__device__ __forceinline__ int acc_row(int r, int lane) {
+  return 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+}
+
+__device__ __forceinline__ f32x16_t mfma_bf16(u32x4_t a, u32x4_t b, f32x16_t c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                 __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x16_t mfma_f32(float a, float b, f32x16_t c) {
+  return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x16_t zero16() {
+  f32x16_t z;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) z[i] = 0.0f;
+  return z;
+}
+
+// bf16 <-> fp32.  A bf16 is the top half of an fp32, so widening is a shift.
+__device__ __forceinline__ float bf16_lo(uint32_t x) { return __uint_as_float(x << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t x) { return __uint_as_float(x & 0xffff0000u); }
+
+// Two fp32 -> packed bf16 pair, round to nearest even (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
+  bf16x2_t r;
+  r[0] = (__bf16)lo;
+  r[1] = (__bf16)hi;
+  return __builtin_bit_cast(uint32_t, r);
+}
+
+// Make this wave's earlier LDS writes visible to its other lanes (LDS
+// operations of one wave execute in order; this stops the compiler from
+// moving memory accesses across the point).
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+__host__ __device__ __forceinline__ int pad32(int d) { return (d + 31) & ~31; }
+
+// ---------------------------------------------------------------------------
+// 32x32x32 fp32 block product on MFMA, operands in LDS (row-major with the
+// given strides, in floats).  acc += op(A) op(B), op = transpose when the
+// template flag is set.  Strides should be odd (e.g. 129) so that the 32
+// lanes reading one column of a row-major block hit 32 distinct banks.
+template <bool AT, bool BT>
+__device__ __forceinline__ f32x16_t blk_mm32(f32x16_t acc, const float* A, int sa, const float* B,
+                                             int sb) {
+  const int lane = lane_id();
+  const int i = lane & 31;
+  const int kh = lane >> 5;
+#pragma unroll
+  for (int kk = 0; kk < 16; ++kk) {
+    const int k = 2 * kk + kh;
+    const float a = AT ? A[k * sa + i] : A[i * sa + k];
+    const float b = BT ? B[i * sb + k] : B[k * sb + i];
+    acc = mfma_f32(a, b, acc);
+  }
+  return acc;
+}
+
+// Store a 32x32 accumulator tile into LDS/global (row-major, stride sc) scaled.
+__device__ __forceinline__ void store_acc(float* C, int sc, const f32x16_t& acc, float scale) {
+  const int lane = lane_id();
+#pragma unroll
+  for (int r = 0; r < 16; ++r) C[acc_row(r, lane) * sc + (lane & 31)] = scale * acc[r];
+}
+
+}  // namespace vda

@@ -1,0 +1,172 @@
+/*
+ * vda.h -- C ABI of the Video Delta Attention (VDA) forward library for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * VDA is the bidirectional, frame-wise delta-rule linear-memory branch of
+ * "Video DeltaNet: A Video-Native Hybrid Attention for Livestream Video
+ * Generation" (arXiv 2609.20744), cited here as [VDN].  For every unit
+ * (one batch x head pair; units are independent) the library computes:
+ *
+ *   1. frame statistics ([VDN] Sec. 3.1 Eq. (3b)), per latent frame t:
+ *        A_t = K_t^T Diag(beta_t) K_t   (d_k x d_k)
+ *        B_t = V_t^T Diag(beta_t) K_t   (d_v x d_k)
+ *      and the same for the text tokens, which form a leading virtual frame
+ *      ([VDN] Sec. 5, "Chunk-wise scans");
+ *   2. the frame-wise update ([VDN] Sec. 3.2 Eq. (5), decay alpha = 1):
+ *        S_t = (S_{t-1} + B_t) (I + A_t)^{-1}
+ *      through a Cholesky factorisation of the SPD matrix I + A_t, giving the
+ *      transition M_t = (I + A_t)^{-1} ([VDN] App. A.1 Eq. (A.1));
+ *   3. the text seed ([VDN] Sec. 2.2 Eq. (1b)): S_T = B_T (I + A_T)^{-1} and
+ *      both scans start at S_T / 2 (seed_mode 0), or at the text written from
+ *      zero at beta / 2 (seed_mode 1);
+ *   4. per chunk of `chunk` frames, the composed affine map
+ *      S_out = S_in M_chunk + J_chunk in both directions ([VDN] Sec. 5), and a
+ *      scan over chunk boundaries in both directions that keeps the forward
+ *      states P[j] (frames [0, j*chunk)) and reverse states R[j] (frames
+ *      [j*chunk, F)), with P[0] = R[n] = seed;
+ *   5. the readout ([VDN] Eq. (1a), App. A.3 Eq. (A.4) with alpha = 1, Eq. (1c)):
+ *      a query of chunk c reads S~ = P[max(c - radius, 0)] + R[min(c + radius + 1, n)],
+ *      o = S~ q, y = w * o / sqrt(mean(o^2) + eps), out = sigmoid(g) * y.
+ *
+ * Layouts (row-major, last index fastest, all tensors contiguous):
+ *   q     [units][frames][tokens][d_k]   in_dtype
+ *   k     [units][frames][tokens][d_k]   in_dtype (prepared features)
+ *   v     [units][frames][tokens][d_v]   in_dtype
+ *   beta  [units][frames][tokens]        float32, >= 0 (write strengths)
+ *   gate  [units][frames][tokens][d_v]   in_dtype (gate logits)
+ *   text_k [units][text_tokens][d_k]     in_dtype
+ *   text_v [units][text_tokens][d_v]     in_dtype
+ *   text_beta [units][text_tokens]       float32, >= 0
+ *   rms_weight [d_v]                     float32 (shared by all units)
+ *   out   [units][frames][tokens][d_v]   out_dtype (== in_dtype)
+ *
+ * Ownership: the caller owns every buffer.  All pointers are device pointers
+ * (HBM), except the descriptor, which is a host pointer read during the call.
+ * The library never allocates or frees memory; it writes only `out` (fully
+ * overwritten) and the caller's workspace.  Inputs are read-only.
+ *
+ * Streams: every call only enqueues kernels (and, for the debug taps,
+ * device-to-device copies) on `stream`; it never synchronises.  Execution
+ * errors surface at the caller's next synchronisation.  The library holds no
+ * mutable global state; calls are reentrant.  Calls that share a workspace
+ * must be ordered on one stream.
+ *
+ * Errors: functions return VDA_OK (0) or a negative vda_status_t.  Argument
+ * checks happen on the host before anything is enqueued, so a failed check
+ * leaves every buffer untouched.  No exceptions cross the ABI.
+ */
+#ifndef VDA_H_
+#define VDA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t* vda_stream_t; /* a hipStream_t; NULL = default stream */
+
+typedef enum vda_status {
+  VDA_OK = 0,
+  VDA_ERR_INVALID_ARG = -1,         /* null pointer, size out of range, bad chunk/radius/eps */
+  VDA_ERR_BAD_DTYPE = -2,           /* unsupported in_dtype/out_dtype combination */
+  VDA_ERR_WORKSPACE_TOO_SMALL = -3, /* workspace_bytes < vda_workspace_bytes(desc) */
+  VDA_ERR_MISALIGNED = -4,          /* a tensor is not 16-byte aligned, workspace not 256-byte */
+  VDA_ERR_HIP = -5                  /* a kernel launch or copy failed (hipGetLastError) */
+} vda_status_t;
+
+typedef enum vda_dtype {
+  VDA_DTYPE_F32 = 0,  /* fp32 features, fp32 arithmetic throughout */
+  VDA_DTYPE_BF16 = 1  /* bf16 features, bf16 x bf16 MFMA with fp32 accumulation, fp32 state */
+} vda_dtype_t;
+
+typedef struct vda_desc {
+  int32_t units;       /* batch x heads, >= 0 */
+  int32_t frames;      /* latent frames F, >= 0 */
+  int32_t tokens;      /* tokens per frame U, >= 0 */
+  int32_t text_tokens; /* text tokens T, >= 0 (0: zero seed) */
+  int32_t d_k;         /* key channels, multiple of 16, 16..128 */
+  int32_t d_v;         /* value channels, multiple of 16, 16..128 */
+  int32_t chunk;       /* frames per chunk C, >= 1 ([VDN] uses 5) */
+  int32_t radius;      /* window radius in chunks r, >= 0 ([VDN] uses 1) */
+  float rms_eps;       /* RMSNorm epsilon, finite and >= 0 */
+  int32_t seed_mode;   /* 0: seed = S_T / 2 ([VDN] Eq. (1b)); 1: text written at beta / 2 */
+  int32_t in_dtype;    /* vda_dtype_t of q, k, v, gate, text_k, text_v */
+  int32_t out_dtype;   /* vda_dtype_t of out; must equal in_dtype */
+} vda_desc_t;
+
+/* Bytes of device workspace vda_forward and the debug taps need for `desc`
+ * (fp32 frame statistics, transitions, chunk maps and boundary states).
+ * Returns 0 when desc is NULL or invalid. Host-only; never touches the GPU. */
+size_t vda_workspace_bytes(const vda_desc_t* desc);
+
+/* Checks desc alone (host-only).  Returns VDA_OK or the error vda_forward
+ * would return for it. */
+int vda_check_desc(const vda_desc_t* desc);
+
+/* The VDA forward pass described at the top of this file.  q, k, v, gate,
+ * out, text_k, text_v and rms_weight must be 16-byte aligned, beta and
+ * text_beta 4-byte aligned, workspace 256-byte aligned.  Pointers to empty
+ * tensors (size 0) may be NULL.  beta and text_beta must be >= 0 (I + A must
+ * be SPD); this is not checked (negative values give undefined results). */
+int vda_forward(const vda_desc_t* desc, const void* q, const void* k, const void* v,
+                const float* beta, const void* gate, const void* text_k, const void* text_v,
+                const float* text_beta, const float* rms_weight, void* out, void* workspace,
+                size_t workspace_bytes, vda_stream_t stream);
+
+/* vda_forward that also records caller-created HIP events (hipEvent_t, cast
+ * to void*) on `stream` at the stage boundaries, for per-kernel timing:
+ * stage_events[0] before the statistics kernel, [1] before the solve, [2]
+ * before the chunk composition, [3] before the scan, [4] before the readout
+ * and [5] after it.  n_events must be 6 and every event non-NULL.  Results
+ * are identical to vda_forward. */
+int vda_forward_timed(const vda_desc_t* desc, const void* q, const void* k, const void* v,
+                      const float* beta, const void* gate, const void* text_k, const void* text_v,
+                      const float* text_beta, const float* rms_weight, void* out, void* workspace,
+                      size_t workspace_bytes, vda_stream_t stream, void* const* stage_events,
+                      int n_events);
+
+/* ---- debug taps (tests only).  Each runs the pipeline up to the named stage in
+ * the caller's workspace and copies that stage's fp32 results to caller
+ * buffers (device pointers, row-major, contiguous). ---- */
+
+/* Frame statistics, [VDN] Eq. (3b).  Frame index 0 is the text frame (its beta
+ * already halved in seed_mode 1), frame f + 1 is latent frame f.
+ * A_out [units][frames + 1][d_k][d_k], B_out [units][frames + 1][d_v][d_k]. */
+int vda_debug_stats(const vda_desc_t* desc, const void* k, const void* v, const float* beta,
+                    const void* text_k, const void* text_v, const float* text_beta,
+                    float* A_out, float* B_out, void* workspace, size_t workspace_bytes,
+                    vda_stream_t stream);
+
+/* Transitions M_t = (I + A_t)^{-1} ([VDN] Eq. (A.1)) and the seed ([VDN] Eq. (1b)).
+ * M_out [units][frames + 1][d_k][d_k] (index 0: text frame), seed_out [units][d_v][d_k]. */
+int vda_debug_solve(const vda_desc_t* desc, const void* k, const void* v, const float* beta,
+                    const void* text_k, const void* text_v, const float* text_beta,
+                    float* M_out, float* seed_out, void* workspace, size_t workspace_bytes,
+                    vda_stream_t stream);
+
+/* Composed chunk maps ([VDN] Sec. 5): forward S_out = S_in Mc + Jf over the
+ * chunk's frames in order, reverse S_out = S_in Mc^T + Jr over them in
+ * reverse order (each M_t is symmetric).  n = ceil(frames / chunk).
+ * Mc_out [units][n][d_k][d_k], Jf_out and Jr_out [units][n][d_v][d_k]. */
+int vda_debug_chunks(const vda_desc_t* desc, const void* k, const void* v, const float* beta,
+                     const void* text_k, const void* text_v, const float* text_beta,
+                     float* Mc_out, float* Jf_out, float* Jr_out, void* workspace,
+                     size_t workspace_bytes, vda_stream_t stream);
+
+/* Boundary states of both scans: P_out[u][j] = forward state after frames
+ * [0, j*chunk), R_out[u][j] = reverse state after frames [j*chunk, F),
+ * j = 0..n, with P[0] = R[n] = seed.  P_out, R_out [units][n + 1][d_v][d_k]. */
+int vda_debug_states(const vda_desc_t* desc, const void* k, const void* v, const float* beta,
+                     const void* text_k, const void* text_v, const float* text_beta,
+                     float* P_out, float* R_out, void* workspace, size_t workspace_bytes,
+                     vda_stream_t stream);
+
+/* Static, human-readable text for a vda_status_t (never NULL). */
+const char* vda_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* VDA_H_ */

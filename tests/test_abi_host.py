@@ -1,0 +1,137 @@
+"""Host-side checks of the C ABI (no GPU needed: every call here returns before
+anything is enqueued)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import frame_wise_delta_gram_amd as vda
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "vda.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(vda.LIB_PATH):
+        pytest.skip("libvda.so not built")
+    return vda.load_library()
+
+
+def header_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(vda_[a-z_]+)\s*\(", src)))
+
+
+def test_header_declares_the_binding_surface():
+    assert header_functions() == sorted(vda.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", vda.LIB_PATH], stdout=subprocess.PIPE,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r" T (vda_[a-z_]+)$", out, flags=re.M))
+    for name in header_functions():
+        assert name in exported, name
+        assert hasattr(lib, name)
+
+
+def desc(**kw):
+    base = dict(units=2, frames=12, tokens=40, text_tokens=7, d_k=64, d_v=32, chunk=5, radius=1,
+                rms_eps=1e-6, seed_mode=0, dtype=vda.VDA_DTYPE_BF16)
+    base.update(kw)
+    return vda.make_desc(**base)
+
+
+def test_workspace_formula(lib):
+    d = desc()
+    n = 3
+    def a(x):
+        return (x + 255) // 256 * 256
+    units, Fp1, dk, dv = 2, 13, 64, 32
+    expect = (a(units * Fp1 * dk * dk * 4) + a(units * Fp1 * dv * dk * 4) + a(units * Fp1 * dk * dk * 4)
+              + a(units * n * dk * dk * 4) + 2 * a(units * n * dv * dk * 4)
+              + a(units * 2 * (n + 1) * dv * dk * 4))
+    assert vda.vda_workspace_bytes(d) == expect
+    assert vda.vda_workspace_bytes(desc(units=0)) == 0
+    assert vda.vda_workspace_bytes(desc(frames=0)) == 0
+    assert vda.vda_workspace_bytes(desc(d_k=12)) == 0  # invalid -> 0
+    assert lib.vda_workspace_bytes(None) == 0
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(), vda.VDA_OK),
+    (dict(d_k=8), vda.VDA_ERR_INVALID_ARG),
+    (dict(d_k=144), vda.VDA_ERR_INVALID_ARG),
+    (dict(d_v=24), vda.VDA_ERR_INVALID_ARG),
+    (dict(chunk=0), vda.VDA_ERR_INVALID_ARG),
+    (dict(radius=-1), vda.VDA_ERR_INVALID_ARG),
+    (dict(units=-1), vda.VDA_ERR_INVALID_ARG),
+    (dict(tokens=-5), vda.VDA_ERR_INVALID_ARG),
+    (dict(rms_eps=-1.0), vda.VDA_ERR_INVALID_ARG),
+    (dict(rms_eps=float("nan")), vda.VDA_ERR_INVALID_ARG),
+    (dict(rms_eps=float("inf")), vda.VDA_ERR_INVALID_ARG),
+    (dict(seed_mode=2), vda.VDA_ERR_INVALID_ARG),
+    (dict(units=70000), vda.VDA_ERR_INVALID_ARG),
+    (dict(dtype=7), vda.VDA_ERR_BAD_DTYPE),
+    (dict(units=0, frames=0, tokens=0), vda.VDA_OK),
+    (dict(d_k=16, d_v=128), vda.VDA_OK),
+])
+def test_descriptor_checks(lib, kw, status):
+    assert vda.vda_check_desc(desc(**kw)) == status
+
+
+def test_out_dtype_must_match(lib):
+    d = desc()
+    d.out_dtype = vda.VDA_DTYPE_F32
+    assert vda.vda_check_desc(d) == vda.VDA_ERR_BAD_DTYPE
+
+
+def call_forward(lib, d, **ptrs):
+    names = ["q", "k", "v", "beta", "gate", "text_k", "text_v", "text_beta", "rms_weight", "out",
+             "workspace"]
+    args = [ptrs.get(n, 4096 * (i + 1)) for i, n in enumerate(names)]
+    ws_bytes = ptrs.get("ws_bytes", vda.vda_workspace_bytes(d))
+    return lib.vda_forward(ctypes.byref(d), *args, ws_bytes, None)
+
+
+def test_forward_argument_errors(lib):
+    d = desc()
+    assert call_forward(lib, d, k=None) == vda.VDA_ERR_INVALID_ARG
+    assert call_forward(lib, d, q=None) == vda.VDA_ERR_INVALID_ARG
+    assert call_forward(lib, d, text_v=None) == vda.VDA_ERR_INVALID_ARG
+    assert call_forward(lib, d, workspace=None) == vda.VDA_ERR_INVALID_ARG
+    assert call_forward(lib, d, ws_bytes=vda.vda_workspace_bytes(d) - 1) == \
+        vda.VDA_ERR_WORKSPACE_TOO_SMALL
+    assert call_forward(lib, d, q=4096 + 8) == vda.VDA_ERR_MISALIGNED
+    assert call_forward(lib, d, workspace=4096 + 128) == vda.VDA_ERR_MISALIGNED
+    assert call_forward(lib, d, rms_weight=4096 + 4) == vda.VDA_ERR_MISALIGNED
+    assert lib.vda_forward(None, *([None] * 11), 0, None) == vda.VDA_ERR_INVALID_ARG
+    # empty problems need no pointers at all and enqueue nothing
+    e = desc(units=0)
+    assert lib.vda_forward(ctypes.byref(e), *([None] * 11), 0, None) == vda.VDA_OK
+    e = desc(frames=0)
+    assert lib.vda_forward(ctypes.byref(e), *([None] * 11), 0, None) == vda.VDA_OK
+
+
+def test_debug_tap_argument_errors(lib):
+    d = desc()
+    P = [4096 * (i + 1) for i in range(9)]
+    ws = vda.vda_workspace_bytes(d)
+    assert lib.vda_debug_stats(ctypes.byref(d), None, *P[1:8], P[8], ws, None) == \
+        vda.VDA_ERR_INVALID_ARG
+    assert lib.vda_debug_solve(ctypes.byref(d), *P[:6], None, P[7], P[8], ws, None) == \
+        vda.VDA_ERR_INVALID_ARG
+    assert lib.vda_debug_chunks(ctypes.byref(d), *P[:6], P[6], P[7], None, P[8], ws, None) == \
+        vda.VDA_ERR_INVALID_ARG
+    assert lib.vda_debug_states(ctypes.byref(d), *P[:8], P[8], ws - 256, None) == \
+        vda.VDA_ERR_WORKSPACE_TOO_SMALL
+
+
+def test_status_strings(lib):
+    for s in (0, -1, -2, -3, -4, -5):
+        assert vda.vda_status_string(s) and vda.vda_status_string(s) != "unknown status"
+    assert vda.vda_status_string(42) == "unknown status"
