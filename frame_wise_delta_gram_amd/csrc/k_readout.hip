@@ -103,20 +103,35 @@ __global__ __launch_bounds__(256, 2) void readout_bf16_kernel(
   const int il = lane & 31;     // token within the 32-row block
   const size_t chunk_row0 = ((size_t)u * F + f0) * U;
   const float inv_dv = 1.0f / (float)dv;
+  const u32x4_t z4 = {0u, 0u, 0u, 0u};
+
+  // software pipeline over this wave's 32-row blocks: the next block's queries
+  // and the current block's gate logits are in flight during the MFMAs
+  auto load_q = [&](u32x4_t (&qr)[8], long rb) {
+    const long myrow = rb + il;
+    const bool valid = rb < rows_total && myrow < rows_total;
+    const uint16_t* qp = q + (chunk_row0 + (size_t)(valid ? myrow : 0)) * dk + g * halfk;
+#pragma unroll
+    for (int s = 0; s < 8; ++s)
+      qr[s] = (s < NKS && valid) ? *reinterpret_cast<const u32x4_t*>(qp + 8 * s) : z4;
+  };
+  u32x4_t qcur[8], qnext[8];
+  load_q(qcur, row0 + (long)w * 32);
 
   for (int it = 0; it < kIters; ++it) {
     const long rb = row0 + (long)(it * 4 + w) * 32;
     if (rb >= rows_total) break;
+    if (it + 1 < kIters) load_q(qnext, row0 + (long)((it + 1) * 4 + w) * 32);
     const long myrow = rb + il;
     const bool valid = myrow < rows_total;
-    const size_t grow = chunk_row0 + (size_t)myrow;
-
-    u32x4_t qr[8];
-    const uint16_t* qp = q + grow * dk + g * halfk;
+    const size_t grow = chunk_row0 + (size_t)(valid ? myrow : 0);
+    u32x4_t gv[8];
+    {
+      const uint16_t* gp = gate + grow * dv + g * HALF;
 #pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      const u32x4_t z = {0u, 0u, 0u, 0u};
-      qr[s] = (s < NKS && valid) ? *reinterpret_cast<const u32x4_t*>(qp + 8 * s) : z;
+      for (int m = 0; m < 8; ++m)
+        gv[m] = (valid && 8 * m < HALF && g * HALF + 8 * m < dv)
+                    ? *reinterpret_cast<const u32x4_t*>(gp + 8 * m) : z4;
     }
     f32x16_t acc[4];
 #pragma unroll
@@ -130,8 +145,8 @@ __global__ __launch_bounds__(256, 2) void readout_bf16_kernel(
         const int off = (32 * T + il) * SROW + g * halfk + 8 * s;
         const u32x4_t ah = *reinterpret_cast<const u32x4_t*>(Shi + off);
         const u32x4_t al = *reinterpret_cast<const u32x4_t*>(Slo + off);
-        acc[T] = mfma_bf16(ah, qr[s], acc[T]);
-        acc[T] = mfma_bf16(al, qr[s], acc[T]);
+        acc[T] = mfma_bf16(ah, qcur[s], acc[T]);
+        acc[T] = mfma_bf16(al, qcur[s], acc[T]);
       }
     }
 
@@ -145,13 +160,11 @@ __global__ __launch_bounds__(256, 2) void readout_bf16_kernel(
     const float inv = rsqrtf(ss * inv_dv + eps);
 
     if (valid) {
-      const uint16_t* gp = gate + grow * dv + g * HALF;
       uint16_t* op = out + grow * dv + g * HALF;
       const float* wp = wrms + g * HALF;
 #pragma unroll
       for (int m = 0; m < 8; ++m) {
         if (8 * m >= HALF || g * HALF + 8 * m >= dv) continue;
-        const u32x4_t gv = *reinterpret_cast<const u32x4_t*>(gp + 8 * m);
         const f32x4_t w0 = *reinterpret_cast<const f32x4_t*>(wp + 8 * m);
         const f32x4_t w1 = *reinterpret_cast<const f32x4_t*>(wp + 8 * m + 4);
         float y[8];
@@ -159,7 +172,7 @@ __global__ __launch_bounds__(256, 2) void readout_bf16_kernel(
         for (int e = 0; e < 8; ++e) {
           const int idx = 8 * m + e;
           const float o = acc[idx >> 4][idx & 15];
-          const float gl = (e & 1) ? bf16_hi(gv[e >> 1]) : bf16_lo(gv[e >> 1]);
+          const float gl = (e & 1) ? bf16_hi(gv[m][e >> 1]) : bf16_lo(gv[m][e >> 1]);
           const float ww = e < 4 ? w0[e] : w1[e - 4];
           const float sig = 1.0f / (1.0f + __expf(-gl));
           y[e] = o * inv * ww * sig;
@@ -170,6 +183,8 @@ __global__ __launch_bounds__(256, 2) void readout_bf16_kernel(
         *reinterpret_cast<u32x4_t*>(op + 8 * m) = ov;
       }
     }
+#pragma unroll
+    for (int s = 0; s < 8; ++s) qcur[s] = qnext[s];
   }
 }
 

@@ -29,19 +29,16 @@ namespace {
 
 constexpr int SG = 129;
 
-// rows x Dk block of a row-major (ld = dk) fp32 matrix into LDS, zero padded
-// to R32 x Dk; adds `add` (same layout) when given.
-__device__ __forceinline__ void load_rows(float* dst, const float* src, const float* add, int rows,
-                                          int R32, int dk, int Dk) {
-  for (int idx = threadIdx.x; idx < R32 * Dk; idx += 256) {
-    const int i = idx / Dk;
-    const int j = idx - i * Dk;
-    float x = 0.0f;
-    if (i < rows && j < dk) {
-      x = src[(size_t)i * dk + j];
-      if (add) x += add[(size_t)i * dk + j];
-    }
-    dst[i * SG + j] = x;
+// acc-layout prefetch of a 32-row x 32-col tile (rows r0.., cols c0..) of a
+// row-major fp32 matrix with `rows` x dk valid entries; zero outside
+__device__ __forceinline__ void tile_prefetch(float (&dst)[16], const float* src, int dk, int rows,
+                                              int r0, int c0) {
+  const int lane = lane_id();
+  const int col = c0 + (lane & 31);
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int row = r0 + acc_row(r, lane);
+    dst[r] = (row < rows && col < dk) ? src[(size_t)row * dk + col] : 0.0f;
   }
 }
 
@@ -73,21 +70,40 @@ __global__ __launch_bounds__(256, 1) void compose_kernel(const float* __restrict
   auto Mp = [&](int f) { return Mw + ((size_t)u * Fp1 + f + 1) * dk * dk; };
   auto Bp = [&](int f) { return Bw + ((size_t)u * Fp1 + f + 1) * dv * dk; };
 
-  if (chain == 0) {
-    for (int idx = t; idx < R32 * Dk; idx += 256) {
-      const int i = idx / Dk;
-      const int j = idx - i * Dk;
-      Xs[i * SG + j] = (i == j) ? 1.0f : 0.0f;
+  {
+    MatRegs m;
+    if (chain != 0) {
+      mat_load(m, Bp(frame(0)), dk, dv, dk);
+      mat_store_lds(m, Xs, SG, R32, Dk);
+    } else {
+      for (int idx = t; idx < R32 * Dk; idx += 256) {
+        const int i = idx / Dk;
+        const int j = idx - i * Dk;
+        Xs[i * SG + j] = (i == j) ? 1.0f : 0.0f;
+      }
     }
-  } else {
-    load_rows(Xs, Bp(frame(0)), nullptr, dv, R32, dk, Dk);
+    mat_load(m, Mp(frame(0)), dk, dk, dk);
+    mat_store_lds(m, Ms, SG, Dk, Dk);
   }
-  load_rows(Ms, Mp(frame(0)), nullptr, dk, Dk, dk, Dk);
   __syncthreads();
 
   float* dst = chain == 0 ? Mc + ((size_t)u * n + c) * dk * dk
                           : (chain == 1 ? Jf : Jr) + ((size_t)u * n + c) * dv * dk;
+  MatRegs mnext;
+  float bnext[4][16];
   for (int s = 0; s < nf; ++s) {
+    const bool last = s == nf - 1;
+    if (!last) {  // next frame's transition (and write) fly while this step multiplies
+      mat_load(mnext, Mp(frame(s + 1)), dk, dk, dk);
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct) {
+        if (chain != 0 && w < nR && ct < nb)
+          tile_prefetch(bnext[ct], Bp(frame(s + 1)), dk, dv, 32 * w, 32 * ct);
+        else
+#pragma unroll
+          for (int r = 0; r < 16; ++r) bnext[ct][r] = 0.0f;
+      }
+    }
     f32x16_t acc[4];
 #pragma unroll
     for (int ct = 0; ct < 4; ++ct) acc[ct] = zero16();
@@ -101,8 +117,6 @@ __global__ __launch_bounds__(256, 1) void compose_kernel(const float* __restrict
       }
     }
     __syncthreads();
-    const bool last = s == nf - 1;
-    const float* addB = (!last && chain != 0) ? Bp(frame(s + 1)) : nullptr;
     if (w < nR) {
 #pragma unroll
       for (int ct = 0; ct < 4; ++ct) {
@@ -111,18 +125,16 @@ __global__ __launch_bounds__(256, 1) void compose_kernel(const float* __restrict
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int row = 32 * w + acc_row(r, lane);
-          float x = acc[ct][r];
           if (last) {
-            if (row < rows && col < dk) dst[(size_t)row * dk + col] = x;
+            if (row < rows && col < dk) dst[(size_t)row * dk + col] = acc[ct][r];
           } else {
-            if (addB && row < rows && col < dk) x += addB[(size_t)row * dk + col];
-            Xs[row * SG + col] = x;
+            Xs[row * SG + col] = acc[ct][r] + bnext[ct][r];
           }
         }
       }
     }
     if (last) break;
-    load_rows(Ms, Mp(frame(s + 1)), nullptr, dk, Dk, dk, Dk);
+    mat_store_lds(mnext, Ms, SG, Dk, Dk);
     __syncthreads();
   }
 }
@@ -145,12 +157,26 @@ __global__ __launch_bounds__(256) void scan_kernel(const float* __restrict__ Mc,
   float* S = ST + (size_t)(u * 2 + dir) * (n + 1) * SS;
   const int r0 = 32 * rb;
   const int nrows = min(32, dv - r0);
+  auto chunk = [&](int s) { return dir == 0 ? s : n - 1 - s; };
+  const float* Jb = (dir == 0 ? Jf : Jr) + (size_t)u * n * SS;
 
-  load_rows(Xs, S + (size_t)(dir == 0 ? 0 : n) * SS + (size_t)r0 * dk, nullptr, nrows, 32, dk, Dk);
+  MatRegs m;
+  mat_load(m, S + (size_t)(dir == 0 ? 0 : n) * SS + (size_t)r0 * dk, dk, nrows, dk);
+  mat_store_lds(m, Xs, SG, 32, Dk);
+  mat_load(m, Mc + ((size_t)u * n + chunk(0)) * dk * dk, dk, dk, dk);
+  mat_store_lds(m, Ms, SG, Dk, Dk);
+  float jreg[16];
+  if (w < nb) tile_prefetch(jreg, Jb + (size_t)chunk(0) * SS + (size_t)r0 * dk, dk, nrows, 0, 32 * w);
+  __syncthreads();
   for (int s = 0; s < n; ++s) {
-    const int j = dir == 0 ? s : n - 1 - s;
-    load_rows(Ms, Mc + ((size_t)u * n + j) * dk * dk, nullptr, dk, Dk, dk, Dk);
-    __syncthreads();
+    const int j = chunk(s);
+    const bool last = s == n - 1;
+    float jnext[16];
+    if (!last) {
+      mat_load(m, Mc + ((size_t)u * n + chunk(s + 1)) * dk * dk, dk, dk, dk);
+      if (w < nb)
+        tile_prefetch(jnext, Jb + (size_t)chunk(s + 1) * SS + (size_t)r0 * dk, dk, nrows, 0, 32 * w);
+    }
     f32x16_t acc = zero16();
     if (w < nb) {
       for (int kb = 0; kb < nb; ++kb) {
@@ -162,20 +188,21 @@ __global__ __launch_bounds__(256) void scan_kernel(const float* __restrict__ Mc,
     }
     __syncthreads();
     if (w < nb) {
-      const float* J = (dir == 0 ? Jf : Jr) + ((size_t)u * n + j) * SS;
       float* dst = S + (size_t)(dir == 0 ? j + 1 : j) * SS;
       const int col = 32 * w + (lane & 31);
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int row = acc_row(r, lane);
-        float x = 0.0f;
-        if (row < nrows && col < dk) {
-          x = acc[r] + J[(size_t)(r0 + row) * dk + col];
-          dst[(size_t)(r0 + row) * dk + col] = x;
-        }
+        const float x = (row < nrows && col < dk) ? acc[r] + jreg[r] : 0.0f;
+        if (row < nrows && col < dk) dst[(size_t)(r0 + row) * dk + col] = x;
         Xs[row * SG + col] = x;
       }
     }
+    if (last) break;
+    mat_store_lds(m, Ms, SG, Dk, Dk);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) jreg[r] = jnext[r];
+    __syncthreads();
   }
 }
 

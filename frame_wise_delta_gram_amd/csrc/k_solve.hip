@@ -6,18 +6,21 @@
 //   write strengths were already halved.
 //
 // I + A_t is symmetric positive definite with every eigenvalue >= 1 (A_t is a
-// Gram matrix with beta >= 0), so a Cholesky factorisation without pivoting is
-// stable; its diagonal is >= 1.  One workgroup (4 waves) per frame keeps the
-// whole d_k x d_k matrix in LDS (fp32, odd row stride) and works on 32 x 32
-// blocks:
+// Gram matrix), so a Cholesky factorisation without pivoting is stable and its
+// diagonal is >= 1.  One workgroup (4 waves) per frame keeps the d_k x d_k
+// matrix in LDS (fp32, odd row stride), in place, and works on 32 x 32 blocks:
 //   1. blocked right-looking Cholesky  I + A = L L^T.  The 32-column diagonal
-//      block is factored by one wave entirely in registers (lane c holds
-//      column c; pivots and columns are broadcast with readlane, no LDS round
-//      trips), which also inverts it.  Panel and trailing updates are 32x32x32
-//      fp32 MFMA block products spread over the 4 waves;
-//   2. W = L^{-1}, block column j by wave j (the block columns are independent);
+//      block is factored by one wave in registers (lane c holds column c;
+//      pivots and columns move with readlane, no LDS round trips) and replaced
+//      by the inverse of its factor, W_pp = L_pp^{-1}.  Panel (L_ip = G_ip
+//      W_pp^T) and trailing (G_ij -= L_ip L_jp^T) updates are 32x32x32 fp32
+//      MFMA block products spread over the 4 waves;
+//   2. W = L^{-1} row block by row block: W_ij = -W_ii sum_{k=j}^{i-1} L_ik W_kj,
+//      the blocks of one row in parallel (sums staged in a small buffer, so L
+//      is overwritten only after the whole row has read it);
 //   3. M = W^T W, the upper blocks by MFMA, mirrored on store.
-// fp32 throughout.
+// One 66 KiB matrix buffer per workgroup lets two workgroups share a CU, so
+// one's serial diagonal work overlaps the other's MFMA work.  fp32 throughout.
 #include "vda_device.h"
 #include "vda_internal.h"
 
@@ -25,14 +28,15 @@ namespace vda {
 namespace {
 
 constexpr int SG = 129;  // LDS row stride in floats (odd: conflict-free column reads)
+constexpr int ST = 33;   // stride of the 32x32 staging blocks
 
 __device__ __forceinline__ float readlane_f(float x, int l) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), l));
 }
 
-// Factor the 32x32 SPD block at G (stride SG) as L L^T and invert L, by one
-// wave.  On return G holds L (zero above the diagonal) and W holds L^{-1}.
-__device__ void factor_diag_block(float* G, float* W) {
+// Factor the 32x32 SPD block at G (stride SG) as L L^T and overwrite it with
+// W = L^{-1} (lower triangular, zeros above the diagonal), by one wave.
+__device__ void factor_invert_diag_block(float* G) {
   const int lane = lane_id();
   const int c = lane & 31;  // lanes 32..63 duplicate lanes 0..31 and do not store
   float col[32];
@@ -43,18 +47,22 @@ __device__ void factor_diag_block(float* G, float* W) {
   for (int j = 0; j < 32; ++j) {
     const float piv = sqrtf(readlane_f(col[j], j));
     const float inv = 1.0f / piv;
-    const float lij = col[j] * inv;  // L[c][j] for c > j (the block is symmetric)
-    if (c == j) {
-#pragma unroll
-      for (int k = 0; k < 32; ++k) col[k] = k < j ? 0.0f : (k == j ? piv : col[k] * inv);
-    }
+    // lanes c > j: L[c][j] = D[c][j] / piv (own copy, the block is symmetric);
+    // t = L[c][j] / piv so that D[k][c] -= L[k][j] L[c][j] = D[k][j] * t
+    const float t = col[j] * inv * inv;
 #pragma unroll
     for (int k = j + 1; k < 32; ++k) {
-      const float lkj = readlane_f(col[k], j);  // L[k][j], finalised by lane j
-      if (c > j) col[k] = fmaf(-lkj, lij, col[k]);
+      const float dkj = readlane_f(col[j], k);  // D[k][j] = D[j][k], held by lane k
+      if (c > j) col[k] = fmaf(-dkj, t, col[k]);
+    }
+    if (c == j) {
+      col[j] = piv;
+#pragma unroll
+      for (int k = j + 1; k < 32; ++k) col[k] *= inv;
     }
   }
-  // column c of W = L^{-1} by forward substitution: L w = e_c
+  // col[k] = L[k][c] for k >= c.  Column c of W: forward substitution L w = e_c,
+  // w[i] = (delta_ic - sum_{k<i} L[i][k] w[k]) / L[i][i]; L[i][k] sits in lane k.
   float wv[32];
 #pragma unroll
   for (int i = 0; i < 32; ++i) {
@@ -65,20 +73,17 @@ __device__ void factor_diag_block(float* G, float* W) {
   }
   if (lane < 32) {
 #pragma unroll
-    for (int k = 0; k < 32; ++k) {
-      G[k * SG + c] = col[k];
-      W[k * SG + c] = wv[k];
-    }
+    for (int k = 0; k < 32; ++k) G[k * SG + c] = wv[k];
   }
 }
 
-__global__ __launch_bounds__(256, 1) void solve_kernel(const float* __restrict__ A,
+__global__ __launch_bounds__(256, 2) void solve_kernel(const float* __restrict__ A,
                                                       const float* __restrict__ B,
                                                       float* __restrict__ Mout,
-                                                      float* __restrict__ ST, int dk, int dv,
+                                                      float* __restrict__ STt, int dk, int dv,
                                                       int Fp1, int n, float seed_scale) {
   __shared__ float Gs[128 * SG];
-  __shared__ float Ws[128 * SG];
+  __shared__ float Ts[3 * 32 * ST];
   const int fi = blockIdx.x;
   const int u = blockIdx.y;
   const int t = threadIdx.x;
@@ -87,26 +92,24 @@ __global__ __launch_bounds__(256, 1) void solve_kernel(const float* __restrict__
   const int Dk = pad32(dk);
   const int nb = Dk >> 5;
   auto G = [&](int i, int j) { return Gs + 32 * i * SG + 32 * j; };
-  auto Wb = [&](int i, int j) { return Ws + 32 * i * SG + 32 * j; };
 
-  const float* Ag = A + ((size_t)u * Fp1 + fi) * dk * dk;
-  for (int idx = t; idx < Dk * Dk; idx += 256) {
-    const int i = idx / Dk;
-    const int j = idx - i * Dk;
-    const float a = (i < dk && j < dk) ? Ag[(size_t)i * dk + j] : 0.0f;
-    Gs[i * SG + j] = a + (i == j ? 1.0f : 0.0f);
-    Ws[i * SG + j] = 0.0f;
+  {
+    MatRegs m;
+    mat_load(m, A + ((size_t)u * Fp1 + fi) * dk * dk, dk, dk, dk);
+    mat_store_lds(m, Gs, SG, Dk, Dk);
+    __syncthreads();
+    for (int i = t; i < Dk; i += 256) Gs[i * SG + i] += 1.0f;  // I + A (identity on padding)
+    __syncthreads();
   }
-  __syncthreads();
 
-  // 1. blocked Cholesky
+  // 1. blocked Cholesky; diagonal blocks end up holding W_pp = L_pp^{-1}
   for (int p = 0; p < nb; ++p) {
-    if (w == 0) factor_diag_block(G(p, p), Wb(p, p));
+    if (w == 0) factor_invert_diag_block(G(p, p));
     __syncthreads();
     {  // panel: L_ip = G_ip L_pp^{-T} = G_ip W_pp^T
       const int i = p + 1 + w;
       if (i < nb) {
-        const f32x16_t acc = blk_mm32<false, true>(zero16(), G(i, p), SG, Wb(p, p), SG);
+        const f32x16_t acc = blk_mm32<false, true>(zero16(), G(i, p), SG, G(p, p), SG);
         store_acc(G(i, p), SG, acc, 1.0f);
       }
     }
@@ -125,23 +128,24 @@ __global__ __launch_bounds__(256, 1) void solve_kernel(const float* __restrict__
     __syncthreads();
   }
 
-  // 2. W = L^{-1}: W_ij = -W_ii sum_{k=j}^{i-1} L_ik W_kj, block column j by wave j
-  if (w < nb - 1) {
-    const int j = w;
-    for (int i = j + 1; i < nb; ++i) {
+  // 2. off-diagonal blocks of W = L^{-1}, row block by row block
+  for (int i = 1; i < nb; ++i) {
+    if (w < i) {  // wave j = w: T_ij = sum_{k=j}^{i-1} L_ik W_kj
+      const int j = w;
       f32x16_t acc = zero16();
-      for (int k = j; k < i; ++k) acc = blk_mm32<false, false>(acc, G(i, k), SG, Wb(k, j), SG);
-      store_acc(Wb(i, j), SG, acc, 1.0f);
-      wave_sync();
-      const f32x16_t acc2 = blk_mm32<false, false>(zero16(), Wb(i, i), SG, Wb(i, j), SG);
-      wave_sync();
-      store_acc(Wb(i, j), SG, acc2, -1.0f);
-      wave_sync();
+      for (int k = j; k < i; ++k) acc = blk_mm32<false, false>(acc, G(i, k), SG, G(k, j), SG);
+      store_acc(Ts + j * 32 * ST, ST, acc, 1.0f);
     }
+    __syncthreads();
+    if (w < i) {  // W_ij = -W_ii T_ij (overwrites L_ij)
+      const int j = w;
+      const f32x16_t acc = blk_mm32<false, false>(zero16(), G(i, i), SG, Ts + j * 32 * ST, ST);
+      store_acc(G(i, j), SG, acc, -1.0f);
+    }
+    __syncthreads();
   }
-  __syncthreads();
 
-  // 3. M = W^T W: M_ab = sum_{k >= max(a,b)} W_ka^T W_kb
+  // 3. M = W^T W: M_ab = sum_{k >= max(a,b)} W_ka^T W_kb, written to global
   float* Mg = Mout + ((size_t)u * Fp1 + fi) * dk * dk;
   {
     int q = 0;
@@ -149,51 +153,48 @@ __global__ __launch_bounds__(256, 1) void solve_kernel(const float* __restrict__
       for (int a = 0; a <= b; ++a, ++q) {
         if ((q & 3) != w) continue;
         f32x16_t acc = zero16();
-        for (int k = b; k < nb; ++k) acc = blk_mm32<true, false>(acc, Wb(k, a), SG, Wb(k, b), SG);
+        for (int k = b; k < nb; ++k) acc = blk_mm32<true, false>(acc, G(k, a), SG, G(k, b), SG);
         const int col = lane & 31;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int row = acc_row(r, lane);
-          const int gi = 32 * a + row, gj = 32 * b + col;
+          const int gi = 32 * a + acc_row(r, lane), gj = 32 * b + col;
           if (gi < dk && gj < dk) {
             Mg[(size_t)gi * dk + gj] = acc[r];
             if (a != b) Mg[(size_t)gj * dk + gi] = acc[r];
-          }
-          if (fi == 0) {  // keep M_T for the seed product (L is no longer needed)
-            G(a, b)[row * SG + col] = acc[r];
-            if (a != b) G(b, a)[col * SG + row] = acc[r];
           }
         }
       }
   }
 
-  // 4. text frame: seed = seed_scale * B_T M_T, written to P[0] and R[n]
+  // 4. text frame: seed = seed_scale * B_T M_T (M_T read back from global memory,
+  //    where this workgroup just wrote it), stored as P[0] and R[n]
   if (fi == 0) {
+    __threadfence();
     __syncthreads();
     const int nV = pad32(dv) >> 5;
     if (w < nV) {
       const float* Bg = B + (size_t)u * Fp1 * dv * dk;
-      float* P0 = ST + ((size_t)(u * 2 + 0) * (n + 1) + 0) * dv * dk;
-      float* Rn = ST + ((size_t)(u * 2 + 1) * (n + 1) + n) * dv * dk;
+      float* P0 = STt + ((size_t)(u * 2 + 0) * (n + 1) + 0) * dv * dk;
+      float* Rn = STt + ((size_t)(u * 2 + 1) * (n + 1) + n) * dv * dk;
       const int il = lane & 31;
       const int kh = lane >> 5;
       const int row = 32 * w + il;
       for (int ct = 0; ct < nb; ++ct) {
+        const int col = 32 * ct + il;
         f32x16_t acc = zero16();
         for (int kk = 0; kk < Dk / 2; ++kk) {
           const int kx = 2 * kk + kh;
           const float a = (row < dv && kx < dk) ? Bg[(size_t)row * dk + kx] : 0.0f;
-          const float b = Gs[kx * SG + 32 * ct + il];
+          const float b = (kx < dk && col < dk) ? Mg[(size_t)kx * dk + col] : 0.0f;
           acc = mfma_f32(a, b, acc);
         }
-        const int col = 32 * ct + il;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int orow = 32 * w + acc_row(r, lane);
           if (orow < dv && col < dk) {
-            const float s = seed_scale * acc[r];
-            P0[(size_t)orow * dk + col] = s;
-            Rn[(size_t)orow * dk + col] = s;
+            const float sv = seed_scale * acc[r];
+            P0[(size_t)orow * dk + col] = sv;
+            Rn[(size_t)orow * dk + col] = sv;
           }
         }
       }

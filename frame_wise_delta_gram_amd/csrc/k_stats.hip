@@ -4,17 +4,22 @@
 // for every (unit, frame), with the text tokens as a leading virtual frame
 // (Sec. 5, "Chunk-wise scans").  Both statistics come from ONE contraction
 // over the frame's tokens,
-//   [A_t ; B_t] = [K_t | V_t]^T (Diag(beta_t) K_t),
+//   [A_t ; B_t] = [X_t | Y_t]^T X_t,   X_t = Diag(sqrt(beta_t)) K_t,
+//                                      Y_t = Diag(sqrt(beta_t)) V_t,
 // so every K/V byte is read from HBM once ("in one pass, sharing input reads
-// and reduction work", Sec. 5).
+// and reduction work", Sec. 5).  Splitting beta as sqrt(beta) * sqrt(beta)
+// makes the computed A = X^T X positive semidefinite by construction even
+// after X is rounded to bf16, so I + A stays SPD with every eigenvalue >= 1
+// and ||(I + A)^{-1}||_2 <= 1 (Prop. 1) holds for the computed transition too.
 //
 // bf16 path: one workgroup (4 waves) per (unit, frame).  Tokens stream in
 // tiles of 64.  Each thread loads a 4-token x 8-channel block of K and of V
 // (16-byte coalesced loads: one wave instruction covers four whole 256-byte
-// rows), transposes it in registers to channel-major order, forms beta*K in
-// fp32 and rounds it to bf16, and writes the three channel-major tiles to LDS
-// with an XOR swizzle that keeps both the 8-byte staging writes and the
-// 16-byte MFMA operand reads free of bank conflicts.  The contraction runs on
+// rows), scales it by sqrt(beta) in fp32, rounds to bf16 and packs it in
+// channel-major order (the transposition happens in the packing), and writes
+// the two channel-major tiles to LDS with an XOR swizzle that keeps both the
+// 8-byte staging writes and the 16-byte MFMA operand reads free of bank
+// conflicts.  X serves as both MFMA operands of the A block.  The contraction runs on
 // v_mfma_f32_32x32x16_bf16 with fp32 accumulators held for the whole frame;
 // the next tile's global loads are in flight while the current one is
 // multiplied (two LDS stages).
@@ -29,9 +34,8 @@ namespace {
 
 constexpr int kTok = 64;                  // tokens per tile
 constexpr int kRowBytes = kTok * 2;       // one LDS row: 64 bf16 tokens of one channel
-constexpr int kXRows = 256;               // K channels in rows [0,128), V channels in [128,256)
-constexpr int kBRows = 128;               // beta-scaled K channels
-constexpr int kStageBytes = (kXRows + kBRows) * kRowBytes;  // 48 KiB
+constexpr int kXRows = 256;               // sqrt(beta) K channels in rows [0,128), sqrt(beta) V in [128,256)
+constexpr int kStageBytes = kXRows * kRowBytes;  // 32 KiB
 
 // Swizzle of a channel row: XOR applied to the 16-byte chunk index.  Rows r..r+7
 // (r a multiple of 8) get 8 distinct values (MFMA reads), and rows 8c+x for 8
@@ -46,7 +50,7 @@ __device__ __forceinline__ uint32_t off16(uint32_t row, uint32_t j) {
   return row * kRowBytes + ((j ^ swz(row)) << 4);
 }
 
-__global__ __launch_bounds__(256, 1) void stats_bf16_kernel(
+__global__ __launch_bounds__(256, 2) void stats_bf16_kernel(
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, const float* __restrict__ beta,
     const uint16_t* __restrict__ tk, const uint16_t* __restrict__ tv,
     const float* __restrict__ tb, float* __restrict__ Aout, float* __restrict__ Bout, int F, int U,
@@ -97,39 +101,29 @@ __global__ __launch_bounds__(256, 1) void stats_bf16_kernel(
       const u32x4_t z = {0u, 0u, 0u, 0u};
       kr[s] = (ok && kact) ? *reinterpret_cast<const u32x4_t*>(sk + (size_t)tok * dk + 8 * cg) : z;
       vr[s] = (ok && vact) ? *reinterpret_cast<const u32x4_t*>(sv + (size_t)tok * dv + 8 * cg) : z;
-      bb[s] = ok ? sb[tok] * bscale : 0.0f;
+      bb[s] = ok ? sqrtf(sb[tok] * bscale) : 0.0f;
     }
+  };
+
+  // channel c of the thread's 8-channel group, tokens 0..3: scale, round, pack
+  auto scaled_pair = [&](const u32x4_t* r, int c) {
+    const int p = c >> 1;
+    const bool hi = (c & 1) != 0;
+    float x[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) x[s] = (hi ? bf16_hi(r[s][p]) : bf16_lo(r[s][p])) * bb[s];
+    u32x2_t e;
+    e[0] = pack_bf16(x[0], x[1]);
+    e[1] = pack_bf16(x[2], x[3]);
+    return e;
   };
 
   auto write = [&](int stage) {
     unsigned char* X = smem + stage * kStageBytes;
-    unsigned char* BK = X + kXRows * kRowBytes;
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
-      const int p = c >> 1;
-      const bool hi = (c & 1) != 0;
-      if (kact) {
-        const uint32_t a0 = kr[0][p], a1 = kr[1][p], a2 = kr[2][p], a3 = kr[3][p];
-        u32x2_t d;
-        d[0] = hi ? ((a0 >> 16) | (a1 & 0xffff0000u)) : ((a0 & 0xffffu) | (a1 << 16));
-        d[1] = hi ? ((a2 >> 16) | (a3 & 0xffff0000u)) : ((a2 & 0xffffu) | (a3 << 16));
-        *reinterpret_cast<u32x2_t*>(X + off8(8 * cg + c, tg)) = d;
-        const float x0 = hi ? bf16_hi(a0) : bf16_lo(a0);
-        const float x1 = hi ? bf16_hi(a1) : bf16_lo(a1);
-        const float x2 = hi ? bf16_hi(a2) : bf16_lo(a2);
-        const float x3 = hi ? bf16_hi(a3) : bf16_lo(a3);
-        u32x2_t e;
-        e[0] = pack_bf16(x0 * bb[0], x1 * bb[1]);
-        e[1] = pack_bf16(x2 * bb[2], x3 * bb[3]);
-        *reinterpret_cast<u32x2_t*>(BK + off8(8 * cg + c, tg)) = e;
-      }
-      if (vact) {
-        const uint32_t a0 = vr[0][p], a1 = vr[1][p], a2 = vr[2][p], a3 = vr[3][p];
-        u32x2_t d;
-        d[0] = hi ? ((a0 >> 16) | (a1 & 0xffff0000u)) : ((a0 & 0xffffu) | (a1 << 16));
-        d[1] = hi ? ((a2 >> 16) | (a3 & 0xffff0000u)) : ((a2 & 0xffffu) | (a3 << 16));
-        *reinterpret_cast<u32x2_t*>(X + off8(128 + 8 * cg + c, tg)) = d;
-      }
+      if (kact) *reinterpret_cast<u32x2_t*>(X + off8(8 * cg + c, tg)) = scaled_pair(kr, c);
+      if (vact) *reinterpret_cast<u32x2_t*>(X + off8(128 + 8 * cg + c, tg)) = scaled_pair(vr, c);
     }
   };
 
@@ -153,7 +147,6 @@ __global__ __launch_bounds__(256, 1) void stats_bf16_kernel(
 
   auto compute = [&](int stage) {
     const unsigned char* X = smem + stage * kStageBytes;
-    const unsigned char* BK = X + kXRows * kRowBytes;
     const int il = lane & 31;
     const int kh = lane >> 5;
 #pragma unroll
@@ -162,7 +155,7 @@ __global__ __launch_bounds__(256, 1) void stats_bf16_kernel(
       u32x4_t b[4];
 #pragma unroll
       for (int ct = 0; ct < 4; ++ct)
-        if (ct < nK) b[ct] = *reinterpret_cast<const u32x4_t*>(BK + off16(32 * ct + il, j));
+        if (ct < nK) b[ct] = *reinterpret_cast<const u32x4_t*>(X + off16(32 * ct + il, j));
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
         if (!ract[i]) continue;
@@ -210,7 +203,8 @@ __global__ __launch_bounds__(256, 1) void stats_bf16_kernel(
   }
 }
 
-// fp32 features: the same contraction on the vector ALUs.
+// fp32 features: the same contraction, [sqrt(b) K | sqrt(b) V]^T (sqrt(b) K), on
+// the vector ALUs.
 constexpr int kTokF = 32;
 constexpr int kXS = 257;  // LDS row stride (floats) of the token tile [K | V]
 constexpr int kBS = 129;
@@ -260,12 +254,12 @@ __global__ __launch_bounds__(256) void stats_f32_kernel(
       const int ch = idx & 127;
       const int tok = base + s;
       const bool ok = tok < ntok;
-      const float kv = (ok && ch < dk) ? sk[(size_t)tok * dk + ch] : 0.0f;
-      const float vv = (ok && ch < dv) ? sv[(size_t)tok * dv + ch] : 0.0f;
-      const float bv = ok ? sb[tok] * bscale : 0.0f;
+      const float rb_ = ok ? sqrtf(sb[tok] * bscale) : 0.0f;
+      const float kv = (ok && ch < dk) ? sk[(size_t)tok * dk + ch] * rb_ : 0.0f;
+      const float vv = (ok && ch < dv) ? sv[(size_t)tok * dv + ch] * rb_ : 0.0f;
       Xs[s * kXS + ch] = kv;
       Xs[s * kXS + 128 + ch] = vv;
-      Bs[s * kBS + ch] = kv * bv;
+      Bs[s * kBS + ch] = kv;
     }
     __syncthreads();
     for (int s = 0; s < kTokF; ++s) {

@@ -103,3 +103,57 @@ __device__ __forceinline__ void store_acc(float* C, int sc, const f32x16_t& acc,
 }
 
 }  // namespace vda
+
+namespace vda {
+
+// Register half of an LDS fill: a thread's share (16 float4) of a row-major
+// fp32 matrix with `rows` x `cols` valid entries (leading dimension ld, cols
+// a multiple of 4, both <= 128), optionally plus a second matrix of the same
+// shape.  All loads are issued before any value is used, so one memory
+// latency covers the whole matrix; entries outside the valid range are 0.
+struct MatRegs {
+  f32x4_t v[16];
+};
+
+__device__ __forceinline__ void mat_load(MatRegs& m, const float* src, int ld, int rows, int cols,
+                                         const float* add = nullptr) {
+  const f32x4_t z = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int id = threadIdx.x + 256 * i;
+    const int r = id >> 5;
+    const int c = (id & 31) << 2;
+    const bool ok = r < rows && c < cols;
+    m.v[i] = ok ? *reinterpret_cast<const f32x4_t*>(src + (size_t)r * ld + c) : z;
+  }
+  if (add) {
+    f32x4_t a[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int id = threadIdx.x + 256 * i;
+      const int r = id >> 5;
+      const int c = (id & 31) << 2;
+      const bool ok = r < rows && c < cols;
+      a[i] = ok ? *reinterpret_cast<const f32x4_t*>(add + (size_t)r * ld + c) : z;
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) m.v[i] += a[i];
+  }
+}
+
+// LDS half: write the registers into an R x C region (row stride sdst) of LDS.
+__device__ __forceinline__ void mat_store_lds(const MatRegs& m, float* dst, int sdst, int R,
+                                              int C) {
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int id = threadIdx.x + 256 * i;
+    const int r = id >> 5;
+    const int c = (id & 31) << 2;
+    if (r < R && c < C) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) dst[r * sdst + c + e] = m.v[i][e];
+    }
+  }
+}
+
+}  // namespace vda
