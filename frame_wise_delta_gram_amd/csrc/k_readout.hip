@@ -33,12 +33,17 @@ namespace {
 constexpr int kIters = 8;                 // 32-row blocks per wave
 constexpr int kRows = 4 * 32 * kIters;    // token rows per workgroup
 
+// DK, DV > 0: compile-time d_k and d_v (the common 128 case); 0: runtime.
+template <int DK, int DV>
 __global__ __launch_bounds__(256, 2) void readout_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ gate,
     const float* __restrict__ wrms, uint16_t* __restrict__ out, const float* __restrict__ ST,
-    int dk, int dv, int F, int U, int C, int radius, int n, float eps) {
+    int dk_rt, int dv_rt, int F, int U, int C, int radius, int n, float eps) {
+  const int dk = DK > 0 ? DK : dk_rt;
+  const int dv = DV > 0 ? DV : dv_rt;
   __shared__ __align__(16) uint16_t Shi[128 * 136];
   __shared__ __align__(16) uint16_t Slo[128 * 136];
+  __shared__ __align__(16) float Ws[128];  // RMSNorm weight (LDS: its reads use lgkmcnt, not vmcnt)
 
   const int blk = blockIdx.x;
   const int c = blockIdx.y;
@@ -59,6 +64,7 @@ __global__ __launch_bounds__(256, 2) void readout_bf16_kernel(
   const int halfk = dk >> 1;   // input channels per lane half
   const int NKS = dk >> 4;     // k-steps of 16 channels
 
+  for (int i = t; i < 128; i += 256) Ws[i] = i < dv ? wrms[i] : 0.0f;
   // gather S~ and split it into bf16 hi + lo, rows permuted (see header)
   {
     const size_t SS = (size_t)dv * dk;
@@ -67,7 +73,26 @@ __global__ __launch_bounds__(256, 2) void readout_bf16_kernel(
     const float* P = ST + ((size_t)(u * 2 + 0) * (n + 1) + pi) * SS;
     const float* R = ST + ((size_t)(u * 2 + 1) * (n + 1) + ri) * SS;
     const int k8n = dk >> 3;
-    for (int it = t; it < Dvp * k8n; it += 256) {
+    const int items = Dvp * k8n;  // <= 2048 = 8 per thread
+    f32x4_t pv[8][2], rv[8][2];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {  // issue every load first
+      const int it = t + 256 * i;
+      const int ch = it / k8n;
+      const int k8 = it - ch * k8n;
+      const f32x4_t z = {0.0f, 0.0f, 0.0f, 0.0f};
+      const bool ok = it < items && ch < dv;
+      const f32x4_t* pp = reinterpret_cast<const f32x4_t*>(P + (size_t)(ok ? ch : 0) * dk + 8 * k8);
+      const f32x4_t* rp = reinterpret_cast<const f32x4_t*>(R + (size_t)(ok ? ch : 0) * dk + 8 * k8);
+      pv[i][0] = ok ? pp[0] : z;
+      pv[i][1] = ok ? pp[1] : z;
+      rv[i][0] = ok ? rp[0] : z;
+      rv[i][1] = ok ? rp[1] : z;
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int it = t + 256 * i;
+      if (it >= items) continue;
       const int ch = it / k8n;
       const int k8 = it - ch * k8n;
       const int h = ch / HALF;
@@ -75,23 +100,18 @@ __global__ __launch_bounds__(256, 2) void readout_bf16_kernel(
       const int T = rem >> 4;
       const int rr = rem & 15;
       const int lrow = 32 * T + 8 * (rr >> 2) + 4 * h + (rr & 3);
-      u32x4_t hi = {0u, 0u, 0u, 0u}, lo = {0u, 0u, 0u, 0u};
-      if (ch < dv) {
-        const f32x4_t* pp = reinterpret_cast<const f32x4_t*>(P + (size_t)ch * dk + 8 * k8);
-        const f32x4_t* rp = reinterpret_cast<const f32x4_t*>(R + (size_t)ch * dk + 8 * k8);
-        const f32x4_t p0 = pp[0], p1 = pp[1], r0 = rp[0], r1 = rp[1];
-        float x[8];
+      float x[8];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          x[e] = p0[e] + r0[e];
-          x[4 + e] = p1[e] + r1[e];
-        }
+      for (int e = 0; e < 4; ++e) {
+        x[e] = pv[i][0][e] + rv[i][0][e];
+        x[4 + e] = pv[i][1][e] + rv[i][1][e];
+      }
+      u32x4_t hi, lo;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const uint32_t hp = pack_bf16(x[2 * e], x[2 * e + 1]);
-          hi[e] = hp;
-          lo[e] = pack_bf16(x[2 * e] - bf16_lo(hp), x[2 * e + 1] - bf16_hi(hp));
-        }
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t hp = pack_bf16(x[2 * e], x[2 * e + 1]);
+        hi[e] = hp;
+        lo[e] = pack_bf16(x[2 * e] - bf16_lo(hp), x[2 * e + 1] - bf16_hi(hp));
       }
       *reinterpret_cast<u32x4_t*>(Shi + lrow * SROW + 8 * k8) = hi;
       *reinterpret_cast<u32x4_t*>(Slo + lrow * SROW + 8 * k8) = lo;
@@ -105,34 +125,32 @@ __global__ __launch_bounds__(256, 2) void readout_bf16_kernel(
   const float inv_dv = 1.0f / (float)dv;
   const u32x4_t z4 = {0u, 0u, 0u, 0u};
 
-  // software pipeline over this wave's 32-row blocks: the next block's queries
-  // and the current block's gate logits are in flight during the MFMAs
-  auto load_q = [&](u32x4_t (&qr)[8], long rb) {
-    const long myrow = rb + il;
-    const bool valid = rb < rows_total && myrow < rows_total;
-    const uint16_t* qp = q + (chunk_row0 + (size_t)(valid ? myrow : 0)) * dk + g * halfk;
+  // Software pipeline over this wave's 32-row blocks.  At block `it` the gate
+  // logits and then the queries of block it + 1 are issued before the MFMAs of
+  // block it; vmcnt retires in issue order, so using block it's registers never
+  // waits for block it + 1's loads, and the stores of block it follow them.
+  // Loads are unconditional from clamped, valid addresses (rows past the chunk's
+  // end reread its last row, padding channels reread the first group); those
+  // rows are never stored and padding channels never reach an output.
+  const int last_m = max((min(HALF, dv - g * HALF) >> 3) - 1, 0);  // last valid 8-channel group
+  auto load_blk = [&](u32x4_t (&qr)[8], u32x4_t (&gr)[8], long rb) {
+    const long myrow = min(rb + il, rows_total - 1);
+    const size_t grow = chunk_row0 + (size_t)myrow;
+    const uint16_t* gp = gate + grow * dv + (g * HALF < dv ? g * HALF : 0);
+#pragma unroll
+    for (int m = 0; m < 8; ++m)
+      gr[m] = *reinterpret_cast<const u32x4_t*>(gp + 8 * min(m, last_m));
+    const uint16_t* qp = q + grow * dk + g * halfk;
 #pragma unroll
     for (int s = 0; s < 8; ++s)
-      qr[s] = (s < NKS && valid) ? *reinterpret_cast<const u32x4_t*>(qp + 8 * s) : z4;
+      qr[s] = *reinterpret_cast<const u32x4_t*>(qp + 8 * min(s, NKS - 1));
   };
-  u32x4_t qcur[8], qnext[8];
-  load_q(qcur, row0 + (long)w * 32);
-
-  for (int it = 0; it < kIters; ++it) {
-    const long rb = row0 + (long)(it * 4 + w) * 32;
-    if (rb >= rows_total) break;
-    if (it + 1 < kIters) load_q(qnext, row0 + (long)((it + 1) * 4 + w) * 32);
+  // one 32-row block: MFMAs on (qr, gr) loaded one block earlier, then the
+  // RMSNorm/gate epilogue and the stores
+  auto process = [&](const u32x4_t (&qr)[8], const u32x4_t (&gr)[8], long rb) {
     const long myrow = rb + il;
     const bool valid = myrow < rows_total;
     const size_t grow = chunk_row0 + (size_t)(valid ? myrow : 0);
-    u32x4_t gv[8];
-    {
-      const uint16_t* gp = gate + grow * dv + g * HALF;
-#pragma unroll
-      for (int m = 0; m < 8; ++m)
-        gv[m] = (valid && 8 * m < HALF && g * HALF + 8 * m < dv)
-                    ? *reinterpret_cast<const u32x4_t*>(gp + 8 * m) : z4;
-    }
     f32x16_t acc[4];
 #pragma unroll
     for (int T = 0; T < 4; ++T) acc[T] = zero16();
@@ -145,8 +163,8 @@ __global__ __launch_bounds__(256, 2) void readout_bf16_kernel(
         const int off = (32 * T + il) * SROW + g * halfk + 8 * s;
         const u32x4_t ah = *reinterpret_cast<const u32x4_t*>(Shi + off);
         const u32x4_t al = *reinterpret_cast<const u32x4_t*>(Slo + off);
-        acc[T] = mfma_bf16(ah, qcur[s], acc[T]);
-        acc[T] = mfma_bf16(al, qcur[s], acc[T]);
+        acc[T] = mfma_bf16(ah, qr[s], acc[T]);
+        acc[T] = mfma_bf16(al, qr[s], acc[T]);
       }
     }
 
@@ -161,7 +179,7 @@ __global__ __launch_bounds__(256, 2) void readout_bf16_kernel(
 
     if (valid) {
       uint16_t* op = out + grow * dv + g * HALF;
-      const float* wp = wrms + g * HALF;
+      const float* wp = Ws + g * HALF;
 #pragma unroll
       for (int m = 0; m < 8; ++m) {
         if (8 * m >= HALF || g * HALF + 8 * m >= dv) continue;
@@ -172,9 +190,9 @@ __global__ __launch_bounds__(256, 2) void readout_bf16_kernel(
         for (int e = 0; e < 8; ++e) {
           const int idx = 8 * m + e;
           const float o = acc[idx >> 4][idx & 15];
-          const float gl = (e & 1) ? bf16_hi(gv[m][e >> 1]) : bf16_lo(gv[m][e >> 1]);
+          const float gl = (e & 1) ? bf16_hi(gr[m][e >> 1]) : bf16_lo(gr[m][e >> 1]);
           const float ww = e < 4 ? w0[e] : w1[e - 4];
-          const float sig = 1.0f / (1.0f + __expf(-gl));
+          const float sig = __builtin_amdgcn_rcpf(1.0f + __expf(-gl));
           y[e] = o * inv * ww * sig;
         }
         u32x4_t ov;
@@ -183,8 +201,19 @@ __global__ __launch_bounds__(256, 2) void readout_bf16_kernel(
         *reinterpret_cast<u32x4_t*>(op + 8 * m) = ov;
       }
     }
-#pragma unroll
-    for (int s = 0; s < 8; ++s) qcur[s] = qnext[s];
+  };
+
+  // ping-pong register sets, unrolled by two (no register copies between blocks)
+  u32x4_t q0[8], g0[8], q1[8], g1[8];
+  auto blk_row = [&](int it) { return row0 + (long)(it * 4 + w) * 32; };
+  load_blk(q0, g0, blk_row(0));
+  for (int it = 0; it < kIters; it += 2) {
+    if (blk_row(it) >= rows_total) break;
+    if (it + 1 < kIters) load_blk(q1, g1, blk_row(it + 1));
+    process(q0, g0, blk_row(it));
+    if (it + 1 >= kIters || blk_row(it + 1) >= rows_total) break;
+    if (it + 2 < kIters) load_blk(q0, g0, blk_row(it + 2));
+    process(q1, g1, blk_row(it + 1));
   }
 }
 
@@ -263,7 +292,9 @@ hipError_t launch_readout(const Plan& p, const void* q, const void* gate, const 
   if (max_rows == 0) return hipSuccess;
   if (p.dtype == VDA_DTYPE_BF16) {
     const dim3 grid((unsigned)((max_rows + kRows - 1) / kRows), p.n, p.units);
-    hipLaunchKernelGGL(readout_bf16_kernel, grid, dim3(kThreads), 0, s,
+    auto kern = (p.dk == 128 && p.dv == 128) ? readout_bf16_kernel<128, 128>
+                                             : readout_bf16_kernel<0, 0>;
+    hipLaunchKernelGGL(kern, grid, dim3(kThreads), 0, s,
                        static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(gate),
                        rms_weight, static_cast<uint16_t*>(out), w.ST, p.dk, p.dv, p.F, p.U, p.C,
                        p.r, p.n, p.eps);

@@ -35,7 +35,9 @@ __device__ __forceinline__ float readlane_f(float x, int l) {
 }
 
 // Factor the 32x32 SPD block at G (stride SG) as L L^T and overwrite it with
-// W = L^{-1} (lower triangular, zeros above the diagonal), by one wave.
+// W = L^{-1} (lower triangular, zeros above the diagonal), by one wave.  The
+// pivots of I + A and of its Schur complements are >= 1, so the hardware
+// reciprocal square root (1 ulp) is safe.
 __device__ void factor_invert_diag_block(float* G) {
   const int lane = lane_id();
   const int c = lane & 31;  // lanes 32..63 duplicate lanes 0..31 and do not store
@@ -43,37 +45,41 @@ __device__ void factor_invert_diag_block(float* G) {
 #pragma unroll
   for (int k = 0; k < 32; ++k) col[k] = G[k * SG + c];  // column c (= row c)
 
+  float rinv[32];  // 1 / L[j][j]
 #pragma unroll
   for (int j = 0; j < 32; ++j) {
-    const float piv = sqrtf(readlane_f(col[j], j));
-    const float inv = 1.0f / piv;
+    const float d = readlane_f(col[j], j);
+    const float inv = __builtin_amdgcn_rsqf(d);
+    rinv[j] = inv;
     // lanes c > j: L[c][j] = D[c][j] / piv (own copy, the block is symmetric);
     // t = L[c][j] / piv so that D[k][c] -= L[k][j] L[c][j] = D[k][j] * t
-    const float t = col[j] * inv * inv;
+    const float t = col[j] * (inv * inv);
 #pragma unroll
     for (int k = j + 1; k < 32; ++k) {
       const float dkj = readlane_f(col[j], k);  // D[k][j] = D[j][k], held by lane k
       if (c > j) col[k] = fmaf(-dkj, t, col[k]);
     }
     if (c == j) {
-      col[j] = piv;
+      col[j] = d * inv;
 #pragma unroll
       for (int k = j + 1; k < 32; ++k) col[k] *= inv;
     }
   }
-  // col[k] = L[k][c] for k >= c.  Column c of W: forward substitution L w = e_c,
-  // w[i] = (delta_ic - sum_{k<i} L[i][k] w[k]) / L[i][i]; L[i][k] sits in lane k.
-  float wv[32];
+  // col[k] = L[k][c] for k >= c.  Column c of W = L^{-1}: solve L x = e_c
+  // right-looking, x[j] /= L[j][j] then x[i] -= L[i][j] x[j] for i > j (the
+  // updates of one step are independent); L[i][j] sits in lane j.
+  float x[32];
 #pragma unroll
-  for (int i = 0; i < 32; ++i) {
-    float s = (i == c) ? 1.0f : 0.0f;
+  for (int k = 0; k < 32; ++k) x[k] = (k == c) ? 1.0f : 0.0f;
 #pragma unroll
-    for (int k = 0; k < i; ++k) s = fmaf(-readlane_f(col[i], k), wv[k], s);
-    wv[i] = s / readlane_f(col[i], i);
+  for (int j = 0; j < 32; ++j) {
+    x[j] *= rinv[j];
+#pragma unroll
+    for (int i = j + 1; i < 32; ++i) x[i] = fmaf(-readlane_f(col[i], j), x[j], x[i]);
   }
   if (lane < 32) {
 #pragma unroll
-    for (int k = 0; k < 32; ++k) G[k * SG + c] = wv[k];
+    for (int k = 0; k < 32; ++k) G[k * SG + c] = x[k];
   }
 }
 

@@ -12,17 +12,17 @@
 // after X is rounded to bf16, so I + A stays SPD with every eigenvalue >= 1
 // and ||(I + A)^{-1}||_2 <= 1 (Prop. 1) holds for the computed transition too.
 //
-// bf16 path: one workgroup (4 waves) per (unit, frame).  Tokens stream in
-// tiles of 64.  Each thread loads a 4-token x 8-channel block of K and of V
-// (16-byte coalesced loads: one wave instruction covers four whole 256-byte
-// rows), scales it by sqrt(beta) in fp32, rounds to bf16 and packs it in
+// bf16 path: one workgroup (8 waves) per (unit, frame); wave w owns output
+// row tile w of [A; B].  Tokens stream in tiles of 128.  Each thread loads a
+// 4-token x 8-channel block of K and of V (16-byte coalesced loads: one wave
+// instruction covers four whole 256-byte rows), scales it by sqrt(beta) in fp32, rounds to bf16 and packs it in
 // channel-major order (the transposition happens in the packing), and writes
 // the two channel-major tiles to LDS with an XOR swizzle that keeps both the
 // 8-byte staging writes and the 16-byte MFMA operand reads free of bank
 // conflicts.  X serves as both MFMA operands of the A block.  The contraction runs on
 // v_mfma_f32_32x32x16_bf16 with fp32 accumulators held for the whole frame;
-// the next tile's global loads are in flight while the current one is
-// multiplied (two LDS stages).
+// the global loads of the next two tiles are in flight while the current one
+// is multiplied (two register sets, two LDS stages).
 //
 // fp32 path: the same contraction in fp32 on the vector ALUs (exact fp32
 // products, fp32 accumulation) for fp32 features.
@@ -32,15 +32,21 @@
 namespace vda {
 namespace {
 
-constexpr int kTok = 64;                  // tokens per tile
-constexpr int kRowBytes = kTok * 2;       // one LDS row: 64 bf16 tokens of one channel
+constexpr int kTok = 128;                 // tokens per tile
+constexpr int kStatsThreads = 512;        // 8 waves
+constexpr int kRowBytes = kTok * 2;       // one LDS row: 128 bf16 tokens of one channel
 constexpr int kXRows = 256;               // sqrt(beta) K channels in rows [0,128), sqrt(beta) V in [128,256)
 constexpr int kStageBytes = kXRows * kRowBytes;  // 32 KiB
 
-// Swizzle of a channel row: XOR applied to the 16-byte chunk index.  Rows r..r+7
-// (r a multiple of 8) get 8 distinct values (MFMA reads), and rows 8c+x for 8
-// consecutive c get 8 distinct values (staging writes).
-__device__ __forceinline__ uint32_t swz(uint32_t row) { return (row & 7) ^ ((row >> 3) & 7); }
+// Swizzle of a channel row: XOR (< 16) applied to the 16-byte chunk index (a
+// row is 256 bytes = 16 chunks, so rows alias in banks).  Rows r..r+15 (r a
+// multiple of 16) get 16 distinct values: the 16 lanes of an MFMA operand read
+// that the LDS serves together hit 16 different chunks.  Rows 8c+x for 16
+// consecutive c get 16 distinct values: the 32 lanes of a staging write (two
+// 8-byte slots per chunk) hit 32 different slots.  Any 8 consecutive rows also
+// get distinct low 3 bits, so the pattern stays conflict-free when the LDS
+// serves 8 lanes of 16 bytes or 16 lanes of 8 bytes per pass.
+__device__ __forceinline__ uint32_t swz(uint32_t row) { return (row & 15) ^ ((row >> 3) & 15); }
 // byte offset of the 8-byte slot `slot` (tokens 4*slot..4*slot+3) of `row`
 __device__ __forceinline__ uint32_t off8(uint32_t row, uint32_t slot) {
   return row * kRowBytes + ((slot ^ (swz(row) << 1)) << 3);
@@ -50,11 +56,15 @@ __device__ __forceinline__ uint32_t off16(uint32_t row, uint32_t j) {
   return row * kRowBytes + ((j ^ swz(row)) << 4);
 }
 
-__global__ __launch_bounds__(256, 2) void stats_bf16_kernel(
+// DK, DV > 0: compile-time d_k and d_v (the common 128 case); 0: runtime.
+template <int DK, int DV>
+__global__ __launch_bounds__(512, 1) void stats_bf16_kernel(
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, const float* __restrict__ beta,
     const uint16_t* __restrict__ tk, const uint16_t* __restrict__ tv,
     const float* __restrict__ tb, float* __restrict__ Aout, float* __restrict__ Bout, int F, int U,
-    int T, int dk, int dv, float text_scale) {
+    int T, int dk_rt, int dv_rt, float text_scale) {
+  const int dk = DK > 0 ? DK : dk_rt;
+  const int dv = DV > 0 ? DV : dv_rt;
   __shared__ __align__(16) unsigned char smem[2 * kStageBytes];
 
   const int fi = blockIdx.x;  // 0 = text frame, f + 1 = latent frame f
@@ -89,104 +99,114 @@ __global__ __launch_bounds__(256, 2) void stats_bf16_kernel(
   const bool kact = cg * 8 < dk;
   const bool vact = cg * 8 < dv;
 
-  u32x4_t kr[4], vr[4];
-  float bb[4];
+  // one tile's worth of this thread's raw inputs (16-byte bf16 vectors).  The
+  // loads are unconditional from clamped, always valid addresses and nothing
+  // uses their values until write(): vmcnt retires in issue order, so a tile's
+  // loads stay in flight behind later work.  Tokens past the frame's end get
+  // write strength 0 in write().
+  struct TileRegs {
+    u32x4_t k[4], v[4];
+    float b[4];  // beta of the 4 tokens
+    int tok0;    // first token of the thread's group
+  };
+  const int kcg = kact ? cg : 0;
+  const int vcg = vact ? cg : 0;
+  const int last_tok = ntok > 0 ? ntok - 1 : 0;
 
-  auto load = [&](int tile) {
-    const int base = tile * kTok + 4 * tg;
+  auto load = [&](TileRegs& r, int tile) {
+    r.tok0 = tile * kTok + 4 * tg;
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      const int tok = base + s;
-      const bool ok = tok < ntok;
-      const u32x4_t z = {0u, 0u, 0u, 0u};
-      kr[s] = (ok && kact) ? *reinterpret_cast<const u32x4_t*>(sk + (size_t)tok * dk + 8 * cg) : z;
-      vr[s] = (ok && vact) ? *reinterpret_cast<const u32x4_t*>(sv + (size_t)tok * dv + 8 * cg) : z;
-      bb[s] = ok ? sqrtf(sb[tok] * bscale) : 0.0f;
+      const int tok = min(r.tok0 + s, last_tok);
+      r.k[s] = *reinterpret_cast<const u32x4_t*>(sk + (size_t)tok * dk + 8 * kcg);
+      r.v[s] = *reinterpret_cast<const u32x4_t*>(sv + (size_t)tok * dv + 8 * vcg);
+      r.b[s] = sb[tok];
     }
   };
 
   // channel c of the thread's 8-channel group, tokens 0..3: scale, round, pack
-  auto scaled_pair = [&](const u32x4_t* r, int c) {
+  auto scaled_pair = [&](const u32x4_t* x4, const float* b, int c) {
     const int p = c >> 1;
     const bool hi = (c & 1) != 0;
     float x[4];
 #pragma unroll
-    for (int s = 0; s < 4; ++s) x[s] = (hi ? bf16_hi(r[s][p]) : bf16_lo(r[s][p])) * bb[s];
+    for (int s = 0; s < 4; ++s) x[s] = (hi ? bf16_hi(x4[s][p]) : bf16_lo(x4[s][p])) * b[s];
+    // b[s] is exactly 0 for tokens past the end; select (not multiply) so that
+    // a non-finite value in the clamped row cannot leak in
+#pragma unroll
+    for (int s = 0; s < 4; ++s) x[s] = b[s] != 0.0f ? x[s] : 0.0f;
     u32x2_t e;
     e[0] = pack_bf16(x[0], x[1]);
     e[1] = pack_bf16(x[2], x[3]);
     return e;
   };
 
-  auto write = [&](int stage) {
+  auto write = [&](const TileRegs& r, int stage) {
     unsigned char* X = smem + stage * kStageBytes;
+    float sb4[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) sb4[s] = r.tok0 + s < ntok ? sqrtf(r.b[s] * bscale) : 0.0f;
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
-      if (kact) *reinterpret_cast<u32x2_t*>(X + off8(8 * cg + c, tg)) = scaled_pair(kr, c);
-      if (vact) *reinterpret_cast<u32x2_t*>(X + off8(128 + 8 * cg + c, tg)) = scaled_pair(vr, c);
+      if (kact) *reinterpret_cast<u32x2_t*>(X + off8(8 * cg + c, tg)) = scaled_pair(r.k, sb4, c);
+      if (vact) *reinterpret_cast<u32x2_t*>(X + off8(128 + 8 * cg + c, tg)) = scaled_pair(r.v, sb4, c);
     }
   };
 
-  // contraction role: this wave owns output row tiles w and w + 4 of [A; B]
+  // contraction role: wave w owns output row tile w of [A; B]
   const int nK = pad32(dk) >> 5;
   const int nV = pad32(dv) >> 5;
   const int nR = nK + nV;
-  bool ract[2];
-  int rbase[2];
+  const bool ract = w < nR;
+  const int rbase = w < nK ? 32 * w : 128 + 32 * (w - nK);
+  f32x16_t acc[4];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int rt = w + 4 * i;
-    ract[i] = rt < nR;
-    rbase[i] = rt < nK ? 32 * rt : 128 + 32 * (rt - nK);
-  }
-  f32x16_t acc[2][4];
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int ct = 0; ct < 4; ++ct) acc[i][ct] = zero16();
+  for (int ct = 0; ct < 4; ++ct) acc[ct] = zero16();
 
   auto compute = [&](int stage) {
+    if (!ract) return;
     const unsigned char* X = smem + stage * kStageBytes;
     const int il = lane & 31;
     const int kh = lane >> 5;
-#pragma unroll
+#pragma unroll 2
     for (int kk = 0; kk < kTok / 16; ++kk) {
       const int j = 2 * kk + kh;  // tokens 16 kk + 8 kh .. + 7
-      u32x4_t b[4];
+      const u32x4_t a = *reinterpret_cast<const u32x4_t*>(X + off16(rbase + il, j));
 #pragma unroll
-      for (int ct = 0; ct < 4; ++ct)
-        if (ct < nK) b[ct] = *reinterpret_cast<const u32x4_t*>(X + off16(32 * ct + il, j));
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        if (!ract[i]) continue;
-        const u32x4_t a = *reinterpret_cast<const u32x4_t*>(X + off16(rbase[i] + il, j));
-#pragma unroll
-        for (int ct = 0; ct < 4; ++ct)
-          if (ct < nK) acc[i][ct] = mfma_bf16(a, b[ct], acc[i][ct]);
+      for (int ct = 0; ct < 4; ++ct) {
+        if (ct < nK) {
+          const u32x4_t b = *reinterpret_cast<const u32x4_t*>(X + off16(32 * ct + il, j));
+          acc[ct] = mfma_bf16(a, b, acc[ct]);
+        }
       }
     }
   };
 
+  // Two register sets in flight: a tile's loads are issued two multiply phases
+  // before its registers are written to LDS.
   const int ntiles = (ntok + kTok - 1) / kTok;
-  if (ntiles > 0) {
-    load(0);
-    write(0);
-  }
-  for (int it = 0; it < ntiles; ++it) {
-    if (it + 1 < ntiles) load(it + 1);
+  TileRegs ra, rb;
+  if (ntiles > 0) load(ra, 0);
+  if (ntiles > 1) load(rb, 1);
+  if (ntiles > 0) write(ra, 0);
+  for (int it = 0; it < ntiles; it += 2) {
+    // LDS stage 0 holds tile it; rb holds tile it + 1
+    if (it + 2 < ntiles) load(ra, it + 2);
     __syncthreads();
-    compute(it & 1);
-    if (it + 1 < ntiles) write((it + 1) & 1);
+    compute(0);
+    if (it + 1 >= ntiles) break;
+    write(rb, 1);
+    if (it + 3 < ntiles) load(rb, it + 3);
+    __syncthreads();
+    compute(1);
+    if (it + 2 < ntiles) write(ra, 0);
   }
 
   // results: rows of A (K tiles) or B (V tiles), columns are key channels
-  const size_t fr = (size_t)u * (F + 1) + fi;
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    if (!ract[i]) continue;
-    const int rt = w + 4 * i;
-    const bool isA = rt < nK;
-    const int ch0 = isA ? 32 * rt : 32 * (rt - nK);
+  if (ract) {
+    const size_t fr = (size_t)u * (F + 1) + fi;
+    const bool isA = w < nK;
+    const int ch0 = isA ? 32 * w : 32 * (w - nK);
     const int nrows = isA ? dk : dv;
     float* dst = isA ? Aout + fr * dk * dk : Bout + fr * dv * dk;
 #pragma unroll
@@ -197,7 +217,7 @@ __global__ __launch_bounds__(256, 2) void stats_bf16_kernel(
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int row = ch0 + acc_row(r, lane);
-        if (row < nrows) dst[(size_t)row * dk + col] = acc[i][ct][r];
+        if (row < nrows) dst[(size_t)row * dk + col] = acc[ct][r];
       }
     }
   }
@@ -300,7 +320,8 @@ hipError_t launch_stats(const Plan& p, const void* k, const void* v, const float
   const dim3 grid(p.F + 1, p.units);
   const float ts = p.seed_mode == 1 ? 0.5f : 1.0f;
   if (p.dtype == VDA_DTYPE_BF16) {
-    hipLaunchKernelGGL(stats_bf16_kernel, grid, dim3(kThreads), 0, s,
+    auto kern = (p.dk == 128 && p.dv == 128) ? stats_bf16_kernel<128, 128> : stats_bf16_kernel<0, 0>;
+    hipLaunchKernelGGL(kern, grid, dim3(kStatsThreads), 0, s,
                        static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), beta,
                        static_cast<const uint16_t*>(text_k), static_cast<const uint16_t*>(text_v),
                        text_beta, w.A, w.B, p.F, p.U, p.T, p.dk, p.dv, ts);

@@ -56,7 +56,7 @@ int make_plan(const vda_desc_t* d, Plan* p) {
 
   const size_t U_ = (size_t)p->units, Fp1 = (size_t)p->F + 1, N = (size_t)p->n;
   const size_t kk = (size_t)p->dk * p->dk * 4, vk = (size_t)p->dv * p->dk * 4;
-  size_t sz[7];
+  size_t sz[8];
   sz[0] = U_ * Fp1 * kk;          // A
   sz[1] = U_ * Fp1 * vk;          // B
   sz[2] = U_ * Fp1 * kk;          // M
@@ -64,10 +64,11 @@ int make_plan(const vda_desc_t* d, Plan* p) {
   sz[4] = U_ * N * vk;            // Jf
   sz[5] = U_ * N * vk;            // Jr
   sz[6] = U_ * 2 * (N + 1) * vk;  // ST
+  sz[7] = U_ * N * kk;            // McT
   if (p->units == 0 || p->F == 0)
     for (size_t& s : sz) s = 0;
   size_t off = 0;
-  for (int i = 0; i < 7; ++i) {
+  for (int i = 0; i < 8; ++i) {
     p->off[i] = off;
     off += align256(sz[i]);
   }
@@ -85,6 +86,7 @@ WsPtrs carve(const Plan& p, void* ws) {
   w.Jf = reinterpret_cast<float*>(b + p.off[4]);
   w.Jr = reinterpret_cast<float*>(b + p.off[5]);
   w.ST = reinterpret_cast<float*>(b + p.off[6]);
+  w.McT = reinterpret_cast<float*>(b + p.off[7]);
   return w;
 }
 

@@ -14,6 +14,7 @@ namespace vda {
 //   B  [units][F + 1][d_v][d_k]
 //   M  [units][F + 1][d_k][d_k]   transitions (I + A)^{-1}
 //   Mc [units][n][d_k][d_k]       chunk transitions (forward order)
+//   McT [units][n][d_k][d_k]      the same, transposed (rows = columns of Mc)
 //   Jf [units][n][d_v][d_k]       chunk injections, forward
 //   Jr [units][n][d_v][d_k]       chunk injections, reverse
 //   ST [units][2][n + 1][d_v][d_k] boundary states: [0] = P (forward), [1] = R (reverse)
@@ -21,19 +22,19 @@ struct Plan {
   int units, F, U, T, dk, dv, C, r, n;
   float eps;
   int seed_mode, dtype;
-  size_t off[7];
+  size_t off[8];
   size_t total;
 };
 
 struct WsPtrs {
-  float *A, *B, *M, *Mc, *Jf, *Jr, *ST;
+  float *A, *B, *M, *Mc, *Jf, *Jr, *ST, *McT;
 };
 
 hipError_t launch_stats(const Plan& p, const void* k, const void* v, const float* beta,
                         const void* text_k, const void* text_v, const float* text_beta,
                         const WsPtrs& w, hipStream_t s);
 hipError_t launch_solve(const Plan& p, const WsPtrs& w, hipStream_t s);
-hipError_t launch_compose(const Plan& p, const WsPtrs& w, hipStream_t s);
+hipError_t launch_compose(const Plan& p, const WsPtrs& w, hipStream_t s);  // Mc, McT, Jf, Jr
 hipError_t launch_scan(const Plan& p, const WsPtrs& w, hipStream_t s);
 hipError_t launch_readout(const Plan& p, const void* q, const void* gate, const float* rms_weight,
                           void* out, const WsPtrs& w, hipStream_t s);

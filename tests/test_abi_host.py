@@ -54,7 +54,7 @@ def test_workspace_formula(lib):
     units, Fp1, dk, dv = 2, 13, 64, 32
     expect = (a(units * Fp1 * dk * dk * 4) + a(units * Fp1 * dv * dk * 4) + a(units * Fp1 * dk * dk * 4)
               + a(units * n * dk * dk * 4) + 2 * a(units * n * dv * dk * 4)
-              + a(units * 2 * (n + 1) * dv * dk * 4))
+              + a(units * 2 * (n + 1) * dv * dk * 4) + a(units * n * dk * dk * 4))
     assert vda.vda_workspace_bytes(d) == expect
     assert vda.vda_workspace_bytes(desc(units=0)) == 0
     assert vda.vda_workspace_bytes(desc(frames=0)) == 0
