@@ -13,15 +13,19 @@
 // part and a bf16 residual (S~ = hi + lo to ~2^-17 relative) and kept in LDS,
 // so the readout is two bf16 MFMAs with fp32 accumulation and the HBM-bound
 // stream of q, gate and out never waits on a conversion.  The transposed
-// product O^T = S~ Q^T runs on v_mfma_f32_32x32x16_bf16 with q as the B
-// operand, loaded straight from HBM (lane l: token l % 32, half l / 32 of its
-// channels, 16-byte loads).  S~'s rows are stored in a permuted order such that
-// accumulator register r of tile T in lane l holds output channel
-//   (l / 32) * d_v' / 2 + 16 T + r,
-// i.e. each lane ends with one contiguous half-row of its token: the RMSNorm
-// reduction is a lane-local sum plus one cross-lane add, and gate loads and
-// output stores are 16-byte vectors.  Math in the epilogue is fp32; the output
-// is rounded to bf16 (nearest even).
+// product O^T = S~ Q^T runs on v_mfma_f32_16x16x32_bf16 with q as the B
+// operand, loaded straight from HBM: lane l serves token l % 16, and the four
+// lanes of a token read four consecutive 16-byte pieces of its row, so one
+// load instruction covers 16 rows x 64 contiguous bytes (measured on MI355X as
+// fast as fully contiguous streaming, where 32 rows x 16 bytes per instruction
+// lose about a quarter of the bandwidth).  S~'s rows are stored permuted so
+// that accumulator register r of tile T in lane group h = l / 16 holds output
+// channel 32 (T / 2) + 8 h + 4 (T % 2) + r: each lane ends with four
+// 8-channel groups of its token (channels 32 m + 8 h .. + 7), gate loads and output stores are
+// 16-byte vectors in the same 16-rows x 64-bytes pattern, and the RMSNorm
+// reduction is a lane-local sum plus two cross-lane adds.  Each A operand read
+// from LDS feeds two 16-token groups.  Math in the epilogue is fp32; the
+// output is rounded to bf16 (nearest even).
 //
 // fp32 path: the same computation on the vector ALUs in fp32.
 #include "vda_device.h"
@@ -57,22 +61,22 @@ __global__ __launch_bounds__(256, 2) void readout_bf16_kernel(
   const int t = threadIdx.x;
   const int lane = t & 63;
   const int w = t >> 6;
-  const int Dvp = pad32(dv);
-  const int NT = Dvp >> 5;     // 32-channel output tiles
-  const int HALF = Dvp >> 1;   // output channels per lane
-  const int SROW = dk + 8;     // LDS row stride (bf16 elements)
-  const int halfk = dk >> 1;   // input channels per lane half
-  const int NKS = dk >> 4;     // k-steps of 16 channels
+  const int Dvp = pad32(dv);   // output channels incl. padding (pairs of 16-channel tiles)
+  const int NT = Dvp >> 4;     // 16-channel output tiles (even)
+  const int Dkp = pad32(dk);   // contraction incl. padding
+  const int NKS = Dkp >> 5;    // k-steps of 32 channels
+  const int SROW = 136;        // LDS row stride (bf16 elements): 17 x 16 bytes
 
   for (int i = t; i < 128; i += 256) Ws[i] = i < dv ? wrms[i] : 0.0f;
-  // gather S~ and split it into bf16 hi + lo, rows permuted (see header)
+  // gather S~ and split it into bf16 hi + lo, rows permuted (see header);
+  // padding rows and columns are zero
   {
     const size_t SS = (size_t)dv * dk;
     const int pi = max(c - radius, 0);
     const int ri = min(c + radius + 1, n);
     const float* P = ST + ((size_t)(u * 2 + 0) * (n + 1) + pi) * SS;
     const float* R = ST + ((size_t)(u * 2 + 1) * (n + 1) + ri) * SS;
-    const int k8n = dk >> 3;
+    const int k8n = Dkp >> 3;
     const int items = Dvp * k8n;  // <= 2048 = 8 per thread
     f32x4_t pv[8][2], rv[8][2];
 #pragma unroll
@@ -81,9 +85,9 @@ __global__ __launch_bounds__(256, 2) void readout_bf16_kernel(
       const int ch = it / k8n;
       const int k8 = it - ch * k8n;
       const f32x4_t z = {0.0f, 0.0f, 0.0f, 0.0f};
-      const bool ok = it < items && ch < dv;
-      const f32x4_t* pp = reinterpret_cast<const f32x4_t*>(P + (size_t)(ok ? ch : 0) * dk + 8 * k8);
-      const f32x4_t* rp = reinterpret_cast<const f32x4_t*>(R + (size_t)(ok ? ch : 0) * dk + 8 * k8);
+      const bool ok = it < items && ch < dv && 8 * k8 < dk;
+      const f32x4_t* pp = reinterpret_cast<const f32x4_t*>(P + (size_t)(ok ? ch : 0) * dk + (ok ? 8 * k8 : 0));
+      const f32x4_t* rp = reinterpret_cast<const f32x4_t*>(R + (size_t)(ok ? ch : 0) * dk + (ok ? 8 * k8 : 0));
       pv[i][0] = ok ? pp[0] : z;
       pv[i][1] = ok ? pp[1] : z;
       rv[i][0] = ok ? rp[0] : z;
@@ -95,11 +99,9 @@ __global__ __launch_bounds__(256, 2) void readout_bf16_kernel(
       if (it >= items) continue;
       const int ch = it / k8n;
       const int k8 = it - ch * k8n;
-      const int h = ch / HALF;
-      const int rem = ch - h * HALF;
-      const int T = rem >> 4;
-      const int rr = rem & 15;
-      const int lrow = 32 * T + 8 * (rr >> 2) + 4 * h + (rr & 3);
+      // channel ch = 32 m + 8 h + 4 (T % 2) + r  ->  LDS row 16 T + 4 h + r
+      const int T = 2 * (ch >> 5) + ((ch >> 2) & 1);
+      const int lrow = 16 * T + 4 * ((ch >> 3) & 3) + (ch & 3);
       float x[8];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -119,86 +121,100 @@ __global__ __launch_bounds__(256, 2) void readout_bf16_kernel(
   }
   __syncthreads();
 
-  const int g = lane >> 5;      // half of the input channels (B operand k slots) and of the outputs
-  const int il = lane & 31;     // token within the 32-row block
+  const int h = lane >> 4;      // lane group: k slots of the operands, output channel group
+  const int jl = lane & 15;     // token within a 16-row group
   const size_t chunk_row0 = ((size_t)u * F + f0) * U;
   const float inv_dv = 1.0f / (float)dv;
   const u32x4_t z4 = {0u, 0u, 0u, 0u};
+  const bool kpad = (dk & 31) != 0;  // last k-step partly past d_k
 
-  // Software pipeline over this wave's 32-row blocks.  At block `it` the gate
-  // logits and then the queries of block it + 1 are issued before the MFMAs of
-  // block it; vmcnt retires in issue order, so using block it's registers never
-  // waits for block it + 1's loads, and the stores of block it follow them.
   // Loads are unconditional from clamped, valid addresses (rows past the chunk's
-  // end reread its last row, padding channels reread the first group); those
-  // rows are never stored and padding channels never reach an output.
-  const int last_m = max((min(HALF, dv - g * HALF) >> 3) - 1, 0);  // last valid 8-channel group
+  // end reread its last row, channel groups past d_k / d_v reread the last valid
+  // one); such rows are never stored, padded S~ columns are zero (and the
+  // partly padded k-step is masked), padded output channels are never stored.
+  // Block of 32 rows = two 16-row groups; per group 4 k-steps of q and 4
+  // channel groups of gate.
   auto load_blk = [&](u32x4_t (&qr)[8], u32x4_t (&gr)[8], long rb) {
-    const long myrow = min(rb + il, rows_total - 1);
-    const size_t grow = chunk_row0 + (size_t)myrow;
-    const uint16_t* gp = gate + grow * dv + (g * HALF < dv ? g * HALF : 0);
 #pragma unroll
-    for (int m = 0; m < 8; ++m)
-      gr[m] = *reinterpret_cast<const u32x4_t*>(gp + 8 * min(m, last_m));
-    const uint16_t* qp = q + grow * dk + g * halfk;
+    for (int gi = 0; gi < 2; ++gi) {
+      const long myrow = min(rb + 16 * gi + jl, rows_total - 1);
+      const size_t grow = chunk_row0 + (size_t)myrow;
+      const uint16_t* gp = gate + grow * dv;
 #pragma unroll
-    for (int s = 0; s < 8; ++s)
-      qr[s] = *reinterpret_cast<const u32x4_t*>(qp + 8 * min(s, NKS - 1));
+      for (int m = 0; m < 4; ++m)
+        gr[4 * gi + m] = *reinterpret_cast<const u32x4_t*>(gp + min(32 * m + 8 * h, dv - 8));
+    }
+#pragma unroll
+    for (int gi = 0; gi < 2; ++gi) {
+      const long myrow = min(rb + 16 * gi + jl, rows_total - 1);
+      const size_t grow = chunk_row0 + (size_t)myrow;
+      const uint16_t* qp = q + grow * dk;
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+        qr[4 * gi + s] = *reinterpret_cast<const u32x4_t*>(qp + min(32 * s + 8 * h, dk - 8));
+    }
   };
+
   // one 32-row block: MFMAs on (qr, gr) loaded one block earlier, then the
   // RMSNorm/gate epilogue and the stores
   auto process = [&](const u32x4_t (&qr)[8], const u32x4_t (&gr)[8], long rb) {
-    const long myrow = rb + il;
-    const bool valid = myrow < rows_total;
-    const size_t grow = chunk_row0 + (size_t)(valid ? myrow : 0);
-    f32x16_t acc[4];
+    f32x4_t acc[2][8];
 #pragma unroll
-    for (int T = 0; T < 4; ++T) acc[T] = zero16();
+    for (int gi = 0; gi < 2; ++gi)
 #pragma unroll
-    for (int s = 0; s < 8; ++s) {
+      for (int T = 0; T < 8; ++T) acc[gi][T] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
       if (s >= NKS) continue;
+      u32x4_t b0 = qr[s], b1 = qr[4 + s];
+      if (kpad && 32 * s + 8 * h >= dk) b0 = b1 = z4;
 #pragma unroll
-      for (int T = 0; T < 4; ++T) {
+      for (int T = 0; T < 8; ++T) {
         if (T >= NT) continue;
-        const int off = (32 * T + il) * SROW + g * halfk + 8 * s;
+        const int off = (16 * T + jl) * SROW + 32 * s + 8 * h;
         const u32x4_t ah = *reinterpret_cast<const u32x4_t*>(Shi + off);
         const u32x4_t al = *reinterpret_cast<const u32x4_t*>(Slo + off);
-        acc[T] = mfma_bf16(ah, qr[s], acc[T]);
-        acc[T] = mfma_bf16(al, qr[s], acc[T]);
+        acc[0][T] = mfma16_bf16(ah, b0, acc[0][T]);
+        acc[1][T] = mfma16_bf16(ah, b1, acc[1][T]);
+        acc[0][T] = mfma16_bf16(al, b0, acc[0][T]);
+        acc[1][T] = mfma16_bf16(al, b1, acc[1][T]);
       }
     }
-
-    // RMSNorm over the token's d_v outputs: this lane's half plus lane ^ 32's
-    float ss = 0.0f;
 #pragma unroll
-    for (int T = 0; T < 4; ++T)
+    for (int gi = 0; gi < 2; ++gi) {
+      // RMSNorm over the token's d_v outputs: 4 lanes x 32 channels each
+      float ss = 0.0f;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) ss = fmaf(acc[T][r], acc[T][r], ss);
-    ss += __shfl_xor(ss, 32);
-    const float inv = rsqrtf(ss * inv_dv + eps);
-
-    if (valid) {
-      uint16_t* op = out + grow * dv + g * HALF;
-      const float* wp = Ws + g * HALF;
+      for (int T = 0; T < 8; ++T)
 #pragma unroll
-      for (int m = 0; m < 8; ++m) {
-        if (8 * m >= HALF || g * HALF + 8 * m >= dv) continue;
-        const f32x4_t w0 = *reinterpret_cast<const f32x4_t*>(wp + 8 * m);
-        const f32x4_t w1 = *reinterpret_cast<const f32x4_t*>(wp + 8 * m + 4);
-        float y[8];
+        for (int r = 0; r < 4; ++r) ss = fmaf(acc[gi][T][r], acc[gi][T][r], ss);
+      ss += __shfl_xor(ss, 16);
+      ss += __shfl_xor(ss, 32);
+      const float inv = rsqrtf(ss * inv_dv + eps);
+      const long myrow = rb + 16 * gi + jl;
+      if (myrow < rows_total) {
+        const size_t grow = chunk_row0 + (size_t)myrow;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int idx = 8 * m + e;
-          const float o = acc[idx >> 4][idx & 15];
-          const float gl = (e & 1) ? bf16_hi(gr[m][e >> 1]) : bf16_lo(gr[m][e >> 1]);
-          const float ww = e < 4 ? w0[e] : w1[e - 4];
-          const float sig = __builtin_amdgcn_rcpf(1.0f + __expf(-gl));
-          y[e] = o * inv * ww * sig;
+        for (int m = 0; m < 4; ++m) {
+          const int ch = 32 * m + 8 * h;
+          if (ch >= dv) continue;
+          const f32x4_t w0 = *reinterpret_cast<const f32x4_t*>(Ws + ch);
+          const f32x4_t w1 = *reinterpret_cast<const f32x4_t*>(Ws + ch + 4);
+          const u32x4_t gv = gr[4 * gi + m];
+          float y[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float o = acc[gi][2 * m + (e >> 2)][e & 3];
+            const float gl = (e & 1) ? bf16_hi(gv[e >> 1]) : bf16_lo(gv[e >> 1]);
+            const float ww = e < 4 ? w0[e] : w1[e - 4];
+            const float sig = __builtin_amdgcn_rcpf(1.0f + __expf(-gl));
+            y[e] = o * inv * ww * sig;
+          }
+          u32x4_t ov;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) ov[e] = pack_bf16(y[2 * e], y[2 * e + 1]);
+          *reinterpret_cast<u32x4_t*>(out + grow * dv + ch) = ov;
         }
-        u32x4_t ov;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) ov[e] = pack_bf16(y[2 * e], y[2 * e + 1]);
-        *reinterpret_cast<u32x4_t*>(op + 8 * m) = ov;
       }
     }
   };
