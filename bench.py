@@ -181,6 +181,21 @@ def main():
             hip.hipEventDestroy(ctypes.c_void_p(e))
     avg_ms = {s: sum(v) / len(v) for s, v in stage_ms.items()}
 
+    # context: what a plain library kernel with the readout's traffic mix (two
+    # reads + one write of the same tensors) reaches on this GPU
+    ceil_out = torch.empty_like(d["q"])
+    for _ in range(2):
+        torch.add(d["q"], d["gate"], out=ceil_out)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(5):
+        torch.add(d["q"], d["gate"], out=ceil_out)
+    e1.record()
+    torch.cuda.synchronize()
+    add_ms = e0.elapsed_time(e1) / 5
+    add_bytes = 3 * d["q"].numel() * d["q"].element_size()
+    del ceil_out
+
     th = cfg.token_heads
     ms_per_step = elapsed * 1e3 / args.steps
     value = th * args.steps / elapsed
@@ -213,6 +228,8 @@ def main():
         "mfma_frac": mfma,
         "hbm_frac_whole_op": hbm_whole,
         "stage_ms": avg_ms,
+        "stream_ceiling": {"kernel": "torch.add over the q and gate tensors (2 reads + 1 write)",
+                           "GB/s": add_bytes / (add_ms * 1e-3) / 1e9, "ms": add_ms},
     }
     if args.cpu_seconds > 0:
         log("[bench] CPU oracle baseline")
