@@ -42,16 +42,21 @@ template <int DK, int DV>
 __global__ __launch_bounds__(256, 2) void readout_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ gate,
     const float* __restrict__ wrms, uint16_t* __restrict__ out, const float* __restrict__ ST,
-    int dk_rt, int dv_rt, int F, int U, int C, int radius, int n, float eps) {
+    int dk_rt, int dv_rt, int F, int U, int C, int radius, int n, float eps, int units, int nblk,
+    unsigned per) {
   const int dk = DK > 0 ? DK : dk_rt;
   const int dv = DV > 0 ? DV : dv_rt;
   __shared__ __align__(16) uint16_t Shi[128 * 136];
   __shared__ __align__(16) uint16_t Slo[128 * 136];
   __shared__ __align__(16) float Ws[128];  // RMSNorm weight (LDS: its reads use lgkmcnt, not vmcnt)
 
-  const int blk = blockIdx.x;
-  const int c = blockIdx.y;
-  const int u = blockIdx.z;
+  // work item = (unit, chunk, row block), row block fastest: the blocks of one
+  // chunk (which all read the same two states) share an XCD
+  const unsigned item = xcd_item(per);
+  if (item >= (unsigned)units * n * nblk) return;
+  const int blk = item % nblk;
+  const int c = (item / nblk) % n;
+  const int u = item / (nblk * n);
   const int f0 = c * C;
   const int f1 = min(f0 + C, F);
   const long rows_total = (long)(f1 - f0) * U;
@@ -307,13 +312,14 @@ hipError_t launch_readout(const Plan& p, const void* q, const void* gate, const 
   const long max_rows = (long)p.C * p.U;
   if (max_rows == 0) return hipSuccess;
   if (p.dtype == VDA_DTYPE_BF16) {
-    const dim3 grid((unsigned)((max_rows + kRows - 1) / kRows), p.n, p.units);
+    const int nblk = (int)((max_rows + kRows - 1) / kRows);
+    const unsigned per = xcd_per((unsigned)p.units * p.n * nblk);
     auto kern = (p.dk == 128 && p.dv == 128) ? readout_bf16_kernel<128, 128>
                                              : readout_bf16_kernel<0, 0>;
-    hipLaunchKernelGGL(kern, grid, dim3(kThreads), 0, s,
+    hipLaunchKernelGGL(kern, dim3(kXcds * per), dim3(kThreads), 0, s,
                        static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(gate),
                        rms_weight, static_cast<uint16_t*>(out), w.ST, p.dk, p.dv, p.F, p.U, p.C,
-                       p.r, p.n, p.eps);
+                       p.r, p.n, p.eps, p.units, nblk, per);
   } else {
     const dim3 grid((unsigned)((max_rows + kRowsF - 1) / kRowsF), p.n, p.units);
     hipLaunchKernelGGL(readout_f32_kernel, grid, dim3(kThreads), 0, s,

@@ -302,14 +302,19 @@ __global__ __launch_bounds__(256, 1) void compose_split_kernel(const float* __re
                                                               float* __restrict__ McT,
                                                               float* __restrict__ Jf,
                                                               float* __restrict__ Jr, int dk,
-                                                              int dv, int F, int C, int n) {
+                                                              int dv, int F, int C, int n,
+                                                              int units, unsigned per) {
   __shared__ __align__(16) __bf16 Xh[128 * SB];
   __shared__ __align__(16) __bf16 Xl[128 * SB];
   __shared__ __align__(16) __bf16 Mh[128 * SB];
   __shared__ __align__(16) __bf16 Ml[128 * SB];
-  const int c = blockIdx.x;
-  const int u = blockIdx.y;
-  const int chain = blockIdx.z;  // 0: Mc, 1: Jf, 2: Jr
+  // work item = (unit, chunk, chain), chain fastest: the three chains of a chunk
+  // read the same transitions and share an XCD
+  const unsigned item = xcd_item(per);
+  if (item >= (unsigned)units * n * 3) return;
+  const int chain = item % 3;  // 0: Mc, 1: Jf, 2: Jr
+  const int c = (item / 3) % n;
+  const int u = item / (3 * n);
   const int t = threadIdx.x;
   const int lane = t & 63;
   const int w = t >> 6;
@@ -470,10 +475,14 @@ __global__ __launch_bounds__(256) void scan_split_kernel(const float* __restrict
 }  // namespace
 
 hipError_t launch_compose(const Plan& p, const WsPtrs& w, hipStream_t s) {
-  const dim3 grid(p.n, p.units, 3);
-  auto kern = p.dtype == VDA_DTYPE_BF16 ? compose_split_kernel : compose_kernel;
-  hipLaunchKernelGGL(kern, grid, dim3(kThreads), 0, s, w.B, w.M, w.Mc, w.McT, w.Jf, w.Jr, p.dk,
-                     p.dv, p.F, p.C, p.n);
+  if (p.dtype == VDA_DTYPE_BF16) {
+    const unsigned per = xcd_per((unsigned)p.units * p.n * 3);
+    hipLaunchKernelGGL(compose_split_kernel, dim3(kXcds * per), dim3(kThreads), 0, s, w.B, w.M,
+                       w.Mc, w.McT, w.Jf, w.Jr, p.dk, p.dv, p.F, p.C, p.n, p.units, per);
+  } else {
+    hipLaunchKernelGGL(compose_kernel, dim3(p.n, p.units, 3), dim3(kThreads), 0, s, w.B, w.M, w.Mc,
+                       w.McT, w.Jf, w.Jr, p.dk, p.dv, p.F, p.C, p.n);
+  }
   return hipGetLastError();
 }
 

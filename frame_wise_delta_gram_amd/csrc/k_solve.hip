@@ -7,8 +7,9 @@
 //
 // I + A_t is symmetric positive definite with every eigenvalue >= 1 (A_t is a
 // Gram matrix), so a Cholesky factorisation without pivoting is stable and its
-// diagonal is >= 1.  One workgroup (4 waves) per frame keeps the d_k x d_k
-// matrix in LDS (fp32, odd row stride), in place, and works on 32 x 32 blocks:
+// diagonal is >= 1.  One workgroup (4 waves) per frame keeps the lower
+// triangle of the d_k x d_k matrix in LDS as 32 x 32 blocks (fp32, row stride
+// 33), in place, and works block by block:
 //   1. blocked right-looking Cholesky  I + A = L L^T.  The 32-column diagonal
 //      block is factored by one wave in registers (lane c holds column c;
 //      pivots and columns move with readlane, no LDS round trips) and replaced
@@ -16,19 +17,21 @@
 //      W_pp^T) and trailing (G_ij -= L_ip L_jp^T) updates are 32x32x32 fp32
 //      MFMA block products spread over the 4 waves;
 //   2. W = L^{-1} row block by row block: W_ij = -W_ii sum_{k=j}^{i-1} L_ik W_kj,
-//      the blocks of one row in parallel (sums staged in a small buffer, so L
-//      is overwritten only after the whole row has read it);
+//      the blocks of one row in parallel; each sum is held in registers until
+//      the whole row has read L, then parked in its own block for the W_ii
+//      product, so no staging buffer is needed;
 //   3. M = W^T W, the upper blocks by MFMA, mirrored on store.
-// One 66 KiB matrix buffer per workgroup lets two workgroups share a CU, so
-// one's serial diagonal work overlaps the other's MFMA work.  fp32 throughout.
+// 42 KiB of LDS per workgroup lets three workgroups share a CU, so their serial
+// diagonal work overlaps each other's MFMA work.  fp32 throughout.
 #include "vda_device.h"
 #include "vda_internal.h"
 
 namespace vda {
 namespace {
 
-constexpr int SG = 129;  // LDS row stride in floats (odd: conflict-free column reads)
-constexpr int ST = 33;   // stride of the 32x32 staging blocks
+constexpr int SG = 33;   // row stride of a stored 32 x 32 block (odd: conflict-free column reads)
+constexpr int kBlk = 32 * SG;  // floats per stored block
+constexpr int kNBlk = 10;      // lower-triangle blocks of a 128 x 128 matrix
 
 __device__ __forceinline__ float readlane_f(float x, int l) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), l));
@@ -83,13 +86,12 @@ __device__ void factor_invert_diag_block(float* G) {
   }
 }
 
-__global__ __launch_bounds__(256, 2) void solve_kernel(const float* __restrict__ A,
+__global__ __launch_bounds__(256, 3) void solve_kernel(const float* __restrict__ A,
                                                       const float* __restrict__ B,
                                                       float* __restrict__ Mout,
                                                       float* __restrict__ STt, int dk, int dv,
                                                       int Fp1, int n, float seed_scale) {
-  __shared__ float Gs[128 * SG];
-  __shared__ float Ts[3 * 32 * ST];
+  __shared__ float Gs[kNBlk * kBlk];  // block (i, j), j <= i, at index i (i + 1) / 2 + j
   const int fi = blockIdx.x;
   const int u = blockIdx.y;
   const int t = threadIdx.x;
@@ -97,14 +99,23 @@ __global__ __launch_bounds__(256, 2) void solve_kernel(const float* __restrict__
   const int w = t >> 6;
   const int Dk = pad32(dk);
   const int nb = Dk >> 5;
-  auto G = [&](int i, int j) { return Gs + 32 * i * SG + 32 * j; };
+  auto G = [&](int i, int j) { return Gs + (i * (i + 1) / 2 + j) * kBlk; };
 
   {
     MatRegs m;
     mat_load(m, A + ((size_t)u * Fp1 + fi) * dk * dk, dk, dk, dk);
-    mat_store_lds(m, Gs, SG, Dk, Dk);
-    __syncthreads();
-    for (int i = t; i < Dk; i += 256) Gs[i * SG + i] += 1.0f;  // I + A (identity on padding)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {  // keep the lower-triangle blocks, add the identity
+      const int id = t + 256 * i;
+      const int r = id >> 5;
+      const int c = (id & 31) << 2;
+      const int bi = r >> 5, bj = c >> 5;
+      if (r < Dk && c < Dk && bj <= bi) {
+        float* dst = G(bi, bj) + (r & 31) * SG + (c & 31);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dst[e] = m.v[i][e] + (r == c + e ? 1.0f : 0.0f);
+      }
+    }
     __syncthreads();
   }
 
@@ -136,17 +147,19 @@ __global__ __launch_bounds__(256, 2) void solve_kernel(const float* __restrict__
 
   // 2. off-diagonal blocks of W = L^{-1}, row block by row block
   for (int i = 1; i < nb; ++i) {
+    f32x16_t acc = zero16();
     if (w < i) {  // wave j = w: T_ij = sum_{k=j}^{i-1} L_ik W_kj
       const int j = w;
-      f32x16_t acc = zero16();
       for (int k = j; k < i; ++k) acc = blk_mm32<false, false>(acc, G(i, k), SG, G(k, j), SG);
-      store_acc(Ts + j * 32 * ST, ST, acc, 1.0f);
     }
-    __syncthreads();
-    if (w < i) {  // W_ij = -W_ii T_ij (overwrites L_ij)
+    __syncthreads();  // every L_ik of row i has been read
+    if (w < i) {      // W_ij = -W_ii T_ij, T_ij parked in block (i, j)
       const int j = w;
-      const f32x16_t acc = blk_mm32<false, false>(zero16(), G(i, i), SG, Ts + j * 32 * ST, ST);
-      store_acc(G(i, j), SG, acc, -1.0f);
+      store_acc(G(i, j), SG, acc, 1.0f);
+      wave_sync();
+      const f32x16_t acc2 = blk_mm32<false, false>(zero16(), G(i, i), SG, G(i, j), SG);
+      wave_sync();
+      store_acc(G(i, j), SG, acc2, -1.0f);
     }
     __syncthreads();
   }

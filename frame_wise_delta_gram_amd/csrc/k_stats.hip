@@ -118,8 +118,8 @@ __global__ __launch_bounds__(512, 1) void stats_bf16_kernel(
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       const int tok = min(r.tok0 + s, last_tok);
-      r.k[s] = *reinterpret_cast<const u32x4_t*>(sk + (size_t)tok * dk + 8 * kcg);
-      r.v[s] = *reinterpret_cast<const u32x4_t*>(sv + (size_t)tok * dv + 8 * vcg);
+      r.k[s] = ld_stream(sk + (size_t)tok * dk + 8 * kcg);
+      r.v[s] = ld_stream(sv + (size_t)tok * dv + 8 * vcg);
       r.b[s] = sb[tok];
     }
   };
@@ -131,10 +131,9 @@ __global__ __launch_bounds__(512, 1) void stats_bf16_kernel(
     float x[4];
 #pragma unroll
     for (int s = 0; s < 4; ++s) x[s] = (hi ? bf16_hi(x4[s][p]) : bf16_lo(x4[s][p])) * b[s];
-    // b[s] is exactly 0 for tokens past the end; select (not multiply) so that
-    // a non-finite value in the clamped row cannot leak in
-#pragma unroll
-    for (int s = 0; s < 4; ++s) x[s] = b[s] != 0.0f ? x[s] : 0.0f;
+    // b[s] is 0 for tokens past the end; their registers hold a copy of the
+    // frame's last token, so the product is exactly 0 (a non-finite input there
+    // would already make the frame's statistics non-finite)
     u32x2_t e;
     e[0] = pack_bf16(x[0], x[1]);
     e[1] = pack_bf16(x[2], x[3]);

@@ -59,6 +59,15 @@ __device__ __forceinline__ f32x16_t zero16() {
   return z;
 }
 
+// Streaming 16-byte accesses for data touched exactly once (q, gate, k, v,
+// out): non-temporal, so they do not evict reused data from the caches.
+__device__ __forceinline__ u32x4_t ld_stream(const void* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+}
+__device__ __forceinline__ void st_stream(void* p, u32x4_t v) {
+  __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t*>(p));
+}
+
 // bf16 <-> fp32.  A bf16 is the top half of an fp32, so widening is a shift.
 __device__ __forceinline__ float bf16_lo(uint32_t x) { return __uint_as_float(x << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t x) { return __uint_as_float(x & 0xffff0000u); }
@@ -81,6 +90,18 @@ __device__ __forceinline__ void wave_sync() {
 }
 
 __host__ __device__ __forceinline__ int pad32(int d) { return (d + 31) & ~31; }
+
+// Workgroups of a launch are dispatched round-robin over the 8 XCDs (each with
+// its own L2).  For a 1-D grid of 8 * per workgroups, give XCD x the
+// contiguous work items [x * per, (x + 1) * per), so items that share inputs
+// (neighbouring items) are served by one L2.  Returns the work item of this
+// workgroup (may be >= the real item count: the caller skips those).
+constexpr int kXcds = 8;
+__device__ __forceinline__ unsigned xcd_item(unsigned per) {
+  const unsigned L = blockIdx.x;
+  return (L % kXcds) * per + L / kXcds;
+}
+__host__ __forceinline__ unsigned xcd_per(unsigned items) { return (items + kXcds - 1) / kXcds; }
 
 // ---------------------------------------------------------------------------
 // 32x32x32 fp32 block product on MFMA, operands in LDS (row-major with the
