@@ -13,6 +13,7 @@ MFMA fraction the metric asks for, and the fp64 CPU oracle timed on a bounded
 sample of the same workload on the host cores.
 
   python bench.py [--steps K] [--warmup W] [--config 4] [--cpu-seconds S]
+  python bench.py --summarize DIR [--config 4]   (profiles/ from rocprofv3 output)
 """
 from __future__ import annotations
 
@@ -32,6 +33,7 @@ HBM_PEAK = 8.0e12          # MI355X HBM3E, bytes/s
 BF16_PEAK = 2.5166e15      # MI355X dense bf16 MFMA, flop/s
 PROFILES = os.path.join(ROOT, "profiles")
 STAGES = ("stats", "solve", "compose", "scan", "readout")
+CEILING_CALLS = 7          # torch.add launches of the stream-ceiling measurement (2 + 5)
 
 
 def log(*a):
@@ -39,25 +41,38 @@ def log(*a):
 
 
 def algorithmic(cfg):
-    """Algorithmic HBM bytes and bf16 MFMA flops per launch of each streaming kernel."""
+    """Algorithmic HBM bytes (and bf16 MFMA flops where the kernel is a contraction)
+    per launch of each kernel: every input read once, every output written once."""
     eb = 2 if cfg.dtype == "bf16" else 4
     th = cfg.units * cfg.frames * cfg.tokens        # token-heads
     tt = cfg.units * cfg.text_tokens
-    dk, dv, n = cfg.d_k, cfg.d_v, cfg.n_chunks
+    dk, dv, n, u, F = cfg.d_k, cfg.d_v, cfg.n_chunks, cfg.units, cfg.frames
+    mat, st = dk * dk * 4, dv * dk * 4               # one transition, one state (fp32)
     stats_bytes = ((th + tt) * ((dk + dv) * eb + 4)                     # k, v, beta read
-                   + cfg.units * (cfg.frames + 1) * (dk + dv) * dk * 4)  # A, B written
+                   + u * (F + 1) * (dk + dv) * dk * 4)                  # A, B written
     readout_bytes = (th * (dk + 2 * dv) * eb                           # q, gate read; out written
-                     + cfg.units * n * 2 * dv * dk * 4 + dv * 4)        # two states per chunk
+                     + u * n * 2 * st + dv * 4)                         # two states per chunk
+    solve_bytes = 2 * u * (F + 1) * mat + u * 3 * st                    # A in, M out; B_T in, 2 seeds
+    compose_bytes = u * F * (mat + st) + u * n * (2 * mat + 2 * st)     # M, B in; Mc, McT, Jf, Jr
+    scan_bytes = u * n * (2 * mat + 2 * st) + u * 2 * n * st            # chunk maps in; P, R out
     stats_flops = 2 * (th + tt) * (dk + dv) * dk     # [K|V]^T (beta K), full Gram
     readout_flops = 2 * th * dk * dv                 # S~ q
-    return {"stats": (stats_bytes, stats_flops), "readout": (readout_bytes, readout_flops)}
+    return {"stats": (stats_bytes, stats_flops), "readout": (readout_bytes, readout_flops),
+            "solve": (solve_bytes, None), "compose": (compose_bytes, None),
+            "scan": (scan_bytes, None)}
+
+
+KERNEL_SOURCES = {"stats": "k_stats.hip", "readout": "k_readout.hip", "solve": "k_solve.hip",
+                  "compose": "k_scan.hip", "scan": "k_scan.hip"}
 
 
 def source_digest(kernel):
-    path = os.path.join(ROOT, "frame_wise_delta_gram_amd", "csrc",
-                        {"stats": "k_stats.hip", "readout": "k_readout.hip"}[kernel])
-    with open(path, "rb") as fh:
-        return hashlib.sha256(fh.read()).hexdigest()
+    """sha256 over the kernel's source file and the device header it includes."""
+    h = hashlib.sha256()
+    for name in (KERNEL_SOURCES[kernel], "vda_device.h"):
+        with open(os.path.join(ROOT, "frame_wise_delta_gram_amd", "csrc", name), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
 
 
 def measured_traffic(kernel, workload):
@@ -71,6 +86,113 @@ def measured_traffic(kernel, workload):
     if rec.get("source_sha256") != source_digest(kernel):
         return None
     return rec.get("hbm_bytes_per_launch")
+
+
+PROFILE_COMMANDS = {
+    "FETCH_SIZE": "timeout -s KILL 120 rocprofv3 --pmc FETCH_SIZE --kernel-include-regex "
+                  "'vda|add' -d DIR/FETCH_SIZE -o p --output-format csv -- python bench.py "
+                  "--steps 2 --warmup 1 --cpu-seconds 0",
+    "WRITE_SIZE": "timeout -s KILL 120 rocprofv3 --pmc WRITE_SIZE --kernel-include-regex "
+                  "'vda|add' -d DIR/WRITE_SIZE -o p --output-format csv -- python bench.py "
+                  "--steps 2 --warmup 1 --cpu-seconds 0",
+    "stats": "rocprofv3 --kernel-trace --stats -d DIR/trace -o vda --output-format csv -- "
+             "python bench.py --steps 5 --warmup 2 --cpu-seconds 0",
+}
+KERNEL_NAMES = {"stats_bf16_kernel": "stats", "stats_f32_kernel": "stats",
+                "readout_bf16_kernel": "readout", "readout_f32_kernel": "readout",
+                "solve_kernel": "solve", "compose_split_kernel": "compose",
+                "compose_kernel": "compose", "scan_split_kernel": "scan", "scan_kernel": "scan"}
+
+
+def short_kernel_name(full):
+    import re
+    m = re.search(r"vda::\(anonymous namespace\)::(\w+)", full)
+    if m:
+        return KERNEL_NAMES.get(m.group(1), m.group(1))
+    return "copy" if "add" in full.lower() else None
+
+
+def summarize(prof_dir, cfg_id):
+    """Write the profiles/ summaries from the rocprofv3 output of PROFILE_COMMANDS
+    (DIR = prof_dir): kernel durations, and HBM bytes per launch from FETCH_SIZE
+    and WRITE_SIZE (KiB per dispatch), each scaled by what the same counter reads
+    for torch.add over the q and gate tensors (2 x bytes read, 1 x written)."""
+    import collections
+    import csv
+    import workloads as W
+
+    cfg = W.CONFIGS[cfg_id]
+    eb = 2 if cfg.dtype == "bf16" else 4
+    copy_bytes = cfg.units * cfg.frames * cfg.tokens * cfg.d_v * eb
+    known = {"FETCH_SIZE": 2 * copy_bytes, "WRITE_SIZE": copy_bytes}
+    alg = algorithmic(cfg)
+    per = {}   # counter -> kernel -> mean KiB per dispatch
+    for ctr in ("FETCH_SIZE", "WRITE_SIZE"):
+        disp = collections.defaultdict(float)
+        names = {}
+        with open(os.path.join(prof_dir, ctr, "p_counter_collection.csv")) as fh:
+            for r in csv.DictReader(fh):
+                k = short_kernel_name(r["Kernel_Name"])
+                if k is None or r["Counter_Name"] != ctr:
+                    continue
+                disp[int(r["Dispatch_Id"])] += float(r["Counter_Value"])
+                names[int(r["Dispatch_Id"])] = k
+        acc = collections.defaultdict(list)
+        for i, v in sorted(disp.items()):
+            acc[names[i]].append(v)
+        acc["copy"] = acc["copy"][-CEILING_CALLS:]  # earlier adds belong to input generation
+        per[ctr] = {k: sum(v) / len(v) for k, v in acc.items()}
+    scale = {c: known[c] / (per[c]["copy"] * 1024.0) for c in per}
+    durations = {}
+    with open(os.path.join(prof_dir, "trace", "vda_kernel_stats.csv")) as fh:
+        for r in csv.DictReader(fh):
+            k = short_kernel_name(r["Name"])
+            if k and k != "copy":
+                durations[k] = (int(r["Calls"]), float(r["AverageNs"]) / 1e3,
+                                float(r["MinNs"]) / 1e3, float(r["MaxNs"]) / 1e3)
+    os.makedirs(PROFILES, exist_ok=True)
+    order = [k for k in STAGES if k in durations]
+    head = (f"{cfg.name} workload ({cfg.units} heads x {cfg.frames} frames x {cfg.tokens} "
+            f"tokens, d_k = {cfg.d_k}, d_v = {cfg.d_v}, {cfg.text_tokens} text tokens)")
+    lines = [f"# VDA forward kernels, {head}", "",
+             "Commands (from the repository root, on one MI355X; DIR = an output folder):", ""]
+    lines += [f"    {PROFILE_COMMANDS[c]}" for c in ("stats", "FETCH_SIZE", "WRITE_SIZE")]
+    lines += [f"    python bench.py --summarize DIR --config {cfg_id}", "",
+              "## Kernel durations (`vda_kernel_stats.csv`)", "",
+              "| kernel | calls | average (us) | min (us) | max (us) | algorithmic GB/s |",
+              "|---|---|---|---|---|---|"]
+    for k in order:
+        c, a, lo, hi = durations[k]
+        lines.append(f"| {k} | {c} | {a:.1f} | {lo:.1f} | {hi:.1f} | "
+                     f"{alg[k][0] / (a * 1e-6) / 1e9:.0f} |")
+    lines += ["", f"Sum of averages: {sum(durations[k][1] for k in order):.1f} us per forward step.",
+              "", "## HBM traffic per launch (`FETCH_SIZE`, `WRITE_SIZE`)", "",
+              f"Scale factors from torch.add over two {copy_bytes} B tensors into a third: "
+              f"FETCH x {scale['FETCH_SIZE']:.3f}, WRITE x {scale['WRITE_SIZE']:.3f} "
+              "(counter KiB x 1024 x factor = bytes).", "",
+              "| kernel | FETCH (KiB) | WRITE (KiB) | read (B) | written (B) | total (B) | "
+              "algorithmic (B) | total / algorithmic |", "|---|---|---|---|---|---|---|---|"]
+    for k in order:
+        f, w = per["FETCH_SIZE"].get(k), per["WRITE_SIZE"].get(k)
+        if f is None or w is None:
+            continue
+        rb = f * 1024 * scale["FETCH_SIZE"]
+        wb = w * 1024 * scale["WRITE_SIZE"]
+        lines.append(f"| {k} | {f:.0f} | {w:.0f} | {rb:.4g} | {wb:.4g} | {rb + wb:.4g} | "
+                     f"{alg[k][0]:.4g} | {(rb + wb) / alg[k][0]:.3f} |")
+        rec = {"kernel": k, "workload": cfg.name, "source_sha256": source_digest(k),
+               "fetch_kib_per_dispatch": f, "write_kib_per_dispatch": w,
+               "fetch_scale": scale["FETCH_SIZE"], "write_scale": scale["WRITE_SIZE"],
+               "read_bytes_per_launch": rb, "write_bytes_per_launch": wb,
+               "hbm_bytes_per_launch": rb + wb, "algorithmic_bytes_per_launch": alg[k][0],
+               "commands": [PROFILE_COMMANDS["FETCH_SIZE"], PROFILE_COMMANDS["WRITE_SIZE"],
+                            f"python bench.py --summarize DIR --config {cfg_id}"]}
+        with open(os.path.join(PROFILES, f"traffic_{k}_{cfg.name}.json"), "w") as fh:
+            json.dump(rec, fh, indent=1)
+            fh.write("\n")
+    with open(os.path.join(PROFILES, f"vda_kernels_{cfg.name}.md"), "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
 
 
 def cpu_baseline(d, cfg, budget_s):
@@ -112,7 +234,12 @@ def main():
     ap.add_argument("--config", type=int, default=4, help="workload id (4 = 768p-bf16)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="CPU budget of the oracle baseline (0 disables it)")
+    ap.add_argument("--summarize", metavar="DIR",
+                    help="write the profiles/ summaries from rocprofv3 output under DIR and exit")
     args = ap.parse_args()
+    if args.summarize:
+        summarize(args.summarize, args.config)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the VDA forward shards by head with no "
               "communication inside the op, and this build runs on a single MI355X. "
