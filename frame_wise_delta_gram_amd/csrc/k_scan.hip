@@ -54,18 +54,21 @@ __global__ __launch_bounds__(256, 1) void compose_kernel(const float* __restrict
                                                         float* __restrict__ Mc,
                                                         float* __restrict__ McT,
                                                         float* __restrict__ Jf,
-                                                        float* __restrict__ Jr, int dk, int dv,
-                                                        int F, int C, int n) {
+                                                        float* __restrict__ Jr,
+                                                        float* __restrict__ ST, int dk, int dv,
+                                                        int F, int C, int n, float seed_scale) {
   __shared__ float Xs[128 * SG];
   __shared__ float Ms[128 * SG];
   const int c = blockIdx.x;
   const int u = blockIdx.y;
-  const int chain = blockIdx.z;  // 0: Mc, 1: Jf, 2: Jr
+  const int chain = blockIdx.z;  // 0: Mc, 1: Jf, 2: Jr, 3: text seed (one per unit)
+  if (chain == 3 && c != 0) return;
   const int t = threadIdx.x;
   const int lane = t & 63;
   const int w = t >> 6;
-  const int f0 = c * C;
-  const int f1 = min(f0 + C, F);
+  // the seed is the text frame's map applied once: (0 + s B_T) M_T
+  const int f0 = chain == 3 ? -1 : c * C;
+  const int f1 = chain == 3 ? 0 : min(f0 + C, F);
   const int nf = f1 - f0;
   const int rows = chain == 0 ? dk : dv;
   const int R32 = pad32(rows);
@@ -82,6 +85,9 @@ __global__ __launch_bounds__(256, 1) void compose_kernel(const float* __restrict
     MatRegs m;
     if (chain != 0) {
       mat_load(m, Bp(frame(0)), dk, dv, dk);
+      if (chain == 3)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) m.v[i] *= seed_scale;
       mat_store_lds(m, Xs, SG, R32, Dk);
     } else {
       for (int idx = t; idx < R32 * Dk; idx += 256) {
@@ -95,8 +101,11 @@ __global__ __launch_bounds__(256, 1) void compose_kernel(const float* __restrict
   }
   __syncthreads();
 
+  const size_t SS = (size_t)dv * dk;
   float* dst = chain == 0 ? Mc + ((size_t)u * n + c) * dk * dk
-                          : (chain == 1 ? Jf : Jr) + ((size_t)u * n + c) * dv * dk;
+               : chain == 3 ? ST + (size_t)u * 2 * (n + 1) * SS                  // P[0]
+                            : (chain == 1 ? Jf : Jr) + ((size_t)u * n + c) * SS;
+  float* dst2 = ST + ((size_t)(u * 2 + 1) * (n + 1) + n) * SS;                 // R[n]
   MatRegs mnext;
   float bnext[4][16];
   for (int s = 0; s < nf; ++s) {
@@ -137,6 +146,7 @@ __global__ __launch_bounds__(256, 1) void compose_kernel(const float* __restrict
             if (row < rows && col < dk) {
               dst[(size_t)row * dk + col] = acc[ct][r];
               if (chain == 0) McT[((size_t)u * n + c) * dk * dk + (size_t)col * dk + row] = acc[ct][r];
+              if (chain == 3) dst2[(size_t)row * dk + col] = acc[ct][r];
             }
           } else {
             Xs[row * SG + col] = acc[ct][r] + bnext[ct][r];
@@ -218,189 +228,326 @@ __global__ __launch_bounds__(256) void scan_kernel(const float* __restrict__ Mc,
 }
 
 // ---------------------------------------------------------------------------
-// bf16x3 versions (bf16 features).  LDS matrices are pairs of bf16 arrays
-// (hi, lo) with a 136-element (272-byte) row stride: 16 consecutive rows read
-// at one column offset land on 16 distinct 16-byte bank groups.
+// bf16x3 versions (bf16 features).  X (the composed map or state) lives in LDS
+// as a pair of bf16 arrays (hi, lo) with a 136-element (272-byte) row stride.
+// A transition never goes through LDS: the product is formed transposed,
+//   T = M[jr .. jr + 31, :] X^T = ((X M)[:, jr .. jr + 31])^T   (M symmetric),
+// so a wave's transition operand is 32 rows of M read straight from memory
+// into MFMA operand registers (16-byte loads), X is the B operand (16-byte LDS
+// rows), and each accumulator lane ends up holding 4 consecutive columns of
+// one row of X M, which are stored as one 8-byte LDS write per half or one
+// 16-byte global store.
 constexpr int SB = 136;
 
-// hi/lo split of one fp32 value
-__device__ __forceinline__ void split_bf16(float x, __bf16& h, __bf16& l) {
-  h = (__bf16)x;
-  l = (__bf16)(x - (float)h);
+// A wave's 32 rows (jr + l % 32) of a d_k x d_k fp32 matrix in A-operand order:
+// v[2 kk + h] = channels 16 kk + 8 (l / 32) + 4 h .. + 3.  Addresses are
+// clamped into the matrix; tile_split zeroes what lies outside.
+struct TileF32 {
+  f32x4_t v[16];
+};
+struct TileSplit {
+  u32x4_t h[8], l[8];
+};
+
+__device__ __forceinline__ void tile_rows_load(TileF32& t, const float* M, int dk, int jr) {
+  const int lane = lane_id();
+  const float* p = M + (size_t)min(jr + (lane & 31), dk - 1) * dk + 8 * (lane >> 5);
+#pragma unroll
+  for (int kk = 0; kk < 8; ++kk) {
+    const int k = min(16 * kk, dk - 16);
+    t.v[2 * kk] = *reinterpret_cast<const f32x4_t*>(p + k);
+    t.v[2 * kk + 1] = *reinterpret_cast<const f32x4_t*>(p + k + 4);
+  }
 }
 
-// MatRegs (row-major rows x cols, zero padded) -> (hi, lo) LDS, as stored
-// (transpose = false) or transposed (true).
-__device__ __forceinline__ void mat_store_split(const MatRegs& m, __bf16* hi, __bf16* lo, int R,
-                                                int C, bool transpose) {
+// fp32 -> (hi, lo) bf16 operand pairs: hi = bf16(x), lo = bf16(x - hi)
+__device__ __forceinline__ void split_pair(float x0, float x1, uint32_t& h, uint32_t& l) {
+  h = pack_bf16(x0, x1);
+  l = pack_bf16(x0 - bf16_lo(h), x1 - bf16_hi(h));
+}
+
+__device__ __forceinline__ void tile_split(TileSplit& s, const TileF32& t, int dk, int jr) {
+  const bool ok = jr + (lane_id() & 31) < dk;
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const int id = threadIdx.x + 256 * i;
-    const int r = id >> 5;
-    const int c = (id & 31) << 2;
-    if (r < R && c < C) {
-      __bf16 h[4], l[4];
+  for (int kk = 0; kk < 8; ++kk) {
+    uint32_t h[4], l[4];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) split_bf16(m.v[i][e], h[e], l[e]);
-      if (!transpose) {
-        bf16x2_t h01 = {h[0], h[1]}, h23 = {h[2], h[3]}, l01 = {l[0], l[1]}, l23 = {l[2], l[3]};
-        u32x2_t hv = {__builtin_bit_cast(uint32_t, h01), __builtin_bit_cast(uint32_t, h23)};
-        u32x2_t lv = {__builtin_bit_cast(uint32_t, l01), __builtin_bit_cast(uint32_t, l23)};
-        *reinterpret_cast<u32x2_t*>(hi + r * SB + c) = hv;
-        *reinterpret_cast<u32x2_t*>(lo + r * SB + c) = lv;
-      } else {
+    for (int e = 0; e < 4; ++e) {
+      const f32x4_t& v = t.v[2 * kk + (e >> 1)];
+      const float x0 = ok ? v[2 * (e & 1)] : 0.0f;
+      const float x1 = ok ? v[2 * (e & 1) + 1] : 0.0f;
+      split_pair(x0, x1, h[e], l[e]);
+    }
+    s.h[kk] = u32x4_t{h[0], h[1], h[2], h[3]};
+    s.l[kk] = u32x4_t{l[0], l[1], l[2], l[3]};
+  }
+}
+
+// acc[x] += T for the X row tiles xr0 + 32 x (x < NX), nk = d_k / 16 k-steps:
+// hi*hi + lo*hi + hi*lo with fp32 accumulation.
+template <int NX>
+__device__ __forceinline__ void split_mm_t(f32x16_t (&acc)[NX], const TileSplit& m,
+                                           const __bf16* xh, const __bf16* xl, int xr0, int nk) {
+  const int lane = lane_id();
+  const int base = (xr0 + (lane & 31)) * SB + 8 * (lane >> 5);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          hi[(c + e) * SB + r] = h[e];
-          lo[(c + e) * SB + r] = l[e];
-        }
+  for (int kk = 0; kk < 8; ++kk) {
+    if (kk < nk) {
+#pragma unroll
+      for (int x = 0; x < NX; ++x) {
+        const int off = base + 32 * x * SB + 16 * kk;
+        const u32x4_t bh = *reinterpret_cast<const u32x4_t*>(xh + off);
+        const u32x4_t bl = *reinterpret_cast<const u32x4_t*>(xl + off);
+        acc[x] = mfma_bf16(m.h[kk], bh, acc[x]);
+        acc[x] = mfma_bf16(m.l[kk], bh, acc[x]);
+        acc[x] = mfma_bf16(m.h[kk], bl, acc[x]);
       }
     }
   }
 }
 
-// acc (+) = X_tile(rows xr.., all K) * B^T where B is given by rows (B[j][k]):
-// 32 x 32 output tile at B rows jr.., K = Kp (multiple of 16) channels.
-__device__ __forceinline__ f32x16_t split_mm(f32x16_t acc, const __bf16* xh, const __bf16* xl,
-                                             int xr, const __bf16* bh, const __bf16* bl, int jr,
-                                             int Kp) {
-  const int lane = lane_id();
-  const int il = lane & 31;
-  const int g = lane >> 5;
-  for (int k0 = 0; k0 < Kp; k0 += 16) {
-    const int ka = (xr + il) * SB + k0 + 8 * g;
-    const int kb = (jr + il) * SB + k0 + 8 * g;
-    const u32x4_t ah = *reinterpret_cast<const u32x4_t*>(xh + ka);
-    const u32x4_t al = *reinterpret_cast<const u32x4_t*>(xl + ka);
-    const u32x4_t bh_ = *reinterpret_cast<const u32x4_t*>(bh + kb);
-    const u32x4_t bl_ = *reinterpret_cast<const u32x4_t*>(bl + kb);
-    acc = mfma_bf16(ah, bh_, acc);
-    acc = mfma_bf16(ah, bl_, acc);
-    acc = mfma_bf16(al, bh_, acc);
-  }
-  return acc;
-}
+// Half (channels 64 kh .. + 63) of a wave's 32 rows of a d_k x d_k fp32
+// matrix, in the same operand order (clamped like tile_rows_load).
+struct HalfTileF32 {
+  f32x4_t v[8];
+};
 
-// store one fp32 32x32 accumulator tile (rows r0.., cols c0..) into (hi, lo) LDS
-__device__ __forceinline__ void acc_store_split(__bf16* hi, __bf16* lo, const f32x16_t& acc,
-                                                const float (&add)[16], int r0, int c0) {
+__device__ __forceinline__ void half_tile_load(HalfTileF32& t, const float* M, int dk, int jr,
+                                               int kh) {
   const int lane = lane_id();
-  const int col = c0 + (lane & 31);
+  const float* p = M + (size_t)min(jr + (lane & 31), dk - 1) * dk + 8 * (lane >> 5);
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int row = r0 + acc_row(r, lane);
-    __bf16 h, l;
-    split_bf16(acc[r] + add[r], h, l);
-    hi[row * SB + col] = h;
-    lo[row * SB + col] = l;
+  for (int kk = 0; kk < 4; ++kk) {
+    const int k = min(64 * kh + 16 * kk, dk - 16);
+    t.v[2 * kk] = *reinterpret_cast<const f32x4_t*>(p + k);
+    t.v[2 * kk + 1] = *reinterpret_cast<const f32x4_t*>(p + k + 4);
   }
 }
 
-__global__ __launch_bounds__(256, 1) void compose_split_kernel(const float* __restrict__ Bw,
-                                                              const float* __restrict__ Mw,
-                                                              float* __restrict__ Mc,
-                                                              float* __restrict__ McT,
-                                                              float* __restrict__ Jf,
-                                                              float* __restrict__ Jr, int dk,
-                                                              int dv, int F, int C, int n,
-                                                              int units, unsigned per) {
+// ... split into (hi, lo) rows of LDS (row jr + l % 32, 16-byte pieces),
+// zero outside the d_k x d_k matrix
+__device__ __forceinline__ void half_tile_store(__bf16* mh, __bf16* ml, const HalfTileF32& t,
+                                                int dk, int jr, int kh) {
+  const int lane = lane_id();
+  const int row = jr + (lane & 31);
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) {
+    const int k0 = 64 * kh + 16 * kk;
+    const bool ok = row < dk && k0 < dk;
+    uint32_t h[4], l[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const f32x4_t& v = t.v[2 * kk + (e >> 1)];
+      split_pair(ok ? v[2 * (e & 1)] : 0.0f, ok ? v[2 * (e & 1) + 1] : 0.0f, h[e], l[e]);
+    }
+    const int off = row * SB + k0 + 8 * (lane >> 5);
+    *reinterpret_cast<u32x4_t*>(mh + off) = u32x4_t{h[0], h[1], h[2], h[3]};
+    *reinterpret_cast<u32x4_t*>(ml + off) = u32x4_t{l[0], l[1], l[2], l[3]};
+  }
+}
+
+// split_mm_t with the transition operand read from (hi, lo) LDS rows jr ..
+template <int NX>
+__device__ __forceinline__ void split_mm_t_lds(f32x16_t (&acc)[NX], const __bf16* mh,
+                                               const __bf16* ml, int jr, const __bf16* xh,
+                                               const __bf16* xl, int xr0, int nk) {
+  const int lane = lane_id();
+  const int mbase = (jr + (lane & 31)) * SB + 8 * (lane >> 5);
+  const int base = (xr0 + (lane & 31)) * SB + 8 * (lane >> 5);
+#pragma unroll
+  for (int kk = 0; kk < 8; ++kk) {
+    if (kk < nk) {
+      const u32x4_t ah = *reinterpret_cast<const u32x4_t*>(mh + mbase + 16 * kk);
+      const u32x4_t al = *reinterpret_cast<const u32x4_t*>(ml + mbase + 16 * kk);
+#pragma unroll
+      for (int x = 0; x < NX; ++x) {
+        const int off = base + 32 * x * SB + 16 * kk;
+        const u32x4_t bh = *reinterpret_cast<const u32x4_t*>(xh + off);
+        const u32x4_t bl = *reinterpret_cast<const u32x4_t*>(xl + off);
+        acc[x] = mfma_bf16(ah, bh, acc[x]);
+        acc[x] = mfma_bf16(al, bh, acc[x]);
+        acc[x] = mfma_bf16(ah, bl, acc[x]);
+      }
+    }
+  }
+}
+
+// The accumulator's share of a row-major rows x d_k fp32 matrix in the
+// transposed layout: b[x][q] = row xr0 + 32 x + l % 32, columns
+// jr + 8 q + 4 (l / 32) .. + 3 (clamped; out_mask() says what is real).
+template <int NX>
+__device__ __forceinline__ void rows_prefetch_t(f32x4_t (&b)[NX][4], const float* src, int rows,
+                                                int dk, int xr0, int jr) {
+  const int lane = lane_id();
+#pragma unroll
+  for (int x = 0; x < NX; ++x) {
+    const int row = min(xr0 + 32 * x + (lane & 31), rows - 1);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int col = min(jr + 8 * q + 4 * (lane >> 5), dk - 4);
+      b[x][q] = *reinterpret_cast<const f32x4_t*>(src + (size_t)row * dk + col);
+    }
+  }
+}
+
+__device__ __forceinline__ bool out_ok(int rows, int dk, int xr0, int x, int jr, int q) {
+  const int lane = lane_id();
+  return xr0 + 32 * x + (lane & 31) < rows && jr + 8 * q + 4 * (lane >> 5) < dk;
+}
+
+// the 4 values of accumulator x, group q (+ b when given and real)
+template <int NX>
+__device__ __forceinline__ f32x4_t out_quad(const f32x16_t (&acc)[NX], int x, int q) {
+  return f32x4_t{acc[x][4 * q], acc[x][4 * q + 1], acc[x][4 * q + 2], acc[x][4 * q + 3]};
+}
+
+__device__ __forceinline__ void x_store_quad(__bf16* xh, __bf16* xl, int row, int col, f32x4_t v) {
+  uint32_t h0, l0, h1, l1;
+  split_pair(v[0], v[1], h0, l0);
+  split_pair(v[2], v[3], h1, l1);
+  *reinterpret_cast<u32x2_t*>(xh + row * SB + col) = u32x2_t{h0, h1};
+  *reinterpret_cast<u32x2_t*>(xl + row * SB + col) = u32x2_t{l0, l1};
+}
+
+// Row-major rows x d_k fp32 matrix (times scale) -> (hi, lo) LDS rows
+// [0, pad32(rows)), zero padded; rows == 0 gives the identity (d_k x d_k).
+// By the first 256 threads of the workgroup.
+__device__ __forceinline__ void x_fill(__bf16* xh, __bf16* xl, const float* src, int rows, int dk,
+                                       float scale) {
+  const int t = threadIdx.x;
+  if (t >= 256) return;
+  const int R = pad32(rows == 0 ? dk : rows);
+  MatRegs m;
+  if (rows > 0) {
+    mat_load(m, src, dk, rows, dk);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int id = t + 256 * i;
+      const int r = id >> 5;
+      const int c = (id & 31) << 2;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) m.v[i][e] = (r == c + e && r < dk) ? 1.0f : 0.0f;
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int id = t + 256 * i;
+    const int r = id >> 5;
+    const int c = (id & 31) << 2;
+    if (r < R) x_store_quad(xh, xl, r, c, scale * m.v[i]);
+  }
+}
+
+// compose (bf16): one workgroup of 8 waves per work item; wave w owns output
+// columns jr = 32 (w % 4) .. + 31 for X rows 64 (w / 4) .. + 63.  The two waves
+// of a column block load one half each of the transition rows they share and
+// stage them, split, in LDS.  Work items: (unit, chunk, chain) with the chain
+// fastest (the three chains of a chunk read the same transitions and share an
+// XCD), then one text-seed item per unit.
+template <bool FULL>
+__global__ __launch_bounds__(512, 1) void compose_split_kernel(
+    const float* __restrict__ Bw, const float* __restrict__ Mw, float* __restrict__ Mc,
+    float* __restrict__ McT, float* __restrict__ Jf, float* __restrict__ Jr,
+    float* __restrict__ ST, int dk, int dv, int F, int C, int n, int units, unsigned per,
+    float seed_scale) {
   __shared__ __align__(16) __bf16 Xh[128 * SB];
   __shared__ __align__(16) __bf16 Xl[128 * SB];
   __shared__ __align__(16) __bf16 Mh[128 * SB];
   __shared__ __align__(16) __bf16 Ml[128 * SB];
-  // work item = (unit, chunk, chain), chain fastest: the three chains of a chunk
-  // read the same transitions and share an XCD
   const unsigned item = xcd_item(per);
-  if (item >= (unsigned)units * n * 3) return;
-  const int chain = item % 3;  // 0: Mc, 1: Jf, 2: Jr
-  const int c = (item / 3) % n;
-  const int u = item / (3 * n);
-  const int t = threadIdx.x;
-  const int lane = t & 63;
-  const int w = t >> 6;
-  const int f0 = c * C;
-  const int f1 = min(f0 + C, F);
+  const unsigned chain_items = (unsigned)units * n * 3;
+  if (item >= chain_items + units) return;
+  const bool seed = item >= chain_items;
+  const int chain = seed ? 3 : item % 3;  // 0: Mc, 1: Jf, 2: Jr, 3: seed
+  const int c = seed ? 0 : (item / 3) % n;
+  const int u = seed ? item - chain_items : item / (3 * n);
+  const int w = threadIdx.x >> 6;
+  const int jr = 32 * (w & 3);
+  const int kh = w >> 2;
+  const int xr0 = 64 * kh;
+  const int nk = FULL ? 8 : dk >> 4;
+  // the seed is the text frame's map applied once: (0 + s B_T) M_T
+  const int f0 = seed ? -1 : c * C;
+  const int f1 = seed ? 0 : min(f0 + C, F);
   const int nf = f1 - f0;
   const int rows = chain == 0 ? dk : dv;
-  const int nR = pad32(rows) >> 5;
-  const int Dk = pad32(dk);
-  const int nb = Dk >> 5;
-  const int Kp = (dk + 15) & ~15;
   const size_t Fp1 = (size_t)F + 1;
+  const size_t SS = (size_t)dv * dk;
+  // workspace frame index f + 1 holds latent frame f (index 0 is the text frame)
   auto frame = [&](int s) { return chain == 2 ? f1 - 1 - s : f0 + s; };
   auto Mp = [&](int f) { return Mw + ((size_t)u * Fp1 + f + 1) * dk * dk; };
-  auto Bp = [&](int f) { return Bw + ((size_t)u * Fp1 + f + 1) * dv * dk; };
+  auto Bp = [&](int f) { return Bw + ((size_t)u * Fp1 + f + 1) * SS; };
+  const bool active = jr < dk && xr0 < rows;
 
-  {
-    MatRegs m;
-    if (chain != 0) {
-      mat_load(m, Bp(frame(0)), dk, dv, dk);
-      mat_store_split(m, Xh, Xl, pad32(rows), Dk, false);
-    } else {
-      for (int idx = t; idx < Dk * Dk; idx += 256) {
-        const int i = idx / Dk;
-        const int j = idx - i * Dk;
-        Xh[i * SB + j] = (__bf16)(i == j ? 1.0f : 0.0f);
-        Xl[i * SB + j] = (__bf16)0.0f;
-      }
-    }
-    mat_load(m, Mp(frame(0)), dk, dk, dk);
-    mat_store_split(m, Mh, Ml, Dk, Dk, false);
-  }
+  HalfTileF32 mf;
+  half_tile_load(mf, Mp(frame(0)), dk, jr, kh);
+  x_fill(Xh, Xl, chain == 0 ? nullptr : Bp(frame(0)), chain == 0 ? 0 : dv, dk,
+         seed ? seed_scale : 1.0f);
+  half_tile_store(Mh, Ml, mf, dk, jr, kh);
   __syncthreads();
 
   float* dst = chain == 0 ? Mc + ((size_t)u * n + c) * dk * dk
-                          : (chain == 1 ? Jf : Jr) + ((size_t)u * n + c) * dv * dk;
-  MatRegs mnext;
-  float bnext[4][16];
+               : seed     ? ST + (size_t)u * 2 * (n + 1) * SS  // P[0]
+                          : (chain == 1 ? Jf : Jr) + ((size_t)u * n + c) * SS;
+  float* dst2 = seed ? ST + ((size_t)(u * 2 + 1) * (n + 1) + n) * SS  // R[n]
+                     : McT + ((size_t)u * n + c) * dk * dk;
+  const int lane = threadIdx.x & 63;
+  f32x4_t bq[2][4];
   for (int s = 0; s < nf; ++s) {
     const bool last = s == nf - 1;
-    if (!last) {  // next frame's transition (and write) fly while this step multiplies
-      mat_load(mnext, Mp(frame(s + 1)), dk, dk, dk);
-#pragma unroll
-      for (int ct = 0; ct < 4; ++ct) {
-        if (chain != 0 && w < nR && ct < nb)
-          tile_prefetch(bnext[ct], Bp(frame(s + 1)), dk, dv, 32 * w, 32 * ct);
-        else
-#pragma unroll
-          for (int r = 0; r < 16; ++r) bnext[ct][r] = 0.0f;
-      }
+    if (!last) {  // the next frame's transition and write fly while this step multiplies
+      half_tile_load(mf, Mp(frame(s + 1)), dk, jr, kh);
+      if (chain != 0) rows_prefetch_t<2>(bq, Bp(frame(s + 1)), dv, dk, xr0, jr);
     }
-    f32x16_t acc[4];
+    f32x16_t acc[2] = {zero16(), zero16()};
+    if (active) split_mm_t_lds<2>(acc, Mh, Ml, jr, Xh, Xl, xr0, nk);
+    __syncthreads();  // every wave has read X and M
+    if (last) {
+      if (active) {
 #pragma unroll
-    for (int ct = 0; ct < 4; ++ct) acc[ct] = zero16();
-    if (w < nR) {
+        for (int x = 0; x < 2; ++x)
 #pragma unroll
-      for (int ct = 0; ct < 4; ++ct)
-        if (ct < nb) acc[ct] = split_mm(acc[ct], Xh, Xl, 32 * w, Mh, Ml, 32 * ct, Kp);
-    }
-    __syncthreads();
-    if (w < nR) {
+          for (int q = 0; q < 4; ++q) {
+            if (!out_ok(rows, dk, xr0, x, jr, q)) continue;
+            const int row = xr0 + 32 * x + (lane & 31);
+            const int col = jr + 8 * q + 4 * (lane >> 5);
+            const f32x4_t v = out_quad(acc, x, q);
+            *reinterpret_cast<f32x4_t*>(dst + (size_t)row * dk + col) = v;
+            if (seed) {
+              *reinterpret_cast<f32x4_t*>(dst2 + (size_t)row * dk + col) = v;
+            } else if (chain == 0) {
 #pragma unroll
-      for (int ct = 0; ct < 4; ++ct) {
-        if (ct >= nb) continue;
-        if (last) {
-          const int col = 32 * ct + (lane & 31);
-          float* dstT = McT + ((size_t)u * n + c) * dk * dk;
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int row = 32 * w + acc_row(r, lane);
-            if (row < rows && col < dk) {
-              dst[(size_t)row * dk + col] = acc[ct][r];
-              if (chain == 0) dstT[(size_t)col * dk + row] = acc[ct][r];
+              for (int e = 0; e < 4; ++e) dst2[(size_t)(col + e) * dk + row] = v[e];
             }
           }
-        } else {
-          acc_store_split(Xh, Xl, acc[ct], bnext[ct], 32 * w, 32 * ct);
-        }
       }
+      break;
     }
-    if (last) break;
-    mat_store_split(mnext, Mh, Ml, Dk, Dk, false);
+    if (active) {
+#pragma unroll
+      for (int x = 0; x < 2; ++x)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          f32x4_t v = out_quad(acc, x, q);
+          if (chain != 0 && out_ok(rows, dk, xr0, x, jr, q)) v += bq[x][q];
+          x_store_quad(Xh, Xl, xr0 + 32 * x + (lane & 31), jr + 8 * q + 4 * (lane >> 5), v);
+        }
+    }
+    half_tile_store(Mh, Ml, mf, dk, jr, kh);
     __syncthreads();
   }
 }
 
+// scan (bf16): one workgroup per (32-row block of the state, unit, direction);
+// wave w owns state columns 32 w .. + 31.  The transition operand of the
+// forward step S Mc is read from the rows of Mc^T, that of the reverse step
+// S Mc^T from the rows of Mc.  Transitions and injections are fetched one
+// chunk ahead, unconditionally (the last step refetches its own chunk), and the
+// injections alternate between two register sets, so that no wait for a
+// load also waits for the state stores issued after it.  FULL: d_k = 128 and
+// d_v a multiple of 32 (no masking anywhere).
+template <bool FULL>
 __global__ __launch_bounds__(256) void scan_split_kernel(const float* __restrict__ McR,
                                                          const float* __restrict__ McTr,
                                                          const float* __restrict__ Jf,
@@ -409,91 +556,97 @@ __global__ __launch_bounds__(256) void scan_split_kernel(const float* __restrict
                                                          int n) {
   __shared__ __align__(16) __bf16 Xh[32 * SB];
   __shared__ __align__(16) __bf16 Xl[32 * SB];
-  __shared__ __align__(16) __bf16 Mh[128 * SB];
-  __shared__ __align__(16) __bf16 Ml[128 * SB];
   const int rb = blockIdx.x;  // rows [32 rb, 32 rb + 32) of the state
   const int u = blockIdx.y;
   const int dir = blockIdx.z;  // 0: forward (P), 1: reverse (R)
-  const int t = threadIdx.x;
-  const int lane = t & 63;
-  const int w = t >> 6;
-  const int Dk = pad32(dk);
-  const int nb = Dk >> 5;
-  const int Kp = (dk + 15) & ~15;
+  const int lane = threadIdx.x & 63;
+  const int jr = 32 * (threadIdx.x >> 6);
+  const int nk = FULL ? 8 : dk >> 4;
   const size_t SS = (size_t)dv * dk;
   float* S = ST + (size_t)(u * 2 + dir) * (n + 1) * SS;
   const int r0 = 32 * rb;
-  const int nrows = min(32, dv - r0);
+  const int nrows = FULL ? 32 : min(32, dv - r0);
   auto chunk = [&](int s) { return dir == 0 ? s : n - 1 - s; };
-  const float* Jb = (dir == 0 ? Jf : Jr) + (size_t)u * n * SS;
-  // the B operand is read by rows: forward S Mc needs the rows of Mc^T, reverse
-  // S Mc^T the rows of Mc
-  const float* Mc = dir == 0 ? McTr : McR;
+  const float* Jb = (dir == 0 ? Jf : Jr) + (size_t)u * n * SS + (size_t)r0 * dk;
+  const float* Mb = (dir == 0 ? McTr : McR) + (size_t)u * n * dk * dk;
+  const bool active = FULL || jr < dk;
 
-  MatRegs m;
-  mat_load(m, S + (size_t)(dir == 0 ? 0 : n) * SS + (size_t)r0 * dk, dk, nrows, dk);
-  mat_store_split(m, Xh, Xl, 32, Dk, false);
-  mat_load(m, Mc + ((size_t)u * n + chunk(0)) * dk * dk, dk, dk, dk);
-  mat_store_split(m, Mh, Ml, Dk, Dk, false);
-  float jreg[16];
-  if (w < nb) tile_prefetch(jreg, Jb + (size_t)chunk(0) * SS + (size_t)r0 * dk, dk, nrows, 0, 32 * w);
+  TileF32 mf;
+  TileSplit ms;
+  f32x4_t ja[1][4], jb[1][4];
+  tile_rows_load(mf, Mb + (size_t)chunk(0) * dk * dk, dk, jr);
+  rows_prefetch_t<1>(ja, Jb + (size_t)chunk(0) * SS, nrows, dk, 0, jr);
+  x_fill(Xh, Xl, S + (size_t)(dir == 0 ? 0 : n) * SS + (size_t)r0 * dk, nrows, dk, 1.0f);
+  tile_split(ms, mf, dk, jr);
   __syncthreads();
-  const float zero[16] = {0.0f};
-  for (int s = 0; s < n; ++s) {
+
+  // one chunk: X <- X Mc_j + J_j using jcur, fetching chunk s + 1 into jnext
+  auto step = [&](int s, f32x4_t (&jcur)[1][4], f32x4_t (&jnext)[1][4]) {
     const int j = chunk(s);
-    const bool last = s == n - 1;
-    float jnext[16];
-    if (!last) {
-      mat_load(m, Mc + ((size_t)u * n + chunk(s + 1)) * dk * dk, dk, dk, dk);
-      if (w < nb)
-        tile_prefetch(jnext, Jb + (size_t)chunk(s + 1) * SS + (size_t)r0 * dk, dk, nrows, 0, 32 * w);
-    }
-    f32x16_t acc = zero16();
-    if (w < nb) acc = split_mm(acc, Xh, Xl, 0, Mh, Ml, 32 * w, Kp);
-    __syncthreads();
-    if (w < nb) {
-      float* dstp = S + (size_t)(dir == 0 ? j + 1 : j) * SS;
-      const int col = 32 * w + (lane & 31);
-      f32x16_t x;
+    const int sn = min(s + 1, n - 1);
+    tile_rows_load(mf, Mb + (size_t)chunk(sn) * dk * dk, dk, jr);
+    rows_prefetch_t<1>(jnext, Jb + (size_t)chunk(sn) * SS, nrows, dk, 0, jr);
+    f32x16_t acc[1] = {zero16()};
+    if (active) split_mm_t<1>(acc, ms, Xh, Xl, 0, nk);
+    __syncthreads();  // every wave has read X
+    if (active) {
+      float* dstp = S + (size_t)(dir == 0 ? j + 1 : j) * SS + (size_t)r0 * dk;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = acc_row(r, lane);
-        const bool ok = row < nrows && col < dk;
-        x[r] = ok ? acc[r] + jreg[r] : 0.0f;
-        if (ok) dstp[(size_t)(r0 + row) * dk + col] = x[r];
+      for (int q = 0; q < 4; ++q) {
+        const int row = lane & 31;
+        const int col = jr + 8 * q + 4 * (lane >> 5);
+        const bool ok = FULL || out_ok(nrows, dk, 0, 0, jr, q);
+        f32x4_t v = out_quad(acc, 0, q);
+        if (ok) v += jcur[0][q];
+        if (FULL || ok) *reinterpret_cast<f32x4_t*>(dstp + (size_t)row * dk + col) = v;
+        x_store_quad(Xh, Xl, row, col, v);
       }
-      acc_store_split(Xh, Xl, x, zero, 0, 32 * w);
     }
-    if (last) break;
-    mat_store_split(m, Mh, Ml, Dk, Dk, false);
-#pragma unroll
-    for (int r = 0; r < 16; ++r) jreg[r] = jnext[r];
+    tile_split(ms, mf, dk, jr);
     __syncthreads();
+  };
+  int s = 0;
+  for (; s + 1 < n; s += 2) {
+    step(s, ja, jb);
+    step(s + 1, jb, ja);
   }
+  if (s < n) step(s, ja, jb);
 }
 
 }  // namespace
 
 hipError_t launch_compose(const Plan& p, const WsPtrs& w, hipStream_t s) {
+  const float seed_scale = p.seed_mode == 1 ? 1.0f : 0.5f;
   if (p.dtype == VDA_DTYPE_BF16) {
-    const unsigned per = xcd_per((unsigned)p.units * p.n * 3);
-    hipLaunchKernelGGL(compose_split_kernel, dim3(kXcds * per), dim3(kThreads), 0, s, w.B, w.M,
-                       w.Mc, w.McT, w.Jf, w.Jr, p.dk, p.dv, p.F, p.C, p.n, p.units, per);
+    const unsigned per = xcd_per((unsigned)p.units * (p.n * 3 + 1));
+    if (p.dk == 128)
+      hipLaunchKernelGGL(compose_split_kernel<true>, dim3(kXcds * per), dim3(512), 0, s, w.B, w.M,
+                         w.Mc, w.McT, w.Jf, w.Jr, w.ST, p.dk, p.dv, p.F, p.C, p.n, p.units, per,
+                         seed_scale);
+    else
+      hipLaunchKernelGGL(compose_split_kernel<false>, dim3(kXcds * per), dim3(512), 0, s, w.B,
+                         w.M, w.Mc, w.McT, w.Jf, w.Jr, w.ST, p.dk, p.dv, p.F, p.C, p.n, p.units,
+                         per, seed_scale);
   } else {
-    hipLaunchKernelGGL(compose_kernel, dim3(p.n, p.units, 3), dim3(kThreads), 0, s, w.B, w.M, w.Mc,
-                       w.McT, w.Jf, w.Jr, p.dk, p.dv, p.F, p.C, p.n);
+    hipLaunchKernelGGL(compose_kernel, dim3(p.n, p.units, 4), dim3(kThreads), 0, s, w.B, w.M, w.Mc,
+                       w.McT, w.Jf, w.Jr, w.ST, p.dk, p.dv, p.F, p.C, p.n, seed_scale);
   }
   return hipGetLastError();
 }
 
 hipError_t launch_scan(const Plan& p, const WsPtrs& w, hipStream_t s) {
   const dim3 grid(pad32(p.dv) >> 5, p.units, 2);
-  if (p.dtype == VDA_DTYPE_BF16)
-    hipLaunchKernelGGL(scan_split_kernel, grid, dim3(kThreads), 0, s, w.Mc, w.McT, w.Jf, w.Jr, w.ST,
-                       p.dk, p.dv, p.n);
-  else
+  if (p.dtype == VDA_DTYPE_BF16) {
+    if (p.dk == 128 && p.dv % 32 == 0)
+      hipLaunchKernelGGL(scan_split_kernel<true>, grid, dim3(kThreads), 0, s, w.Mc, w.McT, w.Jf,
+                         w.Jr, w.ST, p.dk, p.dv, p.n);
+    else
+      hipLaunchKernelGGL(scan_split_kernel<false>, grid, dim3(kThreads), 0, s, w.Mc, w.McT, w.Jf,
+                         w.Jr, w.ST, p.dk, p.dv, p.n);
+  } else {
     hipLaunchKernelGGL(scan_kernel, grid, dim3(kThreads), 0, s, w.Mc, w.Jf, w.Jr, w.ST, p.dk, p.dv,
                        p.n);
+  }
   return hipGetLastError();
 }
 

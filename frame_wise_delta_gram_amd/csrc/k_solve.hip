@@ -1,9 +1,8 @@
 // Transition of the frame-wise delta rule ("Video DeltaNet", arXiv 2609.20744,
 // Sec. 3.2 Eq. (5) and App. A.1 Eq. (A.1) with alpha = 1):
 //   M_t = (I + A_t)^{-1}
-// for every (unit, frame), and the text seed (Sec. 2.2 Eq. (1b)):
-//   seed = s * B_T M_T,  s = 1/2 (S_T / 2), or s = 1 when the text frame's
-//   write strengths were already halved.
+// for every (unit, frame), the text frame included (its map seeds the scans;
+// the chunk composition applies it).
 //
 // I + A_t is symmetric positive definite with every eigenvalue >= 1 (A_t is a
 // Gram matrix), so a Cholesky factorisation without pivoting is stable and its
@@ -87,10 +86,7 @@ __device__ void factor_invert_diag_block(float* G) {
 }
 
 __global__ __launch_bounds__(256, 3) void solve_kernel(const float* __restrict__ A,
-                                                      const float* __restrict__ B,
-                                                      float* __restrict__ Mout,
-                                                      float* __restrict__ STt, int dk, int dv,
-                                                      int Fp1, int n, float seed_scale) {
+                                                      float* __restrict__ Mout, int dk, int Fp1) {
   __shared__ float Gs[kNBlk * kBlk];  // block (i, j), j <= i, at index i (i + 1) / 2 + j
   const int fi = blockIdx.x;
   const int u = blockIdx.y;
@@ -184,50 +180,13 @@ __global__ __launch_bounds__(256, 3) void solve_kernel(const float* __restrict__
         }
       }
   }
-
-  // 4. text frame: seed = seed_scale * B_T M_T (M_T read back from global memory,
-  //    where this workgroup just wrote it), stored as P[0] and R[n]
-  if (fi == 0) {
-    __threadfence();
-    __syncthreads();
-    const int nV = pad32(dv) >> 5;
-    if (w < nV) {
-      const float* Bg = B + (size_t)u * Fp1 * dv * dk;
-      float* P0 = STt + ((size_t)(u * 2 + 0) * (n + 1) + 0) * dv * dk;
-      float* Rn = STt + ((size_t)(u * 2 + 1) * (n + 1) + n) * dv * dk;
-      const int il = lane & 31;
-      const int kh = lane >> 5;
-      const int row = 32 * w + il;
-      for (int ct = 0; ct < nb; ++ct) {
-        const int col = 32 * ct + il;
-        f32x16_t acc = zero16();
-        for (int kk = 0; kk < Dk / 2; ++kk) {
-          const int kx = 2 * kk + kh;
-          const float a = (row < dv && kx < dk) ? Bg[(size_t)row * dk + kx] : 0.0f;
-          const float b = (kx < dk && col < dk) ? Mg[(size_t)kx * dk + col] : 0.0f;
-          acc = mfma_f32(a, b, acc);
-        }
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int orow = 32 * w + acc_row(r, lane);
-          if (orow < dv && col < dk) {
-            const float sv = seed_scale * acc[r];
-            P0[(size_t)orow * dk + col] = sv;
-            Rn[(size_t)orow * dk + col] = sv;
-          }
-        }
-      }
-    }
-  }
 }
 
 }  // namespace
 
 hipError_t launch_solve(const Plan& p, const WsPtrs& w, hipStream_t s) {
   const dim3 grid(p.F + 1, p.units);
-  const float seed_scale = p.seed_mode == 1 ? 1.0f : 0.5f;
-  hipLaunchKernelGGL(solve_kernel, grid, dim3(kThreads), 0, s, w.A, w.B, w.M, w.ST, p.dk, p.dv,
-                     p.F + 1, p.n, seed_scale);
+  hipLaunchKernelGGL(solve_kernel, grid, dim3(kThreads), 0, s, w.A, w.M, p.dk, p.F + 1);
   return hipGetLastError();
 }
 

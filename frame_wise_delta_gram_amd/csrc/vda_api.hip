@@ -233,7 +233,7 @@ int vda_debug_solve(const vda_desc_t* desc, const void* k, const void* v, const 
   if (!M_out || !seed_out) return VDA_ERR_INVALID_ARG;
   const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const WsPtrs w = vda::carve(p, workspace);
-  st = vda::run_states(p, k, v, beta, text_k, text_v, text_beta, w, s, 2);
+  st = vda::run_states(p, k, v, beta, text_k, text_v, text_beta, w, s, 3);  // seed: compose
   if (st != VDA_OK) return st;
   const size_t fr = (size_t)p.units * (p.F + 1);
   if (hipMemcpyAsync(M_out, w.M, fr * p.dk * p.dk * 4, hipMemcpyDeviceToDevice, s) != hipSuccess)

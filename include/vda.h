@@ -140,6 +140,8 @@ int vda_debug_stats(const vda_desc_t* desc, const void* k, const void* v, const 
                     vda_stream_t stream);
 
 /* Transitions M_t = (I + A_t)^{-1} ([VDN] Eq. (A.1)) and the seed ([VDN] Eq. (1b)).
+ * Runs the pipeline through the chunk composition, which applies the text
+ * frame's map to form the seed.
  * M_out [units][frames + 1][d_k][d_k] (index 0: text frame), seed_out [units][d_v][d_k]. */
 int vda_debug_solve(const vda_desc_t* desc, const void* k, const void* v, const float* beta,
                     const void* text_k, const void* text_v, const float* text_beta,
