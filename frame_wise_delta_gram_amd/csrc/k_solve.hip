@@ -5,23 +5,22 @@
 // the chunk composition applies it).
 //
 // I + A_t is symmetric positive definite with every eigenvalue >= 1 (A_t is a
-// Gram matrix), so a Cholesky factorisation without pivoting is stable and its
-// diagonal is >= 1.  One workgroup (4 waves) per frame keeps the lower
-// triangle of the d_k x d_k matrix in LDS as 32 x 32 blocks (fp32, row stride
-// 33), in place, and works block by block:
-//   1. blocked right-looking Cholesky  I + A = L L^T.  The 32-column diagonal
-//      block is factored by one wave in registers (lane c holds column c;
-//      pivots and columns move with readlane, no LDS round trips) and replaced
-//      by the inverse of its factor, W_pp = L_pp^{-1}.  Panel (L_ip = G_ip
-//      W_pp^T) and trailing (G_ij -= L_ip L_jp^T) updates are 32x32x32 fp32
-//      MFMA block products spread over the 4 waves;
-//   2. W = L^{-1} row block by row block: W_ij = -W_ii sum_{k=j}^{i-1} L_ik W_kj,
-//      the blocks of one row in parallel; each sum is held in registers until
-//      the whole row has read L, then parked in its own block for the W_ii
-//      product, so no staging buffer is needed;
-//   3. M = W^T W, the upper blocks by MFMA, mirrored on store.
-// 42 KiB of LDS per workgroup lets three workgroups share a CU, so their serial
-// diagonal work overlaps each other's MFMA work.  fp32 throughout.
+// Gram matrix), so Gauss-Jordan elimination in the symmetric "sweep" form
+// (Beaton 1964; Goodnight 1979, "A tutorial on the SWEEP operator") needs no
+// pivoting: every pivot is a diagonal entry of a Schur complement of I + A_t,
+// hence >= 1.  Sweeping index k of a symmetric matrix G with d = G_kk maps
+//   G_ij -> G_ij - G_ik G_kj / d   (i, j != k),
+//   G_ik -> G_ik / d,  G_kj -> G_kj / d,  G_kk -> -1 / d,
+// and sweeping every index turns G into -G^{-1}.  Applied to 32 x 32 blocks
+// (block P with S = G_PP^{-1}):
+//   G_PP -> -S,  G_Pi -> S G_Pi,  G_iP -> G_iP S,  G_ij -> G_ij - G_iP S G_Pj.
+// One workgroup (4 waves) per frame keeps the lower-triangle 32 x 32 blocks of
+// G = I + A_t in LDS (fp32, row stride 33).  Per pivot block: one wave sweeps
+// the block in its MFMA accumulators (below); each other wave forms one
+// Y_i = S G_Pi and the updates G_ji -= G_jP Y_i with 32x32x2 fp32 MFMA, Y_i
+// staying in registers as an MFMA operand.  At the end the blocks hold -M.
+// 42 KiB of LDS per workgroup lets three workgroups share a CU.  fp32
+// throughout.
 #include "vda_device.h"
 #include "vda_internal.h"
 
@@ -36,53 +35,63 @@ __device__ __forceinline__ float readlane_f(float x, int l) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), l));
 }
 
-// Factor the 32x32 SPD block at G (stride SG) as L L^T and overwrite it with
-// W = L^{-1} (lower triangular, zeros above the diagonal), by one wave.  The
-// pivots of I + A and of its Schur complements are >= 1, so the hardware
-// reciprocal square root (1 ulp) is safe.
-__device__ void factor_invert_diag_block(float* G) {
+// Sweep all 32 indices of the symmetric block T held in accumulator layout
+// (register r of lane l = T[acc_row(r, l)][l % 32]), by one wave; T becomes
+// -T^{-1}.  Row k sits in register rk = 4 (k / 8) + k % 4 of the lanes of half
+// hk = (k / 4) % 2, so it feeds both operands of a rank-1 32x32x2 MFMA through
+// the k-slot hk with no data movement: C_mn -= x_m y_n, x = row k (zero at k),
+// y = x / d.  Row and column k are then scaled in place and T_kk set to -1/d
+// (forming them through the rank-1 update would cancel catastrophically for
+// large pivots).  The hardware reciprocal is within 1 ulp.
+__device__ __forceinline__ void sweep_block(f32x16_t& T) {
   const int lane = lane_id();
-  const int c = lane & 31;  // lanes 32..63 duplicate lanes 0..31 and do not store
-  float col[32];
+  const int half = lane >> 5;
+  const int c = lane & 31;
 #pragma unroll
-  for (int k = 0; k < 32; ++k) col[k] = G[k * SG + c];  // column c (= row c)
+  for (int k = 0; k < 32; ++k) {
+    const int rk = 4 * (k >> 3) + (k & 3);
+    const int hk = (k >> 2) & 1;
+    const float d = readlane_f(T[rk], k + 32 * hk);
+    const float inv = __builtin_amdgcn_rcpf(d);
+    const bool inrow = half == hk;
+    const float x = (inrow && c != k) ? T[rk] : 0.0f;
+    T = mfma_f32(-x, x * inv, T);
+    const float fc = c == k ? inv : 1.0f;  // column k
+#pragma unroll
+    for (int r = 0; r < 16; ++r) T[r] *= fc;
+    T[rk] = inrow ? (c == k ? -inv : T[rk] * inv) : T[rk];  // row k, then the pivot
+  }
+}
 
-  float rinv[32];  // 1 / L[j][j]
+// acc += op(A) Bm for 32 x 32 blocks, A in LDS (row stride sa, op = transpose
+// when AT), Bm in accumulator layout (register r of lane l = Bm[acc_row(r, l)][l % 32]).
+// The contraction index of k-step r, slot h is acc_row(r, 32 h) on both sides.
+template <bool AT>
+__device__ __forceinline__ f32x16_t blk_mm32_breg(f32x16_t acc, const float* A, int sa,
+                                                  const f32x16_t& Bm) {
+  const int lane = lane_id();
+  const int m = lane & 31;
 #pragma unroll
-  for (int j = 0; j < 32; ++j) {
-    const float d = readlane_f(col[j], j);
-    const float inv = __builtin_amdgcn_rsqf(d);
-    rinv[j] = inv;
-    // lanes c > j: L[c][j] = D[c][j] / piv (own copy, the block is symmetric);
-    // t = L[c][j] / piv so that D[k][c] -= L[k][j] L[c][j] = D[k][j] * t
-    const float t = col[j] * (inv * inv);
-#pragma unroll
-    for (int k = j + 1; k < 32; ++k) {
-      const float dkj = readlane_f(col[j], k);  // D[k][j] = D[j][k], held by lane k
-      if (c > j) col[k] = fmaf(-dkj, t, col[k]);
-    }
-    if (c == j) {
-      col[j] = d * inv;
-#pragma unroll
-      for (int k = j + 1; k < 32; ++k) col[k] *= inv;
-    }
+  for (int r = 0; r < 16; ++r) {
+    const int k = acc_row(r, lane);
+    const float a = AT ? A[k * sa + m] : A[m * sa + k];
+    acc = mfma_f32(a, Bm[r], acc);
   }
-  // col[k] = L[k][c] for k >= c.  Column c of W = L^{-1}: solve L x = e_c
-  // right-looking, x[j] /= L[j][j] then x[i] -= L[i][j] x[j] for i > j (the
-  // updates of one step are independent); L[i][j] sits in lane j.
-  float x[32];
+  return acc;
+}
+
+__device__ __forceinline__ f32x16_t tile_from_lds(const float* G) {
+  const int lane = lane_id();
+  f32x16_t T;
 #pragma unroll
-  for (int k = 0; k < 32; ++k) x[k] = (k == c) ? 1.0f : 0.0f;
+  for (int r = 0; r < 16; ++r) T[r] = G[acc_row(r, lane) * SG + (lane & 31)];
+  return T;
+}
+
+__device__ __forceinline__ void tile_to_lds_t(float* G, const f32x16_t& T) {
+  const int lane = lane_id();
 #pragma unroll
-  for (int j = 0; j < 32; ++j) {
-    x[j] *= rinv[j];
-#pragma unroll
-    for (int i = j + 1; i < 32; ++i) x[i] = fmaf(-readlane_f(col[i], j), x[j], x[i]);
-  }
-  if (lane < 32) {
-#pragma unroll
-    for (int k = 0; k < 32; ++k) G[k * SG + c] = x[k];
-  }
+  for (int r = 0; r < 16; ++r) G[(lane & 31) * SG + acc_row(r, lane)] = T[r];
 }
 
 __global__ __launch_bounds__(256, 3) void solve_kernel(const float* __restrict__ A,
@@ -97,11 +106,11 @@ __global__ __launch_bounds__(256, 3) void solve_kernel(const float* __restrict__
   const int nb = Dk >> 5;
   auto G = [&](int i, int j) { return Gs + (i * (i + 1) / 2 + j) * kBlk; };
 
-  {
+  {  // G = I + A (identity on the padding too), lower-triangle blocks
     MatRegs m;
     mat_load(m, A + ((size_t)u * Fp1 + fi) * dk * dk, dk, dk, dk);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {  // keep the lower-triangle blocks, add the identity
+    for (int i = 0; i < 16; ++i) {
       const int id = t + 256 * i;
       const int r = id >> 5;
       const int c = (id & 31) << 2;
@@ -115,70 +124,62 @@ __global__ __launch_bounds__(256, 3) void solve_kernel(const float* __restrict__
     __syncthreads();
   }
 
-  // 1. blocked Cholesky; diagonal blocks end up holding W_pp = L_pp^{-1}
   for (int p = 0; p < nb; ++p) {
-    if (w == 0) factor_invert_diag_block(G(p, p));
+    if (w == 0) {  // G_PP -> -S
+      f32x16_t T = tile_from_lds(G(p, p));
+      sweep_block(T);
+      store_acc(G(p, p), SG, T, 1.0f);
+    }
     __syncthreads();
-    {  // panel: L_ip = G_ip L_pp^{-T} = G_ip W_pp^T
-      const int i = p + 1 + w;
-      if (i < nb) {
-        const f32x16_t acc = blk_mm32<false, true>(zero16(), G(i, p), SG, G(p, p), SG);
-        store_acc(G(i, p), SG, acc, 1.0f);
+    const int i = w < p ? w : w + 1;  // this wave's non-pivot block
+    const bool has = i < nb;
+    f32x16_t Y;
+    if (has) {
+      // Y_i = S G_Pi = -(G_PP) G_Pi with G_Pi = G(p, i) (i < p) or G(i, p)^T
+      Y = i < p ? blk_mm32<false, false>(zero16(), G(p, p), SG, G(p, i), SG)
+                : blk_mm32<false, true>(zero16(), G(p, p), SG, G(i, p), SG);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) Y[r] = -Y[r];
+      // G_ji -= G_jP Y_i for the lower blocks (j >= i) of this column, G_jP still old
+      for (int j = i; j < nb; ++j) {
+        if (j == p) continue;
+        const f32x16_t prod = j > p ? blk_mm32_breg<false>(zero16(), G(j, p), SG, Y)
+                                    : blk_mm32_breg<true>(zero16(), G(p, j), SG, Y);
+        float* C = G(j, i);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) C[acc_row(r, lane) * SG + (lane & 31)] -= prod[r];
       }
     }
-    __syncthreads();
-    {  // trailing: G_ij -= L_ip L_jp^T, p < j <= i
-      int q = 0;
-      for (int i = p + 1; i < nb; ++i)
-        for (int j = p + 1; j <= i; ++j, ++q) {
-          if ((q & 3) != w) continue;
-          const f32x16_t acc = blk_mm32<false, true>(zero16(), G(i, p), SG, G(j, p), SG);
-          float* C = G(i, j);
-#pragma unroll
-          for (int r = 0; r < 16; ++r) C[acc_row(r, lane) * SG + (lane & 31)] -= acc[r];
-        }
+    __syncthreads();  // every old G_jP has been read
+    if (has) {  // G_Pi -> Y_i, stored as block (p, i) or, transposed, (i, p)
+      if (i < p)
+        store_acc(G(p, i), SG, Y, 1.0f);
+      else
+        tile_to_lds_t(G(i, p), Y);
     }
     __syncthreads();
   }
 
-  // 2. off-diagonal blocks of W = L^{-1}, row block by row block
-  for (int i = 1; i < nb; ++i) {
-    f32x16_t acc = zero16();
-    if (w < i) {  // wave j = w: T_ij = sum_{k=j}^{i-1} L_ik W_kj
-      const int j = w;
-      for (int k = j; k < i; ++k) acc = blk_mm32<false, false>(acc, G(i, k), SG, G(k, j), SG);
-    }
-    __syncthreads();  // every L_ik of row i has been read
-    if (w < i) {      // W_ij = -W_ii T_ij, T_ij parked in block (i, j)
-      const int j = w;
-      store_acc(G(i, j), SG, acc, 1.0f);
-      wave_sync();
-      const f32x16_t acc2 = blk_mm32<false, false>(zero16(), G(i, i), SG, G(i, j), SG);
-      wave_sync();
-      store_acc(G(i, j), SG, acc2, -1.0f);
-    }
-    __syncthreads();
-  }
-
-  // 3. M = W^T W: M_ab = sum_{k >= max(a,b)} W_ka^T W_kb, written to global
+  // M = -G, both triangles, row-major, one float4 of a row per store
   float* Mg = Mout + ((size_t)u * Fp1 + fi) * dk * dk;
-  {
-    int q = 0;
-    for (int b = 0; b < nb; ++b)
-      for (int a = 0; a <= b; ++a, ++q) {
-        if ((q & 3) != w) continue;
-        f32x16_t acc = zero16();
-        for (int k = b; k < nb; ++k) acc = blk_mm32<true, false>(acc, G(k, a), SG, G(k, b), SG);
-        const int col = lane & 31;
+#pragma unroll 4
+  for (int i = 0; i < 16; ++i) {
+    const int id = t + 256 * i;
+    const int r = id >> 5;
+    const int c = (id & 31) << 2;
+    if (r >= dk || c >= dk) continue;
+    const int bi = r >> 5, bj = c >> 5;
+    f32x4_t v;
+    if (bj <= bi) {
+      const float* src = G(bi, bj) + (r & 31) * SG + (c & 31);
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int gi = 32 * a + acc_row(r, lane), gj = 32 * b + col;
-          if (gi < dk && gj < dk) {
-            Mg[(size_t)gi * dk + gj] = acc[r];
-            if (a != b) Mg[(size_t)gj * dk + gi] = acc[r];
-          }
-        }
-      }
+      for (int e = 0; e < 4; ++e) v[e] = -src[e];
+    } else {
+      const float* src = G(bj, bi) + (c & 31) * SG + (r & 31);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = -src[e * SG];
+    }
+    *reinterpret_cast<f32x4_t*>(Mg + (size_t)r * dk + c) = v;
   }
 }
 
