@@ -40,9 +40,10 @@ __device__ __forceinline__ float readlane_f(float x, int l) {
 // -T^{-1}.  Row k sits in register rk = 4 (k / 8) + k % 4 of the lanes of half
 // hk = (k / 4) % 2, so it feeds both operands of a rank-1 32x32x2 MFMA through
 // the k-slot hk with no data movement: C_mn -= x_m y_n, x = row k (zero at k),
-// y = x / d.  Row and column k are then scaled in place and T_kk set to -1/d
-// (forming them through the rank-1 update would cancel catastrophically for
-// large pivots).  The hardware reciprocal is within 1 ulp.
+// y = x / d.  That update leaves row and column k alone, so they are scaled
+// (and T_kk set to -1/d) before it, branch-free; forming them through the
+// rank-1 update instead would cancel catastrophically for large pivots.  The
+// hardware reciprocal is within 1 ulp.
 __device__ __forceinline__ void sweep_block(f32x16_t& T) {
   const int lane = lane_id();
   const int half = lane >> 5;
@@ -54,12 +55,17 @@ __device__ __forceinline__ void sweep_block(f32x16_t& T) {
     const float d = readlane_f(T[rk], k + 32 * hk);
     const float inv = __builtin_amdgcn_rcpf(d);
     const bool inrow = half == hk;
-    const float x = (inrow && c != k) ? T[rk] : 0.0f;
-    T = mfma_f32(-x, x * inv, T);
-    const float fc = c == k ? inv : 1.0f;  // column k
+    const bool colk = c == k;
+    const float x = (inrow && !colk) ? T[rk] : 0.0f;
+    const float fc = colk ? inv : 1.0f;  // column k
 #pragma unroll
-    for (int r = 0; r < 16; ++r) T[r] *= fc;
-    T[rk] = inrow ? (c == k ? -inv : T[rk] * inv) : T[rk];  // row k, then the pivot
+    for (int r = 0; r < 16; ++r)
+      if (r != rk) T[r] *= fc;
+    // register rk: row k scaled by 1/d off the pivot, the pivot set to -1/d,
+    // column k (other rows) scaled by 1/d
+    const float frk = inrow ? (colk ? 0.0f : inv) : fc;
+    T[rk] = fmaf(T[rk], frk, (inrow && colk) ? -inv : 0.0f);
+    T = mfma_f32(-x, x * inv, T);
   }
 }
 

@@ -20,9 +20,11 @@
 // the two channel-major tiles to LDS with an XOR swizzle that keeps both the
 // 8-byte staging writes and the 16-byte MFMA operand reads free of bank
 // conflicts.  X serves as both MFMA operands of the A block.  The contraction runs on
-// v_mfma_f32_32x32x16_bf16 with fp32 accumulators held for the whole frame;
-// the global loads of the next two tiles are in flight while the current one
-// is multiplied (two register sets, two LDS stages).
+// v_mfma_f32_32x32x16_bf16 with fp32 accumulators held for the whole frame.
+// Per tile there is one barrier: the next tile is staged into the other LDS
+// stage channel by channel between the k-steps of the current tile's
+// products (vector ALU work overlapping the MFMAs), and the global loads of
+// the tile after that are in flight meanwhile (two register sets).
 //
 // fp32 path: the same contraction in fp32 on the vector ALUs (exact fp32
 // products, fp32 accumulation) for fp32 features.
@@ -100,28 +102,50 @@ __global__ __launch_bounds__(512, 1) void stats_bf16_kernel(
   const bool vact = cg * 8 < dv;
 
   // one tile's worth of this thread's raw inputs (16-byte bf16 vectors).  The
-  // loads are unconditional from clamped, always valid addresses and nothing
-  // uses their values until write(): vmcnt retires in issue order, so a tile's
+  // loads are unconditional from always valid addresses and nothing uses their
+  // values until the tile is staged: vmcnt retires in issue order, so a tile's
   // loads stay in flight behind later work.  Tokens past the frame's end get
-  // write strength 0 in write().
+  // write strength 0 when staged.
   struct TileRegs {
     u32x4_t k[4], v[4];
     float b[4];  // beta of the 4 tokens
-    int tok0;    // first token of the thread's group
   };
   const int kcg = kact ? cg : 0;
   const int vcg = vact ? cg : 0;
   const int last_tok = ntok > 0 ? ntok - 1 : 0;
+  // element offsets of the thread's 4 tokens within a tile (full tiles)
+  const uint32_t koff = (uint32_t)(4 * tg) * dk + 8 * kcg;
+  const uint32_t voff = (uint32_t)(4 * tg) * dv + 8 * vcg;
 
-  auto load = [&](TileRegs& r, int tile) {
-    r.tok0 = tile * kTok + 4 * tg;
+  // a tile that lies wholly inside the frame: uniform base, per-thread offsets
+  auto load_full = [&](TileRegs& r, int tile) {
+    const int tok0 = tile * kTok;
+    const uint16_t* bk = sk + (size_t)tok0 * dk + koff;
+    const uint16_t* bv = sv + (size_t)tok0 * dv + voff;
+    const float* bb = sb + tok0 + 4 * tg;
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      const int tok = min(r.tok0 + s, last_tok);
+      r.k[s] = ld_stream(bk + s * dk);
+      r.v[s] = ld_stream(bv + s * dv);
+      r.b[s] = bb[s];
+    }
+  };
+  // any tile: token indices clamped to the frame's last token
+  auto load = [&](TileRegs& r, int tile) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const int tok = min(tile * kTok + 4 * tg + s, last_tok);
       r.k[s] = ld_stream(sk + (size_t)tok * dk + 8 * kcg);
       r.v[s] = ld_stream(sv + (size_t)tok * dv + 8 * vcg);
       r.b[s] = sb[tok];
     }
+  };
+
+  // sqrt(beta) of the thread's 4 tokens of tile `tile` (0 past the end)
+  auto sqrt_beta = [&](const TileRegs& r, int tile, float (&sb4)[4]) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+      sb4[s] = tile * kTok + 4 * tg + s < ntok ? __builtin_amdgcn_sqrtf(r.b[s] * bscale) : 0.0f;
   };
 
   // channel c of the thread's 8-channel group, tokens 0..3: scale, round, pack
@@ -140,16 +164,22 @@ __global__ __launch_bounds__(512, 1) void stats_bf16_kernel(
     return e;
   };
 
-  auto write = [&](const TileRegs& r, int stage) {
-    unsigned char* X = smem + stage * kStageBytes;
+  // staging write offsets: channel row 8 cg + c, slot tg.  With
+  // Q = swz(8 cg + c) ^ c = (8 (cg & 1)) ^ cg (independent of c),
+  // off8(8 cg + c, tg) = ((2048 cg) | (8 tg ^ 16 Q)) ^ (16 c) + 256 c; V rows
+  // 128 + 8 cg + c have the same swizzle, 32 KiB further.
+  const uint32_t wbase = (uint32_t)(2048 * cg) | ((8u * tg) ^ (16u * ((8u * (cg & 1)) ^ cg)));
+  auto write_channel = [&](const TileRegs& r, const float (&sb4)[4], int stage, int c) {
+    unsigned char* X = smem + stage * kStageBytes + 256 * c;
+    const uint32_t o = wbase ^ (16u * c);
+    if (kact) *reinterpret_cast<u32x2_t*>(X + o) = scaled_pair(r.k, sb4, c);
+    if (vact) *reinterpret_cast<u32x2_t*>(X + o + 128 * kRowBytes) = scaled_pair(r.v, sb4, c);
+  };
+  auto write_all = [&](const TileRegs& r, int tile, int stage) {
     float sb4[4];
+    sqrt_beta(r, tile, sb4);
 #pragma unroll
-    for (int s = 0; s < 4; ++s) sb4[s] = r.tok0 + s < ntok ? sqrtf(r.b[s] * bscale) : 0.0f;
-#pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      if (kact) *reinterpret_cast<u32x2_t*>(X + off8(8 * cg + c, tg)) = scaled_pair(r.k, sb4, c);
-      if (vact) *reinterpret_cast<u32x2_t*>(X + off8(128 + 8 * cg + c, tg)) = scaled_pair(r.v, sb4, c);
-    }
+    for (int c = 0; c < 8; ++c) write_channel(r, sb4, stage, c);
   };
 
   // contraction role: wave w owns output row tile w of [A; B]
@@ -162,43 +192,78 @@ __global__ __launch_bounds__(512, 1) void stats_bf16_kernel(
 #pragma unroll
   for (int ct = 0; ct < 4; ++ct) acc[ct] = zero16();
 
-  auto compute = [&](int stage) {
-    if (!ract) return;
-    const unsigned char* X = smem + stage * kStageBytes;
-    const int il = lane & 31;
-    const int kh = lane >> 5;
-#pragma unroll 2
-    for (int kk = 0; kk < kTok / 16; ++kk) {
-      const int j = 2 * kk + kh;  // tokens 16 kk + 8 kh .. + 7
-      const u32x4_t a = *reinterpret_cast<const u32x4_t*>(X + off16(rbase + il, j));
+  // operand offsets: off16(row, j) with j = 2 kk + kh equals
+  // (row * 256 + ((16 kh) ^ (swz(row) << 4))) ^ (32 kk)
+  const int il = lane & 31;
+  const int kh = lane >> 5;
+  auto opbase = [&](int row) {
+    return (uint32_t)row * kRowBytes + ((16u * kh) ^ (swz(row) << 4));
+  };
+  const uint32_t abase = opbase(rbase + il);
+  uint32_t bbase[4];
 #pragma unroll
-      for (int ct = 0; ct < 4; ++ct) {
-        if (ct < nK) {
-          const u32x4_t b = *reinterpret_cast<const u32x4_t*>(X + off16(32 * ct + il, j));
-          acc[ct] = mfma_bf16(a, b, acc[ct]);
-        }
+  for (int ct = 0; ct < 4; ++ct) bbase[ct] = opbase(32 * ct + il);
+
+  // Multiply the tile in `cstage` (8 k-steps of 16 tokens, operands fetched
+  // one k-step ahead) and, interleaved with it, stage channel c = kk of the
+  // register set `r` (tile `wtile`) into `wstage`.
+  auto compute_write = [&](int cstage, bool do_write, const TileRegs& r, int wtile, int wstage) {
+    const unsigned char* X = smem + cstage * kStageBytes;
+    float sb4[4];
+    if (do_write) sqrt_beta(r, wtile, sb4);
+    u32x4_t a0, b0[4];
+    auto fetch = [&](int kk, u32x4_t& a, u32x4_t (&b)[4]) {
+      a = *reinterpret_cast<const u32x4_t*>(X + (abase ^ (32u * kk)));
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct)
+        if (ct < nK) b[ct] = *reinterpret_cast<const u32x4_t*>(X + (bbase[ct] ^ (32u * kk)));
+    };
+    if (ract) fetch(0, a0, b0);
+#pragma unroll
+    for (int kk = 0; kk < kTok / 16; ++kk) {
+      u32x4_t a1, b1[4];
+      if (ract && kk + 1 < kTok / 16) fetch(kk + 1, a1, b1);
+      if (ract) {
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct)
+          if (ct < nK) acc[ct] = mfma_bf16(a0, b0[ct], acc[ct]);
       }
+      if (do_write) write_channel(r, sb4, wstage, kk);
+      a0 = a1;
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct) b0[ct] = b1[ct];
     }
   };
 
-  // Two register sets in flight: a tile's loads are issued two multiply phases
-  // before its registers are written to LDS.
+  // Stage (it & 1) holds tile it.  Each tile: one barrier, then tile it + 2's
+  // loads are issued into the register set tile it came from, and tile it is
+  // multiplied while tile it + 1 (loaded one tile earlier) is staged into the
+  // other stage.  The steady-state loop only meets full tiles and always
+  // stages, so every register set's loads are consumed on every path (no
+  // conservative waits before reloading a set); the generic loop finishes the
+  // frame.
   const int ntiles = (ntok + kTok - 1) / kTok;
   TileRegs ra, rb;
   if (ntiles > 0) load(ra, 0);
   if (ntiles > 1) load(rb, 1);
-  if (ntiles > 0) write(ra, 0);
-  for (int it = 0; it < ntiles; it += 2) {
-    // LDS stage 0 holds tile it; rb holds tile it + 1
+  if (ntiles > 0) write_all(ra, 0, 0);
+  int it = 0;
+  for (; (it + 4) * kTok <= ntok; it += 2) {  // tiles it + 2, it + 3 are full
+    __syncthreads();
+    load_full(ra, it + 2);
+    compute_write(0, true, rb, it + 1, 1);
+    __syncthreads();
+    load_full(rb, it + 3);
+    compute_write(1, true, ra, it + 2, 0);
+  }
+  for (; it < ntiles; it += 2) {
+    __syncthreads();
     if (it + 2 < ntiles) load(ra, it + 2);
-    __syncthreads();
-    compute(0);
+    compute_write(0, it + 1 < ntiles, rb, it + 1, 1);
     if (it + 1 >= ntiles) break;
-    write(rb, 1);
-    if (it + 3 < ntiles) load(rb, it + 3);
     __syncthreads();
-    compute(1);
-    if (it + 2 < ntiles) write(ra, 0);
+    if (it + 3 < ntiles) load(rb, it + 3);
+    compute_write(1, it + 2 < ntiles, ra, it + 2, 0);
   }
 
   // results: rows of A (K tiles) or B (V tiles), columns are key channels
