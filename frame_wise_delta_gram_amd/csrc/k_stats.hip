@@ -31,6 +31,8 @@
 #include "vda_device.h"
 #include "vda_internal.h"
 
+#include <algorithm>
+
 namespace vda {
 namespace {
 
@@ -58,42 +60,69 @@ __device__ __forceinline__ uint32_t off16(uint32_t row, uint32_t j) {
   return row * kRowBytes + ((j ^ swz(row)) << 4);
 }
 
+// Persistent: one workgroup per CU (the 128 KiB of LDS allow no more) walks
+// the frames b, b + P, b + 2P, ... of the flattened (unit, frame) list, frame
+// g = u (F + 1) + fi with fi = 0 the text frame, as ONE continuous tile
+// stream: the first tiles of the next frame are in flight while the last tile
+// of the current one is multiplied and its results are stored.
+// Raw buffer access (gfx9 descriptor: stride 0, range in bytes, dword 3 =
+// 0x00020000): loads at or past `bytes` return 0 without a memory access.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
+}
+// 16 bytes, non-temporal (cache policy bit 1)
+__device__ __forceinline__ u32x4_t buf_load16_nt(__amdgpu_buffer_rsrc_t r, int off) {
+  return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 2));
+}
+__device__ __forceinline__ float buf_load4(__amdgpu_buffer_rsrc_t r, int off) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+}
+
 // DK, DV > 0: compile-time d_k and d_v (the common 128 case); 0: runtime.
 template <int DK, int DV>
 __global__ __launch_bounds__(512, 1) void stats_bf16_kernel(
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, const float* __restrict__ beta,
     const uint16_t* __restrict__ tk, const uint16_t* __restrict__ tv,
     const float* __restrict__ tb, float* __restrict__ Aout, float* __restrict__ Bout, int F, int U,
-    int T, int dk_rt, int dv_rt, float text_scale) {
+    int T, int dk_rt, int dv_rt, float text_scale, int nframes) {
   const int dk = DK > 0 ? DK : dk_rt;
   const int dv = DV > 0 ? DV : dv_rt;
   __shared__ __align__(16) unsigned char smem[2 * kStageBytes];
 
-  const int fi = blockIdx.x;  // 0 = text frame, f + 1 = latent frame f
-  const int u = blockIdx.y;
   const int t = threadIdx.x;
   const int lane = t & 63;
   const int w = t >> 6;
+  const int P = gridDim.x;
+  const int b0 = blockIdx.x;
 
-  const uint16_t* sk;
-  const uint16_t* sv;
-  const float* sb;
-  int ntok;
-  float bscale;
-  if (fi == 0) {
-    sk = tk + (size_t)u * T * dk;
-    sv = tv + (size_t)u * T * dv;
-    sb = tb + (size_t)u * T;
-    ntok = T;
-    bscale = text_scale;
-  } else {
-    const size_t fr = (size_t)u * F + (fi - 1);
-    sk = k + fr * U * dk;
-    sv = v + fr * U * dv;
-    sb = beta + fr * U;
-    ntok = U;
-    bscale = 1.0f;
-  }
+  struct FrameSrc {
+    const uint16_t* k;
+    const uint16_t* v;
+    const float* b;
+    int ntok;
+    float bscale;
+  };
+  auto frame_src = [&](int g) {
+    FrameSrc f;
+    const int u = g / (F + 1);
+    const int fi = g - u * (F + 1);
+    if (fi == 0) {
+      f = {tk + (size_t)u * T * dk, tv + (size_t)u * T * dv, tb + (size_t)u * T, T, text_scale};
+    } else {
+      const size_t fr = (size_t)u * F + (fi - 1);
+      f = {k + fr * U * dk, v + fr * U * dv, beta + fr * U, U, 1.0f};
+    }
+    return f;
+  };
+  auto ntiles_of = [&](int ntok) { return ntok > 0 ? (ntok + kTok - 1) / kTok : 1; };
+  // tile cursor: frame g (>= nframes past this workgroup's last frame), tile i
+  struct Cur {
+    int g, i;
+  };
+  auto next = [&](Cur c) {
+    if (c.g < nframes && c.i + 1 < ntiles_of(frame_src(c.g).ntok)) return Cur{c.g, c.i + 1};
+    return Cur{c.g + P, 0};
+  };
 
   // staging role: token group tg (4 tokens) x channel group cg (8 channels)
   const int tg = (t & 1) | ((t >> 5) << 1);
@@ -101,63 +130,55 @@ __global__ __launch_bounds__(512, 1) void stats_bf16_kernel(
   const bool kact = cg * 8 < dk;
   const bool vact = cg * 8 < dv;
 
-  // one tile's worth of this thread's raw inputs (16-byte bf16 vectors).  The
-  // loads are unconditional from always valid addresses and nothing uses their
-  // values until the tile is staged: vmcnt retires in issue order, so a tile's
-  // loads stay in flight behind later work.  Tokens past the frame's end get
-  // write strength 0 when staged.
+  // one tile's worth of this thread's raw inputs (16-byte bf16 vectors).
+  // Buffer loads through a per-tile descriptor whose range ends at the frame's
+  // last token: tokens past the end (and every token of an empty frame) read
+  // as exact zeros without touching memory, and the addresses are per-thread
+  // constants (no address arithmetic per load).  Nothing uses the values until
+  // the tile is staged: vmcnt retires in issue order, so a tile's loads stay
+  // in flight behind later work.
   struct TileRegs {
     u32x4_t k[4], v[4];
     float b[4];  // beta of the 4 tokens
   };
   const int kcg = kact ? cg : 0;
   const int vcg = vact ? cg : 0;
-  const int last_tok = ntok > 0 ? ntok - 1 : 0;
-  // element offsets of the thread's 4 tokens within a tile (full tiles)
-  const uint32_t koff = (uint32_t)(4 * tg) * dk + 8 * kcg;
-  const uint32_t voff = (uint32_t)(4 * tg) * dv + 8 * vcg;
+  // byte offsets of the thread's 4 tokens within a tile
+  const int koff = ((4 * tg) * dk + 8 * kcg) * 2;
+  const int voff = ((4 * tg) * dv + 8 * vcg) * 2;
+  const int boff = 16 * tg;
 
-  // a tile that lies wholly inside the frame: uniform base, per-thread offsets
-  auto load_full = [&](TileRegs& r, int tile) {
-    const int tok0 = tile * kTok;
-    const uint16_t* bk = sk + (size_t)tok0 * dk + koff;
-    const uint16_t* bv = sv + (size_t)tok0 * dv + voff;
-    const float* bb = sb + tok0 + 4 * tg;
+  auto load = [&](TileRegs& r, Cur c) {
+    const bool past = c.g >= nframes;  // past this workgroup's last frame: zeros, never used
+    const FrameSrc f = frame_src(past ? b0 : c.g);
+    const int tok0 = c.i * kTok;
+    const int rem = past ? 0 : max(f.ntok - tok0, 0);
+    const size_t t0 = past ? 0 : (size_t)tok0;
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(f.k + t0 * dk, rem * dk * 2);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(f.v + t0 * dv, rem * dv * 2);
+    const __amdgpu_buffer_rsrc_t rbb = make_rsrc(f.b + t0, rem * 4);
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      r.k[s] = ld_stream(bk + s * dk);
-      r.v[s] = ld_stream(bv + s * dv);
-      r.b[s] = bb[s];
-    }
-  };
-  // any tile: token indices clamped to the frame's last token
-  auto load = [&](TileRegs& r, int tile) {
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const int tok = min(tile * kTok + 4 * tg + s, last_tok);
-      r.k[s] = ld_stream(sk + (size_t)tok * dk + 8 * kcg);
-      r.v[s] = ld_stream(sv + (size_t)tok * dv + 8 * vcg);
-      r.b[s] = sb[tok];
+      r.k[s] = buf_load16_nt(rk, koff + s * dk * 2);
+      r.v[s] = buf_load16_nt(rv, voff + s * dv * 2);
+      r.b[s] = buf_load4(rbb, boff + 4 * s);
     }
   };
 
-  // sqrt(beta) of the thread's 4 tokens of tile `tile` (0 past the end)
-  auto sqrt_beta = [&](const TileRegs& r, int tile, float (&sb4)[4]) {
+  // sqrt(beta) of the thread's 4 tokens of tile c (beta reads 0 past the end)
+  auto sqrt_beta = [&](const TileRegs& r, Cur c, float (&sb4)[4]) {
+    const float bscale = frame_src(c.g < nframes ? c.g : b0).bscale;
 #pragma unroll
-    for (int s = 0; s < 4; ++s)
-      sb4[s] = tile * kTok + 4 * tg + s < ntok ? __builtin_amdgcn_sqrtf(r.b[s] * bscale) : 0.0f;
+    for (int s = 0; s < 4; ++s) sb4[s] = __builtin_amdgcn_sqrtf(r.b[s] * bscale);
   };
 
   // channel c of the thread's 8-channel group, tokens 0..3: scale, round, pack
-  auto scaled_pair = [&](const u32x4_t* x4, const float* b, int c) {
+  auto scaled_pair = [&](const u32x4_t* x4, const float* bq, int c) {
     const int p = c >> 1;
     const bool hi = (c & 1) != 0;
     float x[4];
 #pragma unroll
-    for (int s = 0; s < 4; ++s) x[s] = (hi ? bf16_hi(x4[s][p]) : bf16_lo(x4[s][p])) * b[s];
-    // b[s] is 0 for tokens past the end; their registers hold a copy of the
-    // frame's last token, so the product is exactly 0 (a non-finite input there
-    // would already make the frame's statistics non-finite)
+    for (int s = 0; s < 4; ++s) x[s] = (hi ? bf16_hi(x4[s][p]) : bf16_lo(x4[s][p])) * bq[s];
     u32x2_t e;
     e[0] = pack_bf16(x[0], x[1]);
     e[1] = pack_bf16(x[2], x[3]);
@@ -175,13 +196,6 @@ __global__ __launch_bounds__(512, 1) void stats_bf16_kernel(
     if (kact) *reinterpret_cast<u32x2_t*>(X + o) = scaled_pair(r.k, sb4, c);
     if (vact) *reinterpret_cast<u32x2_t*>(X + o + 128 * kRowBytes) = scaled_pair(r.v, sb4, c);
   };
-  auto write_all = [&](const TileRegs& r, int tile, int stage) {
-    float sb4[4];
-    sqrt_beta(r, tile, sb4);
-#pragma unroll
-    for (int c = 0; c < 8; ++c) write_channel(r, sb4, stage, c);
-  };
-
   // contraction role: wave w owns output row tile w of [A; B]
   const int nK = pad32(dk) >> 5;
   const int nV = pad32(dv) >> 5;
@@ -204,86 +218,88 @@ __global__ __launch_bounds__(512, 1) void stats_bf16_kernel(
 #pragma unroll
   for (int ct = 0; ct < 4; ++ct) bbase[ct] = opbase(32 * ct + il);
 
-  // Multiply the tile in `cstage` (8 k-steps of 16 tokens, operands fetched
-  // one k-step ahead) and, interleaved with it, stage channel c = kk of the
-  // register set `r` (tile `wtile`) into `wstage`.
-  auto compute_write = [&](int cstage, bool do_write, const TileRegs& r, int wtile, int wstage) {
+  // Multiply the tile in `cstage` (8 k-steps of 16 tokens) and, interleaved
+  // with it, stage channel c = kk of the
+  // register set `r` (tile cw) into `wstage`.
+  auto compute_write = [&](int cstage, const TileRegs& r, Cur cw, int wstage) {
     const unsigned char* X = smem + cstage * kStageBytes;
     float sb4[4];
-    if (do_write) sqrt_beta(r, wtile, sb4);
-    u32x4_t a0, b0[4];
-    auto fetch = [&](int kk, u32x4_t& a, u32x4_t (&b)[4]) {
-      a = *reinterpret_cast<const u32x4_t*>(X + (abase ^ (32u * kk)));
-#pragma unroll
-      for (int ct = 0; ct < 4; ++ct)
-        if (ct < nK) b[ct] = *reinterpret_cast<const u32x4_t*>(X + (bbase[ct] ^ (32u * kk)));
-    };
-    if (ract) fetch(0, a0, b0);
+    sqrt_beta(r, cw, sb4);
 #pragma unroll
     for (int kk = 0; kk < kTok / 16; ++kk) {
-      u32x4_t a1, b1[4];
-      if (ract && kk + 1 < kTok / 16) fetch(kk + 1, a1, b1);
       if (ract) {
+        const u32x4_t a = *reinterpret_cast<const u32x4_t*>(X + (abase ^ (32u * kk)));
 #pragma unroll
-        for (int ct = 0; ct < 4; ++ct)
-          if (ct < nK) acc[ct] = mfma_bf16(a0, b0[ct], acc[ct]);
+        for (int ct = 0; ct < 4; ++ct) {
+          if (ct < nK) {
+            const u32x4_t bq = *reinterpret_cast<const u32x4_t*>(X + (bbase[ct] ^ (32u * kk)));
+            acc[ct] = mfma_bf16(a, bq, acc[ct]);
+          }
+        }
       }
-      if (do_write) write_channel(r, sb4, wstage, kk);
-      a0 = a1;
-#pragma unroll
-      for (int ct = 0; ct < 4; ++ct) b0[ct] = b1[ct];
+      write_channel(r, sb4, wstage, kk);
     }
   };
 
-  // Stage (it & 1) holds tile it.  Each tile: one barrier, then tile it + 2's
-  // loads are issued into the register set tile it came from, and tile it is
-  // multiplied while tile it + 1 (loaded one tile earlier) is staged into the
-  // other stage.  The steady-state loop only meets full tiles and always
-  // stages, so every register set's loads are consumed on every path (no
-  // conservative waits before reloading a set); the generic loop finishes the
-  // frame.
-  const int ntiles = (ntok + kTok - 1) / kTok;
-  TileRegs ra, rb;
-  if (ntiles > 0) load(ra, 0);
-  if (ntiles > 1) load(rb, 1);
-  if (ntiles > 0) write_all(ra, 0, 0);
-  int it = 0;
-  for (; (it + 4) * kTok <= ntok; it += 2) {  // tiles it + 2, it + 3 are full
-    __syncthreads();
-    load_full(ra, it + 2);
-    compute_write(0, true, rb, it + 1, 1);
-    __syncthreads();
-    load_full(rb, it + 3);
-    compute_write(1, true, ra, it + 2, 0);
-  }
-  for (; it < ntiles; it += 2) {
-    __syncthreads();
-    if (it + 2 < ntiles) load(ra, it + 2);
-    compute_write(0, it + 1 < ntiles, rb, it + 1, 1);
-    if (it + 1 >= ntiles) break;
-    __syncthreads();
-    if (it + 3 < ntiles) load(rb, it + 3);
-    compute_write(1, it + 2 < ntiles, ra, it + 2, 0);
-  }
-
-  // results: rows of A (K tiles) or B (V tiles), columns are key channels
-  if (ract) {
-    const size_t fr = (size_t)u * (F + 1) + fi;
-    const bool isA = w < nK;
-    const int ch0 = isA ? 32 * w : 32 * (w - nK);
-    const int nrows = isA ? dk : dv;
-    float* dst = isA ? Aout + fr * dk * dk : Bout + fr * dv * dk;
+  // results of frame g: rows of A (K tiles) or B (V tiles), columns are key
+  // channels; the accumulators restart at zero
+  auto store_frame = [&](int g) {
+    if (ract) {
+      const bool isA = w < nK;
+      const int ch0 = isA ? 32 * w : 32 * (w - nK);
+      const int nrows = isA ? dk : dv;
+      float* dst = isA ? Aout + (size_t)g * dk * dk : Bout + (size_t)g * dv * dk;
 #pragma unroll
-    for (int ct = 0; ct < 4; ++ct) {
-      if (ct >= nK) continue;
-      const int col = 32 * ct + (lane & 31);
-      if (col >= dk) continue;
+      for (int ct = 0; ct < 4; ++ct) {
+        if (ct >= nK) continue;
+        const int col = 32 * ct + (lane & 31);
+        if (col >= dk) continue;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = ch0 + acc_row(r, lane);
-        if (row < nrows) dst[(size_t)row * dk + col] = acc[ct][r];
+        for (int r = 0; r < 16; ++r) {
+          const int row = ch0 + acc_row(r, lane);
+          if (row < nrows) dst[(size_t)row * dk + col] = acc[ct][r];
+        }
       }
     }
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) acc[ct] = zero16();
+  };
+  auto last_tile = [&](Cur c) { return c.i + 1 == ntiles_of(frame_src(c.g).ntok); };
+
+  // Stage 0 / 1 alternate.  Each tile: one barrier, then the loads of the
+  // tile two ahead go into the register set the current tile came from, and
+  // the current tile is multiplied while the next one (loaded one tile
+  // earlier) is staged into the other stage.  Every register set is staged on
+  // every path, so no wait before reloading a set is needed.
+  Cur c0{b0, 0};
+  Cur c1 = next(c0);
+  Cur c2 = next(c1);
+  TileRegs ra, rb;
+  load(ra, c0);
+  load(rb, c1);
+  {
+    float sb4[4];
+    sqrt_beta(ra, c0, sb4);
+#pragma unroll
+    for (int c = 0; c < 8; ++c) write_channel(ra, sb4, 0, c);
+  }
+  while (true) {
+    __syncthreads();
+    load(ra, c2);
+    compute_write(0, rb, c1, 1);
+    if (last_tile(c0)) store_frame(c0.g);
+    c0 = c1;
+    c1 = c2;
+    c2 = next(c2);
+    if (c0.g >= nframes) break;
+    __syncthreads();
+    load(rb, c2);
+    compute_write(1, ra, c1, 0);
+    if (last_tile(c0)) store_frame(c0.g);
+    c0 = c1;
+    c1 = c2;
+    c2 = next(c2);
+    if (c0.g >= nframes) break;
   }
 }
 
@@ -376,6 +392,20 @@ __global__ __launch_bounds__(256) void stats_f32_kernel(
   }
 }
 
+// compute units of the current device (cached per device)
+int compute_units() {
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cache[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cache[dev] = n;
+  }
+  return cache[dev];
+}
+
 }  // namespace
 
 hipError_t launch_stats(const Plan& p, const void* k, const void* v, const float* beta,
@@ -384,11 +414,13 @@ hipError_t launch_stats(const Plan& p, const void* k, const void* v, const float
   const dim3 grid(p.F + 1, p.units);
   const float ts = p.seed_mode == 1 ? 0.5f : 1.0f;
   if (p.dtype == VDA_DTYPE_BF16) {
+    const int nframes = p.units * (p.F + 1);
+    const int P = std::min(nframes, compute_units());
     auto kern = (p.dk == 128 && p.dv == 128) ? stats_bf16_kernel<128, 128> : stats_bf16_kernel<0, 0>;
-    hipLaunchKernelGGL(kern, grid, dim3(kStatsThreads), 0, s,
+    hipLaunchKernelGGL(kern, dim3(P), dim3(kStatsThreads), 0, s,
                        static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), beta,
                        static_cast<const uint16_t*>(text_k), static_cast<const uint16_t*>(text_v),
-                       text_beta, w.A, w.B, p.F, p.U, p.T, p.dk, p.dv, ts);
+                       text_beta, w.A, w.B, p.F, p.U, p.T, p.dk, p.dv, ts, nframes);
   } else {
     hipLaunchKernelGGL(stats_f32_kernel, grid, dim3(kThreads), 0, s,
                        static_cast<const float*>(k), static_cast<const float*>(v), beta,

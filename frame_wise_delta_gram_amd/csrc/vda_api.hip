@@ -40,6 +40,11 @@ int make_plan(const vda_desc_t* d, Plan* p) {
   if (!mul_ok(rows, 128, &elems)) return VDA_ERR_INVALID_ARG;
   if (!mul_ok((int64_t)d->chunk, d->tokens, &x)) return VDA_ERR_INVALID_ARG;
   if (!mul_ok(d->units, d->text_tokens, &x) || !mul_ok(x, 128, &x)) return VDA_ERR_INVALID_ARG;
+  // one frame's tokens are addressed with 32-bit byte offsets; the frame list
+  // (units x (frames + 1)) is indexed with int
+  if ((int64_t)d->tokens * 512 > INT32_MAX || (int64_t)d->text_tokens * 512 > INT32_MAX)
+    return VDA_ERR_INVALID_ARG;
+  if ((int64_t)d->units * ((int64_t)d->frames + 1) > (INT64_C(1) << 30)) return VDA_ERR_INVALID_ARG;
   // 1-D grids of the readout (units x chunks x 1024-row blocks) and composition must fit
   const int64_t rows_per_chunk = (int64_t)d->chunk * d->tokens;
   if (!mul_ok((int64_t)d->units * n, (rows_per_chunk + 1023) / 1024 + 3, &x) || x > (INT64_C(1) << 30))

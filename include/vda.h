@@ -82,10 +82,10 @@ typedef enum vda_dtype {
 } vda_dtype_t;
 
 typedef struct vda_desc {
-  int32_t units;       /* batch x heads, >= 0 */
-  int32_t frames;      /* latent frames F, >= 0 */
-  int32_t tokens;      /* tokens per frame U, >= 0 */
-  int32_t text_tokens; /* text tokens T, >= 0 (0: zero seed) */
+  int32_t units;       /* batch x heads, 0..65535 */
+  int32_t frames;      /* latent frames F, >= 0; units x (F + 1) <= 2^30 */
+  int32_t tokens;      /* tokens per frame U, 0..4194303 */
+  int32_t text_tokens; /* text tokens T, 0..4194303 (0: zero seed) */
   int32_t d_k;         /* key channels, multiple of 16, 16..128 */
   int32_t d_v;         /* value channels, multiple of 16, 16..128 */
   int32_t chunk;       /* frames per chunk C, >= 1 ([VDN] uses 5) */

@@ -76,6 +76,10 @@ def test_workspace_formula(lib):
     (dict(rms_eps=float("inf")), vda.VDA_ERR_INVALID_ARG),
     (dict(seed_mode=2), vda.VDA_ERR_INVALID_ARG),
     (dict(units=70000), vda.VDA_ERR_INVALID_ARG),
+    (dict(tokens=4194304), vda.VDA_ERR_INVALID_ARG),
+    (dict(text_tokens=4194304), vda.VDA_ERR_INVALID_ARG),
+    (dict(tokens=4194303, units=1, frames=1), vda.VDA_OK),
+    (dict(units=65535, frames=20000), vda.VDA_ERR_INVALID_ARG),
     (dict(dtype=7), vda.VDA_ERR_BAD_DTYPE),
     (dict(units=0, frames=0, tokens=0), vda.VDA_OK),
     (dict(d_k=16, d_v=128), vda.VDA_OK),
