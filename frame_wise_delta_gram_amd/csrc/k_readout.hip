@@ -34,12 +34,13 @@
 namespace vda {
 namespace {
 
-constexpr int kIters = 8;                 // 32-row blocks per wave
-constexpr int kRows = 4 * 32 * kIters;    // token rows per workgroup
+constexpr int kThreadsR = 512;            // 8 waves; two workgroups per CU
+constexpr int kGroups = 8;                // 16-row groups per wave
+constexpr int kRows = 8 * 16 * kGroups;   // token rows per workgroup
 
 // DK, DV > 0: compile-time d_k and d_v (the common 128 case); 0: runtime.
 template <int DK, int DV>
-__global__ __launch_bounds__(256, 2) void readout_bf16_kernel(
+__global__ __launch_bounds__(512, 4) void readout_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ gate,
     const float* __restrict__ wrms, uint16_t* __restrict__ out, const float* __restrict__ ST,
     int dk_rt, int dv_rt, int F, int U, int C, int radius, int n, float eps, int units, int nblk,
@@ -72,7 +73,7 @@ __global__ __launch_bounds__(256, 2) void readout_bf16_kernel(
   const int NKS = Dkp >> 5;    // k-steps of 32 channels
   const int SROW = 136;        // LDS row stride (bf16 elements): 17 x 16 bytes
 
-  for (int i = t; i < 128; i += 256) Ws[i] = i < dv ? wrms[i] : 0.0f;
+  if (t < 128) Ws[t] = t < dv ? wrms[t] : 0.0f;
   // gather S~ and split it into bf16 hi + lo, rows permuted (see header);
   // padding rows and columns are zero
   {
@@ -82,46 +83,49 @@ __global__ __launch_bounds__(256, 2) void readout_bf16_kernel(
     const float* P = ST + ((size_t)(u * 2 + 0) * (n + 1) + pi) * SS;
     const float* R = ST + ((size_t)(u * 2 + 1) * (n + 1) + ri) * SS;
     const int k8n = Dkp >> 3;
-    const int items = Dvp * k8n;  // <= 2048 = 8 per thread
-    f32x4_t pv[8][2], rv[8][2];
+    const int items = Dvp * k8n;  // <= 2048 = 4 per thread, in two rounds of 2
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {  // issue every load first
-      const int it = t + 256 * i;
-      const int ch = it / k8n;
-      const int k8 = it - ch * k8n;
-      const f32x4_t z = {0.0f, 0.0f, 0.0f, 0.0f};
-      const bool ok = it < items && ch < dv && 8 * k8 < dk;
-      const f32x4_t* pp = reinterpret_cast<const f32x4_t*>(P + (size_t)(ok ? ch : 0) * dk + (ok ? 8 * k8 : 0));
-      const f32x4_t* rp = reinterpret_cast<const f32x4_t*>(R + (size_t)(ok ? ch : 0) * dk + (ok ? 8 * k8 : 0));
-      pv[i][0] = ok ? pp[0] : z;
-      pv[i][1] = ok ? pp[1] : z;
-      rv[i][0] = ok ? rp[0] : z;
-      rv[i][1] = ok ? rp[1] : z;
-    }
+    for (int half = 0; half < 2; ++half) {
+      f32x4_t pv[2][2], rv[2][2];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int it = t + 256 * i;
-      if (it >= items) continue;
-      const int ch = it / k8n;
-      const int k8 = it - ch * k8n;
-      // channel ch = 32 m + 8 h + 4 (T % 2) + r  ->  LDS row 16 T + 4 h + r
-      const int T = 2 * (ch >> 5) + ((ch >> 2) & 1);
-      const int lrow = 16 * T + 4 * ((ch >> 3) & 3) + (ch & 3);
-      float x[8];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        x[e] = pv[i][0][e] + rv[i][0][e];
-        x[4 + e] = pv[i][1][e] + rv[i][1][e];
+      for (int i = 0; i < 2; ++i) {  // issue the round's loads first
+        const int it = t + kThreadsR * (2 * half + i);
+        const int ch = it / k8n;
+        const int k8 = it - ch * k8n;
+        const f32x4_t z = {0.0f, 0.0f, 0.0f, 0.0f};
+        const bool ok = it < items && ch < dv && 8 * k8 < dk;
+        const f32x4_t* pp = reinterpret_cast<const f32x4_t*>(P + (size_t)(ok ? ch : 0) * dk + (ok ? 8 * k8 : 0));
+        const f32x4_t* rp = reinterpret_cast<const f32x4_t*>(R + (size_t)(ok ? ch : 0) * dk + (ok ? 8 * k8 : 0));
+        pv[i][0] = ok ? pp[0] : z;
+        pv[i][1] = ok ? pp[1] : z;
+        rv[i][0] = ok ? rp[0] : z;
+        rv[i][1] = ok ? rp[1] : z;
       }
-      u32x4_t hi, lo;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const uint32_t hp = pack_bf16(x[2 * e], x[2 * e + 1]);
-        hi[e] = hp;
-        lo[e] = pack_bf16(x[2 * e] - bf16_lo(hp), x[2 * e + 1] - bf16_hi(hp));
+      for (int i = 0; i < 2; ++i) {
+        const int it = t + kThreadsR * (2 * half + i);
+        if (it >= items) continue;
+        const int ch = it / k8n;
+        const int k8 = it - ch * k8n;
+        // channel ch = 32 m + 8 h + 4 (T % 2) + r  ->  LDS row 16 T + 4 h + r
+        const int T = 2 * (ch >> 5) + ((ch >> 2) & 1);
+        const int lrow = 16 * T + 4 * ((ch >> 3) & 3) + (ch & 3);
+        float x[8];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          x[e] = pv[i][0][e] + rv[i][0][e];
+          x[4 + e] = pv[i][1][e] + rv[i][1][e];
+        }
+        u32x4_t hi, lo;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t hp = pack_bf16(x[2 * e], x[2 * e + 1]);
+          hi[e] = hp;
+          lo[e] = pack_bf16(x[2 * e] - bf16_lo(hp), x[2 * e + 1] - bf16_hi(hp));
+        }
+        *reinterpret_cast<u32x4_t*>(Shi + lrow * SROW + 8 * k8) = hi;
+        *reinterpret_cast<u32x4_t*>(Slo + lrow * SROW + 8 * k8) = lo;
       }
-      *reinterpret_cast<u32x4_t*>(Shi + lrow * SROW + 8 * k8) = hi;
-      *reinterpret_cast<u32x4_t*>(Slo + lrow * SROW + 8 * k8) = lo;
     }
   }
   __syncthreads();
@@ -137,104 +141,92 @@ __global__ __launch_bounds__(256, 2) void readout_bf16_kernel(
   // end reread its last row, channel groups past d_k / d_v reread the last valid
   // one); such rows are never stored, padded S~ columns are zero (and the
   // partly padded k-step is masked), padded output channels are never stored.
-  // Block of 32 rows = two 16-row groups; per group 4 k-steps of q and 4
-  // channel groups of gate.
-  auto load_blk = [&](u32x4_t (&qr)[8], u32x4_t (&gr)[8], long rb) {
+  // One 16-row group: 4 k-steps of q (fetched one group ahead) and 4 channel
+  // groups of gate (fetched when the group starts: first used after its MFMAs).
+  auto grow_of = [&](long rg) { return chunk_row0 + (size_t)min(rg + jl, rows_total - 1); };
+  auto load_q = [&](u32x4_t (&qr)[4], long rg) {
+    const uint16_t* qp = q + grow_of(rg) * dk;
 #pragma unroll
-    for (int gi = 0; gi < 2; ++gi) {
-      const long myrow = min(rb + 16 * gi + jl, rows_total - 1);
-      const size_t grow = chunk_row0 + (size_t)myrow;
-      const uint16_t* gp = gate + grow * dv;
+    for (int s = 0; s < 4; ++s)
+      qr[s] = *reinterpret_cast<const u32x4_t*>(qp + min(32 * s + 8 * h, dk - 8));
+  };
+  auto load_g = [&](u32x4_t (&gr)[4], long rg) {
+    const uint16_t* gp = gate + grow_of(rg) * dv;
 #pragma unroll
-      for (int m = 0; m < 4; ++m)
-        gr[4 * gi + m] = *reinterpret_cast<const u32x4_t*>(gp + min(32 * m + 8 * h, dv - 8));
-    }
-#pragma unroll
-    for (int gi = 0; gi < 2; ++gi) {
-      const long myrow = min(rb + 16 * gi + jl, rows_total - 1);
-      const size_t grow = chunk_row0 + (size_t)myrow;
-      const uint16_t* qp = q + grow * dk;
-#pragma unroll
-      for (int s = 0; s < 4; ++s)
-        qr[4 * gi + s] = *reinterpret_cast<const u32x4_t*>(qp + min(32 * s + 8 * h, dk - 8));
-    }
+    for (int m = 0; m < 4; ++m)
+      gr[m] = *reinterpret_cast<const u32x4_t*>(gp + min(32 * m + 8 * h, dv - 8));
   };
 
-  // one 32-row block: MFMAs on (qr, gr) loaded one block earlier, then the
-  // RMSNorm/gate epilogue and the stores
-  auto process = [&](const u32x4_t (&qr)[8], const u32x4_t (&gr)[8], long rb) {
-    f32x4_t acc[2][8];
+  // one 16-row group: MFMAs on qr, then the RMSNorm/gate epilogue and the stores
+  auto process = [&](const u32x4_t (&qr)[4], const u32x4_t (&gr)[4], long rg) {
+    f32x4_t acc[8];
 #pragma unroll
-    for (int gi = 0; gi < 2; ++gi)
-#pragma unroll
-      for (int T = 0; T < 8; ++T) acc[gi][T] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    for (int T = 0; T < 8; ++T) acc[T] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       if (s >= NKS) continue;
-      u32x4_t b0 = qr[s], b1 = qr[4 + s];
-      if (kpad && 32 * s + 8 * h >= dk) b0 = b1 = z4;
+      u32x4_t b0 = qr[s];
+      if (kpad && 32 * s + 8 * h >= dk) b0 = z4;
 #pragma unroll
       for (int T = 0; T < 8; ++T) {
         if (T >= NT) continue;
         const int off = (16 * T + jl) * SROW + 32 * s + 8 * h;
         const u32x4_t ah = *reinterpret_cast<const u32x4_t*>(Shi + off);
         const u32x4_t al = *reinterpret_cast<const u32x4_t*>(Slo + off);
-        acc[0][T] = mfma16_bf16(ah, b0, acc[0][T]);
-        acc[1][T] = mfma16_bf16(ah, b1, acc[1][T]);
-        acc[0][T] = mfma16_bf16(al, b0, acc[0][T]);
-        acc[1][T] = mfma16_bf16(al, b1, acc[1][T]);
+        acc[T] = mfma16_bf16(ah, b0, acc[T]);
+        acc[T] = mfma16_bf16(al, b0, acc[T]);
       }
     }
+    // RMSNorm over the token's d_v outputs: 4 lanes x 32 channels each
+    float ss = 0.0f;
 #pragma unroll
-    for (int gi = 0; gi < 2; ++gi) {
-      // RMSNorm over the token's d_v outputs: 4 lanes x 32 channels each
-      float ss = 0.0f;
+    for (int T = 0; T < 8; ++T)
 #pragma unroll
-      for (int T = 0; T < 8; ++T)
+      for (int r = 0; r < 4; ++r) ss = fmaf(acc[T][r], acc[T][r], ss);
+    ss += __shfl_xor(ss, 16);
+    ss += __shfl_xor(ss, 32);
+    const float inv = rsqrtf(ss * inv_dv + eps);
+    const long myrow = rg + jl;
+    if (myrow < rows_total) {
+      const size_t grow = chunk_row0 + (size_t)myrow;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) ss = fmaf(acc[gi][T][r], acc[gi][T][r], ss);
-      ss += __shfl_xor(ss, 16);
-      ss += __shfl_xor(ss, 32);
-      const float inv = rsqrtf(ss * inv_dv + eps);
-      const long myrow = rb + 16 * gi + jl;
-      if (myrow < rows_total) {
-        const size_t grow = chunk_row0 + (size_t)myrow;
+      for (int m = 0; m < 4; ++m) {
+        const int ch = 32 * m + 8 * h;
+        if (ch >= dv) continue;
+        const f32x4_t w0 = *reinterpret_cast<const f32x4_t*>(Ws + ch);
+        const f32x4_t w1 = *reinterpret_cast<const f32x4_t*>(Ws + ch + 4);
+        const u32x4_t gv = gr[m];
+        float y[8];
 #pragma unroll
-        for (int m = 0; m < 4; ++m) {
-          const int ch = 32 * m + 8 * h;
-          if (ch >= dv) continue;
-          const f32x4_t w0 = *reinterpret_cast<const f32x4_t*>(Ws + ch);
-          const f32x4_t w1 = *reinterpret_cast<const f32x4_t*>(Ws + ch + 4);
-          const u32x4_t gv = gr[4 * gi + m];
-          float y[8];
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const float o = acc[gi][2 * m + (e >> 2)][e & 3];
-            const float gl = (e & 1) ? bf16_hi(gv[e >> 1]) : bf16_lo(gv[e >> 1]);
-            const float ww = e < 4 ? w0[e] : w1[e - 4];
-            const float sig = __builtin_amdgcn_rcpf(1.0f + __expf(-gl));
-            y[e] = o * inv * ww * sig;
-          }
-          u32x4_t ov;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) ov[e] = pack_bf16(y[2 * e], y[2 * e + 1]);
-          *reinterpret_cast<u32x4_t*>(out + grow * dv + ch) = ov;
+        for (int e = 0; e < 8; ++e) {
+          const float o = acc[2 * m + (e >> 2)][e & 3];
+          const float gl = (e & 1) ? bf16_hi(gv[e >> 1]) : bf16_lo(gv[e >> 1]);
+          const float ww = e < 4 ? w0[e] : w1[e - 4];
+          const float sig = __builtin_amdgcn_rcpf(1.0f + __expf(-gl));
+          y[e] = o * inv * ww * sig;
         }
+        u32x4_t ov;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ov[e] = pack_bf16(y[2 * e], y[2 * e + 1]);
+        *reinterpret_cast<u32x4_t*>(out + grow * dv + ch) = ov;
       }
     }
   };
 
-  // ping-pong register sets, unrolled by two (no register copies between blocks)
-  u32x4_t q0[8], g0[8], q1[8], g1[8];
-  auto blk_row = [&](int it) { return row0 + (long)(it * 4 + w) * 32; };
-  load_blk(q0, g0, blk_row(0));
-  for (int it = 0; it < kIters; it += 2) {
-    if (blk_row(it) >= rows_total) break;
-    if (it + 1 < kIters) load_blk(q1, g1, blk_row(it + 1));
-    process(q0, g0, blk_row(it));
-    if (it + 1 >= kIters || blk_row(it + 1) >= rows_total) break;
-    if (it + 2 < kIters) load_blk(q0, g0, blk_row(it + 2));
-    process(q1, g1, blk_row(it + 1));
+  // groups w, w + 8, w + 16, ... of the block; q ping-pongs between two
+  // register sets, unrolled by two (no register copies between groups)
+  u32x4_t q0[4], q1[4], gr[4];
+  auto grp_row = [&](int it) { return row0 + (long)(it * 8 + w) * 16; };
+  load_q(q0, grp_row(0));
+  for (int it = 0; it < kGroups; it += 2) {
+    if (grp_row(it) >= rows_total) break;
+    load_g(gr, grp_row(it));
+    if (it + 1 < kGroups) load_q(q1, grp_row(it + 1));
+    process(q0, gr, grp_row(it));
+    if (it + 1 >= kGroups || grp_row(it + 1) >= rows_total) break;
+    load_g(gr, grp_row(it + 1));
+    if (it + 2 < kGroups) load_q(q0, grp_row(it + 2));
+    process(q1, gr, grp_row(it + 1));
   }
 }
 
@@ -316,7 +308,7 @@ hipError_t launch_readout(const Plan& p, const void* q, const void* gate, const 
     const unsigned per = xcd_per((unsigned)p.units * p.n * nblk);
     auto kern = (p.dk == 128 && p.dv == 128) ? readout_bf16_kernel<128, 128>
                                              : readout_bf16_kernel<0, 0>;
-    hipLaunchKernelGGL(kern, dim3(kXcds * per), dim3(kThreads), 0, s,
+    hipLaunchKernelGGL(kern, dim3(kXcds * per), dim3(kThreadsR), 0, s,
                        static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(gate),
                        rms_weight, static_cast<uint16_t*>(out), w.ST, p.dk, p.dv, p.F, p.U, p.C,
                        p.r, p.n, p.eps, p.units, nblk, per);
