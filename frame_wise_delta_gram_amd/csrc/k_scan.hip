@@ -228,37 +228,16 @@ __global__ __launch_bounds__(256) void scan_kernel(const float* __restrict__ Mc,
 }
 
 // ---------------------------------------------------------------------------
-// bf16x3 versions (bf16 features).  X (the composed map or state) lives in LDS
-// as a pair of bf16 arrays (hi, lo) with a 136-element (272-byte) row stride.
-// A transition never goes through LDS: the product is formed transposed,
+// bf16x3 versions (bf16 features).  X (the composed map or state) and the
+// current transition live in LDS as pairs of bf16 arrays (hi, lo) with a
+// 136-element (272-byte) row stride.  The product is formed transposed,
 //   T = M[jr .. jr + 31, :] X^T = ((X M)[:, jr .. jr + 31])^T   (M symmetric),
-// so a wave's transition operand is 32 rows of M read straight from memory
-// into MFMA operand registers (16-byte loads), X is the B operand (16-byte LDS
-// rows), and each accumulator lane ends up holding 4 consecutive columns of
-// one row of X M, which are stored as one 8-byte LDS write per half or one
-// 16-byte global store.
+// so a wave's transition operand is 32 rows of M (loaded from memory as whole
+// contiguous rows, split, staged in LDS, read back as 16-byte operand rows), X
+// is the B operand (16-byte LDS rows), and each accumulator lane ends up
+// holding 4 consecutive columns of one row of X M, which are stored as one
+// 8-byte LDS write per half or one 16-byte global store.
 constexpr int SB = 136;
-
-// A wave's 32 rows (jr + l % 32) of a d_k x d_k fp32 matrix in A-operand order:
-// v[2 kk + h] = channels 16 kk + 8 (l / 32) + 4 h .. + 3.  Addresses are
-// clamped into the matrix; tile_split zeroes what lies outside.
-struct TileF32 {
-  f32x4_t v[16];
-};
-struct TileSplit {
-  u32x4_t h[8], l[8];
-};
-
-__device__ __forceinline__ void tile_rows_load(TileF32& t, const float* M, int dk, int jr) {
-  const int lane = lane_id();
-  const float* p = M + (size_t)min(jr + (lane & 31), dk - 1) * dk + 8 * (lane >> 5);
-#pragma unroll
-  for (int kk = 0; kk < 8; ++kk) {
-    const int k = min(16 * kk, dk - 16);
-    t.v[2 * kk] = *reinterpret_cast<const f32x4_t*>(p + k);
-    t.v[2 * kk + 1] = *reinterpret_cast<const f32x4_t*>(p + k + 4);
-  }
-}
 
 // fp32 -> (hi, lo) bf16 operand pairs: hi = bf16(x), lo = bf16(x - hi)
 __device__ __forceinline__ void split_pair(float x0, float x1, uint32_t& h, uint32_t& l) {
@@ -266,83 +245,47 @@ __device__ __forceinline__ void split_pair(float x0, float x1, uint32_t& h, uint
   l = pack_bf16(x0 - bf16_lo(h), x1 - bf16_hi(h));
 }
 
-__device__ __forceinline__ void tile_split(TileSplit& s, const TileF32& t, int dk, int jr) {
-  const bool ok = jr + (lane_id() & 31) < dk;
-#pragma unroll
-  for (int kk = 0; kk < 8; ++kk) {
-    uint32_t h[4], l[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const f32x4_t& v = t.v[2 * kk + (e >> 1)];
-      const float x0 = ok ? v[2 * (e & 1)] : 0.0f;
-      const float x1 = ok ? v[2 * (e & 1) + 1] : 0.0f;
-      split_pair(x0, x1, h[e], l[e]);
-    }
-    s.h[kk] = u32x4_t{h[0], h[1], h[2], h[3]};
-    s.l[kk] = u32x4_t{l[0], l[1], l[2], l[3]};
-  }
-}
-
-// acc[x] += T for the X row tiles xr0 + 32 x (x < NX), nk = d_k / 16 k-steps:
-// hi*hi + lo*hi + hi*lo with fp32 accumulation.
-template <int NX>
-__device__ __forceinline__ void split_mm_t(f32x16_t (&acc)[NX], const TileSplit& m,
-                                           const __bf16* xh, const __bf16* xl, int xr0, int nk) {
-  const int lane = lane_id();
-  const int base = (xr0 + (lane & 31)) * SB + 8 * (lane >> 5);
-#pragma unroll
-  for (int kk = 0; kk < 8; ++kk) {
-    if (kk < nk) {
-#pragma unroll
-      for (int x = 0; x < NX; ++x) {
-        const int off = base + 32 * x * SB + 16 * kk;
-        const u32x4_t bh = *reinterpret_cast<const u32x4_t*>(xh + off);
-        const u32x4_t bl = *reinterpret_cast<const u32x4_t*>(xl + off);
-        acc[x] = mfma_bf16(m.h[kk], bh, acc[x]);
-        acc[x] = mfma_bf16(m.l[kk], bh, acc[x]);
-        acc[x] = mfma_bf16(m.h[kk], bl, acc[x]);
-      }
-    }
-  }
-}
-
-// Half (channels 64 kh .. + 63) of a wave's 32 rows of a d_k x d_k fp32
-// matrix, in the same operand order (clamped like tile_rows_load).
-struct HalfTileF32 {
-  f32x4_t v[8];
+// A wave's share of the rows jr .. jr + 31 of a d_k x d_k fp32 matrix, loaded
+// contiguously: NL 16-byte pieces per lane, piece i = row jr + (64 i + l) / W,
+// channels c0 + 4 ((64 i + l) % W) .. + 3 with W = (channels per row) / 4 lanes
+// per row (W = 32: whole 512-byte rows, two per instruction; W = 16: 256-byte
+// half rows, four per instruction).  Addresses are clamped into the matrix;
+// rows_split zeroes what lies outside.
+template <int NL>
+struct RowsF32 {
+  f32x4_t v[NL];
 };
 
-__device__ __forceinline__ void half_tile_load(HalfTileF32& t, const float* M, int dk, int jr,
-                                               int kh) {
+template <int NL, int W>
+__device__ __forceinline__ void rows_load(RowsF32<NL>& t, const float* M, int dk, int jr, int c0) {
   const int lane = lane_id();
-  const float* p = M + (size_t)min(jr + (lane & 31), dk - 1) * dk + 8 * (lane >> 5);
 #pragma unroll
-  for (int kk = 0; kk < 4; ++kk) {
-    const int k = min(64 * kh + 16 * kk, dk - 16);
-    t.v[2 * kk] = *reinterpret_cast<const f32x4_t*>(p + k);
-    t.v[2 * kk + 1] = *reinterpret_cast<const f32x4_t*>(p + k + 4);
+  for (int i = 0; i < NL; ++i) {
+    const int e = 64 * i + lane;
+    const int row = min(jr + e / W, dk - 1);
+    const int col = min(c0 + 4 * (e % W), dk - 4);
+    t.v[i] = *reinterpret_cast<const f32x4_t*>(M + (size_t)row * dk + col);
   }
 }
 
-// ... split into (hi, lo) rows of LDS (row jr + l % 32, 16-byte pieces),
-// zero outside the d_k x d_k matrix
-__device__ __forceinline__ void half_tile_store(__bf16* mh, __bf16* ml, const HalfTileF32& t,
-                                                int dk, int jr, int kh) {
+// ... split into (hi, lo) LDS rows (row stride SB, row `row - rbase` of the
+// region at mh / ml), zero outside the d_k x d_k matrix
+template <int NL, int W>
+__device__ __forceinline__ void rows_split(__bf16* mh, __bf16* ml, int rbase, const RowsF32<NL>& t,
+                                           int dk, int jr, int c0) {
   const int lane = lane_id();
-  const int row = jr + (lane & 31);
 #pragma unroll
-  for (int kk = 0; kk < 4; ++kk) {
-    const int k0 = 64 * kh + 16 * kk;
-    const bool ok = row < dk && k0 < dk;
-    uint32_t h[4], l[4];
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const f32x4_t& v = t.v[2 * kk + (e >> 1)];
-      split_pair(ok ? v[2 * (e & 1)] : 0.0f, ok ? v[2 * (e & 1) + 1] : 0.0f, h[e], l[e]);
-    }
-    const int off = row * SB + k0 + 8 * (lane >> 5);
-    *reinterpret_cast<u32x4_t*>(mh + off) = u32x4_t{h[0], h[1], h[2], h[3]};
-    *reinterpret_cast<u32x4_t*>(ml + off) = u32x4_t{l[0], l[1], l[2], l[3]};
+  for (int i = 0; i < NL; ++i) {
+    const int e = 64 * i + lane;
+    const int row = jr + e / W;
+    const int col = c0 + 4 * (e % W);
+    const bool ok = row < dk && col < dk;
+    uint32_t h0, l0, h1, l1;
+    split_pair(ok ? t.v[i][0] : 0.0f, ok ? t.v[i][1] : 0.0f, h0, l0);
+    split_pair(ok ? t.v[i][2] : 0.0f, ok ? t.v[i][3] : 0.0f, h1, l1);
+    const int off = (row - rbase) * SB + col;
+    *reinterpret_cast<u32x2_t*>(mh + off) = u32x2_t{h0, h1};
+    *reinterpret_cast<u32x2_t*>(ml + off) = u32x2_t{l0, l1};
   }
 }
 
@@ -441,8 +384,8 @@ __device__ __forceinline__ void x_fill(__bf16* xh, __bf16* xl, const float* src,
 
 // compose (bf16): one workgroup of 8 waves per work item; wave w owns output
 // columns jr = 32 (w % 4) .. + 31 for X rows 64 (w / 4) .. + 63.  The two waves
-// of a column block load one half each of the transition rows they share and
-// stage them, split, in LDS.  Work items: (unit, chunk, chain) with the chain
+// of a column block load one half each (contiguous 256-byte half rows) of the
+// transition rows they share and stage them, split, in LDS.  Work items: (unit, chunk, chain) with the chain
 // fastest (the three chains of a chunk read the same transitions and share an
 // XCD), then one text-seed item per unit.
 template <bool FULL>
@@ -480,11 +423,11 @@ __global__ __launch_bounds__(512, 1) void compose_split_kernel(
   auto Bp = [&](int f) { return Bw + ((size_t)u * Fp1 + f + 1) * SS; };
   const bool active = jr < dk && xr0 < rows;
 
-  HalfTileF32 mf;
-  half_tile_load(mf, Mp(frame(0)), dk, jr, kh);
+  RowsF32<8> mf;
+  rows_load<8, 16>(mf, Mp(frame(0)), dk, jr, 64 * kh);
   x_fill(Xh, Xl, chain == 0 ? nullptr : Bp(frame(0)), chain == 0 ? 0 : dv, dk,
          seed ? seed_scale : 1.0f);
-  half_tile_store(Mh, Ml, mf, dk, jr, kh);
+  rows_split<8, 16>(Mh, Ml, 0, mf, dk, jr, 64 * kh);
   __syncthreads();
 
   float* dst = chain == 0 ? Mc + ((size_t)u * n + c) * dk * dk
@@ -497,7 +440,7 @@ __global__ __launch_bounds__(512, 1) void compose_split_kernel(
   for (int s = 0; s < nf; ++s) {
     const bool last = s == nf - 1;
     if (!last) {  // the next frame's transition and write fly while this step multiplies
-      half_tile_load(mf, Mp(frame(s + 1)), dk, jr, kh);
+      rows_load<8, 16>(mf, Mp(frame(s + 1)), dk, jr, 64 * kh);
       if (chain != 0) rows_prefetch_t<2>(bq, Bp(frame(s + 1)), dv, dk, xr0, jr);
     }
     f32x16_t acc[2] = {zero16(), zero16()};
@@ -534,19 +477,20 @@ __global__ __launch_bounds__(512, 1) void compose_split_kernel(
           x_store_quad(Xh, Xl, xr0 + 32 * x + (lane & 31), jr + 8 * q + 4 * (lane >> 5), v);
         }
     }
-    half_tile_store(Mh, Ml, mf, dk, jr, kh);
+    rows_split<8, 16>(Mh, Ml, 0, mf, dk, jr, 64 * kh);
     __syncthreads();
   }
 }
 
 // scan (bf16): one workgroup per (32-row block of the state, unit, direction);
-// wave w owns state columns 32 w .. + 31.  The transition operand of the
-// forward step S Mc is read from the rows of Mc^T, that of the reverse step
-// S Mc^T from the rows of Mc.  Transitions and injections are fetched one
-// chunk ahead, unconditionally (the last step refetches its own chunk), and the
-// injections alternate between two register sets, so that no wait for a
-// load also waits for the state stores issued after it.  FULL: d_k = 128 and
-// d_v a multiple of 32 (no masking anywhere).
+// wave w owns state columns 32 w .. + 31, i.e. transition rows 32 w .. + 31,
+// which it loads contiguously (whole 512-byte rows) one chunk ahead and stages,
+// split, in its own LDS region.  The transition operand of the forward step
+// S Mc is read from the rows of Mc^T, that of the reverse step S Mc^T from the
+// rows of Mc.  The next chunk's loads are unconditional (the last step
+// refetches its own chunk) and the injections alternate between two register
+// sets, so that no wait for a load also waits for the state stores issued
+// after it.  FULL: d_k = 128 and d_v a multiple of 32 (no masking anywhere).
 template <bool FULL>
 __global__ __launch_bounds__(256) void scan_split_kernel(const float* __restrict__ McR,
                                                          const float* __restrict__ McTr,
@@ -556,6 +500,8 @@ __global__ __launch_bounds__(256) void scan_split_kernel(const float* __restrict
                                                          int n) {
   __shared__ __align__(16) __bf16 Xh[32 * SB];
   __shared__ __align__(16) __bf16 Xl[32 * SB];
+  __shared__ __align__(16) __bf16 Mh[128 * SB];
+  __shared__ __align__(16) __bf16 Ml[128 * SB];
   const int rb = blockIdx.x;  // rows [32 rb, 32 rb + 32) of the state
   const int u = blockIdx.y;
   const int dir = blockIdx.z;  // 0: forward (P), 1: reverse (R)
@@ -571,23 +517,22 @@ __global__ __launch_bounds__(256) void scan_split_kernel(const float* __restrict
   const float* Mb = (dir == 0 ? McTr : McR) + (size_t)u * n * dk * dk;
   const bool active = FULL || jr < dk;
 
-  TileF32 mf;
-  TileSplit ms;
+  RowsF32<16> mf;
   f32x4_t ja[1][4], jb[1][4];
-  tile_rows_load(mf, Mb + (size_t)chunk(0) * dk * dk, dk, jr);
+  rows_load<16, 32>(mf, Mb + (size_t)chunk(0) * dk * dk, dk, jr, 0);
   rows_prefetch_t<1>(ja, Jb + (size_t)chunk(0) * SS, nrows, dk, 0, jr);
   x_fill(Xh, Xl, S + (size_t)(dir == 0 ? 0 : n) * SS + (size_t)r0 * dk, nrows, dk, 1.0f);
-  tile_split(ms, mf, dk, jr);
+  rows_split<16, 32>(Mh, Ml, 0, mf, dk, jr, 0);
   __syncthreads();
 
   // one chunk: X <- X Mc_j + J_j using jcur, fetching chunk s + 1 into jnext
   auto step = [&](int s, f32x4_t (&jcur)[1][4], f32x4_t (&jnext)[1][4]) {
     const int j = chunk(s);
     const int sn = min(s + 1, n - 1);
-    tile_rows_load(mf, Mb + (size_t)chunk(sn) * dk * dk, dk, jr);
+    rows_load<16, 32>(mf, Mb + (size_t)chunk(sn) * dk * dk, dk, jr, 0);
     rows_prefetch_t<1>(jnext, Jb + (size_t)chunk(sn) * SS, nrows, dk, 0, jr);
     f32x16_t acc[1] = {zero16()};
-    if (active) split_mm_t<1>(acc, ms, Xh, Xl, 0, nk);
+    if (active) split_mm_t_lds<1>(acc, Mh, Ml, jr, Xh, Xl, 0, nk);
     __syncthreads();  // every wave has read X
     if (active) {
       float* dstp = S + (size_t)(dir == 0 ? j + 1 : j) * SS + (size_t)r0 * dk;
@@ -602,7 +547,8 @@ __global__ __launch_bounds__(256) void scan_split_kernel(const float* __restrict
         x_store_quad(Xh, Xl, row, col, v);
       }
     }
-    tile_split(ms, mf, dk, jr);
+    // this wave's transition rows: its own MFMA reads of them are done
+    rows_split<16, 32>(Mh, Ml, 0, mf, dk, jr, 0);
     __syncthreads();
   };
   int s = 0;
