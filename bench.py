@@ -52,8 +52,9 @@ def algorithmic(cfg):
                    + u * (F + 1) * (dk + dv) * dk * 4)                  # A, B written
     readout_bytes = (th * (dk + 2 * dv) * eb                           # q, gate read; out written
                      + u * n * 2 * st + dv * 4)                         # two states per chunk
-    solve_bytes = 2 * u * (F + 1) * mat + u * 3 * st                    # A in, M out; B_T in, 2 seeds
-    compose_bytes = u * F * (mat + st) + u * n * (2 * mat + 2 * st)     # M, B in; Mc, McT, Jf, Jr
+    solve_bytes = 2 * u * (F + 1) * mat                                 # A in, M out
+    compose_bytes = (u * (F + 1) * (mat + st) + u * n * (2 * mat + 2 * st)  # M, B in; Mc, McT, Jf, Jr
+                     + u * 2 * st)                                      # the two seed copies
     scan_bytes = u * n * (2 * mat + 2 * st) + u * 2 * n * st            # chunk maps in; P, R out
     stats_flops = 2 * (th + tt) * (dk + dv) * dk     # [K|V]^T (beta K), full Gram
     readout_flops = 2 * th * dk * dv                 # S~ q
