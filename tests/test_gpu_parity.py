@@ -41,6 +41,10 @@ EDGE = {
                             text_tokens=5, dtype="bf16", radius=3),
     "stress-small": C(cfg_id=312, units=2, frames=15, tokens=512, d_k=128, d_v=128,
                       text_tokens=64, dtype="bf16", beta_mu=2.0, stress=True),
+    "no-video-tokens": C(cfg_id=314, units=2, frames=7, tokens=0, d_k=64, d_v=64, text_tokens=9,
+                         dtype="bf16"),
+    "no-tokens-f32": C(cfg_id=315, units=1, frames=4, tokens=0, d_k=16, d_v=16, text_tokens=0,
+                       dtype="f32"),
     "eps-zero-f32": C(cfg_id=313, units=1, frames=10, tokens=16, d_k=16, d_v=16, text_tokens=8,
                       dtype="f32", rms_eps=0.0),
 }

@@ -27,6 +27,13 @@ CASES = {
                                       text_tokens=5, dtype="f32", chunk=2),
     "dk32-dv96-bf16": W.custom_config(cfg_id=203, units=3, frames=11, tokens=70, d_k=32, d_v=96,
                                       text_tokens=0, dtype="bf16", chunk=3, radius=2),
+    # frames without tokens: statistics exactly zero, every state the seed
+    "no-video-tokens-bf16": W.custom_config(cfg_id=204, units=2, frames=7, tokens=0, d_k=32,
+                                            d_v=48, text_tokens=9, dtype="bf16", chunk=2),
+    "no-tokens-bf16": W.custom_config(cfg_id=205, units=2, frames=7, tokens=0, d_k=128, d_v=128,
+                                      text_tokens=0, dtype="bf16"),
+    "no-video-tokens-f32": W.custom_config(cfg_id=206, units=1, frames=6, tokens=0, d_k=16,
+                                           d_v=32, text_tokens=5, dtype="f32"),
 }
 
 
