@@ -18,7 +18,12 @@ in chunks (1 in [VDN] Sec. 2.1); n = ceil(F / C) chunks; T text tokens.
 
 Readings taken where the pages leave a step open (each is also listed in the
 design notes):
-  * decay alpha = 1 (no channel-wise decay, hence no decay bridge in Eq. (A.4));
+  * decay: alpha = 1 by default (no channel-wise decay, no decay bridge).  With
+    a per-frame decay alpha_t in [0, 1]^{d_k} ([VDN] Sec. 3.1 Eq. (2)), the
+    inherited state is S Diag(alpha_t) in BOTH scans, each frame decaying the
+    state it enters with its own gate, and a query of frame t reads the bridged
+    boundary states of App. A.3 Eq. (A.4) (the decay products run over the
+    window frames up to and including t on each side);
   * no boundary anchors: every frame enters both scans;
   * text seed, mode 0 (default): S_T is ONE frame-wise update from S = 0 over all
     T text tokens (the prompt "as a leading virtual frame", [VDN] Sec. 5) and each
@@ -37,9 +42,9 @@ from __future__ import annotations
 import numpy as np
 
 __all__ = [
-    "frame_statistics", "frame_update", "transition", "text_state", "chunk_bounds",
-    "directional_states", "gather", "rms_norm", "sigmoid", "readout", "forward_unit",
-    "forward",
+    "frame_statistics", "frame_update", "decay", "transition", "text_state", "chunk_bounds",
+    "directional_states", "gather", "window_frames", "bridge", "rms_norm", "sigmoid", "readout",
+    "forward_unit", "forward",
 ]
 
 f64 = np.float64
@@ -76,9 +81,19 @@ def frame_update(S_bar, A, B):
     return np.linalg.solve(G.T, (S_bar + B).T).T
 
 
-def transition(A):
-    """Inherited-state transition with alpha = 1, [VDN] App. A.1 Eq. (A.1): M = (I + A)^{-1}."""
-    return np.linalg.inv(np.eye(A.shape[0]) + A)
+def decay(S, alpha):
+    """Channel-wise decay of an inherited state, [VDN] Sec. 3.1 Eq. (2):
+    S_bar = S Diag(alpha) (column j of S, key channel j, scaled by alpha_j)."""
+    return np.asarray(S, f64) * np.asarray(alpha, f64)[None, :]
+
+
+def transition(A, alpha=None):
+    """Inherited-state transition, [VDN] App. A.1 Eq. (A.1):
+    M = Diag(alpha) (I + A)^{-1}, i.e. (I + A)^{-1} when alpha = 1 (None)."""
+    M = np.linalg.inv(np.eye(A.shape[0]) + A)
+    if alpha is None:
+        return M
+    return np.asarray(alpha, f64)[:, None] * M
 
 
 def text_state(text_k, text_v, text_beta, d_k, d_v, seed_mode=0):
@@ -110,13 +125,15 @@ def chunk_bounds(F, C):
     return [(s, min(s + C, F)) for s in range(0, F, C)]
 
 
-def directional_states(stats, seed, C):
-    """Both directional scans of [VDN] Sec. 2.2 / App. A.3 (alpha = 1, no anchors).
+def directional_states(stats, seed, C, alpha=None):
+    """Both directional scans of [VDN] Sec. 2.2 / App. A.3 (no anchors).
 
-    stats: list of (A_f, B_f) for f = 0..F-1.
-    Forward: start at the seed and apply Eq. (5) to frames 0, 1, ..., F-1;
+    stats: list of (A_f, B_f) for f = 0..F-1; alpha: F x d_k decay gates or None
+    (alpha = 1).  Entering frame f, the inherited state is decayed by alpha_f
+    (Eq. (2)) and updated by Eq. (5), in either direction.
+    Forward: start at the seed and apply frames 0, 1, ..., F-1;
       P[0] = seed, P[j+1] = the state after the last frame of chunk j.
-    Reverse: start at the seed and apply Eq. (5) to frames F-1, ..., 0;
+    Reverse: start at the seed and apply frames F-1, ..., 0;
       R[n] = seed, R[j] = the state after the first frame of chunk j.
     Returns (P, R), each of shape (n + 1, d_v, d_k).
     """
@@ -125,18 +142,23 @@ def directional_states(stats, seed, C):
     n = len(bounds)
     P = np.zeros((n + 1,) + seed.shape)
     R = np.zeros((n + 1,) + seed.shape)
+
+    def enter(S, f):
+        S_bar = S if alpha is None else decay(S, alpha[f])
+        return frame_update(S_bar, *stats[f])
+
     S = seed.copy()
     P[0] = S
     for j, (lo, hi) in enumerate(bounds):
         for f in range(lo, hi):
-            S = frame_update(S, *stats[f])
+            S = enter(S, f)
         P[j + 1] = S
     S = seed.copy()
     R[n] = S
     for j in range(n - 1, -1, -1):
         lo, hi = bounds[j]
         for f in range(hi - 1, lo - 1, -1):
-            S = frame_update(S, *stats[f])
+            S = enter(S, f)
         R[j] = S
     return P, R
 
@@ -149,6 +171,33 @@ def gather(P, R, c, radius):
     """
     n = P.shape[0] - 1
     return P[max(c - radius, 0)] + R[min(c + radius + 1, n)]
+
+
+def window_frames(c, C, radius, F):
+    """First and last frame of the local window [c - r, c + r] (in chunks) of chunk c,
+    clipped to the clip: [l, h] with l = C max(c - r, 0), h = min(C (c + r + 1), F) - 1."""
+    return C * max(c - radius, 0), min(C * (c + radius + 1), F) - 1
+
+
+def bridge(P, R, f, C, radius, alpha):
+    """State read by the queries of frame f with decay, [VDN] App. A.3 Eq. (A.4)
+    (no anchors):
+
+      P_{l-1} Diag(prod_{s=l}^{f} alpha_s) + R_{h+1} Diag(prod_{s=f}^{h} alpha_s),
+
+    [l, h] the frames of the window of f's chunk (window_frames), P_{l-1} the
+    forward state through frame l - 1 (the seed when l = 0), R_{h+1} the reverse
+    state from the last frame down to h + 1 (the seed when h = F - 1).  The
+    products are channel-wise over the key channels.
+    """
+    alpha = np.asarray(alpha, f64)
+    F = alpha.shape[0]
+    n = P.shape[0] - 1
+    c = f // C
+    lo, hi = window_frames(c, C, radius, F)
+    d_f = np.prod(alpha[lo:f + 1], axis=0)
+    d_r = np.prod(alpha[f:hi + 1], axis=0)
+    return decay(P[max(c - radius, 0)], d_f) + decay(R[min(c + radius + 1, n)], d_r)
 
 
 def rms_norm(O, w, eps):
@@ -173,14 +222,15 @@ def readout(S_tilde, Q, G, w, eps):
 
 
 def forward_unit(q, k, v, beta, gate, text_k, text_v, text_beta, rms_weight,
-                 chunk=5, radius=1, eps=1e-6, seed_mode=0, taps=False):
+                 chunk=5, radius=1, eps=1e-6, seed_mode=0, taps=False, alpha=None):
     """VDA forward for one unit.
 
     q: F x U x d_k, k: F x U x d_k, v: F x U x d_v, beta: F x U,
     gate: F x U x d_v (gate logits), text_k: T x d_k, text_v: T x d_v,
-    text_beta: T, rms_weight: d_v.  Returns out (F x U x d_v), plus a dict of
-    intermediates when taps=True: A, B (per frame), M (per frame, Eq. (A.1)),
-    seed, P, R.
+    text_beta: T, rms_weight: d_v, alpha: F x d_k decay gates in [0, 1] or None
+    (alpha = 1).  Returns out (F x U x d_v), plus a dict of intermediates when
+    taps=True: A, B (per frame), M (per frame, Eq. (A.1)), seed, P, R, and with
+    decay the bridged state St read by each frame (F x d_v x d_k).
     """
     q = np.asarray(q, f64)
     k = np.asarray(k, f64)
@@ -188,28 +238,40 @@ def forward_unit(q, k, v, beta, gate, text_k, text_v, text_beta, rms_weight,
     beta = np.asarray(beta, f64)
     F, U, d_k = k.shape
     d_v = v.shape[-1]
+    if alpha is not None:
+        alpha = np.asarray(alpha, f64).reshape(F, d_k)
+        if np.any(alpha < 0) or np.any(alpha > 1):
+            raise ValueError("decay gates must lie in [0, 1]")
     seed = text_state(text_k, text_v, text_beta, d_k, d_v, seed_mode)
     stats = [frame_statistics(k[f], v[f], beta[f]) for f in range(F)]
-    P, R = directional_states(stats, seed, chunk)
+    P, R = directional_states(stats, seed, chunk, alpha)
     out = np.zeros((F, U, d_v))
+    St = np.zeros((F, d_v, d_k))
     for c, (lo, hi) in enumerate(chunk_bounds(F, chunk)):
         S_tilde = gather(P, R, c, radius)
         for f in range(lo, hi):
+            if alpha is not None:
+                S_tilde = bridge(P, R, f, chunk, radius, alpha)
+            St[f] = S_tilde
             out[f] = readout(S_tilde, q[f], gate[f], rms_weight, eps)
     if not taps:
         return out
     tap = {
         "A": np.array([s[0] for s in stats]).reshape(F, d_k, d_k),
         "B": np.array([s[1] for s in stats]).reshape(F, d_v, d_k),
-        "M": np.array([transition(s[0]) for s in stats]).reshape(F, d_k, d_k),
+        "M": np.array([transition(stats[f][0], None if alpha is None else alpha[f])
+                       for f in range(F)]).reshape(F, d_k, d_k),
         "seed": seed, "P": P, "R": R,
     }
+    if alpha is not None:
+        tap["St"] = St
     return out, tap
 
 
 def forward(q, k, v, beta, gate, text_k, text_v, text_beta, rms_weight,
-            chunk=5, radius=1, eps=1e-6, seed_mode=0, taps=False, units=None):
-    """VDA forward over all units (leading axis of every per-unit tensor).
+            chunk=5, radius=1, eps=1e-6, seed_mode=0, taps=False, units=None, alpha=None):
+    """VDA forward over all units (leading axis of every per-unit tensor;
+    alpha: units x F x d_k decay gates, or None for alpha = 1).
 
     ``units`` restricts the work to a subset of unit indices; the result then
     holds only those units, in that order.
@@ -218,7 +280,8 @@ def forward(q, k, v, beta, gate, text_k, text_v, text_beta, rms_weight,
     outs, tapl = [], []
     for u in idx:
         r = forward_unit(q[u], k[u], v[u], beta[u], gate[u], text_k[u], text_v[u],
-                         text_beta[u], rms_weight, chunk, radius, eps, seed_mode, taps)
+                         text_beta[u], rms_weight, chunk, radius, eps, seed_mode, taps,
+                         None if alpha is None else alpha[u])
         if taps:
             outs.append(r[0])
             tapl.append(r[1])

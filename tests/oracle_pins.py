@@ -16,6 +16,9 @@ facts come from "Video DeltaNet" (arXiv 2609.20744), cited as [VDN]:
   * Eq. (1b): the two seeds together read the text state exactly once;
   * Sec. 2.2 and Eq. (A.4): forward and reverse regions are disjoint from the
     local window and from each other;
+  * Sec. 3.1 Eq. (2), App. A.1 and A.3: with channel-wise decay the inherited
+    state is S Diag(alpha), Prop. 1 still holds, and with no writes the decay
+    bridge telescopes to a closed form;
   * Eq. (1c): RMSNorm then an element-wise sigmoid gate.
 
 None of these re-types the oracle's own formula: gradients and objectives are
@@ -518,10 +521,217 @@ def pin_rmsnorm_gate(o):
         assert np.max(np.abs(half - 0.5 * full)) <= 1e-13
 
 
+# ----------------------------------------------------------------------------- decay (NEXT-1)
+def _random_alpha(rng, F, dk, lo=0.3):
+    return rng.uniform(lo, 1.0, (F, dk))
+
+
+def pin_decay_update(o):
+    """[VDN] Sec. 3.1 Eq. (2) and App. A.1 Eq. (A.1): entering a frame with decay
+    alpha, the inherited state S Diag(alpha) (scaled channel by channel in a hand
+    loop) is updated by Eq. (5): the gradient of Eq. (4) around that inherited
+    state vanishes, and the result equals S M + J with M = Diag(alpha)(I + A)^{-1},
+    J = B (I + A)^{-1}."""
+    rng = _rng(31)
+    for _ in range(5):
+        S_prev, K, V, beta = _frame(rng, U=9, dk=6, dv=4)
+        alpha = rng.uniform(0, 1, 6)
+        S_bar = S_prev.copy()
+        for i in range(S_bar.shape[0]):
+            for j in range(S_bar.shape[1]):
+                S_bar[i, j] = S_prev[i, j] * alpha[j]
+        assert np.max(np.abs(o.decay(S_prev, alpha) - S_bar)) <= 1e-15
+        A, B = o.frame_statistics(K, V, beta)
+        S = o.frame_update(o.decay(S_prev, alpha), A, B)
+        g = _gradient(S, S_bar, K, V, beta)
+        assert np.linalg.norm(g) <= 1e-12 * max(1.0, np.linalg.norm(S_bar))
+        inv = np.linalg.solve(np.eye(6) + A, np.eye(6))
+        assert np.max(np.abs(S - (S_prev @ o.transition(A, alpha) + B @ inv))) <= 1e-12
+
+
+def pin_decay_one(o):
+    """alpha = 1 everywhere is no decay: identical states and outputs to the
+    undecayed definition (the bridge products are all one)."""
+    rng = _rng(32)
+    x = _random_unit(rng, 11, 5, 6, 4, 3)
+    out0, t0 = _call(o, x, chunk=3, radius=1, taps=True)
+    out1, t1 = _call(o, x, chunk=3, radius=1, taps=True, alpha=np.ones((11, 6)))
+    assert np.array_equal(out0, out1)
+    assert np.array_equal(t0["P"], t1["P"]) and np.array_equal(t0["R"], t1["R"])
+
+
+def pin_decay_pure_bridge(o):
+    """No video writes (beta = 0) and a text seed s: each scan only decays, so
+    P[j] = s Diag(prod_{g < Cj} alpha_g), R[j] = s Diag(prod_{g >= Cj} alpha_g),
+    and the bridge of App. A.3 telescopes: frame f reads
+    s Diag(prod_{g <= f} alpha_g + prod_{g >= f} alpha_g), whatever the chunk
+    length and radius (cumulative products computed here with a running loop)."""
+    rng = _rng(33)
+    for C, r, F in ((5, 1, 17), (2, 2, 9), (3, 0, 10), (1, 1, 6), (4, 3, 8)):
+        x = _random_unit(rng, F, 3, 5, 4, 4)
+        x["beta"][:] = 0.0
+        alpha = _random_alpha(rng, F, 5, lo=0.0)
+        _, t = _call(o, x, chunk=C, radius=r, taps=True, alpha=alpha)
+        s = t["seed"]
+        fwd = np.ones((F + 1, 5))   # fwd[f] = prod_{g < f} alpha_g
+        for f in range(F):
+            fwd[f + 1] = fwd[f] * alpha[f]
+        bwd = np.ones((F + 1, 5))   # bwd[f] = prod_{g >= f} alpha_g
+        for f in range(F - 1, -1, -1):
+            bwd[f] = bwd[f + 1] * alpha[f]
+        n = -(-F // C)
+        for j in range(n + 1):
+            e = min(C * j, F)
+            assert np.max(np.abs(t["P"][j] - s * fwd[e][None, :])) <= 1e-14, (C, r, j)
+            assert np.max(np.abs(t["R"][j] - s * bwd[e][None, :])) <= 1e-14, (C, r, j)
+        for f in range(F):
+            want = s * (fwd[f + 1] + bwd[f])[None, :]
+            assert np.max(np.abs(t["St"][f] - want)) <= 1e-14, (C, r, f)
+
+
+def pin_decay_zero(o):
+    """alpha = 0 erases every inherited state: a frame's state is its own write
+    alone, the state after chunk j comes from its last frame only, and every
+    bridged state is exactly zero (each product contains alpha_f = 0), so every
+    output is zero."""
+    rng = _rng(34)
+    F, C = 8, 3
+    x = _random_unit(rng, F, 4, 5, 3, 2)
+    out, t = _call(o, x, chunk=C, radius=1, taps=True, alpha=np.zeros((F, 5)))
+    assert np.all(out == 0.0) and np.all(t["St"] == 0.0)
+    for j, (lo, hi) in enumerate(o.chunk_bounds(F, C)):
+        A, B = o.frame_statistics(x["k"][hi - 1], x["v"][hi - 1], x["beta"][hi - 1])
+        S_last = _update(o, np.zeros((3, 5)), x["k"][hi - 1], x["v"][hi - 1], x["beta"][hi - 1])
+        assert np.max(np.abs(t["P"][j + 1] - S_last)) <= 1e-14
+        S_first = _update(o, np.zeros((3, 5)), x["k"][lo], x["v"][lo], x["beta"][lo])
+        assert np.max(np.abs(t["R"][j] - S_first)) <= 1e-14
+
+
+def pin_decay_scalar(o):
+    """d_k = d_v = 1, chunk 1, radius 1, exact rational arithmetic: each frame maps
+    s -> (alpha s + b) / (1 + a); the forward and reverse scans and the bridged
+    states follow by hand from that rule (Fractions, no numpy)."""
+    Fr = Fraction
+    v = [Fr(1), Fr(-2), Fr(3), Fr(1, 2), Fr(-1)]
+    beta = [Fr(1, 2), Fr(1), Fr(1, 4), Fr(2), Fr(1, 3)]
+    alpha = [Fr(1, 2), Fr(3, 4), Fr(1), Fr(1, 5), Fr(2, 3)]
+    tv, tb = Fr(2), Fr(1)
+    F = len(v)
+    seed = tb * tv / (1 + tb) / 2
+    step = lambda s, f: (alpha[f] * s + beta[f] * v[f]) / (1 + beta[f])  # noqa: E731
+    P = [seed]
+    for f in range(F):
+        P.append(step(P[-1], f))
+    R = [None] * (F + 1)
+    R[F] = seed
+    for f in range(F - 1, -1, -1):
+        R[f] = step(R[f + 1], f)
+
+    def prod(a, b):
+        out = Fr(1)
+        for g in range(a, b + 1):
+            out *= alpha[g]
+        return out
+    St = []
+    for f in range(F):
+        lo, hi = max(f - 1, 0), min(f + 1, F - 1)
+        St.append(P[lo] * prod(lo, f) + R[hi + 1] * prod(f, hi))
+    k = np.ones((F, 1, 1))
+    q = np.ones((F, 1, 1))
+    _, t = o.forward_unit(q, k, np.array([float(x) for x in v]).reshape(F, 1, 1),
+                          np.array([float(x) for x in beta]).reshape(F, 1), np.zeros((F, 1, 1)),
+                          np.ones((1, 1)), np.array([[float(tv)]]), np.array([float(tb)]),
+                          np.ones(1), chunk=1, radius=1, taps=True,
+                          alpha=np.array([float(x) for x in alpha]).reshape(F, 1))
+    assert np.max(np.abs(t["P"].ravel() - np.array([float(x) for x in P]))) <= 1e-15
+    assert np.max(np.abs(t["R"].ravel() - np.array([float(x) for x in R]))) <= 1e-15
+    assert np.max(np.abs(t["St"].ravel() - np.array([float(x) for x in St]))) <= 1e-15
+
+
+def pin_decay_non_expansive(o):
+    """Prop. 1 / App. A.1 with decay: ||Diag(alpha)(I + A)^{-1}||_2 <= 1 for
+    alpha in [0, 1] (also for lambda_max(A) > 2), and the difference of two
+    entering states never grows through a decayed frame sequence."""
+    rng = _rng(35)
+    for scale in (0.1, 1.0, 30.0):
+        for _ in range(4):
+            K = rng.standard_normal((12, 6))
+            A, _ = o.frame_statistics(K, np.zeros((12, 1)), scale * rng.uniform(0, 1, 12))
+            M = o.transition(A, rng.uniform(0, 1, 6))
+            assert np.linalg.norm(M, 2) <= 1.0 + 1e-12
+    S1, S2 = rng.standard_normal((2, 4, 6))
+    d0 = np.linalg.norm(S1 - S2)
+    for _ in range(8):
+        _, K, V, beta = _frame(rng, U=10, dk=6, dv=4)
+        alpha = rng.uniform(0, 1, 6)
+        A, B = o.frame_statistics(K, V, beta)
+        S1 = o.frame_update(o.decay(S1, alpha), A, B)
+        S2 = o.frame_update(o.decay(S2, alpha), A, B)
+        d1 = np.linalg.norm(S1 - S2)
+        assert d1 <= d0 * (1 + 1e-12)
+        d0 = d1
+
+
+def pin_decay_time_reversal(o):
+    """The two scans stay mirror images with decay: reversing the frame order (and
+    the gates with it; F a multiple of C) maps the output of frame f to frame
+    F-1-f, which holds only if each direction decays with the gate of the frame it
+    enters and the bridge products are taken symmetrically."""
+    rng = _rng(36)
+    for C, r, F in ((5, 1, 20), (2, 1, 8), (3, 2, 15), (1, 1, 6)):
+        x = _random_unit(rng, F, 4, 5, 3, 3)
+        alpha = _random_alpha(rng, F, 5)
+        out = _call(o, x, chunk=C, radius=r, alpha=alpha)
+        xr = dict(x)
+        for key in ("q", "k", "v", "beta", "gate"):
+            xr[key] = x[key][::-1].copy()
+        out_r = _call(o, xr, chunk=C, radius=r, alpha=alpha[::-1].copy())
+        assert np.max(np.abs(out_r[::-1] - out)) <= 1e-12, (C, r, F)
+
+
+def pin_decay_chunk_composition(o):
+    """With decay each frame is the affine map S -> S Diag(alpha) (I+A)^{-1} + J;
+    composing per chunk in each direction reproduces both scans, and the reverse
+    chunk transition is no longer the transpose of the forward one."""
+    rng = _rng(37)
+    F, C, U, dk, dv = 13, 5, 6, 5, 4
+    x = _random_unit(rng, F, U, dk, dv, 3)
+    alpha = _random_alpha(rng, F, dk)
+    _, tap = _call(o, x, chunk=C, radius=1, taps=True, alpha=alpha)
+    n = -(-F // C)
+    I = np.eye(dk)
+    Ms = [np.diag(alpha[f]) @ np.linalg.inv(I + tap["A"][f]) for f in range(F)]
+    Js = [tap["B"][f] @ np.linalg.inv(I + tap["A"][f]) for f in range(F)]
+    assert np.max(np.abs(np.array(Ms) - tap["M"])) <= 1e-12
+    P = [tap["P"][0]]
+    R = [None] * (n + 1)
+    R[n] = tap["R"][n]
+    maps = []
+    asym = 0.0
+    for lo, hi in [(s, min(s + C, F)) for s in range(0, F, C)]:
+        Mf, Jf = I.copy(), np.zeros((dv, dk))
+        for f in range(lo, hi):
+            Mf, Jf = Mf @ Ms[f], Jf @ Ms[f] + Js[f]
+        Mr, Jr = I.copy(), np.zeros((dv, dk))
+        for f in range(hi - 1, lo - 1, -1):
+            Mr, Jr = Mr @ Ms[f], Jr @ Ms[f] + Js[f]
+        asym = max(asym, np.max(np.abs(Mr - Mf.T)))
+        maps.append((Mf, Jf, Mr, Jr))
+    for j in range(n):
+        P.append(P[j] @ maps[j][0] + maps[j][1])
+    for j in range(n - 1, -1, -1):
+        R[j] = R[j + 1] @ maps[j][2] + maps[j][3]
+    assert np.max(np.abs(np.array(P) - tap["P"])) <= 1e-12
+    assert np.max(np.abs(np.array(R) - tap["R"])) <= 1e-12
+    assert asym > 1e-3
+
+
 ALL_PINS = [
     pin_stats_hand_loop, pin_stats_invariants, pin_gradient_zero, pin_lstsq_bruteforce,
     pin_sherman_morrison, pin_repeated_keys, pin_orthonormal_keys, pin_beta_zero,
     pin_non_expansive, pin_scalar_case, pin_orthonormal_golden, pin_exactly_once,
     pin_time_reversal, pin_disjointness, pin_forward_reverse_regions, pin_chunk_composition,
     pin_golden_scan, pin_token_permutation, pin_all_beta_zero, pin_rmsnorm_gate,
+    pin_decay_update, pin_decay_one, pin_decay_pure_bridge, pin_decay_zero, pin_decay_scalar,
+    pin_decay_non_expansive, pin_decay_time_reversal, pin_decay_chunk_composition,
 ]

@@ -121,36 +121,48 @@ def _gather_swapped(m):
 def _reverse_scan_store_late(m):
     orig = m.directional_states
 
-    def directional_states(stats, seed, C):
-        P, R = orig(stats, seed, C)
+    def directional_states(stats, seed, C, alpha=None):
+        P, R = orig(stats, seed, C, alpha)
         R2 = R.copy()
         R2[:-1] = R[1:]   # R[j] := state after chunk j+1
         return P, R2
     m.directional_states = directional_states
 
 
-def _forward_scan_skips_last_frame(m):
-    def directional_states(stats, seed, C):
+def _scan_variant(m, fwd_frames=None, rev_gate=None, decay_fwd=True, decay_after=False):
+    """directional_states with one planted slip (the arguments select it)."""
+    def directional_states(stats, seed, C, alpha=None):
         F = len(stats)
         bounds = m.chunk_bounds(F, C)
         n = len(bounds)
         P = np.zeros((n + 1,) + seed.shape)
         R = np.zeros((n + 1,) + seed.shape)
+
+        def enter(S, f, gate, use_decay=True):
+            if alpha is None or not use_decay:
+                return m.frame_update(S, *stats[f])
+            if decay_after:
+                return m.decay(m.frame_update(S, *stats[f]), alpha[gate])
+            return m.frame_update(m.decay(S, alpha[gate]), *stats[f])
         S = seed.copy()
         P[0] = S
         for j, (lo, hi) in enumerate(bounds):
-            for f in range(lo, hi - 1):
-                S = m.frame_update(S, *stats[f])
+            for f in (fwd_frames(lo, hi) if fwd_frames else range(lo, hi)):
+                S = enter(S, f, f, decay_fwd)
             P[j + 1] = S
         S = seed.copy()
         R[n] = S
         for j in range(n - 1, -1, -1):
             lo, hi = bounds[j]
             for f in range(hi - 1, lo - 1, -1):
-                S = m.frame_update(S, *stats[f])
+                S = enter(S, f, rev_gate(f, F) if rev_gate else f)
             R[j] = S
         return P, R
     m.directional_states = directional_states
+
+
+def _forward_scan_skips_last_frame(m):
+    _scan_variant(m, fwd_frames=lambda lo, hi: range(lo, hi - 1))
 
 
 def _rms_sum_not_mean(m):
@@ -181,7 +193,64 @@ def _readout_transposed(m):
 
 
 def _transition_wrong(m):
-    m.transition = lambda A: np.eye(A.shape[0]) - A
+    m.transition = lambda A, alpha=None: np.eye(A.shape[0]) - A
+
+
+# ---- decay (NEXT-1)
+def _decay_after_solve(m):
+    _scan_variant(m, decay_after=True)
+
+
+def _reverse_uses_next_gate(m):
+    _scan_variant(m, rev_gate=lambda f, F: min(f + 1, F - 1))
+
+
+def _forward_ignores_decay(m):
+    _scan_variant(m, decay_fwd=False)
+
+
+def _decay_on_rows(m):
+    def decay(S, alpha):
+        S = np.asarray(S, float)
+        a = np.asarray(alpha, float)
+        return a[:S.shape[0], None] * S if S.shape[0] <= a.shape[0] else S * a[None, :]
+    m.decay = decay
+
+
+def _bridge_variant(m, lo_shift=0, hi_shift=0, swap=False, none=False):
+    def bridge(P, R, f, C, radius, alpha):
+        alpha = np.asarray(alpha, float)
+        F = alpha.shape[0]
+        n = P.shape[0] - 1
+        c = f // C
+        lo, hi = m.window_frames(c, C, radius, F)
+        if none:
+            return m.gather(P, R, c, radius)
+        d_f = np.prod(alpha[lo:f + 1 + lo_shift], axis=0)
+        d_r = np.prod(alpha[f + hi_shift:hi + 1], axis=0)
+        if swap:
+            d_f, d_r = d_r, d_f
+        return m.decay(P[max(c - radius, 0)], d_f) + m.decay(R[min(c + radius + 1, n)], d_r)
+    m.bridge = bridge
+
+
+def _bridge_excludes_query_frame(m):
+    _bridge_variant(m, lo_shift=-1, hi_shift=1)
+
+
+def _bridge_omitted(m):
+    _bridge_variant(m, none=True)
+
+
+def _bridge_products_swapped(m):
+    _bridge_variant(m, swap=True)
+
+
+def _transition_decay_right(m):
+    def transition(A, alpha=None):
+        M = np.linalg.inv(np.eye(A.shape[0]) + A)
+        return M if alpha is None else M * np.asarray(alpha, float)[None, :]
+    m.transition = transition
 
 
 MUTATIONS = {f.__name__.lstrip("_"): f for f in [
@@ -189,7 +258,9 @@ MUTATIONS = {f.__name__.lstrip("_"): f for f in [
     _update_drops_inherited, _update_frozen_state, _update_left_multiplied, _seed_not_halved,
     _gather_fwd_off_by_one, _gather_rev_off_by_one, _gather_swapped, _reverse_scan_store_late,
     _forward_scan_skips_last_frame, _rms_sum_not_mean, _rms_wrong_axis, _sigmoid_sign,
-    _readout_transposed, _transition_wrong,
+    _readout_transposed, _transition_wrong, _decay_after_solve, _reverse_uses_next_gate,
+    _forward_ignores_decay, _decay_on_rows, _bridge_excludes_query_frame, _bridge_omitted,
+    _bridge_products_swapped, _transition_decay_right,
 ]}
 
 
