@@ -25,8 +25,9 @@ VDA_DTYPE_F32 = 0
 VDA_DTYPE_BF16 = 1
 
 EXPORTED = ("vda_workspace_bytes", "vda_check_desc", "vda_forward", "vda_forward_timed",
-            "vda_debug_stats",
-            "vda_debug_solve", "vda_debug_chunks", "vda_debug_states", "vda_status_string")
+            "vda_forward_decay", "vda_debug_stats", "vda_debug_solve", "vda_debug_chunks",
+            "vda_debug_chunks_decay", "vda_debug_states", "vda_debug_states_decay",
+            "vda_status_string")
 
 
 class VdaDesc(ctypes.Structure):
@@ -76,6 +77,12 @@ def load_library(path: str = LIB_PATH):
     lib.vda_forward_timed.argtypes = [D] + [P] * 11 + [ctypes.c_size_t, P,
                                                       ctypes.POINTER(ctypes.c_void_p), ctypes.c_int]
     lib.vda_forward_timed.restype = ctypes.c_int
+    lib.vda_forward_decay.argtypes = [D] + [P] * 12 + [ctypes.c_size_t, P]
+    lib.vda_forward_decay.restype = ctypes.c_int
+    lib.vda_debug_chunks_decay.argtypes = [D] + [P] * 12 + [ctypes.c_size_t, P]
+    lib.vda_debug_chunks_decay.restype = ctypes.c_int
+    lib.vda_debug_states_decay.argtypes = [D] + [P] * 10 + [ctypes.c_size_t, P]
+    lib.vda_debug_states_decay.restype = ctypes.c_int
     lib.vda_debug_stats.argtypes = [D] + [P] * 9 + [ctypes.c_size_t, P]
     lib.vda_debug_stats.restype = ctypes.c_int
     lib.vda_debug_solve.argtypes = [D] + [P] * 9 + [ctypes.c_size_t, P]
@@ -154,6 +161,17 @@ def vda_forward_timed(desc, q, k, v, beta, gate, text_k, text_v, text_beta, rms_
     _check(st, "vda_forward_timed")
 
 
+def vda_forward_decay(desc, q, k, v, beta, alpha, gate, text_k, text_v, text_beta, rms_weight,
+                      out, workspace, workspace_bytes=None, stream=None):
+    """C vda_forward_decay: vda_forward with channel-wise decay gates alpha
+    [units, F, d_k] (float32)."""
+    st = load_library().vda_forward_decay(
+        ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(alpha), _ptr(gate),
+        _ptr(text_k), _ptr(text_v), _ptr(text_beta), _ptr(rms_weight), _ptr(out),
+        _ptr(workspace), _ws_bytes(workspace, workspace_bytes), _stream(stream))
+    _check(st, "vda_forward_decay")
+
+
 def _ws_bytes(workspace, workspace_bytes):
     if workspace_bytes is not None:
         return workspace_bytes
@@ -196,6 +214,24 @@ def vda_debug_states(desc, k, v, beta, text_k, text_v, text_beta, P_out, R_out, 
     _check(st, "vda_debug_states")
 
 
+def vda_debug_chunks_decay(desc, k, v, beta, alpha, text_k, text_v, text_beta, Mc_out, Mr_t_out,
+                           Jf_out, Jr_out, workspace, workspace_bytes=None, stream=None):
+    st = load_library().vda_debug_chunks_decay(
+        ctypes.byref(desc), _ptr(k), _ptr(v), _ptr(beta), _ptr(alpha), _ptr(text_k),
+        _ptr(text_v), _ptr(text_beta), _ptr(Mc_out), _ptr(Mr_t_out), _ptr(Jf_out), _ptr(Jr_out),
+        _ptr(workspace), _ws_bytes(workspace, workspace_bytes), _stream(stream))
+    _check(st, "vda_debug_chunks_decay")
+
+
+def vda_debug_states_decay(desc, k, v, beta, alpha, text_k, text_v, text_beta, P_out, R_out,
+                           workspace, workspace_bytes=None, stream=None):
+    st = load_library().vda_debug_states_decay(
+        ctypes.byref(desc), _ptr(k), _ptr(v), _ptr(beta), _ptr(alpha), _ptr(text_k),
+        _ptr(text_v), _ptr(text_beta), _ptr(P_out), _ptr(R_out), _ptr(workspace),
+        _ws_bytes(workspace, workspace_bytes), _stream(stream))
+    _check(st, "vda_debug_states_decay")
+
+
 # ----------------------------------------------------------------------------- torch helpers
 def desc_from_tensors(q, k, v, text_k, chunk=5, radius=1, eps=1e-6, seed_mode=0) -> VdaDesc:
     """Descriptor from tensor shapes: q/k [units, F, U, d_k], v [units, F, U, d_v],
@@ -223,13 +259,14 @@ def _check_tensor(name, x, dtype, shape):
 
 
 def forward(q, k, v, beta, gate, text_k, text_v, text_beta, rms_weight, chunk=5, radius=1,
-            eps=1e-6, seed_mode=0, out=None, workspace=None, stream=None):
+            eps=1e-6, seed_mode=0, out=None, workspace=None, stream=None, alpha=None):
     """VDA forward on torch GPU tensors; allocates `out` and the workspace when absent.
 
     Shapes: q, k [units, F, U, d_k]; v, gate [units, F, U, d_v]; beta [units, F, U]
     (float32); text_k [units, T, d_k]; text_v [units, T, d_v]; text_beta
-    [units, T] (float32); rms_weight [d_v] (float32).  Returns out
-    [units, F, U, d_v] in the features' dtype.
+    [units, T] (float32); rms_weight [d_v] (float32); alpha (optional decay
+    gates) [units, F, d_k] (float32).  Returns out [units, F, U, d_v] in the
+    features' dtype.
     """
     import torch
     desc = desc_from_tensors(q, k, v, text_k, chunk, radius, eps, seed_mode)
@@ -244,11 +281,17 @@ def forward(q, k, v, beta, gate, text_k, text_v, text_beta, rms_weight, chunk=5,
     _check_tensor("beta", beta, torch.float32, (units, F, U))
     _check_tensor("text_beta", text_beta, torch.float32, (units, T))
     _check_tensor("rms_weight", rms_weight, torch.float32, (dv,))
+    if alpha is not None:
+        _check_tensor("alpha", alpha, torch.float32, (units, F, dk))
     if out is None:
         out = torch.empty((units, F, U, dv), dtype=fdt, device=k.device)
     nbytes = vda_workspace_bytes(desc)
     if workspace is None:
         workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=k.device)
-    vda_forward(desc, q, k, v, beta, gate, text_k, text_v, text_beta, rms_weight, out,
-                workspace, stream=stream)
+    if alpha is None:
+        vda_forward(desc, q, k, v, beta, gate, text_k, text_v, text_beta, rms_weight, out,
+                    workspace, stream=stream)
+    else:
+        vda_forward_decay(desc, q, k, v, beta, alpha, gate, text_k, text_v, text_beta,
+                          rms_weight, out, workspace, stream=stream)
     return out

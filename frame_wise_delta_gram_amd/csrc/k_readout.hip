@@ -27,6 +27,15 @@
 // from LDS feeds two 16-token groups.  Math in the epilogue is fp32; the
 // output is rounded to bf16 (nearest even).
 //
+// With channel-wise decay (App. A.3 Eq. (A.4) with alpha_t in [0, 1]^{d_k}) the
+// gathered state depends on the frame: frame f of chunk c reads
+//   S~_f = P[max(c - r, 0)] Diag(prod_{s=l}^{f} alpha_s)
+//        + R[min(c + r + 1, n)] Diag(prod_{s=f}^{h} alpha_s),
+// [l, h] = the window's frames C max(c - r, 0) .. min(C (c + r + 1), F) - 1.
+// The work is then split by frame instead of by chunk (a segment is one frame),
+// the two channel-wise products are formed in LDS by the workgroup before the
+// gather, and the gather scales P's and R's columns by them.
+//
 // fp32 path: the same computation on the vector ALUs in fp32.
 #include "vda_device.h"
 #include "vda_internal.h"
@@ -38,28 +47,60 @@ constexpr int kThreadsR = 512;            // 8 waves; two workgroups per CU
 constexpr int kGroups = 8;                // 16-row groups per wave
 constexpr int kRows = 8 * 16 * kGroups;   // token rows per workgroup
 
+// Channel-wise decay products of the bridge for frame f of chunk c, by threads
+// 0 .. 255 of the workgroup: D[k] = prod_{s=l}^{f} alpha_s[k] (applied to P's
+// column k), D[128 + k] = prod_{s=f}^{h} alpha_s[k] (R's); zero past d_k.  The
+// gates are read eight frames at a time (independent loads).
+__device__ __forceinline__ void bridge_products(float* D, const float* alpha, int u, int f, int c,
+                                                int F, int C, int radius, int dk) {
+  const int t = threadIdx.x;
+  if (t >= 256) return;
+  const int k = t & 127;
+  const bool rev = t >= 128;
+  const long l = (long)C * max(c - radius, 0);
+  const long hw = (long)C * (c + radius + 1);
+  const int s0 = rev ? f : (int)l;
+  const int s1 = rev ? (int)(hw < F ? hw : F) - 1 : f;
+  float d = 1.0f;
+  if (k < dk) {
+    const float* a = alpha + (size_t)u * F * dk + k;
+    for (int s = s0; s <= s1; s += 8) {
+      float x[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) x[i] = s + i <= s1 ? a[(size_t)(s + i) * dk] : 1.0f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) d *= x[i];
+    }
+  }
+  D[t] = k < dk ? d : 0.0f;
+}
+
 // DK, DV > 0: compile-time d_k and d_v (the common 128 case); 0: runtime.
-template <int DK, int DV>
+// DECAY: one segment per frame, bridged gather (see header); else one segment
+// per chunk.
+template <int DK, int DV, bool DECAY>
 __global__ __launch_bounds__(512, 4) void readout_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ gate,
     const float* __restrict__ wrms, uint16_t* __restrict__ out, const float* __restrict__ ST,
-    int dk_rt, int dv_rt, int F, int U, int C, int radius, int n, float eps, int units, int nblk,
-    unsigned per) {
+    const float* __restrict__ alpha, int dk_rt, int dv_rt, int F, int U, int C, int radius, int n,
+    float eps, int units, int nseg, int nblk, unsigned per) {
   const int dk = DK > 0 ? DK : dk_rt;
   const int dv = DV > 0 ? DV : dv_rt;
   __shared__ __align__(16) uint16_t Shi[128 * 136];
   __shared__ __align__(16) uint16_t Slo[128 * 136];
   __shared__ __align__(16) float Ws[128];  // RMSNorm weight (LDS: its reads use lgkmcnt, not vmcnt)
+  __shared__ __align__(16) float Dbr[DECAY ? 256 : 1];  // bridge products (P: 0.., R: 128..)
 
-  // work item = (unit, chunk, row block), row block fastest: the blocks of one
-  // chunk (which all read the same two states) share an XCD
+  // work item = (unit, segment, row block), row block fastest: the blocks of
+  // one segment (which all read the same two states) share an XCD
   const unsigned item = xcd_item(per);
-  if (item >= (unsigned)units * n * nblk) return;
+  if (item >= (unsigned)units * nseg * nblk) return;
   const int blk = item % nblk;
-  const int c = (item / nblk) % n;
-  const int u = item / (nblk * n);
-  const int f0 = c * C;
-  const int f1 = min(f0 + C, F);
+  const int seg = (item / nblk) % nseg;
+  const int u = item / (nblk * nseg);
+  const int c = DECAY ? seg / C : seg;
+  const int f0 = DECAY ? seg : c * C;
+  const int f1 = DECAY ? seg + 1 : min(f0 + C, F);
   const long rows_total = (long)(f1 - f0) * U;
   const long row0 = (long)blk * kRows;
   if (row0 >= rows_total) return;
@@ -74,6 +115,10 @@ __global__ __launch_bounds__(512, 4) void readout_bf16_kernel(
   const int SROW = 136;        // LDS row stride (bf16 elements): 17 x 16 bytes
 
   if (t < 128) Ws[t] = t < dv ? wrms[t] : 0.0f;
+  if (DECAY) {
+    bridge_products(Dbr, alpha, u, f0, c, F, C, radius, dk);
+    __syncthreads();
+  }
   // gather S~ and split it into bf16 hi + lo, rows permuted (see header);
   // padding rows and columns are zero
   {
@@ -111,10 +156,24 @@ __global__ __launch_bounds__(512, 4) void readout_bf16_kernel(
         const int T = 2 * (ch >> 5) + ((ch >> 2) & 1);
         const int lrow = 16 * T + 4 * ((ch >> 3) & 3) + (ch & 3);
         float x[8];
+        if (DECAY) {
+          f32x4_t df[2], dr[2];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          x[e] = pv[i][0][e] + rv[i][0][e];
-          x[4 + e] = pv[i][1][e] + rv[i][1][e];
+          for (int j = 0; j < 2; ++j) {
+            df[j] = *reinterpret_cast<const f32x4_t*>(Dbr + 8 * k8 + 4 * j);
+            dr[j] = *reinterpret_cast<const f32x4_t*>(Dbr + 128 + 8 * k8 + 4 * j);
+          }
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            x[e] = pv[i][0][e] * df[0][e] + rv[i][0][e] * dr[0][e];
+            x[4 + e] = pv[i][1][e] * df[1][e] + rv[i][1][e] * dr[1][e];
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            x[e] = pv[i][0][e] + rv[i][0][e];
+            x[4 + e] = pv[i][1][e] + rv[i][1][e];
+          }
         }
         u32x4_t hi, lo;
 #pragma unroll
@@ -231,20 +290,26 @@ __global__ __launch_bounds__(512, 4) void readout_bf16_kernel(
 }
 
 // fp32 features: 64 token rows per workgroup, S~ and the rows' queries in LDS.
+// Work item (unit, segment, row block) on a 1-D grid, segments as in the bf16
+// path (a frame with decay, given by alpha != nullptr; else a chunk).
 constexpr int SG = 129;
 constexpr int kRowsF = 64;
 
 __global__ __launch_bounds__(256) void readout_f32_kernel(
     const float* __restrict__ q, const float* __restrict__ gate, const float* __restrict__ wrms,
-    float* __restrict__ out, const float* __restrict__ ST, int dk, int dv, int F, int U, int C,
-    int radius, int n, float eps) {
+    float* __restrict__ out, const float* __restrict__ ST, const float* __restrict__ alpha, int dk,
+    int dv, int F, int U, int C, int radius, int n, float eps, int nseg, int nblk) {
   __shared__ float Ss[128 * SG];
   __shared__ float Qs[kRowsF * SG];
-  const int blk = blockIdx.x;
-  const int c = blockIdx.y;
-  const int u = blockIdx.z;
-  const int f0 = c * C;
-  const int f1 = min(f0 + C, F);
+  __shared__ float Dbr[256];
+  const bool decay = alpha != nullptr;
+  const unsigned item = blockIdx.x;
+  const int blk = item % nblk;
+  const int seg = (item / nblk) % nseg;
+  const int u = item / (nblk * nseg);
+  const int c = decay ? seg / C : seg;
+  const int f0 = decay ? seg : c * C;
+  const int f1 = decay ? seg + 1 : min(f0 + C, F);
   const long rows_total = (long)(f1 - f0) * U;
   const long row0 = (long)blk * kRowsF;
   if (row0 >= rows_total) return;
@@ -254,10 +319,14 @@ __global__ __launch_bounds__(256) void readout_f32_kernel(
   const int ri = min(c + radius + 1, n);
   const float* P = ST + ((size_t)(u * 2 + 0) * (n + 1) + pi) * SS;
   const float* R = ST + ((size_t)(u * 2 + 1) * (n + 1) + ri) * SS;
+  if (decay) {
+    bridge_products(Dbr, alpha, u, f0, c, F, C, radius, dk);
+    __syncthreads();
+  }
   for (int idx = t; idx < dv * dk; idx += 256) {
     const int i = idx / dk;
     const int j = idx - i * dk;
-    Ss[i * SG + j] = P[idx] + R[idx];
+    Ss[i * SG + j] = decay ? P[idx] * Dbr[j] + R[idx] * Dbr[128 + j] : P[idx] + R[idx];
   }
   const size_t chunk_row0 = ((size_t)u * F + f0) * U;
   for (int idx = t; idx < kRowsF * dk; idx += 256) {
@@ -299,25 +368,39 @@ __global__ __launch_bounds__(256) void readout_f32_kernel(
 
 }  // namespace
 
+template <int DK, int DV, bool DECAY>
+void launch_readout_bf16(const Plan& p, const void* q, const void* gate, const float* rms_weight,
+                         void* out, const WsPtrs& w, const float* alpha, int nseg, int nblk,
+                         hipStream_t s) {
+  const unsigned per = xcd_per((unsigned)p.units * nseg * nblk);
+  hipLaunchKernelGGL((readout_bf16_kernel<DK, DV, DECAY>), dim3(kXcds * per), dim3(kThreadsR), 0,
+                     s, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(gate),
+                     rms_weight, static_cast<uint16_t*>(out), w.ST, alpha, p.dk, p.dv, p.F, p.U,
+                     p.C, p.r, p.n, p.eps, p.units, nseg, nblk, per);
+}
+
 hipError_t launch_readout(const Plan& p, const void* q, const void* gate, const float* rms_weight,
-                          void* out, const WsPtrs& w, hipStream_t s) {
-  const long max_rows = (long)p.C * p.U;
-  if (max_rows == 0) return hipSuccess;
+                          void* out, const WsPtrs& w, const float* alpha, hipStream_t s) {
+  // segments: frames with decay (each frame reads its own bridged state), else chunks
+  const long max_rows = alpha ? (long)p.U : (long)p.C * p.U;
+  const int nseg = alpha ? p.F : p.n;
+  if (max_rows == 0 || nseg == 0 || p.units == 0) return hipSuccess;
   if (p.dtype == VDA_DTYPE_BF16) {
     const int nblk = (int)((max_rows + kRows - 1) / kRows);
-    const unsigned per = xcd_per((unsigned)p.units * p.n * nblk);
-    auto kern = (p.dk == 128 && p.dv == 128) ? readout_bf16_kernel<128, 128>
-                                             : readout_bf16_kernel<0, 0>;
-    hipLaunchKernelGGL(kern, dim3(kXcds * per), dim3(kThreadsR), 0, s,
-                       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(gate),
-                       rms_weight, static_cast<uint16_t*>(out), w.ST, p.dk, p.dv, p.F, p.U, p.C,
-                       p.r, p.n, p.eps, p.units, nblk, per);
+    const bool d128 = p.dk == 128 && p.dv == 128;
+    if (alpha)
+      d128 ? launch_readout_bf16<128, 128, true>(p, q, gate, rms_weight, out, w, alpha, nseg, nblk, s)
+           : launch_readout_bf16<0, 0, true>(p, q, gate, rms_weight, out, w, alpha, nseg, nblk, s);
+    else
+      d128 ? launch_readout_bf16<128, 128, false>(p, q, gate, rms_weight, out, w, alpha, nseg, nblk, s)
+           : launch_readout_bf16<0, 0, false>(p, q, gate, rms_weight, out, w, alpha, nseg, nblk, s);
   } else {
-    const dim3 grid((unsigned)((max_rows + kRowsF - 1) / kRowsF), p.n, p.units);
-    hipLaunchKernelGGL(readout_f32_kernel, grid, dim3(kThreads), 0, s,
+    const int nblk = (int)((max_rows + kRowsF - 1) / kRowsF);
+    const unsigned items = (unsigned)p.units * nseg * nblk;
+    hipLaunchKernelGGL(readout_f32_kernel, dim3(items), dim3(kThreads), 0, s,
                        static_cast<const float*>(q), static_cast<const float*>(gate), rms_weight,
-                       static_cast<float*>(out), w.ST, p.dk, p.dv, p.F, p.U, p.C, p.r, p.n,
-                       p.eps);
+                       static_cast<float*>(out), w.ST, alpha, p.dk, p.dv, p.F, p.U, p.C, p.r, p.n,
+                       p.eps, nseg, nblk);
   }
   return hipGetLastError();
 }

@@ -11,11 +11,18 @@
 //     Jr = (((B_{f1-1}) M_{f1-1} + B_{f1-2}) M_{f1-2} + ...) M_{f0}
 //   The reverse transition is M_{f1-1} ... M_{f0} = Mc^T because every M_t is
 //   symmetric (alpha = 1), so it is not stored.
+//   With channel-wise decay (App. A.1 Eq. (A.1) with alpha_t in [0, 1]^{d_k})
+//   a frame's map is S -> (S D_t + B_t) M_t, D_t = Diag(alpha_t), in both scan
+//   directions: Mc = D_{f0} M_{f0} ... D_{f1-1} M_{f1-1}, each J picks up the
+//   gate of every frame it enters, and the reverse transition
+//   Mr = D_{f1-1} M_{f1-1} ... D_{f0} M_{f0} is a chain of its own, stored
+//   transposed (MrT).
 //
 //   scan: per (unit, direction, 32-row block of the state) -- the rows of S
 //   evolve independently --
 //     P[0] = seed, P[j+1] = P[j] Mc_j + Jf_j          (forward, chunks 0..n-1)
-//     R[n] = seed, R[j]   = R[j+1] Mc_j^T + Jr_j      (reverse, chunks n-1..0)
+//     R[n] = seed, R[j]   = R[j+1] Mc_j^T + Jr_j      (reverse, chunks n-1..0;
+//                                                      Mr_j in place of Mc_j^T with decay)
 //   Only these n + 1 boundary states per direction are ever written.
 //
 // The state and every map stay fp32 in memory ("the inverse and recurrent
@@ -51,8 +58,10 @@ __device__ __forceinline__ void tile_prefetch(float (&dst)[16], const float* src
 
 __global__ __launch_bounds__(256, 1) void compose_kernel(const float* __restrict__ Bw,
                                                         const float* __restrict__ Mw,
+                                                        const float* __restrict__ alpha,
                                                         float* __restrict__ Mc,
                                                         float* __restrict__ McT,
+                                                        float* __restrict__ MrT,
                                                         float* __restrict__ Jf,
                                                         float* __restrict__ Jr,
                                                         float* __restrict__ ST, int dk, int dv,
@@ -61,8 +70,11 @@ __global__ __launch_bounds__(256, 1) void compose_kernel(const float* __restrict
   __shared__ float Ms[128 * SG];
   const int c = blockIdx.x;
   const int u = blockIdx.y;
-  const int chain = blockIdx.z;  // 0: Mc, 1: Jf, 2: Jr, 3: text seed (one per unit)
+  // 0: Mc, 1: Jf, 2: Jr, 3: text seed (one per unit), 4: reverse transition (decay only)
+  const int chain = blockIdx.z;
   if (chain == 3 && c != 0) return;
+  const bool mchain = chain == 0 || chain == 4;    // transition chains
+  const bool reverse = chain == 2 || chain == 4;
   const int t = threadIdx.x;
   const int lane = t & 63;
   const int w = t >> 6;
@@ -70,30 +82,34 @@ __global__ __launch_bounds__(256, 1) void compose_kernel(const float* __restrict
   const int f0 = chain == 3 ? -1 : c * C;
   const int f1 = chain == 3 ? 0 : min(f0 + C, F);
   const int nf = f1 - f0;
-  const int rows = chain == 0 ? dk : dv;
+  const int rows = mchain ? dk : dv;
   const int R32 = pad32(rows);
   const int nR = R32 >> 5;
   const int Dk = pad32(dk);
   const int nb = Dk >> 5;
   const size_t Fp1 = (size_t)F + 1;
   // workspace frame index f + 1 holds latent frame f (index 0 is the text frame)
-  auto frame = [&](int s) { return chain == 2 ? f1 - 1 - s : f0 + s; };
+  auto frame = [&](int s) { return reverse ? f1 - 1 - s : f0 + s; };
   auto Mp = [&](int f) { return Mw + ((size_t)u * Fp1 + f + 1) * dk * dk; };
   auto Bp = [&](int f) { return Bw + ((size_t)u * Fp1 + f + 1) * dv * dk; };
+  // decay gate of latent frame f, key channel j (1 without decay)
+  auto gate = [&](int f, int j) {
+    return alpha && j < dk ? alpha[((size_t)u * F + f) * dk + j] : 1.0f;
+  };
 
   {
     MatRegs m;
-    if (chain != 0) {
+    if (!mchain) {
       mat_load(m, Bp(frame(0)), dk, dv, dk);
       if (chain == 3)
 #pragma unroll
         for (int i = 0; i < 16; ++i) m.v[i] *= seed_scale;
       mat_store_lds(m, Xs, SG, R32, Dk);
-    } else {
+    } else {  // the decayed identity Diag(alpha) of the first frame
       for (int idx = t; idx < R32 * Dk; idx += 256) {
         const int i = idx / Dk;
         const int j = idx - i * Dk;
-        Xs[i * SG + j] = (i == j) ? 1.0f : 0.0f;
+        Xs[i * SG + j] = (i == j) ? gate(frame(0), i) : 0.0f;
       }
     }
     mat_load(m, Mp(frame(0)), dk, dk, dk);
@@ -104,6 +120,7 @@ __global__ __launch_bounds__(256, 1) void compose_kernel(const float* __restrict
   const size_t SS = (size_t)dv * dk;
   float* dst = chain == 0 ? Mc + ((size_t)u * n + c) * dk * dk
                : chain == 3 ? ST + (size_t)u * 2 * (n + 1) * SS                  // P[0]
+               : chain == 4 ? nullptr                                            // MrT only
                             : (chain == 1 ? Jf : Jr) + ((size_t)u * n + c) * SS;
   float* dst2 = ST + ((size_t)(u * 2 + 1) * (n + 1) + n) * SS;                 // R[n]
   MatRegs mnext;
@@ -114,7 +131,7 @@ __global__ __launch_bounds__(256, 1) void compose_kernel(const float* __restrict
       mat_load(mnext, Mp(frame(s + 1)), dk, dk, dk);
 #pragma unroll
       for (int ct = 0; ct < 4; ++ct) {
-        if (chain != 0 && w < nR && ct < nb)
+        if (!mchain && w < nR && ct < nb)
           tile_prefetch(bnext[ct], Bp(frame(s + 1)), dk, dv, 32 * w, 32 * ct);
         else
 #pragma unroll
@@ -139,17 +156,24 @@ __global__ __launch_bounds__(256, 1) void compose_kernel(const float* __restrict
       for (int ct = 0; ct < 4; ++ct) {
         if (ct >= nb) continue;
         const int col = 32 * ct + (lane & 31);
+        // entering the next frame: the state is decayed by its gate, then written
+        const float a = last ? 1.0f : gate(frame(s + 1), col);
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int row = 32 * w + acc_row(r, lane);
           if (last) {
             if (row < rows && col < dk) {
-              dst[(size_t)row * dk + col] = acc[ct][r];
-              if (chain == 0) McT[((size_t)u * n + c) * dk * dk + (size_t)col * dk + row] = acc[ct][r];
-              if (chain == 3) dst2[(size_t)row * dk + col] = acc[ct][r];
+              const size_t tix = ((size_t)u * n + c) * dk * dk + (size_t)col * dk + row;
+              if (chain == 4) {
+                MrT[tix] = acc[ct][r];
+              } else {
+                dst[(size_t)row * dk + col] = acc[ct][r];
+                if (chain == 0) McT[tix] = acc[ct][r];
+                if (chain == 3) dst2[(size_t)row * dk + col] = acc[ct][r];
+              }
             }
           } else {
-            Xs[row * SG + col] = acc[ct][r] + bnext[ct][r];
+            Xs[row * SG + col] = acc[ct][r] * a + bnext[ct][r];
           }
         }
       }
@@ -160,7 +184,9 @@ __global__ __launch_bounds__(256, 1) void compose_kernel(const float* __restrict
   }
 }
 
+// Mrt: the transposed reverse transition, Mc itself without decay
 __global__ __launch_bounds__(256) void scan_kernel(const float* __restrict__ Mc,
+                                                   const float* __restrict__ Mrt,
                                                    const float* __restrict__ Jf,
                                                    const float* __restrict__ Jr,
                                                    float* __restrict__ ST, int dk, int dv, int n) {
@@ -180,11 +206,12 @@ __global__ __launch_bounds__(256) void scan_kernel(const float* __restrict__ Mc,
   const int nrows = min(32, dv - r0);
   auto chunk = [&](int s) { return dir == 0 ? s : n - 1 - s; };
   const float* Jb = (dir == 0 ? Jf : Jr) + (size_t)u * n * SS;
+  const float* Mb = dir == 0 ? Mc : Mrt;
 
   MatRegs m;
   mat_load(m, S + (size_t)(dir == 0 ? 0 : n) * SS + (size_t)r0 * dk, dk, nrows, dk);
   mat_store_lds(m, Xs, SG, 32, Dk);
-  mat_load(m, Mc + ((size_t)u * n + chunk(0)) * dk * dk, dk, dk, dk);
+  mat_load(m, Mb + ((size_t)u * n + chunk(0)) * dk * dk, dk, dk, dk);
   mat_store_lds(m, Ms, SG, Dk, Dk);
   float jreg[16];
   if (w < nb) tile_prefetch(jreg, Jb + (size_t)chunk(0) * SS + (size_t)r0 * dk, dk, nrows, 0, 32 * w);
@@ -194,7 +221,7 @@ __global__ __launch_bounds__(256) void scan_kernel(const float* __restrict__ Mc,
     const bool last = s == n - 1;
     float jnext[16];
     if (!last) {
-      mat_load(m, Mc + ((size_t)u * n + chunk(s + 1)) * dk * dk, dk, dk, dk);
+      mat_load(m, Mb + ((size_t)u * n + chunk(s + 1)) * dk * dk, dk, dk, dk);
       if (w < nb)
         tile_prefetch(jnext, Jb + (size_t)chunk(s + 1) * SS + (size_t)r0 * dk, dk, nrows, 0, 32 * w);
     }
@@ -353,10 +380,10 @@ __device__ __forceinline__ void x_store_quad(__bf16* xh, __bf16* xl, int row, in
 }
 
 // Row-major rows x d_k fp32 matrix (times scale) -> (hi, lo) LDS rows
-// [0, pad32(rows)), zero padded; rows == 0 gives the identity (d_k x d_k).
-// By the first 256 threads of the workgroup.
+// [0, pad32(rows)), zero padded; rows == 0 gives the identity (d_k x d_k), or
+// Diag(diag) when diag is given.  By the first 256 threads of the workgroup.
 __device__ __forceinline__ void x_fill(__bf16* xh, __bf16* xl, const float* src, int rows, int dk,
-                                       float scale) {
+                                       float scale, const float* diag = nullptr) {
   const int t = threadIdx.x;
   if (t >= 256) return;
   const int R = pad32(rows == 0 ? dk : rows);
@@ -370,7 +397,8 @@ __device__ __forceinline__ void x_fill(__bf16* xh, __bf16* xl, const float* src,
       const int r = id >> 5;
       const int c = (id & 31) << 2;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) m.v[i][e] = (r == c + e && r < dk) ? 1.0f : 0.0f;
+      for (int e = 0; e < 4; ++e)
+        m.v[i][e] = (r == c + e && r < dk) ? (diag ? diag[r] : 1.0f) : 0.0f;
     }
   }
 #pragma unroll
@@ -385,26 +413,33 @@ __device__ __forceinline__ void x_fill(__bf16* xh, __bf16* xl, const float* src,
 // compose (bf16): one workgroup of 8 waves per work item; wave w owns output
 // columns jr = 32 (w % 4) .. + 31 for X rows 64 (w / 4) .. + 63.  The two waves
 // of a column block load one half each (contiguous 256-byte half rows) of the
-// transition rows they share and stage them, split, in LDS.  Work items: (unit, chunk, chain) with the chain
-// fastest (the three chains of a chunk read the same transitions and share an
-// XCD), then one text-seed item per unit.
-template <bool FULL>
+// transition rows they share and stage them, split, in LDS.  Work items:
+// (unit, chunk, chain) with the chain fastest (the chains of a chunk read the
+// same transitions and share an XCD), then one text-seed item per unit.
+// Chains: 0 Mc, 1 Jf, 2 Jr and, with decay (DECAY), 3 the reverse transition
+// Mr = D_{f1-1} M_{f1-1} ... D_{f0} M_{f0}, which no longer equals Mc^T.  With
+// decay each step enters the next frame as X <- (X M) Diag(alpha_next) + B_next
+// and a transition chain starts from Diag(alpha) of its first frame.
+template <bool FULL, bool DECAY>
 __global__ __launch_bounds__(512, 1) void compose_split_kernel(
-    const float* __restrict__ Bw, const float* __restrict__ Mw, float* __restrict__ Mc,
-    float* __restrict__ McT, float* __restrict__ Jf, float* __restrict__ Jr,
-    float* __restrict__ ST, int dk, int dv, int F, int C, int n, int units, unsigned per,
-    float seed_scale) {
+    const float* __restrict__ Bw, const float* __restrict__ Mw, const float* __restrict__ alpha,
+    float* __restrict__ Mc, float* __restrict__ McT, float* __restrict__ MrT,
+    float* __restrict__ Jf, float* __restrict__ Jr, float* __restrict__ ST, int dk, int dv, int F,
+    int C, int n, int units, unsigned per, float seed_scale) {
   __shared__ __align__(16) __bf16 Xh[128 * SB];
   __shared__ __align__(16) __bf16 Xl[128 * SB];
   __shared__ __align__(16) __bf16 Mh[128 * SB];
   __shared__ __align__(16) __bf16 Ml[128 * SB];
+  constexpr unsigned nch = DECAY ? 4 : 3;
   const unsigned item = xcd_item(per);
-  const unsigned chain_items = (unsigned)units * n * 3;
+  const unsigned chain_items = (unsigned)units * n * nch;
   if (item >= chain_items + units) return;
   const bool seed = item >= chain_items;
-  const int chain = seed ? 3 : item % 3;  // 0: Mc, 1: Jf, 2: Jr, 3: seed
-  const int c = seed ? 0 : (item / 3) % n;
-  const int u = seed ? item - chain_items : item / (3 * n);
+  const int chain = seed ? 1 : item % nch;  // the seed runs as a forward B chain
+  const int c = seed ? 0 : (item / nch) % n;
+  const int u = seed ? item - chain_items : item / (nch * n);
+  const bool mchain = !seed && (chain == 0 || chain == 3);
+  const bool reverse = !seed && (chain == 2 || chain == 3);
   const int w = threadIdx.x >> 6;
   const int jr = 32 * (w & 3);
   const int kh = w >> 2;
@@ -414,34 +449,44 @@ __global__ __launch_bounds__(512, 1) void compose_split_kernel(
   const int f0 = seed ? -1 : c * C;
   const int f1 = seed ? 0 : min(f0 + C, F);
   const int nf = f1 - f0;
-  const int rows = chain == 0 ? dk : dv;
+  const int rows = mchain ? dk : dv;
   const size_t Fp1 = (size_t)F + 1;
   const size_t SS = (size_t)dv * dk;
   // workspace frame index f + 1 holds latent frame f (index 0 is the text frame)
-  auto frame = [&](int s) { return chain == 2 ? f1 - 1 - s : f0 + s; };
+  auto frame = [&](int s) { return reverse ? f1 - 1 - s : f0 + s; };
   auto Mp = [&](int f) { return Mw + ((size_t)u * Fp1 + f + 1) * dk * dk; };
   auto Bp = [&](int f) { return Bw + ((size_t)u * Fp1 + f + 1) * SS; };
+  auto Ap = [&](int f) { return alpha + ((size_t)u * F + f) * dk; };
   const bool active = jr < dk && xr0 < rows;
 
   RowsF32<8> mf;
   rows_load<8, 16>(mf, Mp(frame(0)), dk, jr, 64 * kh);
-  x_fill(Xh, Xl, chain == 0 ? nullptr : Bp(frame(0)), chain == 0 ? 0 : dv, dk,
-         seed ? seed_scale : 1.0f);
+  x_fill(Xh, Xl, mchain ? nullptr : Bp(frame(0)), mchain ? 0 : dv, dk, seed ? seed_scale : 1.0f,
+         DECAY && mchain ? Ap(frame(0)) : nullptr);
   rows_split<8, 16>(Mh, Ml, 0, mf, dk, jr, 64 * kh);
   __syncthreads();
 
-  float* dst = chain == 0 ? Mc + ((size_t)u * n + c) * dk * dk
-               : seed     ? ST + (size_t)u * 2 * (n + 1) * SS  // P[0]
-                          : (chain == 1 ? Jf : Jr) + ((size_t)u * n + c) * SS;
+  const size_t tile = ((size_t)u * n + c) * dk * dk;
+  float* dst = chain == 0 && !seed ? Mc + tile
+               : seed              ? ST + (size_t)u * 2 * (n + 1) * SS  // P[0]
+               : chain == 3        ? nullptr                            // MrT only
+                                   : (chain == 1 ? Jf : Jr) + ((size_t)u * n + c) * SS;
   float* dst2 = seed ? ST + ((size_t)(u * 2 + 1) * (n + 1) + n) * SS  // R[n]
-                     : McT + ((size_t)u * n + c) * dk * dk;
+                     : (chain == 3 ? MrT : McT) + tile;
   const int lane = threadIdx.x & 63;
   f32x4_t bq[2][4];
+  f32x4_t aq[4];
   for (int s = 0; s < nf; ++s) {
     const bool last = s == nf - 1;
     if (!last) {  // the next frame's transition and write fly while this step multiplies
       rows_load<8, 16>(mf, Mp(frame(s + 1)), dk, jr, 64 * kh);
-      if (chain != 0) rows_prefetch_t<2>(bq, Bp(frame(s + 1)), dv, dk, xr0, jr);
+      if (!mchain) rows_prefetch_t<2>(bq, Bp(frame(s + 1)), dv, dk, xr0, jr);
+      if (DECAY) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          aq[q] = *reinterpret_cast<const f32x4_t*>(
+              Ap(frame(s + 1)) + min(jr + 8 * q + 4 * (lane >> 5), dk - 4));
+      }
     }
     f32x16_t acc[2] = {zero16(), zero16()};
     if (active) split_mm_t_lds<2>(acc, Mh, Ml, jr, Xh, Xl, xr0, nk);
@@ -456,10 +501,11 @@ __global__ __launch_bounds__(512, 1) void compose_split_kernel(
             const int row = xr0 + 32 * x + (lane & 31);
             const int col = jr + 8 * q + 4 * (lane >> 5);
             const f32x4_t v = out_quad(acc, x, q);
-            *reinterpret_cast<f32x4_t*>(dst + (size_t)row * dk + col) = v;
+            if (!DECAY || chain != 3 || seed)
+              *reinterpret_cast<f32x4_t*>(dst + (size_t)row * dk + col) = v;
             if (seed) {
               *reinterpret_cast<f32x4_t*>(dst2 + (size_t)row * dk + col) = v;
-            } else if (chain == 0) {
+            } else if (mchain) {  // Mc^T, or Mr^T
 #pragma unroll
               for (int e = 0; e < 4; ++e) dst2[(size_t)(col + e) * dk + row] = v[e];
             }
@@ -473,7 +519,8 @@ __global__ __launch_bounds__(512, 1) void compose_split_kernel(
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           f32x4_t v = out_quad(acc, x, q);
-          if (chain != 0 && out_ok(rows, dk, xr0, x, jr, q)) v += bq[x][q];
+          if (DECAY) v *= aq[q];
+          if (!mchain && out_ok(rows, dk, xr0, x, jr, q)) v += bq[x][q];
           x_store_quad(Xh, Xl, xr0 + 32 * x + (lane & 31), jr + 8 * q + 4 * (lane >> 5), v);
         }
     }
@@ -561,37 +608,47 @@ __global__ __launch_bounds__(256) void scan_split_kernel(const float* __restrict
 
 }  // namespace
 
-hipError_t launch_compose(const Plan& p, const WsPtrs& w, hipStream_t s) {
+template <bool FULL, bool DECAY>
+void launch_compose_split(const Plan& p, const WsPtrs& w, const float* alpha, float seed_scale,
+                          hipStream_t s) {
+  const unsigned per = xcd_per((unsigned)p.units * (p.n * (DECAY ? 4 : 3) + 1));
+  hipLaunchKernelGGL((compose_split_kernel<FULL, DECAY>), dim3(kXcds * per), dim3(512), 0, s, w.B,
+                     w.M, alpha, w.Mc, w.McT, w.MrT, w.Jf, w.Jr, w.ST, p.dk, p.dv, p.F, p.C, p.n,
+                     p.units, per, seed_scale);
+}
+
+hipError_t launch_compose(const Plan& p, const WsPtrs& w, const float* alpha, hipStream_t s) {
   const float seed_scale = p.seed_mode == 1 ? 1.0f : 0.5f;
   if (p.dtype == VDA_DTYPE_BF16) {
-    const unsigned per = xcd_per((unsigned)p.units * (p.n * 3 + 1));
     if (p.dk == 128)
-      hipLaunchKernelGGL(compose_split_kernel<true>, dim3(kXcds * per), dim3(512), 0, s, w.B, w.M,
-                         w.Mc, w.McT, w.Jf, w.Jr, w.ST, p.dk, p.dv, p.F, p.C, p.n, p.units, per,
-                         seed_scale);
+      alpha ? launch_compose_split<true, true>(p, w, alpha, seed_scale, s)
+            : launch_compose_split<true, false>(p, w, alpha, seed_scale, s);
     else
-      hipLaunchKernelGGL(compose_split_kernel<false>, dim3(kXcds * per), dim3(512), 0, s, w.B,
-                         w.M, w.Mc, w.McT, w.Jf, w.Jr, w.ST, p.dk, p.dv, p.F, p.C, p.n, p.units,
-                         per, seed_scale);
+      alpha ? launch_compose_split<false, true>(p, w, alpha, seed_scale, s)
+            : launch_compose_split<false, false>(p, w, alpha, seed_scale, s);
   } else {
-    hipLaunchKernelGGL(compose_kernel, dim3(p.n, p.units, 4), dim3(kThreads), 0, s, w.B, w.M, w.Mc,
-                       w.McT, w.Jf, w.Jr, w.ST, p.dk, p.dv, p.F, p.C, p.n, seed_scale);
+    hipLaunchKernelGGL(compose_kernel, dim3(p.n, p.units, alpha ? 5 : 4), dim3(kThreads), 0, s,
+                       w.B, w.M, alpha, w.Mc, w.McT, w.MrT, w.Jf, w.Jr, w.ST, p.dk, p.dv, p.F, p.C,
+                       p.n, seed_scale);
   }
   return hipGetLastError();
 }
 
-hipError_t launch_scan(const Plan& p, const WsPtrs& w, hipStream_t s) {
+// The reverse step reads the rows of the reverse transition's transpose: Mc
+// itself without decay (Mr = Mc^T), the stored Mr^T with it.
+hipError_t launch_scan(const Plan& p, const WsPtrs& w, bool decay, hipStream_t s) {
   const dim3 grid(pad32(p.dv) >> 5, p.units, 2);
+  const float* rev = decay ? w.MrT : w.Mc;
   if (p.dtype == VDA_DTYPE_BF16) {
     if (p.dk == 128 && p.dv % 32 == 0)
-      hipLaunchKernelGGL(scan_split_kernel<true>, grid, dim3(kThreads), 0, s, w.Mc, w.McT, w.Jf,
+      hipLaunchKernelGGL(scan_split_kernel<true>, grid, dim3(kThreads), 0, s, rev, w.McT, w.Jf,
                          w.Jr, w.ST, p.dk, p.dv, p.n);
     else
-      hipLaunchKernelGGL(scan_split_kernel<false>, grid, dim3(kThreads), 0, s, w.Mc, w.McT, w.Jf,
+      hipLaunchKernelGGL(scan_split_kernel<false>, grid, dim3(kThreads), 0, s, rev, w.McT, w.Jf,
                          w.Jr, w.ST, p.dk, p.dv, p.n);
   } else {
-    hipLaunchKernelGGL(scan_kernel, grid, dim3(kThreads), 0, s, w.Mc, w.Jf, w.Jr, w.ST, p.dk, p.dv,
-                       p.n);
+    hipLaunchKernelGGL(scan_kernel, grid, dim3(kThreads), 0, s, w.Mc, rev, w.Jf, w.Jr, w.ST, p.dk,
+                       p.dv, p.n);
   }
   return hipGetLastError();
 }

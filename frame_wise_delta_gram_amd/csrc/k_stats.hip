@@ -12,7 +12,7 @@
 // after X is rounded to bf16, so I + A stays SPD with every eigenvalue >= 1
 // and ||(I + A)^{-1}||_2 <= 1 (Prop. 1) holds for the computed transition too.
 //
-// bf16 path: one workgroup (8 waves) per (unit, frame); wave w owns output
+// bf16 path, latent frames: a persistent kernel (below); wave w owns output
 // row tile w of [A; B].  Tokens stream in tiles of 128.  Each thread loads a
 // 4-token x 8-channel block of K and of V (16-byte coalesced loads: one wave
 // instruction covers four whole 256-byte rows), scales it by sqrt(beta) in fp32, rounds to bf16 and packs it in
@@ -25,6 +25,13 @@
 // stage channel by channel between the k-steps of the current tile's
 // products (vector ALU work overlapping the MFMAs), and the global loads of
 // the tile after that are in flight meanwhile (two register sets).
+//
+// bf16 path, text frame: fp32 on the vector ALUs (stats_text_kernel).  The
+// text state seeds both scans and, unlike a latent frame's thousands of
+// tokens, a handful of text tokens does not average out the bf16 rounding of
+// sqrt(beta) k: the seed is low-rank, its rounding errors are not, and a query
+// mostly orthogonal to the text keys reads the errors almost alone.  The text
+// frame is a small share of the work (T tokens per unit against F U).
 //
 // fp32 path: the same contraction in fp32 on the vector ALUs (exact fp32
 // products, fp32 accumulation) for fp32 features.
@@ -61,9 +68,9 @@ __device__ __forceinline__ uint32_t off16(uint32_t row, uint32_t j) {
 }
 
 // Persistent: one workgroup per CU (the 128 KiB of LDS allow no more) walks
-// the frames b, b + P, b + 2P, ... of the flattened (unit, frame) list, frame
-// g = u (F + 1) + fi with fi = 0 the text frame, as ONE continuous tile
-// stream: the first tiles of the next frame are in flight while the last tile
+// the frames b, b + P, b + 2P, ... of the flattened (unit, latent frame) list,
+// g = u F + f (stored at workspace frame u (F + 1) + f + 1), as ONE continuous
+// tile stream: the first tiles of the next frame are in flight while the last tile
 // of the current one is multiplied and its results are stored.
 // Raw buffer access (gfx9 descriptor: stride 0, range in bytes, dword 3 =
 // 0x00020000): loads at or past `bytes` return 0 without a memory access.
@@ -82,9 +89,8 @@ __device__ __forceinline__ float buf_load4(__amdgpu_buffer_rsrc_t r, int off) {
 template <int DK, int DV>
 __global__ __launch_bounds__(512, 1) void stats_bf16_kernel(
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, const float* __restrict__ beta,
-    const uint16_t* __restrict__ tk, const uint16_t* __restrict__ tv,
-    const float* __restrict__ tb, float* __restrict__ Aout, float* __restrict__ Bout, int F, int U,
-    int T, int dk_rt, int dv_rt, float text_scale, int nframes) {
+    float* __restrict__ Aout, float* __restrict__ Bout, int F, int U, int dk_rt, int dv_rt,
+    int nframes) {
   const int dk = DK > 0 ? DK : dk_rt;
   const int dv = DV > 0 ? DV : dv_rt;
   __shared__ __align__(16) unsigned char smem[2 * kStageBytes];
@@ -100,19 +106,9 @@ __global__ __launch_bounds__(512, 1) void stats_bf16_kernel(
     const uint16_t* v;
     const float* b;
     int ntok;
-    float bscale;
   };
   auto frame_src = [&](int g) {
-    FrameSrc f;
-    const int u = g / (F + 1);
-    const int fi = g - u * (F + 1);
-    if (fi == 0) {
-      f = {tk + (size_t)u * T * dk, tv + (size_t)u * T * dv, tb + (size_t)u * T, T, text_scale};
-    } else {
-      const size_t fr = (size_t)u * F + (fi - 1);
-      f = {k + fr * U * dk, v + fr * U * dv, beta + fr * U, U, 1.0f};
-    }
-    return f;
+    return FrameSrc{k + (size_t)g * U * dk, v + (size_t)g * U * dv, beta + (size_t)g * U, U};
   };
   auto ntiles_of = [&](int ntok) { return ntok > 0 ? (ntok + kTok - 1) / kTok : 1; };
   // tile cursor: frame g (>= nframes past this workgroup's last frame), tile i
@@ -165,11 +161,10 @@ __global__ __launch_bounds__(512, 1) void stats_bf16_kernel(
     }
   };
 
-  // sqrt(beta) of the thread's 4 tokens of tile c (beta reads 0 past the end)
-  auto sqrt_beta = [&](const TileRegs& r, Cur c, float (&sb4)[4]) {
-    const float bscale = frame_src(c.g < nframes ? c.g : b0).bscale;
+  // sqrt(beta) of the thread's 4 tokens of a tile (beta reads 0 past the end)
+  auto sqrt_beta = [&](const TileRegs& r, Cur, float (&sb4)[4]) {
 #pragma unroll
-    for (int s = 0; s < 4; ++s) sb4[s] = __builtin_amdgcn_sqrtf(r.b[s] * bscale);
+    for (int s = 0; s < 4; ++s) sb4[s] = __builtin_amdgcn_sqrtf(r.b[s]);
   };
 
   // channel c of the thread's 8-channel group, tokens 0..3: scale, round, pack
@@ -248,7 +243,8 @@ __global__ __launch_bounds__(512, 1) void stats_bf16_kernel(
       const bool isA = w < nK;
       const int ch0 = isA ? 32 * w : 32 * (w - nK);
       const int nrows = isA ? dk : dv;
-      float* dst = isA ? Aout + (size_t)g * dk * dk : Bout + (size_t)g * dv * dk;
+      const size_t slot = (size_t)g + g / F + 1;  // after the unit's text frame
+      float* dst = isA ? Aout + slot * dk * dk : Bout + slot * dv * dk;
 #pragma unroll
       for (int ct = 0; ct < 4; ++ct) {
         if (ct >= nK) continue;
@@ -301,6 +297,123 @@ __global__ __launch_bounds__(512, 1) void stats_bf16_kernel(
     c2 = next(c2);
     if (c0.g >= nframes) break;
   }
+}
+
+// Text frame, bf16 features: [sqrt(b) K | sqrt(b) V]^T (sqrt(b) K) in fp32 on
+// the vector ALUs (sqrt(b) x formed and kept in fp32).  One workgroup per
+// (16-row tile of [A; B], unit); thread t owns row t / 16 of the tile and the
+// 8 key columns 4 (t % 16) + 64 j + e (j < 2, e < 4).  Tokens stream through
+// LDS in tiles of 64, loaded as 16-byte vectors one tile ahead.
+constexpr int kTokT = 64;
+constexpr int kXcS = 132;  // LDS row stride (floats) of the key-channel tile (16-byte rows)
+constexpr int kXrS = 17;   // ... of the tile's 16 row channels
+
+__global__ __launch_bounds__(256) void stats_text_kernel(
+    const uint16_t* __restrict__ tk, const uint16_t* __restrict__ tv, const float* __restrict__ tb,
+    float* __restrict__ Aout, float* __restrict__ Bout, int F, int T, int dk, int dv,
+    float text_scale) {
+  __shared__ __align__(16) float Xc[kTokT * kXcS];  // sqrt(b) k, token-major
+  __shared__ float Xr[kTokT * kXrS];                 // the tile's 16 row channels, token-major
+  const int rt = blockIdx.x;
+  const int u = blockIdx.y;
+  const int t = threadIdx.x;
+  const int nK = dk >> 4;
+  const bool isA = rt < nK;
+  const int ch0 = isA ? 16 * rt : 16 * (rt - nK);
+  const int nrows = isA ? dk : dv;
+  const uint16_t* K = tk + (size_t)u * T * dk;
+  const uint16_t* R = isA ? K : tv + (size_t)u * T * dv;  // source of the row channels
+  const int ldr = isA ? dk : dv;
+  const float* Bt = tb + (size_t)u * T;
+  const u32x4_t z4 = {0u, 0u, 0u, 0u};
+
+  // this thread's share of a token tile: 4 pieces of 8 key channels (token
+  // t / 16 + 16 i, channels 8 (t % 16) ..) and, for t < 128, 8 row channels
+  // (token t / 2, channels ch0 + 8 (t % 2) ..), with the tokens' beta
+  struct Regs {
+    u32x4_t kc[4];
+    float bc[4];
+    u32x4_t xr;
+    float br;
+  };
+  const int c8 = t & 15;
+  const int sr = t >> 1;  // token of the row-channel piece (t < 128)
+  const int h8 = 8 * (t & 1);
+  auto load = [&](Regs& g, int base) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int tok = base + (t >> 4) + 16 * i;
+      const bool ok = tok < T && 8 * c8 < dk;
+      g.kc[i] = ok ? *reinterpret_cast<const u32x4_t*>(K + (size_t)tok * dk + 8 * c8) : z4;
+      g.bc[i] = tok < T ? Bt[tok] : 0.0f;
+    }
+    const int tok = base + sr;
+    const bool ok = t < 128 && tok < T;
+    g.xr = ok ? *reinterpret_cast<const u32x4_t*>(R + (size_t)tok * ldr + ch0 + h8) : z4;
+    g.br = ok ? Bt[tok] : 0.0f;
+  };
+  auto bf_lo = [](uint32_t x) { return __uint_as_float(x << 16); };
+  auto bf_hi = [](uint32_t x) { return __uint_as_float(x & 0xffff0000u); };
+  auto stage = [&](const Regs& g) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float sb = sqrtf(g.bc[i] * text_scale);
+      float* dst = Xc + ((t >> 4) + 16 * i) * kXcS + 8 * c8;
+      f32x4_t lo, hi;
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        lo[2 * e] = sb * bf_lo(g.kc[i][e]);
+        lo[2 * e + 1] = sb * bf_hi(g.kc[i][e]);
+        hi[2 * e] = sb * bf_lo(g.kc[i][2 + e]);
+        hi[2 * e + 1] = sb * bf_hi(g.kc[i][2 + e]);
+      }
+      *reinterpret_cast<f32x4_t*>(dst) = lo;
+      *reinterpret_cast<f32x4_t*>(dst + 4) = hi;
+    }
+    if (t < 128) {
+      const float sb = sqrtf(g.br * text_scale);
+      float* dst = Xr + sr * kXrS + h8;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        dst[2 * e] = sb * bf_lo(g.xr[e]);
+        dst[2 * e + 1] = sb * bf_hi(g.xr[e]);
+      }
+    }
+  };
+
+  const int r = t >> 4;
+  const int c4 = 4 * (t & 15);
+  float acc[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
+  Regs g;
+  load(g, 0);
+  for (int base = 0; base < T; base += kTokT) {
+    stage(g);
+    __syncthreads();
+    if (base + kTokT < T) load(g, base + kTokT);  // in flight during the products
+#pragma unroll 8
+    for (int s = 0; s < kTokT; ++s) {
+      const float xr = Xr[s * kXrS + r];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const f32x4_t xc = *reinterpret_cast<const f32x4_t*>(Xc + s * kXcS + c4 + 64 * j);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[4 * j + e] = fmaf(xr, xc[e], acc[4 * j + e]);
+      }
+    }
+    __syncthreads();
+  }
+  const int row = ch0 + r;
+  if (row >= nrows) return;
+  float* dst = isA ? Aout + (size_t)u * (F + 1) * dk * dk : Bout + (size_t)u * (F + 1) * dv * dk;
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int col = c4 + 64 * j + e;
+      if (col < dk) dst[(size_t)row * dk + col] = acc[4 * j + e];
+    }
 }
 
 // fp32 features: the same contraction, [sqrt(b) K | sqrt(b) V]^T (sqrt(b) K), on
@@ -414,13 +527,16 @@ hipError_t launch_stats(const Plan& p, const void* k, const void* v, const float
   const dim3 grid(p.F + 1, p.units);
   const float ts = p.seed_mode == 1 ? 0.5f : 1.0f;
   if (p.dtype == VDA_DTYPE_BF16) {
-    const int nframes = p.units * (p.F + 1);
+    const dim3 tgrid((p.dk >> 4) + (p.dv >> 4), p.units);
+    hipLaunchKernelGGL(stats_text_kernel, tgrid, dim3(kThreads), 0, s,
+                       static_cast<const uint16_t*>(text_k), static_cast<const uint16_t*>(text_v),
+                       text_beta, w.A, w.B, p.F, p.T, p.dk, p.dv, ts);
+    const int nframes = p.units * p.F;  // latent frames
     const int P = std::min(nframes, compute_units());
     auto kern = (p.dk == 128 && p.dv == 128) ? stats_bf16_kernel<128, 128> : stats_bf16_kernel<0, 0>;
     hipLaunchKernelGGL(kern, dim3(P), dim3(kStatsThreads), 0, s,
-                       static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), beta,
-                       static_cast<const uint16_t*>(text_k), static_cast<const uint16_t*>(text_v),
-                       text_beta, w.A, w.B, p.F, p.U, p.T, p.dk, p.dv, ts, nframes);
+                       static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), beta, w.A,
+                       w.B, p.F, p.U, p.dk, p.dv, nframes);
   } else {
     hipLaunchKernelGGL(stats_f32_kernel, grid, dim3(kThreads), 0, s,
                        static_cast<const float*>(k), static_cast<const float*>(v), beta,

@@ -10,6 +10,7 @@ namespace vda {
 namespace {
 
 constexpr int64_t kMaxGridYZ = 65535;
+constexpr int64_t kMaxFrames = INT64_C(1) << 20;  // the solve grid's x extent is frames + 1
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
@@ -45,10 +46,24 @@ int make_plan(const vda_desc_t* d, Plan* p) {
   if ((int64_t)d->tokens * 512 > INT32_MAX || (int64_t)d->text_tokens * 512 > INT32_MAX)
     return VDA_ERR_INVALID_ARG;
   if ((int64_t)d->units * ((int64_t)d->frames + 1) > (INT64_C(1) << 30)) return VDA_ERR_INVALID_ARG;
-  // 1-D grids of the readout (units x chunks x 1024-row blocks) and composition must fit
+  if (d->frames > kMaxFrames) return VDA_ERR_INVALID_ARG;
+  // A launch holds fewer than 2^32 work-items along x: at most 2^22 workgroups
+  // on the 512-thread 1-D grids (readout, bf16 composition), fewer than 2^24 on
+  // the 256-thread fp32 readout grid.  Readout work items: units x segments x
+  // row blocks (1024 rows bf16, 64 rows fp32); segments are chunks, or frames
+  // with decay (checked by the decay entry points).
   const int64_t rows_per_chunk = (int64_t)d->chunk * d->tokens;
-  if (!mul_ok((int64_t)d->units * n, (rows_per_chunk + 1023) / 1024 + 3, &x) || x > (INT64_C(1) << 30))
-    return VDA_ERR_INVALID_ARG;
+  const bool bf16 = d->in_dtype == VDA_DTYPE_BF16;
+  auto grid_ok = [&](int64_t segs, int64_t seg_rows, int64_t comp_items) {
+    int64_t items;
+    if (!mul_ok((int64_t)d->units * segs, (seg_rows + (bf16 ? 1023 : 63)) / (bf16 ? 1024 : 64),
+                &items))
+      return false;
+    return items < (bf16 ? (INT64_C(1) << 22) : (INT64_C(1) << 24)) &&
+           (int64_t)d->units * comp_items <= (INT64_C(1) << 22);
+  };
+  if (!grid_ok(n, rows_per_chunk, 3 * n + 1)) return VDA_ERR_INVALID_ARG;
+  p->decay_ok = grid_ok(d->frames, d->tokens, 4 * n + 1);
 
   p->units = d->units;
   p->F = d->frames;
@@ -65,7 +80,7 @@ int make_plan(const vda_desc_t* d, Plan* p) {
 
   const size_t U_ = (size_t)p->units, Fp1 = (size_t)p->F + 1, N = (size_t)p->n;
   const size_t kk = (size_t)p->dk * p->dk * 4, vk = (size_t)p->dv * p->dk * 4;
-  size_t sz[8];
+  size_t sz[9];
   sz[0] = U_ * Fp1 * kk;          // A
   sz[1] = U_ * Fp1 * vk;          // B
   sz[2] = U_ * Fp1 * kk;          // M
@@ -74,10 +89,11 @@ int make_plan(const vda_desc_t* d, Plan* p) {
   sz[5] = U_ * N * vk;            // Jr
   sz[6] = U_ * 2 * (N + 1) * vk;  // ST
   sz[7] = U_ * N * kk;            // McT
+  sz[8] = U_ * N * kk;            // MrT
   if (p->units == 0 || p->F == 0)
     for (size_t& s : sz) s = 0;
   size_t off = 0;
-  for (int i = 0; i < 8; ++i) {
+  for (int i = 0; i < 9; ++i) {
     p->off[i] = off;
     off += align256(sz[i]);
   }
@@ -96,15 +112,17 @@ WsPtrs carve(const Plan& p, void* ws) {
   w.Jr = reinterpret_cast<float*>(b + p.off[5]);
   w.ST = reinterpret_cast<float*>(b + p.off[6]);
   w.McT = reinterpret_cast<float*>(b + p.off[7]);
+  w.MrT = reinterpret_cast<float*>(b + p.off[8]);
   return w;
 }
 
 bool aligned(const void* ptr, size_t a) { return (reinterpret_cast<uintptr_t>(ptr) % a) == 0; }
 
-// Checks shared by every entry point that runs the state pipeline.
+// Checks shared by every entry point that runs the state pipeline (alpha:
+// optional decay gates).
 int check_state_inputs(const Plan& p, const void* k, const void* v, const float* beta,
                        const void* tk, const void* tv, const float* tb, const void* ws,
-                       size_t ws_bytes) {
+                       size_t ws_bytes, const float* alpha = nullptr) {
   const bool video = (size_t)p.units * p.F * p.U > 0;
   const bool text = (size_t)p.units * p.T > 0 && p.F > 0;
   if (video && (!k || !v || !beta)) return VDA_ERR_INVALID_ARG;
@@ -114,16 +132,17 @@ int check_state_inputs(const Plan& p, const void* k, const void* v, const float*
   if (video && (!aligned(k, 16) || !aligned(v, 16) || !aligned(beta, 4))) return VDA_ERR_MISALIGNED;
   if (text && (!aligned(tk, 16) || !aligned(tv, 16) || !aligned(tb, 4))) return VDA_ERR_MISALIGNED;
   if (ws && !aligned(ws, 256)) return VDA_ERR_MISALIGNED;
+  if (alpha && !aligned(alpha, 16)) return VDA_ERR_MISALIGNED;
   return VDA_OK;
 }
 
 int hip_status(hipError_t e) { return e == hipSuccess ? VDA_OK : VDA_ERR_HIP; }
 
-// stages: 1 stats, 2 solve, 3 compose, 4 scan.  events (optional): recorded
-// before each launched stage.
+// stages: 1 stats, 2 solve, 3 compose, 4 scan.  alpha (optional): decay
+// gates.  events (optional): recorded before each launched stage.
 int run_states(const Plan& p, const void* k, const void* v, const float* beta, const void* tk,
                const void* tv, const float* tb, const WsPtrs& w, hipStream_t s, int upto,
-               hipEvent_t const* ev = nullptr) {
+               const float* alpha = nullptr, hipEvent_t const* ev = nullptr) {
   auto rec = [&](int i) { return ev ? hipEventRecord(ev[i], s) : hipSuccess; };
   if (p.units == 0 || p.F == 0) {  // nothing to launch; keep the event sequence complete
     for (int i = 0; i < upto; ++i)
@@ -133,20 +152,23 @@ int run_states(const Plan& p, const void* k, const void* v, const float* beta, c
   if (upto >= 1 && (rec(0) != hipSuccess || launch_stats(p, k, v, beta, tk, tv, tb, w, s) != hipSuccess))
     return VDA_ERR_HIP;
   if (upto >= 2 && (rec(1) != hipSuccess || launch_solve(p, w, s) != hipSuccess)) return VDA_ERR_HIP;
-  if (upto >= 3 && (rec(2) != hipSuccess || launch_compose(p, w, s) != hipSuccess))
+  if (upto >= 3 && (rec(2) != hipSuccess || launch_compose(p, w, alpha, s) != hipSuccess))
     return VDA_ERR_HIP;
-  if (upto >= 4 && (rec(3) != hipSuccess || launch_scan(p, w, s) != hipSuccess)) return VDA_ERR_HIP;
+  if (upto >= 4 && (rec(3) != hipSuccess || launch_scan(p, w, alpha != nullptr, s) != hipSuccess))
+    return VDA_ERR_HIP;
   return VDA_OK;
 }
 
 int forward_impl(const vda_desc_t* desc, const void* q, const void* k, const void* v,
-                 const float* beta, const void* gate, const void* text_k, const void* text_v,
-                 const float* text_beta, const float* rms_weight, void* out, void* workspace,
-                 size_t workspace_bytes, vda_stream_t stream, hipEvent_t const* ev) {
+                 const float* beta, const float* alpha, const void* gate, const void* text_k,
+                 const void* text_v, const float* text_beta, const float* rms_weight, void* out,
+                 void* workspace, size_t workspace_bytes, vda_stream_t stream,
+                 hipEvent_t const* ev) {
   Plan p;
   int st = make_plan(desc, &p);
   if (st != VDA_OK) return st;
-  st = check_state_inputs(p, k, v, beta, text_k, text_v, text_beta, workspace, workspace_bytes);
+  st = check_state_inputs(p, k, v, beta, text_k, text_v, text_beta, workspace, workspace_bytes,
+                          alpha);
   if (st != VDA_OK) return st;
   const bool video = (size_t)p.units * p.F * p.U > 0;
   if (video && (!q || !gate || !out || !rms_weight)) return VDA_ERR_INVALID_ARG;
@@ -155,12 +177,80 @@ int forward_impl(const vda_desc_t* desc, const void* q, const void* k, const voi
     return VDA_ERR_MISALIGNED;
   const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const WsPtrs w = carve(p, workspace);
-  st = run_states(p, k, v, beta, text_k, text_v, text_beta, w, s, 4, ev);
+  st = run_states(p, k, v, beta, text_k, text_v, text_beta, w, s, 4, alpha, ev);
   if (st != VDA_OK) return st;
   if (ev && hipEventRecord(ev[4], s) != hipSuccess) return VDA_ERR_HIP;
-  if (video && launch_readout(p, q, gate, rms_weight, out, w, s) != hipSuccess) return VDA_ERR_HIP;
+  if (video && launch_readout(p, q, gate, rms_weight, out, w, alpha, s) != hipSuccess)
+    return VDA_ERR_HIP;
   if (ev && hipEventRecord(ev[5], s) != hipSuccess) return VDA_ERR_HIP;
   return VDA_OK;
+}
+
+// Extra checks of the decay entry points: the gates are required whenever a
+// frame exists, and the per-frame readout grid must fit.
+int check_decay(const vda_desc_t* desc, const float* alpha) {
+  Plan p;
+  const int st = make_plan(desc, &p);
+  if (st != VDA_OK) return st;
+  if (!p.decay_ok) return VDA_ERR_INVALID_ARG;
+  if (p.units > 0 && p.F > 0 && !alpha) return VDA_ERR_INVALID_ARG;
+  return VDA_OK;
+}
+
+// Debug tap bodies shared by the plain and decay variants.
+// want_mr: the caller asked for the reverse maps (Mr_t_out must then be non-NULL)
+int chunks_impl(const vda_desc_t* desc, const void* k, const void* v, const float* beta,
+                const float* alpha, const void* text_k, const void* text_v,
+                const float* text_beta, float* Mc_out, float* Mr_t_out, bool want_mr,
+                float* Jf_out, float* Jr_out, void* workspace, size_t workspace_bytes,
+                vda_stream_t stream) {
+  Plan p;
+  int st = make_plan(desc, &p);
+  if (st != VDA_OK) return st;
+  st = check_state_inputs(p, k, v, beta, text_k, text_v, text_beta, workspace, workspace_bytes,
+                          alpha);
+  if (st != VDA_OK) return st;
+  if (p.units == 0 || p.F == 0) return VDA_OK;
+  if (!Mc_out || !Jf_out || !Jr_out || (want_mr && !Mr_t_out)) return VDA_ERR_INVALID_ARG;
+  const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const WsPtrs w = carve(p, workspace);
+  st = run_states(p, k, v, beta, text_k, text_v, text_beta, w, s, 3, alpha);
+  if (st != VDA_OK) return st;
+  const size_t nc = (size_t)p.units * p.n;
+  const size_t mb = nc * p.dk * p.dk * 4;
+  if (hipMemcpyAsync(Mc_out, w.Mc, mb, hipMemcpyDeviceToDevice, s) != hipSuccess)
+    return VDA_ERR_HIP;
+  // without decay the reverse transition is Mc^T, whose transpose is Mc
+  if (Mr_t_out && hipMemcpyAsync(Mr_t_out, alpha ? w.MrT : w.Mc, mb, hipMemcpyDeviceToDevice, s) !=
+                      hipSuccess)
+    return VDA_ERR_HIP;
+  if (hipMemcpyAsync(Jf_out, w.Jf, nc * p.dv * p.dk * 4, hipMemcpyDeviceToDevice, s) != hipSuccess)
+    return VDA_ERR_HIP;
+  return hip_status(hipMemcpyAsync(Jr_out, w.Jr, nc * p.dv * p.dk * 4, hipMemcpyDeviceToDevice, s));
+}
+
+int states_impl(const vda_desc_t* desc, const void* k, const void* v, const float* beta,
+                const float* alpha, const void* text_k, const void* text_v,
+                const float* text_beta, float* P_out, float* R_out, void* workspace,
+                size_t workspace_bytes, vda_stream_t stream) {
+  Plan p;
+  int st = make_plan(desc, &p);
+  if (st != VDA_OK) return st;
+  st = check_state_inputs(p, k, v, beta, text_k, text_v, text_beta, workspace, workspace_bytes,
+                          alpha);
+  if (st != VDA_OK) return st;
+  if (p.units == 0 || p.F == 0) return VDA_OK;
+  if (!P_out || !R_out) return VDA_ERR_INVALID_ARG;
+  const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const WsPtrs w = carve(p, workspace);
+  st = run_states(p, k, v, beta, text_k, text_v, text_beta, w, s, 4, alpha);
+  if (st != VDA_OK) return st;
+  const size_t dirb = (size_t)(p.n + 1) * p.dv * p.dk * 4;
+  if (hipMemcpy2DAsync(P_out, dirb, w.ST, 2 * dirb, dirb, p.units, hipMemcpyDeviceToDevice, s) !=
+      hipSuccess)
+    return VDA_ERR_HIP;
+  return hip_status(hipMemcpy2DAsync(R_out, dirb, reinterpret_cast<char*>(w.ST) + dirb, 2 * dirb,
+                                     dirb, p.units, hipMemcpyDeviceToDevice, s));
 }
 
 }  // namespace
@@ -186,8 +276,8 @@ int vda_forward(const vda_desc_t* desc, const void* q, const void* k, const void
                 const float* beta, const void* gate, const void* text_k, const void* text_v,
                 const float* text_beta, const float* rms_weight, void* out, void* workspace,
                 size_t workspace_bytes, vda_stream_t stream) {
-  return vda::forward_impl(desc, q, k, v, beta, gate, text_k, text_v, text_beta, rms_weight, out,
-                           workspace, workspace_bytes, stream, nullptr);
+  return vda::forward_impl(desc, q, k, v, beta, nullptr, gate, text_k, text_v, text_beta,
+                           rms_weight, out, workspace, workspace_bytes, stream, nullptr);
 }
 
 int vda_forward_timed(const vda_desc_t* desc, const void* q, const void* k, const void* v,
@@ -198,9 +288,20 @@ int vda_forward_timed(const vda_desc_t* desc, const void* q, const void* k, cons
   if (!stage_events || n_events != 6) return VDA_ERR_INVALID_ARG;
   for (int i = 0; i < 6; ++i)
     if (!stage_events[i]) return VDA_ERR_INVALID_ARG;
-  return vda::forward_impl(desc, q, k, v, beta, gate, text_k, text_v, text_beta, rms_weight, out,
-                           workspace, workspace_bytes, stream,
+  return vda::forward_impl(desc, q, k, v, beta, nullptr, gate, text_k, text_v, text_beta,
+                           rms_weight, out, workspace, workspace_bytes, stream,
                            reinterpret_cast<hipEvent_t const*>(stage_events));
+}
+
+int vda_forward_decay(const vda_desc_t* desc, const void* q, const void* k, const void* v,
+                      const float* beta, const float* alpha, const void* gate,
+                      const void* text_k, const void* text_v, const float* text_beta,
+                      const float* rms_weight, void* out, void* workspace, size_t workspace_bytes,
+                      vda_stream_t stream) {
+  const int st = vda::check_decay(desc, alpha);
+  if (st != VDA_OK) return st;
+  return vda::forward_impl(desc, q, k, v, beta, alpha, gate, text_k, text_v, text_beta,
+                           rms_weight, out, workspace, workspace_bytes, stream, nullptr);
 }
 
 int vda_debug_stats(const vda_desc_t* desc, const void* k, const void* v, const float* beta,
@@ -252,48 +353,37 @@ int vda_debug_chunks(const vda_desc_t* desc, const void* k, const void* v, const
                      const void* text_k, const void* text_v, const float* text_beta, float* Mc_out,
                      float* Jf_out, float* Jr_out, void* workspace, size_t workspace_bytes,
                      vda_stream_t stream) {
-  Plan p;
-  int st = vda::make_plan(desc, &p);
+  return vda::chunks_impl(desc, k, v, beta, nullptr, text_k, text_v, text_beta, Mc_out, nullptr,
+                          false, Jf_out, Jr_out, workspace, workspace_bytes, stream);
+}
+
+int vda_debug_chunks_decay(const vda_desc_t* desc, const void* k, const void* v,
+                           const float* beta, const float* alpha, const void* text_k,
+                           const void* text_v, const float* text_beta, float* Mc_out,
+                           float* Mr_t_out, float* Jf_out, float* Jr_out, void* workspace,
+                           size_t workspace_bytes, vda_stream_t stream) {
+  const int st = vda::check_decay(desc, alpha);
   if (st != VDA_OK) return st;
-  st = vda::check_state_inputs(p, k, v, beta, text_k, text_v, text_beta, workspace,
-                               workspace_bytes);
-  if (st != VDA_OK) return st;
-  if (p.units == 0 || p.F == 0) return VDA_OK;
-  if (!Mc_out || !Jf_out || !Jr_out) return VDA_ERR_INVALID_ARG;
-  const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  const WsPtrs w = vda::carve(p, workspace);
-  st = vda::run_states(p, k, v, beta, text_k, text_v, text_beta, w, s, 3);
-  if (st != VDA_OK) return st;
-  const size_t nc = (size_t)p.units * p.n;
-  if (hipMemcpyAsync(Mc_out, w.Mc, nc * p.dk * p.dk * 4, hipMemcpyDeviceToDevice, s) != hipSuccess)
-    return VDA_ERR_HIP;
-  if (hipMemcpyAsync(Jf_out, w.Jf, nc * p.dv * p.dk * 4, hipMemcpyDeviceToDevice, s) != hipSuccess)
-    return VDA_ERR_HIP;
-  return vda::hip_status(
-      hipMemcpyAsync(Jr_out, w.Jr, nc * p.dv * p.dk * 4, hipMemcpyDeviceToDevice, s));
+  return vda::chunks_impl(desc, k, v, beta, alpha, text_k, text_v, text_beta, Mc_out, Mr_t_out,
+                          true, Jf_out, Jr_out, workspace, workspace_bytes, stream);
 }
 
 int vda_debug_states(const vda_desc_t* desc, const void* k, const void* v, const float* beta,
                      const void* text_k, const void* text_v, const float* text_beta, float* P_out,
                      float* R_out, void* workspace, size_t workspace_bytes, vda_stream_t stream) {
-  Plan p;
-  int st = vda::make_plan(desc, &p);
+  return vda::states_impl(desc, k, v, beta, nullptr, text_k, text_v, text_beta, P_out, R_out,
+                          workspace, workspace_bytes, stream);
+}
+
+int vda_debug_states_decay(const vda_desc_t* desc, const void* k, const void* v,
+                           const float* beta, const float* alpha, const void* text_k,
+                           const void* text_v, const float* text_beta, float* P_out,
+                           float* R_out, void* workspace, size_t workspace_bytes,
+                           vda_stream_t stream) {
+  const int st = vda::check_decay(desc, alpha);
   if (st != VDA_OK) return st;
-  st = vda::check_state_inputs(p, k, v, beta, text_k, text_v, text_beta, workspace,
-                               workspace_bytes);
-  if (st != VDA_OK) return st;
-  if (p.units == 0 || p.F == 0) return VDA_OK;
-  if (!P_out || !R_out) return VDA_ERR_INVALID_ARG;
-  const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  const WsPtrs w = vda::carve(p, workspace);
-  st = vda::run_states(p, k, v, beta, text_k, text_v, text_beta, w, s, 4);
-  if (st != VDA_OK) return st;
-  const size_t dirb = (size_t)(p.n + 1) * p.dv * p.dk * 4;
-  if (hipMemcpy2DAsync(P_out, dirb, w.ST, 2 * dirb, dirb, p.units, hipMemcpyDeviceToDevice, s) !=
-      hipSuccess)
-    return VDA_ERR_HIP;
-  return vda::hip_status(hipMemcpy2DAsync(R_out, dirb, reinterpret_cast<char*>(w.ST) + dirb,
-                                          2 * dirb, dirb, p.units, hipMemcpyDeviceToDevice, s));
+  return vda::states_impl(desc, k, v, beta, alpha, text_k, text_v, text_beta, P_out, R_out,
+                          workspace, workspace_bytes, stream);
 }
 
 const char* vda_status_string(int status) {

@@ -18,25 +18,30 @@ namespace vda {
 //   Jf [units][n][d_v][d_k]       chunk injections, forward
 //   Jr [units][n][d_v][d_k]       chunk injections, reverse
 //   ST [units][2][n + 1][d_v][d_k] boundary states: [0] = P (forward), [1] = R (reverse)
+//   MrT [units][n][d_k][d_k]      reverse chunk transitions, transposed (decay only;
+//                                 without decay the reverse transition is Mc^T)
 struct Plan {
   int units, F, U, T, dk, dv, C, r, n;
   float eps;
   int seed_mode, dtype;
-  size_t off[8];
+  bool decay_ok;  // the decay path's launch grids fit too
+  size_t off[9];
   size_t total;
 };
 
 struct WsPtrs {
-  float *A, *B, *M, *Mc, *Jf, *Jr, *ST, *McT;
+  float *A, *B, *M, *Mc, *Jf, *Jr, *ST, *McT, *MrT;
 };
 
 hipError_t launch_stats(const Plan& p, const void* k, const void* v, const float* beta,
                         const void* text_k, const void* text_v, const float* text_beta,
                         const WsPtrs& w, hipStream_t s);
 hipError_t launch_solve(const Plan& p, const WsPtrs& w, hipStream_t s);
-hipError_t launch_compose(const Plan& p, const WsPtrs& w, hipStream_t s);  // Mc, McT, Jf, Jr
-hipError_t launch_scan(const Plan& p, const WsPtrs& w, hipStream_t s);
+// alpha: decay gates [units][F][d_k] or nullptr (no decay)
+hipError_t launch_compose(const Plan& p, const WsPtrs& w, const float* alpha,
+                          hipStream_t s);  // Mc, McT, Jf, Jr (+ MrT with decay), seeds
+hipError_t launch_scan(const Plan& p, const WsPtrs& w, bool decay, hipStream_t s);
 hipError_t launch_readout(const Plan& p, const void* q, const void* gate, const float* rms_weight,
-                          void* out, const WsPtrs& w, hipStream_t s);
+                          void* out, const WsPtrs& w, const float* alpha, hipStream_t s);
 
 }  // namespace vda

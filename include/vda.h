@@ -14,8 +14,8 @@
  *      ([VDN] Sec. 5, "Chunk-wise scans");
  *   2. the frame-wise update ([VDN] Sec. 3.2 Eq. (5), decay alpha = 1):
  *        S_t = (S_{t-1} + B_t) (I + A_t)^{-1}
- *      through a Cholesky factorisation of the SPD matrix I + A_t, giving the
- *      transition M_t = (I + A_t)^{-1} ([VDN] App. A.1 Eq. (A.1));
+ *      through symmetric Gauss-Jordan elimination of the SPD matrix I + A_t,
+ *      giving the transition M_t = (I + A_t)^{-1} ([VDN] App. A.1 Eq. (A.1));
  *   3. the text seed ([VDN] Sec. 2.2 Eq. (1b)): S_T = B_T (I + A_T)^{-1} and
  *      both scans start at S_T / 2 (seed_mode 0), or at the text written from
  *      zero at beta / 2 (seed_mode 1);
@@ -28,6 +28,16 @@
  *      a query of chunk c reads S~ = P[max(c - radius, 0)] + R[min(c + radius + 1, n)],
  *      o = S~ q, y = w * o / sqrt(mean(o^2) + eps), out = sigmoid(g) * y.
  *
+ * With channel-wise decay (vda_forward_decay; [VDN] Sec. 3.1 Eq. (2), App. A.1
+ * Eq. (A.1) and App. A.3 Eq. (A.4)), frame t carries gates alpha_t in [0, 1]^d_k:
+ * entering frame t, either scan decays the state it inherits, S Diag(alpha_t),
+ * before the update (M_t = Diag(alpha_t) (I + A_t)^{-1}), and a query of frame t
+ * in chunk c, whose window [c - radius, c + radius] spans frames [l, h] of the
+ * clip, reads the bridged state
+ *      S~_t = P[max(c - radius, 0)] Diag(prod_{s=l}^{t} alpha_s)
+ *           + R[min(c + radius + 1, n)] Diag(prod_{s=t}^{h} alpha_s).
+ * The text seed is unchanged (the text state starts from zero).
+ *
  * Layouts (row-major, last index fastest, all tensors contiguous):
  *   q     [units][frames][tokens][d_k]   in_dtype
  *   k     [units][frames][tokens][d_k]   in_dtype (prepared features)
@@ -38,6 +48,7 @@
  *   text_v [units][text_tokens][d_v]     in_dtype
  *   text_beta [units][text_tokens]       float32, >= 0
  *   rms_weight [d_v]                     float32 (shared by all units)
+ *   alpha [units][frames][d_k]           float32 in [0, 1] (decay gates, optional)
  *   out   [units][frames][tokens][d_v]   out_dtype (== in_dtype)
  *
  * Ownership: the caller owns every buffer.  All pointers are device pointers
@@ -83,7 +94,7 @@ typedef enum vda_dtype {
 
 typedef struct vda_desc {
   int32_t units;       /* batch x heads, 0..65535 */
-  int32_t frames;      /* latent frames F, >= 0; units x (F + 1) <= 2^30 */
+  int32_t frames;      /* latent frames F, 0..2^20; units x (F + 1) <= 2^30 */
   int32_t tokens;      /* tokens per frame U, 0..4194303 */
   int32_t text_tokens; /* text tokens T, 0..4194303 (0: zero seed) */
   int32_t d_k;         /* key channels, multiple of 16, 16..128 */
@@ -102,7 +113,12 @@ typedef struct vda_desc {
 size_t vda_workspace_bytes(const vda_desc_t* desc);
 
 /* Checks desc alone (host-only).  Returns VDA_OK or the error vda_forward
- * would return for it. */
+ * would return for it.  Besides the field ranges above, the launch grids must
+ * fit: units x ceil(frames / chunk) x ceil(chunk x tokens / R) < 2^22 with R =
+ * 1024 (bf16; 2^24 and R = 64 for fp32), and units x (3 ceil(frames / chunk) +
+ * 1) <= 2^22.  The decay entry points also need units x frames x
+ * ceil(tokens / R) below the same bound and units x (4 ceil(frames / chunk) +
+ * 1) <= 2^22. */
 int vda_check_desc(const vda_desc_t* desc);
 
 /* The VDA forward pass described at the top of this file.  q, k, v, gate,
@@ -126,6 +142,19 @@ int vda_forward_timed(const vda_desc_t* desc, const void* q, const void* k, cons
                       const float* text_beta, const float* rms_weight, void* out, void* workspace,
                       size_t workspace_bytes, vda_stream_t stream, void* const* stage_events,
                       int n_events);
+
+/* The forward pass with channel-wise decay described at the top of this file;
+ * alpha [units][frames][d_k] float32 in [0, 1], 16-byte aligned, required
+ * (VDA_ERR_INVALID_ARG when NULL and units x frames > 0).  Gates outside
+ * [0, 1] are not checked (they break Prop. 1's contraction bound, not the
+ * arithmetic).  Other arguments as in vda_forward; the same workspace size.
+ * Returns VDA_ERR_INVALID_ARG also when the per-frame launch grids do not fit
+ * (see vda_check_desc). */
+int vda_forward_decay(const vda_desc_t* desc, const void* q, const void* k, const void* v,
+                      const float* beta, const float* alpha, const void* gate,
+                      const void* text_k, const void* text_v, const float* text_beta,
+                      const float* rms_weight, void* out, void* workspace, size_t workspace_bytes,
+                      vda_stream_t stream);
 
 /* ---- debug taps (tests only).  Each runs the pipeline up to the named stage in
  * the caller's workspace and copies that stage's fp32 results to caller
@@ -164,6 +193,25 @@ int vda_debug_states(const vda_desc_t* desc, const void* k, const void* v, const
                      const void* text_k, const void* text_v, const float* text_beta,
                      float* P_out, float* R_out, void* workspace, size_t workspace_bytes,
                      vda_stream_t stream);
+
+/* Chunk maps with decay: forward S_out = S_in Mc + Jf over the chunk's frames in
+ * order, reverse S_out = S_in Mr + Jr over them in reverse order, where each
+ * frame contributes Diag(alpha_t) (I + A_t)^{-1}; Mr is returned transposed
+ * (Mr_t_out = Mr^T, the layout the reverse scan reads).  alpha as in
+ * vda_forward_decay (required).
+ * Mc_out, Mr_t_out [units][n][d_k][d_k], Jf_out and Jr_out [units][n][d_v][d_k]. */
+int vda_debug_chunks_decay(const vda_desc_t* desc, const void* k, const void* v,
+                           const float* beta, const float* alpha, const void* text_k,
+                           const void* text_v, const float* text_beta, float* Mc_out,
+                           float* Mr_t_out, float* Jf_out, float* Jr_out, void* workspace,
+                           size_t workspace_bytes, vda_stream_t stream);
+
+/* Boundary states of both scans with decay (layout as vda_debug_states). */
+int vda_debug_states_decay(const vda_desc_t* desc, const void* k, const void* v,
+                           const float* beta, const float* alpha, const void* text_k,
+                           const void* text_v, const float* text_beta, float* P_out,
+                           float* R_out, void* workspace, size_t workspace_bytes,
+                           vda_stream_t stream);
 
 /* Static, human-readable text for a vda_status_t (never NULL). */
 const char* vda_status_string(int status);

@@ -63,6 +63,7 @@ def workspace_for(desc):
 
 
 def gpu_forward(d: dict, cfg: W.Config, seed_mode=0, ws=None, out=None):
+    """vda_forward, or vda_forward_decay when the inputs hold decay gates."""
     import torch
     import frame_wise_delta_gram_amd as vda
     desc = desc_for(cfg, seed_mode)
@@ -70,8 +71,12 @@ def gpu_forward(d: dict, cfg: W.Config, seed_mode=0, ws=None, out=None):
     if out is None:
         out = torch.empty((cfg.units, cfg.frames, cfg.tokens, cfg.d_v), device="cuda",
                           dtype=torch.bfloat16 if cfg.dtype == "bf16" else torch.float32)
-    vda.vda_forward(desc, d["q"], d["k"], d["v"], d["beta"], d["gate"], d["text_k"], d["text_v"],
-                    d["text_beta"], d["rms_weight"], out, ws)
+    if "alpha" in d:
+        vda.vda_forward_decay(desc, d["q"], d["k"], d["v"], d["beta"], d["alpha"], d["gate"],
+                              d["text_k"], d["text_v"], d["text_beta"], d["rms_weight"], out, ws)
+    else:
+        vda.vda_forward(desc, d["q"], d["k"], d["v"], d["beta"], d["gate"], d["text_k"],
+                        d["text_v"], d["text_beta"], d["rms_weight"], out, ws)
     torch.cuda.synchronize()
     return out
 
@@ -84,7 +89,8 @@ def oracle_forward(x: dict, cfg: W.Config, seed_mode=0, taps=False, units=None):
     import oracle
     return oracle.forward(x["q"], x["k"], x["v"], x["beta"], x["gate"], x["text_k"], x["text_v"],
                           x["text_beta"], x["rms_weight"], chunk=cfg.chunk, radius=cfg.radius,
-                          eps=cfg.rms_eps, seed_mode=seed_mode, taps=taps, units=units)
+                          eps=cfg.rms_eps, seed_mode=seed_mode, taps=taps, units=units,
+                          alpha=x.get("alpha"))
 
 
 def row_rel_err(got: np.ndarray, ref: np.ndarray) -> float:

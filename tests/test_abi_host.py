@@ -30,6 +30,11 @@ def test_header_declares_the_binding_surface():
     assert header_functions() == sorted(vda.EXPORTED)
 
 
+def test_package_exposes_every_entry_point():
+    for name in vda.EXPORTED:
+        assert callable(getattr(vda, name, None)), name
+
+
 def test_library_exports_every_declared_symbol(lib):
     out = subprocess.run(["nm", "-D", "--defined-only", vda.LIB_PATH], stdout=subprocess.PIPE,
                          text=True, check=True).stdout
@@ -54,7 +59,8 @@ def test_workspace_formula(lib):
     units, Fp1, dk, dv = 2, 13, 64, 32
     expect = (a(units * Fp1 * dk * dk * 4) + a(units * Fp1 * dv * dk * 4) + a(units * Fp1 * dk * dk * 4)
               + a(units * n * dk * dk * 4) + 2 * a(units * n * dv * dk * 4)
-              + a(units * 2 * (n + 1) * dv * dk * 4) + a(units * n * dk * dk * 4))
+              + a(units * 2 * (n + 1) * dv * dk * 4) + a(units * n * dk * dk * 4)
+              + a(units * n * dk * dk * 4))  # Mc^T and the reverse transitions (decay)
     assert vda.vda_workspace_bytes(d) == expect
     assert vda.vda_workspace_bytes(desc(units=0)) == 0
     assert vda.vda_workspace_bytes(desc(frames=0)) == 0
@@ -80,6 +86,11 @@ def test_workspace_formula(lib):
     (dict(text_tokens=4194304), vda.VDA_ERR_INVALID_ARG),
     (dict(tokens=4194303, units=1, frames=1), vda.VDA_OK),
     (dict(units=65535, frames=20000), vda.VDA_ERR_INVALID_ARG),
+    (dict(units=1, frames=1048577, chunk=100, tokens=1), vda.VDA_ERR_INVALID_ARG),
+    (dict(units=1, frames=1048576, chunk=100, tokens=1), vda.VDA_OK),
+    # readout grid: units x chunks x 1024-row blocks below 2^22
+    (dict(units=64, frames=50000, chunk=5, tokens=2048), vda.VDA_ERR_INVALID_ARG),
+    (dict(units=64, frames=20000, chunk=5, tokens=2048), vda.VDA_OK),
     (dict(dtype=7), vda.VDA_ERR_BAD_DTYPE),
     (dict(units=0, frames=0, tokens=0), vda.VDA_OK),
     (dict(d_k=16, d_v=128), vda.VDA_OK),
@@ -133,6 +144,42 @@ def test_debug_tap_argument_errors(lib):
         vda.VDA_ERR_INVALID_ARG
     assert lib.vda_debug_states(ctypes.byref(d), *P[:8], P[8], ws - 256, None) == \
         vda.VDA_ERR_WORKSPACE_TOO_SMALL
+
+
+def call_forward_decay(lib, d, **ptrs):
+    names = ["q", "k", "v", "beta", "alpha", "gate", "text_k", "text_v", "text_beta",
+             "rms_weight", "out", "workspace"]
+    args = [ptrs.get(n, 4096 * (i + 1)) for i, n in enumerate(names)]
+    ws_bytes = ptrs.get("ws_bytes", vda.vda_workspace_bytes(d))
+    return lib.vda_forward_decay(ctypes.byref(d), *args, ws_bytes, None)
+
+
+def test_forward_decay_argument_errors(lib):
+    d = desc()
+    assert call_forward_decay(lib, d, alpha=None) == vda.VDA_ERR_INVALID_ARG
+    assert call_forward_decay(lib, d, alpha=4096 + 4) == vda.VDA_ERR_MISALIGNED
+    assert call_forward_decay(lib, d, k=None) == vda.VDA_ERR_INVALID_ARG
+    assert call_forward_decay(lib, d, ws_bytes=vda.vda_workspace_bytes(d) - 1) == \
+        vda.VDA_ERR_WORKSPACE_TOO_SMALL
+    bad = desc(d_k=12)
+    assert call_forward_decay(lib, bad) == vda.VDA_ERR_INVALID_ARG
+    # empty problems need no gates
+    e = desc(units=0)
+    assert lib.vda_forward_decay(ctypes.byref(e), *([None] * 12), 0, None) == vda.VDA_OK
+    # one segment per frame: a problem whose per-chunk readout grid fits but whose
+    # per-frame grid (units x frames x 1024-row blocks) does not is refused by the
+    # decay entry points only
+    big = desc(units=64, frames=39063, tokens=1025, text_tokens=0)
+    assert vda.vda_check_desc(big) == vda.VDA_OK
+    assert call_forward_decay(lib, big) == vda.VDA_ERR_INVALID_ARG
+    P = [4096 * (i + 1) for i in range(12)]
+    ws = vda.vda_workspace_bytes(d)
+    assert lib.vda_debug_chunks_decay(ctypes.byref(d), *P[:3], None, *P[4:11], P[11], ws,
+                                      None) == vda.VDA_ERR_INVALID_ARG
+    assert lib.vda_debug_chunks_decay(ctypes.byref(d), *P[:8], None, *P[9:11], P[11], ws,
+                                      None) == vda.VDA_ERR_INVALID_ARG
+    assert lib.vda_debug_states_decay(ctypes.byref(d), *P[:3], None, *P[4:9], P[11], ws,
+                                      None) == vda.VDA_ERR_INVALID_ARG
 
 
 def test_status_strings(lib):

@@ -1,5 +1,6 @@
-"""The two full-size workloads (768p-shaped head share and the ill-conditioned
-stress workload) in the launch configuration bench.py times, checked against
+"""The full-size workloads (768p-shaped head share, the ill-conditioned stress
+workload and the 768p share with channel-wise decay) in the launch
+configuration bench.py times, checked against
 the fp64 oracle on whole sampled units (first and last unit: every frame and
 every token of those units), plus bitwise run-to-run determinism.
 Inputs come from the device generator (workloads.device_inputs); the sampled
@@ -14,7 +15,7 @@ from gpu_helpers import (TOL_OUT, device_to_host_f64, gpu_forward, oracle_forwar
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
 
 
-@pytest.mark.parametrize("cfg_id", [4, 5])
+@pytest.mark.parametrize("cfg_id", [4, 5, 6])
 def test_fullsize_sampled_units(cfg_id):
     require_gpu()
     import torch

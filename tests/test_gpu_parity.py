@@ -75,10 +75,11 @@ def test_configs(cfg_id, seed_mode):
 
 
 @pytest.mark.parametrize("name", sorted(EDGE))
-def test_edge_cases(name):
+@pytest.mark.parametrize("seed_mode", [0, 1])
+def test_edge_cases(name, seed_mode):
     cfg = EDGE[name]
-    say(f"[parity] edge {name}")
-    got, ref = run_case(cfg)
+    say(f"[parity] edge {name} seed_mode={seed_mode}")
+    got, ref = run_case(cfg, seed_mode)
     err = row_rel_err(got, ref)
     say(f"  max row-rel err {err:.3e}")
     assert np.all(np.isfinite(got))

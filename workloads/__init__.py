@@ -15,6 +15,7 @@ Sec. 6.4: heads are sharded per GPU), with five concrete sizes:
   stress-bf16  16 units, 75 frames, U=4032, d=128, 512 text tokens, bf16,
                90% of each frame's keys clustered around e_1 (near rank-1 Gram),
                write strengths near 1
+  768p-decay-bf16  the 768p workload with per-frame channel-wise decay gates
 
 Recipe (every tensor has its own seeded stream, so any unit can be regenerated
 alone):
@@ -25,6 +26,8 @@ alone):
   stress keys: round(0.9 U) positions per frame (seeded) get e_1 + 0.01 N(0, I),
   renormalised; the rest are unit keys
   rms weight = 1
+  decay gates (only when the config has alpha_mu): alpha = sigmoid(N(alpha_mu, 1))
+  per (unit, frame, key channel), fp32 (alpha_mu = 3: mean about 0.95)
 
 Two generators implement that recipe:
   * ``host_inputs``   numpy PCG64, fp64 draws, rounded fp64 -> fp32 -> bf16 with
@@ -65,6 +68,7 @@ class Config:
     dtype: str            # "f32" or "bf16" for q, k, v, gate, text_k, text_v, out
     beta_mu: float = 0.0  # beta = sigmoid(N(beta_mu, 1))
     stress: bool = False  # clustered keys
+    alpha_mu: float | None = None  # decay gates alpha = sigmoid(N(alpha_mu, 1)); None: no decay
     chunk: int = 5
     radius: int = 1
     rms_eps: float = 1e-6
@@ -84,11 +88,12 @@ CONFIGS = {
     3: Config(3, "medium-bf16", 8, 60, 1024, 128, 128, 256, "bf16"),
     4: Config(4, "768p-bf16", 16, 90, 4032, 128, 128, 512, "bf16"),
     5: Config(5, "stress-bf16", 16, 75, 4032, 128, 128, 512, "bf16", beta_mu=2.0, stress=True),
+    6: Config(6, "768p-decay-bf16", 16, 90, 4032, 128, 128, 512, "bf16", alpha_mu=3.0),
 }
 
 # one independent stream per (config, unit, tensor)
 TENSOR_IDS = {"q": 0, "k": 1, "v": 2, "beta": 3, "gate": 4,
-              "text_k": 5, "text_v": 6, "text_beta": 7, "stress_pos": 8}
+              "text_k": 5, "text_v": 6, "text_beta": 7, "stress_pos": 8, "alpha": 9}
 
 
 def custom_config(cfg_id=100, **kw) -> Config:
@@ -157,6 +162,8 @@ def _host_unit(cfg: Config, u: int):
     out["text_k"] = _unit_rows(_rng(cfg.cfg_id, u, "text_k").standard_normal((T, dk)))
     out["text_v"] = _rng(cfg.cfg_id, u, "text_v").standard_normal((T, dv))
     out["text_beta"] = _sigmoid(_rng(cfg.cfg_id, u, "text_beta").standard_normal(T) + cfg.beta_mu)
+    if cfg.alpha_mu is not None:
+        out["alpha"] = _sigmoid(_rng(cfg.cfg_id, u, "alpha").standard_normal((F, dk)) + cfg.alpha_mu)
     return out
 
 
@@ -164,9 +171,10 @@ def host_inputs(cfg: Config, units=None) -> dict:
     """Inputs of ``cfg`` as host arrays in storage format.
 
     Returns a dict with q, k, v, gate, text_k, text_v (float32 arrays, or uint16
-    bf16 bits when cfg.dtype == "bf16"), beta and text_beta (float32) and
-    rms_weight (float32, ones).  Leading axis is the unit.  ``units`` selects a
-    subset of unit indices (default: all).
+    bf16 bits when cfg.dtype == "bf16"), beta and text_beta (float32),
+    rms_weight (float32, ones) and, for configs with decay, alpha (float32).
+    Leading axis is the unit.  ``units`` selects a subset of unit indices
+    (default: all).
     """
     units = range(cfg.units) if units is None else list(units)
     per = [_host_unit(cfg, u) for u in units]
@@ -174,7 +182,7 @@ def host_inputs(cfg: Config, units=None) -> dict:
     for name in ("q", "k", "v", "gate", "text_k", "text_v"):
         x = np.stack([p[name] for p in per]) if per else np.zeros((0,))
         res[name] = bf16_bits_from_f64(x) if cfg.dtype == "bf16" else x.astype(np.float32)
-    for name in ("beta", "text_beta"):
+    for name in ("beta", "text_beta") + (("alpha",) if cfg.alpha_mu is not None else ()):
         x = np.stack([p[name] for p in per]) if per else np.zeros((0,))
         res[name] = x.astype(np.float32)
     res["rms_weight"] = np.ones(cfg.d_v, dtype=np.float32)
@@ -231,6 +239,8 @@ def device_inputs(cfg: Config, device="cuda", seed: int = 0) -> dict:
     res["text_v"] = normal((N, T, dv), "text_v").to(dt)
     res["text_beta"] = torch.sigmoid(normal((N, T), "text_beta") + cfg.beta_mu).contiguous()
     res["rms_weight"] = torch.ones(dv, device=device, dtype=torch.float32)
+    if cfg.alpha_mu is not None:
+        res["alpha"] = torch.sigmoid(normal((N, F, dk), "alpha") + cfg.alpha_mu).contiguous()
     return res
 
 
