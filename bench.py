@@ -9,8 +9,9 @@ bf16 features, fp32 state), synthetic seeded inputs.
 
 Prints ONE JSON line: token-heads/s, the roofline of the dominant kernel
 (timed with HIP events recorded by the library on the launch stream), the
-MFMA fraction the metric asks for, and the fp64 CPU oracle timed on a bounded
-sample of the same workload on the host cores.
+MFMA fraction the metric asks for, the fp64 CPU oracle timed on a bounded
+sample of the same workload on the host cores, and (object "decay") the same
+workload with channel-wise decay gates through vda_forward_decay.
 
   python bench.py [--steps K] [--warmup W] [--config 4] [--cpu-seconds S]
   python bench.py --summarize DIR [--config 4]   (profiles/ from rocprofv3 output)
@@ -41,29 +42,43 @@ def log(*a):
 
 
 def algorithmic(cfg):
-    """Algorithmic HBM bytes (and bf16 MFMA flops where the kernel is a contraction)
-    per launch of each kernel: every input read once, every output written once."""
+    """Algorithmic HBM bytes (and MFMA flops where the kernel is a contraction)
+    per launch of each kernel: every input read once, every output written once.
+    "stats" is the latent frames' kernel, "stats_text" the text frame's (fp32
+    vector ALUs); with decay the gates are read once by the composition and
+    once by the readout, and the composition also writes the reverse maps."""
     eb = 2 if cfg.dtype == "bf16" else 4
     th = cfg.units * cfg.frames * cfg.tokens        # token-heads
     tt = cfg.units * cfg.text_tokens
     dk, dv, n, u, F = cfg.d_k, cfg.d_v, cfg.n_chunks, cfg.units, cfg.frames
     mat, st = dk * dk * 4, dv * dk * 4               # one transition, one state (fp32)
-    stats_bytes = ((th + tt) * ((dk + dv) * eb + 4)                     # k, v, beta read
-                   + u * (F + 1) * (dk + dv) * dk * 4)                  # A, B written
+    gates = u * F * dk * 4 if cfg.alpha_mu is not None else 0
+    nmaps = 3 if cfg.alpha_mu is not None else 2     # Mc, Mc^T (+ Mr^T)
+    stats_bytes = th * ((dk + dv) * eb + 4) + u * F * (dk + dv) * dk * 4
+    text_bytes = tt * ((dk + dv) * eb + 4) + u * (dk + dv) * dk * 4
     readout_bytes = (th * (dk + 2 * dv) * eb                           # q, gate read; out written
-                     + u * n * 2 * st + dv * 4)                         # two states per chunk
+                     + u * n * 2 * st + dv * 4 + gates)                 # two states per chunk
     solve_bytes = 2 * u * (F + 1) * mat                                 # A in, M out
-    compose_bytes = (u * (F + 1) * (mat + st) + u * n * (2 * mat + 2 * st)  # M, B in; Mc, McT, Jf, Jr
+    compose_bytes = (u * (F + 1) * (mat + st) + gates                  # M, B (and gates) in
+                     + u * n * (nmaps * mat + 2 * st)                   # chunk maps out
                      + u * 2 * st)                                      # the two seed copies
     scan_bytes = u * n * (2 * mat + 2 * st) + u * 2 * n * st            # chunk maps in; P, R out
-    stats_flops = 2 * (th + tt) * (dk + dv) * dk     # [K|V]^T (beta K), full Gram
-    readout_flops = 2 * th * dk * dv                 # S~ q
-    return {"stats": (stats_bytes, stats_flops), "readout": (readout_bytes, readout_flops),
+    return {"stats": (stats_bytes, 2 * th * (dk + dv) * dk),
+            "stats_text": (text_bytes, 2 * tt * (dk + dv) * dk),
+            "readout": (readout_bytes, 2 * th * dk * dv),
             "solve": (solve_bytes, None), "compose": (compose_bytes, None),
             "scan": (scan_bytes, None)}
 
 
-KERNEL_SOURCES = {"stats": "k_stats.hip", "readout": "k_readout.hip", "solve": "k_solve.hip",
+def stage_alg(alg, stage):
+    """(bytes, flops) of a timed stage: the statistics stage runs two kernels."""
+    if stage != "stats":
+        return alg[stage]
+    return (alg["stats"][0] + alg["stats_text"][0], alg["stats"][1] + alg["stats_text"][1])
+
+
+KERNEL_SOURCES = {"stats": "k_stats.hip", "stats_text": "k_stats.hip", "readout": "k_readout.hip",
+                  "solve": "k_solve.hip",
                   "compose": "k_scan.hip", "scan": "k_scan.hip"}
 
 
@@ -89,17 +104,19 @@ def measured_traffic(kernel, workload):
     return rec.get("hbm_bytes_per_launch")
 
 
-PROFILE_COMMANDS = {
+PROFILE_COMMANDS = {  # CFG: the workload id
     "FETCH_SIZE": "timeout -s KILL 120 rocprofv3 --pmc FETCH_SIZE --kernel-include-regex "
                   "'vda|add' -d DIR/FETCH_SIZE -o p --output-format csv -- python bench.py "
-                  "--steps 2 --warmup 1 --cpu-seconds 0",
+                  "--config CFG --steps 2 --warmup 1 --cpu-seconds 0 --decay-steps 0",
     "WRITE_SIZE": "timeout -s KILL 120 rocprofv3 --pmc WRITE_SIZE --kernel-include-regex "
                   "'vda|add' -d DIR/WRITE_SIZE -o p --output-format csv -- python bench.py "
-                  "--steps 2 --warmup 1 --cpu-seconds 0",
+                  "--config CFG --steps 2 --warmup 1 --cpu-seconds 0 --decay-steps 0",
     "stats": "rocprofv3 --kernel-trace --stats -d DIR/trace -o vda --output-format csv -- "
-             "python bench.py --steps 5 --warmup 2 --cpu-seconds 0",
+             "python bench.py --config CFG --steps 5 --warmup 2 --cpu-seconds 0 --decay-steps 0",
 }
+KERNELS = ("stats_text", "stats", "solve", "compose", "scan", "readout")  # launch order
 KERNEL_NAMES = {"stats_bf16_kernel": "stats", "stats_f32_kernel": "stats",
+                "stats_text_kernel": "stats_text",
                 "readout_bf16_kernel": "readout", "readout_f32_kernel": "readout",
                 "solve_kernel": "solve", "compose_split_kernel": "compose",
                 "compose_kernel": "compose", "scan_split_kernel": "scan", "scan_kernel": "scan"}
@@ -152,12 +169,13 @@ def summarize(prof_dir, cfg_id):
                 durations[k] = (int(r["Calls"]), float(r["AverageNs"]) / 1e3,
                                 float(r["MinNs"]) / 1e3, float(r["MaxNs"]) / 1e3)
     os.makedirs(PROFILES, exist_ok=True)
-    order = [k for k in STAGES if k in durations]
+    order = [k for k in KERNELS if k in durations]
     head = (f"{cfg.name} workload ({cfg.units} heads x {cfg.frames} frames x {cfg.tokens} "
             f"tokens, d_k = {cfg.d_k}, d_v = {cfg.d_v}, {cfg.text_tokens} text tokens)")
     lines = [f"# VDA forward kernels, {head}", "",
              "Commands (from the repository root, on one MI355X; DIR = an output folder):", ""]
-    lines += [f"    {PROFILE_COMMANDS[c]}" for c in ("stats", "FETCH_SIZE", "WRITE_SIZE")]
+    cmd = {c: PROFILE_COMMANDS[c].replace("CFG", str(cfg_id)) for c in PROFILE_COMMANDS}
+    lines += [f"    {cmd[c]}" for c in ("stats", "FETCH_SIZE", "WRITE_SIZE")]
     lines += [f"    python bench.py --summarize DIR --config {cfg_id}", "",
               "## Kernel durations (`vda_kernel_stats.csv`)", "",
               "| kernel | calls | average (us) | min (us) | max (us) | algorithmic GB/s |",
@@ -186,7 +204,7 @@ def summarize(prof_dir, cfg_id):
                "fetch_scale": scale["FETCH_SIZE"], "write_scale": scale["WRITE_SIZE"],
                "read_bytes_per_launch": rb, "write_bytes_per_launch": wb,
                "hbm_bytes_per_launch": rb + wb, "algorithmic_bytes_per_launch": alg[k][0],
-               "commands": [PROFILE_COMMANDS["FETCH_SIZE"], PROFILE_COMMANDS["WRITE_SIZE"],
+               "commands": [cmd["FETCH_SIZE"], cmd["WRITE_SIZE"],
                             f"python bench.py --summarize DIR --config {cfg_id}"]}
         with open(os.path.join(PROFILES, f"traffic_{k}_{cfg.name}.json"), "w") as fh:
             json.dump(rec, fh, indent=1)
@@ -214,7 +232,7 @@ def cpu_baseline(d, cfg, budget_s):
         t0 = time.perf_counter()
         oracle.forward(x["q"], x["k"], x["v"], x["beta"], x["gate"], x["text_k"], x["text_v"],
                        x["text_beta"], x["rms_weight"], chunk=cfg.chunk, radius=cfg.radius,
-                       eps=cfg.rms_eps)
+                       eps=cfg.rms_eps, alpha=x.get("alpha"))
         elapsed += time.perf_counter() - t0
         done += 1
         log(f"[bench] oracle unit {u}: {elapsed:.1f} s total")
@@ -227,14 +245,87 @@ def cpu_baseline(d, cfg, budget_s):
                       f"x {cfg.tokens} tokens each), fp64 numpy, {elapsed:.1f} s"}
 
 
+def time_steps(cfg, d, steps, warmup):
+    """Run the forward pass (vda_forward_timed; decay gates when d holds them)
+    warmup + steps times on the current stream; returns (seconds for the timed
+    steps, average ms per stage from the library's stage events)."""
+    import torch
+    import frame_wise_delta_gram_amd as vda
+
+    desc = vda.make_desc(cfg.units, cfg.frames, cfg.tokens, cfg.text_tokens, cfg.d_k, cfg.d_v,
+                         cfg.chunk, cfg.radius, cfg.rms_eps, 0,
+                         vda.VDA_DTYPE_BF16 if cfg.dtype == "bf16" else vda.VDA_DTYPE_F32)
+    ws = torch.empty(max(vda.vda_workspace_bytes(desc), 1), dtype=torch.uint8, device="cuda")
+    out = torch.empty((cfg.units, cfg.frames, cfg.tokens, cfg.d_v), device="cuda",
+                      dtype=d["q"].dtype)
+    stream = torch.cuda.current_stream()
+    fw = (desc, d["q"], d["k"], d["v"], d["beta"], d.get("alpha"), d["gate"], d["text_k"],
+          d["text_v"], d["text_beta"], d["rms_weight"], out, ws)
+
+    hip = ctypes.CDLL(os.path.join(os.path.dirname(torch.__file__), "lib", "libamdhip64.so"))
+    hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+    hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+    hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                        ctypes.c_void_p]
+    events = []
+    for _ in range(max(steps, warmup)):
+        row = []
+        for _ in range(6):
+            e = ctypes.c_void_p()
+            if hip.hipEventCreate(ctypes.byref(e)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+            row.append(e.value)
+        events.append(row)
+
+    log(f"[bench] {cfg.name}: warmup {warmup}")
+    for i in range(warmup):
+        vda.vda_forward_timed(*fw, events[i], stream=stream)
+    torch.cuda.synchronize()
+    log(f"[bench] {cfg.name}: timing {steps} steps")
+    t0 = time.perf_counter()
+    for i in range(steps):
+        vda.vda_forward_timed(*fw, events[i], stream=stream)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+
+    stage_ms = {s: [] for s in STAGES}
+    for row in events[:steps]:
+        for j, s in enumerate(STAGES):
+            ms = ctypes.c_float()
+            if hip.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(row[j]),
+                                       ctypes.c_void_p(row[j + 1])) != 0:
+                raise RuntimeError("hipEventElapsedTime failed")
+            stage_ms[s].append(ms.value)
+    for row in events:
+        for e in row:
+            hip.hipEventDestroy(ctypes.c_void_p(e))
+    return elapsed, {s: sum(v) / len(v) for s, v in stage_ms.items()}
+
+
+def roofline_of(cfg, avg_ms):
+    """Roofline of the dominant HBM-bound kernel (statistics or readout)."""
+    alg = algorithmic(cfg)
+    dominant = max(("stats", "readout"), key=lambda s: avg_ms[s])
+    bytes_ = stage_alg(alg, dominant)[0]
+    achieved = bytes_ / (avg_ms[dominant] * 1e-3)
+    return {"bound": "hbm", "kernel": dominant, "achieved": achieved / 1e9,
+            "peak": HBM_PEAK / 1e9, "unit": "GB/s", "frac": achieved / HBM_PEAK,
+            "traffic": measured_traffic(dominant, cfg.name),
+            "algorithmic_bytes_per_launch": bytes_, "avg_launch_ms": avg_ms[dominant]}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--config", type=int, default=4, help="workload id (4 = 768p-bf16)")
+    ap.add_argument("--config", type=int, default=4,
+                    help="workload id (4 = 768p-bf16, 6 = the same with decay gates)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="CPU budget of the oracle baseline (0 disables it)")
+    ap.add_argument("--decay-steps", type=int, default=None,
+                    help="steps of the decay measurement that follows the 768p-bf16 one "
+                         "(default: --steps; 0 disables it)")
     ap.add_argument("--summarize", metavar="DIR",
                     help="write the profiles/ summaries from rocprofv3 output under DIR and exit")
     args = ap.parse_args()
@@ -259,55 +350,7 @@ def main():
     log(f"[bench] generating {cfg.name} inputs on the device")
     d = W.device_inputs(cfg)
     torch.cuda.synchronize()
-    desc = vda.make_desc(cfg.units, cfg.frames, cfg.tokens, cfg.text_tokens, cfg.d_k, cfg.d_v,
-                         cfg.chunk, cfg.radius, cfg.rms_eps, 0,
-                         vda.VDA_DTYPE_BF16 if cfg.dtype == "bf16" else vda.VDA_DTYPE_F32)
-    ws = torch.empty(max(vda.vda_workspace_bytes(desc), 1), dtype=torch.uint8, device="cuda")
-    out = torch.empty((cfg.units, cfg.frames, cfg.tokens, cfg.d_v), device="cuda",
-                      dtype=d["q"].dtype)
-    stream = torch.cuda.current_stream()
-    args_fw = (desc, d["q"], d["k"], d["v"], d["beta"], d["gate"], d["text_k"], d["text_v"],
-               d["text_beta"], d["rms_weight"], out, ws)
-
-    hip = ctypes.CDLL(os.path.join(os.path.dirname(torch.__file__), "lib", "libamdhip64.so"))
-    hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
-    hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
-    hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
-                                        ctypes.c_void_p]
-    events = []
-    for _ in range(args.steps):
-        row = []
-        for _ in range(6):
-            e = ctypes.c_void_p()
-            if hip.hipEventCreate(ctypes.byref(e)) != 0:
-                raise RuntimeError("hipEventCreate failed")
-            row.append(e.value)
-        events.append(row)
-
-    log(f"[bench] warmup {args.warmup}")
-    for _ in range(args.warmup):
-        vda.vda_forward(*args_fw, stream=stream)
-    torch.cuda.synchronize()
-    log(f"[bench] timing {args.steps} steps")
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        vda.vda_forward_timed(*args_fw, events[i], stream=stream)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    elapsed = t1 - t0
-
-    stage_ms = {s: [] for s in STAGES}
-    for row in events:
-        for j, s in enumerate(STAGES):
-            ms = ctypes.c_float()
-            if hip.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(row[j]),
-                                       ctypes.c_void_p(row[j + 1])) != 0:
-                raise RuntimeError("hipEventElapsedTime failed")
-            stage_ms[s].append(ms.value)
-    for row in events:
-        for e in row:
-            hip.hipEventDestroy(ctypes.c_void_p(e))
-    avg_ms = {s: sum(v) / len(v) for s, v in stage_ms.items()}
+    elapsed, avg_ms = time_steps(cfg, d, args.steps, args.warmup)
 
     # context: what a plain library kernel with the readout's traffic mix (two
     # reads + one write of the same tensors) reaches on this GPU
@@ -328,31 +371,25 @@ def main():
     ms_per_step = elapsed * 1e3 / args.steps
     value = th * args.steps / elapsed
     alg = algorithmic(cfg)
-    dominant = max(("stats", "readout"), key=lambda s: avg_ms[s])
-    bytes_, flops = alg[dominant]
-    achieved = bytes_ / (avg_ms[dominant] * 1e-3)
-    workload = cfg.name
-    roofline = {"bound": "hbm", "kernel": dominant, "achieved": achieved / 1e9,
-                "peak": HBM_PEAK / 1e9, "unit": "GB/s", "frac": achieved / HBM_PEAK,
-                "traffic": measured_traffic(dominant, workload),
-                "algorithmic_bytes_per_launch": bytes_, "avg_launch_ms": avg_ms[dominant]}
-    whole_flops = alg["stats"][1] + alg["readout"][1]
+    stats_flops = stage_alg(alg, "stats")[1]
     mfma = {
-        "whole_op": whole_flops / (ms_per_step * 1e-3) / BF16_PEAK,
-        "stats": alg["stats"][1] / (avg_ms["stats"] * 1e-3) / BF16_PEAK,
+        "whole_op": (stats_flops + alg["readout"][1]) / (ms_per_step * 1e-3) / BF16_PEAK,
+        "stats": stats_flops / (avg_ms["stats"] * 1e-3) / BF16_PEAK,
         "readout": alg["readout"][1] / (avg_ms["readout"] * 1e-3) / BF16_PEAK,
     }
-    hbm_whole = (alg["stats"][0] + alg["readout"][0]) / (ms_per_step * 1e-3) / HBM_PEAK
+    hbm_whole = ((stage_alg(alg, "stats")[0] + alg["readout"][0]) / (ms_per_step * 1e-3)
+                 / HBM_PEAK)
     line = {
         "metric": METRIC, "value": value, "unit": "token-heads/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": cfg.dtype, "data": "synthetic",
-        "config": {"workload": workload, "units": cfg.units, "frames": cfg.frames,
+        "config": {"workload": cfg.name, "units": cfg.units, "frames": cfg.frames,
                    "tokens_per_frame": cfg.tokens, "d_k": cfg.d_k, "d_v": cfg.d_v,
                    "text_tokens": cfg.text_tokens, "chunk": cfg.chunk, "radius": cfg.radius,
-                   "state": "fp32", "parallelism": "single GPU"},
-        "roofline": roofline,
+                   "decay": cfg.alpha_mu is not None, "state": "fp32",
+                   "parallelism": "single GPU"},
+        "roofline": roofline_of(cfg, avg_ms),
         "mfma_frac": mfma,
         "hbm_frac_whole_op": hbm_whole,
         "stage_ms": avg_ms,
@@ -364,6 +401,22 @@ def main():
         line["cpu_baseline"] = cpu_baseline(d, cfg, args.cpu_seconds)
     else:
         line["cpu_baseline"] = None
+    decay_steps = args.steps if args.decay_steps is None else args.decay_steps
+    line["decay"] = None
+    if decay_steps > 0 and args.config == 4:
+        del d
+        dcfg = W.CONFIGS[6]
+        log(f"[bench] generating {dcfg.name} inputs on the device")
+        dd = W.device_inputs(dcfg)
+        torch.cuda.synchronize()
+        el, ms = time_steps(dcfg, dd, decay_steps, args.warmup)
+        dvalue = dcfg.token_heads * decay_steps / el
+        line["decay"] = {
+            "workload": dcfg.name, "entry_point": "vda_forward_decay", "steps": decay_steps,
+            "ms_per_step": el * 1e3 / decay_steps, "value": dvalue, "unit": "token-heads/s",
+            "alpha": f"sigmoid(N({dcfg.alpha_mu}, 1)) per (unit, frame, key channel), fp32",
+            "relative_to_plain": dvalue / value, "stage_ms": ms,
+            "roofline": roofline_of(dcfg, ms)}
     print(json.dumps(line), flush=True)
 
 

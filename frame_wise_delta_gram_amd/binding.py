@@ -74,7 +74,7 @@ def load_library(path: str = LIB_PATH):
     lib.vda_check_desc.restype = ctypes.c_int
     lib.vda_forward.argtypes = [D] + [P] * 11 + [ctypes.c_size_t, P]
     lib.vda_forward.restype = ctypes.c_int
-    lib.vda_forward_timed.argtypes = [D] + [P] * 11 + [ctypes.c_size_t, P,
+    lib.vda_forward_timed.argtypes = [D] + [P] * 12 + [ctypes.c_size_t, P,
                                                       ctypes.POINTER(ctypes.c_void_p), ctypes.c_int]
     lib.vda_forward_timed.restype = ctypes.c_int
     lib.vda_forward_decay.argtypes = [D] + [P] * 12 + [ctypes.c_size_t, P]
@@ -149,15 +149,17 @@ def vda_forward(desc, q, k, v, beta, gate, text_k, text_v, text_beta, rms_weight
     _check(st, "vda_forward")
 
 
-def vda_forward_timed(desc, q, k, v, beta, gate, text_k, text_v, text_beta, rms_weight, out,
-                      workspace, stage_events, workspace_bytes=None, stream=None):
-    """C vda_forward_timed: as vda_forward, recording the six caller-created
-    hipEvent_t handles (ints) in ``stage_events`` at the stage boundaries."""
+def vda_forward_timed(desc, q, k, v, beta, alpha, gate, text_k, text_v, text_beta, rms_weight,
+                      out, workspace, stage_events, workspace_bytes=None, stream=None):
+    """C vda_forward_timed: as vda_forward (alpha None) or vda_forward_decay,
+    recording the six caller-created hipEvent_t handles (ints) in
+    ``stage_events`` at the stage boundaries."""
     ev = (ctypes.c_void_p * 6)(*[int(e) for e in stage_events])
     st = load_library().vda_forward_timed(
-        ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(gate), _ptr(text_k),
-        _ptr(text_v), _ptr(text_beta), _ptr(rms_weight), _ptr(out), _ptr(workspace),
-        _ws_bytes(workspace, workspace_bytes), _stream(stream), ev, len(stage_events))
+        ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(alpha), _ptr(gate),
+        _ptr(text_k), _ptr(text_v), _ptr(text_beta), _ptr(rms_weight), _ptr(out),
+        _ptr(workspace), _ws_bytes(workspace, workspace_bytes), _stream(stream), ev,
+        len(stage_events))
     _check(st, "vda_forward_timed")
 
 

@@ -281,14 +281,18 @@ int vda_forward(const vda_desc_t* desc, const void* q, const void* k, const void
 }
 
 int vda_forward_timed(const vda_desc_t* desc, const void* q, const void* k, const void* v,
-                      const float* beta, const void* gate, const void* text_k, const void* text_v,
-                      const float* text_beta, const float* rms_weight, void* out, void* workspace,
-                      size_t workspace_bytes, vda_stream_t stream, void* const* stage_events,
-                      int n_events) {
+                      const float* beta, const float* alpha, const void* gate,
+                      const void* text_k, const void* text_v, const float* text_beta,
+                      const float* rms_weight, void* out, void* workspace, size_t workspace_bytes,
+                      vda_stream_t stream, void* const* stage_events, int n_events) {
   if (!stage_events || n_events != 6) return VDA_ERR_INVALID_ARG;
   for (int i = 0; i < 6; ++i)
     if (!stage_events[i]) return VDA_ERR_INVALID_ARG;
-  return vda::forward_impl(desc, q, k, v, beta, nullptr, gate, text_k, text_v, text_beta,
+  if (alpha) {
+    const int st = vda::check_decay(desc, alpha);
+    if (st != VDA_OK) return st;
+  }
+  return vda::forward_impl(desc, q, k, v, beta, alpha, gate, text_k, text_v, text_beta,
                            rms_weight, out, workspace, workspace_bytes, stream,
                            reinterpret_cast<hipEvent_t const*>(stage_events));
 }

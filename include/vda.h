@@ -131,17 +131,18 @@ int vda_forward(const vda_desc_t* desc, const void* q, const void* k, const void
                 const float* text_beta, const float* rms_weight, void* out, void* workspace,
                 size_t workspace_bytes, vda_stream_t stream);
 
-/* vda_forward that also records caller-created HIP events (hipEvent_t, cast
- * to void*) on `stream` at the stage boundaries, for per-kernel timing:
- * stage_events[0] before the statistics kernel, [1] before the solve, [2]
- * before the chunk composition, [3] before the scan, [4] before the readout
- * and [5] after it.  n_events must be 6 and every event non-NULL.  Results
- * are identical to vda_forward. */
+/* vda_forward (alpha NULL) or vda_forward_decay (alpha non-NULL) that also
+ * records caller-created HIP events (hipEvent_t, cast to void*) on `stream`
+ * at the stage boundaries, for per-kernel timing: stage_events[0] before the
+ * statistics kernels, [1] before the solve, [2] before the chunk composition,
+ * [3] before the scan, [4] before the readout and [5] after it.  n_events
+ * must be 6 and every event non-NULL.  Results are identical to the untimed
+ * entry point. */
 int vda_forward_timed(const vda_desc_t* desc, const void* q, const void* k, const void* v,
-                      const float* beta, const void* gate, const void* text_k, const void* text_v,
-                      const float* text_beta, const float* rms_weight, void* out, void* workspace,
-                      size_t workspace_bytes, vda_stream_t stream, void* const* stage_events,
-                      int n_events);
+                      const float* beta, const float* alpha, const void* gate,
+                      const void* text_k, const void* text_v, const float* text_beta,
+                      const float* rms_weight, void* out, void* workspace, size_t workspace_bytes,
+                      vda_stream_t stream, void* const* stage_events, int n_events);
 
 /* The forward pass with channel-wise decay described at the top of this file;
  * alpha [units][frames][d_k] float32 in [0, 1], 16-byte aligned, required

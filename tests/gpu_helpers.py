@@ -116,3 +116,44 @@ def mat_rel_err(got: np.ndarray, ref: np.ndarray) -> float:
 
 
 TOL_OUT = {"f32": 1e-4, "bf16": 2e-2}
+
+
+def timed_forward_matches(d: dict, cfg: W.Config):
+    """vda_forward_timed (with decay gates when d holds them) gives bit-identical
+    output to the untimed entry point and records six completed events."""
+    import ctypes
+    import os
+    import torch
+    import frame_wise_delta_gram_amd as vda
+    ref = gpu_forward(d, cfg)
+    hip = ctypes.CDLL(os.path.join(os.path.dirname(torch.__file__), "lib", "libamdhip64.so"))
+    hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+    hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+    hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                        ctypes.c_void_p]
+    ev = []
+    for _ in range(6):
+        e = ctypes.c_void_p()
+        assert hip.hipEventCreate(ctypes.byref(e)) == 0
+        ev.append(e.value)
+    try:
+        desc = desc_for(cfg)
+        ws = workspace_for(desc)
+        out = torch.empty_like(ref)
+        vda.vda_forward_timed(desc, d["q"], d["k"], d["v"], d["beta"], d.get("alpha"), d["gate"],
+                              d["text_k"], d["text_v"], d["text_beta"], d["rms_weight"], out,
+                              ws, ev)
+        torch.cuda.synchronize()
+        total = 0.0
+        for i in range(5):
+            ms = ctypes.c_float()
+            assert hip.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(ev[i]),
+                                           ctypes.c_void_p(ev[i + 1])) == 0
+            assert ms.value >= 0.0
+            total += ms.value
+        assert total > 0.0
+        return torch.equal(out.view(torch.int16) if out.dtype == torch.bfloat16 else out,
+                           ref.view(torch.int16) if ref.dtype == torch.bfloat16 else ref)
+    finally:
+        for e in ev:
+            hip.hipEventDestroy(ctypes.c_void_p(e))

@@ -17,8 +17,8 @@ import pytest
 import oracle
 import workloads as W
 from gpu_helpers import (TOL_OUT, desc_for, gpu_forward, mat_rel_err, oracle_forward,
-                         out_to_f64, require_gpu, row_rel_err, say, to_device, to_f64,
-                         workspace_for)
+                         out_to_f64, require_gpu, row_rel_err, say, timed_forward_matches,
+                         to_device, to_f64, workspace_for)
 
 pytestmark = pytest.mark.gpu
 
@@ -216,3 +216,10 @@ def test_zero_gate_frame_cuts_the_memories(dtype):
     got2 = out_to_f64(gpu_forward(to_device(hp, cfg), cfg), cfg)
     assert np.array_equal(got2[0, 20:], got[0, 20:])
     assert not np.array_equal(got2[0, 10:14], got[0, 10:14])
+
+
+def test_timed_entry_point_matches_decay():
+    require_gpu()
+    cfg = PARITY_CASES["small-decay-bf16"]
+    say("[decay] vda_forward_timed with gates vs vda_forward_decay")
+    assert timed_forward_matches(to_device(W.host_inputs(cfg), cfg), cfg)

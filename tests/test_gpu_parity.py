@@ -10,7 +10,7 @@ import pytest
 
 import workloads as W
 from gpu_helpers import (TOL_OUT, gpu_forward, oracle_forward, out_to_f64, require_gpu,
-                         row_rel_err, say, to_device, to_f64)
+                         row_rel_err, say, timed_forward_matches, to_device, to_f64)
 
 pytestmark = pytest.mark.gpu
 
@@ -167,3 +167,10 @@ def test_bitwise_deterministic():
     b = gpu_forward(d, cfg)
     import torch
     assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def test_timed_entry_point_matches():
+    require_gpu()
+    cfg = W.CONFIGS[2]
+    say("[parity] vda_forward_timed vs vda_forward")
+    assert timed_forward_matches(to_device(W.host_inputs(cfg), cfg), cfg)
