@@ -24,7 +24,13 @@ design notes):
     state it enters with its own gate, and a query of frame t reads the bridged
     boundary states of App. A.3 Eq. (A.4) (the decay products run over the
     window frames up to and including t on each side);
-  * no boundary anchors: every frame enters both scans;
+  * no boundary anchors by default: every frame enters both scans.  With
+    anchors ([VDN] Sec. 2.1, Sec. 2.2, App. A.3, Algorithm 1 steps 2 and 7),
+    frames 0 and F - 1 are excluded from both scans, states are indexed by
+    interior frame, windows are clipped to the interior frames, the anchor rows
+    get zero output, and a query whose (unclipped) window covers the whole clip
+    bypasses the linear path (zero output), as does every row of a clip with no
+    interior frame;
   * text seed, mode 0 (default): S_T is ONE frame-wise update from S = 0 over all
     T text tokens (the prompt "as a leading virtual frame", [VDN] Sec. 5) and each
     scan starts at S_T / 2 ([VDN] Eq. (1b)).  Mode 1: the text tokens are written
@@ -43,8 +49,8 @@ import numpy as np
 
 __all__ = [
     "frame_statistics", "frame_update", "decay", "transition", "text_state", "chunk_bounds",
-    "directional_states", "gather", "window_frames", "bridge", "rms_norm", "sigmoid", "readout",
-    "forward_unit", "forward",
+    "directional_states", "gather", "window_frames", "bridge", "anchored_states",
+    "anchored_state_read", "rms_norm", "sigmoid", "readout", "forward_unit", "forward",
 ]
 
 f64 = np.float64
@@ -200,6 +206,54 @@ def bridge(P, R, f, C, radius, alpha):
     return decay(P[max(c - radius, 0)], d_f) + decay(R[min(c + radius + 1, n)], d_r)
 
 
+def anchored_states(stats, seed, alpha=None):
+    """Both directional scans with boundary anchors, [VDN] Sec. 2.2 and App. A.3.
+
+    stats: list of (A_f, B_f) for f = 0..F-1 (the anchors' entries are never
+    read).  The anchors 0 and F - 1 are excluded: P[j] is the forward state
+    through interior frame j, P[0] = seed its virtual initial state; R[j] is
+    the reverse state from the last interior frame F - 2 down to j, R[F - 1] =
+    seed.  Returns dicts P (keys 0..F-2) and R (keys 1..F-1); empty for F < 2.
+    """
+    F = len(stats)
+    if F < 2:
+        return {}, {}
+
+    def enter(S, f):
+        S_bar = S if alpha is None else decay(S, alpha[f])
+        return frame_update(S_bar, *stats[f])
+
+    P = {0: seed.copy()}
+    for j in range(1, F - 1):
+        P[j] = enter(P[j - 1], j)
+    R = {F - 1: seed.copy()}
+    for j in range(F - 2, 0, -1):
+        R[j] = enter(R[j + 1], j)
+    return P, R
+
+
+def anchored_state_read(P, R, t, C, radius, F, alpha=None):
+    """State read by the queries of frame t with anchors, [VDN] App. A.3 Eq. (A.4);
+    None where the linear path gives no output (anchor rows, Algorithm 1 step 7;
+    a window covering the clip, App. A.3 bypass).
+
+    [l, h] is the window of t's chunk clipped to the interior frames 1..F-2:
+      S~ = P[l - 1] Diag(prod_{s=l}^{t} alpha_s) + R[h + 1] Diag(prod_{s=t}^{h} alpha_s)
+    (alpha = 1: P[l - 1] + R[h + 1]).
+    """
+    if t == 0 or t == F - 1:
+        return None
+    lo, hi = window_frames(t // C, C, radius, F)
+    if lo == 0 and hi == F - 1:
+        return None
+    l, h = max(lo, 1), min(hi, F - 2)
+    if alpha is None:
+        return P[l - 1] + R[h + 1]
+    alpha = np.asarray(alpha, f64)
+    return (decay(P[l - 1], np.prod(alpha[l:t + 1], axis=0))
+            + decay(R[h + 1], np.prod(alpha[t:h + 1], axis=0)))
+
+
 def rms_norm(O, w, eps):
     """RMSNorm of each row of O over its d_v channels, scaled by w ([VDN] Eq. (1c))."""
     O = np.asarray(O, f64)
@@ -222,15 +276,20 @@ def readout(S_tilde, Q, G, w, eps):
 
 
 def forward_unit(q, k, v, beta, gate, text_k, text_v, text_beta, rms_weight,
-                 chunk=5, radius=1, eps=1e-6, seed_mode=0, taps=False, alpha=None):
+                 chunk=5, radius=1, eps=1e-6, seed_mode=0, taps=False, alpha=None,
+                 anchors=False):
     """VDA forward for one unit.
 
     q: F x U x d_k, k: F x U x d_k, v: F x U x d_v, beta: F x U,
     gate: F x U x d_v (gate logits), text_k: T x d_k, text_v: T x d_v,
     text_beta: T, rms_weight: d_v, alpha: F x d_k decay gates in [0, 1] or None
-    (alpha = 1).  Returns out (F x U x d_v), plus a dict of intermediates when
-    taps=True: A, B (per frame), M (per frame, Eq. (A.1)), seed, P, R, and with
-    decay the bridged state St read by each frame (F x d_v x d_k).
+    (alpha = 1), anchors: boundary anchors (frames 0 and F - 1).  Returns out
+    (F x U x d_v), plus a dict of intermediates when taps=True: A, B (per
+    frame), M (per frame, Eq. (A.1)), seed, P, R, and with decay or anchors the
+    state St read by each frame (F x d_v x d_k; zero where nothing is read).
+    With anchors P and R are (F - 1) x d_v x d_k arrays: P[j] through interior
+    frame j (P[0] = seed), R[j - 1] from the last interior frame down to j
+    (R[F - 2] = seed, the key F - 1 of App. A.3).
     """
     q = np.asarray(q, f64)
     k = np.asarray(k, f64)
@@ -243,6 +302,9 @@ def forward_unit(q, k, v, beta, gate, text_k, text_v, text_beta, rms_weight,
         if np.any(alpha < 0) or np.any(alpha > 1):
             raise ValueError("decay gates must lie in [0, 1]")
     seed = text_state(text_k, text_v, text_beta, d_k, d_v, seed_mode)
+    if anchors:
+        return _forward_unit_anchored(q, k, v, beta, gate, rms_weight, seed, chunk, radius,
+                                      eps, taps, alpha)
     stats = [frame_statistics(k[f], v[f], beta[f]) for f in range(F)]
     P, R = directional_states(stats, seed, chunk, alpha)
     out = np.zeros((F, U, d_v))
@@ -268,10 +330,45 @@ def forward_unit(q, k, v, beta, gate, text_k, text_v, text_beta, rms_weight,
     return out, tap
 
 
+def _forward_unit_anchored(q, k, v, beta, gate, rms_weight, seed, chunk, radius, eps, taps,
+                           alpha):
+    """forward_unit with boundary anchors ([VDN] Algorithm 1 steps 2-7): the
+    anchor frames' rows are removed from the linear inputs (their statistics
+    are never formed), the interior frames are scanned, and each interior,
+    non-bypassed query reads anchored_state_read."""
+    F, U, d_k = k.shape
+    d_v = v.shape[-1]
+    stats = [None] * F
+    for f in range(1, F - 1):
+        stats[f] = frame_statistics(k[f], v[f], beta[f])
+    P, R = anchored_states(stats, seed, alpha)
+    out = np.zeros((F, U, d_v))
+    St = np.zeros((F, d_v, d_k))
+    for t in range(F):
+        S_tilde = anchored_state_read(P, R, t, chunk, radius, F, alpha)
+        if S_tilde is None:
+            continue  # zero output row
+        St[t] = S_tilde
+        out[t] = readout(S_tilde, q[t], gate[t], rms_weight, eps)
+    if not taps:
+        return out
+    zero_a, zero_b = np.zeros((d_k, d_k)), np.zeros((d_v, d_k))
+    A = np.array([s[0] if s is not None else zero_a for s in stats]).reshape(F, d_k, d_k)
+    B = np.array([s[1] if s is not None else zero_b for s in stats]).reshape(F, d_v, d_k)
+    Mt = [transition(A[f], None if alpha is None or stats[f] is None else alpha[f])
+          for f in range(F)]
+    tap = {"A": A, "B": B, "M": np.array(Mt).reshape(F, d_k, d_k), "seed": seed, "St": St,
+           "P": np.array([P[j] for j in range(F - 1)]).reshape(max(F - 1, 0), d_v, d_k),
+           "R": np.array([R[j] for j in range(1, F)]).reshape(max(F - 1, 0), d_v, d_k)}
+    return out, tap
+
+
 def forward(q, k, v, beta, gate, text_k, text_v, text_beta, rms_weight,
-            chunk=5, radius=1, eps=1e-6, seed_mode=0, taps=False, units=None, alpha=None):
+            chunk=5, radius=1, eps=1e-6, seed_mode=0, taps=False, units=None, alpha=None,
+            anchors=False):
     """VDA forward over all units (leading axis of every per-unit tensor;
-    alpha: units x F x d_k decay gates, or None for alpha = 1).
+    alpha: units x F x d_k decay gates, or None for alpha = 1; anchors: boundary
+    anchors, see forward_unit).
 
     ``units`` restricts the work to a subset of unit indices; the result then
     holds only those units, in that order.
@@ -281,7 +378,7 @@ def forward(q, k, v, beta, gate, text_k, text_v, text_beta, rms_weight,
     for u in idx:
         r = forward_unit(q[u], k[u], v[u], beta[u], gate[u], text_k[u], text_v[u],
                          text_beta[u], rms_weight, chunk, radius, eps, seed_mode, taps,
-                         None if alpha is None else alpha[u])
+                         None if alpha is None else alpha[u], anchors)
         if taps:
             outs.append(r[0])
             tapl.append(r[1])

@@ -19,7 +19,10 @@ facts come from "Video DeltaNet" (arXiv 2609.20744), cited as [VDN]:
   * Sec. 3.1 Eq. (2), App. A.1 and A.3: with channel-wise decay the inherited
     state is S Diag(alpha), Prop. 1 still holds, and with no writes the decay
     bridge telescopes to a closed form;
-  * Eq. (1c): RMSNorm then an element-wise sigmoid gate.
+  * Eq. (1c): RMSNorm then an element-wise sigmoid gate;
+  * Sec. 2.1, Sec. 2.2, App. A.3 and Algorithm 1: boundary anchors (frames 0 and
+    F - 1) are left out of both states, get no linear output, and a window that
+    covers the clip bypasses the linear path.
 
 None of these re-types the oracle's own formula: gradients and objectives are
 evaluated token by token, least squares goes through numpy's SVD-based solver,
@@ -726,6 +729,162 @@ def pin_decay_chunk_composition(o):
     assert asym > 1e-3
 
 
+# ----------------------------------------------------------------------------- NEXT-2: anchors
+def _anchor_cases():
+    # (F, C, r): interior chunks, clipped windows on both sides, a short last chunk
+    return ((13, 5, 1), (16, 5, 1), (9, 2, 1), (12, 3, 0), (11, 1, 2), (21, 5, 1))
+
+
+def pin_anchor_rows_zero(o):
+    """Algorithm 1 step 7 and App. A.3: the anchor rows (frames 0 and F - 1) get
+    no linear output, and a clip made only of anchors (F <= 2) gets none at all."""
+    rng = _rng(41)
+    for F, C, r in _anchor_cases():
+        x = _random_unit(rng, F, 3, 4, 3, 2)
+        for alpha in (None, _random_alpha(rng, F, 4)):
+            out = _call(o, x, chunk=C, radius=r, alpha=alpha, anchors=True)
+            assert np.all(out[0] == 0.0) and np.all(out[F - 1] == 0.0), (F, C, r)
+    for F in (1, 2):
+        x = _random_unit(rng, F, 3, 4, 3, 2)
+        out = _call(o, x, chunk=5, radius=1, anchors=True)
+        assert out.shape == (F, 3, 3) and np.all(out == 0.0)
+
+
+def pin_anchor_inputs_ignored(o):
+    """Sec. 2.2 / Algorithm 1 step 2: the anchor frames' rows are removed from the
+    linear inputs, so redrawing their keys, values, write strengths, queries,
+    gate logits and decay gates changes no output at all (bit for bit)."""
+    rng = _rng(42)
+    for F, C, r in _anchor_cases():
+        x = _random_unit(rng, F, 3, 4, 3, 2)
+        alpha = _random_alpha(rng, F, 4)
+        out = _call(o, x, chunk=C, radius=r, alpha=alpha, anchors=True)
+        y = {key: val.copy() for key, val in x.items()}
+        a2 = alpha.copy()
+        other = _random_unit(rng, F, 3, 4, 3, 2)
+        for key in ("q", "k", "v", "beta", "gate"):
+            y[key][0] = other[key][0]
+            y[key][F - 1] = other[key][F - 1]
+        a2[0] = rng.uniform(0, 1, 4)
+        a2[F - 1] = rng.uniform(0, 1, 4)
+        out2 = _call(o, y, chunk=C, radius=r, alpha=a2, anchors=True)
+        assert np.array_equal(out, out2), (F, C, r)
+
+
+def pin_anchor_identity_frames(o):
+    """An anchor left out of both scans is the identity map S -> S: with anchors,
+    every interior, non-bypassed row equals the anchor-free forward pass whose
+    anchor frames write nothing (beta = 0: Eq. (5) gives S (I + 0) = S_bar) and
+    do not decay (alpha = 1), because clipping the window to the interior frames
+    then only drops identity factors from the bridge (App. A.3)."""
+    rng = _rng(43)
+    for F, C, r in _anchor_cases():
+        x = _random_unit(rng, F, 4, 5, 3, 3)
+        for alpha in (None, _random_alpha(rng, F, 5)):
+            out = _call(o, x, chunk=C, radius=r, alpha=alpha, anchors=True)
+            y = {key: val.copy() for key, val in x.items()}
+            y["beta"][0] = 0.0
+            y["beta"][F - 1] = 0.0
+            a2 = None
+            if alpha is not None:
+                a2 = alpha.copy()
+                a2[0] = 1.0
+                a2[F - 1] = 1.0
+            ref = _call(o, y, chunk=C, radius=r, alpha=a2)
+            live = [t for t in range(1, F - 1) if np.any(out[t] != 0.0)]
+            assert live, (F, C, r)
+            for t in live:
+                assert np.max(np.abs(out[t] - ref[t])) <= 1e-12, (F, C, r, t)
+
+
+def pin_anchor_bypass(o):
+    """App. A.3: a query whose window (chunks c - r .. c + r) covers the whole clip
+    bypasses the linear path.  Hand-enumerated zero rows for four clips."""
+    rng = _rng(44)
+    cases = {  # (F, C, r): frames with zero output (anchors included)
+        (10, 5, 1): set(range(10)),         # both chunks' windows span frames 0..9
+        (11, 5, 1): {0, 5, 6, 7, 8, 9, 10},  # chunk 1's window spans 0..10
+        (16, 5, 1): {0, 15},                 # no window spans the clip
+        (3, 1, 1): {0, 1, 2},                # frame 1's window spans 0..2
+    }
+    for (F, C, r), zero in cases.items():
+        x = _random_unit(rng, F, 3, 4, 3, 2)
+        out = _call(o, x, chunk=C, radius=r, anchors=True)
+        for t in range(F):
+            if t in zero:
+                assert np.all(out[t] == 0.0), (F, C, r, t)
+            else:
+                assert np.all(np.abs(out[t]).max(axis=-1) > 0), (F, C, r, t)
+
+
+def pin_anchor_scalar(o):
+    """d_k = d_v = 1, exact rational arithmetic, App. A.3 written out by hand: the
+    interior frames 1..F-2 map s -> (alpha s + b) / (1 + a); P_0 = R_{F-1} = seed;
+    P_j through interior frame j, R_j from frame F-2 down to j; frame t reads
+    P_{l-1} prod_{l..t} alpha + R_{h+1} prod_{t..h} alpha over its window [l, h]
+    clipped to 1..F-2 (F = 7, chunks of 2, radius 0)."""
+    Fr = Fraction
+    v = [Fr(5), Fr(1), Fr(-2), Fr(3), Fr(1, 2), Fr(-1), Fr(7)]
+    beta = [Fr(3), Fr(1, 2), Fr(1), Fr(1, 4), Fr(2), Fr(1, 3), Fr(4)]
+    alpha = [Fr(1, 9), Fr(1, 2), Fr(3, 4), Fr(1), Fr(1, 5), Fr(2, 3), Fr(1, 7)]
+    tv, tb = Fr(2), Fr(1)
+    F, C = 7, 2
+    seed = tb * tv / (1 + tb) / 2
+    step = lambda s, f: (alpha[f] * s + beta[f] * v[f]) / (1 + beta[f])  # noqa: E731
+    P = {0: seed}
+    for j in range(1, F - 1):
+        P[j] = step(P[j - 1], j)
+    R = {F - 1: seed}
+    for j in range(F - 2, 0, -1):
+        R[j] = step(R[j + 1], j)
+
+    def prod(a, b):
+        out = Fr(1)
+        for g in range(a, b + 1):
+            out *= alpha[g]
+        return out
+    windows = {1: (1, 1), 2: (2, 3), 3: (2, 3), 4: (4, 5), 5: (4, 5)}  # chunk [2c, 2c+1] clipped
+    St = [Fr(0)] * F
+    for t, (lo, hi) in windows.items():
+        St[t] = P[lo - 1] * prod(lo, t) + R[hi + 1] * prod(t, hi)
+    k = np.ones((F, 1, 1))
+    q = np.ones((F, 1, 1))
+    _, tap = o.forward_unit(q, k, np.array([float(x) for x in v]).reshape(F, 1, 1),
+                            np.array([float(x) for x in beta]).reshape(F, 1),
+                            np.zeros((F, 1, 1)), np.ones((1, 1)), np.array([[float(tv)]]),
+                            np.array([float(tb)]), np.ones(1), chunk=C, radius=0, taps=True,
+                            alpha=np.array([float(x) for x in alpha]).reshape(F, 1),
+                            anchors=True)
+    assert np.max(np.abs(tap["St"].ravel() - np.array([float(x) for x in St]))) <= 1e-15
+    assert np.max(np.abs(tap["P"].ravel() - np.array([float(P[j]) for j in range(F - 1)]))) \
+        <= 1e-15
+    assert np.max(np.abs(tap["R"].ravel() - np.array([float(R[j]) for j in range(1, F)]))) \
+        <= 1e-15
+
+
+def pin_anchor_disjointness(o):
+    """Sec. 2.2 with anchors: one writing interior frame f*, no text.  A live query
+    frame t (interior, not bypassed) reads f* iff f* lies outside t's window; an
+    anchor's write is never read."""
+    rng = _rng(45)
+    for F, C, r in ((16, 5, 1), (13, 3, 1), (9, 2, 0)):
+        for fstar in range(F):
+            x = _random_unit(rng, F, 3, 4, 3, 0)
+            x["beta"][:] = 0.0
+            x["beta"][fstar] = rng.uniform(0.3, 1.0, 3)
+            out = _call(o, x, chunk=C, radius=r, anchors=True)
+            for t in range(1, F - 1):
+                c = t // C
+                lo, hi = C * max(c - r, 0), min(C * (c + r + 1), F) - 1
+                if lo == 0 and hi == F - 1:
+                    continue
+                seen = 0 < fstar < F - 1 and not (lo <= fstar <= hi)
+                if seen:
+                    assert np.all(np.abs(out[t]).max(axis=-1) > 0), (F, C, r, fstar, t)
+                else:
+                    assert np.all(out[t] == 0.0), (F, C, r, fstar, t)
+
+
 ALL_PINS = [
     pin_stats_hand_loop, pin_stats_invariants, pin_gradient_zero, pin_lstsq_bruteforce,
     pin_sherman_morrison, pin_repeated_keys, pin_orthonormal_keys, pin_beta_zero,
@@ -734,4 +893,6 @@ ALL_PINS = [
     pin_golden_scan, pin_token_permutation, pin_all_beta_zero, pin_rmsnorm_gate,
     pin_decay_update, pin_decay_one, pin_decay_pure_bridge, pin_decay_zero, pin_decay_scalar,
     pin_decay_non_expansive, pin_decay_time_reversal, pin_decay_chunk_composition,
+    pin_anchor_rows_zero, pin_anchor_inputs_ignored, pin_anchor_identity_frames,
+    pin_anchor_bypass, pin_anchor_scalar, pin_anchor_disjointness,
 ]

@@ -253,6 +253,67 @@ def _transition_decay_right(m):
     m.transition = transition
 
 
+def _read_variant(m, rows_kept=False, no_bypass=False, rev_early=False, gate_from_window=False,
+                  interior_chunks=False):
+    def anchored_state_read(P, R, t, C, radius, F, alpha=None):
+        if (t == 0 or t == F - 1) and not rows_kept:
+            return None
+        c = (t - 1) // C if interior_chunks else t // C
+        lo, hi = m.window_frames(max(c, 0), C, radius, F)
+        if lo == 0 and hi == F - 1 and not no_bypass:
+            return None
+        l, h = max(lo, 1), min(hi, F - 2)
+        rk = h if rev_early else h + 1
+        a0 = lo if gate_from_window else l
+        if alpha is None:
+            return P[l - 1] + R[max(rk, 1)]
+        alpha = np.asarray(alpha, float)
+        return (m.decay(P[l - 1], np.prod(alpha[a0:t + 1], axis=0))
+                + m.decay(R[max(rk, 1)], np.prod(alpha[t:h + 1], axis=0)))
+    m.anchored_state_read = anchored_state_read
+
+
+def _anchor_rows_kept(m):
+    _read_variant(m, rows_kept=True)
+
+
+def _anchor_no_bypass(m):
+    _read_variant(m, no_bypass=True)
+
+
+def _anchor_reverse_read_early(m):
+    _read_variant(m, rev_early=True)
+
+
+def _anchor_bridge_from_unclipped_window(m):
+    _read_variant(m, gate_from_window=True)
+
+
+def _anchor_chunks_over_interior(m):
+    _read_variant(m, interior_chunks=True)
+
+
+def _anchor_reverse_scan_skips_frame(m):
+    def anchored_states(stats, seed, alpha=None):
+        F = len(stats)
+        if F < 2:
+            return {}, {}
+
+        def enter(S, f):
+            S_bar = S if alpha is None else m.decay(S, alpha[f])
+            return m.frame_update(S_bar, *stats[f])
+        P = {0: seed.copy()}
+        for j in range(1, F - 1):
+            P[j] = enter(P[j - 1], j)
+        R = {F - 1: seed.copy()}
+        if F > 2:
+            R[F - 2] = seed.copy()  # slip: the last interior frame never written
+        for j in range(F - 3, 0, -1):
+            R[j] = enter(R[j + 1], j)
+        return P, R
+    m.anchored_states = anchored_states
+
+
 MUTATIONS = {f.__name__.lstrip("_"): f for f in [
     _stats_no_beta, _stats_beta_squared, _stats_b_swapped, _update_minus, _update_no_identity,
     _update_drops_inherited, _update_frozen_state, _update_left_multiplied, _seed_not_halved,
@@ -260,7 +321,9 @@ MUTATIONS = {f.__name__.lstrip("_"): f for f in [
     _forward_scan_skips_last_frame, _rms_sum_not_mean, _rms_wrong_axis, _sigmoid_sign,
     _readout_transposed, _transition_wrong, _decay_after_solve, _reverse_uses_next_gate,
     _forward_ignores_decay, _decay_on_rows, _bridge_excludes_query_frame, _bridge_omitted,
-    _bridge_products_swapped, _transition_decay_right,
+    _bridge_products_swapped, _transition_decay_right, _anchor_rows_kept, _anchor_no_bypass,
+    _anchor_reverse_read_early, _anchor_bridge_from_unclipped_window,
+    _anchor_chunks_over_interior, _anchor_reverse_scan_skips_frame,
 ]}
 
 
