@@ -36,6 +36,12 @@
 // the two channel-wise products are formed in LDS by the workgroup before the
 // gather, and the gather scales P's and R's columns by them.
 //
+// Boundary anchors (Sec. 2.1, App. A.3, Algorithm 1 step 7): frames 0 and F - 1
+// wrote nothing into the states (they are identity frames there, so the
+// chunk-indexed states and the window clipped to the interior frames agree),
+// carry no gate in the bridge products, and their rows are written as zeros,
+// as are all rows of a segment whose window spans the whole clip (bypass).
+//
 // fp32 path: the same computation on the vector ALUs in fp32.
 #include "vda_device.h"
 #include "vda_internal.h"
@@ -52,7 +58,7 @@ constexpr int kRows = 8 * 16 * kGroups;   // token rows per workgroup
 // column k), D[128 + k] = prod_{s=f}^{h} alpha_s[k] (R's); zero past d_k.  The
 // gates are read eight frames at a time (independent loads).
 __device__ __forceinline__ void bridge_products(float* D, const float* alpha, int u, int f, int c,
-                                                int F, int C, int radius, int dk) {
+                                                int F, int C, int radius, int dk, int anchors) {
   const int t = threadIdx.x;
   if (t >= 256) return;
   const int k = t & 127;
@@ -67,12 +73,33 @@ __device__ __forceinline__ void bridge_products(float* D, const float* alpha, in
     for (int s = s0; s <= s1; s += 8) {
       float x[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) x[i] = s + i <= s1 ? a[(size_t)(s + i) * dk] : 1.0f;
+      for (int i = 0; i < 8; ++i) {
+        const int g = s + i;
+        const bool one = g > s1 || (anchors && (g == 0 || g == F - 1));
+        x[i] = one ? 1.0f : a[(size_t)g * dk];
+      }
 #pragma unroll
       for (int i = 0; i < 8; ++i) d *= x[i];
     }
   }
   D[t] = k < dk ? d : 0.0f;
+}
+
+// Rows of a segment (frames f0 .. f1-1 of chunk c, U rows each) that get linear
+// output: [zlo, zhi).  Without anchors, all of them.  With anchors, none when
+// the window (chunks c - radius .. c + radius) spans the whole clip, else all
+// but the rows of frames 0 and F - 1.
+__device__ __forceinline__ void live_rows(int anchors, int f0, int f1, int c, int F, int U, int C,
+                                          int radius, long rows_total, long& zlo, long& zhi) {
+  zlo = 0;
+  zhi = rows_total;
+  if (!anchors) return;
+  if (c - radius <= 0 && (long)C * (c + radius + 1) >= F) {
+    zhi = 0;
+    return;
+  }
+  if (f0 == 0) zlo = U;
+  if (f1 == F) zhi = (long)(F - 1 - f0) * U;
 }
 
 // DK, DV > 0: compile-time d_k and d_v (the common 128 case); 0: runtime.
@@ -83,7 +110,7 @@ __global__ __launch_bounds__(512, 4) void readout_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ gate,
     const float* __restrict__ wrms, uint16_t* __restrict__ out, const float* __restrict__ ST,
     const float* __restrict__ alpha, int dk_rt, int dv_rt, int F, int U, int C, int radius, int n,
-    float eps, int units, int nseg, int nblk, unsigned per) {
+    float eps, int units, int nseg, int nblk, unsigned per, int anchors) {
   const int dk = DK > 0 ? DK : dk_rt;
   const int dv = DV > 0 ? DV : dv_rt;
   __shared__ __align__(16) uint16_t Shi[128 * 136];
@@ -104,6 +131,8 @@ __global__ __launch_bounds__(512, 4) void readout_bf16_kernel(
   const long rows_total = (long)(f1 - f0) * U;
   const long row0 = (long)blk * kRows;
   if (row0 >= rows_total) return;
+  long zlo, zhi;  // rows [zlo, zhi) of the segment get linear output
+  live_rows(anchors, f0, f1, c, F, U, C, radius, rows_total, zlo, zhi);
 
   const int t = threadIdx.x;
   const int lane = t & 63;
@@ -116,7 +145,7 @@ __global__ __launch_bounds__(512, 4) void readout_bf16_kernel(
 
   if (t < 128) Ws[t] = t < dv ? wrms[t] : 0.0f;
   if (DECAY) {
-    bridge_products(Dbr, alpha, u, f0, c, F, C, radius, dk);
+    bridge_products(Dbr, alpha, u, f0, c, F, C, radius, dk, anchors);
     __syncthreads();
   }
   // gather S~ and split it into bf16 hi + lo, rows permuted (see header);
@@ -246,6 +275,7 @@ __global__ __launch_bounds__(512, 4) void readout_bf16_kernel(
     ss += __shfl_xor(ss, 32);
     const float inv = rsqrtf(ss * inv_dv + eps);
     const long myrow = rg + jl;
+    const bool live = myrow >= zlo && myrow < zhi;
     if (myrow < rows_total) {
       const size_t grow = chunk_row0 + (size_t)myrow;
 #pragma unroll
@@ -262,7 +292,7 @@ __global__ __launch_bounds__(512, 4) void readout_bf16_kernel(
           const float gl = (e & 1) ? bf16_hi(gv[e >> 1]) : bf16_lo(gv[e >> 1]);
           const float ww = e < 4 ? w0[e] : w1[e - 4];
           const float sig = __builtin_amdgcn_rcpf(1.0f + __expf(-gl));
-          y[e] = o * inv * ww * sig;
+          y[e] = live ? o * inv * ww * sig : 0.0f;
         }
         u32x4_t ov;
 #pragma unroll
@@ -298,7 +328,7 @@ constexpr int kRowsF = 64;
 __global__ __launch_bounds__(256) void readout_f32_kernel(
     const float* __restrict__ q, const float* __restrict__ gate, const float* __restrict__ wrms,
     float* __restrict__ out, const float* __restrict__ ST, const float* __restrict__ alpha, int dk,
-    int dv, int F, int U, int C, int radius, int n, float eps, int nseg, int nblk) {
+    int dv, int F, int U, int C, int radius, int n, float eps, int nseg, int nblk, int anchors) {
   __shared__ float Ss[128 * SG];
   __shared__ float Qs[kRowsF * SG];
   __shared__ float Dbr[256];
@@ -313,6 +343,8 @@ __global__ __launch_bounds__(256) void readout_f32_kernel(
   const long rows_total = (long)(f1 - f0) * U;
   const long row0 = (long)blk * kRowsF;
   if (row0 >= rows_total) return;
+  long zlo, zhi;
+  live_rows(anchors, f0, f1, c, F, U, C, radius, rows_total, zlo, zhi);
   const int t = threadIdx.x;
   const size_t SS = (size_t)dv * dk;
   const int pi = max(c - radius, 0);
@@ -320,7 +352,7 @@ __global__ __launch_bounds__(256) void readout_f32_kernel(
   const float* P = ST + ((size_t)(u * 2 + 0) * (n + 1) + pi) * SS;
   const float* R = ST + ((size_t)(u * 2 + 1) * (n + 1) + ri) * SS;
   if (decay) {
-    bridge_products(Dbr, alpha, u, f0, c, F, C, radius, dk);
+    bridge_products(Dbr, alpha, u, f0, c, F, C, radius, dk, anchors);
     __syncthreads();
   }
   for (int idx = t; idx < dv * dk; idx += 256) {
@@ -355,12 +387,13 @@ __global__ __launch_bounds__(256) void readout_f32_kernel(
   const float inv = 1.0f / sqrtf(ss / (float)dv + eps);
   if (myrow < rows_total) {
     const size_t grow = chunk_row0 + (size_t)myrow;
+    const bool live = myrow >= zlo && myrow < zhi;
 #pragma unroll
     for (int j = 0; j < 32; ++j) {
       const int ch = part + 4 * j;
       if (ch < dv) {
         const float gl = gate[grow * dv + ch];
-        out[grow * dv + ch] = wrms[ch] * o[j] * inv / (1.0f + expf(-gl));
+        out[grow * dv + ch] = live ? wrms[ch] * o[j] * inv / (1.0f + expf(-gl)) : 0.0f;
       }
     }
   }
@@ -376,7 +409,7 @@ void launch_readout_bf16(const Plan& p, const void* q, const void* gate, const f
   hipLaunchKernelGGL((readout_bf16_kernel<DK, DV, DECAY>), dim3(kXcds * per), dim3(kThreadsR), 0,
                      s, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(gate),
                      rms_weight, static_cast<uint16_t*>(out), w.ST, alpha, p.dk, p.dv, p.F, p.U,
-                     p.C, p.r, p.n, p.eps, p.units, nseg, nblk, per);
+                     p.C, p.r, p.n, p.eps, p.units, nseg, nblk, per, p.anchors);
 }
 
 hipError_t launch_readout(const Plan& p, const void* q, const void* gate, const float* rms_weight,
@@ -400,7 +433,7 @@ hipError_t launch_readout(const Plan& p, const void* q, const void* gate, const 
     hipLaunchKernelGGL(readout_f32_kernel, dim3(items), dim3(kThreads), 0, s,
                        static_cast<const float*>(q), static_cast<const float*>(gate), rms_weight,
                        static_cast<float*>(out), w.ST, alpha, p.dk, p.dv, p.F, p.U, p.C, p.r, p.n,
-                       p.eps, nseg, nblk);
+                       p.eps, nseg, nblk, p.anchors);
   }
   return hipGetLastError();
 }

@@ -65,7 +65,8 @@ __global__ __launch_bounds__(256, 1) void compose_kernel(const float* __restrict
                                                         float* __restrict__ Jf,
                                                         float* __restrict__ Jr,
                                                         float* __restrict__ ST, int dk, int dv,
-                                                        int F, int C, int n, float seed_scale) {
+                                                        int F, int C, int n, float seed_scale,
+                                                        int anchors) {
   __shared__ float Xs[128 * SG];
   __shared__ float Ms[128 * SG];
   const int c = blockIdx.x;
@@ -92,9 +93,11 @@ __global__ __launch_bounds__(256, 1) void compose_kernel(const float* __restrict
   auto frame = [&](int s) { return reverse ? f1 - 1 - s : f0 + s; };
   auto Mp = [&](int f) { return Mw + ((size_t)u * Fp1 + f + 1) * dk * dk; };
   auto Bp = [&](int f) { return Bw + ((size_t)u * Fp1 + f + 1) * dv * dk; };
-  // decay gate of latent frame f, key channel j (1 without decay)
+  // decay gate of latent frame f, key channel j (1 without decay and for the
+  // boundary anchors, which leave the states alone)
   auto gate = [&](int f, int j) {
-    return alpha && j < dk ? alpha[((size_t)u * F + f) * dk + j] : 1.0f;
+    const bool anchor = anchors && (f == 0 || f == F - 1);
+    return alpha && j < dk && !anchor ? alpha[((size_t)u * F + f) * dk + j] : 1.0f;
   };
 
   {
@@ -425,7 +428,7 @@ __global__ __launch_bounds__(512, 1) void compose_split_kernel(
     const float* __restrict__ Bw, const float* __restrict__ Mw, const float* __restrict__ alpha,
     float* __restrict__ Mc, float* __restrict__ McT, float* __restrict__ MrT,
     float* __restrict__ Jf, float* __restrict__ Jr, float* __restrict__ ST, int dk, int dv, int F,
-    int C, int n, int units, unsigned per, float seed_scale) {
+    int C, int n, int units, unsigned per, float seed_scale, int anchors) {
   __shared__ __align__(16) __bf16 Xh[128 * SB];
   __shared__ __align__(16) __bf16 Xl[128 * SB];
   __shared__ __align__(16) __bf16 Mh[128 * SB];
@@ -457,12 +460,14 @@ __global__ __launch_bounds__(512, 1) void compose_split_kernel(
   auto Mp = [&](int f) { return Mw + ((size_t)u * Fp1 + f + 1) * dk * dk; };
   auto Bp = [&](int f) { return Bw + ((size_t)u * Fp1 + f + 1) * SS; };
   auto Ap = [&](int f) { return alpha + ((size_t)u * F + f) * dk; };
+  // boundary anchors carry no gate (the identity)
+  auto anchor = [&](int f) { return anchors && (f == 0 || f == F - 1); };
   const bool active = jr < dk && xr0 < rows;
 
   RowsF32<8> mf;
   rows_load<8, 16>(mf, Mp(frame(0)), dk, jr, 64 * kh);
   x_fill(Xh, Xl, mchain ? nullptr : Bp(frame(0)), mchain ? 0 : dv, dk, seed ? seed_scale : 1.0f,
-         DECAY && mchain ? Ap(frame(0)) : nullptr);
+         DECAY && mchain && !anchor(frame(0)) ? Ap(frame(0)) : nullptr);
   rows_split<8, 16>(Mh, Ml, 0, mf, dk, jr, 64 * kh);
   __syncthreads();
 
@@ -482,10 +487,12 @@ __global__ __launch_bounds__(512, 1) void compose_split_kernel(
       rows_load<8, 16>(mf, Mp(frame(s + 1)), dk, jr, 64 * kh);
       if (!mchain) rows_prefetch_t<2>(bq, Bp(frame(s + 1)), dv, dk, xr0, jr);
       if (DECAY) {
+        const bool one = anchor(frame(s + 1));
 #pragma unroll
         for (int q = 0; q < 4; ++q)
-          aq[q] = *reinterpret_cast<const f32x4_t*>(
-              Ap(frame(s + 1)) + min(jr + 8 * q + 4 * (lane >> 5), dk - 4));
+          aq[q] = one ? f32x4_t{1.0f, 1.0f, 1.0f, 1.0f}
+                      : *reinterpret_cast<const f32x4_t*>(
+                            Ap(frame(s + 1)) + min(jr + 8 * q + 4 * (lane >> 5), dk - 4));
       }
     }
     f32x16_t acc[2] = {zero16(), zero16()};
@@ -614,7 +621,7 @@ void launch_compose_split(const Plan& p, const WsPtrs& w, const float* alpha, fl
   const unsigned per = xcd_per((unsigned)p.units * (p.n * (DECAY ? 4 : 3) + 1));
   hipLaunchKernelGGL((compose_split_kernel<FULL, DECAY>), dim3(kXcds * per), dim3(512), 0, s, w.B,
                      w.M, alpha, w.Mc, w.McT, w.MrT, w.Jf, w.Jr, w.ST, p.dk, p.dv, p.F, p.C, p.n,
-                     p.units, per, seed_scale);
+                     p.units, per, seed_scale, p.anchors);
 }
 
 hipError_t launch_compose(const Plan& p, const WsPtrs& w, const float* alpha, hipStream_t s) {
@@ -629,7 +636,7 @@ hipError_t launch_compose(const Plan& p, const WsPtrs& w, const float* alpha, hi
   } else {
     hipLaunchKernelGGL(compose_kernel, dim3(p.n, p.units, alpha ? 5 : 4), dim3(kThreads), 0, s,
                        w.B, w.M, alpha, w.Mc, w.McT, w.MrT, w.Jf, w.Jr, w.ST, p.dk, p.dv, p.F, p.C,
-                       p.n, seed_scale);
+                       p.n, seed_scale, p.anchors);
   }
   return hipGetLastError();
 }

@@ -90,7 +90,7 @@ template <int DK, int DV>
 __global__ __launch_bounds__(512, 1) void stats_bf16_kernel(
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, const float* __restrict__ beta,
     float* __restrict__ Aout, float* __restrict__ Bout, int F, int U, int dk_rt, int dv_rt,
-    int nframes) {
+    int nframes, int anchors) {
   const int dk = DK > 0 ? DK : dk_rt;
   const int dv = DV > 0 ? DV : dv_rt;
   __shared__ __align__(16) unsigned char smem[2 * kStageBytes];
@@ -107,8 +107,12 @@ __global__ __launch_bounds__(512, 1) void stats_bf16_kernel(
     const float* b;
     int ntok;
   };
+  // boundary anchors (frames 0 and F - 1) write nothing: read as empty frames
   auto frame_src = [&](int g) {
-    return FrameSrc{k + (size_t)g * U * dk, v + (size_t)g * U * dv, beta + (size_t)g * U, U};
+    const int f = g % F;
+    const bool anchor = anchors && (f == 0 || f == F - 1);
+    return FrameSrc{k + (size_t)g * U * dk, v + (size_t)g * U * dv, beta + (size_t)g * U,
+                    anchor ? 0 : U};
   };
   auto ntiles_of = [&](int ntok) { return ntok > 0 ? (ntok + kTok - 1) / kTok : 1; };
   // tile cursor: frame g (>= nframes past this workgroup's last frame), tile i
@@ -426,7 +430,7 @@ __global__ __launch_bounds__(256) void stats_f32_kernel(
     const float* __restrict__ k, const float* __restrict__ v, const float* __restrict__ beta,
     const float* __restrict__ tk, const float* __restrict__ tv, const float* __restrict__ tb,
     float* __restrict__ Aout, float* __restrict__ Bout, int F, int U, int T, int dk, int dv,
-    float text_scale) {
+    float text_scale, int anchors) {
   __shared__ float Xs[kTokF * kXS];
   __shared__ float Bs[kTokF * kBS];
 
@@ -449,7 +453,7 @@ __global__ __launch_bounds__(256) void stats_f32_kernel(
     sk = k + fr * U * dk;
     sv = v + fr * U * dv;
     sb = beta + fr * U;
-    ntok = U;
+    ntok = anchors && (fi == 1 || fi == F) ? 0 : U;  // boundary anchors write nothing
     bscale = 1.0f;
   }
   // thread t accumulates rows 16*(t/16) .. +15 of [K | V] channels x key columns 8*(t%16) .. +7
@@ -536,12 +540,12 @@ hipError_t launch_stats(const Plan& p, const void* k, const void* v, const float
     auto kern = (p.dk == 128 && p.dv == 128) ? stats_bf16_kernel<128, 128> : stats_bf16_kernel<0, 0>;
     hipLaunchKernelGGL(kern, dim3(P), dim3(kStatsThreads), 0, s,
                        static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), beta, w.A,
-                       w.B, p.F, p.U, p.dk, p.dv, nframes);
+                       w.B, p.F, p.U, p.dk, p.dv, nframes, p.anchors);
   } else {
     hipLaunchKernelGGL(stats_f32_kernel, grid, dim3(kThreads), 0, s,
                        static_cast<const float*>(k), static_cast<const float*>(v), beta,
                        static_cast<const float*>(text_k), static_cast<const float*>(text_v),
-                       text_beta, w.A, w.B, p.F, p.U, p.T, p.dk, p.dv, ts);
+                       text_beta, w.A, w.B, p.F, p.U, p.T, p.dk, p.dv, ts, p.anchors);
   }
   return hipGetLastError();
 }

@@ -32,6 +32,7 @@ int make_plan(const vda_desc_t* d, Plan* p) {
   if (d->chunk < 1 || d->radius < 0) return VDA_ERR_INVALID_ARG;
   if (!(d->rms_eps >= 0.0f) || !isfinite(d->rms_eps)) return VDA_ERR_INVALID_ARG;
   if (d->seed_mode != 0 && d->seed_mode != 1) return VDA_ERR_INVALID_ARG;
+  if (d->anchors != 0 && d->anchors != 1) return VDA_ERR_INVALID_ARG;
   if (d->units > kMaxGridYZ) return VDA_ERR_INVALID_ARG;
   const int64_t n = d->frames > 0 ? (d->frames + (int64_t)d->chunk - 1) / d->chunk : 0;
   if (n > kMaxGridYZ) return VDA_ERR_INVALID_ARG;
@@ -76,6 +77,7 @@ int make_plan(const vda_desc_t* d, Plan* p) {
   p->n = (int)n;
   p->eps = d->rms_eps;
   p->seed_mode = d->seed_mode;
+  p->anchors = d->anchors;
   p->dtype = d->in_dtype;
 
   const size_t U_ = (size_t)p->units, Fp1 = (size_t)p->F + 1, N = (size_t)p->n;

@@ -24,6 +24,7 @@ struct Plan {
   int units, F, U, T, dk, dv, C, r, n;
   float eps;
   int seed_mode, dtype;
+  int anchors;    // 1: frames 0 and F - 1 are boundary anchors
   bool decay_ok;  // the decay path's launch grids fit too
   size_t off[9];
   size_t total;

@@ -38,6 +38,15 @@
  *           + R[min(c + radius + 1, n)] Diag(prod_{s=t}^{h} alpha_s).
  * The text seed is unchanged (the text state starts from zero).
  *
+ * Boundary anchors (desc->anchors = 1; [VDN] Sec. 2.1, Sec. 2.2, App. A.3 and
+ * Algorithm 1 steps 2 and 7): frames 0 and F - 1 are left out of both scans
+ * (their k, v, beta and alpha are never read), so the states are those of the
+ * interior frames 1..F-2 with P_0 = R_{F-1} = seed, a query's window is
+ * clipped to the interior frames, the anchor rows of `out` are zero, and so is
+ * every row whose window (chunks c - radius .. c + radius) spans the whole clip
+ * (the linear path is bypassed there); a clip of at most two frames has only
+ * zero rows.  An anchor frame therefore acts on the states as the identity.
+ *
  * Layouts (row-major, last index fastest, all tensors contiguous):
  *   q     [units][frames][tokens][d_k]   in_dtype
  *   k     [units][frames][tokens][d_k]   in_dtype (prepared features)
@@ -105,6 +114,7 @@ typedef struct vda_desc {
   int32_t seed_mode;   /* 0: seed = S_T / 2 ([VDN] Eq. (1b)); 1: text written at beta / 2 */
   int32_t in_dtype;    /* vda_dtype_t of q, k, v, gate, text_k, text_v */
   int32_t out_dtype;   /* vda_dtype_t of out; must equal in_dtype */
+  int32_t anchors;     /* 0: no anchors; 1: boundary anchors (see above) */
 } vda_desc_t;
 
 /* Bytes of device workspace vda_forward and the debug taps need for `desc`

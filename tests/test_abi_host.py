@@ -30,6 +30,15 @@ def test_header_declares_the_binding_surface():
     assert header_functions() == sorted(vda.EXPORTED)
 
 
+def test_descriptor_layout_matches_header():
+    src = open(HEADER).read()
+    body = re.search(r"typedef struct vda_desc \{(.*?)\} vda_desc_t;", src, flags=re.S).group(1)
+    body = re.sub(r"/\*.*?\*/", "", body, flags=re.S)
+    fields = re.findall(r"(int32_t|float)\s+(\w+);", body)
+    assert [n for _, n in fields] == [n for n, _ in vda.VdaDesc._fields_]
+    assert ctypes.sizeof(vda.VdaDesc) == 4 * len(fields)
+
+
 def test_package_exposes_every_entry_point():
     for name in vda.EXPORTED:
         assert callable(getattr(vda, name, None)), name
@@ -81,6 +90,8 @@ def test_workspace_formula(lib):
     (dict(rms_eps=float("nan")), vda.VDA_ERR_INVALID_ARG),
     (dict(rms_eps=float("inf")), vda.VDA_ERR_INVALID_ARG),
     (dict(seed_mode=2), vda.VDA_ERR_INVALID_ARG),
+    (dict(anchors=2), vda.VDA_ERR_INVALID_ARG),
+    (dict(anchors=1), vda.VDA_OK),
     (dict(units=70000), vda.VDA_ERR_INVALID_ARG),
     (dict(tokens=4194304), vda.VDA_ERR_INVALID_ARG),
     (dict(text_tokens=4194304), vda.VDA_ERR_INVALID_ARG),

@@ -69,6 +69,7 @@ class Config:
     beta_mu: float = 0.0  # beta = sigmoid(N(beta_mu, 1))
     stress: bool = False  # clustered keys
     alpha_mu: float | None = None  # decay gates alpha = sigmoid(N(alpha_mu, 1)); None: no decay
+    anchors: bool = False  # boundary anchors: frames 0 and F - 1 out of the linear states
     chunk: int = 5
     radius: int = 1
     rms_eps: float = 1e-6
