@@ -41,14 +41,21 @@ design notes):
     and Eq. (A.4)); a missing side reads the text seed;
   * RMSNorm over the d_v channels of one (unit, frame, token) row with weight
     w in R^{d_v} and epsilon eps, then an element-wise sigmoid gate
-    ([VDN] Eq. (1c)).
+    ([VDN] Eq. (1c));
+  * comparison rules (rule 1, 2): the frozen-state batched update of SANA-WM,
+    S = S_bar (I - A) + B ([VDN] Sec. 3.1 Eq. (3a)/(3c)), replaces Eq. (5)
+    everywhere the frame-wise update is used (both scans and the text frame);
+    rule 2 adds SANA-WM's frame-size key scaling (every key of a frame of N
+    tokens scaled by 1/sqrt(N), [VDN] App. A.2: A -> A / N, B -> B / sqrt(N));
+    the text frame is scaled by its own token count T.  Both run with alpha = 1.
 """
 from __future__ import annotations
 
 import numpy as np
 
 __all__ = [
-    "frame_statistics", "frame_update", "decay", "transition", "text_state", "chunk_bounds",
+    "frame_statistics", "frame_update", "batched_update", "scaled_statistics", "update_rule",
+    "decay", "transition", "text_state", "chunk_bounds",
     "directional_states", "gather", "window_frames", "bridge", "anchored_states",
     "anchored_state_read", "rms_norm", "sigmoid", "readout", "forward_unit", "forward",
 ]
@@ -87,6 +94,34 @@ def frame_update(S_bar, A, B):
     return np.linalg.solve(G.T, (S_bar + B).T).T
 
 
+def batched_update(S_bar, A, B):
+    """Frozen-state batched update of SANA-WM, [VDN] Sec. 3.1 Eq. (3c):
+    S = S_bar (I - A) + B, every token correction evaluated at the same S_bar
+    (Eq. (3a))."""
+    S_bar = np.asarray(S_bar, f64)
+    return S_bar @ (np.eye(A.shape[0]) - A) + B
+
+
+def scaled_statistics(A, B, n_tokens):
+    """SANA-WM's frame-size key scaling, [VDN] App. A.2: every key of a frame of
+    n_tokens tokens scaled by 1/sqrt(n_tokens), so A -> A / n_tokens and
+    B -> B / sqrt(n_tokens) (no change for an empty frame)."""
+    if n_tokens == 0:
+        return A, B
+    return A / n_tokens, B / np.sqrt(n_tokens)
+
+
+def update_rule(rule):
+    """The state update of a rule: 0 the frame-wise delta rule (Eq. (5)), 1 and 2
+    the frozen-state batched rule (Eq. (3c); 2 with scaled statistics).  Looked
+    up at call time."""
+    if rule == 0:
+        return frame_update
+    if rule in (1, 2):
+        return batched_update
+    raise ValueError("rule must be 0, 1 or 2")
+
+
 def decay(S, alpha):
     """Channel-wise decay of an inherited state, [VDN] Sec. 3.1 Eq. (2):
     S_bar = S Diag(alpha) (column j of S, key channel j, scaled by alpha_j)."""
@@ -102,14 +137,15 @@ def transition(A, alpha=None):
     return np.asarray(alpha, f64)[:, None] * M
 
 
-def text_state(text_k, text_v, text_beta, d_k, d_v, seed_mode=0):
+def text_state(text_k, text_v, text_beta, d_k, d_v, seed_mode=0, rule=0):
     """Initial state of each directional scan, [VDN] Sec. 2.2 Eq. (1b).
 
     mode 0: S_T = one frame-wise update (Eq. (5)) from S = 0 over all text
             tokens; the seed is S_T / 2, so that the forward and reverse seeds
             together read S_T q exactly once.
     mode 1: the text tokens are written from S = 0 at half write strength.
-    No text tokens gives a zero seed.
+    No text tokens gives a zero seed.  rule: the update used (update_rule;
+    rule 2 scales the text frame's statistics by its token count).
     """
     text_k = np.asarray(text_k, f64).reshape(-1, d_k)
     text_v = np.asarray(text_v, f64).reshape(-1, d_v)
@@ -117,12 +153,17 @@ def text_state(text_k, text_v, text_beta, d_k, d_v, seed_mode=0):
     zero = np.zeros((d_v, d_k))
     if text_k.shape[0] == 0:
         return zero
+    T = text_k.shape[0]
     if seed_mode == 0:
         A, B = frame_statistics(text_k, text_v, text_beta)
-        return 0.5 * frame_update(zero, A, B)
+        if rule == 2:
+            A, B = scaled_statistics(A, B, T)
+        return 0.5 * update_rule(rule)(zero, A, B)
     if seed_mode == 1:
         A, B = frame_statistics(text_k, text_v, 0.5 * text_beta)
-        return frame_update(zero, A, B)
+        if rule == 2:
+            A, B = scaled_statistics(A, B, T)
+        return update_rule(rule)(zero, A, B)
     raise ValueError("seed_mode must be 0 or 1")
 
 
@@ -131,12 +172,12 @@ def chunk_bounds(F, C):
     return [(s, min(s + C, F)) for s in range(0, F, C)]
 
 
-def directional_states(stats, seed, C, alpha=None):
+def directional_states(stats, seed, C, alpha=None, update=None):
     """Both directional scans of [VDN] Sec. 2.2 / App. A.3 (no anchors).
 
     stats: list of (A_f, B_f) for f = 0..F-1; alpha: F x d_k decay gates or None
     (alpha = 1).  Entering frame f, the inherited state is decayed by alpha_f
-    (Eq. (2)) and updated by Eq. (5), in either direction.
+    (Eq. (2)) and updated by Eq. (5) (or ``update``), in either direction.
     Forward: start at the seed and apply frames 0, 1, ..., F-1;
       P[0] = seed, P[j+1] = the state after the last frame of chunk j.
     Reverse: start at the seed and apply frames F-1, ..., 0;
@@ -151,7 +192,7 @@ def directional_states(stats, seed, C, alpha=None):
 
     def enter(S, f):
         S_bar = S if alpha is None else decay(S, alpha[f])
-        return frame_update(S_bar, *stats[f])
+        return (update or frame_update)(S_bar, *stats[f])
 
     S = seed.copy()
     P[0] = S
@@ -206,7 +247,7 @@ def bridge(P, R, f, C, radius, alpha):
     return decay(P[max(c - radius, 0)], d_f) + decay(R[min(c + radius + 1, n)], d_r)
 
 
-def anchored_states(stats, seed, alpha=None):
+def anchored_states(stats, seed, alpha=None, update=None):
     """Both directional scans with boundary anchors, [VDN] Sec. 2.2 and App. A.3.
 
     stats: list of (A_f, B_f) for f = 0..F-1 (the anchors' entries are never
@@ -221,7 +262,7 @@ def anchored_states(stats, seed, alpha=None):
 
     def enter(S, f):
         S_bar = S if alpha is None else decay(S, alpha[f])
-        return frame_update(S_bar, *stats[f])
+        return (update or frame_update)(S_bar, *stats[f])
 
     P = {0: seed.copy()}
     for j in range(1, F - 1):
@@ -277,15 +318,18 @@ def readout(S_tilde, Q, G, w, eps):
 
 def forward_unit(q, k, v, beta, gate, text_k, text_v, text_beta, rms_weight,
                  chunk=5, radius=1, eps=1e-6, seed_mode=0, taps=False, alpha=None,
-                 anchors=False):
+                 anchors=False, rule=0):
     """VDA forward for one unit.
 
     q: F x U x d_k, k: F x U x d_k, v: F x U x d_v, beta: F x U,
     gate: F x U x d_v (gate logits), text_k: T x d_k, text_v: T x d_v,
     text_beta: T, rms_weight: d_v, alpha: F x d_k decay gates in [0, 1] or None
-    (alpha = 1), anchors: boundary anchors (frames 0 and F - 1).  Returns out
+    (alpha = 1), anchors: boundary anchors (frames 0 and F - 1), rule: 0 the
+    frame-wise delta rule, 1 / 2 the batched comparison rules (alpha = 1 only;
+    see the module notes).  Returns out
     (F x U x d_v), plus a dict of intermediates when taps=True: A, B (per
-    frame), M (per frame, Eq. (A.1)), seed, P, R, and with decay or anchors the
+    frame; scaled under rule 2), M (per frame: the inherited-state factor,
+    Eq. (A.1), or I - A for the batched rules), seed, P, R, and with decay or anchors the
     state St read by each frame (F x d_v x d_k; zero where nothing is read).
     With anchors P and R are (F - 1) x d_v x d_k arrays: P[j] through interior
     frame j (P[0] = seed), R[j - 1] from the last interior frame down to j
@@ -301,12 +345,14 @@ def forward_unit(q, k, v, beta, gate, text_k, text_v, text_beta, rms_weight,
         alpha = np.asarray(alpha, f64).reshape(F, d_k)
         if np.any(alpha < 0) or np.any(alpha > 1):
             raise ValueError("decay gates must lie in [0, 1]")
-    seed = text_state(text_k, text_v, text_beta, d_k, d_v, seed_mode)
+    if rule != 0 and alpha is not None:
+        raise ValueError("the batched comparison rules run without decay")
+    seed = text_state(text_k, text_v, text_beta, d_k, d_v, seed_mode, rule)
     if anchors:
         return _forward_unit_anchored(q, k, v, beta, gate, rms_weight, seed, chunk, radius,
-                                      eps, taps, alpha)
-    stats = [frame_statistics(k[f], v[f], beta[f]) for f in range(F)]
-    P, R = directional_states(stats, seed, chunk, alpha)
+                                      eps, taps, alpha, rule)
+    stats = [_stats(k[f], v[f], beta[f], rule) for f in range(F)]
+    P, R = directional_states(stats, seed, chunk, alpha, update_rule(rule))
     out = np.zeros((F, U, d_v))
     St = np.zeros((F, d_v, d_k))
     for c, (lo, hi) in enumerate(chunk_bounds(F, chunk)):
@@ -321,7 +367,7 @@ def forward_unit(q, k, v, beta, gate, text_k, text_v, text_beta, rms_weight,
     tap = {
         "A": np.array([s[0] for s in stats]).reshape(F, d_k, d_k),
         "B": np.array([s[1] for s in stats]).reshape(F, d_v, d_k),
-        "M": np.array([transition(stats[f][0], None if alpha is None else alpha[f])
+        "M": np.array([_factor(stats[f][0], None if alpha is None else alpha[f], rule)
                        for f in range(F)]).reshape(F, d_k, d_k),
         "seed": seed, "P": P, "R": R,
     }
@@ -330,8 +376,19 @@ def forward_unit(q, k, v, beta, gate, text_k, text_v, text_beta, rms_weight,
     return out, tap
 
 
+def _stats(K, V, beta, rule):
+    """A frame's statistics under a rule (rule 2: scaled by the frame's size)."""
+    A, B = frame_statistics(K, V, beta)
+    return scaled_statistics(A, B, np.shape(K)[0]) if rule == 2 else (A, B)
+
+
+def _factor(A, alpha, rule):
+    """Inherited-state factor of a frame: Eq. (A.1), or I - A (Eq. (3c))."""
+    return transition(A, alpha) if rule == 0 else np.eye(A.shape[0]) - A
+
+
 def _forward_unit_anchored(q, k, v, beta, gate, rms_weight, seed, chunk, radius, eps, taps,
-                           alpha):
+                           alpha, rule=0):
     """forward_unit with boundary anchors ([VDN] Algorithm 1 steps 2-7): the
     anchor frames' rows are removed from the linear inputs (their statistics
     are never formed), the interior frames are scanned, and each interior,
@@ -340,8 +397,8 @@ def _forward_unit_anchored(q, k, v, beta, gate, rms_weight, seed, chunk, radius,
     d_v = v.shape[-1]
     stats = [None] * F
     for f in range(1, F - 1):
-        stats[f] = frame_statistics(k[f], v[f], beta[f])
-    P, R = anchored_states(stats, seed, alpha)
+        stats[f] = _stats(k[f], v[f], beta[f], rule)
+    P, R = anchored_states(stats, seed, alpha, update_rule(rule))
     out = np.zeros((F, U, d_v))
     St = np.zeros((F, d_v, d_k))
     for t in range(F):
@@ -355,7 +412,7 @@ def _forward_unit_anchored(q, k, v, beta, gate, rms_weight, seed, chunk, radius,
     zero_a, zero_b = np.zeros((d_k, d_k)), np.zeros((d_v, d_k))
     A = np.array([s[0] if s is not None else zero_a for s in stats]).reshape(F, d_k, d_k)
     B = np.array([s[1] if s is not None else zero_b for s in stats]).reshape(F, d_v, d_k)
-    Mt = [transition(A[f], None if alpha is None or stats[f] is None else alpha[f])
+    Mt = [_factor(A[f], None if alpha is None or stats[f] is None else alpha[f], rule)
           for f in range(F)]
     tap = {"A": A, "B": B, "M": np.array(Mt).reshape(F, d_k, d_k), "seed": seed, "St": St,
            "P": np.array([P[j] for j in range(F - 1)]).reshape(max(F - 1, 0), d_v, d_k),
@@ -365,10 +422,10 @@ def _forward_unit_anchored(q, k, v, beta, gate, rms_weight, seed, chunk, radius,
 
 def forward(q, k, v, beta, gate, text_k, text_v, text_beta, rms_weight,
             chunk=5, radius=1, eps=1e-6, seed_mode=0, taps=False, units=None, alpha=None,
-            anchors=False):
+            anchors=False, rule=0):
     """VDA forward over all units (leading axis of every per-unit tensor;
     alpha: units x F x d_k decay gates, or None for alpha = 1; anchors: boundary
-    anchors, see forward_unit).
+    anchors, see forward_unit; rule: the update rule, see forward_unit).
 
     ``units`` restricts the work to a subset of unit indices; the result then
     holds only those units, in that order.
@@ -378,7 +435,7 @@ def forward(q, k, v, beta, gate, text_k, text_v, text_beta, rms_weight,
     for u in idx:
         r = forward_unit(q[u], k[u], v[u], beta[u], gate[u], text_k[u], text_v[u],
                          text_beta[u], rms_weight, chunk, radius, eps, seed_mode, taps,
-                         None if alpha is None else alpha[u], anchors)
+                         None if alpha is None else alpha[u], anchors, rule)
         if taps:
             outs.append(r[0])
             tapl.append(r[1])

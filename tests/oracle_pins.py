@@ -22,7 +22,11 @@ facts come from "Video DeltaNet" (arXiv 2609.20744), cited as [VDN]:
   * Eq. (1c): RMSNorm then an element-wise sigmoid gate;
   * Sec. 2.1, Sec. 2.2, App. A.3 and Algorithm 1: boundary anchors (frames 0 and
     F - 1) are left out of both states, get no linear output, and a window that
-    covers the clip bypasses the linear path.
+    covers the clip bypasses the linear path;
+  * Sec. 3.1 Eq. (3a)/(3c) and App. A.2: the frozen-state batched rule of
+    SANA-WM is the token-wise correction sum at a shared state, its factor
+    I - A stops being non-expansive once an eigenvalue of A passes 2, and the
+    frame-size key scaling restores it and assigns the weights A.2 states.
 
 None of these re-types the oracle's own formula: gradients and objectives are
 evaluated token by token, least squares goes through numpy's SVD-based solver,
@@ -885,6 +889,104 @@ def pin_anchor_disjointness(o):
                     assert np.all(out[t] == 0.0), (F, C, r, fstar, t)
 
 
+# ----------------------------------------------------------------------------- NEXT-4: batched rule
+def pin_batched_token_sum(o):
+    """[VDN] Eq. (3a) with plain loops: every token's correction
+    beta_u (v_u - S_bar k_u) k_u^T is evaluated at the same S_bar and added; the
+    oracle's Eq. (3c) form S_bar (I - A) + B must agree."""
+    rng = _rng(51)
+    for _ in range(5):
+        S_bar, K, V, beta = _frame(rng, U=8, dk=5, dv=3)
+        S = S_bar.copy()
+        for u in range(K.shape[0]):
+            r = V[u] - S_bar @ K[u]
+            for i in range(S.shape[0]):
+                for j in range(S.shape[1]):
+                    S[i, j] += beta[u] * r[i] * K[u, j]
+        A, B = o.frame_statistics(K, V, beta)
+        assert np.max(np.abs(o.batched_update(S_bar, A, B) - S)) <= 1e-13
+
+
+def pin_batched_scaled_keys(o):
+    """App. A.2: rule 2 is rule 1 with every key divided by sqrt(frame size): the
+    video keys by sqrt(U), the text keys by sqrt(T) (queries untouched)."""
+    rng = _rng(52)
+    for F, C, r, U, T in ((12, 5, 1, 6, 4), (7, 2, 1, 3, 0), (9, 3, 0, 5, 2)):
+        x = _random_unit(rng, F, U, 4, 3, T)
+        for anchors in (False, True):
+            out2 = _call(o, x, chunk=C, radius=r, rule=2, anchors=anchors)
+            y = dict(x)
+            y["k"] = x["k"] / np.sqrt(U)
+            y["text_k"] = x["text_k"] / np.sqrt(max(T, 1))
+            out1 = _call(o, y, chunk=C, radius=r, rule=1, anchors=anchors)
+            assert np.max(np.abs(out2 - out1)) <= 1e-12, (F, C, r, U, T, anchors)
+
+
+def pin_batched_seed(o):
+    """Eq. (1b) under the batched rule: from S = 0 the update is just B_T, so the
+    seed is B_T / 2 in mode 0 and B_T(beta / 2) = B_T / 2 in mode 1."""
+    rng = _rng(53)
+    _, K, V, beta = _frame(rng, U=6, dk=4, dv=3)
+    A, B = o.frame_statistics(K, V, beta)
+    for mode in (0, 1):
+        seed = o.text_state(K, V, beta, 4, 3, mode, rule=1)
+        assert np.max(np.abs(seed - 0.5 * B)) <= 1e-14, mode
+
+
+def pin_batched_contraction(o):
+    """App. A.2 through the oracle's scans: a frame of U copies of one unit key k
+    with common beta and zero values maps the state's k-component by 1 - U beta
+    under rule 1 (growth once U beta > 2), by 1 - beta under rule 2 (scaled keys)
+    and by 1 / (1 + U beta) under the frame-wise rule."""
+    rng = _rng(54)
+    dk, dv, U, F = 4, 3, 6, 4
+    k = _unit(rng.standard_normal(dk))
+    b = 0.7  # U b = 4.2 > 2
+    x = dict(q=rng.standard_normal((F, U, dk)), k=np.tile(k, (F, U, 1)),
+             v=np.zeros((F, U, dv)), beta=np.full((F, U), b),
+             gate=rng.standard_normal((F, U, dv)), text_k=k[None, :],
+             text_v=rng.standard_normal((1, dv)), text_beta=np.array([0.9]),
+             rms_weight=np.ones(dv))
+    for rule, factor in ((1, 1 - U * b), (2, 1 - b), (0, 1 / (1 + U * b))):
+        _, tap = _call(o, x, chunk=1, radius=0, rule=rule, taps=True)
+        Pk = tap["P"] @ k
+        for j in range(F):
+            assert np.max(np.abs(Pk[j + 1] - factor * Pk[j])) <= 1e-12 * np.abs(Pk[j]).max()
+    # unit keys, beta <= 1: lambda_max(A) <= tr A <= U, and the scaled factor is
+    # non-expansive while the unscaled one is not once lambda_max > 2
+    K = _unit(rng.standard_normal((50, dk)))
+    K[:40] = k
+    A, _ = o.frame_statistics(K, np.zeros((50, dv)), rng.uniform(0.5, 1.0, 50))
+    lam = np.linalg.eigvalsh(A)
+    assert lam.max() <= np.trace(A) + 1e-12 and lam.max() > 2
+    As, _ = o.scaled_statistics(A, np.zeros((dv, dk)), 50)
+    assert np.linalg.norm(np.eye(dk) - As, 2) <= 1 + 1e-12
+    assert np.linalg.norm(np.eye(dk) - A, 2) > 1
+
+
+def pin_batched_a2_weights(o):
+    """App. A.2: with scaled keys k' = k / sqrt(U), U repeats of one unit key give
+    S k' = (1 - beta) S_bar k' + beta v_mean (weight beta on the consensus),
+    while U orthonormal keys give S k'_u = (1 - beta / U) S_bar k'_u + (beta / U) v_u."""
+    rng = _rng(55)
+    U, dv = 8, 3
+    b = 0.6
+    k = _unit(rng.standard_normal(U))
+    V = rng.standard_normal((U, dv))
+    S_bar = rng.standard_normal((dv, U))
+    A, B = o.frame_statistics(np.tile(k, (U, 1)), V, np.full(U, b))
+    S = o.batched_update(S_bar, *o.scaled_statistics(A, B, U))
+    kp = k / np.sqrt(U)
+    assert np.max(np.abs(S @ kp - ((1 - b) * S_bar @ kp + b * V.mean(axis=0)))) <= 1e-13
+    Q, _ = np.linalg.qr(rng.standard_normal((U, U)))
+    A, B = o.frame_statistics(Q, V, np.full(U, b))
+    S = o.batched_update(S_bar, *o.scaled_statistics(A, B, U))
+    for u in range(U):
+        kp = Q[u] / np.sqrt(U)
+        want = (1 - b / U) * S_bar @ kp + (b / U) * V[u]
+        assert np.max(np.abs(S @ kp - want)) <= 1e-13
+
+
 ALL_PINS = [
     pin_stats_hand_loop, pin_stats_invariants, pin_gradient_zero, pin_lstsq_bruteforce,
     pin_sherman_morrison, pin_repeated_keys, pin_orthonormal_keys, pin_beta_zero,
@@ -895,4 +997,6 @@ ALL_PINS = [
     pin_decay_non_expansive, pin_decay_time_reversal, pin_decay_chunk_composition,
     pin_anchor_rows_zero, pin_anchor_inputs_ignored, pin_anchor_identity_frames,
     pin_anchor_bypass, pin_anchor_scalar, pin_anchor_disjointness,
+    pin_batched_token_sum, pin_batched_scaled_keys, pin_batched_seed, pin_batched_contraction,
+    pin_batched_a2_weights,
 ]

@@ -314,6 +314,38 @@ def _anchor_reverse_scan_skips_frame(m):
     m.anchored_states = anchored_states
 
 
+def _batched_plus(m):
+    def batched_update(S_bar, A, B):
+        return np.asarray(S_bar, float) @ (np.eye(A.shape[0]) + A) + B
+    m.batched_update = batched_update
+
+
+def _batched_write_inside(m):
+    def batched_update(S_bar, A, B):
+        return (np.asarray(S_bar, float) + B) @ (np.eye(A.shape[0]) - A)
+    m.batched_update = batched_update
+
+
+def _scaling_b_by_n(m):
+    def scaled_statistics(A, B, n_tokens):
+        return (A, B) if n_tokens == 0 else (A / n_tokens, B / n_tokens)
+    m.scaled_statistics = scaled_statistics
+
+
+def _scaling_a_by_sqrt_n(m):
+    def scaled_statistics(A, B, n_tokens):
+        return (A, B) if n_tokens == 0 else (A / np.sqrt(n_tokens), B / np.sqrt(n_tokens))
+    m.scaled_statistics = scaled_statistics
+
+
+def _text_frame_not_scaled(m):
+    orig = m.text_state
+
+    def text_state(text_k, text_v, text_beta, d_k, d_v, seed_mode=0, rule=0):
+        return orig(text_k, text_v, text_beta, d_k, d_v, seed_mode, 1 if rule == 2 else rule)
+    m.text_state = text_state
+
+
 MUTATIONS = {f.__name__.lstrip("_"): f for f in [
     _stats_no_beta, _stats_beta_squared, _stats_b_swapped, _update_minus, _update_no_identity,
     _update_drops_inherited, _update_frozen_state, _update_left_multiplied, _seed_not_halved,
@@ -323,7 +355,8 @@ MUTATIONS = {f.__name__.lstrip("_"): f for f in [
     _forward_ignores_decay, _decay_on_rows, _bridge_excludes_query_frame, _bridge_omitted,
     _bridge_products_swapped, _transition_decay_right, _anchor_rows_kept, _anchor_no_bypass,
     _anchor_reverse_read_early, _anchor_bridge_from_unclipped_window,
-    _anchor_chunks_over_interior, _anchor_reverse_scan_skips_frame,
+    _anchor_chunks_over_interior, _anchor_reverse_scan_skips_frame, _batched_plus,
+    _batched_write_inside, _scaling_b_by_n, _scaling_a_by_sqrt_n, _text_frame_not_scaled,
 ]}
 
 
