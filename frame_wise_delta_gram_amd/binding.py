@@ -37,7 +37,7 @@ class VdaDesc(ctypes.Structure):
         ("text_tokens", ctypes.c_int32), ("d_k", ctypes.c_int32), ("d_v", ctypes.c_int32),
         ("chunk", ctypes.c_int32), ("radius", ctypes.c_int32), ("rms_eps", ctypes.c_float),
         ("seed_mode", ctypes.c_int32), ("in_dtype", ctypes.c_int32), ("out_dtype", ctypes.c_int32),
-        ("anchors", ctypes.c_int32),
+        ("anchors", ctypes.c_int32), ("rule", ctypes.c_int32),
     ]
 
     @property
@@ -103,9 +103,9 @@ def vda_status_string(status: int) -> str:
 
 
 def make_desc(units, frames, tokens, text_tokens, d_k, d_v, chunk=5, radius=1, rms_eps=1e-6,
-              seed_mode=0, dtype=VDA_DTYPE_BF16, anchors=0) -> VdaDesc:
+              seed_mode=0, dtype=VDA_DTYPE_BF16, anchors=0, rule=0) -> VdaDesc:
     return VdaDesc(units, frames, tokens, text_tokens, d_k, d_v, chunk, radius, rms_eps,
-                   seed_mode, dtype, dtype, int(anchors))
+                   seed_mode, dtype, dtype, int(anchors), int(rule))
 
 
 def vda_workspace_bytes(desc: VdaDesc) -> int:
@@ -237,7 +237,7 @@ def vda_debug_states_decay(desc, k, v, beta, alpha, text_k, text_v, text_beta, P
 
 # ----------------------------------------------------------------------------- torch helpers
 def desc_from_tensors(q, k, v, text_k, chunk=5, radius=1, eps=1e-6, seed_mode=0,
-                      anchors=False) -> VdaDesc:
+                      anchors=False, rule=0) -> VdaDesc:
     """Descriptor from tensor shapes: q/k [units, F, U, d_k], v [units, F, U, d_v],
     text_k [units, T, d_k]."""
     import torch
@@ -250,7 +250,7 @@ def desc_from_tensors(q, k, v, text_k, chunk=5, radius=1, eps=1e-6, seed_mode=0,
         dt = VDA_DTYPE_F32
     else:
         raise TypeError("features must be bfloat16 or float32, got %s" % k.dtype)
-    return make_desc(units, F, U, T, dk, dv, chunk, radius, eps, seed_mode, dt, anchors)
+    return make_desc(units, F, U, T, dk, dv, chunk, radius, eps, seed_mode, dt, anchors, rule)
 
 
 def _check_tensor(name, x, dtype, shape):
@@ -264,18 +264,19 @@ def _check_tensor(name, x, dtype, shape):
 
 def forward(q, k, v, beta, gate, text_k, text_v, text_beta, rms_weight, chunk=5, radius=1,
             eps=1e-6, seed_mode=0, out=None, workspace=None, stream=None, alpha=None,
-            anchors=False):
+            anchors=False, rule=0):
     """VDA forward on torch GPU tensors; allocates `out` and the workspace when absent.
 
     Shapes: q, k [units, F, U, d_k]; v, gate [units, F, U, d_v]; beta [units, F, U]
     (float32); text_k [units, T, d_k]; text_v [units, T, d_v]; text_beta
     [units, T] (float32); rms_weight [d_v] (float32); alpha (optional decay
     gates) [units, F, d_k] (float32); anchors: boundary anchors (frames 0 and
-    F - 1 out of the linear states, their rows zero).  Returns out
+    F - 1 out of the linear states, their rows zero); rule: 0 the frame-wise
+    delta rule, 1 / 2 the batched comparison rules (no decay).  Returns out
     [units, F, U, d_v] in the features' dtype.
     """
     import torch
-    desc = desc_from_tensors(q, k, v, text_k, chunk, radius, eps, seed_mode, anchors)
+    desc = desc_from_tensors(q, k, v, text_k, chunk, radius, eps, seed_mode, anchors, rule)
     units, F, U, dk = k.shape
     dv = v.shape[-1]
     T = desc.text_tokens

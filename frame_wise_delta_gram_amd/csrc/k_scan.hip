@@ -66,7 +66,7 @@ __global__ __launch_bounds__(256, 1) void compose_kernel(const float* __restrict
                                                         float* __restrict__ Jr,
                                                         float* __restrict__ ST, int dk, int dv,
                                                         int F, int C, int n, float seed_scale,
-                                                        int anchors) {
+                                                        int anchors, int batched) {
   __shared__ float Xs[128 * SG];
   __shared__ float Ms[128 * SG];
   const int c = blockIdx.x;
@@ -99,6 +99,25 @@ __global__ __launch_bounds__(256, 1) void compose_kernel(const float* __restrict
     const bool anchor = anchors && (f == 0 || f == F - 1);
     return alpha && j < dk && !anchor ? alpha[((size_t)u * F + f) * dk + j] : 1.0f;
   };
+  // batched comparison rule: a write chain (and the seed) starts at X = B of its
+  // first frame and steps X <- X M_g + B_g over the others
+  const int sh = batched && !mchain ? 1 : 0;
+  const int nsteps = nf - sh;
+  const size_t SS = (size_t)dv * dk;
+  float* dst = chain == 0 ? Mc + ((size_t)u * n + c) * dk * dk
+               : chain == 3 ? ST + (size_t)u * 2 * (n + 1) * SS                  // P[0]
+               : chain == 4 ? nullptr                                            // MrT only
+                            : (chain == 1 ? Jf : Jr) + ((size_t)u * n + c) * SS;
+  float* dst2 = ST + ((size_t)(u * 2 + 1) * (n + 1) + n) * SS;                 // R[n]
+  if (batched && nsteps == 0) {  // the chain is its first frame's write
+    const float scale = chain == 3 ? seed_scale : 1.0f;
+    const float* src = Bp(frame(0));
+    for (size_t i = t; i < SS; i += 256) {
+      dst[i] = src[i] * scale;
+      if (chain == 3) dst2[i] = src[i] * scale;
+    }
+    return;
+  }
 
   {
     MatRegs m;
@@ -115,23 +134,17 @@ __global__ __launch_bounds__(256, 1) void compose_kernel(const float* __restrict
         Xs[i * SG + j] = (i == j) ? gate(frame(0), i) : 0.0f;
       }
     }
-    mat_load(m, Mp(frame(0)), dk, dk, dk);
+    mat_load(m, Mp(frame(sh)), dk, dk, dk);
     mat_store_lds(m, Ms, SG, Dk, Dk);
   }
   __syncthreads();
 
-  const size_t SS = (size_t)dv * dk;
-  float* dst = chain == 0 ? Mc + ((size_t)u * n + c) * dk * dk
-               : chain == 3 ? ST + (size_t)u * 2 * (n + 1) * SS                  // P[0]
-               : chain == 4 ? nullptr                                            // MrT only
-                            : (chain == 1 ? Jf : Jr) + ((size_t)u * n + c) * SS;
-  float* dst2 = ST + ((size_t)(u * 2 + 1) * (n + 1) + n) * SS;                 // R[n]
   MatRegs mnext;
   float bnext[4][16];
-  for (int s = 0; s < nf; ++s) {
-    const bool last = s == nf - 1;
-    if (!last) {  // next frame's transition (and write) fly while this step multiplies
-      mat_load(mnext, Mp(frame(s + 1)), dk, dk, dk);
+  for (int s = 0; s < nsteps; ++s) {
+    const bool last = s == nsteps - 1;
+    if (!last || sh) {  // next frame's transition (and write) fly while this step multiplies
+      if (!last) mat_load(mnext, Mp(frame(s + 1 + sh)), dk, dk, dk);
 #pragma unroll
       for (int ct = 0; ct < 4; ++ct) {
         if (!mchain && w < nR && ct < nb)
@@ -167,12 +180,13 @@ __global__ __launch_bounds__(256, 1) void compose_kernel(const float* __restrict
           if (last) {
             if (row < rows && col < dk) {
               const size_t tix = ((size_t)u * n + c) * dk * dk + (size_t)col * dk + row;
+              const float val = acc[ct][r] + (sh ? bnext[ct][r] : 0.0f);
               if (chain == 4) {
-                MrT[tix] = acc[ct][r];
+                MrT[tix] = val;
               } else {
-                dst[(size_t)row * dk + col] = acc[ct][r];
-                if (chain == 0) McT[tix] = acc[ct][r];
-                if (chain == 3) dst2[(size_t)row * dk + col] = acc[ct][r];
+                dst[(size_t)row * dk + col] = val;
+                if (chain == 0) McT[tix] = val;
+                if (chain == 3) dst2[(size_t)row * dk + col] = val;
               }
             }
           } else {
@@ -423,7 +437,11 @@ __device__ __forceinline__ void x_fill(__bf16* xh, __bf16* xl, const float* src,
 // Mr = D_{f1-1} M_{f1-1} ... D_{f0} M_{f0}, which no longer equals Mc^T.  With
 // decay each step enters the next frame as X <- (X M) Diag(alpha_next) + B_next
 // and a transition chain starts from Diag(alpha) of its first frame.
-template <bool FULL, bool DECAY>
+// BATCHED (the frozen-state comparison rule, S -> S M + B with M = I - A):
+// a write chain starts at X = B of its first frame and steps X <- X M_g + B_g
+// over the others (the transition index runs one frame ahead of the write's);
+// the seed and one-frame chunks are plain copies of B.
+template <bool FULL, bool DECAY, bool BATCHED>
 __global__ __launch_bounds__(512, 1) void compose_split_kernel(
     const float* __restrict__ Bw, const float* __restrict__ Mw, const float* __restrict__ alpha,
     float* __restrict__ Mc, float* __restrict__ McT, float* __restrict__ MrT,
@@ -463,13 +481,8 @@ __global__ __launch_bounds__(512, 1) void compose_split_kernel(
   // boundary anchors carry no gate (the identity)
   auto anchor = [&](int f) { return anchors && (f == 0 || f == F - 1); };
   const bool active = jr < dk && xr0 < rows;
-
-  RowsF32<8> mf;
-  rows_load<8, 16>(mf, Mp(frame(0)), dk, jr, 64 * kh);
-  x_fill(Xh, Xl, mchain ? nullptr : Bp(frame(0)), mchain ? 0 : dv, dk, seed ? seed_scale : 1.0f,
-         DECAY && mchain && !anchor(frame(0)) ? Ap(frame(0)) : nullptr);
-  rows_split<8, 16>(Mh, Ml, 0, mf, dk, jr, 64 * kh);
-  __syncthreads();
+  const int sh = BATCHED && !mchain ? 1 : 0;  // transition index offset of a write chain
+  const int nsteps = nf - sh;
 
   const size_t tile = ((size_t)u * n + c) * dk * dk;
   float* dst = chain == 0 && !seed ? Mc + tile
@@ -478,13 +491,32 @@ __global__ __launch_bounds__(512, 1) void compose_split_kernel(
                                    : (chain == 1 ? Jf : Jr) + ((size_t)u * n + c) * SS;
   float* dst2 = seed ? ST + ((size_t)(u * 2 + 1) * (n + 1) + n) * SS  // R[n]
                      : (chain == 3 ? MrT : McT) + tile;
+  if (BATCHED && nsteps == 0) {  // the chain is its first frame's write
+    const float scale = seed ? seed_scale : 1.0f;
+    const f32x4_t* src = reinterpret_cast<const f32x4_t*>(Bp(frame(0)));
+    for (int i = threadIdx.x; i < (int)(SS / 4); i += blockDim.x) {
+      const f32x4_t v = src[i] * scale;
+      reinterpret_cast<f32x4_t*>(dst)[i] = v;
+      if (seed) reinterpret_cast<f32x4_t*>(dst2)[i] = v;
+    }
+    return;
+  }
+
+  RowsF32<8> mf;
+  rows_load<8, 16>(mf, Mp(frame(sh)), dk, jr, 64 * kh);
+  x_fill(Xh, Xl, mchain ? nullptr : Bp(frame(0)), mchain ? 0 : dv, dk, seed ? seed_scale : 1.0f,
+         DECAY && mchain && !anchor(frame(0)) ? Ap(frame(0)) : nullptr);
+  rows_split<8, 16>(Mh, Ml, 0, mf, dk, jr, 64 * kh);
+  __syncthreads();
+
   const int lane = threadIdx.x & 63;
   f32x4_t bq[2][4];
   f32x4_t aq[4];
-  for (int s = 0; s < nf; ++s) {
-    const bool last = s == nf - 1;
+  for (int s = 0; s < nsteps; ++s) {
+    const bool last = s == nsteps - 1;
+    if (BATCHED && last && !mchain) rows_prefetch_t<2>(bq, Bp(frame(s + 1)), dv, dk, xr0, jr);
     if (!last) {  // the next frame's transition and write fly while this step multiplies
-      rows_load<8, 16>(mf, Mp(frame(s + 1)), dk, jr, 64 * kh);
+      rows_load<8, 16>(mf, Mp(frame(s + 1 + sh)), dk, jr, 64 * kh);
       if (!mchain) rows_prefetch_t<2>(bq, Bp(frame(s + 1)), dv, dk, xr0, jr);
       if (DECAY) {
         const bool one = anchor(frame(s + 1));
@@ -507,7 +539,8 @@ __global__ __launch_bounds__(512, 1) void compose_split_kernel(
             if (!out_ok(rows, dk, xr0, x, jr, q)) continue;
             const int row = xr0 + 32 * x + (lane & 31);
             const int col = jr + 8 * q + 4 * (lane >> 5);
-            const f32x4_t v = out_quad(acc, x, q);
+            f32x4_t v = out_quad(acc, x, q);
+            if (BATCHED && !mchain) v += bq[x][q];
             if (!DECAY || chain != 3 || seed)
               *reinterpret_cast<f32x4_t*>(dst + (size_t)row * dk + col) = v;
             if (seed) {
@@ -615,11 +648,12 @@ __global__ __launch_bounds__(256) void scan_split_kernel(const float* __restrict
 
 }  // namespace
 
-template <bool FULL, bool DECAY>
+template <bool FULL, bool DECAY, bool BATCHED = false>
 void launch_compose_split(const Plan& p, const WsPtrs& w, const float* alpha, float seed_scale,
                           hipStream_t s) {
   const unsigned per = xcd_per((unsigned)p.units * (p.n * (DECAY ? 4 : 3) + 1));
-  hipLaunchKernelGGL((compose_split_kernel<FULL, DECAY>), dim3(kXcds * per), dim3(512), 0, s, w.B,
+  hipLaunchKernelGGL((compose_split_kernel<FULL, DECAY, BATCHED>), dim3(kXcds * per), dim3(512),
+                     0, s, w.B,
                      w.M, alpha, w.Mc, w.McT, w.MrT, w.Jf, w.Jr, w.ST, p.dk, p.dv, p.F, p.C, p.n,
                      p.units, per, seed_scale, p.anchors);
 }
@@ -627,7 +661,10 @@ void launch_compose_split(const Plan& p, const WsPtrs& w, const float* alpha, fl
 hipError_t launch_compose(const Plan& p, const WsPtrs& w, const float* alpha, hipStream_t s) {
   const float seed_scale = p.seed_mode == 1 ? 1.0f : 0.5f;
   if (p.dtype == VDA_DTYPE_BF16) {
-    if (p.dk == 128)
+    if (p.rule != 0)  // the batched comparison rules (no decay)
+      p.dk == 128 ? launch_compose_split<true, false, true>(p, w, nullptr, seed_scale, s)
+                  : launch_compose_split<false, false, true>(p, w, nullptr, seed_scale, s);
+    else if (p.dk == 128)
       alpha ? launch_compose_split<true, true>(p, w, alpha, seed_scale, s)
             : launch_compose_split<true, false>(p, w, alpha, seed_scale, s);
     else
@@ -636,7 +673,7 @@ hipError_t launch_compose(const Plan& p, const WsPtrs& w, const float* alpha, hi
   } else {
     hipLaunchKernelGGL(compose_kernel, dim3(p.n, p.units, alpha ? 5 : 4), dim3(kThreads), 0, s,
                        w.B, w.M, alpha, w.Mc, w.McT, w.MrT, w.Jf, w.Jr, w.ST, p.dk, p.dv, p.F, p.C,
-                       p.n, seed_scale, p.anchors);
+                       p.n, seed_scale, p.anchors, p.rule != 0 ? 1 : 0);
   }
   return hipGetLastError();
 }

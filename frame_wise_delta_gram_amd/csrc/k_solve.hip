@@ -189,11 +189,48 @@ __global__ __launch_bounds__(256, 3) void solve_kernel(const float* __restrict__
   }
 }
 
+// Inherited-state factor of the batched comparison rules (SANA-WM's frozen-state
+// update, Sec. 3.1 Eq. (3c)): M = I - s A, and with frame-size key scaling
+// (App. A.2, rule 2) s = 1 / N and B <- B / sqrt(N), N the frame's token count
+// (the text frame's own T); rule 1: s = 1.  One workgroup per (frame, unit),
+// float4 element-wise.
+__global__ __launch_bounds__(256) void batched_factor_kernel(const float* __restrict__ A,
+                                                             float* __restrict__ M,
+                                                             float* __restrict__ B, int dk,
+                                                             int dv, int Fp1, int U, int T,
+                                                             int rule) {
+  const int fi = blockIdx.x;
+  const int u = blockIdx.y;
+  const size_t fr = (size_t)u * Fp1 + fi;
+  const int N = fi == 0 ? T : U;
+  const bool scale = rule == 2 && N > 0;
+  const float s = scale ? 1.0f / (float)N : 1.0f;
+  const f32x4_t* a = reinterpret_cast<const f32x4_t*>(A + fr * dk * dk);
+  f32x4_t* m = reinterpret_cast<f32x4_t*>(M + fr * dk * dk);
+  for (int i = threadIdx.x; i < dk * dk / 4; i += blockDim.x) {
+    const int r = (4 * i) / dk;
+    const int c = 4 * i - r * dk;
+    f32x4_t x = a[i];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) x[e] = (r == c + e ? 1.0f : 0.0f) - s * x[e];
+    m[i] = x;
+  }
+  if (scale) {
+    const float sb = 1.0f / sqrtf((float)N);
+    f32x4_t* b = reinterpret_cast<f32x4_t*>(B + fr * dv * dk);
+    for (int i = threadIdx.x; i < dv * dk / 4; i += blockDim.x) b[i] *= sb;
+  }
+}
+
 }  // namespace
 
 hipError_t launch_solve(const Plan& p, const WsPtrs& w, hipStream_t s) {
   const dim3 grid(p.F + 1, p.units);
-  hipLaunchKernelGGL(solve_kernel, grid, dim3(kThreads), 0, s, w.A, w.M, p.dk, p.F + 1);
+  if (p.rule == 0)
+    hipLaunchKernelGGL(solve_kernel, grid, dim3(kThreads), 0, s, w.A, w.M, p.dk, p.F + 1);
+  else
+    hipLaunchKernelGGL(batched_factor_kernel, grid, dim3(kThreads), 0, s, w.A, w.M, w.B, p.dk,
+                       p.dv, p.F + 1, p.U, p.T, p.rule);
   return hipGetLastError();
 }
 

@@ -33,6 +33,7 @@ int make_plan(const vda_desc_t* d, Plan* p) {
   if (!(d->rms_eps >= 0.0f) || !isfinite(d->rms_eps)) return VDA_ERR_INVALID_ARG;
   if (d->seed_mode != 0 && d->seed_mode != 1) return VDA_ERR_INVALID_ARG;
   if (d->anchors != 0 && d->anchors != 1) return VDA_ERR_INVALID_ARG;
+  if (d->rule < 0 || d->rule > 2) return VDA_ERR_INVALID_ARG;
   if (d->units > kMaxGridYZ) return VDA_ERR_INVALID_ARG;
   const int64_t n = d->frames > 0 ? (d->frames + (int64_t)d->chunk - 1) / d->chunk : 0;
   if (n > kMaxGridYZ) return VDA_ERR_INVALID_ARG;
@@ -78,6 +79,7 @@ int make_plan(const vda_desc_t* d, Plan* p) {
   p->eps = d->rms_eps;
   p->seed_mode = d->seed_mode;
   p->anchors = d->anchors;
+  p->rule = d->rule;
   p->dtype = d->in_dtype;
 
   const size_t U_ = (size_t)p->units, Fp1 = (size_t)p->F + 1, N = (size_t)p->n;
@@ -195,6 +197,7 @@ int check_decay(const vda_desc_t* desc, const float* alpha) {
   const int st = make_plan(desc, &p);
   if (st != VDA_OK) return st;
   if (!p.decay_ok) return VDA_ERR_INVALID_ARG;
+  if (p.rule != 0) return VDA_ERR_INVALID_ARG;  // the batched comparison rules run without decay
   if (p.units > 0 && p.F > 0 && !alpha) return VDA_ERR_INVALID_ARG;
   return VDA_OK;
 }

@@ -25,6 +25,7 @@ struct Plan {
   float eps;
   int seed_mode, dtype;
   int anchors;    // 1: frames 0 and F - 1 are boundary anchors
+  int rule;       // 0: frame-wise delta rule; 1, 2: batched comparison rules
   bool decay_ok;  // the decay path's launch grids fit too
   size_t off[9];
   size_t total;

@@ -47,6 +47,15 @@
  * (the linear path is bypassed there); a clip of at most two frames has only
  * zero rows.  An anchor frame therefore acts on the states as the identity.
  *
+ * Comparison rules (desc->rule; [VDN] Sec. 3.1 Eq. (3a)/(3c), App. A.2): rule 1
+ * replaces the frame-wise update of step 2 everywhere (both scans and the text
+ * frame) by SANA-WM's frozen-state batched update S_t = S_{t-1} (I - A_t) + B_t;
+ * rule 2 adds its frame-size key scaling (every key of a frame of N tokens
+ * scaled by 1/sqrt(N): A -> A / N, B -> B / sqrt(N); N = tokens, T for the text
+ * frame).  Their factor I - A is not non-expansive once an eigenvalue of A
+ * passes 2 (rule 1 can overflow on real inputs); they exist for comparison and
+ * run without decay (the decay entry points reject rule != 0).
+ *
  * Layouts (row-major, last index fastest, all tensors contiguous):
  *   q     [units][frames][tokens][d_k]   in_dtype
  *   k     [units][frames][tokens][d_k]   in_dtype (prepared features)
@@ -115,6 +124,7 @@ typedef struct vda_desc {
   int32_t in_dtype;    /* vda_dtype_t of q, k, v, gate, text_k, text_v */
   int32_t out_dtype;   /* vda_dtype_t of out; must equal in_dtype */
   int32_t anchors;     /* 0: no anchors; 1: boundary anchors (see above) */
+  int32_t rule;        /* 0: the frame-wise delta rule; 1, 2: batched comparison rules (above) */
 } vda_desc_t;
 
 /* Bytes of device workspace vda_forward and the debug taps need for `desc`

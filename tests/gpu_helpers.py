@@ -53,7 +53,8 @@ def desc_for(cfg: W.Config, seed_mode=0):
     import frame_wise_delta_gram_amd as vda
     dt = vda.VDA_DTYPE_BF16 if cfg.dtype == "bf16" else vda.VDA_DTYPE_F32
     return vda.make_desc(cfg.units, cfg.frames, cfg.tokens, cfg.text_tokens, cfg.d_k, cfg.d_v,
-                         cfg.chunk, cfg.radius, cfg.rms_eps, seed_mode, dt, int(cfg.anchors))
+                         cfg.chunk, cfg.radius, cfg.rms_eps, seed_mode, dt, int(cfg.anchors),
+                         cfg.rule)
 
 
 def workspace_for(desc):
@@ -90,7 +91,7 @@ def oracle_forward(x: dict, cfg: W.Config, seed_mode=0, taps=False, units=None):
     return oracle.forward(x["q"], x["k"], x["v"], x["beta"], x["gate"], x["text_k"], x["text_v"],
                           x["text_beta"], x["rms_weight"], chunk=cfg.chunk, radius=cfg.radius,
                           eps=cfg.rms_eps, seed_mode=seed_mode, taps=taps, units=units,
-                          alpha=x.get("alpha"), anchors=cfg.anchors)
+                          alpha=x.get("alpha"), anchors=cfg.anchors, rule=cfg.rule)
 
 
 def row_rel_err(got: np.ndarray, ref: np.ndarray) -> float:

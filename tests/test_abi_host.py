@@ -92,6 +92,10 @@ def test_workspace_formula(lib):
     (dict(seed_mode=2), vda.VDA_ERR_INVALID_ARG),
     (dict(anchors=2), vda.VDA_ERR_INVALID_ARG),
     (dict(anchors=1), vda.VDA_OK),
+    (dict(rule=1), vda.VDA_OK),
+    (dict(rule=2), vda.VDA_OK),
+    (dict(rule=3), vda.VDA_ERR_INVALID_ARG),
+    (dict(rule=-1), vda.VDA_ERR_INVALID_ARG),
     (dict(units=70000), vda.VDA_ERR_INVALID_ARG),
     (dict(tokens=4194304), vda.VDA_ERR_INVALID_ARG),
     (dict(text_tokens=4194304), vda.VDA_ERR_INVALID_ARG),
@@ -174,6 +178,8 @@ def test_forward_decay_argument_errors(lib):
         vda.VDA_ERR_WORKSPACE_TOO_SMALL
     bad = desc(d_k=12)
     assert call_forward_decay(lib, bad) == vda.VDA_ERR_INVALID_ARG
+    # the batched comparison rules run without decay
+    assert call_forward_decay(lib, desc(rule=1)) == vda.VDA_ERR_INVALID_ARG
     # empty problems need no gates
     e = desc(units=0)
     assert lib.vda_forward_decay(ctypes.byref(e), *([None] * 12), 0, None) == vda.VDA_OK

@@ -70,6 +70,7 @@ class Config:
     stress: bool = False  # clustered keys
     alpha_mu: float | None = None  # decay gates alpha = sigmoid(N(alpha_mu, 1)); None: no decay
     anchors: bool = False  # boundary anchors: frames 0 and F - 1 out of the linear states
+    rule: int = 0  # 0: frame-wise delta rule; 1, 2: batched comparison rules (SANA-WM)
     chunk: int = 5
     radius: int = 1
     rms_eps: float = 1e-6
