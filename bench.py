@@ -10,8 +10,10 @@ bf16 features, fp32 state), synthetic seeded inputs.
 Prints ONE JSON line: token-heads/s, the roofline of the dominant kernel
 (timed with HIP events recorded by the library on the launch stream), the
 MFMA fraction the metric asks for, the fp64 CPU oracle timed on a bounded
-sample of the same workload on the host cores, and (object "decay") the same
-workload with channel-wise decay gates through vda_forward_decay.
+sample of the same workload on the host cores, (object "batched_rule") the
+same inputs under SANA-WM's batched comparison rule with the boundary-state
+norms of every rule, and (object "decay") the same workload with channel-wise
+decay gates through vda_forward_decay.
 
   python bench.py [--steps K] [--warmup W] [--config 4] [--cpu-seconds S]
   python bench.py --summarize DIR [--config 4]   (profiles/ from rocprofv3 output)
@@ -107,18 +109,22 @@ def measured_traffic(kernel, workload):
 PROFILE_COMMANDS = {  # CFG: the workload id
     "FETCH_SIZE": "timeout -s KILL 120 rocprofv3 --pmc FETCH_SIZE --kernel-include-regex "
                   "'vda|add' -d DIR/FETCH_SIZE -o p --output-format csv -- python bench.py "
-                  "--config CFG --steps 2 --warmup 1 --cpu-seconds 0 --decay-steps 0",
+                  "--config CFG --steps 2 --warmup 1 --cpu-seconds 0 --decay-steps 0 "
+                  "--batched-steps 0",
     "WRITE_SIZE": "timeout -s KILL 120 rocprofv3 --pmc WRITE_SIZE --kernel-include-regex "
                   "'vda|add' -d DIR/WRITE_SIZE -o p --output-format csv -- python bench.py "
-                  "--config CFG --steps 2 --warmup 1 --cpu-seconds 0 --decay-steps 0",
+                  "--config CFG --steps 2 --warmup 1 --cpu-seconds 0 --decay-steps 0 "
+                  "--batched-steps 0",
     "stats": "rocprofv3 --kernel-trace --stats -d DIR/trace -o vda --output-format csv -- "
-             "python bench.py --config CFG --steps 5 --warmup 2 --cpu-seconds 0 --decay-steps 0",
+             "python bench.py --config CFG --steps 5 --warmup 2 --cpu-seconds 0 --decay-steps 0 "
+             "--batched-steps 0",
 }
 KERNELS = ("stats_text", "stats", "solve", "compose", "scan", "readout")  # launch order
 KERNEL_NAMES = {"stats_bf16_kernel": "stats", "stats_f32_kernel": "stats",
                 "stats_text_kernel": "stats_text",
                 "readout_bf16_kernel": "readout", "readout_f32_kernel": "readout",
-                "solve_kernel": "solve", "compose_split_kernel": "compose",
+                "solve_kernel": "solve", "batched_factor_kernel": "solve",
+                "compose_split_kernel": "compose",
                 "compose_kernel": "compose", "scan_split_kernel": "scan", "scan_kernel": "scan"}
 
 
@@ -245,6 +251,43 @@ def cpu_baseline(d, cfg, budget_s):
                       f"x {cfg.tokens} tokens each), fp64 numpy, {elapsed:.1f} s"}
 
 
+def make_desc(cfg):
+    import frame_wise_delta_gram_amd as vda
+    return vda.make_desc(cfg.units, cfg.frames, cfg.tokens, cfg.text_tokens, cfg.d_k, cfg.d_v,
+                         cfg.chunk, cfg.radius, cfg.rms_eps, 0,
+                         vda.VDA_DTYPE_BF16 if cfg.dtype == "bf16" else vda.VDA_DTYPE_F32,
+                         int(cfg.anchors), cfg.rule)
+
+
+def state_growth(cfg, d):
+    """Largest Frobenius norm over all boundary states of all units, for each
+    update rule on the same inputs (App. A.2: the batched rule's factor I - A
+    expands once an eigenvalue of A passes 2)."""
+    import dataclasses
+    import torch
+    import frame_wise_delta_gram_amd as vda
+    res = {}
+    n = cfg.n_chunks
+    P = torch.empty((cfg.units, n + 1, cfg.d_v, cfg.d_k), device="cuda")
+    R = torch.empty_like(P)
+    for rule, name in ((0, "frame-wise (I + A)^-1"), (1, "batched I - A"),
+                       (2, "batched I - A/U, keys / sqrt(U)")):
+        desc = make_desc(dataclasses.replace(cfg, rule=rule))
+        ws = torch.empty(max(vda.vda_workspace_bytes(desc), 1), dtype=torch.uint8,
+                         device="cuda")
+        vda.vda_debug_states(desc, d["k"], d["v"], d["beta"], d["text_k"], d["text_v"],
+                             d["text_beta"], P, R, ws)
+        torch.cuda.synchronize()
+        norms = torch.cat([torch.linalg.matrix_norm(P).flatten(),
+                           torch.linalg.matrix_norm(R).flatten()])
+        fin = torch.isfinite(norms)
+        res[name] = {"max_state_norm": float(norms[fin].max()) if bool(fin.any()) else None,
+                     "seed_norm": float(torch.linalg.matrix_norm(P[:, 0]).max()),
+                     "non_finite_states": int((~fin).sum()), "states": int(norms.numel())}
+        del ws
+    return res
+
+
 def time_steps(cfg, d, steps, warmup):
     """Run the forward pass (vda_forward_timed; decay gates when d holds them)
     warmup + steps times on the current stream; returns (seconds for the timed
@@ -252,9 +295,7 @@ def time_steps(cfg, d, steps, warmup):
     import torch
     import frame_wise_delta_gram_amd as vda
 
-    desc = vda.make_desc(cfg.units, cfg.frames, cfg.tokens, cfg.text_tokens, cfg.d_k, cfg.d_v,
-                         cfg.chunk, cfg.radius, cfg.rms_eps, 0,
-                         vda.VDA_DTYPE_BF16 if cfg.dtype == "bf16" else vda.VDA_DTYPE_F32)
+    desc = make_desc(cfg)
     ws = torch.empty(max(vda.vda_workspace_bytes(desc), 1), dtype=torch.uint8, device="cuda")
     out = torch.empty((cfg.units, cfg.frames, cfg.tokens, cfg.d_v), device="cuda",
                       dtype=d["q"].dtype)
@@ -326,6 +367,9 @@ def main():
     ap.add_argument("--decay-steps", type=int, default=None,
                     help="steps of the decay measurement that follows the 768p-bf16 one "
                          "(default: --steps; 0 disables it)")
+    ap.add_argument("--batched-steps", type=int, default=None,
+                    help="steps of the batched comparison rule measurement on the 768p-bf16 "
+                         "inputs (default: --steps; 0 disables it)")
     ap.add_argument("--summarize", metavar="DIR",
                     help="write the profiles/ summaries from rocprofv3 output under DIR and exit")
     args = ap.parse_args()
@@ -401,6 +445,18 @@ def main():
         line["cpu_baseline"] = cpu_baseline(d, cfg, args.cpu_seconds)
     else:
         line["cpu_baseline"] = None
+    line["batched_rule"] = None
+    if args.config == 4 and args.batched_steps != 0:
+        import dataclasses
+        bcfg = dataclasses.replace(cfg, rule=2)
+        bsteps = args.steps if args.batched_steps is None else args.batched_steps
+        el, ms = time_steps(bcfg, d, bsteps, args.warmup)
+        bvalue = th * bsteps / el
+        line["batched_rule"] = {
+            "workload": cfg.name, "rule": "SANA-WM frozen-state batched update with frame-size "
+            "key scaling (rule 2)", "steps": bsteps, "ms_per_step": el * 1e3 / bsteps,
+            "value": bvalue, "unit": "token-heads/s", "relative_to_vda": bvalue / value,
+            "stage_ms": ms, "state_growth": state_growth(cfg, d)}
     decay_steps = args.steps if args.decay_steps is None else args.decay_steps
     line["decay"] = None
     if decay_steps > 0 and args.config == 4:
