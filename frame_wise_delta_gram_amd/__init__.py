@@ -6,7 +6,8 @@ package is its ctypes binding (argument marshalling only) and its build step.
 from .binding import (  # noqa: F401
     EXPORTED, LIB_PATH, VDA_DTYPE_BF16, VDA_DTYPE_F32, VDA_ERR_BAD_DTYPE, VDA_ERR_HIP,
     VDA_ERR_INVALID_ARG, VDA_ERR_MISALIGNED, VDA_ERR_WORKSPACE_TOO_SMALL, VDA_OK, VdaDesc,
-    VdaError, desc_from_tensors, forward, load_library, make_desc, vda_check_desc,
+    VdaError, VdaPrepDesc, desc_from_tensors, forward, load_library, make_desc, make_prep_desc,
+    vda_check_desc, vda_prep, vda_prep_check_desc,
     vda_debug_chunks, vda_debug_chunks_decay, vda_debug_solve, vda_debug_stats,
     vda_debug_states, vda_debug_states_decay, vda_forward, vda_forward_decay, vda_forward_timed,
     vda_status_string, vda_workspace_bytes,

@@ -27,7 +27,7 @@ VDA_DTYPE_BF16 = 1
 EXPORTED = ("vda_workspace_bytes", "vda_check_desc", "vda_forward", "vda_forward_timed",
             "vda_forward_decay", "vda_debug_stats", "vda_debug_solve", "vda_debug_chunks",
             "vda_debug_chunks_decay", "vda_debug_states", "vda_debug_states_decay",
-            "vda_status_string")
+            "vda_prep", "vda_prep_check_desc", "vda_status_string")
 
 
 class VdaDesc(ctypes.Structure):
@@ -43,6 +43,15 @@ class VdaDesc(ctypes.Structure):
     @property
     def n_chunks(self):
         return -(-self.frames // self.chunk) if self.frames > 0 else 0
+
+
+class VdaPrepDesc(ctypes.Structure):
+    """vda_prep_desc_t of include/vda.h."""
+    _fields_ = [
+        ("batch", ctypes.c_int32), ("heads", ctypes.c_int32), ("frames", ctypes.c_int32),
+        ("height", ctypes.c_int32), ("width", ctypes.c_int32), ("d_k", ctypes.c_int32),
+        ("d_v", ctypes.c_int32), ("eps", ctypes.c_float), ("dtype", ctypes.c_int32),
+    ]
 
 
 class VdaError(RuntimeError):
@@ -92,6 +101,11 @@ def load_library(path: str = LIB_PATH):
     lib.vda_debug_chunks.restype = ctypes.c_int
     lib.vda_debug_states.argtypes = [D] + [P] * 9 + [ctypes.c_size_t, P]
     lib.vda_debug_states.restype = ctypes.c_int
+    DP = ctypes.POINTER(VdaPrepDesc)
+    lib.vda_prep_check_desc.argtypes = [DP]
+    lib.vda_prep_check_desc.restype = ctypes.c_int
+    lib.vda_prep.argtypes = [DP] + [P] * 10 + [P]
+    lib.vda_prep.restype = ctypes.c_int
     lib.vda_status_string.argtypes = [ctypes.c_int]
     lib.vda_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -233,6 +247,23 @@ def vda_debug_states_decay(desc, k, v, beta, alpha, text_k, text_v, text_beta, P
         _ptr(text_v), _ptr(text_beta), _ptr(P_out), _ptr(R_out), _ptr(workspace),
         _ws_bytes(workspace, workspace_bytes), _stream(stream))
     _check(st, "vda_debug_states_decay")
+
+
+def make_prep_desc(batch, heads, frames, height, width, d_k, d_v, eps=1e-6,
+                   dtype=VDA_DTYPE_BF16) -> VdaPrepDesc:
+    return VdaPrepDesc(batch, heads, frames, height, width, d_k, d_v, eps, dtype)
+
+
+def vda_prep_check_desc(desc: VdaPrepDesc) -> int:
+    return int(load_library().vda_prep_check_desc(ctypes.byref(desc)))
+
+
+def vda_prep(desc, q, k, v, wk_s, wk_t, wv_s, wv_t, q_out, k_out, v_out, stream=None):
+    """C vda_prep: the feature map from projection outputs to prepared features."""
+    st = load_library().vda_prep(
+        ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(wk_s), _ptr(wk_t), _ptr(wv_s),
+        _ptr(wv_t), _ptr(q_out), _ptr(k_out), _ptr(v_out), _stream(stream))
+    _check(st, "vda_prep")
 
 
 # ----------------------------------------------------------------------------- torch helpers

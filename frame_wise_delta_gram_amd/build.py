@@ -18,7 +18,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_PATH = os.path.join(PKG, "libvda.so")
-SOURCES = ["k_stats.hip", "k_solve.hip", "k_scan.hip", "k_readout.hip", "vda_api.hip"]
+SOURCES = ["k_stats.hip", "k_solve.hip", "k_scan.hip", "k_readout.hip", "k_prep.hip",
+           "vda_api.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

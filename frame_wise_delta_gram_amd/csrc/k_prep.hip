@@ -1,0 +1,315 @@
+// Feature map of the linear branch ("Video DeltaNet", arXiv 2609.20744,
+// Sec. 2.3; fused with the layout conversion as Sec. 5 "Fused VDA kernels"
+// describes):
+//   K' = L2(SiLU(conv(K))),   V' = SiLU(conv(V)),   Q' = L2(Q)
+// conv: depthwise (one filter per head and channel) separable short
+// convolution, a 5 x 5 spatial and a five-tap temporal filter, applied as the
+// centred 3-D correlation with kernel w_t[tau] w_s[a][b] and zero padding at
+// the clip's and the frame's borders.  L2(x) = x / max(||x||_2, eps) over the d
+// channels of one (token, head).  Input layout: the projection output
+// [batch][F][H_l][W_l][heads][d]; output: [batch * heads][F][H_l * W_l][d].
+//
+// conv kernel: one workgroup (8 waves) per (unit, 8 x 8 spatial tile), sweeping
+// all frames.  Per input frame the 12 x 12 halo tile of the unit's channels is
+// staged in LDS as fp32 (converted once) while the next frame's tile is in
+// flight in registers.  Wave w owns output row w of the tile, lane l the
+// channel pair 2l, 2l + 1: its 8 outputs x 2 channels are a 5 x 12 window
+// product (read once per window row, 8-byte conflict-free LDS reads); the
+// spatial taps of the unit's channels sit in LDS (one 8-byte read per tap
+// serves the lane's 8 outputs), its five temporal taps in registers.  The temporal filter runs
+// in scatter form: input frame t adds w_t[tau] times its spatial result to the
+// pending outputs t + 2 - tau, kept in a ring of five register sets (the frame
+// loop is unrolled by five so every ring index is static); output frame t - 2
+// is then complete: SiLU, the channel sum of squares across the wave's 64
+// lanes, scaling, one 256-byte row per position.  The kernel does about 30
+// fp32 FMA per output element against 4 bytes (bf16 in + out) of HBM traffic,
+// so it is bound by the vector ALUs rather than by HBM.
+#include <type_traits>
+
+#include "vda_device.h"
+#include "vda_internal.h"
+
+namespace vda {
+namespace {
+
+constexpr int kTR = 8;            // output tile rows
+constexpr int kTC = 8;            // output tile columns
+constexpr int kHR = kTR + 4;      // halo tile rows
+constexpr int kHC = kTC + 4;      // halo tile columns
+constexpr int kPrepThreads = 512;
+
+// 16-byte pieces of a tensor element type: 8 bf16 or 4 fp32 channels
+template <typename T>
+struct Piece;
+template <>
+struct Piece<uint16_t> {
+  static constexpr int kElems = 8;
+  __device__ static void to_f32(const u32x4_t& v, float* out) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      out[2 * e] = bf16_lo(v[e]);
+      out[2 * e + 1] = bf16_hi(v[e]);
+    }
+  }
+};
+template <>
+struct Piece<float> {
+  static constexpr int kElems = 4;
+  __device__ static void to_f32(const u32x4_t& v, float* out) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) out[e] = __uint_as_float(v[e]);
+  }
+};
+
+__device__ __forceinline__ void store2(uint16_t* p, float a, float b) {
+  *reinterpret_cast<uint32_t*>(p) = pack_bf16(a, b);
+}
+__device__ __forceinline__ void store2(float* p, float a, float b) {
+  *reinterpret_cast<float2*>(p) = make_float2(a, b);
+}
+
+__device__ __forceinline__ float silu(float x) {
+  return x * __builtin_amdgcn_rcpf(1.0f + __expf(-x));
+}
+
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) x += __shfl_xor(x, m);
+  return x;
+}
+
+template <typename T, bool NORM>
+__global__ __launch_bounds__(kPrepThreads, 1) void prep_conv_kernel(
+    const T* __restrict__ x, const float* __restrict__ ws, const float* __restrict__ wt,
+    T* __restrict__ y, int F, int Hl, int Wl, int H, int d, int tiles_r, int tiles_c, int units,
+    unsigned per, float eps) {
+  __shared__ __align__(16) float Xs[kHR * kHC * 128];  // one frame's halo tile, [pos][channel]
+  __shared__ __align__(16) float Ws[25 * 128];          // spatial taps, [tap][channel]
+  constexpr int EPP = Piece<T>::kElems;
+  constexpr int kIter = (kHR * kHC * (128 / EPP) + kPrepThreads - 1) / kPrepThreads;
+  const unsigned ntiles = (unsigned)tiles_r * tiles_c;
+  const unsigned item = xcd_item(per);
+  if (item >= (unsigned)units * ntiles) return;
+  const int unit = item / ntiles;
+  const int tile = item - unit * ntiles;
+  const int b = unit / H;
+  const int h = unit - b * H;
+  const int r0 = (tile / tiles_c) * kTR;
+  const int c0 = (tile % tiles_c) * kTC;
+  const int t = threadIdx.x;
+  const int lane = t & 63;
+  const int w = t >> 6;
+  const int ch = 2 * lane;
+  const bool cact = ch < d;
+  const int U = Hl * Wl;
+
+  // filters of head h: spatial taps to LDS (zero for channels past d, which
+  // only idle lanes read), this lane's temporal taps (channels ch, ch + 1)
+  for (int i = t; i < 25 * 128; i += kPrepThreads) {
+    const int tap = i >> 7;
+    const int c = i & 127;
+    Ws[i] = c < d ? ws[((size_t)h * d + c) * 25 + tap] : 0.0f;
+  }
+  float ft[2][5];
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    const size_t c = (size_t)h * d + (cact ? ch + e : 0);
+#pragma unroll
+    for (int i = 0; i < 5; ++i) ft[e][i] = cact ? wt[c * 5 + i] : 0.0f;
+  }
+
+  // staging: 16-byte pieces of the halo tile's positions
+  const int gpp = d / EPP;  // pieces per position
+  const int npieces = kHR * kHC * gpp;
+  u32x4_t pre[kIter];
+  auto load_frame = [&](int tin) {
+#pragma unroll
+    for (int i = 0; i < kIter; ++i) {
+      const int p = t + kPrepThreads * i;
+      const int pos = p / gpp;
+      const int cg = p - pos * gpp;
+      const int gi = r0 - 2 + pos / kHC;
+      const int gj = c0 - 2 + pos % kHC;
+      const bool ok = p < npieces && gi >= 0 && gi < Hl && gj >= 0 && gj < Wl;
+      const size_t off = ((((size_t)b * F + tin) * Hl + (ok ? gi : 0)) * Wl + (ok ? gj : 0)) * H + h;
+      pre[i] = ok ? *reinterpret_cast<const u32x4_t*>(x + off * d + cg * EPP)
+                  : u32x4_t{0u, 0u, 0u, 0u};
+    }
+  };
+  auto store_frame = [&]() {
+#pragma unroll
+    for (int i = 0; i < kIter; ++i) {
+      const int p = t + kPrepThreads * i;
+      if (p >= npieces) continue;
+      const int pos = p / gpp;
+      const int cg = p - pos * gpp;
+      float v[EPP];
+      Piece<T>::to_f32(pre[i], v);
+      float* dst = Xs + pos * 128 + cg * EPP;
+#pragma unroll
+      for (int e = 0; e < EPP; e += 4)
+        *reinterpret_cast<f32x4_t*>(dst + e) = f32x4_t{v[e], v[e + 1], v[e + 2], v[e + 3]};
+    }
+  };
+
+  float acc[5][2][kTC];
+#pragma unroll
+  for (int s = 0; s < 5; ++s)
+#pragma unroll
+    for (int e = 0; e < 2; ++e)
+#pragma unroll
+      for (int o = 0; o < kTC; ++o) acc[s][e][o] = 0.0f;
+
+  const int gi_out = r0 + w;
+  // one input frame tin (k = tin mod 5): spatial product of the staged tile,
+  // scatter into the ring, then output frame tin - 2 is complete
+  auto step = [&](int tin, auto kc) {
+    constexpr int k = decltype(kc)::value;
+    if (tin < F) store_frame();
+    if (tin + 1 < F) load_frame(tin + 1);  // in flight during the products below
+    __syncthreads();
+    if (tin < F) {
+      float s[2][kTC];
+#pragma unroll
+      for (int e = 0; e < 2; ++e)
+#pragma unroll
+        for (int o = 0; o < kTC; ++o) s[e][o] = 0.0f;
+#pragma unroll
+      for (int a = 0; a < 5; ++a) {
+        float xr[2][kHC];
+        const float* row = Xs + ((w + a) * kHC) * 128 + ch;
+#pragma unroll
+        for (int c = 0; c < kHC; ++c) {
+          const float2 v = *reinterpret_cast<const float2*>(row + c * 128);
+          xr[0][c] = v.x;
+          xr[1][c] = v.y;
+        }
+#pragma unroll
+        for (int bb = 0; bb < 5; ++bb) {
+          const float2 f = *reinterpret_cast<const float2*>(Ws + (a * 5 + bb) * 128 + ch);
+#pragma unroll
+          for (int o = 0; o < kTC; ++o) {
+            s[0][o] = fmaf(f.x, xr[0][o + bb], s[0][o]);
+            s[1][o] = fmaf(f.y, xr[1][o + bb], s[1][o]);
+          }
+        }
+      }
+      // input frame tin feeds output frame t_out = tin + 2 - tau with w_t[tau];
+      // ring slot t_out mod 5 = (k + 2 - tau) mod 5
+#pragma unroll
+      for (int sl = 0; sl < 5; ++sl) {
+        const int tau = (k + 2 - sl + 10) % 5;
+#pragma unroll
+        for (int e = 0; e < 2; ++e)
+#pragma unroll
+          for (int o = 0; o < kTC; ++o) acc[sl][e][o] = fmaf(ft[e][tau], s[e][o], acc[sl][e][o]);
+      }
+    }
+    // output frame tin - 2 (ring slot (k + 3) mod 5) is complete
+    constexpr int fin = (k + 3) % 5;
+    const int t_out = tin - 2;
+    if (t_out >= 0) {
+#pragma unroll
+      for (int o = 0; o < kTC; ++o) {
+        float v0 = silu(acc[fin][0][o]);
+        float v1 = silu(acc[fin][1][o]);
+        if (NORM) {
+          const float ss = wave_sum(cact ? v0 * v0 + v1 * v1 : 0.0f);
+          const float inv = 1.0f / fmaxf(sqrtf(ss), eps);
+          v0 *= inv;
+          v1 *= inv;
+        }
+        const int gj = c0 + o;
+        if (cact && gi_out < Hl && gj < Wl)
+          store2(y + (((size_t)unit * F + t_out) * U + (size_t)gi_out * Wl + gj) * d + ch, v0, v1);
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 2; ++e)
+#pragma unroll
+      for (int o = 0; o < kTC; ++o) acc[fin][e][o] = 0.0f;
+    __syncthreads();  // every wave is done with the staged tile
+  };
+
+  if (F > 0) load_frame(0);
+  for (int tb = 0; tb < F + 2; tb += 5) {
+    step(tb, std::integral_constant<int, 0>{});
+    if (tb + 1 < F + 2) step(tb + 1, std::integral_constant<int, 1>{});
+    if (tb + 2 < F + 2) step(tb + 2, std::integral_constant<int, 2>{});
+    if (tb + 3 < F + 2) step(tb + 3, std::integral_constant<int, 3>{});
+    if (tb + 4 < F + 2) step(tb + 4, std::integral_constant<int, 4>{});
+  }
+}
+
+// Q' = L2(Q) with the layout conversion: G = d / EPP lanes per (token, head)
+// row, rows taken in input order (contiguous reads), each written as one
+// contiguous row of its unit.
+template <typename T>
+__global__ __launch_bounds__(256) void prep_q_kernel(const T* __restrict__ x, T* __restrict__ y,
+                                                     long rows, int F, int U, int H, int d,
+                                                     float eps) {
+  constexpr int EPP = Piece<T>::kElems;
+  constexpr int G = 128 / EPP;  // lanes per row (some idle when d < 128)
+  const int lane = threadIdx.x & 63;
+  const int sub = lane % G;
+  const int rows_per_wave = 64 / G;
+  const long wave = ((long)blockIdx.x * blockDim.x + threadIdx.x) / 64;
+  const long nwaves = (long)gridDim.x * blockDim.x / 64;
+  const bool act = sub * EPP < d;
+  for (long r0 = wave * rows_per_wave; r0 < rows; r0 += nwaves * rows_per_wave) {
+    const long r = r0 + lane / G;  // (b, t, p, h) row in input order
+    const bool ok = r < rows && act;
+    u32x4_t raw = ok ? *reinterpret_cast<const u32x4_t*>(x + r * d + sub * EPP)
+                     : u32x4_t{0u, 0u, 0u, 0u};
+    float v[EPP];
+    Piece<T>::to_f32(raw, v);
+    float ss = 0.0f;
+#pragma unroll
+    for (int e = 0; e < EPP; ++e) ss = fmaf(v[e], v[e], ss);
+#pragma unroll
+    for (int m = G / 2; m >= 1; m >>= 1) ss += __shfl_xor(ss, m);
+    const float inv = 1.0f / fmaxf(sqrtf(ss), eps);
+    if (!ok) continue;
+    const long h = r % H;
+    const long tp = r / H;  // (b F + t) U + p
+    const long p = tp % U;
+    const long bt = tp / U;  // b F + t
+    const long t = bt % F;
+    const long b = bt / F;
+    T* dst = y + ((((b * H + h) * F + t) * U + p) * d + sub * EPP);
+#pragma unroll
+    for (int e = 0; e < EPP; e += 2) store2(dst + e, v[e] * inv, v[e + 1] * inv);
+  }
+}
+
+template <typename T>
+hipError_t launch_prep_typed(const PrepPlan& p, const void* q, const void* k, const void* v,
+                             const float* wk_s, const float* wk_t, const float* wv_s,
+                             const float* wv_t, void* qo, void* ko, void* vo, hipStream_t s) {
+  const long rows = (long)p.batch * p.F * p.U * p.H;
+  if (rows > 0) {
+    hipLaunchKernelGGL(prep_q_kernel<T>, dim3(2048), dim3(256), 0, s, static_cast<const T*>(q),
+                       static_cast<T*>(qo), rows, p.F, p.U, p.H, p.dk, p.eps);
+    const unsigned items = (unsigned)(p.batch * p.H) * p.tiles_r * p.tiles_c;
+    const unsigned per = xcd_per(items);
+    hipLaunchKernelGGL((prep_conv_kernel<T, true>), dim3(kXcds * per), dim3(kPrepThreads), 0, s,
+                       static_cast<const T*>(k), wk_s, wk_t, static_cast<T*>(ko), p.F, p.Hl,
+                       p.Wl, p.H, p.dk, p.tiles_r, p.tiles_c, p.batch * p.H, per, p.eps);
+    hipLaunchKernelGGL((prep_conv_kernel<T, false>), dim3(kXcds * per), dim3(kPrepThreads), 0,
+                       s, static_cast<const T*>(v), wv_s, wv_t, static_cast<T*>(vo), p.F, p.Hl,
+                       p.Wl, p.H, p.dv, p.tiles_r, p.tiles_c, p.batch * p.H, per, p.eps);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_prep(const PrepPlan& p, const void* q, const void* k, const void* v,
+                       const float* wk_s, const float* wk_t, const float* wv_s, const float* wv_t,
+                       void* qo, void* ko, void* vo, hipStream_t s) {
+  if (p.dtype == VDA_DTYPE_BF16)
+    return launch_prep_typed<uint16_t>(p, q, k, v, wk_s, wk_t, wv_s, wv_t, qo, ko, vo, s);
+  return launch_prep_typed<float>(p, q, k, v, wk_s, wk_t, wv_s, wv_t, qo, ko, vo, s);
+}
+
+}  // namespace vda

@@ -261,6 +261,45 @@ int states_impl(const vda_desc_t* desc, const void* k, const void* v, const floa
 }  // namespace
 }  // namespace vda
 
+namespace vda {
+namespace {
+
+int make_prep_plan(const vda_prep_desc_t* d, PrepPlan* p) {
+  if (!d) return VDA_ERR_INVALID_ARG;
+  if (d->dtype != VDA_DTYPE_F32 && d->dtype != VDA_DTYPE_BF16) return VDA_ERR_BAD_DTYPE;
+  if (d->batch < 0 || d->heads < 0 || d->frames < 0 || d->height < 0 || d->width < 0)
+    return VDA_ERR_INVALID_ARG;
+  if ((int64_t)d->batch * d->heads > kMaxGridYZ) return VDA_ERR_INVALID_ARG;
+  if (d->frames > kMaxFrames) return VDA_ERR_INVALID_ARG;
+  if ((int64_t)d->height * d->width > 4194303) return VDA_ERR_INVALID_ARG;
+  if (d->d_k < 16 || d->d_k > 128 || d->d_k % 16) return VDA_ERR_INVALID_ARG;
+  if (d->d_v < 16 || d->d_v > 128 || d->d_v % 16) return VDA_ERR_INVALID_ARG;
+  if (!(d->eps > 0.0f) || !isfinite(d->eps)) return VDA_ERR_INVALID_ARG;
+  int64_t x;
+  const int64_t units = (int64_t)d->batch * d->heads;
+  if (!mul_ok(units * d->frames, (int64_t)d->height * d->width, &x) || !mul_ok(x, 128, &x))
+    return VDA_ERR_INVALID_ARG;
+  p->batch = d->batch;
+  p->H = d->heads;
+  p->F = d->frames;
+  p->Hl = d->height;
+  p->Wl = d->width;
+  p->U = d->height * d->width;
+  p->dk = d->d_k;
+  p->dv = d->d_v;
+  p->dtype = d->dtype;
+  p->eps = d->eps;
+  p->tiles_r = (d->height + 7) / 8;  // 8 x 8 output tiles of the convolution
+  p->tiles_c = (d->width + 7) / 8;
+  // the convolution's 1-D grid: fewer than 2^22 workgroups of 512 threads
+  if (!mul_ok(units, (int64_t)p->tiles_r * p->tiles_c, &x) || x >= (INT64_C(1) << 22))
+    return VDA_ERR_INVALID_ARG;
+  return VDA_OK;
+}
+
+}  // namespace
+}  // namespace vda
+
 using vda::Plan;
 using vda::WsPtrs;
 
@@ -393,6 +432,30 @@ int vda_debug_states_decay(const vda_desc_t* desc, const void* k, const void* v,
   if (st != VDA_OK) return st;
   return vda::states_impl(desc, k, v, beta, alpha, text_k, text_v, text_beta, P_out, R_out,
                           workspace, workspace_bytes, stream);
+}
+
+int vda_prep_check_desc(const vda_prep_desc_t* desc) {
+  vda::PrepPlan p;
+  return vda::make_prep_plan(desc, &p);
+}
+
+int vda_prep(const vda_prep_desc_t* desc, const void* q, const void* k, const void* v,
+             const float* wk_s, const float* wk_t, const float* wv_s, const float* wv_t,
+             void* q_out, void* k_out, void* v_out, vda_stream_t stream) {
+  vda::PrepPlan p;
+  const int st = vda::make_prep_plan(desc, &p);
+  if (st != VDA_OK) return st;
+  const int64_t rows = (int64_t)p.batch * p.H * p.F * p.U;
+  if (rows == 0) return VDA_OK;
+  if (!q || !k || !v || !q_out || !k_out || !v_out || !wk_s || !wk_t || !wv_s || !wv_t)
+    return VDA_ERR_INVALID_ARG;
+  for (const void* ptr : {q, k, v, static_cast<const void*>(q_out), static_cast<const void*>(k_out),
+                          static_cast<const void*>(v_out)})
+    if (!vda::aligned(ptr, 16)) return VDA_ERR_MISALIGNED;
+  for (const float* ptr : {wk_s, wk_t, wv_s, wv_t})
+    if (!vda::aligned(ptr, 4)) return VDA_ERR_MISALIGNED;
+  return vda::hip_status(vda::launch_prep(p, q, k, v, wk_s, wk_t, wv_s, wv_t, q_out, k_out, v_out,
+                                          reinterpret_cast<hipStream_t>(stream)));
 }
 
 const char* vda_status_string(int status) {

@@ -31,6 +31,15 @@ struct Plan {
   size_t total;
 };
 
+// Feature-map (prep) launch: batch x heads units of F frames of Hl x Wl tokens
+struct PrepPlan {
+  int batch, H, F, Hl, Wl, U, dk, dv, dtype, tiles_r, tiles_c;
+  float eps;
+};
+hipError_t launch_prep(const PrepPlan& p, const void* q, const void* k, const void* v,
+                       const float* wk_s, const float* wk_t, const float* wv_s, const float* wv_t,
+                       void* qo, void* ko, void* vo, hipStream_t s);
+
 struct WsPtrs {
   float *A, *B, *M, *Mc, *Jf, *Jr, *ST, *McT, *MrT;
 };

@@ -177,6 +177,46 @@ int vda_forward_decay(const vda_desc_t* desc, const void* q, const void* k, cons
                       const float* rms_weight, void* out, void* workspace, size_t workspace_bytes,
                       vda_stream_t stream);
 
+/* ---- feature map (VDA-Prep; [VDN] Sec. 2.3, fused as in Sec. 5) ----
+ * From the QKV projection outputs to the prepared features vda_forward takes:
+ *   K' = L2(SiLU(conv_k(K))),  V' = SiLU(conv_v(V)),  Q' = L2(Q)
+ * conv: depthwise (one filter per head and channel) separable short
+ * convolution -- a 5 x 5 spatial filter w_s and a five-tap temporal filter
+ * w_t -- applied as the centred correlation
+ *   y[t][i][j] = sum_{tau,a,b} w_t[tau] w_s[a][b] x[t+tau-2][i+a-2][j+b-2]
+ * with zero padding at the clip's and the frame's borders; SiLU(x) =
+ * x sigmoid(x); L2(x) = x / max(||x||_2, eps) over the d channels of one
+ * (token, head).  Layouts:
+ *   q, k in   [batch][frames][height][width][heads][d_k]   dtype
+ *   v in      [batch][frames][height][width][heads][d_v]   dtype
+ *   wk_s [heads][d_k][5][5], wk_t [heads][d_k][5], wv_s [heads][d_v][5][5],
+ *   wv_t [heads][d_v][5]                                   float32
+ *   q, k out  [batch * heads][frames][height * width][d_k] dtype (unit = b * heads + h)
+ *   v out     [batch * heads][frames][height * width][d_v] dtype
+ * The outputs are exactly the q, k, v layouts of vda_forward (tokens =
+ * height * width).  Outputs must not overlap inputs. */
+typedef struct vda_prep_desc {
+  int32_t batch;  /* >= 0 */
+  int32_t heads;  /* >= 0; batch x heads <= 65535 */
+  int32_t frames; /* 0..2^20 */
+  int32_t height; /* latent rows H_l >= 0 */
+  int32_t width;  /* latent columns W_l >= 0; height x width <= 4194303 */
+  int32_t d_k;    /* channels of q and k: multiple of 16, 16..128 */
+  int32_t d_v;    /* channels of v: multiple of 16, 16..128 */
+  float eps;      /* L2 normalisation floor: finite, > 0 */
+  int32_t dtype;  /* vda_dtype_t of q, k, v in and out */
+} vda_prep_desc_t;
+
+/* Checks desc alone (host-only); VDA_OK or the error vda_prep would return. */
+int vda_prep_check_desc(const vda_prep_desc_t* desc);
+
+/* Enqueues the feature map on `stream`.  Tensors 16-byte aligned, filters
+ * 4-byte aligned; pointers of empty tensors may be NULL.  The caller owns
+ * every buffer; nothing is allocated. */
+int vda_prep(const vda_prep_desc_t* desc, const void* q, const void* k, const void* v,
+             const float* wk_s, const float* wk_t, const float* wv_s, const float* wv_t,
+             void* q_out, void* k_out, void* v_out, vda_stream_t stream);
+
 /* ---- debug taps (tests only).  Each runs the pipeline up to the named stage in
  * the caller's workspace and copies that stage's fp32 results to caller
  * buffers (device pointers, row-major, contiguous). ---- */

@@ -20,7 +20,7 @@ def pytest_collection_modifyitems(config, items):
     # run the GPU suite in a fixed order: layout probes, stages, parity, full size
     order = {"test_gpu_layout": 0, "test_gpu_stages": 1, "test_gpu_parity": 2,
              "test_gpu_decay": 3, "test_gpu_anchors": 3,
-             "test_gpu_batched": 3, "test_gpu_fullsize": 4}
+             "test_gpu_batched": 3, "test_gpu_prep": 3, "test_gpu_fullsize": 4}
 
     def key(item):
         mod = item.module.__name__.rsplit(".", 1)[-1]

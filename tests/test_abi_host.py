@@ -39,6 +39,55 @@ def test_descriptor_layout_matches_header():
     assert ctypes.sizeof(vda.VdaDesc) == 4 * len(fields)
 
 
+def test_prep_descriptor_layout_matches_header():
+    src = open(HEADER).read()
+    body = re.search(r"typedef struct vda_prep_desc \{(.*?)\} vda_prep_desc_t;", src,
+                     flags=re.S).group(1)
+    body = re.sub(r"/\*.*?\*/", "", body, flags=re.S)
+    fields = re.findall(r"(int32_t|float)\s+(\w+);", body)
+    assert [n for _, n in fields] == [n for n, _ in vda.VdaPrepDesc._fields_]
+    assert ctypes.sizeof(vda.VdaPrepDesc) == 4 * len(fields)
+
+
+def prep_desc(**kw):
+    base = dict(batch=2, heads=3, frames=7, height=9, width=13, d_k=64, d_v=32, eps=1e-6,
+                dtype=vda.VDA_DTYPE_BF16)
+    base.update(kw)
+    return vda.make_prep_desc(**base)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(), vda.VDA_OK),
+    (dict(batch=-1), vda.VDA_ERR_INVALID_ARG),
+    (dict(width=-2), vda.VDA_ERR_INVALID_ARG),
+    (dict(d_k=24), vda.VDA_ERR_INVALID_ARG),
+    (dict(d_v=256), vda.VDA_ERR_INVALID_ARG),
+    (dict(eps=0.0), vda.VDA_ERR_INVALID_ARG),
+    (dict(eps=float("nan")), vda.VDA_ERR_INVALID_ARG),
+    (dict(dtype=5), vda.VDA_ERR_BAD_DTYPE),
+    (dict(batch=300, heads=300), vda.VDA_ERR_INVALID_ARG),
+    (dict(height=2048, width=2048), vda.VDA_ERR_INVALID_ARG),
+    (dict(frames=(1 << 20) + 1), vda.VDA_ERR_INVALID_ARG),
+    (dict(batch=0), vda.VDA_OK),
+    (dict(height=0), vda.VDA_OK),
+])
+def test_prep_descriptor_checks(lib, kw, status):
+    assert vda.vda_prep_check_desc(prep_desc(**kw)) == status
+
+
+def test_prep_argument_errors(lib):
+    d = prep_desc()
+    P = [4096 * (i + 1) for i in range(10)]
+    assert lib.vda_prep(ctypes.byref(d), None, *P[1:], None) == vda.VDA_ERR_INVALID_ARG
+    assert lib.vda_prep(ctypes.byref(d), *P[:9], None, None) == vda.VDA_ERR_INVALID_ARG
+    assert lib.vda_prep(ctypes.byref(d), P[0] + 8, *P[1:], None) == vda.VDA_ERR_MISALIGNED
+    assert lib.vda_prep(ctypes.byref(d), *P[:3], P[3] + 2, *P[4:], None) == \
+        vda.VDA_ERR_MISALIGNED
+    assert lib.vda_prep(None, *P, None) == vda.VDA_ERR_INVALID_ARG
+    e = prep_desc(frames=0)
+    assert lib.vda_prep(ctypes.byref(e), *([None] * 10), None) == vda.VDA_OK
+
+
 def test_package_exposes_every_entry_point():
     for name in vda.EXPORTED:
         assert callable(getattr(vda, name, None)), name

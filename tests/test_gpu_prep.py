@@ -1,0 +1,136 @@
+"""The feature map (VDA-Prep: "Video DeltaNet" Sec. 2.3, fused as in Sec. 5) on
+the HIP path through vda_prep, against the fp64 oracle (oracle/prep_oracle.py).
+
+Bar: per output row (unit, frame, token) ||gpu - oracle||_inf / ||oracle||_inf
+<= 1e-4 for fp32 features and 2e-2 for bf16 (bf16 in, fp32 arithmetic, bf16
+out).  Every row of every unit on the small shapes; at the 768p share, whole
+units of q' and sampled units of k' and v' over the first and last six frames
+(the oracle's clip prefix / suffix gives those frames exactly: an output frame
+reads input frames t - 2 .. t + 2).
+"""
+import dataclasses
+
+import numpy as np
+import pytest
+
+import workloads as W
+from gpu_helpers import require_gpu, row_rel_err, say
+
+pytestmark = pytest.mark.gpu
+
+P = W.PrepConfig
+SHAPES = {
+    "tiny-f32": W.PREP_CONFIGS[1],
+    "small-bf16": W.PREP_CONFIGS[2],
+    "partial-tiles-bf16": P(711, "partial-tiles-bf16", 1, 2, 9, 11, 13, 128, 128, "bf16"),
+    "smaller-than-tile-bf16": P(712, "smaller-than-tile-bf16", 2, 1, 4, 3, 5, 32, 48, "bf16"),
+    "one-frame-bf16": P(713, "one-frame-bf16", 1, 3, 1, 9, 9, 64, 64, "bf16"),
+    "two-frames-f32": P(714, "two-frames-f32", 1, 1, 2, 10, 6, 16, 16, "f32"),
+    "dk16-dv128-bf16": P(715, "dk16-dv128-bf16", 2, 2, 6, 8, 16, 16, 128, "bf16"),
+    "dk128-f32": P(716, "dk128-f32", 1, 2, 7, 9, 17, 128, 64, "f32"),
+}
+
+TOL = {"f32": 1e-4, "bf16": 2e-2}
+
+
+def _run(cfg, h):
+    import torch
+    import frame_wise_delta_gram_amd as vda
+    dt = vda.VDA_DTYPE_BF16 if cfg.dtype == "bf16" else vda.VDA_DTYPE_F32
+    desc = vda.make_prep_desc(cfg.batch, cfg.heads, cfg.frames, cfg.height, cfg.width,
+                              cfg.d_k, cfg.d_v, cfg.eps, dt)
+    d = {name: (W.host_to_tensor(x, cfg.dtype if name in ("q", "k", "v") else "f32", "cuda")
+                if isinstance(x, np.ndarray) else x) for name, x in h.items()}
+    tdt = d["q"].dtype
+    N, F, Uq = cfg.units, cfg.frames, cfg.tokens
+    qo = torch.empty((N, F, Uq, cfg.d_k), dtype=tdt, device="cuda")
+    ko = torch.empty_like(qo)
+    vo = torch.empty((N, F, Uq, cfg.d_v), dtype=tdt, device="cuda")
+    vda.vda_prep(desc, d["q"], d["k"], d["v"], d["wk_s"], d["wk_t"], d["wv_s"], d["wv_t"],
+                 qo, ko, vo)
+    torch.cuda.synchronize()
+    return [W.to_f64(W.tensor_to_host(t), cfg.dtype) for t in (qo, ko, vo)]
+
+
+def _f64(cfg, h):
+    return {k: (W.to_f64(v, cfg.dtype) if k in ("q", "k", "v") else v.astype(np.float64))
+            for k, v in h.items()}
+
+
+@pytest.mark.parametrize("name", sorted(SHAPES))
+def test_prep_parity(name):
+    require_gpu()
+    from oracle import prep_oracle
+    cfg = SHAPES[name]
+    say(f"[prep parity] {name}")
+    h = W.host_prep_inputs(cfg)
+    got = _run(cfg, h)
+    x = _f64(cfg, h)
+    ref = prep_oracle.prep(x["q"], x["k"], x["v"], x["wk_s"], x["wk_t"], x["wv_s"], x["wv_t"],
+                           cfg.eps)
+    for label, g, r in zip(("q", "k", "v"), got, ref):
+        err = row_rel_err(g, r)
+        say(f"  {label}' max row-rel err {err:.3e}")
+        assert g.shape == r.shape and np.all(np.isfinite(g))
+        assert err <= TOL[cfg.dtype], label
+
+
+def test_prep_zero_rows_stay_zero():
+    """An all-zero query row, and a key row whose convolution is zero, are
+    normalised to zero (x / max(||x||, eps)), not to NaN."""
+    require_gpu()
+    cfg = P(720, "zeros-bf16", 1, 2, 5, 6, 6, 64, 64, "bf16")
+    say("[prep] zero rows")
+    h = W.host_prep_inputs(cfg)
+    h["q"][:, 1] = 0
+    h["k"][:] = 0
+    got = _run(cfg, h)
+    assert np.all(got[0][:, 1] == 0) and np.all(np.isfinite(got[0]))
+    assert np.all(got[1] == 0)
+    # SiLU(0) = 0 for v when the filters are zero
+    h = W.host_prep_inputs(cfg)
+    h["wv_s"][:] = 0
+    got = _run(cfg, h)
+    assert np.all(got[2] == 0)
+
+
+@pytest.mark.slow
+def test_prep_fullsize_sampled():
+    require_gpu()
+    import torch
+    from oracle import prep_oracle
+    import frame_wise_delta_gram_amd as vda
+    cfg = W.PREP_CONFIGS[3]
+    say(f"[prep fullsize] {cfg.name}: generating inputs")
+    d = W.device_prep_inputs(cfg)
+    desc = vda.make_prep_desc(cfg.batch, cfg.heads, cfg.frames, cfg.height, cfg.width,
+                              cfg.d_k, cfg.d_v, cfg.eps, vda.VDA_DTYPE_BF16)
+    N, F, Uq = cfg.units, cfg.frames, cfg.tokens
+    qo = torch.empty((N, F, Uq, cfg.d_k), dtype=torch.bfloat16, device="cuda")
+    ko = torch.empty_like(qo)
+    vo = torch.empty((N, F, Uq, cfg.d_v), dtype=torch.bfloat16, device="cuda")
+    say("[prep fullsize] vda_prep")
+    vda.vda_prep(desc, d["q"], d["k"], d["v"], d["wk_s"], d["wk_t"], d["wv_s"], d["wv_t"],
+                 qo, ko, vo)
+    torch.cuda.synchronize()
+    ko2 = torch.empty_like(ko)
+    vda.vda_prep(desc, d["q"], d["k"], d["v"], d["wk_s"], d["wk_t"], d["wv_s"], d["wv_t"],
+                 qo, ko2, vo)
+    torch.cuda.synchronize()
+    assert torch.equal(ko.view(torch.int16), ko2.view(torch.int16)), "not deterministic"
+    one = dataclasses.replace(cfg, batch=1, heads=1)
+    for b, hh in ((0, 0), (1, 7)):
+        u = b * cfg.heads + hh
+        for lo, hi, keep in ((0, 8, slice(0, 6)), (F - 8, F, slice(2, 8))):
+            sub = {name: W.tensor_to_host(d[name][b:b + 1, lo:hi, :, :, hh:hh + 1])
+                   for name in ("q", "k", "v")}
+            for name in ("wk_s", "wk_t", "wv_s", "wv_t"):
+                sub[name] = W.tensor_to_host(d[name][hh:hh + 1])
+            x = _f64(one, sub)
+            ref = prep_oracle.prep(x["q"], x["k"], x["v"], x["wk_s"], x["wk_t"], x["wv_s"],
+                                   x["wv_t"], cfg.eps)
+            for label, out, r in (("q", qo, ref[0]), ("k", ko, ref[1]), ("v", vo, ref[2])):
+                g = W.to_f64(W.tensor_to_host(out[u, lo:hi][keep]), "bf16")
+                err = row_rel_err(g, r[0][keep])
+                say(f"  unit {u} frames {lo}..{hi - 1} {label}': {err:.3e}")
+                assert err <= TOL["bf16"], (u, lo, label)

@@ -51,7 +51,8 @@ import numpy as np
 
 __all__ = [
     "Config", "CONFIGS", "TENSOR_IDS", "bf16_bits_from_f64", "bf16_bits_to_f64",
-    "host_inputs", "device_inputs", "to_f64", "custom_config",
+    "host_inputs", "device_inputs", "to_f64", "custom_config", "PrepConfig", "PREP_CONFIGS",
+    "host_prep_inputs", "device_prep_inputs",
 ]
 
 
@@ -95,7 +96,90 @@ CONFIGS = {
 
 # one independent stream per (config, unit, tensor)
 TENSOR_IDS = {"q": 0, "k": 1, "v": 2, "beta": 3, "gate": 4,
-              "text_k": 5, "text_v": 6, "text_beta": 7, "stress_pos": 8, "alpha": 9}
+              "text_k": 5, "text_v": 6, "text_beta": 7, "stress_pos": 8, "alpha": 9,
+              "q_raw": 10, "k_raw": 11, "v_raw": 12, "wk_s": 13, "wk_t": 14, "wv_s": 15,
+              "wv_t": 16}
+
+
+# ----------------------------------------------------------------------------- feature map
+@dataclasses.dataclass(frozen=True)
+class PrepConfig:
+    """A feature-map (VDA-Prep) workload: projection outputs q, k, v in the layout
+    [batch][frames][height][width][heads][d] and the depthwise filters.
+
+    Recipe: q, k, v ~ N(0, 1); spatial taps ~ U(-1/5, 1/5) and temporal taps
+    ~ U(-1/sqrt(5), 1/sqrt(5)) per (head, channel) (bound 1/sqrt(fan-in), the
+    usual initial scale of a depthwise convolution: the pages' trained filters
+    are not available)."""
+    cfg_id: int
+    name: str
+    batch: int
+    heads: int
+    frames: int
+    height: int
+    width: int
+    d_k: int
+    d_v: int
+    dtype: str
+    eps: float = 1e-6
+
+    @property
+    def units(self) -> int:
+        return self.batch * self.heads
+
+    @property
+    def tokens(self) -> int:
+        return self.height * self.width
+
+
+PREP_CONFIGS = {
+    1: PrepConfig(701, "tiny-prep-f32", 1, 2, 6, 5, 7, 16, 32, "f32"),
+    2: PrepConfig(702, "small-prep-bf16", 2, 2, 12, 12, 20, 64, 64, "bf16"),
+    # the 768p head share: 48 x 84 latents, 16 heads as 2 x 8, 90 frames
+    3: PrepConfig(703, "768p-prep-bf16", 2, 8, 90, 48, 84, 128, 128, "bf16"),
+}
+
+
+def host_prep_inputs(cfg: PrepConfig) -> dict:
+    """Feature-map inputs of ``cfg`` as host arrays (features in storage format:
+    fp32, or uint16 bf16 bits; filters fp32).  One stream per (config, batch
+    index, tensor) for the features, per config for the filters."""
+    Bt, F, Hl, Wl, H = cfg.batch, cfg.frames, cfg.height, cfg.width, cfg.heads
+    res = {}
+    for name, d in (("q", cfg.d_k), ("k", cfg.d_k), ("v", cfg.d_v)):
+        x = np.stack([_rng(cfg.cfg_id, b, name + "_raw").standard_normal((F, Hl, Wl, H, d))
+                      for b in range(Bt)]) if Bt else np.zeros((0, F, Hl, Wl, H, d))
+        res[name] = bf16_bits_from_f64(x) if cfg.dtype == "bf16" else x.astype(np.float32)
+    for name, d in (("wk", cfg.d_k), ("wv", cfg.d_v)):
+        res[name + "_s"] = _rng(cfg.cfg_id, 0, name + "_s").uniform(
+            -0.2, 0.2, (H, d, 5, 5)).astype(np.float32)
+        res[name + "_t"] = _rng(cfg.cfg_id, 0, name + "_t").uniform(
+            -1 / math.sqrt(5), 1 / math.sqrt(5), (H, d, 5)).astype(np.float32)
+    return res
+
+
+def device_prep_inputs(cfg: PrepConfig, device="cuda", seed: int = 0) -> dict:
+    """The same recipe drawn with torch's device generator (full-size runs)."""
+    import torch
+
+    dt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+    Bt, F, Hl, Wl, H = cfg.batch, cfg.frames, cfg.height, cfg.width, cfg.heads
+
+    def gen(tensor):
+        g = torch.Generator(device=device)
+        g.manual_seed(((seed * 131 + cfg.cfg_id) * 1009 + TENSOR_IDS[tensor]) & 0x7FFFFFFFFFFF)
+        return g
+
+    res = {}
+    for name, d in (("q", cfg.d_k), ("k", cfg.d_k), ("v", cfg.d_v)):
+        res[name] = torch.randn((Bt, F, Hl, Wl, H, d), generator=gen(name + "_raw"),
+                                device=device, dtype=torch.float32).to(dt)
+    for name, d in (("wk", cfg.d_k), ("wv", cfg.d_v)):
+        u = torch.rand((H, d, 5, 5), generator=gen(name + "_s"), device=device)
+        res[name + "_s"] = (u * 0.4 - 0.2).contiguous()
+        u = torch.rand((H, d, 5), generator=gen(name + "_t"), device=device)
+        res[name + "_t"] = ((u * 2 - 1) / math.sqrt(5)).contiguous()
+    return res
 
 
 def custom_config(cfg_id=100, **kw) -> Config:
