@@ -110,16 +110,20 @@ PROFILE_COMMANDS = {  # CFG: the workload id
     "FETCH_SIZE": "timeout -s KILL 120 rocprofv3 --pmc FETCH_SIZE --kernel-include-regex "
                   "'vda|add' -d DIR/FETCH_SIZE -o p --output-format csv -- python bench.py "
                   "--config CFG --steps 2 --warmup 1 --cpu-seconds 0 --decay-steps 0 "
-                  "--batched-steps 0",
+                  "--batched-steps 0 --prep-steps 0",
     "WRITE_SIZE": "timeout -s KILL 120 rocprofv3 --pmc WRITE_SIZE --kernel-include-regex "
                   "'vda|add' -d DIR/WRITE_SIZE -o p --output-format csv -- python bench.py "
                   "--config CFG --steps 2 --warmup 1 --cpu-seconds 0 --decay-steps 0 "
-                  "--batched-steps 0",
+                  "--batched-steps 0 --prep-steps 0",
     "stats": "rocprofv3 --kernel-trace --stats -d DIR/trace -o vda --output-format csv -- "
              "python bench.py --config CFG --steps 5 --warmup 2 --cpu-seconds 0 --decay-steps 0 "
-             "--batched-steps 0",
+             "--batched-steps 0 --prep-steps 0",
 }
 KERNELS = ("stats_text", "stats", "solve", "compose", "scan", "readout")  # launch order
+PREP_COMMAND = ("rocprofv3 {pmc} -d DIR/{sub} -o p --output-format csv -- python bench.py "
+                "--steps 1 --warmup 0 --cpu-seconds 0 --decay-steps 0 --batched-steps 0 "
+                "--prep-steps 5")
+PREP_KERNELS = ("prep_q", "prep_conv_k", "prep_conv_v")
 KERNEL_NAMES = {"stats_bf16_kernel": "stats", "stats_f32_kernel": "stats",
                 "stats_text_kernel": "stats_text",
                 "readout_bf16_kernel": "readout", "readout_f32_kernel": "readout",
@@ -132,8 +136,84 @@ def short_kernel_name(full):
     import re
     m = re.search(r"vda::\(anonymous namespace\)::(\w+)", full)
     if m:
+        if m.group(1) == "prep_conv_kernel":
+            return "prep_conv_k" if re.search(r"prep_conv_kernel<[^,]+, true>", full) else "prep_conv_v"
+        if m.group(1) == "prep_q_kernel":
+            return "prep_q"
         return KERNEL_NAMES.get(m.group(1), m.group(1))
     return "copy" if "add" in full.lower() else None
+
+
+def summarize_prep(prep_dir):
+    """profiles/prep_kernels_<workload>.md from a kernel trace and FETCH_SIZE /
+    WRITE_SIZE passes of PREP_COMMAND (DIR = prep_dir)."""
+    import collections
+    import csv
+    import workloads as W
+
+    cfg = W.PREP_CONFIGS[3]
+    base = W.CONFIGS[4]
+    copy_bytes = base.units * base.frames * base.tokens * base.d_v * 2
+    known = {"FETCH_SIZE": 2 * copy_bytes, "WRITE_SIZE": copy_bytes}
+    eb = 2
+    rows = cfg.batch * cfg.frames * cfg.tokens * cfg.heads
+    alg = {"prep_q": 2 * eb * rows * cfg.d_k,
+           "prep_conv_k": 2 * eb * rows * cfg.d_k + cfg.heads * cfg.d_k * 120,
+           "prep_conv_v": 2 * eb * rows * cfg.d_v + cfg.heads * cfg.d_v * 120}
+    flops = {"prep_q": 0, "prep_conv_k": 60 * rows * cfg.d_k, "prep_conv_v": 60 * rows * cfg.d_v}
+    per = {}
+    for ctr in ("FETCH_SIZE", "WRITE_SIZE"):
+        path = os.path.join(prep_dir, ctr, "p_counter_collection.csv")
+        disp = collections.defaultdict(float)
+        names = {}
+        with open(path) as fh:
+            for r in csv.DictReader(fh):
+                k = short_kernel_name(r["Kernel_Name"])
+                if k is None or r["Counter_Name"] != ctr:
+                    continue
+                disp[int(r["Dispatch_Id"])] += float(r["Counter_Value"])
+                names[int(r["Dispatch_Id"])] = k
+        acc = collections.defaultdict(list)
+        for i, v in sorted(disp.items()):
+            acc[names[i]].append(v)
+        # the calibration adds are the largest "add" dispatches (input generation adds
+        # small tensors)
+        acc["copy"] = sorted(acc["copy"])[-CEILING_CALLS:]
+        per[ctr] = {k: sum(v) / len(v) for k, v in acc.items()}
+    scale = {c: known[c] / (per[c]["copy"] * 1024.0) for c in per}
+    durations = {}
+    with open(os.path.join(prep_dir, "trace", "p_kernel_stats.csv")) as fh:
+        for r in csv.DictReader(fh):
+            k = short_kernel_name(r["Name"])
+            if k in PREP_KERNELS:
+                durations[k] = (int(r["Calls"]), float(r["AverageNs"]) / 1e3)
+    cmds = [PREP_COMMAND.format(pmc="--kernel-trace --stats", sub="trace"),
+            "timeout -s KILL 120 " + PREP_COMMAND.format(pmc="--pmc FETCH_SIZE", sub="FETCH_SIZE"),
+            "timeout -s KILL 120 " + PREP_COMMAND.format(pmc="--pmc WRITE_SIZE", sub="WRITE_SIZE"),
+            "python bench.py --summarize-prep DIR"]
+    lines = [f"# Feature-map kernels (vda_prep), {cfg.name} ({cfg.batch} x {cfg.heads} heads, "
+             f"{cfg.frames} frames of {cfg.height} x {cfg.width} tokens, d_k = {cfg.d_k}, "
+             f"d_v = {cfg.d_v}, bf16)", "",
+             "Commands (from the repository root, on one MI355X; DIR = an output folder):", ""]
+    lines += [f"    {c}" for c in cmds]
+    lines += ["", "| kernel | calls | average (us) | algorithmic GB/s | fp32 TFLOP/s (of "
+              f"{VALU_FP32_PEAK / 1e12:.1f}) | HBM read (B) | HBM written (B) | total / algorithmic |",
+              "|---|---|---|---|---|---|---|---|"]
+    for k in PREP_KERNELS:
+        if k not in durations:
+            continue
+        c, a = durations[k]
+        rb = per["FETCH_SIZE"].get(k, 0.0) * 1024 * scale["FETCH_SIZE"]
+        wb = per["WRITE_SIZE"].get(k, 0.0) * 1024 * scale["WRITE_SIZE"]
+        lines.append(f"| {k} | {c} | {a:.1f} | {alg[k] / (a * 1e-6) / 1e9:.0f} | "
+                     f"{flops[k] / (a * 1e-6) / 1e12:.1f} | {rb:.4g} | {wb:.4g} | "
+                     f"{(rb + wb) / alg[k]:.3f} |")
+    lines += ["", f"Counter scale factors (torch.add calibration in the same runs): FETCH x "
+              f"{scale['FETCH_SIZE']:.3f}, WRITE x {scale['WRITE_SIZE']:.3f}."]
+    os.makedirs(PROFILES, exist_ok=True)
+    with open(os.path.join(PROFILES, f"prep_kernels_{cfg.name}.md"), "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
 
 
 def summarize(prof_dir, cfg_id):
@@ -370,11 +450,19 @@ def main():
     ap.add_argument("--batched-steps", type=int, default=None,
                     help="steps of the batched comparison rule measurement on the 768p-bf16 "
                          "inputs (default: --steps; 0 disables it)")
+    ap.add_argument("--prep-steps", type=int, default=None,
+                    help="steps of the feature-map (vda_prep) measurement on the 768p head share "
+                         "(default: --steps; 0 disables it)")
+    ap.add_argument("--summarize-prep", metavar="DIR",
+                    help="write the feature-map profile summary from rocprofv3 output under DIR")
     ap.add_argument("--summarize", metavar="DIR",
                     help="write the profiles/ summaries from rocprofv3 output under DIR and exit")
     args = ap.parse_args()
     if args.summarize:
         summarize(args.summarize, args.config)
+        return
+    if args.summarize_prep:
+        summarize_prep(args.summarize_prep)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the VDA forward shards by head with no "
@@ -459,8 +547,8 @@ def main():
             "stage_ms": ms, "state_growth": state_growth(cfg, d)}
     decay_steps = args.steps if args.decay_steps is None else args.decay_steps
     line["decay"] = None
+    del d
     if decay_steps > 0 and args.config == 4:
-        del d
         dcfg = W.CONFIGS[6]
         log(f"[bench] generating {dcfg.name} inputs on the device")
         dd = W.device_inputs(dcfg)
@@ -473,7 +561,63 @@ def main():
             "alpha": f"sigmoid(N({dcfg.alpha_mu}, 1)) per (unit, frame, key channel), fp32",
             "relative_to_plain": dvalue / value, "stage_ms": ms,
             "roofline": roofline_of(dcfg, ms)}
+        del dd
+    prep_steps = args.steps if args.prep_steps is None else args.prep_steps
+    line["prep"] = None
+    if prep_steps > 0 and args.config == 4:
+        line["prep"] = bench_prep(W.PREP_CONFIGS[3], prep_steps, args.warmup)
     print(json.dumps(line), flush=True)
+
+
+VALU_FP32_PEAK = 256 * 4 * 16 * 2 * 2.4e9  # unpacked fp32 FMA: CUs x SIMDs x lanes x 2 flop x clock
+
+
+def prep_algorithmic(cfg):
+    """Bytes (q, k, v read once, q', k', v' written once, filters) and fp32 flops
+    (30 multiply-adds per convolved element of k and v) of one vda_prep call."""
+    eb = 2 if cfg.dtype == "bf16" else 4
+    rows = cfg.batch * cfg.frames * cfg.tokens * cfg.heads
+    elems = rows * (2 * cfg.d_k + cfg.d_v)
+    filt = cfg.heads * (cfg.d_k + cfg.d_v) * 30 * 4
+    return 2 * elems * eb + filt, 2 * 30 * rows * (cfg.d_k + cfg.d_v)
+
+
+def bench_prep(cfg, steps, warmup):
+    """Whole-call time of vda_prep on ``cfg`` (inputs resident), with its ALU and
+    HBM fractions."""
+    import torch
+    import frame_wise_delta_gram_amd as vda
+    import workloads as W
+    log(f"[bench] generating {cfg.name} inputs on the device")
+    d = W.device_prep_inputs(cfg)
+    desc = vda.make_prep_desc(cfg.batch, cfg.heads, cfg.frames, cfg.height, cfg.width, cfg.d_k,
+                              cfg.d_v, cfg.eps, vda.VDA_DTYPE_BF16)
+    N, F, U = cfg.units, cfg.frames, cfg.tokens
+    qo = torch.empty((N, F, U, cfg.d_k), dtype=torch.bfloat16, device="cuda")
+    ko = torch.empty_like(qo)
+    vo = torch.empty((N, F, U, cfg.d_v), dtype=torch.bfloat16, device="cuda")
+    a = (desc, d["q"], d["k"], d["v"], d["wk_s"], d["wk_t"], d["wv_s"], d["wv_t"], qo, ko, vo)
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        vda.vda_prep(*a, stream=stream)
+    torch.cuda.synchronize()
+    log(f"[bench] {cfg.name}: timing {steps} steps")
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        vda.vda_prep(*a, stream=stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    bytes_, flops = prep_algorithmic(cfg)
+    return {"workload": cfg.name, "entry_point": "vda_prep", "steps": steps, "ms_per_call": ms,
+            "token_heads_per_s": N * F * U / (ms * 1e-3),
+            "roofline": {"bound": "alu", "achieved": flops / (ms * 1e-3) / 1e12,
+                         "peak": VALU_FP32_PEAK / 1e12, "unit": "TFLOP/s",
+                         "frac": flops / (ms * 1e-3) / VALU_FP32_PEAK,
+                         "hbm_GB/s": bytes_ / (ms * 1e-3) / 1e9,
+                         "hbm_frac": bytes_ / (ms * 1e-3) / HBM_PEAK,
+                         "algorithmic_bytes": bytes_, "flops": flops}}
 
 
 if __name__ == "__main__":

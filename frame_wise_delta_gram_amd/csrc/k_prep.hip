@@ -9,12 +9,13 @@
 // channels of one (token, head).  Input layout: the projection output
 // [batch][F][H_l][W_l][heads][d]; output: [batch * heads][F][H_l * W_l][d].
 //
-// conv kernel: one workgroup (8 waves) per (unit, 8 x 8 spatial tile), sweeping
-// all frames.  Per input frame the 12 x 12 halo tile of the unit's channels is
-// staged in LDS as fp32 (converted once) while the next frame's tile is in
-// flight in registers.  Wave w owns output row w of the tile, lane l the
-// channel pair 2l, 2l + 1: its 8 outputs x 2 channels are a 5 x 12 window
-// product (read once per window row, 8-byte conflict-free LDS reads); the
+// conv kernel: one workgroup (16 waves, four per SIMD to hide LDS latency) per
+// (unit, 8 x 8 spatial tile), sweeping all frames.  Per input frame the
+// 12 x 12 halo tile of the unit's channels is staged in LDS as fp32 (converted
+// once) while the next frame's tile is in flight in registers.  Wave w owns
+// output row w % 8, columns 4 (w / 8) .. + 3 of the tile, lane l the channel
+// pair 2l, 2l + 1: its 4 outputs x 2 channels are a 5 x 8 window product (read
+// once per window row, 8-byte conflict-free LDS reads); the
 // spatial taps of the unit's channels sit in LDS (one 8-byte read per tap
 // serves the lane's 8 outputs), its five temporal taps in registers.  The temporal filter runs
 // in scatter form: input frame t adds w_t[tau] times its spatial result to the
@@ -36,7 +37,8 @@ constexpr int kTR = 8;            // output tile rows
 constexpr int kTC = 8;            // output tile columns
 constexpr int kHR = kTR + 4;      // halo tile rows
 constexpr int kHC = kTC + 4;      // halo tile columns
-constexpr int kPrepThreads = 512;
+constexpr int kPrepThreads = 1024;
+constexpr int kCols = 4;          // output columns per wave
 
 // 16-byte pieces of a tensor element type: 8 bf16 or 4 fp32 channels
 template <typename T>
@@ -72,10 +74,24 @@ __device__ __forceinline__ float silu(float x) {
   return x * __builtin_amdgcn_rcpf(1.0f + __expf(-x));
 }
 
-__device__ __forceinline__ float wave_sum(float x) {
+// Sums over the wave's 64 lanes of 4 values per lane at once, as a halving
+// butterfly: after the exchanges across lane bits 5 and 4 each lane holds one
+// partial sum, of value (lane >> 4) & 3, which lane bits 3..0 complete.
+// 6 lane exchanges instead of 24.  Returns the sum of value (lane >> 4) & 3.
+__device__ __forceinline__ float wave_sum4(const float (&v)[4]) {
+  const int lane = lane_id();
+  const bool h5 = lane & 32, h4 = lane & 16;
+  float a[2];
 #pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) x += __shfl_xor(x, m);
-  return x;
+  for (int i = 0; i < 2; ++i) {
+    const float keep = h5 ? v[i + 2] : v[i];
+    const float send = h5 ? v[i] : v[i + 2];
+    a[i] = keep + __shfl_xor(send, 32);
+  }
+  float c = (h4 ? a[1] : a[0]) + __shfl_xor(h4 ? a[0] : a[1], 16);
+#pragma unroll
+  for (int m = 8; m >= 1; m >>= 1) c += __shfl_xor(c, m);
+  return c;
 }
 
 template <typename T, bool NORM>
@@ -99,6 +115,8 @@ __global__ __launch_bounds__(kPrepThreads, 1) void prep_conv_kernel(
   const int t = threadIdx.x;
   const int lane = t & 63;
   const int w = t >> 6;
+  const int orow = w & 7;            // output row of the tile
+  const int oc0 = kCols * (w >> 3);  // first output column
   const int ch = 2 * lane;
   const bool cact = ch < d;
   const int U = Hl * Wl;
@@ -118,23 +136,28 @@ __global__ __launch_bounds__(kPrepThreads, 1) void prep_conv_kernel(
     for (int i = 0; i < 5; ++i) ft[e][i] = cact ? wt[c * 5 + i] : 0.0f;
   }
 
-  // staging: 16-byte pieces of the halo tile's positions
+  // staging: 16-byte pieces of the halo tile's positions, loaded through a
+  // per-frame buffer descriptor: a piece outside the frame (or past the tile)
+  // gets an offset past the descriptor's range and reads as zero
   const int gpp = d / EPP;  // pieces per position
   const int npieces = kHR * kHC * gpp;
+  const int frame_bytes = U * H * d * (int)sizeof(T);
+  int poff[kIter];
+#pragma unroll
+  for (int i = 0; i < kIter; ++i) {
+    const int p = t + kPrepThreads * i;
+    const int pos = p / gpp;
+    const int cg = p - pos * gpp;
+    const int gi = r0 - 2 + pos / kHC;
+    const int gj = c0 - 2 + pos % kHC;
+    const bool ok = p < npieces && gi >= 0 && gi < Hl && gj >= 0 && gj < Wl;
+    poff[i] = ok ? (((gi * Wl + gj) * H + h) * d + cg * EPP) * (int)sizeof(T) : frame_bytes;
+  }
   u32x4_t pre[kIter];
   auto load_frame = [&](int tin) {
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(x + ((size_t)b * F + tin) * U * H * d, frame_bytes);
 #pragma unroll
-    for (int i = 0; i < kIter; ++i) {
-      const int p = t + kPrepThreads * i;
-      const int pos = p / gpp;
-      const int cg = p - pos * gpp;
-      const int gi = r0 - 2 + pos / kHC;
-      const int gj = c0 - 2 + pos % kHC;
-      const bool ok = p < npieces && gi >= 0 && gi < Hl && gj >= 0 && gj < Wl;
-      const size_t off = ((((size_t)b * F + tin) * Hl + (ok ? gi : 0)) * Wl + (ok ? gj : 0)) * H + h;
-      pre[i] = ok ? *reinterpret_cast<const u32x4_t*>(x + off * d + cg * EPP)
-                  : u32x4_t{0u, 0u, 0u, 0u};
-    }
+    for (int i = 0; i < kIter; ++i) pre[i] = buf_load16(rs, poff[i]);
   };
   auto store_frame = [&]() {
 #pragma unroll
@@ -152,15 +175,16 @@ __global__ __launch_bounds__(kPrepThreads, 1) void prep_conv_kernel(
     }
   };
 
-  float acc[5][2][kTC];
+  float acc[5][2][kCols];
 #pragma unroll
   for (int s = 0; s < 5; ++s)
 #pragma unroll
     for (int e = 0; e < 2; ++e)
 #pragma unroll
-      for (int o = 0; o < kTC; ++o) acc[s][e][o] = 0.0f;
+      for (int o = 0; o < kCols; ++o) acc[s][e][o] = 0.0f;
 
-  const int gi_out = r0 + w;
+  const int gi_out = r0 + orow;
+  T* ybase = y + ((size_t)unit * F * U + (size_t)gi_out * Wl + c0 + oc0) * d + ch;
   // one input frame tin (k = tin mod 5): spatial product of the staged tile,
   // scatter into the ring, then output frame tin - 2 is complete
   auto step = [&](int tin, auto kc) {
@@ -169,17 +193,17 @@ __global__ __launch_bounds__(kPrepThreads, 1) void prep_conv_kernel(
     if (tin + 1 < F) load_frame(tin + 1);  // in flight during the products below
     __syncthreads();
     if (tin < F) {
-      float s[2][kTC];
+      float s[2][kCols];
 #pragma unroll
       for (int e = 0; e < 2; ++e)
 #pragma unroll
-        for (int o = 0; o < kTC; ++o) s[e][o] = 0.0f;
+        for (int o = 0; o < kCols; ++o) s[e][o] = 0.0f;
 #pragma unroll
       for (int a = 0; a < 5; ++a) {
-        float xr[2][kHC];
-        const float* row = Xs + ((w + a) * kHC) * 128 + ch;
+        float xr[2][kCols + 4];
+        const float* row = Xs + ((orow + a) * kHC + oc0) * 128 + ch;
 #pragma unroll
-        for (int c = 0; c < kHC; ++c) {
+        for (int c = 0; c < kCols + 4; ++c) {
           const float2 v = *reinterpret_cast<const float2*>(row + c * 128);
           xr[0][c] = v.x;
           xr[1][c] = v.y;
@@ -188,7 +212,7 @@ __global__ __launch_bounds__(kPrepThreads, 1) void prep_conv_kernel(
         for (int bb = 0; bb < 5; ++bb) {
           const float2 f = *reinterpret_cast<const float2*>(Ws + (a * 5 + bb) * 128 + ch);
 #pragma unroll
-          for (int o = 0; o < kTC; ++o) {
+          for (int o = 0; o < kCols; ++o) {
             s[0][o] = fmaf(f.x, xr[0][o + bb], s[0][o]);
             s[1][o] = fmaf(f.y, xr[1][o + bb], s[1][o]);
           }
@@ -202,32 +226,42 @@ __global__ __launch_bounds__(kPrepThreads, 1) void prep_conv_kernel(
 #pragma unroll
         for (int e = 0; e < 2; ++e)
 #pragma unroll
-          for (int o = 0; o < kTC; ++o) acc[sl][e][o] = fmaf(ft[e][tau], s[e][o], acc[sl][e][o]);
+          for (int o = 0; o < kCols; ++o) acc[sl][e][o] = fmaf(ft[e][tau], s[e][o], acc[sl][e][o]);
       }
     }
     // output frame tin - 2 (ring slot (k + 3) mod 5) is complete
     constexpr int fin = (k + 3) % 5;
     const int t_out = tin - 2;
     if (t_out >= 0) {
+      float v[2][kCols];
 #pragma unroll
-      for (int o = 0; o < kTC; ++o) {
-        float v0 = silu(acc[fin][0][o]);
-        float v1 = silu(acc[fin][1][o]);
-        if (NORM) {
-          const float ss = wave_sum(cact ? v0 * v0 + v1 * v1 : 0.0f);
-          const float inv = 1.0f / fmaxf(sqrtf(ss), eps);
-          v0 *= inv;
-          v1 *= inv;
+      for (int o = 0; o < kCols; ++o) {
+        v[0][o] = silu(acc[fin][0][o]);
+        v[1][o] = silu(acc[fin][1][o]);
+      }
+      if (NORM) {  // sum of squares over the position's d channels (all 64 lanes)
+        float sq[kCols];
+#pragma unroll
+        for (int o = 0; o < kCols; ++o) sq[o] = cact ? v[0][o] * v[0][o] + v[1][o] * v[1][o] : 0.0f;
+        const float inv_l = 1.0f / fmaxf(sqrtf(wave_sum4(sq)), eps);  // of output (lane >> 4) & 3
+#pragma unroll
+        for (int o = 0; o < kCols; ++o) {
+          const float inv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(inv_l), 16 * o));
+          v[0][o] *= inv;
+          v[1][o] *= inv;
         }
-        const int gj = c0 + o;
+      }
+#pragma unroll
+      for (int o = 0; o < kCols; ++o) {
+        const int gj = c0 + oc0 + o;
         if (cact && gi_out < Hl && gj < Wl)
-          store2(y + (((size_t)unit * F + t_out) * U + (size_t)gi_out * Wl + gj) * d + ch, v0, v1);
+          store2(ybase + ((size_t)t_out * U + o) * d, v[0][o], v[1][o]);
       }
     }
 #pragma unroll
     for (int e = 0; e < 2; ++e)
 #pragma unroll
-      for (int o = 0; o < kTC; ++o) acc[fin][e][o] = 0.0f;
+      for (int o = 0; o < kCols; ++o) acc[fin][e][o] = 0.0f;
     __syncthreads();  // every wave is done with the staged tile
   };
 

@@ -72,18 +72,6 @@ __device__ __forceinline__ uint32_t off16(uint32_t row, uint32_t j) {
 // g = u F + f (stored at workspace frame u (F + 1) + f + 1), as ONE continuous
 // tile stream: the first tiles of the next frame are in flight while the last tile
 // of the current one is multiplied and its results are stored.
-// Raw buffer access (gfx9 descriptor: stride 0, range in bytes, dword 3 =
-// 0x00020000): loads at or past `bytes` return 0 without a memory access.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
-}
-// 16 bytes, non-temporal (cache policy bit 1)
-__device__ __forceinline__ u32x4_t buf_load16_nt(__amdgpu_buffer_rsrc_t r, int off) {
-  return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 2));
-}
-__device__ __forceinline__ float buf_load4(__amdgpu_buffer_rsrc_t r, int off) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
-}
 
 // DK, DV > 0: compile-time d_k and d_v (the common 128 case); 0: runtime.
 template <int DK, int DV>

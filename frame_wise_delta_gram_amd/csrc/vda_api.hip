@@ -272,6 +272,8 @@ int make_prep_plan(const vda_prep_desc_t* d, PrepPlan* p) {
   if ((int64_t)d->batch * d->heads > kMaxGridYZ) return VDA_ERR_INVALID_ARG;
   if (d->frames > kMaxFrames) return VDA_ERR_INVALID_ARG;
   if ((int64_t)d->height * d->width > 4194303) return VDA_ERR_INVALID_ARG;
+  // one frame of one batch entry (all heads) is addressed with 32-bit byte offsets
+  if ((int64_t)d->height * d->width * d->heads * 128 * 4 > INT32_MAX) return VDA_ERR_INVALID_ARG;
   if (d->d_k < 16 || d->d_k > 128 || d->d_k % 16) return VDA_ERR_INVALID_ARG;
   if (d->d_v < 16 || d->d_v > 128 || d->d_v % 16) return VDA_ERR_INVALID_ARG;
   if (!(d->eps > 0.0f) || !isfinite(d->eps)) return VDA_ERR_INVALID_ARG;

@@ -96,6 +96,23 @@ __host__ __device__ __forceinline__ int pad32(int d) { return (d + 31) & ~31; }
 // contiguous work items [x * per, (x + 1) * per), so items that share inputs
 // (neighbouring items) are served by one L2.  Returns the work item of this
 // workgroup (may be >= the real item count: the caller skips those).
+// Raw buffer access (gfx9 descriptor: stride 0, range in bytes, dword 3 =
+// 0x00020000): loads at or past `bytes` return 0 without a memory access.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
+}
+// 16 bytes, non-temporal (cache policy bit 1)
+__device__ __forceinline__ u32x4_t buf_load16_nt(__amdgpu_buffer_rsrc_t r, int off) {
+  return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 2));
+}
+// 16 bytes, default cache policy
+__device__ __forceinline__ u32x4_t buf_load16(__amdgpu_buffer_rsrc_t r, int off) {
+  return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+__device__ __forceinline__ float buf_load4(__amdgpu_buffer_rsrc_t r, int off) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+}
+
 constexpr int kXcds = 8;
 __device__ __forceinline__ unsigned xcd_item(unsigned per) {
   const unsigned L = blockIdx.x;
