@@ -17,6 +17,12 @@ Sec. 6.4: heads are sharded per GPU), with five concrete sizes:
                write strengths near 1
   768p-decay-bf16  the 768p workload with per-frame channel-wise decay gates
 
+Custom configs (custom_config) add boundary anchors (anchors=True) or the
+batched comparison rules (rule=1, 2) to any shape.  Feature-map workloads
+(PrepConfig / PREP_CONFIGS) hold the projection outputs q, k, v in the layout
+[batch][frames][height][width][heads][d] and depthwise filters; the 768p one is
+the same head share as 2 x 8 heads of 48 x 84 latents.
+
 Recipe (every tensor has its own seeded stream, so any unit can be regenerated
 alone):
   q, v, gate logits ~ N(0, 1)
