@@ -115,6 +115,11 @@ PROFILE_COMMANDS = {  # CFG: the workload id
                   "'vda|add' -d DIR/WRITE_SIZE -o p --output-format csv -- python bench.py "
                   "--config CFG --steps 2 --warmup 1 --cpu-seconds 0 --decay-steps 0 "
                   "--batched-steps 0 --prep-steps 0",
+    "MFMA": "timeout -s KILL 120 rocprofv3 --pmc SQ_INSTS_VALU_MFMA_MOPS_BF16 "
+            "SQ_INSTS_VALU_MFMA_MOPS_F32 SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE "
+            "--kernel-include-regex vda -d DIR/MFMA -o p --output-format csv -- python bench.py "
+            "--config CFG --steps 2 --warmup 1 --cpu-seconds 0 --decay-steps 0 "
+            "--batched-steps 0 --prep-steps 0",
     "stats": "rocprofv3 --kernel-trace --stats -d DIR/trace -o vda --output-format csv -- "
              "python bench.py --config CFG --steps 5 --warmup 2 --cpu-seconds 0 --decay-steps 0 "
              "--batched-steps 0 --prep-steps 0",
@@ -261,7 +266,7 @@ def summarize(prof_dir, cfg_id):
     lines = [f"# VDA forward kernels, {head}", "",
              "Commands (from the repository root, on one MI355X; DIR = an output folder):", ""]
     cmd = {c: PROFILE_COMMANDS[c].replace("CFG", str(cfg_id)) for c in PROFILE_COMMANDS}
-    lines += [f"    {cmd[c]}" for c in ("stats", "FETCH_SIZE", "WRITE_SIZE")]
+    lines += [f"    {cmd[c]}" for c in ("stats", "FETCH_SIZE", "WRITE_SIZE", "MFMA")]
     lines += [f"    python bench.py --summarize DIR --config {cfg_id}", "",
               "## Kernel durations (`vda_kernel_stats.csv`)", "",
               "| kernel | calls | average (us) | min (us) | max (us) | algorithmic GB/s |",
@@ -270,8 +275,48 @@ def summarize(prof_dir, cfg_id):
         c, a, lo, hi = durations[k]
         lines.append(f"| {k} | {c} | {a:.1f} | {lo:.1f} | {hi:.1f} | "
                      f"{alg[k][0] / (a * 1e-6) / 1e9:.0f} |")
-    lines += ["", f"Sum of averages: {sum(durations[k][1] for k in order):.1f} us per forward step.",
-              "", "## HBM traffic per launch (`FETCH_SIZE`, `WRITE_SIZE`)", "",
+    lines += ["", f"Sum of averages: {sum(durations[k][1] for k in order):.1f} us per forward step."]
+    mfma_path = os.path.join(prof_dir, "MFMA", "p_counter_collection.csv")
+    if os.path.exists(mfma_path):
+        # per dispatch: MOPS (x 512 flop), MFMA busy cycles summed over the SIMDs,
+        # GPU-active cycles (the dispatch's duration in clocks)
+        ctr = collections.defaultdict(lambda: collections.defaultdict(float))
+        kname = {}
+        with open(mfma_path) as fh:
+            for r in csv.DictReader(fh):
+                k = short_kernel_name(r["Kernel_Name"])
+                if k is None or k == "copy":
+                    continue
+                i = int(r["Dispatch_Id"])
+                kname[i] = k
+                if r["Counter_Name"] == "GRBM_GUI_ACTIVE":
+                    ctr[i]["GRBM_GUI_ACTIVE"] = max(ctr[i]["GRBM_GUI_ACTIVE"],
+                                                    float(r["Counter_Value"]))
+                else:
+                    ctr[i][r["Counter_Name"]] += float(r["Counter_Value"])
+        agg = collections.defaultdict(lambda: collections.defaultdict(list))
+        for i, c in ctr.items():
+            for name, val in c.items():
+                agg[kname[i]][name].append(val)
+        lines += ["", "## MFMA counters per launch (`SQ_INSTS_VALU_MFMA_MOPS_*`)", "",
+                  "Executed MFMA flops = MOPS x 512 (hi/lo splits execute more than the algorithmic "
+                  "flops); rates use the trace's average duration; peaks: bf16 2516.6, fp32 matrix "
+                  "157.3 TFLOP/s.", "",
+                  "| kernel | bf16 flops executed | fp32 flops executed | algorithmic bf16 flops | "
+                  "executed bf16 TFLOP/s (% of peak) | executed fp32 TFLOP/s (% of peak) |",
+                  "|---|---|---|---|---|---|"]
+        for k in order:
+            if k not in agg:
+                continue
+            m = {name: sum(v) / len(v) for name, v in agg[k].items()}
+            algf = alg[k][1] if alg[k][1] is not None else 0
+            sec = durations[k][1] * 1e-6
+            fb = m.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", 0) * 512
+            ff = m.get("SQ_INSTS_VALU_MFMA_MOPS_F32", 0) * 512
+            lines.append(f"| {k} | {fb:.4g} | {ff:.4g} | {algf:.4g} | "
+                         f"{fb / sec / 1e12:.0f} ({100 * fb / sec / BF16_PEAK:.1f}%) | "
+                         f"{ff / sec / 1e12:.1f} ({100 * ff / sec / 157.3e12:.1f}%) |")
+    lines += ["", "## HBM traffic per launch (`FETCH_SIZE`, `WRITE_SIZE`)", "",
               f"Scale factors from torch.add over two {copy_bytes} B tensors into a third: "
               f"FETCH x {scale['FETCH_SIZE']:.3f}, WRITE x {scale['WRITE_SIZE']:.3f} "
               "(counter KiB x 1024 x factor = bytes).", "",
@@ -326,7 +371,17 @@ def cpu_baseline(d, cfg, budget_s):
             break
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     th = done * cfg.frames * cfg.tokens
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for ln in fh:
+                if ln.startswith("model name"):
+                    model = ln.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
     return {"value": th / elapsed, "unit": "token-heads/s", "cores": threads, "kind": "oracle",
+            "cpu_model": model, "affinity_cpus": len(os.sched_getaffinity(0)),
             "sample": f"{done} of {cfg.units} units of the same inputs (all {cfg.frames} frames "
                       f"x {cfg.tokens} tokens each), fp64 numpy, {elapsed:.1f} s"}
 
@@ -420,7 +475,17 @@ def time_steps(cfg, d, steps, warmup):
     for row in events:
         for e in row:
             hip.hipEventDestroy(ctypes.c_void_p(e))
-    return elapsed, {s: sum(v) / len(v) for s, v in stage_ms.items()}
+    per_step = sorted(sum(stage_ms[s][i] for s in STAGES) for i in range(steps))
+    avg = {s: sum(v) / len(v) for s, v in stage_ms.items()}
+    avg["step_events_median"] = per_step[len(per_step) // 2]
+    avg["step_events_min"] = per_step[0]
+    return elapsed, avg
+
+
+def split_steps(avg_ms):
+    """(per-stage averages, {median, min} of the per-step event totals)."""
+    stages = {s: avg_ms[s] for s in STAGES}
+    return stages, {"median": avg_ms["step_events_median"], "min": avg_ms["step_events_min"]}
 
 
 def roofline_of(cfg, avg_ms):
@@ -524,7 +589,8 @@ def main():
         "roofline": roofline_of(cfg, avg_ms),
         "mfma_frac": mfma,
         "hbm_frac_whole_op": hbm_whole,
-        "stage_ms": avg_ms,
+        "stage_ms": split_steps(avg_ms)[0],
+        "step_ms_from_events": split_steps(avg_ms)[1],
         "stream_ceiling": {"kernel": "torch.add over the q and gate tensors (2 reads + 1 write)",
                            "GB/s": add_bytes / (add_ms * 1e-3) / 1e9, "ms": add_ms},
     }
@@ -544,7 +610,7 @@ def main():
             "workload": cfg.name, "rule": "SANA-WM frozen-state batched update with frame-size "
             "key scaling (rule 2)", "steps": bsteps, "ms_per_step": el * 1e3 / bsteps,
             "value": bvalue, "unit": "token-heads/s", "relative_to_vda": bvalue / value,
-            "stage_ms": ms, "state_growth": state_growth(cfg, d)}
+            "stage_ms": split_steps(ms)[0], "state_growth": state_growth(cfg, d)}
     decay_steps = args.steps if args.decay_steps is None else args.decay_steps
     line["decay"] = None
     del d
@@ -559,8 +625,8 @@ def main():
             "workload": dcfg.name, "entry_point": "vda_forward_decay", "steps": decay_steps,
             "ms_per_step": el * 1e3 / decay_steps, "value": dvalue, "unit": "token-heads/s",
             "alpha": f"sigmoid(N({dcfg.alpha_mu}, 1)) per (unit, frame, key channel), fp32",
-            "relative_to_plain": dvalue / value, "stage_ms": ms,
-            "roofline": roofline_of(dcfg, ms)}
+            "relative_to_plain": dvalue / value, "stage_ms": split_steps(ms)[0],
+            "step_ms_from_events": split_steps(ms)[1], "roofline": roofline_of(dcfg, ms)}
         del dd
     prep_steps = args.steps if args.prep_steps is None else args.prep_steps
     line["prep"] = None
