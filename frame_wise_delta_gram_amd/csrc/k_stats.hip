@@ -74,8 +74,11 @@ __device__ __forceinline__ uint32_t off16(uint32_t row, uint32_t j) {
 // of the current one is multiplied and its results are stored.
 
 // DK, DV > 0: compile-time d_k and d_v (the common 128 case); 0: runtime.
-template <int DK, int DV>
-__global__ __launch_bounds__(512, 1) void stats_bf16_kernel(
+// NT: tokens each thread stages per tile: 4 with 512 threads (wave w owns
+// output row tile w and all four column tiles), 2 with 1024 threads (wave w
+// owns row tile w % 8 and column tiles 2 (w / 8), + 1: four waves per SIMD).
+template <int DK, int DV, int NT>
+__global__ __launch_bounds__(512 * (4 / NT), 1) void stats_bf16_kernel(
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, const float* __restrict__ beta,
     float* __restrict__ Aout, float* __restrict__ Bout, int F, int U, int dk_rt, int dv_rt,
     int nframes, int anchors) {
@@ -112,7 +115,8 @@ __global__ __launch_bounds__(512, 1) void stats_bf16_kernel(
     return Cur{c.g + P, 0};
   };
 
-  // staging role: token group tg (4 tokens) x channel group cg (8 channels)
+  constexpr int NCT = NT == 4 ? 4 : 2;  // column tiles per wave
+  // staging role: token group tg (NT tokens) x channel group cg (8 channels)
   const int tg = (t & 1) | ((t >> 5) << 1);
   const int cg = (t >> 1) & 15;
   const bool kact = cg * 8 < dk;
@@ -126,15 +130,15 @@ __global__ __launch_bounds__(512, 1) void stats_bf16_kernel(
   // the tile is staged: vmcnt retires in issue order, so a tile's loads stay
   // in flight behind later work.
   struct TileRegs {
-    u32x4_t k[4], v[4];
-    float b[4];  // beta of the 4 tokens
+    u32x4_t k[NT], v[NT];
+    float b[NT];  // beta of the NT tokens
   };
   const int kcg = kact ? cg : 0;
   const int vcg = vact ? cg : 0;
-  // byte offsets of the thread's 4 tokens within a tile
-  const int koff = ((4 * tg) * dk + 8 * kcg) * 2;
-  const int voff = ((4 * tg) * dv + 8 * vcg) * 2;
-  const int boff = 16 * tg;
+  // byte offsets of the thread's NT tokens within a tile
+  const int koff = ((NT * tg) * dk + 8 * kcg) * 2;
+  const int voff = ((NT * tg) * dv + 8 * vcg) * 2;
+  const int boff = 4 * NT * tg;
 
   auto load = [&](TileRegs& r, Cur c) {
     const bool past = c.g >= nframes;  // past this workgroup's last frame: zeros, never used
@@ -146,52 +150,66 @@ __global__ __launch_bounds__(512, 1) void stats_bf16_kernel(
     const __amdgpu_buffer_rsrc_t rv = make_rsrc(f.v + t0 * dv, rem * dv * 2);
     const __amdgpu_buffer_rsrc_t rbb = make_rsrc(f.b + t0, rem * 4);
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
+    for (int s = 0; s < NT; ++s) {
       r.k[s] = buf_load16_nt(rk, koff + s * dk * 2);
       r.v[s] = buf_load16_nt(rv, voff + s * dv * 2);
       r.b[s] = buf_load4(rbb, boff + 4 * s);
     }
   };
 
-  // sqrt(beta) of the thread's 4 tokens of a tile (beta reads 0 past the end)
-  auto sqrt_beta = [&](const TileRegs& r, Cur, float (&sb4)[4]) {
+  // sqrt(beta) of the thread's NT tokens of a tile (beta reads 0 past the end)
+  auto sqrt_beta = [&](const TileRegs& r, Cur, float (&sb4)[NT]) {
 #pragma unroll
-    for (int s = 0; s < 4; ++s) sb4[s] = __builtin_amdgcn_sqrtf(r.b[s]);
+    for (int s = 0; s < NT; ++s) sb4[s] = __builtin_amdgcn_sqrtf(r.b[s]);
   };
 
-  // channel c of the thread's 8-channel group, tokens 0..3: scale, round, pack
-  auto scaled_pair = [&](const u32x4_t* x4, const float* bq, int c) {
+  // channel c of the thread's 8-channel group, its NT tokens: scale, round, pack
+  auto scaled = [&](const u32x4_t* x4, const float* bq, int c, uint32_t (&e)[NT / 2]) {
     const int p = c >> 1;
     const bool hi = (c & 1) != 0;
-    float x[4];
+    float x[NT];
 #pragma unroll
-    for (int s = 0; s < 4; ++s) x[s] = (hi ? bf16_hi(x4[s][p]) : bf16_lo(x4[s][p])) * bq[s];
-    u32x2_t e;
-    e[0] = pack_bf16(x[0], x[1]);
-    e[1] = pack_bf16(x[2], x[3]);
-    return e;
+    for (int s = 0; s < NT; ++s) x[s] = (hi ? bf16_hi(x4[s][p]) : bf16_lo(x4[s][p])) * bq[s];
+#pragma unroll
+    for (int s = 0; s < NT / 2; ++s) e[s] = pack_bf16(x[2 * s], x[2 * s + 1]);
   };
 
-  // staging write offsets: channel row 8 cg + c, slot tg.  With
-  // Q = swz(8 cg + c) ^ c = (8 (cg & 1)) ^ cg (independent of c),
-  // off8(8 cg + c, tg) = ((2048 cg) | (8 tg ^ 16 Q)) ^ (16 c) + 256 c; V rows
-  // 128 + 8 cg + c have the same swizzle, 32 KiB further.
-  const uint32_t wbase = (uint32_t)(2048 * cg) | ((8u * tg) ^ (16u * ((8u * (cg & 1)) ^ cg)));
-  auto write_channel = [&](const TileRegs& r, const float (&sb4)[4], int stage, int c) {
+  // staging write offsets: channel row 8 cg + c, token slot tg (NT tokens,
+  // 2 NT bytes; 8 / NT slots per 16-byte chunk).  With
+  // Q = swz(8 cg + c) ^ c = (8 (cg & 1)) ^ cg (independent of c), the byte
+  // offset is ((2048 cg) | (((tg / (8 / NT)) ^ Q) << 4) | (2 NT (tg % (8 / NT))))
+  // ^ (16 c), + 256 c; V rows 128 + 8 cg + c have the same swizzle, 32 KiB further.
+  constexpr int kSlots = 8 / NT;
+  const uint32_t Q = (8u * (cg & 1)) ^ cg;
+  const uint32_t wbase = (uint32_t)(2048 * cg) | ((((uint32_t)tg / kSlots) ^ Q) << 4) |
+                         (2u * NT * ((uint32_t)tg % kSlots));
+  auto write_channel = [&](const TileRegs& r, const float (&sb4)[NT], int stage, int c) {
     unsigned char* X = smem + stage * kStageBytes + 256 * c;
     const uint32_t o = wbase ^ (16u * c);
-    if (kact) *reinterpret_cast<u32x2_t*>(X + o) = scaled_pair(r.k, sb4, c);
-    if (vact) *reinterpret_cast<u32x2_t*>(X + o + 128 * kRowBytes) = scaled_pair(r.v, sb4, c);
+    uint32_t e[NT / 2];
+    if (kact) {
+      scaled(r.k, sb4, c, e);
+      if constexpr (NT == 4) *reinterpret_cast<u32x2_t*>(X + o) = u32x2_t{e[0], e[NT / 2 - 1]};
+      else *reinterpret_cast<uint32_t*>(X + o) = e[0];
+    }
+    if (vact) {
+      scaled(r.v, sb4, c, e);
+      if constexpr (NT == 4) *reinterpret_cast<u32x2_t*>(X + o + 128 * kRowBytes) = u32x2_t{e[0], e[NT / 2 - 1]};
+      else *reinterpret_cast<uint32_t*>(X + o + 128 * kRowBytes) = e[0];
+    }
   };
-  // contraction role: wave w owns output row tile w of [A; B]
+  // contraction role: wave w owns output row tile rt of [A; B] and column
+  // tiles ct0 .. ct0 + NCT - 1
   const int nK = pad32(dk) >> 5;
   const int nV = pad32(dv) >> 5;
   const int nR = nK + nV;
-  const bool ract = w < nR;
-  const int rbase = w < nK ? 32 * w : 128 + 32 * (w - nK);
-  f32x16_t acc[4];
+  const int rt = NT == 4 ? w : (w & 7);
+  const int ct0 = NT == 4 ? 0 : 2 * (w >> 3);
+  const bool ract = rt < nR;
+  const int rbase = rt < nK ? 32 * rt : 128 + 32 * (rt - nK);
+  f32x16_t acc[NCT];
 #pragma unroll
-  for (int ct = 0; ct < 4; ++ct) acc[ct] = zero16();
+  for (int j = 0; j < NCT; ++j) acc[j] = zero16();
 
   // operand offsets: off16(row, j) with j = 2 kk + kh equals
   // (row * 256 + ((16 kh) ^ (swz(row) << 4))) ^ (32 kk)
@@ -201,26 +219,26 @@ __global__ __launch_bounds__(512, 1) void stats_bf16_kernel(
     return (uint32_t)row * kRowBytes + ((16u * kh) ^ (swz(row) << 4));
   };
   const uint32_t abase = opbase(rbase + il);
-  uint32_t bbase[4];
+  uint32_t bbase[NCT];
 #pragma unroll
-  for (int ct = 0; ct < 4; ++ct) bbase[ct] = opbase(32 * ct + il);
+  for (int j = 0; j < NCT; ++j) bbase[j] = opbase(32 * (ct0 + j) + il);
 
   // Multiply the tile in `cstage` (8 k-steps of 16 tokens) and, interleaved
   // with it, stage channel c = kk of the
   // register set `r` (tile cw) into `wstage`.
   auto compute_write = [&](int cstage, const TileRegs& r, Cur cw, int wstage) {
     const unsigned char* X = smem + cstage * kStageBytes;
-    float sb4[4];
+    float sb4[NT];
     sqrt_beta(r, cw, sb4);
 #pragma unroll
     for (int kk = 0; kk < kTok / 16; ++kk) {
       if (ract) {
         const u32x4_t a = *reinterpret_cast<const u32x4_t*>(X + (abase ^ (32u * kk)));
 #pragma unroll
-        for (int ct = 0; ct < 4; ++ct) {
-          if (ct < nK) {
-            const u32x4_t bq = *reinterpret_cast<const u32x4_t*>(X + (bbase[ct] ^ (32u * kk)));
-            acc[ct] = mfma_bf16(a, bq, acc[ct]);
+        for (int j = 0; j < NCT; ++j) {
+          if (ct0 + j < nK) {
+            const u32x4_t bq = *reinterpret_cast<const u32x4_t*>(X + (bbase[j] ^ (32u * kk)));
+            acc[j] = mfma_bf16(a, bq, acc[j]);
           }
         }
       }
@@ -232,25 +250,25 @@ __global__ __launch_bounds__(512, 1) void stats_bf16_kernel(
   // channels; the accumulators restart at zero
   auto store_frame = [&](int g) {
     if (ract) {
-      const bool isA = w < nK;
-      const int ch0 = isA ? 32 * w : 32 * (w - nK);
+      const bool isA = rt < nK;
+      const int ch0 = isA ? 32 * rt : 32 * (rt - nK);
       const int nrows = isA ? dk : dv;
       const size_t slot = (size_t)g + g / F + 1;  // after the unit's text frame
       float* dst = isA ? Aout + slot * dk * dk : Bout + slot * dv * dk;
 #pragma unroll
-      for (int ct = 0; ct < 4; ++ct) {
-        if (ct >= nK) continue;
-        const int col = 32 * ct + (lane & 31);
+      for (int j = 0; j < NCT; ++j) {
+        if (ct0 + j >= nK) continue;
+        const int col = 32 * (ct0 + j) + (lane & 31);
         if (col >= dk) continue;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int row = ch0 + acc_row(r, lane);
-          if (row < nrows) dst[(size_t)row * dk + col] = acc[ct][r];
+          if (row < nrows) dst[(size_t)row * dk + col] = acc[j][r];
         }
       }
     }
 #pragma unroll
-    for (int ct = 0; ct < 4; ++ct) acc[ct] = zero16();
+    for (int j = 0; j < NCT; ++j) acc[j] = zero16();
   };
   auto last_tile = [&](Cur c) { return c.i + 1 == ntiles_of(frame_src(c.g).ntok); };
 
@@ -266,7 +284,7 @@ __global__ __launch_bounds__(512, 1) void stats_bf16_kernel(
   load(ra, c0);
   load(rb, c1);
   {
-    float sb4[4];
+    float sb4[NT];
     sqrt_beta(ra, c0, sb4);
 #pragma unroll
     for (int c = 0; c < 8; ++c) write_channel(ra, sb4, 0, c);
@@ -525,10 +543,14 @@ hipError_t launch_stats(const Plan& p, const void* k, const void* v, const float
                        text_beta, w.A, w.B, p.F, p.T, p.dk, p.dv, ts);
     const int nframes = p.units * p.F;  // latent frames
     const int P = std::min(nframes, compute_units());
-    auto kern = (p.dk == 128 && p.dv == 128) ? stats_bf16_kernel<128, 128> : stats_bf16_kernel<0, 0>;
-    hipLaunchKernelGGL(kern, dim3(P), dim3(kStatsThreads), 0, s,
-                       static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), beta, w.A,
-                       w.B, p.F, p.U, p.dk, p.dv, nframes, p.anchors);
+    if (p.dk == 128 && p.dv == 128)
+      hipLaunchKernelGGL((stats_bf16_kernel<128, 128, 2>), dim3(P), dim3(2 * kStatsThreads), 0, s,
+                         static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), beta,
+                         w.A, w.B, p.F, p.U, p.dk, p.dv, nframes, p.anchors);
+    else
+      hipLaunchKernelGGL((stats_bf16_kernel<0, 0, 4>), dim3(P), dim3(kStatsThreads), 0, s,
+                         static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), beta,
+                         w.A, w.B, p.F, p.U, p.dk, p.dv, nframes, p.anchors);
   } else {
     hipLaunchKernelGGL(stats_f32_kernel, grid, dim3(kThreads), 0, s,
                        static_cast<const float*>(k), static_cast<const float*>(v), beta,
