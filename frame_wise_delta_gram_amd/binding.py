@@ -168,8 +168,8 @@ def vda_forward_timed(desc, q, k, v, beta, alpha, gate, text_k, text_v, text_bet
                       out, workspace, stage_events, workspace_bytes=None, stream=None):
     """C vda_forward_timed: as vda_forward (alpha None) or vda_forward_decay,
     recording the six caller-created hipEvent_t handles (ints) in
-    ``stage_events`` at the stage boundaries."""
-    ev = (ctypes.c_void_p * 6)(*[int(e) for e in stage_events])
+    ``stage_events`` at the stage boundaries (None or 0 skips a boundary)."""
+    ev = (ctypes.c_void_p * 6)(*[int(e) if e else None for e in stage_events])
     st = load_library().vda_forward_timed(
         ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(alpha), _ptr(gate),
         _ptr(text_k), _ptr(text_v), _ptr(text_beta), _ptr(rms_weight), _ptr(out),

@@ -147,7 +147,7 @@ int hip_status(hipError_t e) { return e == hipSuccess ? VDA_OK : VDA_ERR_HIP; }
 int run_states(const Plan& p, const void* k, const void* v, const float* beta, const void* tk,
                const void* tv, const float* tb, const WsPtrs& w, hipStream_t s, int upto,
                const float* alpha = nullptr, hipEvent_t const* ev = nullptr) {
-  auto rec = [&](int i) { return ev ? hipEventRecord(ev[i], s) : hipSuccess; };
+  auto rec = [&](int i) { return ev && ev[i] ? hipEventRecord(ev[i], s) : hipSuccess; };
   if (p.units == 0 || p.F == 0) {  // nothing to launch; keep the event sequence complete
     for (int i = 0; i < upto; ++i)
       if (rec(i) != hipSuccess) return VDA_ERR_HIP;
@@ -183,10 +183,10 @@ int forward_impl(const vda_desc_t* desc, const void* q, const void* k, const voi
   const WsPtrs w = carve(p, workspace);
   st = run_states(p, k, v, beta, text_k, text_v, text_beta, w, s, 4, alpha, ev);
   if (st != VDA_OK) return st;
-  if (ev && hipEventRecord(ev[4], s) != hipSuccess) return VDA_ERR_HIP;
+  if (ev && ev[4] && hipEventRecord(ev[4], s) != hipSuccess) return VDA_ERR_HIP;
   if (video && launch_readout(p, q, gate, rms_weight, out, w, alpha, s) != hipSuccess)
     return VDA_ERR_HIP;
-  if (ev && hipEventRecord(ev[5], s) != hipSuccess) return VDA_ERR_HIP;
+  if (ev && ev[5] && hipEventRecord(ev[5], s) != hipSuccess) return VDA_ERR_HIP;
   return VDA_OK;
 }
 
@@ -332,8 +332,6 @@ int vda_forward_timed(const vda_desc_t* desc, const void* q, const void* k, cons
                       const float* rms_weight, void* out, void* workspace, size_t workspace_bytes,
                       vda_stream_t stream, void* const* stage_events, int n_events) {
   if (!stage_events || n_events != 6) return VDA_ERR_INVALID_ARG;
-  for (int i = 0; i < 6; ++i)
-    if (!stage_events[i]) return VDA_ERR_INVALID_ARG;
   if (alpha) {
     const int st = vda::check_decay(desc, alpha);
     if (st != VDA_OK) return st;

@@ -156,8 +156,10 @@ int vda_forward(const vda_desc_t* desc, const void* q, const void* k, const void
  * at the stage boundaries, for per-kernel timing: stage_events[0] before the
  * statistics kernels, [1] before the solve, [2] before the chunk composition,
  * [3] before the scan, [4] before the readout and [5] after it.  n_events
- * must be 6 and every event non-NULL.  Results are identical to the untimed
- * entry point. */
+ * must be 6; a NULL entry skips that boundary (each recorded event is a
+ * stream marker that adds a few microseconds between the kernels it
+ * separates, so timing one stage needs only its two events).  Results are
+ * identical to the untimed entry point. */
 int vda_forward_timed(const vda_desc_t* desc, const void* q, const void* k, const void* v,
                       const float* beta, const float* alpha, const void* gate,
                       const void* text_k, const void* text_v, const float* text_beta,
