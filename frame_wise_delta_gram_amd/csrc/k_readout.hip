@@ -8,8 +8,11 @@
 //   readout: o = S~ q                              (d_v outputs per token)
 //   epilogue: out = sigmoid(g) * w * o / sqrt(mean(o^2) + eps)
 //
-// bf16 path.  One workgroup per (unit, chunk, block of 1024 token rows); all
-// frames of a chunk share S~.  S~ is formed in fp32, split into a bf16 high
+// bf16 path.  One workgroup per (unit, chunk, row block); all frames of a
+// chunk share S~.  A chunk's rows are cut into 128-row pieces dealt round-robin
+// to its nblk workgroups (workgroup b takes pieces b, b + nblk, b + 2 nblk,
+// b + 3 nblk), so the workgroups of a chunk sweep its rows side by side (on
+// MI355X about 2% faster than contiguous 1024-row blocks per workgroup).  S~ is formed in fp32, split into a bf16 high
 // part and a bf16 residual (S~ = hi + lo to ~2^-17 relative) and kept in LDS,
 // so the readout is two bf16 MFMAs with fp32 accumulation and the HBM-bound
 // stream of q, gate and out never waits on a conversion.  The transposed
@@ -23,9 +26,8 @@
 // channel 32 (T / 2) + 8 h + 4 (T % 2) + r: each lane ends with four
 // 8-channel groups of its token (channels 32 m + 8 h .. + 7), gate loads and output stores are
 // 16-byte vectors in the same 16-rows x 64-bytes pattern, and the RMSNorm
-// reduction is a lane-local sum plus two cross-lane adds.  Each A operand read
-// from LDS feeds two 16-token groups.  Math in the epilogue is fp32; the
-// output is rounded to bf16 (nearest even).
+// reduction is a lane-local sum plus two cross-lane adds.  Math in the
+// epilogue is fp32; the output is rounded to bf16 (nearest even).
 //
 // With channel-wise decay (App. A.3 Eq. (A.4) with alpha_t in [0, 1]^{d_k}) the
 // gathered state depends on the frame: frame f of chunk c reads
@@ -50,7 +52,7 @@ namespace vda {
 namespace {
 
 constexpr int kThreadsR = 512;            // 8 waves; two workgroups per CU
-constexpr int kGroups = 8;                // 16-row groups per wave
+constexpr int kGroups = 4;                // 16-row groups per wave (one per 128-row piece)
 constexpr int kRows = 8 * 16 * kGroups;   // token rows per workgroup
 
 // Channel-wise decay products of the bridge for frame f of chunk c, by threads
@@ -129,7 +131,7 @@ __global__ __launch_bounds__(512, 4) void readout_bf16_kernel(
   const int f0 = DECAY ? seg : c * C;
   const int f1 = DECAY ? seg + 1 : min(f0 + C, F);
   const long rows_total = (long)(f1 - f0) * U;
-  const long row0 = (long)blk * kRows;
+  const long row0 = (long)blk * 128;  // first of the workgroup's 128-row pieces
   if (row0 >= rows_total) return;
   long zlo, zhi;  // rows [zlo, zhi) of the segment get linear output
   live_rows(anchors, f0, f1, c, F, U, C, radius, rows_total, zlo, zhi);
@@ -302,10 +304,11 @@ __global__ __launch_bounds__(512, 4) void readout_bf16_kernel(
     }
   };
 
-  // groups w, w + 8, w + 16, ... of the block; q ping-pongs between two
-  // register sets, unrolled by two (no register copies between groups)
+  // wave w takes rows 16 w .. 16 w + 15 of each of the workgroup's pieces; q
+  // ping-pongs between two register sets, unrolled by two (no register copies
+  // between groups)
   u32x4_t q0[4], q1[4], gr[4];
-  auto grp_row = [&](int it) { return row0 + (long)(it * 8 + w) * 16; };
+  auto grp_row = [&](int it) { return ((long)it * nblk + blk) * 128 + (long)w * 16; };
   load_q(q0, grp_row(0));
   for (int it = 0; it < kGroups; it += 2) {
     if (grp_row(it) >= rows_total) break;

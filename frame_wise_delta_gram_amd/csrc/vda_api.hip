@@ -52,13 +52,13 @@ int make_plan(const vda_desc_t* d, Plan* p) {
   // A launch holds fewer than 2^32 work-items along x: at most 2^22 workgroups
   // on the 512-thread 1-D grids (readout, bf16 composition), fewer than 2^24 on
   // the 256-thread fp32 readout grid.  Readout work items: units x segments x
-  // row blocks (1024 rows bf16, 64 rows fp32); segments are chunks, or frames
+  // row blocks (512 rows bf16, 64 rows fp32); segments are chunks, or frames
   // with decay (checked by the decay entry points).
   const int64_t rows_per_chunk = (int64_t)d->chunk * d->tokens;
   const bool bf16 = d->in_dtype == VDA_DTYPE_BF16;
   auto grid_ok = [&](int64_t segs, int64_t seg_rows, int64_t comp_items) {
     int64_t items;
-    if (!mul_ok((int64_t)d->units * segs, (seg_rows + (bf16 ? 1023 : 63)) / (bf16 ? 1024 : 64),
+    if (!mul_ok((int64_t)d->units * segs, (seg_rows + (bf16 ? 511 : 63)) / (bf16 ? 512 : 64),
                 &items))
       return false;
     return items < (bf16 ? (INT64_C(1) << 22) : (INT64_C(1) << 24)) &&

@@ -121,7 +121,8 @@ TOL_OUT = {"f32": 1e-4, "bf16": 2e-2}
 
 def timed_forward_matches(d: dict, cfg: W.Config):
     """vda_forward_timed (with decay gates when d holds them) gives bit-identical
-    output to the untimed entry point and records six completed events."""
+    output to the untimed entry point and records six completed events; with
+    four of them (two NULL entries) the same output and the four recorded."""
     import ctypes
     import os
     import torch
@@ -153,8 +154,23 @@ def timed_forward_matches(d: dict, cfg: W.Config):
             assert ms.value >= 0.0
             total += ms.value
         assert total > 0.0
-        return torch.equal(out.view(torch.int16) if out.dtype == torch.bfloat16 else out,
-                           ref.view(torch.int16) if ref.dtype == torch.bfloat16 else ref)
+        same = lambda x: torch.equal(x.view(torch.int16) if x.dtype == torch.bfloat16 else x,
+                                     ref.view(torch.int16) if ref.dtype == torch.bfloat16 else ref)
+        if not same(out):
+            return False
+        # NULL entries skip their boundaries; the others are still recorded
+        out2 = torch.empty_like(ref)
+        part = [ev[0], ev[1], None, None, ev[4], ev[5]]
+        vda.vda_forward_timed(desc, d["q"], d["k"], d["v"], d["beta"], d.get("alpha"), d["gate"],
+                              d["text_k"], d["text_v"], d["text_beta"], d["rms_weight"], out2,
+                              ws, part)
+        torch.cuda.synchronize()
+        for a, b in ((0, 1), (4, 5)):
+            ms = ctypes.c_float()
+            assert hip.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(ev[a]),
+                                           ctypes.c_void_p(ev[b])) == 0
+            assert ms.value >= 0.0
+        return same(out2)
     finally:
         for e in ev:
             hip.hipEventDestroy(ctypes.c_void_p(e))

@@ -152,9 +152,10 @@ def test_workspace_formula(lib):
     (dict(units=65535, frames=20000), vda.VDA_ERR_INVALID_ARG),
     (dict(units=1, frames=1048577, chunk=100, tokens=1), vda.VDA_ERR_INVALID_ARG),
     (dict(units=1, frames=1048576, chunk=100, tokens=1), vda.VDA_OK),
-    # readout grid: units x chunks x 1024-row blocks below 2^22
-    (dict(units=64, frames=50000, chunk=5, tokens=2048), vda.VDA_ERR_INVALID_ARG),
-    (dict(units=64, frames=20000, chunk=5, tokens=2048), vda.VDA_OK),
+    # readout grid: units x chunks x 512-row blocks below 2^22 (64 x 3400 x 20 > 2^22,
+    # 64 x 3200 x 20 < 2^22)
+    (dict(units=64, frames=17000, chunk=5, tokens=2048), vda.VDA_ERR_INVALID_ARG),
+    (dict(units=64, frames=16000, chunk=5, tokens=2048), vda.VDA_OK),
     (dict(dtype=7), vda.VDA_ERR_BAD_DTYPE),
     (dict(units=0, frames=0, tokens=0), vda.VDA_OK),
     (dict(d_k=16, d_v=128), vda.VDA_OK),
@@ -233,9 +234,9 @@ def test_forward_decay_argument_errors(lib):
     e = desc(units=0)
     assert lib.vda_forward_decay(ctypes.byref(e), *([None] * 12), 0, None) == vda.VDA_OK
     # one segment per frame: a problem whose per-chunk readout grid fits but whose
-    # per-frame grid (units x frames x 1024-row blocks) does not is refused by the
-    # decay entry points only
-    big = desc(units=64, frames=39063, tokens=1025, text_tokens=0)
+    # per-frame grid (units x frames x 512-row blocks) does not is refused by the
+    # decay entry points only: 64 x 8000 chunks x 6 blocks < 2^22 <= 64 x 40000 x 2
+    big = desc(units=64, frames=40000, tokens=513, text_tokens=0)
     assert vda.vda_check_desc(big) == vda.VDA_OK
     assert call_forward_decay(lib, big) == vda.VDA_ERR_INVALID_ARG
     P = [4096 * (i + 1) for i in range(12)]
