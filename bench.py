@@ -121,9 +121,10 @@ PROFILE_COMMANDS = {  # CFG: the workload id
             "--config CFG --steps 2 --warmup 1 --cpu-seconds 0 --decay-steps 0 "
             "--batched-steps 0 --prep-steps 0",
     "stats": "rocprofv3 --kernel-trace --stats -d DIR/trace -o vda --output-format csv -- "
-             "python bench.py --config CFG --steps 5 --warmup 2 --cpu-seconds 0 --decay-steps 0 "
-             "--batched-steps 0 --prep-steps 0",
+             "python bench.py --config CFG --steps 20 --warmup 50 --cpu-seconds 0 "
+             "--decay-steps 0 --batched-steps 0 --prep-steps 0",
 }
+TRACE_WARMUP, TRACE_STEPS = 50, 20  # of the kernel-trace command above
 KERNELS = ("stats_text", "stats", "solve", "compose", "scan", "readout")  # launch order
 PREP_COMMAND = ("rocprofv3 {pmc} -d DIR/{sub} -o p --output-format csv -- python bench.py "
                 "--steps 1 --warmup 0 --cpu-seconds 0 --decay-steps 0 --batched-steps 0 "
@@ -259,6 +260,20 @@ def summarize(prof_dir, cfg_id):
             if k and k != "copy":
                 durations[k] = (int(r["Calls"]), float(r["AverageNs"]) / 1e3,
                                 float(r["MinNs"]) / 1e3, float(r["MaxNs"]) / 1e3)
+    # the launches of the bench's timed steps: each kernel's calls after the
+    # warm-up ones, in launch order
+    launches = collections.defaultdict(list)
+    with open(os.path.join(prof_dir, "trace", "vda_kernel_trace.csv")) as fh:
+        for r in csv.DictReader(fh):
+            k = short_kernel_name(r["Kernel_Name"])
+            if k and k != "copy":
+                launches[k].append((int(r["Start_Timestamp"]), int(r["End_Timestamp"])))
+    timed = {}
+    for k, v in launches.items():
+        v.sort()
+        sel = v[TRACE_WARMUP:TRACE_WARMUP + TRACE_STEPS]
+        if sel:
+            timed[k] = sum(e - b for b, e in sel) / len(sel) / 1e3
     os.makedirs(PROFILES, exist_ok=True)
     order = [k for k in KERNELS if k in durations]
     head = (f"{cfg.name} workload ({cfg.units} heads x {cfg.frames} frames x {cfg.tokens} "
@@ -268,14 +283,20 @@ def summarize(prof_dir, cfg_id):
     cmd = {c: PROFILE_COMMANDS[c].replace("CFG", str(cfg_id)) for c in PROFILE_COMMANDS}
     lines += [f"    {cmd[c]}" for c in ("stats", "FETCH_SIZE", "WRITE_SIZE", "MFMA")]
     lines += [f"    python bench.py --summarize DIR --config {cfg_id}", "",
-              "## Kernel durations (`vda_kernel_stats.csv`)", "",
-              "| kernel | calls | average (us) | min (us) | max (us) | algorithmic GB/s |",
-              "|---|---|---|---|---|---|"]
+              "## Kernel durations (`vda_kernel_stats.csv`, `vda_kernel_trace.csv`)", "",
+              f"All calls: {TRACE_WARMUP} warm-up steps, {TRACE_STEPS} timed steps, "
+              f"{TRACE_STEPS} per-stage breakdown steps. Timed: the {TRACE_STEPS} launches of "
+              "the timed steps (the bench's own events time the same launches).", "",
+              "| kernel | calls | average, all calls (us) | min (us) | max (us) | "
+              "average, timed steps (us) | algorithmic GB/s (timed) |",
+              "|---|---|---|---|---|---|---|"]
     for k in order:
         c, a, lo, hi = durations[k]
-        lines.append(f"| {k} | {c} | {a:.1f} | {lo:.1f} | {hi:.1f} | "
-                     f"{alg[k][0] / (a * 1e-6) / 1e9:.0f} |")
-    lines += ["", f"Sum of averages: {sum(durations[k][1] for k in order):.1f} us per forward step."]
+        tk = timed.get(k, a)
+        lines.append(f"| {k} | {c} | {a:.1f} | {lo:.1f} | {hi:.1f} | {tk:.1f} | "
+                     f"{alg[k][0] / (tk * 1e-6) / 1e9:.0f} |")
+    lines += ["", f"Sum of the timed-step averages: {sum(timed.get(k, durations[k][1]) for k in order):.1f} "
+              "us per forward step."]
     mfma_path = os.path.join(prof_dir, "MFMA", "p_counter_collection.csv")
     if os.path.exists(mfma_path):
         # per dispatch: MOPS (x 512 flop), MFMA busy cycles summed over the SIMDs,
@@ -300,7 +321,7 @@ def summarize(prof_dir, cfg_id):
                 agg[kname[i]][name].append(val)
         lines += ["", "## MFMA counters per launch (`SQ_INSTS_VALU_MFMA_MOPS_*`)", "",
                   "Executed MFMA flops = MOPS x 512 (hi/lo splits execute more than the algorithmic "
-                  "flops); rates use the trace's average duration; peaks: bf16 2516.6, fp32 matrix "
+                  "flops); rates use the timed-step average duration; peaks: bf16 2516.6, fp32 matrix "
                   "157.3 TFLOP/s.", "",
                   "| kernel | bf16 flops executed | fp32 flops executed | algorithmic bf16 flops | "
                   "executed bf16 TFLOP/s (% of peak) | executed fp32 TFLOP/s (% of peak) |",
@@ -310,7 +331,7 @@ def summarize(prof_dir, cfg_id):
                 continue
             m = {name: sum(v) / len(v) for name, v in agg[k].items()}
             algf = alg[k][1] if alg[k][1] is not None else 0
-            sec = durations[k][1] * 1e-6
+            sec = timed.get(k, durations[k][1]) * 1e-6
             fb = m.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", 0) * 512
             ff = m.get("SQ_INSTS_VALU_MFMA_MOPS_F32", 0) * 512
             lines.append(f"| {k} | {fb:.4g} | {ff:.4g} | {algf:.4g} | "
