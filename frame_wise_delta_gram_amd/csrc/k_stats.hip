@@ -309,121 +309,103 @@ __global__ __launch_bounds__(512 * (4 / NT), 1) void stats_bf16_kernel(
   }
 }
 
-// Text frame, bf16 features: [sqrt(b) K | sqrt(b) V]^T (sqrt(b) K) in fp32 on
-// the vector ALUs (sqrt(b) x formed and kept in fp32).  One workgroup per
-// (16-row tile of [A; B], unit); thread t owns row t / 16 of the tile and the
-// 8 key columns 4 (t % 16) + 64 j + e (j < 2, e < 4).  Tokens stream through
-// LDS in tiles of 64, loaded as 16-byte vectors one tile ahead.
-constexpr int kTokT = 64;
-constexpr int kXcS = 132;  // LDS row stride (floats) of the key-channel tile (16-byte rows)
-constexpr int kXrS = 17;   // ... of the tile's 16 row channels
+// Text frame, bf16 features: [sqrt(b) K | sqrt(b) V]^T (sqrt(b) K) with
+// sqrt(b) x formed in fp32 (never rounded to bf16) and multiplied on
+// v_mfma_f32_32x32x2_f32 (fp32 products and sums).  One workgroup per (32 x 32
+// output tile of [A; B], unit); its eight waves take an eighth of the text
+// tokens each, two tokens per instruction (the k slots: lane l reads token
+// 2 p + l / 32, channel l % 32 of the tile's row and column channels, 64
+// contiguous bytes per half-wave), loading one batch of 16 token pairs ahead,
+// and their partial tiles are summed in a fixed order through LDS.
+constexpr int kPairsT = 16;  // token pairs per load batch
+constexpr int kWavesT = 8;
 
-__global__ __launch_bounds__(256) void stats_text_kernel(
+__global__ __launch_bounds__(64 * kWavesT) void stats_text_kernel(
     const uint16_t* __restrict__ tk, const uint16_t* __restrict__ tv, const float* __restrict__ tb,
     float* __restrict__ Aout, float* __restrict__ Bout, int F, int T, int dk, int dv,
     float text_scale) {
-  __shared__ __align__(16) float Xc[kTokT * kXcS];  // sqrt(b) k, token-major
-  __shared__ float Xr[kTokT * kXrS];                 // the tile's 16 row channels, token-major
-  const int rt = blockIdx.x;
+  __shared__ float Ps[(kWavesT - 1) * 16 * 64];  // partial tiles of waves 1.., [wave][register][lane]
+  const int nK = pad32(dk) >> 5;
+  const int rt = blockIdx.x / nK;
+  const int ct = blockIdx.x - rt * nK;
   const int u = blockIdx.y;
-  const int t = threadIdx.x;
-  const int nK = dk >> 4;
   const bool isA = rt < nK;
-  const int ch0 = isA ? 16 * rt : 16 * (rt - nK);
+  const int rch0 = 32 * (isA ? rt : rt - nK);
   const int nrows = isA ? dk : dv;
+  const int cch0 = 32 * ct;
   const uint16_t* K = tk + (size_t)u * T * dk;
   const uint16_t* R = isA ? K : tv + (size_t)u * T * dv;  // source of the row channels
   const int ldr = isA ? dk : dv;
   const float* Bt = tb + (size_t)u * T;
-  const u32x4_t z4 = {0u, 0u, 0u, 0u};
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  const int ks = lane >> 5;
+  // channels clamped into the row (padding lanes read a valid channel, zeroed below)
+  const int rch = min(rch0 + (lane & 31), nrows - 1);
+  const int cch = min(cch0 + (lane & 31), dk - 1);
+  const bool rok = rch0 + (lane & 31) < nrows;
+  const bool cok = cch0 + (lane & 31) < dk;
+  const int npairs = (T + 1) >> 1;
+  const int per = (npairs + kWavesT - 1) / kWavesT;
+  const int p0 = min(w * per, npairs);
+  const int p1 = min(p0 + per, npairs);
 
-  // this thread's share of a token tile: 4 pieces of 8 key channels (token
-  // t / 16 + 16 i, channels 8 (t % 16) ..) and, for t < 128, 8 row channels
-  // (token t / 2, channels ch0 + 8 (t % 2) ..), with the tokens' beta
-  struct Regs {
-    u32x4_t kc[4];
-    float bc[4];
-    u32x4_t xr;
-    float br;
+  struct Batch {
+    uint16_t a[kPairsT], b[kPairsT];
+    float beta[kPairsT];
   };
-  const int c8 = t & 15;
-  const int sr = t >> 1;  // token of the row-channel piece (t < 128)
-  const int h8 = 8 * (t & 1);
-  auto load = [&](Regs& g, int base) {
+  auto load = [&](Batch& g, int p) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int tok = base + (t >> 4) + 16 * i;
-      const bool ok = tok < T && 8 * c8 < dk;
-      g.kc[i] = ok ? *reinterpret_cast<const u32x4_t*>(K + (size_t)tok * dk + 8 * c8) : z4;
-      g.bc[i] = tok < T ? Bt[tok] : 0.0f;
-    }
-    const int tok = base + sr;
-    const bool ok = t < 128 && tok < T;
-    g.xr = ok ? *reinterpret_cast<const u32x4_t*>(R + (size_t)tok * ldr + ch0 + h8) : z4;
-    g.br = ok ? Bt[tok] : 0.0f;
-  };
-  auto bf_lo = [](uint32_t x) { return __uint_as_float(x << 16); };
-  auto bf_hi = [](uint32_t x) { return __uint_as_float(x & 0xffff0000u); };
-  auto stage = [&](const Regs& g) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float sb = sqrtf(g.bc[i] * text_scale);
-      float* dst = Xc + ((t >> 4) + 16 * i) * kXcS + 8 * c8;
-      f32x4_t lo, hi;
-#pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        lo[2 * e] = sb * bf_lo(g.kc[i][e]);
-        lo[2 * e + 1] = sb * bf_hi(g.kc[i][e]);
-        hi[2 * e] = sb * bf_lo(g.kc[i][2 + e]);
-        hi[2 * e + 1] = sb * bf_hi(g.kc[i][2 + e]);
-      }
-      *reinterpret_cast<f32x4_t*>(dst) = lo;
-      *reinterpret_cast<f32x4_t*>(dst + 4) = hi;
-    }
-    if (t < 128) {
-      const float sb = sqrtf(g.br * text_scale);
-      float* dst = Xr + sr * kXrS + h8;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        dst[2 * e] = sb * bf_lo(g.xr[e]);
-        dst[2 * e + 1] = sb * bf_hi(g.xr[e]);
-      }
+    for (int e = 0; e < kPairsT; ++e) {
+      const int tok = 2 * (p + e) + ks;
+      const int tc = tok < T && p + e < p1 ? tok : 0;  // T > 0 whenever a batch is loaded
+      g.a[e] = R[(size_t)tc * ldr + rch];
+      g.b[e] = K[(size_t)tc * dk + cch];
+      g.beta[e] = tok < T && p + e < p1 ? Bt[tc] : 0.0f;
     }
   };
-
-  const int r = t >> 4;
-  const int c4 = 4 * (t & 15);
-  float acc[8];
+  auto bf = [](uint16_t x) { return __uint_as_float((uint32_t)x << 16); };
+  f32x16_t acc0 = zero16(), acc1 = zero16();
+  auto mul = [&](const Batch& g) {
 #pragma unroll
-  for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
-  Regs g;
-  load(g, 0);
-  for (int base = 0; base < T; base += kTokT) {
-    stage(g);
-    __syncthreads();
-    if (base + kTokT < T) load(g, base + kTokT);  // in flight during the products
-#pragma unroll 8
-    for (int s = 0; s < kTokT; ++s) {
-      const float xr = Xr[s * kXrS + r];
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const f32x4_t xc = *reinterpret_cast<const f32x4_t*>(Xc + s * kXcS + c4 + 64 * j);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) acc[4 * j + e] = fmaf(xr, xc[e], acc[4 * j + e]);
-      }
+    for (int e = 0; e < kPairsT; e += 2) {
+      const float s0 = __builtin_amdgcn_sqrtf(g.beta[e] * text_scale);
+      const float s1 = __builtin_amdgcn_sqrtf(g.beta[e + 1] * text_scale);
+      acc0 = mfma_f32(rok ? s0 * bf(g.a[e]) : 0.0f, cok ? s0 * bf(g.b[e]) : 0.0f, acc0);
+      acc1 = mfma_f32(rok ? s1 * bf(g.a[e + 1]) : 0.0f, cok ? s1 * bf(g.b[e + 1]) : 0.0f, acc1);
     }
-    __syncthreads();
+  };
+  Batch ga, gb;
+  int p = p0;
+  if (p < p1) load(ga, p);
+  while (p < p1) {
+    if (p + kPairsT < p1) load(gb, p + kPairsT);
+    mul(ga);
+    p += kPairsT;
+    if (p >= p1) break;
+    if (p + kPairsT < p1) load(ga, p + kPairsT);
+    mul(gb);
+    p += kPairsT;
   }
-  const int row = ch0 + r;
-  if (row >= nrows) return;
+  f32x16_t acc = acc0 + acc1;
+  if (w > 0) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) Ps[((w - 1) * 16 + r) * 64 + lane] = acc[r];
+  }
+  __syncthreads();
+  if (w != 0) return;
+#pragma unroll
+  for (int q = 0; q < kWavesT - 1; ++q)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[r] += Ps[(q * 16 + r) * 64 + lane];
   float* dst = isA ? Aout + (size_t)u * (F + 1) * dk * dk : Bout + (size_t)u * (F + 1) * dv * dk;
+  const int col = cch0 + (lane & 31);
+  if (col >= dk) return;
 #pragma unroll
-  for (int j = 0; j < 2; ++j)
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int col = c4 + 64 * j + e;
-      if (col < dk) dst[(size_t)row * dk + col] = acc[4 * j + e];
-    }
+  for (int r = 0; r < 16; ++r) {
+    const int row = rch0 + acc_row(r, lane);
+    if (row < nrows) dst[(size_t)row * dk + col] = acc[r];
+  }
 }
 
 // fp32 features: the same contraction, [sqrt(b) K | sqrt(b) V]^T (sqrt(b) K), on
@@ -537,8 +519,9 @@ hipError_t launch_stats(const Plan& p, const void* k, const void* v, const float
   const dim3 grid(p.F + 1, p.units);
   const float ts = p.seed_mode == 1 ? 0.5f : 1.0f;
   if (p.dtype == VDA_DTYPE_BF16) {
-    const dim3 tgrid((p.dk >> 4) + (p.dv >> 4), p.units);
-    hipLaunchKernelGGL(stats_text_kernel, tgrid, dim3(kThreads), 0, s,
+    const int nK = pad32(p.dk) >> 5;
+    const dim3 tgrid((nK + (pad32(p.dv) >> 5)) * nK, p.units);
+    hipLaunchKernelGGL(stats_text_kernel, tgrid, dim3(64 * kWavesT), 0, s,
                        static_cast<const uint16_t*>(text_k), static_cast<const uint16_t*>(text_v),
                        text_beta, w.A, w.B, p.F, p.T, p.dk, p.dv, ts);
     const int nframes = p.units * p.F;  // latent frames
