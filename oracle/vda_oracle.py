@@ -329,8 +329,8 @@ def forward_unit(q, k, v, beta, gate, text_k, text_v, text_beta, rms_weight,
     see the module notes).  Returns out
     (F x U x d_v), plus a dict of intermediates when taps=True: A, B (per
     frame; scaled under rule 2), M (per frame: the inherited-state factor,
-    Eq. (A.1), or I - A for the batched rules), seed, P, R, and with decay or anchors the
-    state St read by each frame (F x d_v x d_k; zero where nothing is read).
+    Eq. (A.1), or I - A for the batched rules), seed, P, R, and the state St read
+    by each frame (F x d_v x d_k; zero where nothing is read).
     With anchors P and R are (F - 1) x d_v x d_k arrays: P[j] through interior
     frame j (P[0] = seed), R[j - 1] from the last interior frame down to j
     (R[F - 2] = seed, the key F - 1 of App. A.3).
@@ -369,10 +369,8 @@ def forward_unit(q, k, v, beta, gate, text_k, text_v, text_beta, rms_weight,
         "B": np.array([s[1] for s in stats]).reshape(F, d_v, d_k),
         "M": np.array([_factor(stats[f][0], None if alpha is None else alpha[f], rule)
                        for f in range(F)]).reshape(F, d_k, d_k),
-        "seed": seed, "P": P, "R": R,
+        "seed": seed, "P": P, "R": R, "St": St,
     }
-    if alpha is not None:
-        tap["St"] = St
     return out, tap
 
 
