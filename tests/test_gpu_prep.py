@@ -134,3 +134,39 @@ def test_prep_fullsize_sampled():
                 err = row_rel_err(g, r[0][keep])
                 say(f"  unit {u} frames {lo}..{hi - 1} {label}': {err:.3e}")
                 assert err <= TOL["bf16"], (u, lo, label)
+
+
+def _random_prep_shapes(n=24, seed=2027):
+    rng = np.random.default_rng(seed)
+    dims = (16, 32, 48, 64, 80, 96, 112, 128)
+    out = []
+    for i in range(n):
+        cfg = P(740 + i, f"random-{i}", int(rng.integers(1, 3)), int(rng.integers(1, 4)),
+                int(rng.integers(1, 9)), int(rng.integers(1, 20)), int(rng.integers(1, 20)),
+                int(rng.choice(dims)), int(rng.choice(dims)), str(rng.choice(["f32", "bf16"])))
+        out.append((f"{i:02d}-{cfg.dtype}-B{cfg.batch}H{cfg.heads}F{cfg.frames}"
+                    f"-{cfg.height}x{cfg.width}-dk{cfg.d_k}dv{cfg.d_v}", cfg))
+    return out
+
+
+RANDOM = _random_prep_shapes()
+
+
+@pytest.mark.parametrize("name,cfg", RANDOM, ids=[r[0] for r in RANDOM])
+def test_prep_random_shapes(name, cfg):
+    """24 shapes from a fixed generator: batch 1-2, heads 1-3, frames 1-8, latent
+    grids from 1 x 1 to 19 x 19 (partial 8 x 8 tiles on both axes), d_k and d_v
+    independently from 16 to 128, fp32 or bf16; every row at the usual bars."""
+    require_gpu()
+    from oracle import prep_oracle
+    say(f"[prep random] {name}")
+    h = W.host_prep_inputs(cfg)
+    got = _run(cfg, h)
+    x = _f64(cfg, h)
+    ref = prep_oracle.prep(x["q"], x["k"], x["v"], x["wk_s"], x["wk_t"], x["wv_s"], x["wv_t"],
+                           cfg.eps)
+    for label, g, r in zip(("q", "k", "v"), got, ref):
+        err = row_rel_err(g, r)
+        say(f"  {label}' max row-rel err {err:.3e}")
+        assert g.shape == r.shape and np.all(np.isfinite(g))
+        assert err <= TOL[cfg.dtype], label
