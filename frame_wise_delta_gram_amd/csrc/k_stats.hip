@@ -26,12 +26,15 @@
 // products (vector ALU work overlapping the MFMAs), and the global loads of
 // the tile after that are in flight meanwhile (two register sets).
 //
-// bf16 path, text frame: fp32 on the vector ALUs (stats_text_kernel).  The
-// text state seeds both scans and, unlike a latent frame's thousands of
-// tokens, a handful of text tokens does not average out the bf16 rounding of
-// sqrt(beta) k: the seed is low-rank, its rounding errors are not, and a query
-// mostly orthogonal to the text keys reads the errors almost alone.  The text
-// frame is a small share of the work (T tokens per unit against F U).
+// bf16 path, text frame: fp32 products on v_mfma_f32_32x32x2_f32 with
+// sqrt(beta) x formed in fp32 (text_tile).  The text state seeds both scans
+// and, unlike a latent frame's thousands of tokens, a handful of text tokens
+// does not average out the bf16 rounding of sqrt(beta) k: the seed is
+// low-rank, its rounding errors are not, and a query mostly orthogonal to the
+// text keys reads the errors almost alone.  The text frame is a small share of
+// the work (T tokens per unit against F U): at d_k = d_v = 128 its tiles are
+// extra work items of the persistent kernel's workgroups that have one frame
+// fewer than the others (no launch of its own), else a kernel of its own.
 //
 // fp32 path: the same contraction in fp32 on the vector ALUs (exact fp32
 // products, fp32 accumulation) for fp32 features.
@@ -67,6 +70,118 @@ __device__ __forceinline__ uint32_t off16(uint32_t row, uint32_t j) {
   return row * kRowBytes + ((j ^ swz(row)) << 4);
 }
 
+// Text frame, bf16 features: tile `tile` (32 x 32, rows of [A; B], columns of
+// key channels) of unit u's [sqrt(b) K | sqrt(b) V]^T (sqrt(b) K), sqrt(b) x
+// formed in fp32 (never rounded to bf16) and multiplied on
+// v_mfma_f32_32x32x2_f32 (fp32 products and sums) by the NW waves of the
+// calling workgroup.  The waves split the text tokens, two per instruction
+// (the k slots: lane l reads token 2 p + l / 32, channel l % 32 of the tile's
+// row and column channels, 64 contiguous bytes per half-wave), loading one
+// batch of PAIRS token pairs ahead; their partial tiles are summed in a fixed
+// order through Ps ((NW - 1) x 4 KiB of LDS).  Every thread of the workgroup
+// calls it (it holds a barrier).
+template <int NW, int PAIRS>
+__device__ __forceinline__ void text_tile(const uint16_t* __restrict__ tk,
+                                          const uint16_t* __restrict__ tv,
+                                          const float* __restrict__ tb, float* __restrict__ Aout,
+                                          float* __restrict__ Bout, int F, int T, int dk, int dv,
+                                          float text_scale, int u, int tile, float* Ps) {
+  const int nK = pad32(dk) >> 5;
+  const int rt = tile / nK;
+  const int ct = tile - rt * nK;
+  const bool isA = rt < nK;
+  const int rch0 = 32 * (isA ? rt : rt - nK);
+  const int nrows = isA ? dk : dv;
+  const int cch0 = 32 * ct;
+  const uint16_t* K = tk + (size_t)u * T * dk;
+  const uint16_t* R = isA ? K : tv + (size_t)u * T * dv;  // source of the row channels
+  const int ldr = isA ? dk : dv;
+  const float* Bt = tb + (size_t)u * T;
+  const int lane = threadIdx.x & 63;
+  const int w = threadIdx.x >> 6;
+  const int ks = lane >> 5;
+  // channels clamped into the row (padding lanes read a valid channel, zeroed below)
+  const int rch = min(rch0 + (lane & 31), nrows - 1);
+  const int cch = min(cch0 + (lane & 31), dk - 1);
+  const bool rok = rch0 + (lane & 31) < nrows;
+  const bool cok = cch0 + (lane & 31) < dk;
+  const int npairs = (T + 1) >> 1;
+  const int per = (npairs + NW - 1) / NW;
+  const int p0 = min(w * per, npairs);
+  const int p1 = min(p0 + per, npairs);
+
+  struct Batch {
+    uint16_t a[PAIRS], b[PAIRS];
+    float beta[PAIRS];
+  };
+  auto load = [&](Batch& g, int p) {
+#pragma unroll
+    for (int e = 0; e < PAIRS; ++e) {
+      const int tok = 2 * (p + e) + ks;
+      const bool ok = tok < T && p + e < p1;
+      const int tc = ok ? tok : 0;  // T > 0 whenever a batch is loaded
+      g.a[e] = R[(size_t)tc * ldr + rch];
+      g.b[e] = K[(size_t)tc * dk + cch];
+      g.beta[e] = ok ? Bt[tc] : 0.0f;
+    }
+  };
+  auto bf = [](uint16_t x) { return __uint_as_float((uint32_t)x << 16); };
+  f32x16_t acc0 = zero16(), acc1 = zero16();
+  auto mul = [&](const Batch& g) {
+#pragma unroll
+    for (int e = 0; e < PAIRS; e += 2) {
+      const float s0 = __builtin_amdgcn_sqrtf(g.beta[e] * text_scale);
+      const float s1 = __builtin_amdgcn_sqrtf(g.beta[e + 1] * text_scale);
+      acc0 = mfma_f32(rok ? s0 * bf(g.a[e]) : 0.0f, cok ? s0 * bf(g.b[e]) : 0.0f, acc0);
+      acc1 = mfma_f32(rok ? s1 * bf(g.a[e + 1]) : 0.0f, cok ? s1 * bf(g.b[e + 1]) : 0.0f, acc1);
+    }
+  };
+  Batch ga, gb;
+  int p = p0;
+  if (p < p1) load(ga, p);
+  while (p < p1) {
+    if (p + PAIRS < p1) load(gb, p + PAIRS);
+    mul(ga);
+    p += PAIRS;
+    if (p >= p1) break;
+    if (p + PAIRS < p1) load(ga, p + PAIRS);
+    mul(gb);
+    p += PAIRS;
+  }
+  f32x16_t acc = acc0 + acc1;
+  if (w > 0 && w < NW) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) Ps[((w - 1) * 16 + r) * 64 + lane] = acc[r];
+  }
+  __syncthreads();
+  if (w == 0) {
+#pragma unroll 1
+    for (int q = 0; q < NW - 1; ++q)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[r] += Ps[(q * 16 + r) * 64 + lane];
+    float* dst = isA ? Aout + (size_t)u * (F + 1) * dk * dk : Bout + (size_t)u * (F + 1) * dv * dk;
+    const int col = cch0 + (lane & 31);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int row = rch0 + acc_row(r, lane);
+      if (row < nrows && col < dk) dst[(size_t)row * dk + col] = acc[r];
+    }
+  }
+  __syncthreads();  // Ps is free again
+}
+
+constexpr int kWavesT = 8;  // waves of the text-frame kernel
+
+// The text frame as a kernel of its own: one workgroup per (tile, unit).
+__global__ __launch_bounds__(64 * kWavesT) void stats_text_kernel(
+    const uint16_t* __restrict__ tk, const uint16_t* __restrict__ tv, const float* __restrict__ tb,
+    float* __restrict__ Aout, float* __restrict__ Bout, int F, int T, int dk, int dv,
+    float text_scale) {
+  __shared__ float Ps[(kWavesT - 1) * 16 * 64];
+  text_tile<kWavesT, 16>(tk, tv, tb, Aout, Bout, F, T, dk, dv, text_scale, blockIdx.y, blockIdx.x,
+                         Ps);
+}
+
 // Persistent: one workgroup per CU (the 128 KiB of LDS allow no more) walks
 // the frames b, b + P, b + 2P, ... of the flattened (unit, latent frame) list,
 // g = u F + f (stored at workspace frame u (F + 1) + f + 1), as ONE continuous
@@ -81,7 +196,8 @@ template <int DK, int DV, int NT>
 __global__ __launch_bounds__(512 * (4 / NT), 1) void stats_bf16_kernel(
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, const float* __restrict__ beta,
     float* __restrict__ Aout, float* __restrict__ Bout, int F, int U, int dk_rt, int dv_rt,
-    int nframes, int anchors) {
+    int nframes, int anchors, const uint16_t* __restrict__ tk, const uint16_t* __restrict__ tv,
+    const float* __restrict__ tb, int T, float text_scale, int text_items) {
   const int dk = DK > 0 ? DK : dk_rt;
   const int dv = DV > 0 ? DV : dv_rt;
   __shared__ __align__(16) unsigned char smem[2 * kStageBytes];
@@ -310,104 +426,20 @@ __global__ __launch_bounds__(512 * (4 / NT), 1) void stats_bf16_kernel(
     c2 = next(c2);
     if (c0.g >= nframes) break;
   }
-}
 
-// Text frame, bf16 features: [sqrt(b) K | sqrt(b) V]^T (sqrt(b) K) with
-// sqrt(b) x formed in fp32 (never rounded to bf16) and multiplied on
-// v_mfma_f32_32x32x2_f32 (fp32 products and sums).  One workgroup per (32 x 32
-// output tile of [A; B], unit); its eight waves take an eighth of the text
-// tokens each, two tokens per instruction (the k slots: lane l reads token
-// 2 p + l / 32, channel l % 32 of the tile's row and column channels, 64
-// contiguous bytes per half-wave), loading one batch of 16 token pairs ahead,
-// and their partial tiles are summed in a fixed order through LDS.
-constexpr int kPairsT = 16;  // token pairs per load batch
-constexpr int kWavesT = 8;
-
-__global__ __launch_bounds__(64 * kWavesT) void stats_text_kernel(
-    const uint16_t* __restrict__ tk, const uint16_t* __restrict__ tv, const float* __restrict__ tb,
-    float* __restrict__ Aout, float* __restrict__ Bout, int F, int T, int dk, int dv,
-    float text_scale) {
-  __shared__ float Ps[(kWavesT - 1) * 16 * 64];  // partial tiles of waves 1.., [wave][register][lane]
-  const int nK = pad32(dk) >> 5;
-  const int rt = blockIdx.x / nK;
-  const int ct = blockIdx.x - rt * nK;
-  const int u = blockIdx.y;
-  const bool isA = rt < nK;
-  const int rch0 = 32 * (isA ? rt : rt - nK);
-  const int nrows = isA ? dk : dv;
-  const int cch0 = 32 * ct;
-  const uint16_t* K = tk + (size_t)u * T * dk;
-  const uint16_t* R = isA ? K : tv + (size_t)u * T * dv;  // source of the row channels
-  const int ldr = isA ? dk : dv;
-  const float* Bt = tb + (size_t)u * T;
-  const int lane = threadIdx.x & 63;
-  const int w = threadIdx.x >> 6;
-  const int ks = lane >> 5;
-  // channels clamped into the row (padding lanes read a valid channel, zeroed below)
-  const int rch = min(rch0 + (lane & 31), nrows - 1);
-  const int cch = min(cch0 + (lane & 31), dk - 1);
-  const bool rok = rch0 + (lane & 31) < nrows;
-  const bool cok = cch0 + (lane & 31) < dk;
-  const int npairs = (T + 1) >> 1;
-  const int per = (npairs + kWavesT - 1) / kWavesT;
-  const int p0 = min(w * per, npairs);
-  const int p1 = min(p0 + per, npairs);
-
-  struct Batch {
-    uint16_t a[kPairsT], b[kPairsT];
-    float beta[kPairsT];
-  };
-  auto load = [&](Batch& g, int p) {
-#pragma unroll
-    for (int e = 0; e < kPairsT; ++e) {
-      const int tok = 2 * (p + e) + ks;
-      const int tc = tok < T && p + e < p1 ? tok : 0;  // T > 0 whenever a batch is loaded
-      g.a[e] = R[(size_t)tc * ldr + rch];
-      g.b[e] = K[(size_t)tc * dk + cch];
-      g.beta[e] = tok < T && p + e < p1 ? Bt[tc] : 0.0f;
-    }
-  };
-  auto bf = [](uint16_t x) { return __uint_as_float((uint32_t)x << 16); };
-  f32x16_t acc0 = zero16(), acc1 = zero16();
-  auto mul = [&](const Batch& g) {
-#pragma unroll
-    for (int e = 0; e < kPairsT; e += 2) {
-      const float s0 = __builtin_amdgcn_sqrtf(g.beta[e] * text_scale);
-      const float s1 = __builtin_amdgcn_sqrtf(g.beta[e + 1] * text_scale);
-      acc0 = mfma_f32(rok ? s0 * bf(g.a[e]) : 0.0f, cok ? s0 * bf(g.b[e]) : 0.0f, acc0);
-      acc1 = mfma_f32(rok ? s1 * bf(g.a[e + 1]) : 0.0f, cok ? s1 * bf(g.b[e + 1]) : 0.0f, acc1);
-    }
-  };
-  Batch ga, gb;
-  int p = p0;
-  if (p < p1) load(ga, p);
-  while (p < p1) {
-    if (p + kPairsT < p1) load(gb, p + kPairsT);
-    mul(ga);
-    p += kPairsT;
-    if (p >= p1) break;
-    if (p + kPairsT < p1) load(ga, p + kPairsT);
-    mul(gb);
-    p += kPairsT;
-  }
-  f32x16_t acc = acc0 + acc1;
-  if (w > 0) {
-#pragma unroll
-    for (int r = 0; r < 16; ++r) Ps[((w - 1) * 16 + r) * 64 + lane] = acc[r];
-  }
-  __syncthreads();
-  if (w != 0) return;
-#pragma unroll
-  for (int q = 0; q < kWavesT - 1; ++q)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) acc[r] += Ps[(q * 16 + r) * 64 + lane];
-  float* dst = isA ? Aout + (size_t)u * (F + 1) * dk * dk : Bout + (size_t)u * (F + 1) * dv * dk;
-  const int col = cch0 + (lane & 31);
-  if (col >= dk) return;
-#pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int row = rch0 + acc_row(r, lane);
-    if (row < nrows) dst[(size_t)row * dk + col] = acc[r];
+  // text-frame tiles (text_items > 0 only with 16 waves at d_k = d_v = 128):
+  // taken by the workgroups with one frame fewer than the others (by all of
+  // them when every workgroup has as many frames), round robin
+  if (NT == 2 && text_items > 0) {
+    __syncthreads();  // the stages are free
+    const int rem = nframes % P;
+    const int slot = rem == 0 ? b0 : b0 - rem;
+    const int nslots = rem == 0 ? P : P - rem;
+    const int tiles = text_items / (nframes / F);  // per unit
+    if (slot >= 0)
+      for (int j = slot; j < text_items; j += nslots)
+        text_tile<16, 4>(tk, tv, tb, Aout, Bout, F, T, dk, dv, text_scale, j / tiles, j % tiles,
+                         reinterpret_cast<float*>(smem));
   }
 }
 
@@ -523,20 +555,24 @@ hipError_t launch_stats(const Plan& p, const void* k, const void* v, const float
   const float ts = p.seed_mode == 1 ? 0.5f : 1.0f;
   if (p.dtype == VDA_DTYPE_BF16) {
     const int nK = pad32(p.dk) >> 5;
-    const dim3 tgrid((nK + (pad32(p.dv) >> 5)) * nK, p.units);
-    hipLaunchKernelGGL(stats_text_kernel, tgrid, dim3(64 * kWavesT), 0, s,
-                       static_cast<const uint16_t*>(text_k), static_cast<const uint16_t*>(text_v),
-                       text_beta, w.A, w.B, p.F, p.T, p.dk, p.dv, ts);
-    const int nframes = p.units * p.F;  // latent frames
+    const int tiles = (nK + (pad32(p.dv) >> 5)) * nK;  // text-frame tiles per unit
+    const int nframes = p.units * p.F;                 // latent frames
     const int P = std::min(nframes, compute_units());
-    if (p.dk == 128 && p.dv == 128)
+    const uint16_t* tk = static_cast<const uint16_t*>(text_k);
+    const uint16_t* tv = static_cast<const uint16_t*>(text_v);
+    if (p.dk == 128 && p.dv == 128) {  // the text tiles ride in the persistent kernel
       hipLaunchKernelGGL((stats_bf16_kernel<128, 128, 2>), dim3(P), dim3(2 * kStatsThreads), 0, s,
                          static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), beta,
-                         w.A, w.B, p.F, p.U, p.dk, p.dv, nframes, p.anchors);
-    else
+                         w.A, w.B, p.F, p.U, p.dk, p.dv, nframes, p.anchors, tk, tv, text_beta,
+                         p.T, ts, p.units * tiles);
+    } else {
+      hipLaunchKernelGGL(stats_text_kernel, dim3(tiles, p.units), dim3(64 * kWavesT), 0, s, tk, tv,
+                         text_beta, w.A, w.B, p.F, p.T, p.dk, p.dv, ts);
       hipLaunchKernelGGL((stats_bf16_kernel<0, 0, 4>), dim3(P), dim3(kStatsThreads), 0, s,
                          static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), beta,
-                         w.A, w.B, p.F, p.U, p.dk, p.dv, nframes, p.anchors);
+                         w.A, w.B, p.F, p.U, p.dk, p.dv, nframes, p.anchors, tk, tv, text_beta,
+                         p.T, ts, 0);
+    }
   } else {
     hipLaunchKernelGGL(stats_f32_kernel, grid, dim3(kThreads), 0, s,
                        static_cast<const float*>(k), static_cast<const float*>(v), beta,
