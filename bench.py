@@ -47,8 +47,10 @@ def algorithmic(cfg):
     """Algorithmic HBM bytes (and MFMA flops where the kernel is a contraction)
     per launch of each kernel: every input read once, every output written once.
     "stats" is the latent frames' kernel, "stats_text" the text frame's (fp32
-    vector ALUs); with decay the gates are read once by the composition and
-    once by the readout, and the composition also writes the reverse maps."""
+    MFMA), which at bf16 with d_k = d_v = 128 runs inside the "stats" kernel (its
+    work is then counted there and "stats_text" is zero); with decay the gates
+    are read once by the composition and once by the readout, and the
+    composition also writes the reverse maps."""
     eb = 2 if cfg.dtype == "bf16" else 4
     th = cfg.units * cfg.frames * cfg.tokens        # token-heads
     tt = cfg.units * cfg.text_tokens
@@ -65,8 +67,12 @@ def algorithmic(cfg):
                      + u * n * (nmaps * mat + 2 * st)                   # chunk maps out
                      + u * 2 * st)                                      # the two seed copies
     scan_bytes = u * n * (2 * mat + 2 * st) + u * 2 * n * st            # chunk maps in; P, R out
-    return {"stats": (stats_bytes, 2 * th * (dk + dv) * dk),
-            "stats_text": (text_bytes, 2 * tt * (dk + dv) * dk),
+    stats_flops, text_flops = 2 * th * (dk + dv) * dk, 2 * tt * (dk + dv) * dk
+    if cfg.dtype == "bf16" and dk == 128 and dv == 128:  # one kernel
+        stats_bytes, stats_flops, text_bytes, text_flops = (stats_bytes + text_bytes,
+                                                            stats_flops + text_flops, 0, 0)
+    return {"stats": (stats_bytes, stats_flops),
+            "stats_text": (text_bytes, text_flops),
             "readout": (readout_bytes, 2 * th * dk * dv),
             "solve": (solve_bytes, None), "compose": (compose_bytes, None),
             "scan": (scan_bytes, None)}
