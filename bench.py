@@ -619,6 +619,16 @@ def main():
     }
     hbm_whole = ((stage_alg(alg, "stats")[0] + alg["readout"][0]) / (ms_per_step * 1e-3)
                  / HBM_PEAK)
+    # the MFMA fraction a contraction can reach when its operands stream from HBM
+    # at the full 8 TB/s: arithmetic intensity x HBM peak / MFMA peak
+    def ceiling(flops, bytes_):
+        return min(1.0, flops / bytes_ * HBM_PEAK / BF16_PEAK)
+    mfma_ceiling = {
+        "whole_op": ceiling(stats_flops + alg["readout"][1],
+                            stage_alg(alg, "stats")[0] + alg["readout"][0]),
+        "stats": ceiling(stats_flops, stage_alg(alg, "stats")[0]),
+        "readout": ceiling(alg["readout"][1], alg["readout"][0]),
+    }
     line = {
         "metric": METRIC, "value": value, "unit": "token-heads/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
@@ -631,12 +641,17 @@ def main():
                    "parallelism": "single GPU"},
         "roofline": roofline_of(cfg, avg_ms),
         "mfma_frac": mfma,
+        "mfma_ceiling_at_hbm_peak": mfma_ceiling,
+        "mfma_frac_of_ceiling": {k: mfma[k] / mfma_ceiling[k] for k in mfma},
         "hbm_frac_whole_op": hbm_whole,
         "stage_ms": split_steps(avg_ms)[0],
         "step_ms_from_events": split_steps(avg_ms)[1],
         "stream_ceiling": {"kernel": "torch.add over the q and gate tensors (2 reads + 1 write)",
                            "GB/s": add_bytes / (add_ms * 1e-3) / 1e9, "ms": add_ms},
     }
+    rl = line["roofline"]
+    line["stream_ceiling"]["dominant_kernel_frac"] = (rl["achieved"] * 1e9
+                                                      / (add_bytes / (add_ms * 1e-3)))
     if args.cpu_seconds > 0:
         log("[bench] CPU oracle baseline")
         line["cpu_baseline"] = cpu_baseline(d, cfg, args.cpu_seconds)
