@@ -39,34 +39,39 @@ __device__ __forceinline__ float readlane_f(float x, int l) {
 // (register r of lane l = T[acc_row(r, l)][l % 32]), by one wave; T becomes
 // -T^{-1}.  Row k sits in register rk = 4 (k / 8) + k % 4 of the lanes of half
 // hk = (k / 4) % 2, so it feeds both operands of a rank-1 32x32x2 MFMA through
-// the k-slot hk with no data movement: C_mn -= x_m y_n, x = row k (zero at k),
-// y = x / d.  That update leaves row and column k alone, so they are scaled
-// (and T_kk set to -1/d) before it, branch-free; forming them through the
-// rank-1 update instead would cancel catastrophically for large pivots.  The
-// hardware reciprocal is within 1 ulp.
+// the k-slot hk with no data movement.  The scaling of column k by 1/d is
+// deferred: each lane keeps a factor g for its column (true T = stored T times
+// g per column), which only column k's lanes change at step k, and the block is
+// multiplied by it once at the end, so a step costs two lane reads, one
+// reciprocal and a handful of vector ops besides the MFMA.  In stored terms, step
+// k with d = S_kk g_k (the true pivot) is, for i, j != k,
+//   S_ij -= (S_ki g_i) (S_kj / d)    (S_ki g_i = T_ki = T_ik by symmetry),
+// then S_kj *= 1/d (j != k), S_kk *= -1/d, g_k *= 1/d; row and column k are left
+// alone by the rank-1 update (its operands are zero at k).  The hardware
+// reciprocal is within 1 ulp.
 __device__ __forceinline__ void sweep_block(f32x16_t& T) {
   const int lane = lane_id();
   const int half = lane >> 5;
   const int c = lane & 31;
+  float g = 1.0f;
 #pragma unroll
   for (int k = 0; k < 32; ++k) {
     const int rk = 4 * (k >> 3) + (k & 3);
     const int hk = (k >> 2) & 1;
-    const float d = readlane_f(T[rk], k + 32 * hk);
-    const float inv = __builtin_amdgcn_rcpf(d);
+    const float skk = readlane_f(T[rk], k + 32 * hk);
+    const float gk = readlane_f(g, k);
+    const float inv = __builtin_amdgcn_rcpf(skk * gk);
     const bool inrow = half == hk;
     const bool colk = c == k;
-    const float x = (inrow && !colk) ? T[rk] : 0.0f;
-    const float fc = colk ? inv : 1.0f;  // column k
-#pragma unroll
-    for (int r = 0; r < 16; ++r)
-      if (r != rk) T[r] *= fc;
-    // register rk: row k scaled by 1/d off the pivot, the pivot set to -1/d,
-    // column k (other rows) scaled by 1/d
-    const float frk = inrow ? (colk ? 0.0f : inv) : fc;
-    T[rk] = fmaf(T[rk], frk, (inrow && colk) ? -inv : 0.0f);
-    T = mfma_f32(-x, x * inv, T);
+    const float s = (inrow && !colk) ? T[rk] : 0.0f;  // row k off the pivot (stored)
+    const float xa = s * g;
+    const float xb = s * inv;
+    T[rk] *= inrow ? (colk ? -inv : inv) : 1.0f;
+    g = colk ? g * inv : g;
+    T = mfma_f32(-xa, xb, T);
   }
+#pragma unroll
+  for (int r = 0; r < 16; ++r) T[r] *= g;
 }
 
 // acc += op(A) Bm for 32 x 32 blocks, A in LDS (row stride sa, op = transpose
