@@ -25,8 +25,8 @@
 //                                                      Mr_j in place of Mc_j^T with decay)
 //   Only these n + 1 boundary states per direction are ever written.
 //
-// The state and every map stay fp32 in memory ("the inverse and recurrent
-// state updates remain in FP32", Sec. 5).  Products:
+// The state and every map stay fp32 in memory (as the pages keep the inverse
+// and the recurrent state updates in fp32, Sec. 5).  Products:
 //   fp32 features: 32x32x2 fp32 MFMA block products (exact fp32 products);
 //   bf16 features: split bf16 MFMA ("bf16x3"): each fp32 operand x is held
 //     in LDS as x_hi = bf16(x), x_lo = bf16(x - x_hi) and x y is formed as

@@ -1,5 +1,7 @@
 // C ABI of the VDA forward library: argument checks, workspace carve-up and
-// the five-launch sequence on the caller's stream.  See include/vda.h for the
+// the launch sequence on the caller's stream (statistics, solve, composition,
+// scan, readout; a separate text-frame statistics launch except at bf16 with
+// d_k = d_v = 128).  See include/vda.h for the
 // contract of every entry point.
 #include <math.h>
 #include <stdint.h>
