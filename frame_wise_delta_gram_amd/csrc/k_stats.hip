@@ -428,13 +428,14 @@ __global__ __launch_bounds__(512 * (4 / NT), 1) void stats_bf16_kernel(
   }
 
   // text-frame tiles (text_items > 0 only with 16 waves at d_k = d_v = 128):
-  // taken by the workgroups with one frame fewer than the others (by all of
-  // them when every workgroup has as many frames), round robin
+  // taken round robin by the workgroups with one frame fewer than the others
+  // when there are enough of them for at most 8 tiles each, else by all
   if (NT == 2 && text_items > 0) {
     __syncthreads();  // the stages are free
     const int rem = nframes % P;
-    const int slot = rem == 0 ? b0 : b0 - rem;
-    const int nslots = rem == 0 ? P : P - rem;
+    const bool slack = rem != 0 && (P - rem) * 8 >= text_items;
+    const int slot = slack ? b0 - rem : b0;
+    const int nslots = slack ? P - rem : P;
     const int tiles = text_items / (nframes / F);  // per unit
     if (slot >= 0)
       for (int j = slot; j < text_items; j += nslots)
