@@ -62,7 +62,29 @@ def build(verbose: bool = False, jobs: int | None = None) -> str:
         # guaranteed across tmp and the tree, so move then return the final path
     finally:
         shutil.rmtree(tmp, ignore_errors=True)
+    build_c_demo()
     return LIB_PATH
+
+
+C_DEMO_SRC = os.path.join(ROOT, "tests", "c_abi", "forward_demo.c")
+C_DEMO = os.path.join(ROOT, "tests", "c_abi", "forward_demo")
+
+
+def build_c_demo() -> str | None:
+    """The plain-C consumer of the ABI that a GPU test runs (tests/c_abi):
+    gcc, C99, warnings as errors, linked against libvda.so (found next to the
+    package through an $ORIGIN-relative rpath) and the HIP runtime.  Returns
+    the executable's path, or None when no C compiler is installed."""
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None or not os.path.exists(C_DEMO_SRC):
+        return None
+    rocm = os.path.dirname(os.path.dirname(HIPCC))
+    _run([cc, "-std=c99", "-Wall", "-Wextra", "-pedantic", "-Werror", "-O2",
+          "-D__HIP_PLATFORM_AMD__", "-isystem", os.path.join(rocm, "include"), "-I", INCLUDE,
+          C_DEMO_SRC, "-o", C_DEMO, "-L", PKG, "-lvda", "-L", os.path.join(rocm, "lib"),
+          "-lamdhip64", "-lm", "-Wl,-rpath,$ORIGIN/../../frame_wise_delta_gram_amd",
+          "-Wl,-rpath," + os.path.join(rocm, "lib")])
+    return C_DEMO
 
 
 if __name__ == "__main__":
