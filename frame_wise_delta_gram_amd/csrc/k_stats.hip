@@ -197,7 +197,7 @@ __global__ __launch_bounds__(512 * (4 / NT), 1) void stats_bf16_kernel(
     const uint16_t* __restrict__ k, const uint16_t* __restrict__ v, const float* __restrict__ beta,
     float* __restrict__ Aout, float* __restrict__ Bout, int F, int U, int dk_rt, int dv_rt,
     int nframes, int anchors, const uint16_t* __restrict__ tk, const uint16_t* __restrict__ tv,
-    const float* __restrict__ tb, int T, float text_scale, int text_items) {
+    const float* __restrict__ tb, int T, float text_scale, int text_items, int upper) {
   const int dk = DK > 0 ? DK : dk_rt;
   const int dv = DV > 0 ? DV : dv_rt;
   __shared__ __align__(16) unsigned char smem[2 * kStageBytes];
@@ -363,7 +363,10 @@ __global__ __launch_bounds__(512 * (4 / NT), 1) void stats_bf16_kernel(
   };
 
   // results of frame g: rows of A (K tiles) or B (V tiles), columns are key
-  // channels; the accumulators restart at zero.  Non-temporal stores: in the
+  // channels; the accumulators restart at zero.  A is symmetric and the
+  // frame-wise solve reads only its lower 32 x 32 blocks, so unless `upper` is
+  // set (the batched rules read all of A, the statistics tap returns it) the
+  // blocks above the diagonal are not stored.  Non-temporal stores: in the
   // k / v read stream, plain stores of the 128 KB per frame measured about 25%
   // slower on MI355X (a stats-shaped read probe: 0.425 ms without stores,
   // 0.540 ms with plain ones, 0.481 ms with non-temporal ones)
@@ -377,6 +380,7 @@ __global__ __launch_bounds__(512 * (4 / NT), 1) void stats_bf16_kernel(
 #pragma unroll
       for (int j = 0; j < NCT; ++j) {
         if (ct0 + j >= nK) continue;
+        if (isA && !upper && ct0 + j > rt) continue;  // A's upper blocks: not read
         const int col = 32 * (ct0 + j) + (lane & 31);
         if (col >= dk) continue;
 #pragma unroll
@@ -559,20 +563,21 @@ hipError_t launch_stats(const Plan& p, const void* k, const void* v, const float
     const int tiles = (nK + (pad32(p.dv) >> 5)) * nK;  // text-frame tiles per unit
     const int nframes = p.units * p.F;                 // latent frames
     const int P = std::min(nframes, compute_units());
+    const int upper = p.rule != 0 || p.full_stats ? 1 : 0;
     const uint16_t* tk = static_cast<const uint16_t*>(text_k);
     const uint16_t* tv = static_cast<const uint16_t*>(text_v);
     if (p.dk == 128 && p.dv == 128) {  // the text tiles ride in the persistent kernel
       hipLaunchKernelGGL((stats_bf16_kernel<128, 128, 2>), dim3(P), dim3(2 * kStatsThreads), 0, s,
                          static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), beta,
                          w.A, w.B, p.F, p.U, p.dk, p.dv, nframes, p.anchors, tk, tv, text_beta,
-                         p.T, ts, p.units * tiles);
+                         p.T, ts, p.units * tiles, upper);
     } else {
       hipLaunchKernelGGL(stats_text_kernel, dim3(tiles, p.units), dim3(64 * kWavesT), 0, s, tk, tv,
                          text_beta, w.A, w.B, p.F, p.T, p.dk, p.dv, ts);
       hipLaunchKernelGGL((stats_bf16_kernel<0, 0, 4>), dim3(P), dim3(kStatsThreads), 0, s,
                          static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), beta,
                          w.A, w.B, p.F, p.U, p.dk, p.dv, nframes, p.anchors, tk, tv, text_beta,
-                         p.T, ts, 0);
+                         p.T, ts, 0, upper);
     }
   } else {
     hipLaunchKernelGGL(stats_f32_kernel, grid, dim3(kThreads), 0, s,

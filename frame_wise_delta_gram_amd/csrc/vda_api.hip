@@ -68,6 +68,7 @@ int make_plan(const vda_desc_t* d, Plan* p) {
   };
   if (!grid_ok(n, rows_per_chunk, 3 * n + 1)) return VDA_ERR_INVALID_ARG;
   p->decay_ok = grid_ok(d->frames, d->tokens, 4 * n + 1);
+  p->full_stats = false;
 
   p->units = d->units;
   p->F = d->frames;
@@ -367,6 +368,7 @@ int vda_debug_stats(const vda_desc_t* desc, const void* k, const void* v, const 
   if (!A_out || !B_out) return VDA_ERR_INVALID_ARG;
   const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   const WsPtrs w = vda::carve(p, workspace);
+  p.full_stats = true;  // the tap returns whole matrices
   st = vda::run_states(p, k, v, beta, text_k, text_v, text_beta, w, s, 1);
   if (st != VDA_OK) return st;
   const size_t fr = (size_t)p.units * (p.F + 1);

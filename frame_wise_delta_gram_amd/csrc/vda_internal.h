@@ -27,6 +27,8 @@ struct Plan {
   int anchors;    // 1: frames 0 and F - 1 are boundary anchors
   int rule;       // 0: frame-wise delta rule; 1, 2: batched comparison rules
   bool decay_ok;  // the decay path's launch grids fit too
+  bool full_stats;  // store both triangles of every A_t (else the lower 32 x 32 blocks
+                   // of latent frames only: all the frame-wise solve reads)
   size_t off[9];
   size_t total;
 };
