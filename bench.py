@@ -58,11 +58,15 @@ def algorithmic(cfg):
     mat, st = dk * dk * 4, dv * dk * 4               # one transition, one state (fp32)
     gates = u * F * dk * 4 if cfg.alpha_mu is not None else 0
     nmaps = 3 if cfg.alpha_mu is not None else 2     # Mc, Mc^T (+ Mr^T)
-    stats_bytes = th * ((dk + dv) * eb + 4) + u * F * (dk + dv) * dk * 4
+    # A is symmetric: under the frame-wise rule the kernel writes its blocks on
+    # and below the diagonal (all the solve reads); the batched rules read all of A
+    nkb = -(-dk // 32)
+    a_frac = 1.0 if cfg.rule != 0 else nkb * (nkb + 1) / 2 / (nkb * nkb)
+    stats_bytes = th * ((dk + dv) * eb + 4) + u * F * (a_frac * dk + dv) * dk * 4
     text_bytes = tt * ((dk + dv) * eb + 4) + u * (dk + dv) * dk * 4
     readout_bytes = (th * (dk + 2 * dv) * eb                           # q, gate read; out written
                      + u * n * 2 * st + dv * 4 + gates)                 # two states per chunk
-    solve_bytes = 2 * u * (F + 1) * mat                                 # A in, M out
+    solve_bytes = (a_frac + 1) * u * (F + 1) * mat                     # A in, M out
     compose_bytes = (u * (F + 1) * (mat + st) + gates                  # M, B (and gates) in
                      + u * n * (nmaps * mat + 2 * st)                   # chunk maps out
                      + u * 2 * st)                                      # the two seed copies

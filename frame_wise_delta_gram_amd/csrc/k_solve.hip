@@ -117,9 +117,19 @@ __global__ __launch_bounds__(256, 3) void solve_kernel(const float* __restrict__
   const int nb = Dk >> 5;
   auto G = [&](int i, int j) { return Gs + (i * (i + 1) / 2 + j) * kBlk; };
 
-  {  // G = I + A (identity on the padding too), lower-triangle blocks
-    MatRegs m;
-    mat_load(m, A + ((size_t)u * Fp1 + fi) * dk * dk, dk, dk, dk);
+  {  // G = I + A (identity on the padding too), lower-triangle blocks only (the
+     // statistics may leave the blocks above the diagonal unwritten)
+    const float* Af = A + ((size_t)u * Fp1 + fi) * dk * dk;
+    const f32x4_t z = {0.0f, 0.0f, 0.0f, 0.0f};
+    f32x4_t m[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int id = t + 256 * i;
+      const int r = id >> 5;
+      const int c = (id & 31) << 2;
+      const bool ok = r < dk && c < dk && (c >> 5) <= (r >> 5);
+      m[i] = ok ? *reinterpret_cast<const f32x4_t*>(Af + (size_t)r * dk + c) : z;
+    }
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int id = t + 256 * i;
@@ -129,7 +139,7 @@ __global__ __launch_bounds__(256, 3) void solve_kernel(const float* __restrict__
       if (r < Dk && c < Dk && bj <= bi) {
         float* dst = G(bi, bj) + (r & 31) * SG + (c & 31);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) dst[e] = m.v[i][e] + (r == c + e ? 1.0f : 0.0f);
+        for (int e = 0; e < 4; ++e) dst[e] = m[i][e] + (r == c + e ? 1.0f : 0.0f);
       }
     }
     __syncthreads();
