@@ -457,12 +457,13 @@ def state_growth(cfg, d):
 def time_steps(cfg, d, steps, warmup):
     """Run the forward pass (vda_forward_timed; decay gates when d holds them)
     on the current stream: `warmup` untimed steps, `steps` timed steps that
-    record only the events around the two HBM-bound kernels (statistics and
-    readout: each stream marker between kernels adds a few microseconds), then
-    `steps` more steps with all six stage events for the per-stage breakdown.
-    Returns (seconds for the timed steps, dict of average ms: per stage from
-    the breakdown pass, "timed_stats" / "timed_readout" from the timed steps,
-    and the median / minimum of the breakdown pass's per-step totals)."""
+    record only the two events around the readout, the dominant kernel (each
+    stream marker between kernels adds a few microseconds), then `steps` more
+    steps with all six stage events for the per-stage breakdown.  Returns
+    (seconds for the timed steps, dict of average ms: per stage from the
+    breakdown pass, "timed_readout" from the timed steps, "timed_stats" from
+    the breakdown pass, and the median / minimum of the breakdown pass's
+    per-step totals)."""
     import torch
     import frame_wise_delta_gram_amd as vda
 
@@ -496,8 +497,8 @@ def time_steps(cfg, d, steps, warmup):
             raise RuntimeError("hipEventElapsedTime failed")
         return ms.value
 
-    # events 0 / 1 bracket the statistics kernels, 4 / 5 the readout
-    timed_row = lambda i: [e if j in (0, 1, 4, 5) else None for j, e in enumerate(events[i])]
+    # events 4 / 5 bracket the readout
+    timed_row = lambda i: [e if j in (4, 5) else None for j, e in enumerate(events[i])]
     log(f"[bench] {cfg.name}: warmup {warmup}")
     for i in range(warmup):
         vda.vda_forward_timed(*fw, timed_row(i % len(events)), stream=stream)
@@ -508,8 +509,7 @@ def time_steps(cfg, d, steps, warmup):
         vda.vda_forward_timed(*fw, timed_row(i), stream=stream)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    avg = {"timed_stats": sum(elapsed_ms(events[i], 0, 1) for i in range(steps)) / steps,
-           "timed_readout": sum(elapsed_ms(events[i], 4, 5) for i in range(steps)) / steps}
+    avg = {"timed_readout": sum(elapsed_ms(events[i], 4, 5) for i in range(steps)) / steps}
 
     log(f"[bench] {cfg.name}: per-stage breakdown over {steps} more steps")
     for i in range(steps):
@@ -522,6 +522,7 @@ def time_steps(cfg, d, steps, warmup):
             hip.hipEventDestroy(ctypes.c_void_p(e))
     per_step = sorted(sum(stage_ms[s][i] for s in STAGES) for i in range(steps))
     avg.update({s: sum(v) / len(v) for s, v in stage_ms.items()})
+    avg["timed_stats"] = avg["stats"]
     avg["step_events_median"] = per_step[len(per_step) // 2]
     avg["step_events_min"] = per_step[0]
     return elapsed, avg
@@ -535,7 +536,8 @@ def split_steps(avg_ms):
 
 def roofline_of(cfg, avg_ms):
     """Roofline of the dominant HBM-bound kernel (statistics or readout), with
-    its average launch duration from the events of the timed steps."""
+    its average launch duration from events (the readout's recorded in the
+    timed steps, the statistics' in the breakdown pass)."""
     alg = algorithmic(cfg)
     dominant = max(("stats", "readout"), key=lambda s: avg_ms["timed_" + s])
     ms = avg_ms["timed_" + dominant]
