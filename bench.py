@@ -580,7 +580,7 @@ def main():
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the VDA forward shards by head with no "
-              "communication inside the op, and this build runs on a single MI355X. "
+              "communication inside the op, and this benchmark times a single MI355X. "
               "Run it with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
