@@ -139,7 +139,7 @@ KERNELS = ("stats_text", "stats", "solve", "compose", "scan", "readout")  # laun
 PREP_COMMAND = ("rocprofv3 {pmc} -d DIR/{sub} -o p --output-format csv -- python bench.py "
                 "--steps 1 --warmup 0 --cpu-seconds 0 --decay-steps 0 --batched-steps 0 "
                 "--prep-steps 5")
-PREP_KERNELS = ("prep_q", "prep_conv_k", "prep_conv_v")
+PREP_KERNELS = ("prep",)  # one launch: the K and V sweeps, then the Q pass
 KERNEL_NAMES = {"stats_bf16_kernel": "stats", "stats_f32_kernel": "stats",
                 "stats_text_kernel": "stats_text",
                 "readout_bf16_kernel": "readout", "readout_f32_kernel": "readout",
@@ -153,9 +153,7 @@ def short_kernel_name(full):
     m = re.search(r"vda::\(anonymous namespace\)::(\w+)", full)
     if m:
         if m.group(1) == "prep_conv_kernel":
-            return "prep_conv_k" if re.search(r"prep_conv_kernel<[^,]+, true>", full) else "prep_conv_v"
-        if m.group(1) == "prep_q_kernel":
-            return "prep_q"
+            return "prep"
         return KERNEL_NAMES.get(m.group(1), m.group(1))
     return "copy" if "add" in full.lower() else None
 
@@ -173,10 +171,9 @@ def summarize_prep(prep_dir):
     known = {"FETCH_SIZE": 2 * copy_bytes, "WRITE_SIZE": copy_bytes}
     eb = 2
     rows = cfg.batch * cfg.frames * cfg.tokens * cfg.heads
-    alg = {"prep_q": 2 * eb * rows * cfg.d_k,
-           "prep_conv_k": 2 * eb * rows * cfg.d_k + cfg.heads * cfg.d_k * 120,
-           "prep_conv_v": 2 * eb * rows * cfg.d_v + cfg.heads * cfg.d_v * 120}
-    flops = {"prep_q": 0, "prep_conv_k": 60 * rows * cfg.d_k, "prep_conv_v": 60 * rows * cfg.d_v}
+    # q, k, v read and written once; the K and V filters (30 fp32 taps per channel)
+    alg = {"prep": 2 * eb * rows * (2 * cfg.d_k + cfg.d_v) + cfg.heads * (cfg.d_k + cfg.d_v) * 120}
+    flops = {"prep": 60 * rows * (cfg.d_k + cfg.d_v)}
     per = {}
     for ctr in ("FETCH_SIZE", "WRITE_SIZE"):
         path = os.path.join(prep_dir, ctr, "p_counter_collection.csv")

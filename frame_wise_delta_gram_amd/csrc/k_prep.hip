@@ -25,6 +25,11 @@
 // lanes, scaling, one 256-byte row per position.  The kernel does about 30
 // fp32 FMA per output element against 4 bytes (bf16 in + out) of HBM traffic,
 // so it is bound by the vector ALUs rather than by HBM.
+//
+// One launch does all three tensors: the K sweeps and the V sweeps (each XCD
+// takes a range of K sweeps, then the same range of V) and, as its last
+// workgroups, the bandwidth-bound Q pass, which fills the CUs that the sweeps'
+// last round leaves idle.
 #include <type_traits>
 
 #include "vda_device.h"
@@ -39,6 +44,7 @@ constexpr int kHR = kTR + 4;      // halo tile rows
 constexpr int kHC = kTC + 4;      // halo tile columns
 constexpr int kPrepThreads = 1024;
 constexpr int kCols = 4;          // output columns per wave
+constexpr unsigned kQBlocks = 1024;  // workgroups of the Q pass (16 waves each)
 
 // 16-byte pieces of a tensor element type: 8 bf16 or 4 fp32 channels
 template <typename T>
@@ -74,10 +80,33 @@ __device__ __forceinline__ float silu(float x) {
   return x * __builtin_amdgcn_rcpf(1.0f + __expf(-x));
 }
 
+// Value of lane ^ 32 and of lane ^ 16, by gfx950's row-swap permutes (VALU
+// instructions, no LDS round trip).  permlane32_swap(x, x) returns
+// {[x_lo, x_lo], [x_hi, x_hi]} (halves of 32 lanes), permlane16_swap(x, x)
+// returns {rows [x0, x0, x2, x2], rows [x1, x1, x3, x3]} (rows of 16 lanes).
+__device__ __forceinline__ float lane_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return __uint_as_float(lane_id() < 32 ? r[1] : r[0]);
+}
+__device__ __forceinline__ float lane_xor16(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return __uint_as_float((lane_id() & 16) ? r[0] : r[1]);
+}
+// x plus the value of a lane in the other half of its quad, 8-lane or 16-lane
+// group (DPP: quad_perm [1,0,3,2], quad_perm [2,3,0,1], row_half_mirror,
+// row_mirror); four steps leave the 16-lane sum in every lane of a row.
+template <int CTRL>
+__device__ __forceinline__ float dpp_add(float x) {
+  return x + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
 // Sums over the wave's 64 lanes of 4 values per lane at once, as a halving
 // butterfly: after the exchanges across lane bits 5 and 4 each lane holds one
-// partial sum, of value (lane >> 4) & 3, which lane bits 3..0 complete.
-// 6 lane exchanges instead of 24.  Returns the sum of value (lane >> 4) & 3.
+// partial sum, of value (lane >> 4) & 3, which the four in-row steps complete.
+// 6 lane exchanges instead of 24, all on the vector ALUs.  Returns the sum of
+// value (lane >> 4) & 3.
 __device__ __forceinline__ float wave_sum4(const float (&v)[4]) {
   const int lane = lane_id();
   const bool h5 = lane & 32, h4 = lane & 16;
@@ -86,26 +115,103 @@ __device__ __forceinline__ float wave_sum4(const float (&v)[4]) {
   for (int i = 0; i < 2; ++i) {
     const float keep = h5 ? v[i + 2] : v[i];
     const float send = h5 ? v[i] : v[i + 2];
-    a[i] = keep + __shfl_xor(send, 32);
+    a[i] = keep + lane_xor32(send);
   }
-  float c = (h4 ? a[1] : a[0]) + __shfl_xor(h4 ? a[0] : a[1], 16);
-#pragma unroll
-  for (int m = 8; m >= 1; m >>= 1) c += __shfl_xor(c, m);
+  float c = (h4 ? a[1] : a[0]) + lane_xor16(h4 ? a[0] : a[1]);
+  c = dpp_add<0xB1>(c);
+  c = dpp_add<0x4E>(c);
+  c = dpp_add<0x141>(c);
+  c = dpp_add<0x140>(c);
   return c;
 }
 
-template <typename T, bool NORM>
+// Q' = L2(Q) with the layout conversion: G = d / EPP lanes per (token, head)
+// row, rows taken in input order (contiguous reads), each written as one
+// contiguous row of its unit.  Wave `wave` of `nwaves` takes every nwaves-th
+// group of 64 / G rows.
+template <typename T>
+__device__ __forceinline__ void q_rows(const T* __restrict__ x, T* __restrict__ y, long rows, int F,
+                                       int U, int H, int d, float eps, long wave, long nwaves) {
+  constexpr int EPP = Piece<T>::kElems;
+  constexpr int G = 128 / EPP;  // lanes per row (some idle when d < 128)
+  const int lane = threadIdx.x & 63;
+  const int sub = lane % G;
+  const int rows_per_wave = 64 / G;
+  const bool act = sub * EPP < d;
+  for (long r0 = wave * rows_per_wave; r0 < rows; r0 += nwaves * rows_per_wave) {
+    const long r = r0 + lane / G;  // (b, t, p, h) row in input order
+    const bool ok = r < rows && act;
+    u32x4_t raw = ok ? *reinterpret_cast<const u32x4_t*>(x + r * d + sub * EPP)
+                     : u32x4_t{0u, 0u, 0u, 0u};
+    float v[EPP];
+    Piece<T>::to_f32(raw, v);
+    float ss = 0.0f;
+#pragma unroll
+    for (int e = 0; e < EPP; ++e) ss = fmaf(v[e], v[e], ss);
+#pragma unroll
+    for (int m = G / 2; m >= 1; m >>= 1) ss += __shfl_xor(ss, m);
+    const float inv = 1.0f / fmaxf(sqrtf(ss), eps);
+    if (!ok) continue;
+    const long h = r % H;
+    const long tp = r / H;  // (b F + t) U + p
+    const long p = tp % U;
+    const long bt = tp / U;  // b F + t
+    const long t = bt % F;
+    const long b = bt / F;
+    T* dst = y + ((((b * H + h) * F + t) * U + p) * d + sub * EPP);
+#pragma unroll
+    for (int e = 0; e < EPP; e += 2) store2(dst + e, v[e] * inv, v[e + 1] * inv);
+  }
+}
+
+// One tensor of the convolution: input, spatial taps [head][channel][25],
+// temporal taps [head][channel][5], output, channel count.
+template <typename T>
+struct ConvSide {
+  const T* x;
+  const float* ws;
+  const float* wt;
+  T* y;
+  int d;
+};
+
+// K (L2 normalised) and V in one launch, so that the last, partial round of
+// (unit, tile) sweeps is shared by the two tensors.  XCD x takes the sweeps
+// x * per .. x * per + per - 1 of K, then the same sweeps of V (workgroup L
+// runs on XCD L % 8 as the L / 8-th of its queue), so the sweeps running side
+// by side on an XCD are neighbouring tiles of one tensor at the same pace and
+// share their halo reads in its L2.
+// The Q rows follow as the last qblocks workgroups of the launch: they are
+// dispatched once every convolution sweep has started, onto the CUs that the
+// sweeps' last, partial round leaves free, so the bandwidth-bound Q pass runs
+// beside the ALU-bound tail of the convolution instead of after it.
+template <typename T>
 __global__ __launch_bounds__(kPrepThreads, 1) void prep_conv_kernel(
-    const T* __restrict__ x, const float* __restrict__ ws, const float* __restrict__ wt,
-    T* __restrict__ y, int F, int Hl, int Wl, int H, int d, int tiles_r, int tiles_c, int units,
-    unsigned per, float eps) {
+    ConvSide<T> ks, ConvSide<T> vs, int F, int Hl, int Wl, int H, int tiles_r, int tiles_c,
+    int units, unsigned per, float eps, const T* __restrict__ qx, T* __restrict__ qy, long qrows,
+    int dq, unsigned qblocks) {
   __shared__ __align__(16) float Xs[kHR * kHC * 128];  // one frame's halo tile, [pos][channel]
   __shared__ __align__(16) float Ws[25 * 128];          // spatial taps, [tap][channel]
   constexpr int EPP = Piece<T>::kElems;
   constexpr int kIter = (kHR * kHC * (128 / EPP) + kPrepThreads - 1) / kPrepThreads;
+  constexpr int kWaves = kPrepThreads / 64;
+  if (blockIdx.x >= 2 * kXcds * per) {
+    const unsigned qb = blockIdx.x - 2 * kXcds * per;
+    q_rows(qx, qy, qrows, F, Hl * Wl, H, dq, eps, (long)qb * kWaves + (threadIdx.x >> 6),
+           (long)qblocks * kWaves);
+    return;
+  }
   const unsigned ntiles = (unsigned)tiles_r * tiles_c;
-  const unsigned item = xcd_item(per);
-  if (item >= (unsigned)units * ntiles) return;
+  const unsigned j = blockIdx.x / kXcds;  // position in the XCD's queue
+  const bool norm = j < per;              // K first, then V
+  const unsigned item = (blockIdx.x % kXcds) * per + (norm ? j : j - per);
+  if (j >= 2 * per || item >= (unsigned)units * ntiles) return;
+  const ConvSide<T> side = norm ? ks : vs;
+  const T* __restrict__ x = side.x;
+  const float* __restrict__ ws = side.ws;
+  const float* __restrict__ wt = side.wt;
+  T* __restrict__ y = side.y;
+  const int d = side.d;
   const int unit = item / ntiles;
   const int tile = item - unit * ntiles;
   const int b = unit / H;
@@ -239,7 +345,7 @@ __global__ __launch_bounds__(kPrepThreads, 1) void prep_conv_kernel(
         v[0][o] = silu(acc[fin][0][o]);
         v[1][o] = silu(acc[fin][1][o]);
       }
-      if (NORM) {  // sum of squares over the position's d channels (all 64 lanes)
+      if (norm) {  // sum of squares over the position's d channels (all 64 lanes)
         float sq[kCols];
 #pragma unroll
         for (int o = 0; o < kCols; ++o) sq[o] = cact ? v[0][o] * v[0][o] + v[1][o] * v[1][o] : 0.0f;
@@ -275,46 +381,6 @@ __global__ __launch_bounds__(kPrepThreads, 1) void prep_conv_kernel(
   }
 }
 
-// Q' = L2(Q) with the layout conversion: G = d / EPP lanes per (token, head)
-// row, rows taken in input order (contiguous reads), each written as one
-// contiguous row of its unit.
-template <typename T>
-__global__ __launch_bounds__(256) void prep_q_kernel(const T* __restrict__ x, T* __restrict__ y,
-                                                     long rows, int F, int U, int H, int d,
-                                                     float eps) {
-  constexpr int EPP = Piece<T>::kElems;
-  constexpr int G = 128 / EPP;  // lanes per row (some idle when d < 128)
-  const int lane = threadIdx.x & 63;
-  const int sub = lane % G;
-  const int rows_per_wave = 64 / G;
-  const long wave = ((long)blockIdx.x * blockDim.x + threadIdx.x) / 64;
-  const long nwaves = (long)gridDim.x * blockDim.x / 64;
-  const bool act = sub * EPP < d;
-  for (long r0 = wave * rows_per_wave; r0 < rows; r0 += nwaves * rows_per_wave) {
-    const long r = r0 + lane / G;  // (b, t, p, h) row in input order
-    const bool ok = r < rows && act;
-    u32x4_t raw = ok ? *reinterpret_cast<const u32x4_t*>(x + r * d + sub * EPP)
-                     : u32x4_t{0u, 0u, 0u, 0u};
-    float v[EPP];
-    Piece<T>::to_f32(raw, v);
-    float ss = 0.0f;
-#pragma unroll
-    for (int e = 0; e < EPP; ++e) ss = fmaf(v[e], v[e], ss);
-#pragma unroll
-    for (int m = G / 2; m >= 1; m >>= 1) ss += __shfl_xor(ss, m);
-    const float inv = 1.0f / fmaxf(sqrtf(ss), eps);
-    if (!ok) continue;
-    const long h = r % H;
-    const long tp = r / H;  // (b F + t) U + p
-    const long p = tp % U;
-    const long bt = tp / U;  // b F + t
-    const long t = bt % F;
-    const long b = bt / F;
-    T* dst = y + ((((b * H + h) * F + t) * U + p) * d + sub * EPP);
-#pragma unroll
-    for (int e = 0; e < EPP; e += 2) store2(dst + e, v[e] * inv, v[e + 1] * inv);
-  }
-}
 
 template <typename T>
 hipError_t launch_prep_typed(const PrepPlan& p, const void* q, const void* k, const void* v,
@@ -322,16 +388,13 @@ hipError_t launch_prep_typed(const PrepPlan& p, const void* q, const void* k, co
                              const float* wv_t, void* qo, void* ko, void* vo, hipStream_t s) {
   const long rows = (long)p.batch * p.F * p.U * p.H;
   if (rows > 0) {
-    hipLaunchKernelGGL(prep_q_kernel<T>, dim3(2048), dim3(256), 0, s, static_cast<const T*>(q),
-                       static_cast<T*>(qo), rows, p.F, p.U, p.H, p.dk, p.eps);
-    const unsigned items = (unsigned)(p.batch * p.H) * p.tiles_r * p.tiles_c;
-    const unsigned per = xcd_per(items);
-    hipLaunchKernelGGL((prep_conv_kernel<T, true>), dim3(kXcds * per), dim3(kPrepThreads), 0, s,
-                       static_cast<const T*>(k), wk_s, wk_t, static_cast<T*>(ko), p.F, p.Hl,
-                       p.Wl, p.H, p.dk, p.tiles_r, p.tiles_c, p.batch * p.H, per, p.eps);
-    hipLaunchKernelGGL((prep_conv_kernel<T, false>), dim3(kXcds * per), dim3(kPrepThreads), 0,
-                       s, static_cast<const T*>(v), wv_s, wv_t, static_cast<T*>(vo), p.F, p.Hl,
-                       p.Wl, p.H, p.dv, p.tiles_r, p.tiles_c, p.batch * p.H, per, p.eps);
+    const unsigned per = xcd_per((unsigned)(p.batch * p.H) * p.tiles_r * p.tiles_c);
+    const ConvSide<T> ks{static_cast<const T*>(k), wk_s, wk_t, static_cast<T*>(ko), p.dk};
+    const ConvSide<T> vs{static_cast<const T*>(v), wv_s, wv_t, static_cast<T*>(vo), p.dv};
+    const unsigned qblocks = kQBlocks;
+    hipLaunchKernelGGL(prep_conv_kernel<T>, dim3(2 * kXcds * per + qblocks), dim3(kPrepThreads), 0,
+                       s, ks, vs, p.F, p.Hl, p.Wl, p.H, p.tiles_r, p.tiles_c, p.batch * p.H, per,
+                       p.eps, static_cast<const T*>(q), static_cast<T*>(qo), rows, p.dk, qblocks);
   }
   return hipGetLastError();
 }

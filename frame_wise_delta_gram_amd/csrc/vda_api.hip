@@ -296,8 +296,10 @@ int make_prep_plan(const vda_prep_desc_t* d, PrepPlan* p) {
   p->eps = d->eps;
   p->tiles_r = (d->height + 7) / 8;  // 8 x 8 output tiles of the convolution
   p->tiles_c = (d->width + 7) / 8;
-  // the convolution's 1-D grid: fewer than 2^22 workgroups of 512 threads
-  if (!mul_ok(units, (int64_t)p->tiles_r * p->tiles_c, &x) || x >= (INT64_C(1) << 22))
+  // the feature map's 1-D grid (a K and a V workgroup per unit and tile, each
+  // count rounded up to a multiple of 8, then 1024 workgroups of the Q pass):
+  // fewer than 2^22 workgroups of 1024 threads
+  if (!mul_ok(units, (int64_t)p->tiles_r * p->tiles_c, &x) || x >= (INT64_C(1) << 21) - 1024)
     return VDA_ERR_INVALID_ARG;
   return VDA_OK;
 }

@@ -202,7 +202,9 @@ typedef struct vda_prep_desc {
   int32_t heads;  /* >= 0; batch x heads <= 65535 */
   int32_t frames; /* 0..2^20 */
   int32_t height; /* latent rows H_l >= 0 */
-  int32_t width;  /* latent columns W_l >= 0; height x width <= 4194303 */
+  int32_t width;  /* latent columns W_l >= 0; height x width <= 4194303, height x
+                     width x heads x 512 <= 2^31 - 1, and batch x heads x
+                     ceil(height / 8) x ceil(width / 8) < 2^21 - 1024 */
   int32_t d_k;    /* channels of q and k: multiple of 16, 16..128 */
   int32_t d_v;    /* channels of v: multiple of 16, 16..128 */
   float eps;      /* L2 normalisation floor: finite, > 0 */

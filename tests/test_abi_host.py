@@ -68,6 +68,11 @@ def prep_desc(**kw):
     (dict(batch=300, heads=300), vda.VDA_ERR_INVALID_ARG),
     (dict(height=2048, width=2048), vda.VDA_ERR_INVALID_ARG),
     (dict(frames=(1 << 20) + 1), vda.VDA_ERR_INVALID_ARG),
+    # the convolution grid: a K and a V workgroup per (unit, 8 x 8 tile) must
+    # stay under 2^22 workgroups with the Q pass's 1024 (2,096,000 sweeps pass,
+    # 2,097,000 do not)
+    (dict(batch=1000, heads=1, height=8, width=8 * 2096), vda.VDA_OK),
+    (dict(batch=1000, heads=1, height=8, width=8 * 2097), vda.VDA_ERR_INVALID_ARG),
     (dict(batch=0), vda.VDA_OK),
     (dict(height=0), vda.VDA_OK),
 ])
