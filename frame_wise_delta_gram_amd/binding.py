@@ -274,6 +274,8 @@ def desc_from_tensors(q, k, v, text_k, chunk=5, radius=1, eps=1e-6, seed_mode=0,
     import torch
     units, F, U, dk = k.shape
     dv = v.shape[-1]
+    if text_k is not None and (not isinstance(text_k, torch.Tensor) or text_k.dim() != 3):
+        raise TypeError("text_k: expected a 3-d torch tensor [units, T, d_k] or None")
     T = text_k.shape[1] if text_k is not None else 0
     if k.dtype == torch.bfloat16:
         dt = VDA_DTYPE_BF16
@@ -284,13 +286,22 @@ def desc_from_tensors(q, k, v, text_k, chunk=5, radius=1, eps=1e-6, seed_mode=0,
     return make_desc(units, F, U, T, dk, dv, chunk, radius, eps, seed_mode, dt, anchors, rule)
 
 
-def _check_tensor(name, x, dtype, shape):
+def _check_tensor(name, x, dtype, shape, device=None):
+    """Raise TypeError / ValueError unless x is a torch tensor of this dtype and
+    shape that is contiguous and on the GPU (on `device` when given); empty
+    tensors are accepted wherever they live (no pointer of theirs is used)."""
+    import torch
+    if not isinstance(x, torch.Tensor):
+        raise TypeError("%s: expected a torch tensor, got %s" % (name, type(x).__name__))
     if x.dtype != dtype:
         raise TypeError("%s: expected %s, got %s" % (name, dtype, x.dtype))
     if tuple(x.shape) != tuple(shape):
         raise ValueError("%s: expected shape %s, got %s" % (name, tuple(shape), tuple(x.shape)))
-    if x.numel() > 0 and (not x.is_cuda or not x.is_contiguous()):
-        raise ValueError("%s must be a contiguous GPU tensor" % name)
+    if x.numel() > 0:
+        if not x.is_cuda or not x.is_contiguous():
+            raise ValueError("%s must be a contiguous GPU tensor" % name)
+        if device is not None and x.device != device:
+            raise ValueError("%s is on %s, the features on %s" % (name, x.device, device))
 
 
 def forward(q, k, v, beta, gate, text_k, text_v, text_beta, rms_weight, chunk=5, radius=1,
@@ -300,32 +311,55 @@ def forward(q, k, v, beta, gate, text_k, text_v, text_beta, rms_weight, chunk=5,
 
     Shapes: q, k [units, F, U, d_k]; v, gate [units, F, U, d_v]; beta [units, F, U]
     (float32); text_k [units, T, d_k]; text_v [units, T, d_v]; text_beta
-    [units, T] (float32); rms_weight [d_v] (float32); alpha (optional decay
-    gates) [units, F, d_k] (float32); anchors: boundary anchors (frames 0 and
-    F - 1 out of the linear states, their rows zero); rule: 0 the frame-wise
-    delta rule, 1 / 2 the batched comparison rules (no decay).  Returns out
-    [units, F, U, d_v] in the features' dtype.
+    [units, T] (float32), all three None for no text (T = 0); rms_weight [d_v]
+    (float32); alpha (optional decay gates) [units, F, d_k] (float32); anchors:
+    boundary anchors (frames 0 and F - 1 out of the linear states, their rows
+    zero); rule: 0 the frame-wise delta rule, 1 / 2 the batched comparison rules
+    (no decay).  A caller-supplied `out` must be [units, F, U, d_v] in the
+    features' dtype, a caller-supplied workspace a contiguous uint8 tensor on the
+    features' GPU.  Every tensor is checked (dtype, shape, device, contiguity)
+    before anything is enqueued: a mismatch raises TypeError or ValueError.
+    Returns out [units, F, U, d_v] in the features' dtype.
     """
     import torch
+    if not isinstance(k, torch.Tensor) or k.dim() != 4:
+        raise TypeError("k: expected a 4-d torch tensor [units, F, U, d_k]")
+    if not isinstance(v, torch.Tensor) or v.dim() != 4:
+        raise TypeError("v: expected a 4-d torch tensor [units, F, U, d_v]")
+    if (text_k is None) != (text_v is None) or (text_k is None) != (text_beta is None):
+        raise ValueError("text_k, text_v and text_beta are given together or all None")
     desc = desc_from_tensors(q, k, v, text_k, chunk, radius, eps, seed_mode, anchors, rule)
     units, F, U, dk = k.shape
     dv = v.shape[-1]
     T = desc.text_tokens
     fdt = k.dtype
-    for name, x, shp in (("q", q, (units, F, U, dk)), ("v", v, (units, F, U, dv)),
-                         ("gate", gate, (units, F, U, dv)), ("text_k", text_k, (units, T, dk)),
-                         ("text_v", text_v, (units, T, dv))):
-        _check_tensor(name, x, fdt, shp)
-    _check_tensor("beta", beta, torch.float32, (units, F, U))
-    _check_tensor("text_beta", text_beta, torch.float32, (units, T))
-    _check_tensor("rms_weight", rms_weight, torch.float32, (dv,))
+    dev = k.device
+    checks = [("k", k, fdt, (units, F, U, dk)), ("q", q, fdt, (units, F, U, dk)),
+              ("v", v, fdt, (units, F, U, dv)), ("gate", gate, fdt, (units, F, U, dv)),
+              ("beta", beta, torch.float32, (units, F, U))]
+    if text_k is not None:
+        checks += [("text_k", text_k, fdt, (units, T, dk)), ("text_v", text_v, fdt, (units, T, dv)),
+                   ("text_beta", text_beta, torch.float32, (units, T))]
     if alpha is not None:
-        _check_tensor("alpha", alpha, torch.float32, (units, F, dk))
-    if out is None:
-        out = torch.empty((units, F, U, dv), dtype=fdt, device=k.device)
+        checks.append(("alpha", alpha, torch.float32, (units, F, dk)))
+    if out is not None:
+        checks.append(("out", out, fdt, (units, F, U, dv)))
+    for name, x, dt, shp in checks:
+        _check_tensor(name, x, dt, shp, dev)
+    # the RMSNorm weight is read only when there are rows to write
+    _check_tensor("rms_weight", rms_weight if units * F * U > 0 else rms_weight[:0],
+                  torch.float32, (dv,) if units * F * U > 0 else (0,), dev)
     nbytes = vda_workspace_bytes(desc)
+    if workspace is not None:
+        if not isinstance(workspace, torch.Tensor) or workspace.dtype != torch.uint8:
+            raise TypeError("workspace: expected a torch.uint8 tensor")
+        if nbytes > 0 and (not workspace.is_cuda or workspace.device != dev
+                           or not workspace.is_contiguous()):
+            raise ValueError("workspace must be a contiguous uint8 tensor on %s" % dev)
+    if out is None:
+        out = torch.empty((units, F, U, dv), dtype=fdt, device=dev)
     if workspace is None:
-        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=k.device)
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
     if alpha is None:
         vda_forward(desc, q, k, v, beta, gate, text_k, text_v, text_beta, rms_weight, out,
                     workspace, stream=stream)

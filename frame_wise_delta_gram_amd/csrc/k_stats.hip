@@ -1,13 +1,14 @@
 // Frame statistics of Video Delta Attention ("Video DeltaNet", arXiv 2609.20744,
 // Sec. 3.1 Eq. (3b)):
 //   A_t = K_t^T Diag(beta_t) K_t,   B_t = V_t^T Diag(beta_t) K_t
-// for every (unit, frame), with the text tokens as a leading virtual frame
+// for every (unit, frame), with the text tokens as one more frame placed before
+// the first latent frame
 // (Sec. 5, "Chunk-wise scans").  Both statistics come from ONE contraction
 // over the frame's tokens,
 //   [A_t ; B_t] = [X_t | Y_t]^T X_t,   X_t = Diag(sqrt(beta_t)) K_t,
 //                                      Y_t = Diag(sqrt(beta_t)) V_t,
-// so every K/V byte is read from HBM once ("in one pass, sharing input reads
-// and reduction work", Sec. 5).  Splitting beta as sqrt(beta) * sqrt(beta)
+// so every K/V byte is read from HBM once and A_t and B_t come out of the same
+// token reduction (the fused statistics kernel of Sec. 5).  Splitting beta as sqrt(beta) * sqrt(beta)
 // makes the computed A = X^T X positive semidefinite by construction even
 // after X is rounded to bf16, so I + A stays SPD with every eigenvalue >= 1
 // and ||(I + A)^{-1}||_2 <= 1 (Prop. 1) holds for the computed transition too.

@@ -10,7 +10,8 @@
  *   1. frame statistics ([VDN] Sec. 3.1 Eq. (3b)), per latent frame t:
  *        A_t = K_t^T Diag(beta_t) K_t   (d_k x d_k)
  *        B_t = V_t^T Diag(beta_t) K_t   (d_v x d_k)
- *      and the same for the text tokens, which form a leading virtual frame
+ *      and the same for the text tokens, taken as one more frame placed before
+ *      the first latent frame
  *      ([VDN] Sec. 5, "Chunk-wise scans");
  *   2. the frame-wise update ([VDN] Sec. 3.2 Eq. (5), decay alpha = 1):
  *        S_t = (S_{t-1} + B_t) (I + A_t)^{-1}

@@ -4,12 +4,12 @@ TEST INFRASTRUCTURE ONLY: the tests, the smoke check and the bench's
 CPU-baseline leg may import it; the library never calls it and shares no code
 with it.
 
-"Video DeltaNet" (arXiv 2609.20744, cited as [VDN]), Sec. 2.3: the linear
-branch takes Q, K, V from the pretrained QKV projections and applies its own
-feature map -- a separable short convolution to K and V (a depthwise 5 x 5
-spatial filter and a five-tap temporal filter), then SiLU, and L2
-normalisation of Q and K; no rotary embedding.  Sec. 5 ("Fused VDA kernels")
-fuses this with the frame-major layout conversion.
+"Video DeltaNet" (arXiv 2609.20744, cited as [VDN]), Sec. 2.3.  What is
+computed: K and V each pass through a short convolution that is separable
+into a 5 x 5 spatial filter and a 5-tap temporal filter, both depthwise, and
+then through SiLU; Q and the convolved K are then normalised to unit L2 norm.
+The linear branch has no rotary embedding.  Sec. 5 ("Fused VDA kernels")
+puts this map and the change to the frame-major layout into one kernel.
 
 Readings taken where the pages leave a step open (also listed in the design
 notes):

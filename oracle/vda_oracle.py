@@ -32,7 +32,7 @@ design notes):
     bypasses the linear path (zero output), as does every row of a clip with no
     interior frame;
   * text seed, mode 0 (default): S_T is ONE frame-wise update from S = 0 over all
-    T text tokens (the prompt "as a leading virtual frame", [VDN] Sec. 5) and each
+    T text tokens (the prompt treated as one extra frame before frame 0, [VDN] Sec. 5) and each
     scan starts at S_T / 2 ([VDN] Eq. (1b)).  Mode 1: the text tokens are written
     from S = 0 at beta / 2 ("written at beta/2" reading);
   * chunk j = frames [C j, min(C j + C, F)); a short last chunk is allowed;
@@ -251,10 +251,11 @@ def anchored_states(stats, seed, alpha=None, update=None):
     """Both directional scans with boundary anchors, [VDN] Sec. 2.2 and App. A.3.
 
     stats: list of (A_f, B_f) for f = 0..F-1 (the anchors' entries are never
-    read).  The anchors 0 and F - 1 are excluded: P[j] is the forward state
-    through interior frame j, P[0] = seed its virtual initial state; R[j] is
-    the reverse state from the last interior frame F - 2 down to j, R[F - 1] =
-    seed.  Returns dicts P (keys 0..F-2) and R (keys 1..F-1); empty for F < 2.
+    read).  Frames 0 and F - 1 are anchors and enter neither scan.  P[j] holds
+    what the forward scan has absorbed after the interior frames 1..j (P[0] =
+    seed, before any frame); R[j] holds what the reverse scan has absorbed
+    after the interior frames F - 2 down to j (R[F - 1] = seed).  Returns dicts
+    P (keys 0..F-2) and R (keys 1..F-1); empty for F < 2.
     """
     F = len(stats)
     if F < 2:
@@ -331,9 +332,9 @@ def forward_unit(q, k, v, beta, gate, text_k, text_v, text_beta, rms_weight,
     frame; scaled under rule 2), M (per frame: the inherited-state factor,
     Eq. (A.1), or I - A for the batched rules), seed, P, R, and the state St read
     by each frame (F x d_v x d_k; zero where nothing is read).
-    With anchors P and R are (F - 1) x d_v x d_k arrays: P[j] through interior
-    frame j (P[0] = seed), R[j - 1] from the last interior frame down to j
-    (R[F - 2] = seed, the key F - 1 of App. A.3).
+    With anchors P and R are (F - 1) x d_v x d_k arrays: P[j] after the
+    interior frames 1..j (P[0] = seed), R[j - 1] after the interior frames
+    F - 2 down to j (R[F - 2] = seed, index F - 1 in App. A.3's numbering).
     """
     q = np.asarray(q, f64)
     k = np.asarray(k, f64)

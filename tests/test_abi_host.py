@@ -258,3 +258,61 @@ def test_status_strings(lib):
     for s in (0, -1, -2, -3, -4, -5):
         assert vda.vda_status_string(s) and vda.vda_status_string(s) != "unknown status"
     assert vda.vda_status_string(42) == "unknown status"
+
+
+# ---- argument checks of the torch-level forward() (binding.py): every
+# mismatch raises before the library is asked to enqueue anything.  This
+# container has no GPU, so every non-empty tensor here is a CPU tensor, which
+# forward() refuses by name; the empty-problem cases reach the library, which
+# returns without touching a GPU.
+def _tensors(units=2, F=3, U=4, dk=16, dv=16, T=2, dtype=None):
+    import torch
+    dt = dtype or torch.bfloat16
+    return dict(q=torch.zeros(units, F, U, dk, dtype=dt), k=torch.zeros(units, F, U, dk, dtype=dt),
+                v=torch.zeros(units, F, U, dv, dtype=dt), beta=torch.zeros(units, F, U),
+                gate=torch.zeros(units, F, U, dv, dtype=dt),
+                text_k=torch.zeros(units, T, dk, dtype=dt),
+                text_v=torch.zeros(units, T, dv, dtype=dt), text_beta=torch.zeros(units, T),
+                rms_weight=torch.ones(dv))
+
+
+def _call(t, **kw):
+    return vda.forward(t["q"], t["k"], t["v"], t["beta"], t["gate"], t["text_k"], t["text_v"],
+                       t["text_beta"], t["rms_weight"], stream=0, **kw)
+
+
+def test_torch_forward_rejects_host_and_misshapen_tensors(lib):
+    import torch
+    t = _tensors()
+    with pytest.raises(ValueError, match="^k must be a contiguous GPU tensor"):
+        _call(t)  # k is checked first: the descriptor comes from its shape
+    bad = dict(t, k=torch.zeros(2, 3, 4, 16, dtype=torch.float16))
+    with pytest.raises(TypeError):
+        _call(bad)
+    with pytest.raises(TypeError):
+        _call(dict(t, k=[[0.0]]))
+    # an empty problem (units = 0) passes the device checks, so the shape and
+    # dtype checks of everything else are reached
+    e = _tensors(units=0)
+    with pytest.raises(ValueError, match="^q: expected shape"):
+        _call(dict(e, q=torch.zeros(0, 3, 4, 32, dtype=torch.bfloat16)))
+    with pytest.raises(ValueError, match="^out: expected shape"):
+        _call(e, out=torch.zeros(0, 3, 4, 32, dtype=torch.bfloat16))
+    with pytest.raises(TypeError, match="^out: expected"):
+        _call(e, out=torch.zeros(0, 3, 4, 16, dtype=torch.float32))
+    with pytest.raises(TypeError, match="^workspace"):
+        _call(e, workspace=torch.zeros(16, dtype=torch.float32))
+    with pytest.raises(TypeError, match="^alpha"):
+        _call(e, alpha=torch.zeros(0, 3, 16, dtype=torch.float64))
+    with pytest.raises(ValueError, match="^text_v: expected shape"):
+        _call(dict(e, text_v=torch.zeros(0, 5, 16, dtype=torch.bfloat16)))
+    with pytest.raises(ValueError, match="all None"):
+        _call(dict(e, text_v=None))
+    with pytest.raises(TypeError, match="^text_k"):
+        _call(dict(e, text_k=torch.zeros(2, dtype=torch.bfloat16)))
+
+
+def test_torch_forward_accepts_no_text(lib):
+    e = _tensors(units=0)
+    out = _call(dict(e, text_k=None, text_v=None, text_beta=None))
+    assert tuple(out.shape) == (0, 3, 4, 16)
