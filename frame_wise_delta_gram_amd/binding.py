@@ -359,7 +359,7 @@ def forward(q, k, v, beta, gate, text_k, text_v, text_beta, rms_weight, chunk=5,
     if out is None:
         out = torch.empty((units, F, U, dv), dtype=fdt, device=dev)
     if workspace is None:
-        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)  # empty: NULL
     if alpha is None:
         vda_forward(desc, q, k, v, beta, gate, text_k, text_v, text_beta, rms_weight, out,
                     workspace, stream=stream)
