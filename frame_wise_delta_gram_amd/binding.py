@@ -21,10 +21,13 @@ VDA_ERR_BAD_DTYPE = -2
 VDA_ERR_WORKSPACE_TOO_SMALL = -3
 VDA_ERR_MISALIGNED = -4
 VDA_ERR_HIP = -5
+VDA_ERR_SCRATCH_TOO_SMALL = -6
+VDA_NOALLOC_MAX_BYTES = 64 << 20  # the fixed scratch of vda_forward_noalloc
 VDA_DTYPE_F32 = 0
 VDA_DTYPE_BF16 = 1
 
-EXPORTED = ("vda_workspace_bytes", "vda_check_desc", "vda_forward", "vda_forward_timed",
+EXPORTED = ("vda_workspace_bytes", "vda_check_desc", "vda_forward", "vda_forward_noalloc",
+            "vda_forward_timed",
             "vda_forward_decay", "vda_debug_stats", "vda_debug_solve", "vda_debug_chunks",
             "vda_debug_chunks_decay", "vda_debug_states", "vda_debug_states_decay",
             "vda_prep", "vda_prep_check_desc", "vda_status_string")
@@ -84,6 +87,8 @@ def load_library(path: str = LIB_PATH):
     lib.vda_check_desc.restype = ctypes.c_int
     lib.vda_forward.argtypes = [D] + [P] * 11 + [ctypes.c_size_t, P]
     lib.vda_forward.restype = ctypes.c_int
+    lib.vda_forward_noalloc.argtypes = [D] + [P] * 10 + [P]
+    lib.vda_forward_noalloc.restype = ctypes.c_int
     lib.vda_forward_timed.argtypes = [D] + [P] * 12 + [ctypes.c_size_t, P,
                                                       ctypes.POINTER(ctypes.c_void_p), ctypes.c_int]
     lib.vda_forward_timed.restype = ctypes.c_int
@@ -162,6 +167,17 @@ def vda_forward(desc, q, k, v, beta, gate, text_k, text_v, text_beta, rms_weight
         _ptr(text_v), _ptr(text_beta), _ptr(rms_weight), _ptr(out), _ptr(workspace),
         workspace_bytes, _stream(stream))
     _check(st, "vda_forward")
+
+
+def vda_forward_noalloc(desc, q, k, v, beta, gate, text_k, text_v, text_beta, rms_weight, out,
+                        stream=None):
+    """C vda_forward_noalloc: vda_forward in the library's fixed per-GPU scratch
+    (no workspace argument, nothing allocated; problems whose workspace exceeds
+    VDA_NOALLOC_MAX_BYTES are refused)."""
+    st = load_library().vda_forward_noalloc(
+        ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(beta), _ptr(gate), _ptr(text_k),
+        _ptr(text_v), _ptr(text_beta), _ptr(rms_weight), _ptr(out), _stream(stream))
+    _check(st, "vda_forward_noalloc")
 
 
 def vda_forward_timed(desc, q, k, v, beta, alpha, gate, text_k, text_v, text_beta, rms_weight,

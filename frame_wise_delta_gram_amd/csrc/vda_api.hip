@@ -6,6 +6,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "vda_internal.h"
 
 namespace vda {
@@ -125,21 +127,43 @@ WsPtrs carve(const Plan& p, void* ws) {
 
 bool aligned(const void* ptr, size_t a) { return (reinterpret_cast<uintptr_t>(ptr) % a) == 0; }
 
-// Checks shared by every entry point that runs the state pipeline (alpha:
-// optional decay gates).
-int check_state_inputs(const Plan& p, const void* k, const void* v, const float* beta,
-                       const void* tk, const void* tv, const float* tb, const void* ws,
-                       size_t ws_bytes, const float* alpha = nullptr) {
+// Input checks shared by every entry point that runs the state pipeline
+// (alpha: optional decay gates); the workspace is checked separately.
+int check_state_tensors(const Plan& p, const void* k, const void* v, const float* beta,
+                        const void* tk, const void* tv, const float* tb,
+                        const float* alpha = nullptr) {
   const bool video = (size_t)p.units * p.F * p.U > 0;
   const bool text = (size_t)p.units * p.T > 0 && p.F > 0;
   if (video && (!k || !v || !beta)) return VDA_ERR_INVALID_ARG;
   if (text && (!tk || !tv || !tb)) return VDA_ERR_INVALID_ARG;
-  if (p.total > 0 && !ws) return VDA_ERR_INVALID_ARG;
-  if (ws_bytes < p.total) return VDA_ERR_WORKSPACE_TOO_SMALL;
   if (video && (!aligned(k, 16) || !aligned(v, 16) || !aligned(beta, 4))) return VDA_ERR_MISALIGNED;
   if (text && (!aligned(tk, 16) || !aligned(tv, 16) || !aligned(tb, 4))) return VDA_ERR_MISALIGNED;
-  if (ws && !aligned(ws, 256)) return VDA_ERR_MISALIGNED;
   if (alpha && !aligned(alpha, 16)) return VDA_ERR_MISALIGNED;
+  return VDA_OK;
+}
+
+int check_workspace(const Plan& p, const void* ws, size_t ws_bytes) {
+  if (p.total > 0 && !ws) return VDA_ERR_INVALID_ARG;
+  if (ws_bytes < p.total) return VDA_ERR_WORKSPACE_TOO_SMALL;
+  if (ws && !aligned(ws, 256)) return VDA_ERR_MISALIGNED;
+  return VDA_OK;
+}
+
+int check_state_inputs(const Plan& p, const void* k, const void* v, const float* beta,
+                       const void* tk, const void* tv, const float* tb, const void* ws,
+                       size_t ws_bytes, const float* alpha = nullptr) {
+  const int st = check_state_tensors(p, k, v, beta, tk, tv, tb, alpha);
+  return st != VDA_OK ? st : check_workspace(p, ws, ws_bytes);
+}
+
+// The readout's tensors (the forward entry points).
+int check_readout_tensors(const Plan& p, const void* q, const void* gate, const float* rms_weight,
+                          const void* out) {
+  const bool video = (size_t)p.units * p.F * p.U > 0;
+  if (video && (!q || !gate || !out || !rms_weight)) return VDA_ERR_INVALID_ARG;
+  if (video && (!aligned(q, 16) || !aligned(gate, 16) || !aligned(out, 16) ||
+                !aligned(rms_weight, 16)))
+    return VDA_ERR_MISALIGNED;
   return VDA_OK;
 }
 
@@ -166,6 +190,23 @@ int run_states(const Plan& p, const void* k, const void* v, const float* beta, c
   return VDA_OK;
 }
 
+// The forward pass on a checked plan and workspace.
+int launch_forward(const Plan& p, const void* q, const void* k, const void* v, const float* beta,
+                   const float* alpha, const void* gate, const void* text_k, const void* text_v,
+                   const float* text_beta, const float* rms_weight, void* out, void* workspace,
+                   vda_stream_t stream, hipEvent_t const* ev) {
+  const bool video = (size_t)p.units * p.F * p.U > 0;
+  const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const WsPtrs w = carve(p, workspace);
+  int st = run_states(p, k, v, beta, text_k, text_v, text_beta, w, s, 4, alpha, ev);
+  if (st != VDA_OK) return st;
+  if (ev && ev[4] && hipEventRecord(ev[4], s) != hipSuccess) return VDA_ERR_HIP;
+  if (video && launch_readout(p, q, gate, rms_weight, out, w, alpha, s) != hipSuccess)
+    return VDA_ERR_HIP;
+  if (ev && ev[5] && hipEventRecord(ev[5], s) != hipSuccess) return VDA_ERR_HIP;
+  return VDA_OK;
+}
+
 int forward_impl(const vda_desc_t* desc, const void* q, const void* k, const void* v,
                  const float* beta, const float* alpha, const void* gate, const void* text_k,
                  const void* text_v, const float* text_beta, const float* rms_weight, void* out,
@@ -177,20 +218,10 @@ int forward_impl(const vda_desc_t* desc, const void* q, const void* k, const voi
   st = check_state_inputs(p, k, v, beta, text_k, text_v, text_beta, workspace, workspace_bytes,
                           alpha);
   if (st != VDA_OK) return st;
-  const bool video = (size_t)p.units * p.F * p.U > 0;
-  if (video && (!q || !gate || !out || !rms_weight)) return VDA_ERR_INVALID_ARG;
-  if (video && (!aligned(q, 16) || !aligned(gate, 16) || !aligned(out, 16) ||
-                !aligned(rms_weight, 16)))
-    return VDA_ERR_MISALIGNED;
-  const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  const WsPtrs w = carve(p, workspace);
-  st = run_states(p, k, v, beta, text_k, text_v, text_beta, w, s, 4, alpha, ev);
+  st = check_readout_tensors(p, q, gate, rms_weight, out);
   if (st != VDA_OK) return st;
-  if (ev && ev[4] && hipEventRecord(ev[4], s) != hipSuccess) return VDA_ERR_HIP;
-  if (video && launch_readout(p, q, gate, rms_weight, out, w, alpha, s) != hipSuccess)
-    return VDA_ERR_HIP;
-  if (ev && ev[5] && hipEventRecord(ev[5], s) != hipSuccess) return VDA_ERR_HIP;
-  return VDA_OK;
+  return launch_forward(p, q, k, v, beta, alpha, gate, text_k, text_v, text_beta, rms_weight, out,
+                        workspace, stream, ev);
 }
 
 // Extra checks of the decay entry points: the gates are required whenever a
@@ -307,6 +338,46 @@ int make_prep_plan(const vda_prep_desc_t* d, PrepPlan* p) {
 }  // namespace
 }  // namespace vda
 
+namespace vda {
+namespace {
+
+// Workspace of vda_forward_noalloc: a fixed device array in this library's
+// code object, one copy per GPU, held until the process ends.  Its name is
+// only a host-side handle: host code uses the address hipGetSymbolAddress
+// returns for the current device (scratch_ptr below), never the name itself.
+__device__ __align__(256) unsigned char scratch[VDA_NOALLOC_MAX_BYTES];
+
+constexpr int kMaxDevices = 64;
+void* g_scratch[kMaxDevices];  // device address of `scratch`, per device ordinal
+std::mutex g_scratch_mu;
+
+// The device address of `scratch` on the device `stream` belongs to (the
+// current device for the null stream), looked up once per device with that
+// device current.  Returns VDA_ERR_HIP when the device cannot be queried or
+// the lookup fails.
+int scratch_ptr(hipStream_t stream, void** out) {
+  int dev = -1;
+  if (stream ? hipStreamGetDevice(stream, &dev) != hipSuccess : hipGetDevice(&dev) != hipSuccess)
+    return VDA_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return VDA_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    int cur = -1;
+    if (hipGetDevice(&cur) != hipSuccess) return VDA_ERR_HIP;
+    if (cur != dev && hipSetDevice(dev) != hipSuccess) return VDA_ERR_HIP;
+    void* ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (cur != dev && hipSetDevice(cur) != hipSuccess) return VDA_ERR_HIP;
+    if (e != hipSuccess || !ptr) return VDA_ERR_HIP;
+    g_scratch[dev] = ptr;
+  }
+  *out = g_scratch[dev];
+  return VDA_OK;
+}
+
+}  // namespace
+}  // namespace vda
+
 using vda::Plan;
 using vda::WsPtrs;
 
@@ -329,6 +400,28 @@ int vda_forward(const vda_desc_t* desc, const void* q, const void* k, const void
                 size_t workspace_bytes, vda_stream_t stream) {
   return vda::forward_impl(desc, q, k, v, beta, nullptr, gate, text_k, text_v, text_beta,
                            rms_weight, out, workspace, workspace_bytes, stream, nullptr);
+}
+
+int vda_forward_noalloc(const vda_desc_t* desc, const void* q, const void* k, const void* v,
+                        const float* beta, const void* gate, const void* text_k,
+                        const void* text_v, const float* text_beta, const float* rms_weight,
+                        void* out, vda_stream_t stream) {
+  Plan p;
+  int st = vda::make_plan(desc, &p);
+  if (st != VDA_OK) return st;
+  if (p.total > (size_t)VDA_NOALLOC_MAX_BYTES) return VDA_ERR_SCRATCH_TOO_SMALL;
+  st = vda::check_state_tensors(p, k, v, beta, text_k, text_v, text_beta);
+  if (st != VDA_OK) return st;
+  st = vda::check_readout_tensors(p, q, gate, rms_weight, out);
+  if (st != VDA_OK) return st;
+  if (p.total == 0) return VDA_OK;  // an empty problem enqueues nothing
+  void* ws = nullptr;
+  st = vda::scratch_ptr(reinterpret_cast<hipStream_t>(stream), &ws);
+  if (st != VDA_OK) return st;
+  // every workspace section the pipeline reads is written earlier in the same
+  // call (no counters, no accumulation), so the array needs no clearing
+  return vda::launch_forward(p, q, k, v, beta, nullptr, gate, text_k, text_v, text_beta,
+                             rms_weight, out, ws, stream, nullptr);
 }
 
 int vda_forward_timed(const vda_desc_t* desc, const void* q, const void* k, const void* v,
@@ -472,6 +565,8 @@ const char* vda_status_string(int status) {
     case VDA_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
     case VDA_ERR_MISALIGNED: return "misaligned pointer";
     case VDA_ERR_HIP: return "HIP launch or copy failed";
+    case VDA_ERR_SCRATCH_TOO_SMALL:
+      return "problem needs more workspace than vda_forward_noalloc's fixed scratch";
     default: return "unknown status";
   }
 }

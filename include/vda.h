@@ -73,13 +73,15 @@
  * Ownership: the caller owns every buffer.  All pointers are device pointers
  * (HBM), except the descriptor, which is a host pointer read during the call.
  * The library never allocates or frees memory; it writes only `out` (fully
- * overwritten) and the caller's workspace.  Inputs are read-only.
+ * overwritten) and the caller's workspace (vda_forward_noalloc: its own fixed
+ * scratch instead).  Inputs are read-only.
  *
  * Streams: every call only enqueues kernels (and, for the debug taps,
  * device-to-device copies) on `stream`; it never synchronises.  Execution
- * errors surface at the caller's next synchronisation.  The library holds no
- * mutable global state; calls are reentrant.  Calls that share a workspace
- * must be ordered on one stream.
+ * errors surface at the caller's next synchronisation.  Apart from
+ * vda_forward_noalloc's per-GPU scratch (below), the library holds no mutable
+ * global state; calls are reentrant.  Calls that share a workspace must be
+ * ordered on one stream.
  *
  * Errors: functions return VDA_OK (0) or a negative vda_status_t.  Argument
  * checks happen on the host before anything is enqueued, so a failed check
@@ -103,7 +105,8 @@ typedef enum vda_status {
   VDA_ERR_BAD_DTYPE = -2,           /* unsupported in_dtype/out_dtype combination */
   VDA_ERR_WORKSPACE_TOO_SMALL = -3, /* workspace_bytes < vda_workspace_bytes(desc) */
   VDA_ERR_MISALIGNED = -4,          /* a tensor is not 16-byte aligned, workspace not 256-byte */
-  VDA_ERR_HIP = -5                  /* a kernel launch or copy failed (hipGetLastError) */
+  VDA_ERR_HIP = -5,                 /* a kernel launch or copy failed (hipGetLastError) */
+  VDA_ERR_SCRATCH_TOO_SMALL = -6    /* vda_forward_noalloc: workspace > VDA_NOALLOC_MAX_BYTES */
 } vda_status_t;
 
 typedef enum vda_dtype {
@@ -151,6 +154,30 @@ int vda_forward(const vda_desc_t* desc, const void* q, const void* k, const void
                 const float* beta, const void* gate, const void* text_k, const void* text_v,
                 const float* text_beta, const float* rms_weight, void* out, void* workspace,
                 size_t workspace_bytes, vda_stream_t stream);
+
+/* Bytes of the fixed device scratch vda_forward_noalloc works in (64 MiB). */
+#define VDA_NOALLOC_MAX_BYTES (64u << 20)
+
+/* vda_forward for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same pass with the same arguments minus the workspace, computed in a fixed
+ * array of VDA_NOALLOC_MAX_BYTES in the library's own device memory (one copy
+ * per GPU, created with the library's code object on that GPU and held until
+ * the process ends).  The call allocates and frees nothing.  Problems whose
+ * vda_workspace_bytes(desc) exceeds VDA_NOALLOC_MAX_BYTES are refused with
+ * VDA_ERR_SCRATCH_TOO_SMALL before anything is enqueued (the small and tiny
+ * workloads fit; the 768p head share, 420 MB, does not: use vda_forward).  The
+ * first call on a GPU looks up the array's device address with that GPU
+ * current (VDA_ERR_HIP if that fails); later calls reuse it.  The work runs on
+ * the GPU `stream` belongs to.  Every call on one GPU shares that GPU's array,
+ * which keeps the last call's contents; nothing in it needs to start at zero.
+ * Calls that overlap on one GPU (on different streams, or from several host
+ * threads without ordering) race on the array and give undefined results:
+ * order them on one stream.  Results are bit-identical to vda_forward. */
+int vda_forward_noalloc(const vda_desc_t* desc, const void* q, const void* k, const void* v,
+                        const float* beta, const void* gate, const void* text_k,
+                        const void* text_v, const float* text_beta, const float* rms_weight,
+                        void* out, vda_stream_t stream);
 
 /* vda_forward (alpha NULL) or vda_forward_decay (alpha non-NULL) that also
  * records caller-created HIP events (hipEvent_t, cast to void*) on `stream`

@@ -66,6 +66,18 @@ int main(void) {
   d = base();
   CHECK(vda_forward(&d, NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL, 0,
                     NULL) != VDA_OK);
+  /* the allocation-free entry point refuses what its fixed scratch cannot hold
+   * (the 768p head share), and checks pointers first on smaller problems */
+  CHECK(vda_workspace_bytes(&d) > VDA_NOALLOC_MAX_BYTES);
+  CHECK(vda_forward_noalloc(&d, NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL,
+                            NULL) == VDA_ERR_SCRATCH_TOO_SMALL);
+  d.units = 1;
+  d.frames = 10;
+  d.tokens = 256;
+  CHECK(vda_workspace_bytes(&d) <= VDA_NOALLOC_MAX_BYTES);
+  CHECK(vda_forward_noalloc(&d, NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL,
+                            NULL) == VDA_ERR_INVALID_ARG);
+  d = base();
   {
     vda_prep_desc_t p;
     memset(&p, 0, sizeof p);

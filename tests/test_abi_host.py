@@ -255,7 +255,7 @@ def test_forward_decay_argument_errors(lib):
 
 
 def test_status_strings(lib):
-    for s in (0, -1, -2, -3, -4, -5):
+    for s in (0, -1, -2, -3, -4, -5, -6):
         assert vda.vda_status_string(s) and vda.vda_status_string(s) != "unknown status"
     assert vda.vda_status_string(42) == "unknown status"
 
@@ -316,3 +316,39 @@ def test_torch_forward_accepts_no_text(lib):
     e = _tensors(units=0)
     out = _call(dict(e, text_k=None, text_v=None, text_beta=None))
     assert tuple(out.shape) == (0, 3, 4, 16)
+
+
+def call_noalloc(lib, d, **ptrs):
+    names = ["q", "k", "v", "beta", "gate", "text_k", "text_v", "text_beta", "rms_weight", "out"]
+    args = [ptrs.get(n, 4096 * (i + 1)) for i, n in enumerate(names)]
+    return lib.vda_forward_noalloc(ctypes.byref(d), *args, None)
+
+
+def test_noalloc_host_checks(lib):
+    """vda_forward_noalloc refuses, on the host and before any GPU call, every
+    problem whose workspace exceeds its fixed scratch, and checks its pointers
+    like vda_forward (this container has no GPU: any call that got past the
+    checks would report a HIP error)."""
+    assert vda.VDA_NOALLOC_MAX_BYTES == 64 << 20
+    small = desc()
+    assert vda.vda_workspace_bytes(small) <= vda.VDA_NOALLOC_MAX_BYTES
+    # the 768p head share needs 420 MB
+    big = desc(units=16, frames=90, tokens=4032, text_tokens=512, d_k=128, d_v=128)
+    assert vda.vda_workspace_bytes(big) > vda.VDA_NOALLOC_MAX_BYTES
+    assert call_noalloc(lib, big) == vda.VDA_ERR_SCRATCH_TOO_SMALL
+    # the largest problem of a family that fits, and the next one up
+    fits = [f for f in range(1, 200)
+            if vda.vda_workspace_bytes(desc(units=4, frames=f, d_k=128, d_v=128))
+            <= vda.VDA_NOALLOC_MAX_BYTES]
+    f = max(fits)
+    assert f < 199
+    assert call_noalloc(lib, desc(units=4, frames=f + 1, d_k=128, d_v=128)) == \
+        vda.VDA_ERR_SCRATCH_TOO_SMALL
+    assert call_noalloc(lib, small, k=None) == vda.VDA_ERR_INVALID_ARG
+    assert call_noalloc(lib, small, out=None) == vda.VDA_ERR_INVALID_ARG
+    assert call_noalloc(lib, small, q=4096 + 8) == vda.VDA_ERR_MISALIGNED
+    assert call_noalloc(lib, desc(d_k=12)) == vda.VDA_ERR_INVALID_ARG
+    assert lib.vda_forward_noalloc(None, *([None] * 10), None) == vda.VDA_ERR_INVALID_ARG
+    e = desc(units=0)
+    assert lib.vda_forward_noalloc(ctypes.byref(e), *([None] * 10), None) == vda.VDA_OK
+    assert "scratch" in vda.vda_status_string(vda.VDA_ERR_SCRATCH_TOO_SMALL)
