@@ -1,9 +1,9 @@
 #!/usr/bin/env python3
 """Throughput of the VDA forward pass on one MI355X.
 
-One step = one vda_forward call (statistics, Cholesky solve, chunk composition,
-bidirectional boundary scan, fused readout) over the whole workload, inputs
-already resident in HBM.  Default workload: the 768p-shaped one-GPU head share
+One step = one vda_forward call (statistics, symmetric Gauss-Jordan solve, chunk
+composition, bidirectional boundary scan, fused readout) over the whole
+workload, inputs already resident in HBM.  Default workload: the 768p-shaped one-GPU head share
 (16 heads x 90 latent frames x 4032 tokens, d_k = d_v = 128, 512 text tokens,
 bf16 features, fp32 state), synthetic seeded inputs.
 
@@ -12,8 +12,12 @@ Prints ONE JSON line: token-heads/s, the roofline of the dominant kernel
 MFMA fraction the metric asks for, the fp64 CPU oracle timed on a bounded
 sample of the same workload on the host cores, (object "batched_rule") the
 same inputs under SANA-WM's batched comparison rule with the boundary-state
-norms of every rule, and (object "decay") the same workload with channel-wise
-decay gates through vda_forward_decay.
+norms of every rule, (object "decay") the same workload with channel-wise
+decay gates through vda_forward_decay, (object "prep") the feature map on the
+768p head share, and (object "configs") the tiny, small, medium and stress
+workloads, each with its own roofline and oracle baseline (the small ones
+rotate through input copies that do not fit in the MALL together).  The text
+seed follows --seed-mode (default 1: the text written at beta / 2).
 
   python bench.py [--steps K] [--warmup W] [--config 4] [--cpu-seconds S]
   python bench.py --summarize DIR [--config 4]   (profiles/ from rocprofv3 output)
@@ -120,25 +124,25 @@ PROFILE_COMMANDS = {  # CFG: the workload id
     "FETCH_SIZE": "timeout -s KILL 120 rocprofv3 --pmc FETCH_SIZE --kernel-include-regex "
                   "'vda|add' -d DIR/FETCH_SIZE -o p --output-format csv -- python bench.py "
                   "--config CFG --steps 2 --warmup 1 --cpu-seconds 0 --decay-steps 0 "
-                  "--batched-steps 0 --prep-steps 0",
+                  "--batched-steps 0 --prep-steps 0 --other-configs=",
     "WRITE_SIZE": "timeout -s KILL 120 rocprofv3 --pmc WRITE_SIZE --kernel-include-regex "
                   "'vda|add' -d DIR/WRITE_SIZE -o p --output-format csv -- python bench.py "
                   "--config CFG --steps 2 --warmup 1 --cpu-seconds 0 --decay-steps 0 "
-                  "--batched-steps 0 --prep-steps 0",
+                  "--batched-steps 0 --prep-steps 0 --other-configs=",
     "MFMA": "timeout -s KILL 120 rocprofv3 --pmc SQ_INSTS_VALU_MFMA_MOPS_BF16 "
             "SQ_INSTS_VALU_MFMA_MOPS_F32 SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE "
             "--kernel-include-regex vda -d DIR/MFMA -o p --output-format csv -- python bench.py "
             "--config CFG --steps 2 --warmup 1 --cpu-seconds 0 --decay-steps 0 "
-            "--batched-steps 0 --prep-steps 0",
+            "--batched-steps 0 --prep-steps 0 --other-configs=",
     "stats": "rocprofv3 --kernel-trace --stats -d DIR/trace -o vda --output-format csv -- "
              "python bench.py --config CFG --steps 20 --warmup 50 --cpu-seconds 0 "
-             "--decay-steps 0 --batched-steps 0 --prep-steps 0",
+             "--decay-steps 0 --batched-steps 0 --prep-steps 0 --other-configs=",
 }
 TRACE_WARMUP, TRACE_STEPS = 50, 20  # of the kernel-trace command above
 KERNELS = ("stats_text", "stats", "solve", "compose", "scan", "readout")  # launch order
 PREP_COMMAND = ("rocprofv3 {pmc} -d DIR/{sub} -o p --output-format csv -- python bench.py "
                 "--steps 1 --warmup 0 --cpu-seconds 0 --decay-steps 0 --batched-steps 0 "
-                "--prep-steps 5")
+                "--prep-steps 5 --other-configs=")
 PREP_KERNELS = ("prep",)  # one launch: the K and V sweeps, then the Q pass
 KERNEL_NAMES = {"stats_bf16_kernel": "stats", "stats_f32_kernel": "stats",
                 "stats_text_kernel": "stats_text",
@@ -374,7 +378,9 @@ def summarize(prof_dir, cfg_id):
 
 
 def cpu_baseline(d, cfg, budget_s):
-    """The fp64 oracle on whole units of the same inputs until ~budget_s of CPU time."""
+    """The fp64 oracle on whole units of the same inputs until ~budget_s of CPU
+    time (passes over all units are repeated while the budget lasts, so that
+    small workloads are timed over more than one pass)."""
     import numpy as np
     import oracle
     import workloads as W
@@ -383,20 +389,25 @@ def cpu_baseline(d, cfg, budget_s):
     feats = ("q", "k", "v", "gate", "text_k", "text_v")
     done = 0
     elapsed = 0.0
-    for u in range(cfg.units):
-        x = {}
-        for name, t in d.items():
-            a = W.tensor_to_host(t if name == "rms_weight" else t[u:u + 1])
-            x[name] = W.to_f64(a, cfg.dtype) if name in feats else a.astype(np.float64)
-        t0 = time.perf_counter()
-        oracle.forward(x["q"], x["k"], x["v"], x["beta"], x["gate"], x["text_k"], x["text_v"],
-                       x["text_beta"], x["rms_weight"], chunk=cfg.chunk, radius=cfg.radius,
-                       eps=cfg.rms_eps, alpha=x.get("alpha"))
-        elapsed += time.perf_counter() - t0
-        done += 1
-        log(f"[bench] oracle unit {u}: {elapsed:.1f} s total")
-        if elapsed >= budget_s:
-            break
+    passes = 0
+    while elapsed < budget_s:
+        for u in range(cfg.units):
+            x = {}
+            for name, t in d.items():
+                a = W.tensor_to_host(t if name == "rms_weight" else t[u:u + 1])
+                x[name] = W.to_f64(a, cfg.dtype) if name in feats else a.astype(np.float64)
+            t0 = time.perf_counter()
+            oracle.forward(x["q"], x["k"], x["v"], x["beta"], x["gate"], x["text_k"],
+                           x["text_v"], x["text_beta"], x["rms_weight"], chunk=cfg.chunk,
+                           radius=cfg.radius, eps=cfg.rms_eps, alpha=x.get("alpha"),
+                           seed_mode=SEED_MODE)
+            elapsed += time.perf_counter() - t0
+            done += 1
+            if passes == 0:
+                log(f"[bench] oracle unit {u}: {elapsed:.1f} s total")
+            if elapsed >= budget_s:
+                break
+        passes += 1
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     th = done * cfg.frames * cfg.tokens
     model = "unknown"
@@ -410,14 +421,18 @@ def cpu_baseline(d, cfg, budget_s):
         pass
     return {"value": th / elapsed, "unit": "token-heads/s", "cores": threads, "kind": "oracle",
             "cpu_model": model, "affinity_cpus": len(os.sched_getaffinity(0)),
-            "sample": f"{done} of {cfg.units} units of the same inputs (all {cfg.frames} frames "
-                      f"x {cfg.tokens} tokens each), fp64 numpy, {elapsed:.1f} s"}
+            "sample": f"{done} unit passes over {min(done, cfg.units)} of the {cfg.units} units "
+                      f"of the same inputs (all {cfg.frames} frames x {cfg.tokens} tokens each), "
+                      f"fp64 numpy, {elapsed:.2f} s"}
+
+
+SEED_MODE = 1  # the text written into both states at beta / 2 (set from --seed-mode)
 
 
 def make_desc(cfg):
     import frame_wise_delta_gram_amd as vda
     return vda.make_desc(cfg.units, cfg.frames, cfg.tokens, cfg.text_tokens, cfg.d_k, cfg.d_v,
-                         cfg.chunk, cfg.radius, cfg.rms_eps, 0,
+                         cfg.chunk, cfg.radius, cfg.rms_eps, SEED_MODE,
                          vda.VDA_DTYPE_BF16 if cfg.dtype == "bf16" else vda.VDA_DTYPE_F32,
                          int(cfg.anchors), cfg.rule)
 
@@ -456,21 +471,27 @@ def time_steps(cfg, d, steps, warmup):
     on the current stream: `warmup` untimed steps, `steps` timed steps that
     record only the two events around the readout, the dominant kernel (each
     stream marker between kernels adds a few microseconds), then `steps` more
-    steps with all six stage events for the per-stage breakdown.  Returns
-    (seconds for the timed steps, dict of average ms: per stage from the
-    breakdown pass, "timed_readout" from the timed steps, "timed_stats" from
-    the breakdown pass, and the median / minimum of the breakdown pass's
-    per-step totals)."""
+    steps with all six stage events for the per-stage breakdown.  d is one
+    input set, or a list of input sets that the steps take in turn (step i
+    reads copy i mod len(d) and writes its own output: for workloads small
+    enough to stay in the 256 MB MALL, so that every step streams its inputs
+    from HBM).  Returns (seconds for the timed steps, dict of average ms: per
+    stage from the breakdown pass, "timed_readout" from the timed steps,
+    "timed_stats" from the breakdown pass, and the median / minimum of the
+    breakdown pass's per-step totals)."""
     import torch
     import frame_wise_delta_gram_amd as vda
 
+    copies = d if isinstance(d, list) else [d]
     desc = make_desc(cfg)
     ws = torch.empty(max(vda.vda_workspace_bytes(desc), 1), dtype=torch.uint8, device="cuda")
-    out = torch.empty((cfg.units, cfg.frames, cfg.tokens, cfg.d_v), device="cuda",
-                      dtype=d["q"].dtype)
     stream = torch.cuda.current_stream()
-    fw = (desc, d["q"], d["k"], d["v"], d["beta"], d.get("alpha"), d["gate"], d["text_k"],
-          d["text_v"], d["text_beta"], d["rms_weight"], out, ws)
+    fws = []
+    for c in copies:
+        out = torch.empty((cfg.units, cfg.frames, cfg.tokens, cfg.d_v), device="cuda",
+                          dtype=c["q"].dtype)
+        fws.append((desc, c["q"], c["k"], c["v"], c["beta"], c.get("alpha"), c["gate"],
+                    c["text_k"], c["text_v"], c["text_beta"], c["rms_weight"], out, ws))
 
     hip = ctypes.CDLL(os.path.join(os.path.dirname(torch.__file__), "lib", "libamdhip64.so"))
     hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
@@ -498,19 +519,19 @@ def time_steps(cfg, d, steps, warmup):
     timed_row = lambda i: [e if j in (4, 5) else None for j, e in enumerate(events[i])]
     log(f"[bench] {cfg.name}: warmup {warmup}")
     for i in range(warmup):
-        vda.vda_forward_timed(*fw, timed_row(i % len(events)), stream=stream)
+        vda.vda_forward_timed(*fws[i % len(fws)], timed_row(i % len(events)), stream=stream)
     torch.cuda.synchronize()
     log(f"[bench] {cfg.name}: timing {steps} steps")
     t0 = time.perf_counter()
     for i in range(steps):
-        vda.vda_forward_timed(*fw, timed_row(i), stream=stream)
+        vda.vda_forward_timed(*fws[i % len(fws)], timed_row(i), stream=stream)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     avg = {"timed_readout": sum(elapsed_ms(events[i], 4, 5) for i in range(steps)) / steps}
 
     log(f"[bench] {cfg.name}: per-stage breakdown over {steps} more steps")
     for i in range(steps):
-        vda.vda_forward_timed(*fw, events[i], stream=stream)
+        vda.vda_forward_timed(*fws[i % len(fws)], events[i], stream=stream)
     torch.cuda.synchronize()
     stage_ms = {s: [elapsed_ms(events[i], j, j + 1) for i in range(steps)]
                 for j, s in enumerate(STAGES)}
@@ -546,6 +567,50 @@ def roofline_of(cfg, avg_ms):
             "algorithmic_bytes_per_launch": bytes_, "avg_launch_ms": ms}
 
 
+MALL_BYTES = 256 << 20  # MI355X Infinity Cache
+
+
+def input_copies(cfg):
+    """Input sets the steps of ``cfg`` rotate through: enough that the steps'
+    inputs and outputs together exceed four times the MALL (at most 64), so
+    that no step finds its inputs cached; one set for the large workloads."""
+    eb = 2 if cfg.dtype == "bf16" else 4
+    per = cfg.token_heads * ((2 * cfg.d_k + 3 * cfg.d_v) * eb + 4)
+    return max(1, min(64, -(-4 * MALL_BYTES // max(per, 1))))
+
+
+def bench_config(cfg_id, steps, warmup, cpu_seconds):
+    """One more workload (the tiny, small, medium and stress configs): its own
+    throughput, per-stage breakdown, the roofline of its dominant kernel, the
+    HBM fraction of the whole op, and the fp64 oracle on a bounded sample of
+    its inputs."""
+    import torch
+    import workloads as W
+    cfg = W.CONFIGS[cfg_id]
+    n = input_copies(cfg)
+    log(f"[bench] generating {n} input set(s) of {cfg.name} on the device")
+    copies = [W.device_inputs(cfg, seed=i) for i in range(n)]
+    torch.cuda.synchronize()
+    elapsed, avg_ms = time_steps(cfg, copies, steps, warmup)
+    alg = algorithmic(cfg)
+    ms_step = elapsed * 1e3 / steps
+    total_bytes = stage_alg(alg, "stats")[0] + alg["readout"][0]
+    res = {"workload": cfg.name, "units": cfg.units, "frames": cfg.frames,
+           "tokens_per_frame": cfg.tokens, "d_k": cfg.d_k, "d_v": cfg.d_v,
+           "text_tokens": cfg.text_tokens, "dtype": cfg.dtype, "steps": steps,
+           "input_sets": n, "ms_per_step": ms_step,
+           "value": cfg.token_heads * steps / elapsed, "unit": "token-heads/s",
+           "roofline": roofline_of(cfg, avg_ms),
+           "hbm_frac_whole_op": total_bytes / (ms_step * 1e-3) / HBM_PEAK,
+           "hbm_floor_ms": total_bytes / HBM_PEAK * 1e3,
+           "stage_ms": split_steps(avg_ms)[0], "step_ms_from_events": split_steps(avg_ms)[1]}
+    if cpu_seconds > 0:
+        log(f"[bench] CPU oracle baseline, {cfg.name}")
+        res["cpu_baseline"] = cpu_baseline(copies[0], cfg, cpu_seconds)
+    del copies
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -564,6 +629,12 @@ def main():
     ap.add_argument("--prep-steps", type=int, default=None,
                     help="steps of the feature-map (vda_prep) measurement on the 768p head share "
                          "(default: --steps; 0 disables it)")
+    ap.add_argument("--seed-mode", type=int, default=1, choices=(0, 1),
+                    help="text seed: 1 = the text written into both states at beta / 2 (the "
+                         "workload's statement, default), 0 = half the text state S_T / 2")
+    ap.add_argument("--other-configs", default="1,2,3,5",
+                    help="workload ids timed after the headline one, each with its own "
+                         "roofline and oracle baseline (empty: none)")
     ap.add_argument("--summarize-prep", metavar="DIR",
                     help="write the feature-map profile summary from rocprofv3 output under DIR")
     ap.add_argument("--summarize", metavar="DIR",
@@ -581,6 +652,8 @@ def main():
               "Run it with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
+    global SEED_MODE
+    SEED_MODE = args.seed_mode
     import torch
     import frame_wise_delta_gram_amd as vda
     import workloads as W
@@ -641,7 +714,7 @@ def main():
                    "tokens_per_frame": cfg.tokens, "d_k": cfg.d_k, "d_v": cfg.d_v,
                    "text_tokens": cfg.text_tokens, "chunk": cfg.chunk, "radius": cfg.radius,
                    "decay": cfg.alpha_mu is not None, "state": "fp32",
-                   "parallelism": "single GPU"},
+                   "seed_mode": SEED_MODE, "parallelism": "single GPU"},
         "roofline": roofline_of(cfg, avg_ms),
         "mfma_frac": mfma,
         "mfma_ceiling_at_hbm_peak": mfma_ceiling,
@@ -693,6 +766,11 @@ def main():
     line["prep"] = None
     if prep_steps > 0 and args.config == 4:
         line["prep"] = bench_prep(W.PREP_CONFIGS[3], prep_steps, args.warmup)
+    line["configs"] = {}
+    for cid in [int(x) for x in args.other_configs.split(",") if x.strip()]:
+        if cid != args.config:
+            r = bench_config(cid, args.steps, args.warmup, min(args.cpu_seconds, 3.0))
+            line["configs"][r["workload"]] = r
     print(json.dumps(line), flush=True)
 
 

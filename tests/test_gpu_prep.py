@@ -94,11 +94,54 @@ def test_prep_zero_rows_stay_zero():
     assert np.all(got[2] == 0)
 
 
+# units of the 768p share checked at full size: every frame of two of them,
+# and the first and last frames of one unit in each eighth of the units (the
+# convolution's work items run in unit order over the eight XCDs, one eighth
+# of the units on each)
+FULL_UNITS = (3, 12)
+EDGE_UNITS = (0, 4, 7, 8, 11, 15)
+
+
+def _oracle_blocks(jobs, d, cfg):
+    """The prep oracle on frame blocks, in parallel threads (numpy releases the
+    GIL in its array loops).  jobs: (unit, lo, hi) output frame ranges; the
+    oracle sees input frames [lo - 2, hi + 2) clipped to the clip, which gives
+    output frames [lo, hi) exactly (five temporal taps, zero padding only at the
+    clip's own borders).  Returns {(unit, lo, hi): (q', k', v') of those frames}."""
+    import concurrent.futures
+    import os
+    from oracle import prep_oracle
+    one = dataclasses.replace(cfg, batch=1, heads=1)
+    F = cfg.frames
+    subs = {}
+    for (u, lo, hi) in jobs:
+        b, hh = divmod(u, cfg.heads)
+        a, z = max(lo - 2, 0), min(hi + 2, F)
+        sub = {name: W.tensor_to_host(d[name][b:b + 1, a:z, :, :, hh:hh + 1])
+               for name in ("q", "k", "v")}
+        for name in ("wk_s", "wk_t", "wv_s", "wv_t"):
+            sub[name] = W.tensor_to_host(d[name][hh:hh + 1])
+        subs[(u, lo, hi)] = (sub, lo - a, hi - a)
+
+    def run(key):
+        sub, s0, s1 = subs[key]
+        x = _f64(one, sub)
+        ref = prep_oracle.prep(x["q"], x["k"], x["v"], x["wk_s"], x["wk_t"], x["wv_s"],
+                               x["wv_t"], cfg.eps)
+        return key, tuple(r[0][s0:s1] for r in ref)
+
+    workers = max(1, min(16, len(os.sched_getaffinity(0))))
+    with concurrent.futures.ThreadPoolExecutor(workers) as ex:
+        return dict(ex.map(run, list(subs)))
+
+
 @pytest.mark.slow
-def test_prep_fullsize_sampled():
+def test_prep_fullsize():
+    """The 768p share (2 x 8 heads, 90 frames of 48 x 84): every frame of units
+    FULL_UNITS and the first and last six frames of EDGE_UNITS against the prep
+    oracle at the bf16 bar, plus run-to-run determinism."""
     require_gpu()
     import torch
-    from oracle import prep_oracle
     import frame_wise_delta_gram_amd as vda
     cfg = W.PREP_CONFIGS[3]
     say(f"[prep fullsize] {cfg.name}: generating inputs")
@@ -114,26 +157,27 @@ def test_prep_fullsize_sampled():
                  qo, ko, vo)
     torch.cuda.synchronize()
     ko2 = torch.empty_like(ko)
+    vo2 = torch.empty_like(vo)
     vda.vda_prep(desc, d["q"], d["k"], d["v"], d["wk_s"], d["wk_t"], d["wv_s"], d["wv_t"],
-                 qo, ko2, vo)
+                 qo, ko2, vo2)
     torch.cuda.synchronize()
     assert torch.equal(ko.view(torch.int16), ko2.view(torch.int16)), "not deterministic"
-    one = dataclasses.replace(cfg, batch=1, heads=1)
-    for b, hh in ((0, 0), (1, 7)):
-        u = b * cfg.heads + hh
-        for lo, hi, keep in ((0, 8, slice(0, 6)), (F - 8, F, slice(2, 8))):
-            sub = {name: W.tensor_to_host(d[name][b:b + 1, lo:hi, :, :, hh:hh + 1])
-                   for name in ("q", "k", "v")}
-            for name in ("wk_s", "wk_t", "wv_s", "wv_t"):
-                sub[name] = W.tensor_to_host(d[name][hh:hh + 1])
-            x = _f64(one, sub)
-            ref = prep_oracle.prep(x["q"], x["k"], x["v"], x["wk_s"], x["wk_t"], x["wv_s"],
-                                   x["wv_t"], cfg.eps)
-            for label, out, r in (("q", qo, ref[0]), ("k", ko, ref[1]), ("v", vo, ref[2])):
-                g = W.to_f64(W.tensor_to_host(out[u, lo:hi][keep]), "bf16")
-                err = row_rel_err(g, r[0][keep])
-                say(f"  unit {u} frames {lo}..{hi - 1} {label}': {err:.3e}")
-                assert err <= TOL["bf16"], (u, lo, label)
+    assert torch.equal(vo.view(torch.int16), vo2.view(torch.int16)), "not deterministic"
+    del ko2, vo2
+    jobs = [(u, lo, min(lo + 10, F)) for u in FULL_UNITS for lo in range(0, F, 10)]
+    jobs += [(u, lo, hi) for u in EDGE_UNITS for lo, hi in ((0, 6), (F - 6, F))]
+    say(f"[prep fullsize] oracle on {len(jobs)} frame blocks")
+    refs = _oracle_blocks(jobs, d, cfg)
+    worst = {}
+    for (u, lo, hi), ref in sorted(refs.items()):
+        for label, out, r in (("q", qo, ref[0]), ("k", ko, ref[1]), ("v", vo, ref[2])):
+            g = W.to_f64(W.tensor_to_host(out[u, lo:hi]), "bf16")
+            err = row_rel_err(g, r)
+            worst[(u, label)] = max(worst.get((u, label), 0.0), err)
+            assert err <= TOL["bf16"], (u, lo, hi, label, err)
+    for u in FULL_UNITS + EDGE_UNITS:
+        say(f"  unit {u} ({'every frame' if u in FULL_UNITS else 'frames 0-5, 84-89'}): "
+            + ", ".join(f"{lb}' {worst[(u, lb)]:.3e}" for lb in "qkv"))
 
 
 def _random_prep_shapes(n=24, seed=2027):

@@ -15,11 +15,22 @@ Random shapes also produce rank-deficient gathered states (one text token and a
 window that covers the clip leave S~ = S_T of rank one), and for such a state
 some queries fall almost into its null space: o = S~ q is then a small
 difference of large terms, and no fixed-precision evaluation keeps a relative
-error of 1e-4 on it.  Each output row's condition number
-kappa = ||S~||_2 ||q|| / ||S~ q|| (from the oracle's gathered state) says how
-much the rounding of S~ is amplified in that row, and the bar for the row is
-the usual one times max(1, kappa / 100): rows with kappa <= 100 (nearly all of
-them) keep the plain bar.  The fixed-shape tests keep the plain bar everywhere.
+error of 1e-4 on it.  The state is fp32 on both paths (the text frame's
+statistics are fp32 too), so representing S~ in fp32 alone perturbs o by up to
+about u ||S~||_2 ||q|| (u = 2^-24), i.e. by u * kappa relative to ||S~ q||, with
+kappa = ||S~||_2 ||q|| / ||S~ q|| the row's condition number (from the
+oracle's gathered state).  A row's bar is therefore
+    max(tol, min(C_KAPPA * u * kappa, 2e-2)),   C_KAPPA = 4,
+the usual bar unless the round-off of fp32 states, amplified by the row's
+condition number, is larger; never looser than the bf16 bar.  C_KAPPA leaves
+room for the few fp32 roundings the state goes through after the statistics
+(solve, composition, scans, readout sum) beyond the single rounding of its
+representation.  For every row that gets a relaxed bar the test also forms
+o = fl32(S~) q from the oracle's state rounded to fp32 (an fp32 evaluation of
+the same product, epilogue in fp64) and logs its error next to the GPU's, and
+requires the GPU's worst relaxed-row error to be within C_EVAL = 16 times the
+fp32 evaluation's (or within the usual bar).  The fixed-shape tests keep the
+plain bar everywhere.
 """
 import numpy as np
 import pytest
@@ -80,6 +91,21 @@ def row_condition(x, St):
     return np.where(num == 0, 1.0, num / np.where(den == 0, np.inf, den))
 
 
+U32 = 2.0 ** -24
+C_KAPPA = 4.0
+C_EVAL = 16.0
+
+
+def fp32_evaluation(x, St, cfg):
+    """out from the oracle's gathered state rounded to fp32, S~ q formed in
+    fp32 (q as given to the GPU), RMSNorm and gate in fp64."""
+    o = np.einsum("nfvk,nfuk->nfuv", St.astype(np.float32), x["q"].astype(np.float32),
+                  dtype=np.float32).astype(np.float64)
+    ms = np.mean(o * o, axis=-1, keepdims=True)
+    y = x["rms_weight"] * o / np.sqrt(ms + cfg.rms_eps)
+    return y / (1.0 + np.exp(-x["gate"]))
+
+
 @pytest.mark.parametrize("name,cfg,seed_mode", CASES, ids=[c[0] for c in CASES])
 def test_random_shape_parity(name, cfg, seed_mode):
     require_gpu()
@@ -90,14 +116,23 @@ def test_random_shape_parity(name, cfg, seed_mode):
     ref, tap = oracle_forward(x, cfg, seed_mode, taps=True)
     assert got.shape == ref.shape and np.all(np.isfinite(got))
     tol = TOL_OUT[cfg.dtype]
-    d = np.abs(got - ref).max(axis=-1)
     r = np.abs(ref).max(axis=-1)
-    err = d / np.where(r == 0, 1.0, r)
+    r = np.where(r == 0, 1.0, r)
+    err = np.abs(got - ref).max(axis=-1) / r
     kappa = row_condition(x, tap["St"])
-    well = kappa <= 100
-    say(f"  max row-rel err {err.max():.3e} (bar {tol:.0e}); rows with kappa <= 100: "
-        f"{well.mean():.4f}, their max {err[well].max() if well.any() else 0.0:.3e}; "
-        f"max kappa {kappa.max():.3g}")
-    bad = err > tol * np.maximum(1.0, kappa / 100)
+    bar = np.maximum(tol, np.minimum(C_KAPPA * U32 * kappa, 2e-2))
+    relaxed = bar > tol
+    say(f"  max row-rel err {err.max():.3e} (bar {tol:.0e}); max kappa {kappa.max():.3g}; "
+        f"rows on a relaxed bar: {int(relaxed.sum())} of {relaxed.size}"
+        + (f", their max err / (u kappa) {np.max(err[relaxed] / (U32 * kappa[relaxed])):.3g}"
+           if relaxed.any() else ""))
+    bad = err > bar
     assert not bad.any(), (f"{bad.sum()} rows over the bar; worst err {err[bad].max():.3e} "
                            f"at kappa {kappa[bad][np.argmax(err[bad])]:.3g}")
+    if relaxed.any():
+        ev = fp32_evaluation(x, tap["St"], cfg)
+        ev_err = np.abs(ev - ref).max(axis=-1) / r
+        worst_gpu, worst_ev = err[relaxed].max(), ev_err[relaxed].max()
+        say(f"  relaxed rows: GPU worst {worst_gpu:.3e}, fp32 evaluation of S~ q worst "
+            f"{worst_ev:.3e}")
+        assert worst_gpu <= max(tol, C_EVAL * worst_ev), (worst_gpu, worst_ev)
