@@ -427,6 +427,95 @@ __device__ __forceinline__ void x_fill(__bf16* xh, __bf16* xl, const float* src,
   }
 }
 
+// Forward transition chain and reverse injection of one chunk in one pass over
+// its frames (bf16 features, alpha = 1, frame-wise rule, d_k = d_v = 128).
+// Every M_t is symmetric, so the reverse injection
+//   Jr = sum_t B_t M_t M_{t-1} ... M_{f0} = sum_t B_t X_t^T,
+//   X_t = M_{f0} M_{f0+1} ... M_t   (the forward transition chain's prefix),
+// and both come from one sweep over the chunk's frames in forward order, the
+// order in which the chunk's Jf workgroup reads the same transitions (the two
+// run side by side on one XCD, so the second read of each transition hits L2).
+// Frame f0: X = M_{f0}, Jr = B_{f0} X^T.  Frame t > f0: X_t = X_{t-1} M_t (M_t
+// in LDS as the A operand, X_{t-1} as B), then B_t is staged where M_t was and
+// Jr += B_t X_t^T (X_t as the A operand, B_t as B; the product helper returns
+// the tile in the layout of Jr's rows).  The next frame's transition and write
+// are in flight while the current one is multiplied.  Writes Mc = X_{f1-1},
+// its transpose McT and Jr.
+__device__ __forceinline__ void compose_mc_jr(__bf16* Xh, __bf16* Xl, __bf16* Mh, __bf16* Ml,
+                                              const float* __restrict__ Mw,
+                                              const float* __restrict__ Bw, float* __restrict__ Mc,
+                                              float* __restrict__ McT, float* __restrict__ Jr,
+                                              int u, int c, int F, int C, int n) {
+  constexpr int dk = 128;
+  const int w = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int jr = 32 * (w & 3);
+  const int kh = w >> 2;
+  const int xr0 = 64 * kh;
+  const int f0 = c * C;
+  const int f1 = min(f0 + C, F);
+  const size_t Fp1 = (size_t)F + 1;
+  auto Mp = [&](int f) { return Mw + ((size_t)u * Fp1 + f + 1) * dk * dk; };
+  auto Bp = [&](int f) { return Bw + ((size_t)u * Fp1 + f + 1) * dk * dk; };
+  const size_t tile = ((size_t)u * n + c) * dk * dk;
+  RowsF32<8> mf, bf;  // this wave's share (rows jr .., columns 64 kh ..) of a transition, a write
+  f32x16_t accj[2] = {zero16(), zero16()};
+  f32x16_t accx[2] = {zero16(), zero16()};
+
+  rows_load<8, 16>(bf, Bp(f0), dk, jr, 64 * kh);
+  if (f0 + 1 < f1) rows_load<8, 16>(mf, Mp(f0 + 1), dk, jr, 64 * kh);
+  x_fill(Xh, Xl, Mp(f0), dk, dk, 1.0f);  // X = M_{f0}
+  rows_split<8, 16>(Mh, Ml, 0, bf, dk, jr, 64 * kh);
+  __syncthreads();
+  if (f0 + 1 < f1) rows_load<8, 16>(bf, Bp(f0 + 1), dk, jr, 64 * kh);
+  split_mm_t_lds<2>(accj, Xh, Xl, jr, Mh, Ml, xr0, 8);  // Jr = B_{f0} X^T
+  __syncthreads();
+  for (int t = f0 + 1; t < f1; ++t) {
+    const bool last = t == f1 - 1;
+    rows_split<8, 16>(Mh, Ml, 0, mf, dk, jr, 64 * kh);  // M_t
+    __syncthreads();
+    if (!last) rows_load<8, 16>(mf, Mp(t + 1), dk, jr, 64 * kh);
+    accx[0] = zero16();
+    accx[1] = zero16();
+    split_mm_t_lds<2>(accx, Mh, Ml, jr, Xh, Xl, xr0, 8);  // X_t = X_{t-1} M_t
+    __syncthreads();  // every wave has read X_{t-1} and M_t
+#pragma unroll
+    for (int x = 0; x < 2; ++x)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        x_store_quad(Xh, Xl, xr0 + 32 * x + (lane & 31), jr + 8 * q + 4 * (lane >> 5),
+                     out_quad(accx, x, q));
+    rows_split<8, 16>(Mh, Ml, 0, bf, dk, jr, 64 * kh);  // B_t
+    __syncthreads();
+    if (!last) rows_load<8, 16>(bf, Bp(t + 1), dk, jr, 64 * kh);
+    split_mm_t_lds<2>(accj, Xh, Xl, jr, Mh, Ml, xr0, 8);  // Jr += B_t X_t^T
+    __syncthreads();  // every wave has read B_t
+  }
+  // Mc = X_{f1-1} (a one-frame chunk: M_{f0}, symmetric, so Mc^T = Mc as well)
+  if (f1 - f0 == 1) {
+    const f32x4_t* src = reinterpret_cast<const f32x4_t*>(Mp(f0));
+    for (int i = threadIdx.x; i < dk * dk / 4; i += blockDim.x) {
+      const f32x4_t v = src[i];
+      reinterpret_cast<f32x4_t*>(Mc + tile)[i] = v;
+      reinterpret_cast<f32x4_t*>(McT + tile)[i] = v;
+    }
+  }
+#pragma unroll
+  for (int x = 0; x < 2; ++x)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int row = xr0 + 32 * x + (lane & 31);
+      const int col = jr + 8 * q + 4 * (lane >> 5);
+      *reinterpret_cast<f32x4_t*>(Jr + tile + (size_t)row * dk + col) = out_quad(accj, x, q);
+      if (f1 - f0 > 1) {
+        const f32x4_t v = out_quad(accx, x, q);
+        *reinterpret_cast<f32x4_t*>(Mc + tile + (size_t)row * dk + col) = v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) McT[tile + (size_t)(col + e) * dk + row] = v[e];
+      }
+    }
+}
+
 // compose (bf16): one workgroup of 8 waves per work item; wave w owns output
 // columns jr = 32 (w % 4) .. + 31 for X rows 64 (w / 4) .. + 63.  The two waves
 // of a column block load one half each (contiguous 256-byte half rows) of the
@@ -441,7 +530,9 @@ __device__ __forceinline__ void x_fill(__bf16* xh, __bf16* xl, const float* src,
 // a write chain starts at X = B of its first frame and steps X <- X M_g + B_g
 // over the others (the transition index runs one frame ahead of the write's);
 // the seed and one-frame chunks are plain copies of B.
-template <bool FULL, bool DECAY, bool BATCHED>
+// MCJR (frame-wise rule, no decay, d_k = d_v = 128): two items per chunk, the
+// forward transition chain with the reverse injection (compose_mc_jr) and Jf.
+template <bool FULL, bool DECAY, bool BATCHED, bool MCJR = false>
 __global__ __launch_bounds__(512, 1) void compose_split_kernel(
     const float* __restrict__ Bw, const float* __restrict__ Mw, const float* __restrict__ alpha,
     float* __restrict__ Mc, float* __restrict__ McT, float* __restrict__ MrT,
@@ -451,7 +542,7 @@ __global__ __launch_bounds__(512, 1) void compose_split_kernel(
   __shared__ __align__(16) __bf16 Xl[128 * SB];
   __shared__ __align__(16) __bf16 Mh[128 * SB];
   __shared__ __align__(16) __bf16 Ml[128 * SB];
-  constexpr unsigned nch = DECAY ? 4 : 3;
+  constexpr unsigned nch = MCJR ? 2 : (DECAY ? 4 : 3);
   const unsigned item = xcd_item(per);
   const unsigned chain_items = (unsigned)units * n * nch;
   if (item >= chain_items + units) return;
@@ -459,6 +550,10 @@ __global__ __launch_bounds__(512, 1) void compose_split_kernel(
   const int chain = seed ? 1 : item % nch;  // the seed runs as a forward B chain
   const int c = seed ? 0 : (item / nch) % n;
   const int u = seed ? item - chain_items : item / (nch * n);
+  if (MCJR && chain == 0) {
+    compose_mc_jr(Xh, Xl, Mh, Ml, Mw, Bw, Mc, McT, Jr, u, c, F, C, n);
+    return;
+  }
   const bool mchain = !seed && (chain == 0 || chain == 3);
   const bool reverse = !seed && (chain == 2 || chain == 3);
   const int w = threadIdx.x >> 6;
@@ -648,11 +743,11 @@ __global__ __launch_bounds__(256) void scan_split_kernel(const float* __restrict
 
 }  // namespace
 
-template <bool FULL, bool DECAY, bool BATCHED = false>
+template <bool FULL, bool DECAY, bool BATCHED = false, bool MCJR = false>
 void launch_compose_split(const Plan& p, const WsPtrs& w, const float* alpha, float seed_scale,
                           hipStream_t s) {
-  const unsigned per = xcd_per((unsigned)p.units * (p.n * (DECAY ? 4 : 3) + 1));
-  hipLaunchKernelGGL((compose_split_kernel<FULL, DECAY, BATCHED>), dim3(kXcds * per), dim3(512),
+  const unsigned per = xcd_per((unsigned)p.units * (p.n * (MCJR ? 2 : DECAY ? 4 : 3) + 1));
+  hipLaunchKernelGGL((compose_split_kernel<FULL, DECAY, BATCHED, MCJR>), dim3(kXcds * per), dim3(512),
                      0, s, w.B,
                      w.M, alpha, w.Mc, w.McT, w.MrT, w.Jf, w.Jr, w.ST, p.dk, p.dv, p.F, p.C, p.n,
                      p.units, per, seed_scale, p.anchors);
@@ -664,6 +759,8 @@ hipError_t launch_compose(const Plan& p, const WsPtrs& w, const float* alpha, hi
     if (p.rule != 0)  // the batched comparison rules (no decay)
       p.dk == 128 ? launch_compose_split<true, false, true>(p, w, nullptr, seed_scale, s)
                   : launch_compose_split<false, false, true>(p, w, nullptr, seed_scale, s);
+    else if (p.dk == 128 && p.dv == 128 && !alpha)
+      launch_compose_split<true, false, false, true>(p, w, alpha, seed_scale, s);
     else if (p.dk == 128)
       alpha ? launch_compose_split<true, true>(p, w, alpha, seed_scale, s)
             : launch_compose_split<true, false>(p, w, alpha, seed_scale, s);
