@@ -427,14 +427,17 @@ def cpu_baseline(d, cfg, budget_s):
 
 
 SEED_MODE = 1  # the text written into both states at beta / 2 (set from --seed-mode)
+ARITH = {"solver": 0, "fp32_products": 0}  # descriptor options (set from --solver, --fp32-products)
 
 
-def make_desc(cfg):
+def make_desc(cfg, **arith):
     import frame_wise_delta_gram_amd as vda
+    a = dict(ARITH, **arith)
     return vda.make_desc(cfg.units, cfg.frames, cfg.tokens, cfg.text_tokens, cfg.d_k, cfg.d_v,
                          cfg.chunk, cfg.radius, cfg.rms_eps, SEED_MODE,
                          vda.VDA_DTYPE_BF16 if cfg.dtype == "bf16" else vda.VDA_DTYPE_F32,
-                         int(cfg.anchors), cfg.rule)
+                         int(cfg.anchors), cfg.rule, a["fp32_products"],
+                         a["solver"] if cfg.rule == 0 else 0)
 
 
 def state_growth(cfg, d):
@@ -632,6 +635,14 @@ def main():
     ap.add_argument("--seed-mode", type=int, default=1, choices=(0, 1),
                     help="text seed: 1 = the text written into both states at beta / 2 (the "
                          "workload's statement, default), 0 = half the text state S_T / 2")
+    ap.add_argument("--solver", type=int, default=0, choices=(0, 1),
+                    help="transition solver: 0 = block sweep (default), 1 = blocked Cholesky")
+    ap.add_argument("--fp32-products", type=int, default=0, choices=(0, 1),
+                    help="bf16 features: 1 = composition and scan with fp32 MFMA products "
+                         "(default 0: split-bf16 products)")
+    ap.add_argument("--variant-steps", type=int, default=None,
+                    help="steps of the solver / product variants timed on the headline "
+                         "workload (default: --steps; 0 disables them)")
     ap.add_argument("--other-configs", default="1,2,3,5",
                     help="workload ids timed after the headline one, each with its own "
                          "roofline and oracle baseline (empty: none)")
@@ -654,6 +665,7 @@ def main():
 
     global SEED_MODE
     SEED_MODE = args.seed_mode
+    ARITH.update(solver=args.solver, fp32_products=args.fp32_products)
     import torch
     import frame_wise_delta_gram_amd as vda
     import workloads as W
@@ -714,7 +726,9 @@ def main():
                    "tokens_per_frame": cfg.tokens, "d_k": cfg.d_k, "d_v": cfg.d_v,
                    "text_tokens": cfg.text_tokens, "chunk": cfg.chunk, "radius": cfg.radius,
                    "decay": cfg.alpha_mu is not None, "state": "fp32",
-                   "seed_mode": SEED_MODE, "parallelism": "single GPU"},
+                   "seed_mode": SEED_MODE, "solver": ["sweep", "cholesky"][args.solver],
+                   "products": ["split-bf16", "fp32"][args.fp32_products or cfg.dtype == "f32"],
+                   "parallelism": "single GPU"},
         "roofline": roofline_of(cfg, avg_ms),
         "mfma_frac": mfma,
         "mfma_ceiling_at_hbm_peak": mfma_ceiling,
@@ -745,6 +759,23 @@ def main():
             "key scaling (rule 2)", "steps": bsteps, "ms_per_step": el * 1e3 / bsteps,
             "value": bvalue, "unit": "token-heads/s", "relative_to_vda": bvalue / value,
             "stage_ms": split_steps(ms)[0], "state_growth": state_growth(cfg, d)}
+    line["variants"] = None
+    vsteps = args.steps if args.variant_steps is None else args.variant_steps
+    if vsteps > 0 and args.config == 4:
+        line["variants"] = {}
+        base = dict(ARITH)
+        for name, arith in (("cholesky_solver", dict(solver=1)),
+                            ("sweep_solver", dict(solver=0)),
+                            ("fp32_products", dict(fp32_products=1)),
+                            ("split_bf16_products", dict(fp32_products=0))):
+            ARITH.update(base, **arith)
+            log(f"[bench] variant {name}")
+            el, ms = time_steps(cfg, d, vsteps, args.warmup)
+            st = split_steps(ms)[0]
+            line["variants"][name] = {
+                "descriptor": dict(ARITH), "steps": vsteps, "ms_per_step": el * 1e3 / vsteps,
+                "value": th * vsteps / el, "unit": "token-heads/s", "stage_ms": st}
+        ARITH.update(base)
     decay_steps = args.steps if args.decay_steps is None else args.decay_steps
     line["decay"] = None
     del d

@@ -41,6 +41,7 @@ class VdaDesc(ctypes.Structure):
         ("chunk", ctypes.c_int32), ("radius", ctypes.c_int32), ("rms_eps", ctypes.c_float),
         ("seed_mode", ctypes.c_int32), ("in_dtype", ctypes.c_int32), ("out_dtype", ctypes.c_int32),
         ("anchors", ctypes.c_int32), ("rule", ctypes.c_int32),
+        ("fp32_products", ctypes.c_int32), ("solver", ctypes.c_int32),
     ]
 
     @property
@@ -122,9 +123,11 @@ def vda_status_string(status: int) -> str:
 
 
 def make_desc(units, frames, tokens, text_tokens, d_k, d_v, chunk=5, radius=1, rms_eps=1e-6,
-              seed_mode=0, dtype=VDA_DTYPE_BF16, anchors=0, rule=0) -> VdaDesc:
+              seed_mode=0, dtype=VDA_DTYPE_BF16, anchors=0, rule=0, fp32_products=0,
+              solver=0) -> VdaDesc:
     return VdaDesc(units, frames, tokens, text_tokens, d_k, d_v, chunk, radius, rms_eps,
-                   seed_mode, dtype, dtype, int(anchors), int(rule))
+                   seed_mode, dtype, dtype, int(anchors), int(rule), int(fp32_products),
+                   int(solver))
 
 
 def vda_workspace_bytes(desc: VdaDesc) -> int:
@@ -284,7 +287,7 @@ def vda_prep(desc, q, k, v, wk_s, wk_t, wv_s, wv_t, q_out, k_out, v_out, stream=
 
 # ----------------------------------------------------------------------------- torch helpers
 def desc_from_tensors(q, k, v, text_k, chunk=5, radius=1, eps=1e-6, seed_mode=0,
-                      anchors=False, rule=0) -> VdaDesc:
+                      anchors=False, rule=0, fp32_products=0, solver=0) -> VdaDesc:
     """Descriptor from tensor shapes: q/k [units, F, U, d_k], v [units, F, U, d_v],
     text_k [units, T, d_k]."""
     import torch
@@ -299,7 +302,8 @@ def desc_from_tensors(q, k, v, text_k, chunk=5, radius=1, eps=1e-6, seed_mode=0,
         dt = VDA_DTYPE_F32
     else:
         raise TypeError("features must be bfloat16 or float32, got %s" % k.dtype)
-    return make_desc(units, F, U, T, dk, dv, chunk, radius, eps, seed_mode, dt, anchors, rule)
+    return make_desc(units, F, U, T, dk, dv, chunk, radius, eps, seed_mode, dt, anchors, rule,
+                     fp32_products, solver)
 
 
 def _check_tensor(name, x, dtype, shape, device=None):
@@ -322,7 +326,7 @@ def _check_tensor(name, x, dtype, shape, device=None):
 
 def forward(q, k, v, beta, gate, text_k, text_v, text_beta, rms_weight, chunk=5, radius=1,
             eps=1e-6, seed_mode=0, out=None, workspace=None, stream=None, alpha=None,
-            anchors=False, rule=0):
+            anchors=False, rule=0, fp32_products=0, solver=0):
     """VDA forward on torch GPU tensors; allocates `out` and the workspace when absent.
 
     Shapes: q, k [units, F, U, d_k]; v, gate [units, F, U, d_v]; beta [units, F, U]
@@ -331,7 +335,8 @@ def forward(q, k, v, beta, gate, text_k, text_v, text_beta, rms_weight, chunk=5,
     (float32); alpha (optional decay gates) [units, F, d_k] (float32); anchors:
     boundary anchors (frames 0 and F - 1 out of the linear states, their rows
     zero); rule: 0 the frame-wise delta rule, 1 / 2 the batched comparison rules
-    (no decay).  A caller-supplied `out` must be [units, F, U, d_v] in the
+    (no decay); fp32_products: composition and scan on fp32 MFMA for bf16
+    features; solver: 0 symmetric Gauss-Jordan, 1 blocked Cholesky.  A caller-supplied `out` must be [units, F, U, d_v] in the
     features' dtype, a caller-supplied workspace a contiguous uint8 tensor on the
     features' GPU.  Every tensor is checked (dtype, shape, device, contiguity)
     before anything is enqueued: a mismatch raises TypeError or ValueError.
@@ -344,7 +349,8 @@ def forward(q, k, v, beta, gate, text_k, text_v, text_beta, rms_weight, chunk=5,
         raise TypeError("v: expected a 4-d torch tensor [units, F, U, d_v]")
     if (text_k is None) != (text_v is None) or (text_k is None) != (text_beta is None):
         raise ValueError("text_k, text_v and text_beta are given together or all None")
-    desc = desc_from_tensors(q, k, v, text_k, chunk, radius, eps, seed_mode, anchors, rule)
+    desc = desc_from_tensors(q, k, v, text_k, chunk, radius, eps, seed_mode, anchors, rule,
+                             fp32_products, solver)
     units, F, U, dk = k.shape
     dv = v.shape[-1]
     T = desc.text_tokens

@@ -755,7 +755,7 @@ void launch_compose_split(const Plan& p, const WsPtrs& w, const float* alpha, fl
 
 hipError_t launch_compose(const Plan& p, const WsPtrs& w, const float* alpha, hipStream_t s) {
   const float seed_scale = p.seed_mode == 1 ? 1.0f : 0.5f;
-  if (p.dtype == VDA_DTYPE_BF16) {
+  if (!p.fp32_products) {
     if (p.rule != 0)  // the batched comparison rules (no decay)
       p.dk == 128 ? launch_compose_split<true, false, true>(p, w, nullptr, seed_scale, s)
                   : launch_compose_split<false, false, true>(p, w, nullptr, seed_scale, s);
@@ -780,7 +780,7 @@ hipError_t launch_compose(const Plan& p, const WsPtrs& w, const float* alpha, hi
 hipError_t launch_scan(const Plan& p, const WsPtrs& w, bool decay, hipStream_t s) {
   const dim3 grid(pad32(p.dv) >> 5, p.units, 2);
   const float* rev = decay ? w.MrT : w.Mc;
-  if (p.dtype == VDA_DTYPE_BF16) {
+  if (!p.fp32_products) {
     if (p.dk == 128 && p.dv % 32 == 0)
       hipLaunchKernelGGL(scan_split_kernel<true>, grid, dim3(kThreads), 0, s, rev, w.McT, w.Jf,
                          w.Jr, w.ST, p.dk, p.dv, p.n);

@@ -204,6 +204,256 @@ __global__ __launch_bounds__(256, 3) void solve_kernel(const float* __restrict__
   }
 }
 
+// ---------------------------------------------------------------------------
+// The same transition through a blocked Cholesky factorisation (desc->solver
+// = 1), the factor-and-solve route of a classical SPD inverse:
+//   I + A_t = L L^T  (right-looking, 32 x 32 blocks: factor the diagonal block,
+//                     its triangular inverse W_p, panel L_ip = G_ip W_p^T,
+//                     trailing update G_ij -= L_ip L_jp^T),
+//   Y = L^{-1}       (block column by block column: Y_jj = W_j,
+//                     Y_ij = -W_i sum_{k=j}^{i-1} L_ik Y_kj),
+//   M_t = Y^T Y.
+// Every pivot of I + A_t is >= 1, so no pivoting.  One workgroup (4 waves)
+// per frame: the lower blocks of G (then L, then Y) in LDS, the four W_p and a
+// column of Y in progress next to them (72 KiB: two workgroups per CU); the
+// diagonal blocks are factored and inverted by one wave each in its MFMA
+// accumulators with rank-1 v_mfma_f32_32x32x2_f32 updates (32 dependent steps
+// each, twice per block: 256 in all against the sweep's 128, the reason the
+// sweep is the default).  fp32 throughout.
+
+// Cholesky factor of the symmetric positive definite 32 x 32 block T (accumulator
+// layout, both triangles), by one wave: T becomes L (lower, zeros above).  Step
+// k: d = sqrt(T_kk); column k below the diagonal is scaled by 1 / d (lane k
+// holds column k, and by symmetry the untouched T_ik = T_ki); the trailing
+// block gets T_ij -= x_i x_j (x = row k / d beyond k) as a rank-1 MFMA through
+// k-slot hk (row k sits in register rk of the lanes of half hk); row k beyond
+// the diagonal is set to zero.
+__device__ __forceinline__ void chol_block(f32x16_t& T) {
+  const int lane = lane_id();
+  const int half = lane >> 5;
+  const int c = lane & 31;
+#pragma unroll
+  for (int k = 0; k < 32; ++k) {
+    const int rk = 4 * (k >> 3) + (k & 3);
+    const int hk = (k >> 2) & 1;
+    const float tkk = readlane_f(T[rk], k + 32 * hk);
+    const float d = __builtin_sqrtf(tkk);
+    const float inv = 1.0f / d;
+    const bool inrow = half == hk;
+    const float x = (inrow && c > k) ? T[rk] * inv : 0.0f;  // L_ck for c > k
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int i = acc_row(r, lane);
+      if (c == k) T[r] = i > k ? T[r] * inv : (i == k ? d : T[r]);
+    }
+    if (inrow && c > k) T[rk] = 0.0f;  // upper triangle
+    T = mfma_f32(-x, x, T);
+  }
+}
+
+// Inverse of the lower-triangular 32 x 32 block L (in LDS, row stride SG), by
+// one wave: W = L^{-1} in accumulator layout.  Gauss-Jordan on the rows of
+// W = I: step k divides row k by L_kk and subtracts L_ik (row k) from every row
+// i > k, a rank-1 MFMA with L's column k (read from LDS) in k-slot hk.
+__device__ __forceinline__ f32x16_t tri_inv_block(const float* L) {
+  const int lane = lane_id();
+  const int half = lane >> 5;
+  const int c = lane & 31;
+  f32x16_t W;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) W[r] = acc_row(r, lane) == c ? 1.0f : 0.0f;
+#pragma unroll
+  for (int k = 0; k < 32; ++k) {
+    const int rk = 4 * (k >> 3) + (k & 3);
+    const int hk = (k >> 2) & 1;
+    const bool inrow = half == hk;
+    const float lkk = L[k * SG + k];
+    if (inrow) W[rk] *= 1.0f / lkk;
+    const float a = (inrow && c > k) ? -L[c * SG + k] : 0.0f;  // -L_ck for rows c > k
+    const float b = inrow ? W[rk] : 0.0f;                       // row k of W
+    W = mfma_f32(a, b, W);
+  }
+  return W;
+}
+
+// q-th lower block (i, j), j <= i < n, in the order (0,0), (1,0), (1,1), (2,0), ...
+__device__ __forceinline__ bool lower_pair(int q, int n, int& i, int& j) {
+  i = 0;
+  while (q > i && i < n) {
+    q -= i + 1;
+    ++i;
+  }
+  j = q;
+  return i < n;
+}
+
+constexpr int kCholLds = (kNBlk + 4 + 3) * kBlk;  // L/Y blocks, the W_p, a column of Y
+
+__global__ __launch_bounds__(256, 2) void solve_chol_kernel(const float* __restrict__ A,
+                                                           float* __restrict__ Mout, int dk,
+                                                           int Fp1) {
+  __shared__ float Gs[kCholLds];
+  const int fi = blockIdx.x;
+  const int u = blockIdx.y;
+  const int t = threadIdx.x;
+  const int lane = t & 63;
+  const int w = t >> 6;
+  const int Dk = pad32(dk);
+  const int nb = Dk >> 5;
+  auto G = [&](int i, int j) { return Gs + (i * (i + 1) / 2 + j) * kBlk; };
+  auto Wb = [&](int i) { return Gs + (kNBlk + i) * kBlk; };
+  auto Yc = [&](int i) { return Gs + (kNBlk + 4 + i) * kBlk; };  // column scratch, i = 0..2
+
+  {  // G = I + A, lower-triangle blocks (identity on the padding)
+    const float* Af = A + ((size_t)u * Fp1 + fi) * dk * dk;
+    const f32x4_t z = {0.0f, 0.0f, 0.0f, 0.0f};
+    f32x4_t m[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int id = t + 256 * i;
+      const int r = id >> 5;
+      const int c = (id & 31) << 2;
+      const bool ok = r < dk && c < dk && (c >> 5) <= (r >> 5);
+      m[i] = ok ? *reinterpret_cast<const f32x4_t*>(Af + (size_t)r * dk + c) : z;
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int id = t + 256 * i;
+      const int r = id >> 5;
+      const int c = (id & 31) << 2;
+      const int bi = r >> 5, bj = c >> 5;
+      if (r < Dk && c < Dk && bj <= bi) {
+        float* dst = G(bi, bj) + (r & 31) * SG + (c & 31);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dst[e] = m[i][e] + (r == c + e ? 1.0f : 0.0f);
+      }
+    }
+    __syncthreads();
+  }
+  // the diagonal block of G is symmetric but only its lower triangle is stored
+  // as read from A; complete it for the factorisation
+  auto load_sym = [&](const float* Bk) {
+    f32x16_t T;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int i = acc_row(r, lane), j = lane & 31;
+      T[r] = i >= j ? Bk[i * SG + j] : Bk[j * SG + i];
+    }
+    return T;
+  };
+
+  for (int p = 0; p < nb; ++p) {
+    if (w == 0) {
+      f32x16_t T = load_sym(G(p, p));
+      chol_block(T);
+      store_acc(G(p, p), SG, T, 1.0f);
+      wave_sync();
+      const f32x16_t Wp = tri_inv_block(G(p, p));
+      store_acc(Wb(p), SG, Wp, 1.0f);
+    }
+    __syncthreads();
+    // panel: L_ip = G_ip W_p^T
+    const int i = p + 1 + w;
+    if (i < nb) {
+      const f32x16_t L = blk_mm32<false, true>(zero16(), G(i, p), SG, Wb(p), SG);
+      store_acc(G(i, p), SG, L, 1.0f);
+    }
+    __syncthreads();
+    // trailing update G_ij -= L_ip L_jp^T, i >= j > p: the lower blocks of the
+    // trailing matrix dealt over the waves
+    for (int q = w;; q += 4) {
+      int ii, jj;
+      if (!lower_pair(q, nb - p - 1, ii, jj)) break;
+      ii += p + 1;
+      jj += p + 1;
+      const f32x16_t prod = blk_mm32<false, true>(zero16(), G(ii, p), SG, G(jj, p), SG);
+      float* C = G(ii, jj);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) C[acc_row(r, lane) * SG + (lane & 31)] -= prod[r];
+    }
+    __syncthreads();
+  }
+
+  // Y = L^{-1}, block column j: Y_ij = -W_i sum_{k=j}^{i-1} L_ik Y_kj, i = j + 1 ..,
+  // built in the scratch by wave 0 (each entry needs the previous ones), then
+  // copied over L's column j (later columns read only L's columns > j)
+  for (int j = 0; j + 1 < nb; ++j) {
+    if (w == 0) {
+      for (int i = j + 1; i < nb; ++i) {
+        f32x16_t S = zero16();
+        for (int k = j; k < i; ++k) {
+          const float* Ykj = k == j ? Wb(j) : Yc(k - j - 1);
+          S = blk_mm32<false, false>(S, G(i, k), SG, Ykj, SG);
+        }
+        store_acc(Yc(i - j - 1), SG, S, 1.0f);
+        wave_sync();
+        const f32x16_t Yij = blk_mm32<false, false>(zero16(), Wb(i), SG, Yc(i - j - 1), SG);
+        wave_sync();
+        store_acc(Yc(i - j - 1), SG, Yij, -1.0f);
+        wave_sync();
+      }
+    }
+    __syncthreads();
+    for (int idx = t; idx < (nb - 1 - j) * 32 * 32; idx += 256) {
+      const int b = idx >> 10, e = idx & 1023;
+      const int r = e >> 5, c = e & 31;
+      G(j + 1 + b, j)[r * SG + c] = Yc(b)[r * SG + c];
+    }
+    __syncthreads();
+  }
+
+  // M = Y^T Y: M_ij = sum_{k >= i} Y_ki^T Y_kj for the lower blocks (i >= j), at
+  // most three per wave, held in registers until every wave has read Y, then
+  // stored over the lower blocks (a diagonal block from its lower triangle, so
+  // M is exactly symmetric) and written out row-major as in the sweep
+  f32x16_t Mb[3];
+#pragma unroll
+  for (int s3 = 0; s3 < 3; ++s3) {
+    Mb[s3] = zero16();
+    int ii, jj;
+    if (!lower_pair(w + 4 * s3, nb, ii, jj)) continue;
+    for (int k = ii; k < nb; ++k) {
+      const float* Yki = k == ii ? Wb(ii) : G(k, ii);
+      const float* Ykj = k == jj ? Wb(jj) : G(k, jj);
+      Mb[s3] = blk_mm32<true, false>(Mb[s3], Yki, SG, Ykj, SG);
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int s3 = 0; s3 < 3; ++s3) {
+    int ii, jj;
+    if (!lower_pair(w + 4 * s3, nb, ii, jj)) continue;
+    float* C = G(ii, jj);
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int row = acc_row(r, lane), col = lane & 31;
+      if (ii != jj || row >= col) C[row * SG + col] = Mb[s3][r];
+      if (ii == jj && row > col) C[col * SG + row] = Mb[s3][r];
+    }
+  }
+  __syncthreads();
+  float* Mg = Mout + ((size_t)u * Fp1 + fi) * dk * dk;
+#pragma unroll 4
+  for (int i = 0; i < 16; ++i) {
+    const int id = t + 256 * i;
+    const int r = id >> 5;
+    const int c = (id & 31) << 2;
+    if (r >= dk || c >= dk) continue;
+    const int bi = r >> 5, bj = c >> 5;
+    f32x4_t v;
+    if (bj <= bi) {
+      const float* src = G(bi, bj) + (r & 31) * SG + (c & 31);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = src[e];
+    } else {
+      const float* src = G(bj, bi) + (c & 31) * SG + (r & 31);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = src[e * SG];
+    }
+    *reinterpret_cast<f32x4_t*>(Mg + (size_t)r * dk + c) = v;
+  }
+}
+
 // Inherited-state factor of the batched comparison rules (SANA-WM's frozen-state
 // update, Sec. 3.1 Eq. (3c)): M = I - s A, and with frame-size key scaling
 // (App. A.2, rule 2) s = 1 / N and B <- B / sqrt(N), N the frame's token count
@@ -241,7 +491,9 @@ __global__ __launch_bounds__(256) void batched_factor_kernel(const float* __rest
 
 hipError_t launch_solve(const Plan& p, const WsPtrs& w, hipStream_t s) {
   const dim3 grid(p.F + 1, p.units);
-  if (p.rule == 0)
+  if (p.rule == 0 && p.solver == 1)
+    hipLaunchKernelGGL(solve_chol_kernel, grid, dim3(kThreads), 0, s, w.A, w.M, p.dk, p.F + 1);
+  else if (p.rule == 0)
     hipLaunchKernelGGL(solve_kernel, grid, dim3(kThreads), 0, s, w.A, w.M, p.dk, p.F + 1);
   else
     hipLaunchKernelGGL(batched_factor_kernel, grid, dim3(kThreads), 0, s, w.A, w.M, w.B, p.dk,

@@ -38,6 +38,9 @@ int make_plan(const vda_desc_t* d, Plan* p) {
   if (d->seed_mode != 0 && d->seed_mode != 1) return VDA_ERR_INVALID_ARG;
   if (d->anchors != 0 && d->anchors != 1) return VDA_ERR_INVALID_ARG;
   if (d->rule < 0 || d->rule > 2) return VDA_ERR_INVALID_ARG;
+  if (d->fp32_products != 0 && d->fp32_products != 1) return VDA_ERR_INVALID_ARG;
+  if (d->solver != 0 && d->solver != 1) return VDA_ERR_INVALID_ARG;
+  if (d->solver == 1 && d->rule != 0) return VDA_ERR_INVALID_ARG;  // a factor of I + A_t only
   if (d->units > kMaxGridYZ) return VDA_ERR_INVALID_ARG;
   const int64_t n = d->frames > 0 ? (d->frames + (int64_t)d->chunk - 1) / d->chunk : 0;
   if (n > kMaxGridYZ) return VDA_ERR_INVALID_ARG;
@@ -85,6 +88,8 @@ int make_plan(const vda_desc_t* d, Plan* p) {
   p->seed_mode = d->seed_mode;
   p->anchors = d->anchors;
   p->rule = d->rule;
+  p->fp32_products = d->fp32_products != 0 || d->in_dtype == VDA_DTYPE_F32;
+  p->solver = d->solver;
   p->dtype = d->in_dtype;
 
   const size_t U_ = (size_t)p->units, Fp1 = (size_t)p->F + 1, N = (size_t)p->n;
@@ -306,6 +311,8 @@ int make_prep_plan(const vda_prep_desc_t* d, PrepPlan* p) {
   if ((int64_t)d->batch * d->heads > kMaxGridYZ) return VDA_ERR_INVALID_ARG;
   if (d->frames > kMaxFrames) return VDA_ERR_INVALID_ARG;
   if ((int64_t)d->height * d->width > 4194303) return VDA_ERR_INVALID_ARG;
+  // each side alone too (an empty frame with one side at INT32_MAX would overflow the tiling)
+  if (d->height > 4194303 || d->width > 4194303) return VDA_ERR_INVALID_ARG;
   // one frame of one batch entry (all heads) is addressed with 32-bit byte offsets
   if ((int64_t)d->height * d->width * d->heads * 128 * 4 > INT32_MAX) return VDA_ERR_INVALID_ARG;
   if (d->d_k < 16 || d->d_k > 128 || d->d_k % 16) return VDA_ERR_INVALID_ARG;

@@ -129,6 +129,15 @@ typedef struct vda_desc {
   int32_t out_dtype;   /* vda_dtype_t of out; must equal in_dtype */
   int32_t anchors;     /* 0: no anchors; 1: boundary anchors (see above) */
   int32_t rule;        /* 0: the frame-wise delta rule; 1, 2: batched comparison rules (above) */
+  int32_t fp32_products; /* bf16 features: 0 = the composition and the scan multiply their
+                            fp32 maps with split-bf16 MFMA (hi/lo operands, about 2^-16
+                            relative per product, the fast default); 1 = with fp32 MFMA
+                            (exact fp32 products, the fp32 state updates of [VDN] Sec. 5).
+                            fp32 features always use fp32 products. */
+  int32_t solver;      /* frame-wise rule: 0 = symmetric Gauss-Jordan elimination of I + A_t
+                          (block sweep, the default); 1 = blocked Cholesky factorisation
+                          I + A_t = L L^T, then M_t = L^-T L^-1 (same result to rounding);
+                          rules 1, 2 take 0 only */
 } vda_desc_t;
 
 /* Bytes of device workspace vda_forward and the debug taps need for `desc`
@@ -230,9 +239,9 @@ typedef struct vda_prep_desc {
   int32_t heads;  /* >= 0; batch x heads <= 65535 */
   int32_t frames; /* 0..2^20 */
   int32_t height; /* latent rows H_l >= 0 */
-  int32_t width;  /* latent columns W_l >= 0; height x width <= 4194303, height x
-                     width x heads x 512 <= 2^31 - 1, and batch x heads x
-                     ceil(height / 8) x ceil(width / 8) < 2^21 - 1024 */
+  int32_t width;  /* latent columns W_l >= 0; height, width and height x width each
+                     <= 4194303, height x width x heads x 512 <= 2^31 - 1, and batch x
+                     heads x ceil(height / 8) x ceil(width / 8) < 2^21 - 1024 */
   int32_t d_k;    /* channels of q and k: multiple of 16, 16..128 */
   int32_t d_v;    /* channels of v: multiple of 16, 16..128 */
   float eps;      /* L2 normalisation floor: finite, > 0 */

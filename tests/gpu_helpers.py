@@ -49,12 +49,12 @@ def device_to_host_f64(d: dict, cfg: W.Config, units=None) -> dict:
     return res
 
 
-def desc_for(cfg: W.Config, seed_mode=0):
+def desc_for(cfg: W.Config, seed_mode=0, fp32_products=0, solver=0):
     import frame_wise_delta_gram_amd as vda
     dt = vda.VDA_DTYPE_BF16 if cfg.dtype == "bf16" else vda.VDA_DTYPE_F32
     return vda.make_desc(cfg.units, cfg.frames, cfg.tokens, cfg.text_tokens, cfg.d_k, cfg.d_v,
                          cfg.chunk, cfg.radius, cfg.rms_eps, seed_mode, dt, int(cfg.anchors),
-                         cfg.rule)
+                         cfg.rule, fp32_products, solver)
 
 
 def workspace_for(desc):
@@ -63,11 +63,12 @@ def workspace_for(desc):
     return torch.empty(max(vda.vda_workspace_bytes(desc), 1), dtype=torch.uint8, device="cuda")
 
 
-def gpu_forward(d: dict, cfg: W.Config, seed_mode=0, ws=None, out=None):
+def gpu_forward(d: dict, cfg: W.Config, seed_mode=0, ws=None, out=None, fp32_products=0,
+                solver=0):
     """vda_forward, or vda_forward_decay when the inputs hold decay gates."""
     import torch
     import frame_wise_delta_gram_amd as vda
-    desc = desc_for(cfg, seed_mode)
+    desc = desc_for(cfg, seed_mode, fp32_products, solver)
     ws = workspace_for(desc) if ws is None else ws
     if out is None:
         out = torch.empty((cfg.units, cfg.frames, cfg.tokens, cfg.d_v), device="cuda",

@@ -149,6 +149,10 @@ def test_workspace_formula(lib):
     (dict(rule=1), vda.VDA_OK),
     (dict(rule=2), vda.VDA_OK),
     (dict(rule=3), vda.VDA_ERR_INVALID_ARG),
+    (dict(fp32_products=2), vda.VDA_ERR_INVALID_ARG),
+    (dict(fp32_products=-1), vda.VDA_ERR_INVALID_ARG),
+    (dict(solver=2), vda.VDA_ERR_INVALID_ARG),
+    (dict(solver=1, rule=1), vda.VDA_ERR_INVALID_ARG),
     (dict(rule=-1), vda.VDA_ERR_INVALID_ARG),
     (dict(units=70000), vda.VDA_ERR_INVALID_ARG),
     (dict(tokens=4194304), vda.VDA_ERR_INVALID_ARG),
