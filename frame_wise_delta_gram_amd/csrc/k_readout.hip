@@ -322,6 +322,223 @@ __global__ __launch_bounds__(512, 4) void readout_bf16_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------
+// bf16 with d_k = d_v = 128, no decay: the same readout in two kernels.
+//
+// (1) split_states_kernel: for every (unit, chunk) S~ = P[max(c - r, 0)] +
+//     R[min(c + r + 1, n)] in fp32, split into bf16 hi + lo and written in the
+//     readout's LDS image (hi rows, then lo rows, 136 bf16 per row, rows
+//     permuted as below): 69632 bytes per chunk.
+// (2) readout_c128_kernel: one workgroup (8 waves) per (unit, chunk, 256-row
+//     block) copies its chunk's image into LDS with global_load_lds (68 x 1 KB,
+//     no registers), then each wave runs two 16-row groups.
+//
+// Access pattern.  Every q / gate load and out store instruction covers 8
+// rows x 128 contiguous bytes (eight full cache lines; the bytes are streamed,
+// so the loads and stores are non-temporal): in the four instructions i =
+// (i1, i0) of a 16-row group, lane l takes row 8 i1 + (l & 7) and 16-byte chunk
+// 8 i0 + (l >> 3) of that row.  The MFMA operand wants token = l & 15, so one
+// exchange of register bit i1 with lane bit 3 (DPP row_ror:8, which is lane
+// xor 8 inside each row of 16 lanes, and a select) gives register s = (c0, c3)
+// at lane (h = l >> 4, token l & 15) the chunk 8 (s & 1) + 2 h + (s >> 1) of
+// its token.  That is the B operand of k-step s (the k order inside a step is
+// a fixed permutation; S~'s columns are read in the same order), and, applied
+// to gate, the epilogue's operand.  S~'s rows (output channels) are permuted
+// so that the accumulators of output register s are the 8 channels of the
+// same chunk, so the outputs go back through the same exchange and leave as
+// 8 rows x 128 B stores.
+constexpr int kSRow = 136;                      // bf16 per LDS row of S~ (17 x 16 bytes)
+constexpr int kSplitBytes = 2 * 128 * kSRow * 2;  // hi + lo image of one chunk's S~
+
+// chunk of 8 channels held in output register s by lane group h
+__device__ __forceinline__ int c128_chunk(int s, int h) { return 8 * (s & 1) + 2 * h + (s >> 1); }
+// LDS row of S~'s output channel ch: tile T = 2 s + (e >> 2), row 4 h + (e & 3)
+__device__ __forceinline__ int c128_row(int ch) {
+  const int chunk = ch >> 3, e = ch & 7;
+  const int s = 2 * (chunk & 1) + (chunk >> 3);
+  const int h = (chunk >> 1) & 3;
+  return 16 * (2 * s + (e >> 2)) + 4 * h + (e & 3);
+}
+
+__global__ __launch_bounds__(256) void split_states_kernel(const float* __restrict__ ST,
+                                                           uint16_t* __restrict__ Sp, int n,
+                                                           int radius) {
+  const int c = blockIdx.x;
+  const int u = blockIdx.y;
+  const size_t SS = 128 * 128;
+  const float* P = ST + ((size_t)(u * 2 + 0) * (n + 1) + max(c - radius, 0)) * SS;
+  const float* R = ST + ((size_t)(u * 2 + 1) * (n + 1) + min(c + radius + 1, n)) * SS;
+  uint16_t* dst = Sp + ((size_t)u * n + c) * (kSplitBytes / 2);
+  for (int it = threadIdx.x; it < 128 * 17; it += kThreads) {
+    const int ch = it / 17, k8 = it - 17 * (it / 17);
+    u32x4_t hi = {0u, 0u, 0u, 0u}, lo = {0u, 0u, 0u, 0u};
+    if (k8 < 16) {  // column group 16 is the row's padding
+      const f32x4_t* pp = reinterpret_cast<const f32x4_t*>(P + (size_t)ch * 128 + 8 * k8);
+      const f32x4_t* rp = reinterpret_cast<const f32x4_t*>(R + (size_t)ch * 128 + 8 * k8);
+      const f32x4_t p0 = pp[0], p1 = pp[1], r0 = rp[0], r1 = rp[1];
+      float x[8];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        x[e] = p0[e] + r0[e];
+        x[4 + e] = p1[e] + r1[e];
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t hp = pack_bf16(x[2 * e], x[2 * e + 1]);
+        hi[e] = hp;
+        lo[e] = pack_bf16(x[2 * e] - bf16_lo(hp), x[2 * e + 1] - bf16_hi(hp));
+      }
+    }
+    const int lr = c128_row(ch);
+    *reinterpret_cast<u32x4_t*>(dst + lr * kSRow + 8 * k8) = hi;
+    *reinterpret_cast<u32x4_t*>(dst + 128 * kSRow + lr * kSRow + 8 * k8) = lo;
+  }
+}
+
+__device__ __forceinline__ uint32_t lane_xor8(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x128 /* row_ror:8 */, 0xF, 0xF, false);
+}
+// exchange register bit 1 with lane bit 3 (b3) across X[0..3]; every lane runs it
+// (the DPP reads other lanes), so both rotated values are formed before selecting
+__device__ __forceinline__ void c128_exchange(u32x4_t (&X)[4], bool b3) {
+#pragma unroll
+  for (int lo = 0; lo < 2; ++lo) {
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      const uint32_t a = X[lo][d], b = X[lo + 2][d];
+      const uint32_t ra = lane_xor8(a), rb = lane_xor8(b);
+      X[lo][d] = b3 ? rb : a;
+      X[lo + 2][d] = b3 ? b : ra;
+    }
+  }
+}
+
+constexpr int kGroupsC = 2;                       // 16-row groups per wave
+constexpr int kRowsC = 8 * 16 * kGroupsC;         // token rows per workgroup
+
+__global__ __launch_bounds__(512, 4) void readout_c128_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ gate,
+    const float* __restrict__ wrms, uint16_t* __restrict__ out, const uint16_t* __restrict__ Sp,
+    int F, int U, int C, int radius, int n, float eps, int units, int nblk, unsigned per,
+    int anchors) {
+  __shared__ __align__(16) uint16_t S[kSplitBytes / 2];  // hi rows 0..127, lo rows 128..255
+  __shared__ __align__(16) float Ws[128];
+  const unsigned item = xcd_item(per);
+  if (item >= (unsigned)units * n * nblk) return;
+  const int blk = item % nblk;
+  const int c = (item / nblk) % n;
+  const int u = item / (nblk * n);
+  const int f0 = c * C;
+  const int f1 = min(f0 + C, F);
+  const long rows_total = (long)(f1 - f0) * U;
+  if ((long)blk * 128 >= rows_total) return;
+  long zlo, zhi;
+  live_rows(anchors, f0, f1, c, F, U, C, radius, rows_total, zlo, zhi);
+
+  const int t = threadIdx.x;
+  const int lane = t & 63;
+  const int w = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int h = lane >> 4;
+  const int jl = lane & 15;
+  const bool b3 = (lane >> 3) & 1;
+  const size_t chunk_row0 = ((size_t)u * F + f0) * U;
+  const uint16_t* Shi = S;
+  const uint16_t* Slo = S + 128 * kSRow;
+  // lane's row (within a 16-row group) and 16-byte chunk in load / store instruction i
+  auto row_in = [&](int i) { return 8 * (i >> 1) + (lane & 7); };
+  auto chunk_in = [&](int i) { return 8 * (i & 1) + (lane >> 3); };
+  auto load16 = [&](u32x4_t (&X)[4], const uint16_t* base, long rg) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const long r = min(rg + row_in(i), rows_total - 1);  // clamped: never stored
+      X[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(
+          base + (chunk_row0 + (size_t)r) * 128 + 8 * chunk_in(i)));
+    }
+  };
+  auto grp_row = [&](int it) { return ((long)it * nblk + blk) * 128 + (long)w * 16; };
+
+  // S~ image -> LDS by DMA, then the first group's q and gate
+  {
+    const char* src = reinterpret_cast<const char*>(Sp + ((size_t)u * n + c) * (kSplitBytes / 2));
+    char* dst = reinterpret_cast<char*>(S);
+    for (int j = w; j < kSplitBytes / 1024; j += 8)
+      __builtin_amdgcn_global_load_lds(
+          static_cast<const void*>(src + (size_t)j * 1024 + lane * 16),
+          (void __attribute__((address_space(3)))*)(dst + j * 1024), 16, 0, 0);
+  }
+  if (t < 128) Ws[t] = wrms[t];
+  u32x4_t q0[4], q1[4], gr[4];
+  load16(q0, q, grp_row(0));
+  load16(gr, gate, grp_row(0));
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the DMA into LDS has landed
+  __syncthreads();
+
+  auto process = [&](u32x4_t (&qr)[4], u32x4_t (&g)[4], long rg) {
+    c128_exchange(qr, b3);
+    f32x4_t acc[8];
+#pragma unroll
+    for (int T = 0; T < 8; ++T) acc[T] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const int col = 8 * c128_chunk(s, h);
+#pragma unroll
+      for (int T = 0; T < 8; ++T) {
+        const int off = (16 * T + jl) * kSRow + col;
+        const u32x4_t ah = *reinterpret_cast<const u32x4_t*>(Shi + off);
+        const u32x4_t al = *reinterpret_cast<const u32x4_t*>(Slo + off);
+        acc[T] = mfma16_bf16(ah, qr[s], acc[T]);
+        acc[T] = mfma16_bf16(al, qr[s], acc[T]);
+      }
+    }
+    c128_exchange(g, b3);
+    float ss = 0.0f;
+#pragma unroll
+    for (int T = 0; T < 8; ++T)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) ss = fmaf(acc[T][r], acc[T][r], ss);
+    ss += __shfl_xor(ss, 16);
+    ss += __shfl_xor(ss, 32);
+    const float inv = rsqrtf(ss * (1.0f / 128.0f) + eps);
+    const long myrow = rg + jl;
+    const bool live = myrow >= zlo && myrow < zhi;
+    u32x4_t ov[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const int ch = 8 * c128_chunk(m, h);
+      const f32x4_t w0 = *reinterpret_cast<const f32x4_t*>(Ws + ch);
+      const f32x4_t w1 = *reinterpret_cast<const f32x4_t*>(Ws + ch + 4);
+      const u32x4_t gv = g[m];
+      float y[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float o = acc[2 * m + (e >> 2)][e & 3];
+        const float gl = (e & 1) ? bf16_hi(gv[e >> 1]) : bf16_lo(gv[e >> 1]);
+        const float ww = e < 4 ? w0[e] : w1[e - 4];
+        const float sig = __builtin_amdgcn_rcpf(1.0f + __expf(-gl));
+        y[e] = live ? o * inv * ww * sig : 0.0f;
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) ov[m][e] = pack_bf16(y[2 * e], y[2 * e + 1]);
+    }
+    c128_exchange(ov, b3);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const long r = rg + row_in(i);
+      if (r < rows_total)
+        __builtin_nontemporal_store(ov[i], reinterpret_cast<u32x4_t*>(
+            out + (chunk_row0 + (size_t)r) * 128 + 8 * chunk_in(i)));
+    }
+  };
+
+  // two groups per wave: q of the second is fetched before the first is processed
+  if (grp_row(0) >= rows_total) return;
+  load16(q1, q, grp_row(1));
+  process(q0, gr, grp_row(0));
+  if (grp_row(1) >= rows_total) return;
+  load16(gr, gate, grp_row(1));
+  process(q1, gr, grp_row(1));
+}
+
 // fp32 features: 64 token rows per workgroup, S~ and the rows' queries in LDS.
 // Work item (unit, segment, row block) on a 1-D grid, segments as in the bf16
 // path (a frame with decay, given by alpha != nullptr; else a chunk).
@@ -427,9 +644,17 @@ hipError_t launch_readout(const Plan& p, const void* q, const void* gate, const 
     if (alpha)
       d128 ? launch_readout_bf16<128, 128, true>(p, q, gate, rms_weight, out, w, alpha, nseg, nblk, s)
            : launch_readout_bf16<0, 0, true>(p, q, gate, rms_weight, out, w, alpha, nseg, nblk, s);
-    else
-      d128 ? launch_readout_bf16<128, 128, false>(p, q, gate, rms_weight, out, w, alpha, nseg, nblk, s)
-           : launch_readout_bf16<0, 0, false>(p, q, gate, rms_weight, out, w, alpha, nseg, nblk, s);
+    else if (d128) {
+      hipLaunchKernelGGL(split_states_kernel, dim3(p.n, p.units), dim3(kThreads), 0, s, w.ST,
+                         w.Sp, p.n, p.r);
+      const int nb = (int)((max_rows + kRowsC - 1) / kRowsC);
+      const unsigned per = xcd_per((unsigned)p.units * p.n * nb);
+      hipLaunchKernelGGL(readout_c128_kernel, dim3(kXcds * per), dim3(kThreadsR), 0, s,
+                         static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(gate),
+                         rms_weight, static_cast<uint16_t*>(out), w.Sp, p.F, p.U, p.C, p.r, p.n,
+                         p.eps, p.units, nb, per, p.anchors);
+    } else
+      launch_readout_bf16<0, 0, false>(p, q, gate, rms_weight, out, w, alpha, nseg, nblk, s);
   } else {
     const int nblk = (int)((max_rows + kRowsF - 1) / kRowsF);
     const unsigned items = (unsigned)p.units * nseg * nblk;

@@ -94,7 +94,7 @@ int make_plan(const vda_desc_t* d, Plan* p) {
 
   const size_t U_ = (size_t)p->units, Fp1 = (size_t)p->F + 1, N = (size_t)p->n;
   const size_t kk = (size_t)p->dk * p->dk * 4, vk = (size_t)p->dv * p->dk * 4;
-  size_t sz[9];
+  size_t sz[10];
   sz[0] = U_ * Fp1 * kk;          // A
   sz[1] = U_ * Fp1 * vk;          // B
   sz[2] = U_ * Fp1 * kk;          // M
@@ -104,10 +104,13 @@ int make_plan(const vda_desc_t* d, Plan* p) {
   sz[6] = U_ * 2 * (N + 1) * vk;  // ST
   sz[7] = U_ * N * kk;            // McT
   sz[8] = U_ * N * kk;            // MrT
+  sz[9] = (p->dtype == VDA_DTYPE_BF16 && p->dk == 128 && p->dv == 128)
+              ? U_ * N * (size_t)(2 * 128 * 136 * 2)
+              : 0;                  // Sp: split S~ images of the bf16 d = 128 readout
   if (p->units == 0 || p->F == 0)
     for (size_t& s : sz) s = 0;
   size_t off = 0;
-  for (int i = 0; i < 9; ++i) {
+  for (int i = 0; i < 10; ++i) {
     p->off[i] = off;
     off += align256(sz[i]);
   }
@@ -127,6 +130,7 @@ WsPtrs carve(const Plan& p, void* ws) {
   w.ST = reinterpret_cast<float*>(b + p.off[6]);
   w.McT = reinterpret_cast<float*>(b + p.off[7]);
   w.MrT = reinterpret_cast<float*>(b + p.off[8]);
+  w.Sp = reinterpret_cast<uint16_t*>(b + p.off[9]);
   return w;
 }
 

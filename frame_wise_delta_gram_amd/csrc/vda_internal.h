@@ -20,6 +20,8 @@ namespace vda {
 //   ST [units][2][n + 1][d_v][d_k] boundary states: [0] = P (forward), [1] = R (reverse)
 //   MrT [units][n][d_k][d_k]      reverse chunk transitions, transposed (decay only;
 //                                 without decay the reverse transition is Mc^T)
+//   Sp [units][n][69632 bytes]    bf16 features with d_k = d_v = 128: each chunk's gathered
+//                                 state S~ split into bf16 hi + lo in the readout's LDS image
 struct Plan {
   int units, F, U, T, dk, dv, C, r, n;
   float eps;
@@ -31,7 +33,7 @@ struct Plan {
   bool decay_ok;  // the decay path's launch grids fit too
   bool full_stats;  // store both triangles of every A_t (else the lower 32 x 32 blocks
                    // of latent frames only: all the frame-wise solve reads)
-  size_t off[9];
+  size_t off[10];
   size_t total;
 };
 
@@ -46,6 +48,7 @@ hipError_t launch_prep(const PrepPlan& p, const void* q, const void* k, const vo
 
 struct WsPtrs {
   float *A, *B, *M, *Mc, *Jf, *Jr, *ST, *McT, *MrT;
+  uint16_t* Sp;  // bf16 readout with d_k = d_v = 128: per (unit, chunk) the split S~ image
 };
 
 hipError_t launch_stats(const Plan& p, const void* k, const void* v, const float* beta,

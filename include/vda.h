@@ -141,7 +141,9 @@ typedef struct vda_desc {
 } vda_desc_t;
 
 /* Bytes of device workspace vda_forward and the debug taps need for `desc`
- * (fp32 frame statistics, transitions, chunk maps and boundary states).
+ * (fp32 frame statistics, transitions, chunk maps and boundary states; with bf16
+ * features and d_k = d_v = 128 also each chunk's gathered readout state split into
+ * bf16 high and low parts, 69632 bytes per (unit, chunk)).
  * Returns 0 when desc is NULL or invalid. Host-only; never touches the GPU. */
 size_t vda_workspace_bytes(const vda_desc_t* desc);
 

@@ -125,6 +125,14 @@ def test_workspace_formula(lib):
               + a(units * 2 * (n + 1) * dv * dk * 4) + a(units * n * dk * dk * 4)
               + a(units * n * dk * dk * 4))  # Mc^T and the reverse transitions (decay)
     assert vda.vda_workspace_bytes(d) == expect
+    # bf16 with d_k = d_v = 128 adds the readout's split S~ images (69632 bytes per chunk)
+    d128 = desc(d_k=128, d_v=128)
+    kk = 128 * 128 * 4
+    expect128 = (a(units * Fp1 * kk) * 3 + a(units * n * kk) * 3 + 2 * a(units * n * kk)
+                 + a(units * 2 * (n + 1) * kk) + a(units * n * 2 * 128 * 136 * 2))
+    assert vda.vda_workspace_bytes(d128) == expect128
+    assert vda.vda_workspace_bytes(desc(d_k=128, d_v=128, dtype=vda.VDA_DTYPE_F32)) == \
+        expect128 - a(units * n * 2 * 128 * 136 * 2)
     assert vda.vda_workspace_bytes(desc(units=0)) == 0
     assert vda.vda_workspace_bytes(desc(frames=0)) == 0
     assert vda.vda_workspace_bytes(desc(d_k=12)) == 0  # invalid -> 0
