@@ -68,8 +68,12 @@ def algorithmic(cfg):
     a_frac = 1.0 if cfg.rule != 0 else nkb * (nkb + 1) / 2 / (nkb * nkb)
     stats_bytes = th * ((dk + dv) * eb + 4) + u * F * (a_frac * dk + dv) * dk * 4
     text_bytes = tt * ((dk + dv) * eb + 4) + u * (dk + dv) * dk * 4
+    split = cfg.dtype == "bf16" and dk == 128 and dv == 128 and cfg.alpha_mu is None
+    image = 2 * 128 * 136 * 2                        # one chunk's split S~ (bf16 hi + lo)
     readout_bytes = (th * (dk + 2 * dv) * eb                           # q, gate read; out written
-                     + u * n * 2 * st + dv * 4 + gates)                 # two states per chunk
+                     + (u * n * image if split else u * n * 2 * st)     # the chunk's state(s)
+                     + dv * 4 + gates)
+    split_bytes = u * n * (2 * st + image) if split else 0             # P, R in; image out
     solve_bytes = (a_frac + 1) * u * (F + 1) * mat                     # A in, M out
     compose_bytes = (u * (F + 1) * (mat + st) + gates                  # M, B (and gates) in
                      + u * n * (nmaps * mat + 2 * st)                   # chunk maps out
@@ -83,18 +87,22 @@ def algorithmic(cfg):
             "stats_text": (text_bytes, text_flops),
             "readout": (readout_bytes, 2 * th * dk * dv),
             "solve": (solve_bytes, None), "compose": (compose_bytes, None),
-            "scan": (scan_bytes, None)}
+            "scan": (scan_bytes, None), "split": (split_bytes, None)}
 
 
 def stage_alg(alg, stage):
-    """(bytes, flops) of a timed stage: the statistics stage runs two kernels."""
+    """(bytes, flops) of a timed stage: the statistics stage runs two kernels, the
+    scan stage ends with the readout's state split."""
+    if stage == "scan":
+        return (alg["scan"][0] + alg["split"][0], None)
     if stage != "stats":
         return alg[stage]
     return (alg["stats"][0] + alg["stats_text"][0], alg["stats"][1] + alg["stats_text"][1])
 
 
+
 KERNEL_SOURCES = {"stats": "k_stats.hip", "stats_text": "k_stats.hip", "readout": "k_readout.hip",
-                  "solve": "k_solve.hip",
+                  "split": "k_readout.hip", "solve": "k_solve.hip",
                   "compose": "k_scan.hip", "scan": "k_scan.hip"}
 
 
@@ -139,7 +147,7 @@ PROFILE_COMMANDS = {  # CFG: the workload id
              "--decay-steps 0 --batched-steps 0 --prep-steps 0 --other-configs=",
 }
 TRACE_WARMUP, TRACE_STEPS = 50, 20  # of the kernel-trace command above
-KERNELS = ("stats_text", "stats", "solve", "compose", "scan", "readout")  # launch order
+KERNELS = ("stats_text", "stats", "solve", "compose", "scan", "split", "readout")  # launch order
 PREP_COMMAND = ("rocprofv3 {pmc} -d DIR/{sub} -o p --output-format csv -- python bench.py "
                 "--steps 1 --warmup 0 --cpu-seconds 0 --decay-steps 0 --batched-steps 0 "
                 "--prep-steps 5 --other-configs=")
@@ -147,7 +155,9 @@ PREP_KERNELS = ("prep",)  # one launch: the K and V sweeps, then the Q pass
 KERNEL_NAMES = {"stats_bf16_kernel": "stats", "stats_f32_kernel": "stats",
                 "stats_text_kernel": "stats_text",
                 "readout_bf16_kernel": "readout", "readout_f32_kernel": "readout",
+                "readout_c128_kernel": "readout", "split_states_kernel": "split",
                 "solve_kernel": "solve", "batched_factor_kernel": "solve",
+                "solve_chol_kernel": "solve",
                 "compose_split_kernel": "compose",
                 "compose_kernel": "compose", "scan_split_kernel": "scan", "scan_kernel": "scan"}
 
@@ -279,12 +289,15 @@ def summarize(prof_dir, cfg_id):
             k = short_kernel_name(r["Kernel_Name"])
             if k and k != "copy":
                 launches[k].append((int(r["Start_Timestamp"]), int(r["End_Timestamp"])))
-    timed = {}
+    timed, serial = {}, {}
     for k, v in launches.items():
         v.sort()
         sel = v[TRACE_WARMUP:TRACE_WARMUP + TRACE_STEPS]
         if sel:
             timed[k] = sum(e - b for b, e in sel) / len(sel) / 1e3
+        sel = v[TRACE_WARMUP + TRACE_STEPS:TRACE_WARMUP + 2 * TRACE_STEPS]
+        if sel:
+            serial[k] = sum(e - b for b, e in sel) / len(sel) / 1e3
     os.makedirs(PROFILES, exist_ok=True)
     order = [k for k in KERNELS if k in durations]
     head = (f"{cfg.name} workload ({cfg.units} heads x {cfg.frames} frames x {cfg.tokens} "
@@ -296,18 +309,21 @@ def summarize(prof_dir, cfg_id):
     lines += [f"    python bench.py --summarize DIR --config {cfg_id}", "",
               "## Kernel durations (`vda_kernel_stats.csv`, `vda_kernel_trace.csv`)", "",
               f"All calls: {TRACE_WARMUP} warm-up steps, {TRACE_STEPS} timed steps, "
-              f"{TRACE_STEPS} per-stage breakdown steps. Timed: the {TRACE_STEPS} launches of "
-              "the timed steps (the bench's own events time the same launches).", "",
+              f"{TRACE_STEPS} per-stage breakdown steps (one launch of each kernel per "
+              "step). Timed steps: vda_forward. Breakdown steps: vda_forward_timed, the "
+              "same launches with the bench's stage events between them.", "",
               "| kernel | calls | average, all calls (us) | min (us) | max (us) | "
-              "average, timed steps (us) | algorithmic GB/s (timed) |",
-              "|---|---|---|---|---|---|---|"]
+              "average, timed steps (us) | average, breakdown steps (us) | "
+              "algorithmic GB/s (breakdown) |",
+              "|---|---|---|---|---|---|---|---|"]
     for k in order:
         c, a, lo, hi = durations[k]
         tk = timed.get(k, a)
-        lines.append(f"| {k} | {c} | {a:.1f} | {lo:.1f} | {hi:.1f} | {tk:.1f} | "
-                     f"{alg[k][0] / (tk * 1e-6) / 1e9:.0f} |")
-    lines += ["", f"Sum of the timed-step averages: {sum(timed.get(k, durations[k][1]) for k in order):.1f} "
-              "us per forward step."]
+        sk = serial.get(k, a)
+        lines.append(f"| {k} | {c} | {a:.1f} | {lo:.1f} | {hi:.1f} | {tk:.1f} | {sk:.1f} | "
+                     f"{alg[k][0] / (sk * 1e-6) / 1e9:.0f} |")
+    lines += ["", "Sum of the breakdown-step averages: "
+              f"{sum(serial.get(k, durations[k][1]) for k in order):.1f} us per forward step."]
     mfma_path = os.path.join(prof_dir, "MFMA", "p_counter_collection.csv")
     if os.path.exists(mfma_path):
         # per dispatch: MOPS (x 512 flop), MFMA busy cycles summed over the SIMDs,
@@ -332,7 +348,7 @@ def summarize(prof_dir, cfg_id):
                 agg[kname[i]][name].append(val)
         lines += ["", "## MFMA counters per launch (`SQ_INSTS_VALU_MFMA_MOPS_*`)", "",
                   "Executed MFMA flops = MOPS x 512 (hi/lo splits execute more than the algorithmic "
-                  "flops); rates use the timed-step average duration; peaks: bf16 2516.6, fp32 matrix "
+                  "flops); rates use the breakdown-step average duration; peaks: bf16 2516.6, fp32 matrix "
                   "157.3 TFLOP/s.", "",
                   "| kernel | bf16 flops executed | fp32 flops executed | algorithmic bf16 flops | "
                   "executed bf16 TFLOP/s (% of peak) | executed fp32 TFLOP/s (% of peak) |",
@@ -342,7 +358,7 @@ def summarize(prof_dir, cfg_id):
                 continue
             m = {name: sum(v) / len(v) for name, v in agg[k].items()}
             algf = alg[k][1] if alg[k][1] is not None else 0
-            sec = timed.get(k, durations[k][1]) * 1e-6
+            sec = serial.get(k, durations[k][1]) * 1e-6
             fb = m.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", 0) * 512
             ff = m.get("SQ_INSTS_VALU_MFMA_MOPS_F32", 0) * 512
             lines.append(f"| {k} | {fb:.4g} | {ff:.4g} | {algf:.4g} | "
@@ -470,17 +486,15 @@ def state_growth(cfg, d):
 
 
 def time_steps(cfg, d, steps, warmup):
-    """Run the forward pass (vda_forward_timed; decay gates when d holds them)
-    on the current stream: `warmup` untimed steps, `steps` timed steps that
-    record only the two events around the readout, the dominant kernel (each
-    stream marker between kernels adds a few microseconds), then `steps` more
-    steps with all six stage events for the per-stage breakdown.  d is one
-    input set, or a list of input sets that the steps take in turn (step i
-    reads copy i mod len(d) and writes its own output: for workloads small
-    enough to stay in the 256 MB MALL, so that every step streams its inputs
-    from HBM).  Returns (seconds for the timed steps, dict of average ms: per
-    stage from the breakdown pass, "timed_readout" from the timed steps,
-    "timed_stats" from the breakdown pass, and the median / minimum of the
+    """Run the forward pass on the current stream: `warmup` untimed steps, then
+    `steps` timed steps of vda_forward (vda_forward_decay when d holds decay
+    gates), then `steps` more steps of vda_forward_timed, the same launches with
+    all six stage events between them, for the per-stage breakdown.  d is one input set, or a list of input sets that the steps take
+    in turn (step i reads copy i mod len(d) and writes its own output: for
+    workloads small enough to stay in the 256 MB MALL, so that every step
+    streams its inputs from HBM).  Returns (seconds for the timed steps, dict of
+    average ms: per stage from the breakdown pass, "timed_readout" and
+    "timed_stats" the same two stages, and the median / minimum of the
     breakdown pass's per-step totals)."""
     import torch
     import frame_wise_delta_gram_amd as vda
@@ -518,19 +532,25 @@ def time_steps(cfg, d, steps, warmup):
             raise RuntimeError("hipEventElapsedTime failed")
         return ms.value
 
-    # events 4 / 5 bracket the readout
-    timed_row = lambda i: [e if j in (4, 5) else None for j, e in enumerate(events[i])]
+    def forward(args):  # the untimed entry point (decay gates: vda_forward_decay)
+        desc_, q, k, v, beta, alpha, gate, tk, tv, tb, w, out, ws_ = args
+        if alpha is None:
+            vda.vda_forward(desc_, q, k, v, beta, gate, tk, tv, tb, w, out, ws_, stream=stream)
+        else:
+            vda.vda_forward_decay(desc_, q, k, v, beta, alpha, gate, tk, tv, tb, w, out, ws_,
+                                  stream=stream)
+
     log(f"[bench] {cfg.name}: warmup {warmup}")
     for i in range(warmup):
-        vda.vda_forward_timed(*fws[i % len(fws)], timed_row(i % len(events)), stream=stream)
+        forward(fws[i % len(fws)])
     torch.cuda.synchronize()
     log(f"[bench] {cfg.name}: timing {steps} steps")
     t0 = time.perf_counter()
     for i in range(steps):
-        vda.vda_forward_timed(*fws[i % len(fws)], timed_row(i), stream=stream)
+        forward(fws[i % len(fws)])
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    avg = {"timed_readout": sum(elapsed_ms(events[i], 4, 5) for i in range(steps)) / steps}
+    avg = {}
 
     log(f"[bench] {cfg.name}: per-stage breakdown over {steps} more steps")
     for i in range(steps):
@@ -544,6 +564,7 @@ def time_steps(cfg, d, steps, warmup):
     per_step = sorted(sum(stage_ms[s][i] for s in STAGES) for i in range(steps))
     avg.update({s: sum(v) / len(v) for s, v in stage_ms.items()})
     avg["timed_stats"] = avg["stats"]
+    avg["timed_readout"] = avg["readout"]
     avg["step_events_median"] = per_step[len(per_step) // 2]
     avg["step_events_min"] = per_step[0]
     return elapsed, avg
@@ -557,8 +578,8 @@ def split_steps(avg_ms):
 
 def roofline_of(cfg, avg_ms):
     """Roofline of the dominant HBM-bound kernel (statistics or readout), with
-    its average launch duration from events (the readout's recorded in the
-    timed steps, the statistics' in the breakdown pass)."""
+    its average launch duration from the breakdown pass's stage events (one
+    launch per stage)."""
     alg = algorithmic(cfg)
     dominant = max(("stats", "readout"), key=lambda s: avg_ms["timed_" + s])
     ms = avg_ms["timed_" + dominant]

@@ -349,6 +349,7 @@ __global__ __launch_bounds__(512, 4) void readout_bf16_kernel(
 // 8 rows x 128 B stores.
 constexpr int kSRow = 136;                      // bf16 per LDS row of S~ (17 x 16 bytes)
 constexpr int kSplitBytes = 2 * 128 * kSRow * 2;  // hi + lo image of one chunk's S~
+static_assert(kSplitBytes == 2 * kSplitElems, "split image size");
 
 // chunk of 8 channels held in output register s by lane group h
 __device__ __forceinline__ int c128_chunk(int s, int h) { return 8 * (s & 1) + 2 * h + (s >> 1); }
@@ -632,6 +633,14 @@ void launch_readout_bf16(const Plan& p, const void* q, const void* gate, const f
                      p.C, p.r, p.n, p.eps, p.units, nseg, nblk, per, p.anchors);
 }
 
+hipError_t launch_split(const Plan& p, const WsPtrs& w, bool decay, hipStream_t s) {
+  if (decay || !split_readout(p.dtype, p.dk, p.dv) || p.units == 0 || p.n == 0 || p.U == 0)
+    return hipSuccess;
+  hipLaunchKernelGGL(split_states_kernel, dim3(p.n, p.units), dim3(kThreads), 0, s, w.ST, w.Sp,
+                     p.n, p.r);
+  return hipGetLastError();
+}
+
 hipError_t launch_readout(const Plan& p, const void* q, const void* gate, const float* rms_weight,
                           void* out, const WsPtrs& w, const float* alpha, hipStream_t s) {
   // segments: frames with decay (each frame reads its own bridged state), else chunks
@@ -644,9 +653,7 @@ hipError_t launch_readout(const Plan& p, const void* q, const void* gate, const 
     if (alpha)
       d128 ? launch_readout_bf16<128, 128, true>(p, q, gate, rms_weight, out, w, alpha, nseg, nblk, s)
            : launch_readout_bf16<0, 0, true>(p, q, gate, rms_weight, out, w, alpha, nseg, nblk, s);
-    else if (d128) {
-      hipLaunchKernelGGL(split_states_kernel, dim3(p.n, p.units), dim3(kThreads), 0, s, w.ST,
-                         w.Sp, p.n, p.r);
+    else if (d128) {  // Sp was written by launch_split after the scans
       const int nb = (int)((max_rows + kRowsC - 1) / kRowsC);
       const unsigned per = xcd_per((unsigned)p.units * p.n * nb);
       hipLaunchKernelGGL(readout_c128_kernel, dim3(kXcds * per), dim3(kThreadsR), 0, s,

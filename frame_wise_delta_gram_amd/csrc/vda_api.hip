@@ -104,9 +104,7 @@ int make_plan(const vda_desc_t* d, Plan* p) {
   sz[6] = U_ * 2 * (N + 1) * vk;  // ST
   sz[7] = U_ * N * kk;            // McT
   sz[8] = U_ * N * kk;            // MrT
-  sz[9] = (p->dtype == VDA_DTYPE_BF16 && p->dk == 128 && p->dv == 128)
-              ? U_ * N * (size_t)(2 * 128 * 136 * 2)
-              : 0;                  // Sp: split S~ images of the bf16 d = 128 readout
+  sz[9] = split_readout(p->dtype, p->dk, p->dv) ? U_ * N * kSplitElems * 2 : 0;  // Sp
   if (p->units == 0 || p->F == 0)
     for (size_t& s : sz) s = 0;
   size_t off = 0;
@@ -178,8 +176,9 @@ int check_readout_tensors(const Plan& p, const void* q, const void* gate, const 
 
 int hip_status(hipError_t e) { return e == hipSuccess ? VDA_OK : VDA_ERR_HIP; }
 
-// stages: 1 stats, 2 solve, 3 compose, 4 scan.  alpha (optional): decay
-// gates.  events (optional): recorded before each launched stage.
+// stages: 1 stats, 2 solve, 3 compose, 4 scan (and the readout's split
+// states).  alpha (optional): decay gates.  events (optional): recorded before
+// each launched stage.
 int run_states(const Plan& p, const void* k, const void* v, const float* beta, const void* tk,
                const void* tv, const float* tb, const WsPtrs& w, hipStream_t s, int upto,
                const float* alpha = nullptr, hipEvent_t const* ev = nullptr) {
@@ -194,7 +193,8 @@ int run_states(const Plan& p, const void* k, const void* v, const float* beta, c
   if (upto >= 2 && (rec(1) != hipSuccess || launch_solve(p, w, s) != hipSuccess)) return VDA_ERR_HIP;
   if (upto >= 3 && (rec(2) != hipSuccess || launch_compose(p, w, alpha, s) != hipSuccess))
     return VDA_ERR_HIP;
-  if (upto >= 4 && (rec(3) != hipSuccess || launch_scan(p, w, alpha != nullptr, s) != hipSuccess))
+  if (upto >= 4 && (rec(3) != hipSuccess || launch_scan(p, w, alpha != nullptr, s) != hipSuccess ||
+                    launch_split(p, w, alpha != nullptr, s) != hipSuccess))
     return VDA_ERR_HIP;
   return VDA_OK;
 }

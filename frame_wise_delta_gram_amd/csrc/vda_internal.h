@@ -9,7 +9,7 @@
 namespace vda {
 
 // Sizes derived from a validated descriptor, and the workspace carve-up.
-// Workspace sections (all fp32, each 256-byte aligned):
+// Workspace sections (fp32 but Sp, each 256-byte aligned):
 //   A  [units][F + 1][d_k][d_k]   frame statistics, index 0 = text frame
 //   B  [units][F + 1][d_v][d_k]
 //   M  [units][F + 1][d_k][d_k]   transitions (I + A)^{-1}
@@ -46,6 +46,13 @@ hipError_t launch_prep(const PrepPlan& p, const void* q, const void* k, const vo
                        const float* wk_s, const float* wk_t, const float* wv_s, const float* wv_t,
                        void* qo, void* ko, void* vo, hipStream_t s);
 
+// bf16 elements of one (unit, chunk) image in Sp: hi and lo, 128 rows of 136 each
+constexpr size_t kSplitElems = 2 * 128 * 136;
+// the bf16 readout with d_k = d_v = 128 (no decay) reads Sp
+inline bool split_readout(int dtype, int dk, int dv) {
+  return dtype == VDA_DTYPE_BF16 && dk == 128 && dv == 128;
+}
+
 struct WsPtrs {
   float *A, *B, *M, *Mc, *Jf, *Jr, *ST, *McT, *MrT;
   uint16_t* Sp;  // bf16 readout with d_k = d_v = 128: per (unit, chunk) the split S~ image
@@ -59,6 +66,8 @@ hipError_t launch_solve(const Plan& p, const WsPtrs& w, hipStream_t s);
 hipError_t launch_compose(const Plan& p, const WsPtrs& w, const float* alpha,
                           hipStream_t s);  // Mc, McT, Jf, Jr (+ MrT with decay), seeds
 hipError_t launch_scan(const Plan& p, const WsPtrs& w, bool decay, hipStream_t s);
+// Sp from ST when the readout reads it (split_readout, no decay); else nothing
+hipError_t launch_split(const Plan& p, const WsPtrs& w, bool decay, hipStream_t s);
 hipError_t launch_readout(const Plan& p, const void* q, const void* gate, const float* rms_weight,
                           void* out, const WsPtrs& w, const float* alpha, hipStream_t s);
 

@@ -12,7 +12,7 @@ import pytest
 
 import workloads as W
 from gpu_helpers import (TOL_OUT, device_to_host_f64, gpu_forward, oracle_forward, out_to_f64,
-                         require_gpu, row_rel_err, say)
+                         require_gpu, row_rel_err, say, timed_forward_matches)
 
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
 
@@ -42,6 +42,8 @@ def test_fullsize_every_unit(cfg_id):
     out2 = gpu_forward(d, cfg)
     assert torch.equal(out.view(torch.int16), out2.view(torch.int16)), "not deterministic"
     del out2
+    # the overlapped schedule (two unit groups) against the stage-by-stage one
+    assert timed_forward_matches(d, cfg)
     say(f"[fullsize] {cfg.name}: oracle on all {cfg.units} units")
     err = check_every_unit(d, cfg, out)
     say(f"[fullsize] {cfg.name}: max row-rel err over every unit {err:.3e}")
