@@ -128,29 +128,37 @@ def measured_traffic(kernel, workload):
     return rec.get("hbm_bytes_per_launch")
 
 
+# occupancy, vector ALU and LDS counters of one pass (8 SQ + 1 GRBM counters)
+XCDS = 8  # accelerator complex dies of an MI355X (one GRBM instance each)
+SQ_COUNTERS = ("SQ_WAVES SQ_WAVE_CYCLES SQ_BUSY_CYCLES SQ_ACTIVE_INST_VALU SQ_INSTS_VALU "
+               "SQ_INSTS_LDS SQ_LDS_BANK_CONFLICT SQ_WAIT_INST_LDS GRBM_GUI_ACTIVE")
 PROFILE_COMMANDS = {  # CFG: the workload id
     "FETCH_SIZE": "timeout -s KILL 120 rocprofv3 --pmc FETCH_SIZE --kernel-include-regex "
                   "'vda|add' -d DIR/FETCH_SIZE -o p --output-format csv -- python bench.py "
                   "--config CFG --steps 2 --warmup 1 --cpu-seconds 0 --decay-steps 0 "
-                  "--batched-steps 0 --prep-steps 0 --other-configs=",
+                  "--batched-steps 0 --prep-steps 0 --variant-steps 0 --other-configs=",
     "WRITE_SIZE": "timeout -s KILL 120 rocprofv3 --pmc WRITE_SIZE --kernel-include-regex "
                   "'vda|add' -d DIR/WRITE_SIZE -o p --output-format csv -- python bench.py "
                   "--config CFG --steps 2 --warmup 1 --cpu-seconds 0 --decay-steps 0 "
-                  "--batched-steps 0 --prep-steps 0 --other-configs=",
+                  "--batched-steps 0 --prep-steps 0 --variant-steps 0 --other-configs=",
     "MFMA": "timeout -s KILL 120 rocprofv3 --pmc SQ_INSTS_VALU_MFMA_MOPS_BF16 "
             "SQ_INSTS_VALU_MFMA_MOPS_F32 SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE "
             "--kernel-include-regex vda -d DIR/MFMA -o p --output-format csv -- python bench.py "
             "--config CFG --steps 2 --warmup 1 --cpu-seconds 0 --decay-steps 0 "
-            "--batched-steps 0 --prep-steps 0 --other-configs=",
+            "--batched-steps 0 --prep-steps 0 --variant-steps 0 --other-configs=",
+    "OCC": "timeout -s KILL 120 rocprofv3 --pmc " + SQ_COUNTERS + " "
+           "--kernel-include-regex vda -d DIR/OCC -o p --output-format csv -- python bench.py "
+           "--config CFG --steps 2 --warmup 1 --cpu-seconds 0 --decay-steps 0 "
+           "--batched-steps 0 --prep-steps 0 --variant-steps 0 --other-configs=",
     "stats": "rocprofv3 --kernel-trace --stats -d DIR/trace -o vda --output-format csv -- "
              "python bench.py --config CFG --steps 20 --warmup 50 --cpu-seconds 0 "
-             "--decay-steps 0 --batched-steps 0 --prep-steps 0 --other-configs=",
+             "--decay-steps 0 --batched-steps 0 --prep-steps 0 --variant-steps 0 --other-configs=",
 }
 TRACE_WARMUP, TRACE_STEPS = 50, 20  # of the kernel-trace command above
 KERNELS = ("stats_text", "stats", "solve", "compose", "scan", "split", "readout")  # launch order
 PREP_COMMAND = ("rocprofv3 {pmc} -d DIR/{sub} -o p --output-format csv -- python bench.py "
                 "--steps 1 --warmup 0 --cpu-seconds 0 --decay-steps 0 --batched-steps 0 "
-                "--prep-steps 5 --other-configs=")
+                "--prep-steps 5 --variant-steps 0 --other-configs=")
 PREP_KERNELS = ("prep",)  # one launch: the K and V sweeps, then the Q pass
 KERNEL_NAMES = {"stats_bf16_kernel": "stats", "stats_f32_kernel": "stats",
                 "stats_text_kernel": "stats_text",
@@ -170,6 +178,65 @@ def short_kernel_name(full):
             return "prep"
         return KERNEL_NAMES.get(m.group(1), m.group(1))
     return "copy" if "add" in full.lower() else None
+
+
+def sq_table(path, order):
+    """Markdown lines of the SQ_COUNTERS pass at `path` (empty when absent):
+    per kernel, occupancy, vector ALU activity and LDS figures per launch."""
+    import collections
+    import csv
+    if not os.path.exists(path):
+        return []
+    ctr = collections.defaultdict(lambda: collections.defaultdict(float))
+    kname = {}
+    gui_rows = collections.Counter()
+    with open(path) as fh:
+        for r in csv.DictReader(fh):
+            k = short_kernel_name(r["Kernel_Name"])
+            if k is None or k == "copy":
+                continue
+            i = int(r["Dispatch_Id"])
+            kname[i] = k
+            if r["Counter_Name"] == "GRBM_GUI_ACTIVE":
+                gui_rows[i] += 1
+                ctr[i]["GRBM_GUI_ACTIVE"] = max(ctr[i]["GRBM_GUI_ACTIVE"], float(r["Counter_Value"]))
+            else:
+                ctr[i][r["Counter_Name"]] += float(r["Counter_Value"])
+    for i, n in gui_rows.items():
+        if n == 1:  # one row: the sum over the XCDs' GRBM instances; per XCD = sum / 8
+            ctr[i]["GRBM_GUI_ACTIVE"] /= XCDS
+    agg = collections.defaultdict(lambda: collections.defaultdict(list))
+    for i, c in ctr.items():
+        for name, val in c.items():
+            agg[kname[i]][name].append(val)
+    lines = ["", "## Occupancy, vector ALU and LDS per launch (`SQ_WAVE_CYCLES`, "
+             "`SQ_ACTIVE_INST_VALU`, `SQ_LDS_BANK_CONFLICT`, ...)", "",
+             "Occupancy = 400 x SQ_WAVE_CYCLES (quad-cycles) / GRBM_GUI_ACTIVE / 256 CUs / 32 "
+             "wave slots per CU (rocprofv3's OccupancyPercent; GRBM_GUI_ACTIVE of one XCD, the "
+             "per-dispatch value rocprofv3 writes being the sum over the 8 XCDs): the mean share of the wave "
+             "slots holding a wave over the launch; mean waves per CU = that x 32. VALU active "
+             "= SQ_ACTIVE_INST_VALU / SQ_WAVE_CYCLES (share of resident wave-cycles issuing "
+             "vector ALU work). VALU instructions per wave = SQ_INSTS_VALU / SQ_WAVES. LDS "
+             "conflict = SQ_LDS_BANK_CONFLICT cycles per LDS instruction; LDS wait = "
+             "SQ_WAIT_INST_LDS / SQ_WAVE_CYCLES.", "",
+             "| kernel | waves | occupancy | mean waves per CU | VALU active | VALU instructions "
+             "per wave | LDS instructions | LDS conflict cycles per instruction | LDS wait |",
+             "|---|---|---|---|---|---|---|---|---|"]
+    for k in order:
+        if k not in agg:
+            continue
+        m = {name: sum(v) / len(v) for name, v in agg[k].items()}
+        gui = max(m.get("GRBM_GUI_ACTIVE", 0.0), 1.0)
+        wc = max(m.get("SQ_WAVE_CYCLES", 0.0), 1.0)
+        waves = max(m.get("SQ_WAVES", 0.0), 1.0)
+        occ = 400.0 * wc / gui / 256 / 32
+        lds = m.get("SQ_INSTS_LDS", 0.0)
+        conf = m.get("SQ_LDS_BANK_CONFLICT", 0.0) / lds if lds else 0.0
+        lines.append(f"| {k} | {waves:.0f} | {occ:.1f}% | {occ / 100 * 32:.1f} | "
+                     f"{100 * m.get('SQ_ACTIVE_INST_VALU', 0.0) / wc:.1f}% | "
+                     f"{m.get('SQ_INSTS_VALU', 0.0) / waves:.0f} | {lds:.4g} | {conf:.2f} | "
+                     f"{100 * m.get('SQ_WAIT_INST_LDS', 0.0) / wc:.1f}% |")
+    return lines
 
 
 def summarize_prep(prep_dir):
@@ -217,6 +284,7 @@ def summarize_prep(prep_dir):
     cmds = [PREP_COMMAND.format(pmc="--kernel-trace --stats", sub="trace"),
             "timeout -s KILL 120 " + PREP_COMMAND.format(pmc="--pmc FETCH_SIZE", sub="FETCH_SIZE"),
             "timeout -s KILL 120 " + PREP_COMMAND.format(pmc="--pmc WRITE_SIZE", sub="WRITE_SIZE"),
+            "timeout -s KILL 120 " + PREP_COMMAND.format(pmc="--pmc " + SQ_COUNTERS, sub="SQ"),
             "python bench.py --summarize-prep DIR"]
     lines = [f"# Feature-map kernels (vda_prep), {cfg.name} ({cfg.batch} x {cfg.heads} heads, "
              f"{cfg.frames} frames of {cfg.height} x {cfg.width} tokens, d_k = {cfg.d_k}, "
@@ -237,6 +305,7 @@ def summarize_prep(prep_dir):
                      f"{(rb + wb) / alg[k]:.3f} |")
     lines += ["", f"Counter scale factors (torch.add calibration in the same runs): FETCH x "
               f"{scale['FETCH_SIZE']:.3f}, WRITE x {scale['WRITE_SIZE']:.3f}."]
+    lines += sq_table(os.path.join(prep_dir, "SQ", "p_counter_collection.csv"), PREP_KERNELS)
     os.makedirs(PROFILES, exist_ok=True)
     with open(os.path.join(PROFILES, f"prep_kernels_{cfg.name}.md"), "w") as fh:
         fh.write("\n".join(lines) + "\n")
@@ -305,7 +374,7 @@ def summarize(prof_dir, cfg_id):
     lines = [f"# VDA forward kernels, {head}", "",
              "Commands (from the repository root, on one MI355X; DIR = an output folder):", ""]
     cmd = {c: PROFILE_COMMANDS[c].replace("CFG", str(cfg_id)) for c in PROFILE_COMMANDS}
-    lines += [f"    {cmd[c]}" for c in ("stats", "FETCH_SIZE", "WRITE_SIZE", "MFMA")]
+    lines += [f"    {cmd[c]}" for c in ("stats", "FETCH_SIZE", "WRITE_SIZE", "MFMA", "OCC")]
     lines += [f"    python bench.py --summarize DIR --config {cfg_id}", "",
               "## Kernel durations (`vda_kernel_stats.csv`, `vda_kernel_trace.csv`)", "",
               f"All calls: {TRACE_WARMUP} warm-up steps, {TRACE_STEPS} timed steps, "
@@ -364,6 +433,7 @@ def summarize(prof_dir, cfg_id):
             lines.append(f"| {k} | {fb:.4g} | {ff:.4g} | {algf:.4g} | "
                          f"{fb / sec / 1e12:.0f} ({100 * fb / sec / BF16_PEAK:.1f}%) | "
                          f"{ff / sec / 1e12:.1f} ({100 * ff / sec / 157.3e12:.1f}%) |")
+    lines += sq_table(os.path.join(prof_dir, "OCC", "p_counter_collection.csv"), order)
     lines += ["", "## HBM traffic per launch (`FETCH_SIZE`, `WRITE_SIZE`)", "",
               f"Scale factors from torch.add over two {copy_bytes} B tensors into a third: "
               f"FETCH x {scale['FETCH_SIZE']:.3f}, WRITE x {scale['WRITE_SIZE']:.3f} "
