@@ -22,13 +22,15 @@ VDA_ERR_WORKSPACE_TOO_SMALL = -3
 VDA_ERR_MISALIGNED = -4
 VDA_ERR_HIP = -5
 VDA_ERR_SCRATCH_TOO_SMALL = -6
+VDA_ERR_NOT_SPD = -7
 VDA_NOALLOC_MAX_BYTES = 64 << 20  # the fixed scratch of vda_forward_noalloc
 VDA_DTYPE_F32 = 0
 VDA_DTYPE_BF16 = 1
 
 EXPORTED = ("vda_workspace_bytes", "vda_check_desc", "vda_forward", "vda_forward_noalloc",
             "vda_forward_timed",
-            "vda_forward_decay", "vda_debug_stats", "vda_debug_solve", "vda_debug_chunks",
+            "vda_forward_decay", "vda_debug_stats", "vda_debug_solve", "vda_debug_frame_maps",
+            "vda_debug_chunks",
             "vda_debug_chunks_decay", "vda_debug_states", "vda_debug_states_decay",
             "vda_prep", "vda_prep_check_desc", "vda_status_string")
 
@@ -103,6 +105,8 @@ def load_library(path: str = LIB_PATH):
     lib.vda_debug_stats.restype = ctypes.c_int
     lib.vda_debug_solve.argtypes = [D] + [P] * 9 + [ctypes.c_size_t, P]
     lib.vda_debug_solve.restype = ctypes.c_int
+    lib.vda_debug_frame_maps.argtypes = [D] + [P] * 10 + [ctypes.c_size_t, P]
+    lib.vda_debug_frame_maps.restype = ctypes.c_int
     lib.vda_debug_chunks.argtypes = [D] + [P] * 10 + [ctypes.c_size_t, P]
     lib.vda_debug_chunks.restype = ctypes.c_int
     lib.vda_debug_states.argtypes = [D] + [P] * 9 + [ctypes.c_size_t, P]
@@ -230,6 +234,18 @@ def vda_debug_solve(desc, k, v, beta, text_k, text_v, text_beta, M_out, seed_out
         _ptr(text_beta), _ptr(M_out), _ptr(seed_out), _ptr(workspace),
         _ws_bytes(workspace, workspace_bytes), _stream(stream))
     _check(st, "vda_debug_solve")
+
+
+def vda_debug_frame_maps(desc, k, v, beta, text_k, text_v, text_beta, M_out, J_out, not_spd,
+                         workspace, workspace_bytes=None, stream=None):
+    """C vda_debug_frame_maps: per-frame M_t and J_t = B_t M_t; not_spd (an int32
+    GPU tensor of one element, or None) receives VDA_ERR_NOT_SPD when a pivot of
+    some I + A_t is not positive."""
+    st = load_library().vda_debug_frame_maps(
+        ctypes.byref(desc), _ptr(k), _ptr(v), _ptr(beta), _ptr(text_k), _ptr(text_v),
+        _ptr(text_beta), _ptr(M_out), _ptr(J_out), _ptr(not_spd), _ptr(workspace),
+        _ws_bytes(workspace, workspace_bytes), _stream(stream))
+    _check(st, "vda_debug_frame_maps")
 
 
 def vda_debug_chunks(desc, k, v, beta, text_k, text_v, text_beta, Mc_out, Jf_out, Jr_out,

@@ -49,7 +49,9 @@ __device__ __forceinline__ float readlane_f(float x, int l) {
 // then S_kj *= 1/d (j != k), S_kk *= -1/d, g_k *= 1/d; row and column k are left
 // alone by the rank-1 update (its operands are zero at k).  The hardware
 // reciprocal is within 1 ulp.
-__device__ __forceinline__ void sweep_block(f32x16_t& T) {
+// `bad` turns true when a pivot is not positive (or not a number): I + A_t
+// was not numerically positive definite.
+__device__ __forceinline__ void sweep_block(f32x16_t& T, bool& bad) {
   const int lane = lane_id();
   const int half = lane >> 5;
   const int c = lane & 31;
@@ -60,6 +62,7 @@ __device__ __forceinline__ void sweep_block(f32x16_t& T) {
     const int hk = (k >> 2) & 1;
     const float skk = readlane_f(T[rk], k + 32 * hk);
     const float gk = readlane_f(g, k);
+    bad |= !(skk * gk > 0.0f);
     const float inv = __builtin_amdgcn_rcpf(skk * gk);
     const bool inrow = half == hk;
     const bool colk = c == k;
@@ -105,8 +108,10 @@ __device__ __forceinline__ void tile_to_lds_t(float* G, const f32x16_t& T) {
   for (int r = 0; r < 16; ++r) G[(lane & 31) * SG + acc_row(r, lane)] = T[r];
 }
 
+// not_spd (nullable): set to VDA_ERR_NOT_SPD when a pivot is not positive
 __global__ __launch_bounds__(256, 3) void solve_kernel(const float* __restrict__ A,
-                                                      float* __restrict__ Mout, int dk, int Fp1) {
+                                                      float* __restrict__ Mout, int dk, int Fp1,
+                                                      int* __restrict__ not_spd) {
   __shared__ float Gs[kNBlk * kBlk];  // block (i, j), j <= i, at index i (i + 1) / 2 + j
   const int fi = blockIdx.x;
   const int u = blockIdx.y;
@@ -148,8 +153,10 @@ __global__ __launch_bounds__(256, 3) void solve_kernel(const float* __restrict__
   for (int p = 0; p < nb; ++p) {
     if (w == 0) {  // G_PP -> -S
       f32x16_t T = tile_from_lds(G(p, p));
-      sweep_block(T);
+      bool bad = false;
+      sweep_block(T, bad);
       store_acc(G(p, p), SG, T, 1.0f);
+      if (not_spd && bad && lane == 0) *not_spd = VDA_ERR_NOT_SPD;
     }
     __syncthreads();
     const int i = w < p ? w : w + 1;  // this wave's non-pivot block
@@ -228,7 +235,7 @@ __global__ __launch_bounds__(256, 3) void solve_kernel(const float* __restrict__
 // block gets T_ij -= x_i x_j (x = row k / d beyond k) as a rank-1 MFMA through
 // k-slot hk (row k sits in register rk of the lanes of half hk); row k beyond
 // the diagonal is set to zero.
-__device__ __forceinline__ void chol_block(f32x16_t& T) {
+__device__ __forceinline__ void chol_block(f32x16_t& T, bool& bad) {
   const int lane = lane_id();
   const int half = lane >> 5;
   const int c = lane & 31;
@@ -237,6 +244,7 @@ __device__ __forceinline__ void chol_block(f32x16_t& T) {
     const int rk = 4 * (k >> 3) + (k & 3);
     const int hk = (k >> 2) & 1;
     const float tkk = readlane_f(T[rk], k + 32 * hk);
+    bad |= !(tkk > 0.0f);  // not positive definite (or not a number)
     const float d = __builtin_sqrtf(tkk);
     const float inv = 1.0f / d;
     const bool inrow = half == hk;
@@ -291,7 +299,7 @@ constexpr int kCholLds = (kNBlk + 4 + 3) * kBlk;  // L/Y blocks, the W_p, a colu
 
 __global__ __launch_bounds__(256, 2) void solve_chol_kernel(const float* __restrict__ A,
                                                            float* __restrict__ Mout, int dk,
-                                                           int Fp1) {
+                                                           int Fp1, int* __restrict__ not_spd) {
   __shared__ float Gs[kCholLds];
   const int fi = blockIdx.x;
   const int u = blockIdx.y;
@@ -345,8 +353,10 @@ __global__ __launch_bounds__(256, 2) void solve_chol_kernel(const float* __restr
   for (int p = 0; p < nb; ++p) {
     if (w == 0) {
       f32x16_t T = load_sym(G(p, p));
-      chol_block(T);
+      bool bad = false;
+      chol_block(T, bad);
       store_acc(G(p, p), SG, T, 1.0f);
+      if (not_spd && bad && lane == 0) *not_spd = VDA_ERR_NOT_SPD;
       wave_sync();
       const f32x16_t Wp = tri_inv_block(G(p, p));
       store_acc(Wb(p), SG, Wp, 1.0f);
@@ -489,12 +499,40 @@ __global__ __launch_bounds__(256) void batched_factor_kernel(const float* __rest
 
 }  // namespace
 
-hipError_t launch_solve(const Plan& p, const WsPtrs& w, hipStream_t s) {
+// Per-frame injection J_t = B_t M_t (debug tap only; the forward pass folds it
+// into the chunk composition): one workgroup per (unit, frame), each output a
+// plain fp32 dot product over d_k.
+__global__ __launch_bounds__(256) void frame_injection_kernel(const float* __restrict__ B,
+                                                              const float* __restrict__ M,
+                                                              float* __restrict__ J, int dk,
+                                                              int dv, int Fp1) {
+  const size_t fr = (size_t)blockIdx.y * Fp1 + blockIdx.x;
+  const float* Bf = B + fr * dv * dk;
+  const float* Mf = M + fr * dk * dk;
+  float* Jf = J + fr * dv * dk;
+  for (int idx = threadIdx.x; idx < dv * dk; idx += kThreads) {
+    const int r = idx / dk;
+    const int c = idx - r * dk;
+    float acc = 0.0f;
+    for (int k = 0; k < dk; ++k) acc = fmaf(Bf[(size_t)r * dk + k], Mf[(size_t)k * dk + c], acc);
+    Jf[idx] = acc;
+  }
+}
+
+hipError_t launch_frame_injections(const Plan& p, const WsPtrs& w, float* J, hipStream_t s) {
+  hipLaunchKernelGGL(frame_injection_kernel, dim3(p.F + 1, p.units), dim3(kThreads), 0, s, w.B,
+                     w.M, J, p.dk, p.dv, p.F + 1);
+  return hipGetLastError();
+}
+
+hipError_t launch_solve(const Plan& p, const WsPtrs& w, hipStream_t s, int* not_spd) {
   const dim3 grid(p.F + 1, p.units);
   if (p.rule == 0 && p.solver == 1)
-    hipLaunchKernelGGL(solve_chol_kernel, grid, dim3(kThreads), 0, s, w.A, w.M, p.dk, p.F + 1);
+    hipLaunchKernelGGL(solve_chol_kernel, grid, dim3(kThreads), 0, s, w.A, w.M, p.dk, p.F + 1,
+                       not_spd);
   else if (p.rule == 0)
-    hipLaunchKernelGGL(solve_kernel, grid, dim3(kThreads), 0, s, w.A, w.M, p.dk, p.F + 1);
+    hipLaunchKernelGGL(solve_kernel, grid, dim3(kThreads), 0, s, w.A, w.M, p.dk, p.F + 1,
+                       not_spd);
   else
     hipLaunchKernelGGL(batched_factor_kernel, grid, dim3(kThreads), 0, s, w.A, w.M, w.B, p.dk,
                        p.dv, p.F + 1, p.U, p.T, p.rule);

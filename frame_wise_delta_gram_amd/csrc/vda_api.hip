@@ -507,6 +507,32 @@ int vda_debug_solve(const vda_desc_t* desc, const void* k, const void* v, const 
                                           hipMemcpyDeviceToDevice, s));
 }
 
+int vda_debug_frame_maps(const vda_desc_t* desc, const void* k, const void* v, const float* beta,
+                         const void* text_k, const void* text_v, const float* text_beta,
+                         float* M_out, float* J_out, int* not_spd, void* workspace,
+                         size_t workspace_bytes, vda_stream_t stream) {
+  Plan p;
+  int st = vda::make_plan(desc, &p);
+  if (st != VDA_OK) return st;
+  if (p.rule != 0) return VDA_ERR_INVALID_ARG;
+  st = vda::check_state_inputs(p, k, v, beta, text_k, text_v, text_beta, workspace,
+                               workspace_bytes);
+  if (st != VDA_OK) return st;
+  if (p.units == 0 || p.F == 0) return VDA_OK;
+  if (!M_out || !J_out) return VDA_ERR_INVALID_ARG;
+  if (!vda::aligned(not_spd, 4)) return VDA_ERR_MISALIGNED;
+  const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const WsPtrs w = vda::carve(p, workspace);
+  st = vda::run_states(p, k, v, beta, text_k, text_v, text_beta, w, s, 1);
+  if (st != VDA_OK) return st;
+  if (vda::launch_solve(p, w, s, not_spd) != hipSuccess ||
+      vda::launch_frame_injections(p, w, J_out, s) != hipSuccess)
+    return VDA_ERR_HIP;
+  const size_t fr = (size_t)p.units * (p.F + 1);
+  return vda::hip_status(
+      hipMemcpyAsync(M_out, w.M, fr * p.dk * p.dk * 4, hipMemcpyDeviceToDevice, s));
+}
+
 int vda_debug_chunks(const vda_desc_t* desc, const void* k, const void* v, const float* beta,
                      const void* text_k, const void* text_v, const float* text_beta, float* Mc_out,
                      float* Jf_out, float* Jr_out, void* workspace, size_t workspace_bytes,
@@ -578,6 +604,8 @@ const char* vda_status_string(int status) {
     case VDA_ERR_HIP: return "HIP launch or copy failed";
     case VDA_ERR_SCRATCH_TOO_SMALL:
       return "problem needs more workspace than vda_forward_noalloc's fixed scratch";
+    case VDA_ERR_NOT_SPD:
+      return "some I + A_t is not numerically positive definite (a pivot <= 0 or NaN: beta < 0?)";
     default: return "unknown status";
   }
 }

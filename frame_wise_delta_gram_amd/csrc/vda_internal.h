@@ -61,7 +61,10 @@ struct WsPtrs {
 hipError_t launch_stats(const Plan& p, const void* k, const void* v, const float* beta,
                         const void* text_k, const void* text_v, const float* text_beta,
                         const WsPtrs& w, hipStream_t s);
-hipError_t launch_solve(const Plan& p, const WsPtrs& w, hipStream_t s);
+// not_spd (device, nullable): set to VDA_ERR_NOT_SPD when a pivot is not positive
+hipError_t launch_solve(const Plan& p, const WsPtrs& w, hipStream_t s, int* not_spd = nullptr);
+// J [units][F + 1][d_v][d_k] = B_t M_t per frame (debug tap)
+hipError_t launch_frame_injections(const Plan& p, const WsPtrs& w, float* J, hipStream_t s);
 // alpha: decay gates [units][F][d_k] or nullptr (no decay)
 hipError_t launch_compose(const Plan& p, const WsPtrs& w, const float* alpha,
                           hipStream_t s);  // Mc, McT, Jf, Jr (+ MrT with decay), seeds

@@ -106,7 +106,9 @@ typedef enum vda_status {
   VDA_ERR_WORKSPACE_TOO_SMALL = -3, /* workspace_bytes < vda_workspace_bytes(desc) */
   VDA_ERR_MISALIGNED = -4,          /* a tensor is not 16-byte aligned, workspace not 256-byte */
   VDA_ERR_HIP = -5,                 /* a kernel launch or copy failed (hipGetLastError) */
-  VDA_ERR_SCRATCH_TOO_SMALL = -6    /* vda_forward_noalloc: workspace > VDA_NOALLOC_MAX_BYTES */
+  VDA_ERR_SCRATCH_TOO_SMALL = -6,   /* vda_forward_noalloc: workspace > VDA_NOALLOC_MAX_BYTES */
+  VDA_ERR_NOT_SPD = -7              /* debug only: the value vda_debug_frame_maps writes to its
+                                       device flag when some I + A_t is not numerically SPD */
 } vda_status_t;
 
 typedef enum vda_dtype {
@@ -280,6 +282,23 @@ int vda_debug_solve(const vda_desc_t* desc, const void* k, const void* v, const 
                     const void* text_k, const void* text_v, const float* text_beta,
                     float* M_out, float* seed_out, void* workspace, size_t workspace_bytes,
                     vda_stream_t stream);
+
+/* Per-frame maps of the frame-wise rule ([VDN] App. A.1 Eq. (A.1): the update
+ * S_t = (S_{t-1} + B_t) M_t written as the affine map S_t = S_{t-1} M_t + J_t):
+ * M_t = (I + A_t)^{-1} and J_t = B_t M_t for every frame, text frame at index 0.
+ * The forward pass never forms J_t (the chunk composition folds B_t in); this
+ * tap computes it from the same B_t and M_t with an fp32 product.
+ * M_out [units][frames + 1][d_k][d_k], J_out [units][frames + 1][d_v][d_k].
+ * not_spd (device int, may be NULL): the solve writes VDA_ERR_NOT_SPD there when
+ * a pivot of some I + A_t is not positive or not a number, i.e. the inputs broke
+ * the beta >= 0 precondition of the frame statistics (a negative beta makes
+ * sqrt(beta) a NaN); it is never written otherwise, so the caller sets it to
+ * VDA_OK first and reads it after synchronising.  The frame-wise rule only
+ * (rules 1, 2: VDA_ERR_INVALID_ARG). */
+int vda_debug_frame_maps(const vda_desc_t* desc, const void* k, const void* v, const float* beta,
+                         const void* text_k, const void* text_v, const float* text_beta,
+                         float* M_out, float* J_out, int* not_spd, void* workspace,
+                         size_t workspace_bytes, vda_stream_t stream);
 
 /* Composed chunk maps ([VDN] Sec. 5): forward S_out = S_in Mc + Jf over the
  * chunk's frames in order, reverse S_out = S_in Mc^T + Jr over them in

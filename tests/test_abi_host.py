@@ -266,9 +266,30 @@ def test_forward_decay_argument_errors(lib):
                                       None) == vda.VDA_ERR_INVALID_ARG
 
 
+def test_frame_maps_tap_host_checks(lib):
+    """vda_debug_frame_maps refuses the batched rules, missing outputs and a
+    misaligned flag before anything is enqueued (no GPU here: nothing is)."""
+    import ctypes
+    fake = ctypes.c_void_p(1 << 20)  # never dereferenced: every call fails its checks first
+    d = desc()
+    ws_bytes = vda.vda_workspace_bytes(d)
+    P = [fake] * 6
+    assert lib.vda_debug_frame_maps(ctypes.byref(desc(rule=1)), *P, fake, fake, None, fake,
+                                    ws_bytes, None) == vda.VDA_ERR_INVALID_ARG
+    assert lib.vda_debug_frame_maps(ctypes.byref(d), *P, None, fake, None, fake, ws_bytes,
+                                    None) == vda.VDA_ERR_INVALID_ARG
+    assert lib.vda_debug_frame_maps(ctypes.byref(d), *P, fake, None, None, fake, ws_bytes,
+                                    None) == vda.VDA_ERR_INVALID_ARG
+    assert lib.vda_debug_frame_maps(ctypes.byref(d), *P, fake, fake, ctypes.c_void_p((1 << 20) + 2),
+                                    fake, ws_bytes, None) == vda.VDA_ERR_MISALIGNED
+    assert lib.vda_debug_frame_maps(None, *P, fake, fake, None, fake, ws_bytes,
+                                    None) == vda.VDA_ERR_INVALID_ARG
+
+
 def test_status_strings(lib):
-    for s in (0, -1, -2, -3, -4, -5, -6):
+    for s in (0, -1, -2, -3, -4, -5, -6, -7):
         assert vda.vda_status_string(s) and vda.vda_status_string(s) != "unknown status"
+    assert "positive definite" in vda.vda_status_string(vda.VDA_ERR_NOT_SPD)
     assert vda.vda_status_string(42) == "unknown status"
 
 

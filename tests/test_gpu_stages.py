@@ -135,3 +135,73 @@ def test_chunks_and_states(case):
     assert e_p <= tol(cfg, "P") and e_r <= tol(cfg, "R")
     # exactly once (Eq. (1b)): the two seeds are equal halves
     assert np.array_equal(P[:, 0], R[:, n])
+
+
+def frame_maps(d, cfg, vda, torch, solver=0):
+    """vda_debug_frame_maps: (M, J, flag), M and J as fp64 host arrays."""
+    U, F, dk, dv = cfg.units, cfg.frames, cfg.d_k, cfg.d_v
+    desc = desc_for(cfg, 0, 0, solver)
+    ws = workspace_for(desc)
+    M = torch.empty((U, F + 1, dk, dk), device="cuda")
+    J = torch.empty((U, F + 1, dv, dk), device="cuda")
+    flag = torch.full((1,), vda.VDA_OK, dtype=torch.int32, device="cuda")
+    vda.vda_debug_frame_maps(desc, d["k"], d["v"], d["beta"], d["text_k"], d["text_v"],
+                             d["text_beta"], M, J, flag, ws)
+    torch.cuda.synchronize()
+    return (M.cpu().numpy().astype(np.float64), J.cpu().numpy().astype(np.float64),
+            int(flag.item()))
+
+
+def test_frame_maps(case):
+    """Per-frame J_t = B_t M_t (App. A.1 Eq. (A.1)): against the fp64 product of
+    the GPU's own B_t and M_t (the tap's product alone, fp32 dot products of d_k
+    terms: 1e-5), and against the oracle's per-frame maps (the stage bar); the
+    not-SPD flag stays clear."""
+    name, cfg, h, d, x, vda, torch = case
+    say(f"[stages] {name}: per-frame maps")
+    U, F, dk, dv = cfg.units, cfg.frames, cfg.d_k, cfg.d_v
+    M, J, flag = frame_maps(d, cfg, vda, torch)
+    assert flag == vda.VDA_OK
+    desc = desc_for(cfg, 0)
+    ws = workspace_for(desc)
+    A = torch.empty((U, F + 1, dk, dk), device="cuda")
+    B = torch.empty((U, F + 1, dv, dk), device="cuda")
+    vda.vda_debug_stats(desc, d["k"], d["v"], d["beta"], d["text_k"], d["text_v"], d["text_beta"],
+                        A, B, ws)
+    torch.cuda.synchronize()
+    B = B.cpu().numpy().astype(np.float64)
+    e_own = mat_rel_err(J, B @ M)
+    _, tap = oracle_forward(x, cfg, 0, taps=True)
+    e_j = mat_rel_err(J[:, 1:], tap["B"] @ tap["M"])
+    e_m = mat_rel_err(M[:, 1:], tap["M"])
+    say(f"  J vs own B M {e_own:.2e}, J vs oracle {e_j:.2e}, M vs oracle {e_m:.2e}")
+    assert e_own <= 1e-5
+    assert e_j <= tol(cfg, "J") and e_m <= tol(cfg, "M")
+    for u in range(U):  # the text frame
+        At, Bt = oracle.frame_statistics(x["text_k"][u], x["text_v"][u], x["text_beta"][u])
+        Jt = Bt @ oracle.transition(At)
+        if cfg.text_tokens:
+            assert mat_rel_err(J[u, 0], Jt) <= tol(cfg, "J")
+        else:
+            assert np.all(J[u, 0] == 0)
+
+
+@pytest.mark.parametrize("solver", [0, 1])
+def test_not_spd_flag(solver):
+    """A negative beta breaks the precondition of the frame statistics (sqrt(beta)
+    is NaN, so is a pivot): the tap's flag reads VDA_ERR_NOT_SPD; on the same
+    inputs with beta >= 0 it stays VDA_OK."""
+    vda = require_gpu()
+    import torch
+    cfg = CASES["small-bf16"]
+    h = W.host_inputs(cfg)
+    d = to_device(h, cfg)
+    _, _, flag = frame_maps(d, cfg, vda, torch, solver)
+    assert flag == vda.VDA_OK
+    bad = dict(d)
+    bad["beta"] = d["beta"].clone()
+    bad["beta"][1, 3, :5] = -1.0  # unit 1, latent frame 3
+    M, J, flag = frame_maps(bad, cfg, vda, torch, solver)
+    say(f"[stages] negative beta, solver {solver}: flag {flag}")
+    assert flag == vda.VDA_ERR_NOT_SPD
+    assert np.all(np.isfinite(M[0]))  # other units untouched
