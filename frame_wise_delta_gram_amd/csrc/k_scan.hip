@@ -679,14 +679,19 @@ __global__ __launch_bounds__(256) void scan_split_kernel(const float* __restrict
                                                          const float* __restrict__ Jf,
                                                          const float* __restrict__ Jr,
                                                          float* __restrict__ ST, int dk, int dv,
-                                                         int n) {
+                                                         int n, int units, unsigned per) {
   __shared__ __align__(16) __bf16 Xh[32 * SB];
   __shared__ __align__(16) __bf16 Xl[32 * SB];
   __shared__ __align__(16) __bf16 Mh[128 * SB];
   __shared__ __align__(16) __bf16 Ml[128 * SB];
-  const int rb = blockIdx.x;  // rows [32 rb, 32 rb + 32) of the state
-  const int u = blockIdx.y;
-  const int dir = blockIdx.z;  // 0: forward (P), 1: reverse (R)
+  // work item (unit, direction, row block), row block fastest: the row blocks of
+  // one chain read the same transitions every step and share an XCD (its L2)
+  const int nrb = (dv + 31) >> 5;
+  const unsigned item = xcd_item(per);
+  if (item >= (unsigned)units * 2 * nrb) return;
+  const int rb = item % nrb;  // rows [32 rb, 32 rb + 32) of the state
+  const int u = (item / nrb) % units;
+  const int dir = item / (nrb * units);  // 0: forward (P), 1: reverse (R)
   const int lane = threadIdx.x & 63;
   const int jr = 32 * (threadIdx.x >> 6);
   const int nk = FULL ? 8 : dk >> 4;
@@ -781,12 +786,13 @@ hipError_t launch_scan(const Plan& p, const WsPtrs& w, bool decay, hipStream_t s
   const dim3 grid(pad32(p.dv) >> 5, p.units, 2);
   const float* rev = decay ? w.MrT : w.Mc;
   if (!p.fp32_products) {
+    const unsigned per = xcd_per((unsigned)(pad32(p.dv) >> 5) * p.units * 2);
     if (p.dk == 128 && p.dv % 32 == 0)
-      hipLaunchKernelGGL(scan_split_kernel<true>, grid, dim3(kThreads), 0, s, rev, w.McT, w.Jf,
-                         w.Jr, w.ST, p.dk, p.dv, p.n);
+      hipLaunchKernelGGL(scan_split_kernel<true>, dim3(kXcds * per), dim3(kThreads), 0, s, rev,
+                         w.McT, w.Jf, w.Jr, w.ST, p.dk, p.dv, p.n, p.units, per);
     else
-      hipLaunchKernelGGL(scan_split_kernel<false>, grid, dim3(kThreads), 0, s, rev, w.McT, w.Jf,
-                         w.Jr, w.ST, p.dk, p.dv, p.n);
+      hipLaunchKernelGGL(scan_split_kernel<false>, dim3(kXcds * per), dim3(kThreads), 0, s, rev,
+                         w.McT, w.Jf, w.Jr, w.ST, p.dk, p.dv, p.n, p.units, per);
   } else {
     hipLaunchKernelGGL(scan_kernel, grid, dim3(kThreads), 0, s, w.Mc, rev, w.Jf, w.Jr, w.ST, p.dk,
                        p.dv, p.n);
