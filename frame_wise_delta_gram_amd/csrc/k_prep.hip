@@ -80,15 +80,9 @@ __device__ __forceinline__ float silu(float x) {
   return x * __builtin_amdgcn_rcpf(1.0f + __expf(-x));
 }
 
-// Value of lane ^ 32 and of lane ^ 16, by gfx950's row-swap permutes (VALU
-// instructions, no LDS round trip).  permlane32_swap(x, x) returns
-// {[x_lo, x_lo], [x_hi, x_hi]} (halves of 32 lanes), permlane16_swap(x, x)
-// returns {rows [x0, x0, x2, x2], rows [x1, x1, x3, x3]} (rows of 16 lanes).
-__device__ __forceinline__ float lane_xor32(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
-                                                  false);
-  return __uint_as_float(lane_id() < 32 ? r[1] : r[0]);
-}
+// Value of lane ^ 16, by gfx950's row-swap permute (a VALU instruction, no
+// LDS round trip; lane ^ 32 is lane_xor32): permlane16_swap(x, x) returns
+// {rows [x0, x0, x2, x2], rows [x1, x1, x3, x3]} (rows of 16 lanes).
 __device__ __forceinline__ float lane_xor16(float x) {
   const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
                                                   false);

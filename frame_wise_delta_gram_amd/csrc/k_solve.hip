@@ -36,61 +36,73 @@ __device__ __forceinline__ float readlane_f(float x, int l) {
 }
 
 // Sweep all 32 indices of the symmetric block T held in accumulator layout
-// (register r of lane l = T[acc_row(r, l)][l % 32]), by one wave; T becomes
-// -T^{-1}.  Row k sits in register rk = 4 (k / 8) + k % 4 of the lanes of half
-// hk = (k / 4) % 2, so it feeds both operands of a rank-1 32x32x2 MFMA through
-// the k-slot hk with no data movement.  The scaling of column k by 1/d is
-// deferred: each lane keeps a factor g for its column (true T = stored T times
-// g per column), which only column k's lanes change at step k, and the block is
-// multiplied by it once at the end, so a step costs two lane reads, one
-// reciprocal and a handful of vector ops besides the MFMA.  In stored terms, step
-// k with d = S_kk g_k (the true pivot) is, for i, j != k,
-//   S_ij -= (S_ki g_i) (S_kj / d)    (S_ki g_i = T_ki = T_ik by symmetry),
-// then S_kj *= 1/d (j != k), S_kk *= -1/d, g_k *= 1/d; row and column k are left
-// alone by the rank-1 update (its operands are zero at k).  The hardware
+// (register r of lane l = T[acc_row(r, l)][l % 32]), by one wave, two indices
+// at a time; T becomes -T^{-1}.  Register q holds rows a = 8 (q / 4) + q % 4
+// (lanes 0..31) and b = a + 4 (lanes 32..63), and those two rows are exactly
+// the two k slots of a 32x32x2 MFMA operand, so sweeping the pair P = {a, b}
+// is one rank-2 MFMA with no data movement beyond a half swap.  With the 2 x 2
+// pivot block Pi = T_PP and S = Pi^{-1} (closed form, one reciprocal of its
+// determinant), the block sweep is
+//   T_ij -= T_iP S T_Pj   (i, j not in P),   T_Pj -> S T_Pj,   T_iP -> T_iP S,
+//   T_PP -> -S,
+// and the MFMA takes A[i][s] = -T_{i,P_s} (zero on the pivot rows, so they
+// only take the values written here) and B[s][j] = (S T_Pj)_s off the pivot
+// columns, (I - S)_{s,t} on pivot column P_t, which turns T_iP into T_iP S by
+// the same update (the block stays symmetric throughout, so T_{i,P_s} is row
+// P_s's entry in column i).  Sweeping a pair equals sweeping its two indices
+// one after the other; 16 dependent steps instead of 32.  The hardware
 // reciprocal is within 1 ulp.
-// `bad` turns true when a pivot is not positive (or not a number): I + A_t
-// was not numerically positive definite.
+// `bad` turns true when a 2 x 2 pivot block is not positive definite (or not a
+// number): I + A_t was not numerically positive definite.
 __device__ __forceinline__ void sweep_block(f32x16_t& T, bool& bad) {
   const int lane = lane_id();
   const int half = lane >> 5;
   const int c = lane & 31;
-  float g = 1.0f;
 #pragma unroll
-  for (int k = 0; k < 32; ++k) {
-    const int rk = 4 * (k >> 3) + (k & 3);
-    const int hk = (k >> 2) & 1;
-    const float skk = readlane_f(T[rk], k + 32 * hk);
-    const float gk = readlane_f(g, k);
-    bad |= !(skk * gk > 0.0f);
-    const float inv = __builtin_amdgcn_rcpf(skk * gk);
-    const bool inrow = half == hk;
-    const bool colk = c == k;
-    const float s = (inrow && !colk) ? T[rk] : 0.0f;  // row k off the pivot (stored)
-    const float xa = s * g;
-    const float xb = s * inv;
-    T[rk] *= inrow ? (colk ? -inv : inv) : 1.0f;
-    g = colk ? g * inv : g;
-    T = mfma_f32(-xa, xb, T);
+  for (int q = 0; q < 16; ++q) {
+    const int a = 8 * (q >> 2) + (q & 3);
+    const int b = a + 4;
+    const float x = T[q];              // row P_half, column c
+    const float y = lane_xor32(x);     // the other pivot row, column c
+    const float taa = readlane_f(x, a);
+    const float tab = readlane_f(x, b);
+    const float tbb = readlane_f(x, 32 + b);
+    const float det = taa * tbb - tab * tab;
+    bad |= !(taa > 0.0f && det > 0.0f);
+    const float inv = __builtin_amdgcn_rcpf(det);
+    const float sown = (half ? taa : tbb) * inv;  // S[half][half]
+    const float sab = -tab * inv;                 // S[0][1] = S[1][0]
+    const float st = sown * x + sab * y;          // (S T_Pc)[half]
+    const bool pa = c == a, pb = c == b;
+    const float shc = (half == (int)pb) ? sown : sab;  // S[half][t] on pivot column P_t
+    const float id = (half == (int)pb) ? 1.0f : 0.0f;
+    const bool piv = pa || pb;
+    const float bop = piv ? id - shc : st;
+    const float aop = piv ? 0.0f : -x;
+    T[q] = piv ? -shc : st;
+    T = mfma_f32(aop, bop, T);
   }
-#pragma unroll
-  for (int r = 0; r < 16; ++r) T[r] *= g;
 }
 
 // acc += op(A) Bm for 32 x 32 blocks, A in LDS (row stride sa, op = transpose
 // when AT), Bm in accumulator layout (register r of lane l = Bm[acc_row(r, l)][l % 32]).
 // The contraction index of k-step r, slot h is acc_row(r, 32 h) on both sides.
+// The A operands are read before the first MFMA (16 dependent MFMAs back to
+// back).
 template <bool AT>
 __device__ __forceinline__ f32x16_t blk_mm32_breg(f32x16_t acc, const float* A, int sa,
                                                   const f32x16_t& Bm) {
   const int lane = lane_id();
   const int m = lane & 31;
+  float a[16];
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
     const int k = acc_row(r, lane);
-    const float a = AT ? A[k * sa + m] : A[m * sa + k];
-    acc = mfma_f32(a, Bm[r], acc);
+    a[r] = AT ? A[k * sa + m] : A[m * sa + k];
   }
+  __builtin_amdgcn_sched_barrier(0);  // keep the reads ahead of the MFMA chain
+#pragma unroll
+  for (int r = 0; r < 16; ++r) acc = mfma_f32(a[r], Bm[r], acc);
   return acc;
 }
 
@@ -163,27 +175,26 @@ __global__ __launch_bounds__(256, 3) void solve_kernel(const float* __restrict__
     const bool has = i < nb;
     f32x16_t Y;
     if (has) {
-      // Y_i = S G_Pi = -(G_PP) G_Pi with G_Pi = G(p, i) (i < p) or G(i, p)^T
+      // Yn = -Y_i = -S G_Pi = (G_PP) G_Pi with G_Pi = G(p, i) (i < p) or G(i, p)^T
       Y = i < p ? blk_mm32<false, false>(zero16(), G(p, p), SG, G(p, i), SG)
                 : blk_mm32<false, true>(zero16(), G(p, p), SG, G(i, p), SG);
-#pragma unroll
-      for (int r = 0; r < 16; ++r) Y[r] = -Y[r];
-      // G_ji -= G_jP Y_i for the lower blocks (j >= i) of this column, G_jP still old
+      // G_ji -= G_jP Y_i for the lower blocks (j >= i, j != p) of this column,
+      // G_jP still old: the MFMAs accumulate G_jP Yn onto G_ji itself
       for (int j = i; j < nb; ++j) {
         if (j == p) continue;
-        const f32x16_t prod = j > p ? blk_mm32_breg<false>(zero16(), G(j, p), SG, Y)
-                                    : blk_mm32_breg<true>(zero16(), G(p, j), SG, Y);
         float* C = G(j, i);
-#pragma unroll
-        for (int r = 0; r < 16; ++r) C[acc_row(r, lane) * SG + (lane & 31)] -= prod[r];
+        const f32x16_t Cj = tile_from_lds(C);
+        const f32x16_t upd = j > p ? blk_mm32_breg<false>(Cj, G(j, p), SG, Y)
+                                   : blk_mm32_breg<true>(Cj, G(p, j), SG, Y);
+        store_acc(C, SG, upd, 1.0f);
       }
     }
     __syncthreads();  // every old G_jP has been read
-    if (has) {  // G_Pi -> Y_i, stored as block (p, i) or, transposed, (i, p)
+    if (has) {  // G_Pi -> Y_i = -Yn, stored as block (p, i) or, transposed, (i, p)
       if (i < p)
-        store_acc(G(p, i), SG, Y, 1.0f);
+        store_acc(G(p, i), SG, Y, -1.0f);
       else
-        tile_to_lds_t(G(i, p), Y);
+        tile_to_lds_t(G(i, p), -Y);
     }
     __syncthreads();
   }

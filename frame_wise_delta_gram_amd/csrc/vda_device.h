@@ -113,6 +113,15 @@ __device__ __forceinline__ float buf_load4(__amdgpu_buffer_rsrc_t r, int off) {
   return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
 }
 
+// Value of lane ^ 32, by gfx950's half swap (a VALU permute, no LDS round
+// trip): permlane32_swap(x, x) returns {[x_lo, x_lo], [x_hi, x_hi]} (halves of
+// 32 lanes).
+__device__ __forceinline__ float lane_xor32(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return __uint_as_float(lane_id() < 32 ? r[1] : r[0]);
+}
+
 constexpr int kXcds = 8;
 __device__ __forceinline__ unsigned xcd_item(unsigned per) {
   const unsigned L = blockIdx.x;
@@ -125,19 +134,24 @@ __host__ __forceinline__ unsigned xcd_per(unsigned items) { return (items + kXcd
 // given strides, in floats).  acc += op(A) op(B), op = transpose when the
 // template flag is set.  Strides should be odd (e.g. 129) so that the 32
 // lanes reading one column of a row-major block hit 32 distinct banks.
+// Every operand is read before the first MFMA, so the 16 dependent MFMAs
+// issue back to back instead of each waiting for its own LDS round trip.
 template <bool AT, bool BT>
 __device__ __forceinline__ f32x16_t blk_mm32(f32x16_t acc, const float* A, int sa, const float* B,
                                              int sb) {
   const int lane = lane_id();
   const int i = lane & 31;
   const int kh = lane >> 5;
+  float a[16], b[16];
 #pragma unroll
   for (int kk = 0; kk < 16; ++kk) {
     const int k = 2 * kk + kh;
-    const float a = AT ? A[k * sa + i] : A[i * sa + k];
-    const float b = BT ? B[i * sb + k] : B[k * sb + i];
-    acc = mfma_f32(a, b, acc);
+    a[kk] = AT ? A[k * sa + i] : A[i * sa + k];
+    b[kk] = BT ? B[i * sb + k] : B[k * sb + i];
   }
+  __builtin_amdgcn_sched_barrier(0);  // keep the reads ahead of the MFMA chain
+#pragma unroll
+  for (int kk = 0; kk < 16; ++kk) acc = mfma_f32(a[kk], b[kk], acc);
   return acc;
 }
 
