@@ -9,6 +9,10 @@
 // channels of one (token, head).  Input layout: the projection output
 // [batch][F][H_l][W_l][heads][d]; output: [batch * heads][F][H_l * W_l][d].
 //
+// Two convolution kernels share the tiling below: bf16 features run the
+// spatial filter on the matrix cores (prep_mfma_kernel, described with it);
+// fp32 features take the vector-ALU kernel described here.
+//
 // conv kernel: one workgroup (16 waves, four per SIMD to hide LDS latency) per
 // (unit, 8 x 8 spatial tile), sweeping all frames.  Per input frame the
 // 12 x 12 halo tile of the unit's channels is staged in LDS as fp32 (converted
@@ -376,6 +380,346 @@ __global__ __launch_bounds__(kPrepThreads, 1) void prep_conv_kernel(
 }
 
 
+// ---------------------------------------------------------------------------
+// bf16 convolution on the matrix cores.  The 5 x 5 spatial filter of one
+// channel, along one halo row, is a banded Toeplitz product: outputs
+// x0 .. x0 + 3 of that row are T_a (4 x 8) times halo columns x0 .. x0 + 7,
+// T_a[m][k] = w_s[a][k - m] for 0 <= k - m <= 4.  v_mfma_f32_4x4x4_16b_bf16
+// runs 16 independent 4 x 4 x 4 products, one per channel: block b = lane / 4
+// is channel 16 g + b of the wave's channel group g, the A operand of lane
+// (b, m = lane % 4) is row m of T_a (a k step of 4 columns), the B operand of
+// lane (b, n = lane % 4) is 4 consecutive halo columns of row 4 hh + n + a,
+// and the accumulator of lane (b, n) ends holding outputs x0 .. x0 + 3 of
+// output row 4 hh + n.  The taps are split into bf16 hi + lo (hi = bf16(w),
+// lo = bf16(w - hi)); the inputs are bf16 already, so every product is exact
+// and only the fp32 accumulation rounds, as on the vector path.  Per frame a
+// wave forms two such 4 x 4 position blocks (columns 0 .. 3 and 4 .. 7 of four
+// output rows) for its 16 channels: 5 rows x 2 k steps x 2 (hi, lo) x 2
+// blocks = 40 MFMAs from 15 + 20 eight-byte LDS reads (inputs, taps).
+//
+// Temporal filter in scatter form on the accumulators, with four ring slots:
+// input frame tin adds w_t[tau] times its spatial result to pending output
+// tin + 2 - tau; output tin - 2 is finished by its last term and leaves the
+// slot that output tin + 2 then starts in (slot = output frame mod 4).
+//
+// Staged tile: channel-major bf16, 40 eight-byte slots per channel (slot
+// 3 hr + q = halo row hr, columns 4 q .. 4 q + 3), channel pitch 88 words,
+// slot index XORed with (c / 4) mod 8.  Both access patterns then touch 32
+// distinct banks per 16 lanes: the MFMA operand reads (4 channels x 4 rows:
+// channel pitch 24 mod 32 words, rows 3 slots apart, the XOR constant over the
+// 4 channels) and the staging writes (16 channels of one slot: the XOR spreads
+// them).  A staging piece is 8 channels of one halo position (16 bytes, as
+// laid out in memory); the four lanes of a quad load four consecutive
+// columns, and a 4 x 4 word transpose across the quad (DPP) leaves each lane
+// two channels x four columns, written as two 8-byte slots.
+//
+// Output: each wave writes its finished fp32 values (before SiLU) to an
+// output tile [64 positions][128 channels] over the staged tile (channel
+// XORed with 16 on odd rows: two lanes per bank per write); after a barrier
+// each half wave reads one position's channels (16 bytes a lane), applies
+// SiLU, forms the L2 norm over its 32 lanes (K) and stores one contiguous row.
+constexpr int kXPitch = 88;   // words (bf16 pairs) per channel of the staged tile
+constexpr int kXSlots = 40;   // 8-byte slots per channel (36 used, the XOR reaches 39)
+static_assert(kXPitch >= 2 * kXSlots && kXPitch % 32 == 24, "staged tile pitch");
+// taps: 8 bytes per (channel, row a, k step s, hi / lo, A row m), channel pitch
+// 168 words (8 mod 32: a read's 16 lanes, 4 channels x 4 rows m, hit 32
+// distinct banks)
+constexpr int kWPitch = 168;
+static_assert(kWPitch >= 2 * 5 * 2 * 2 * 4 && kWPitch % 32 == 8, "tap table pitch");
+
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ f32x4_t mfma4(u32x2_t a, u32x2_t b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(__builtin_bit_cast(bf16x4_t, a),
+                                                __builtin_bit_cast(bf16x4_t, b), c, 0, 0, 0);
+}
+
+// word offset of slot (halo row hr, column quad q) of channel c
+__device__ __forceinline__ int xs_word(int c, int hr, int q) {
+  return kXPitch * c + 2 * ((3 * hr + q) ^ ((c >> 2) & 7));
+}
+// word offset of the A operand (row a, k step s, hi / lo part hl, A row m) of channel c
+__device__ __forceinline__ int wt_word(int c, int a, int s, int hl, int m) {
+  return kWPitch * c + 2 * (4 * (2 * (2 * a + s) + hl) + m);
+}
+
+// 4 x 4 transpose of 32-bit words across the four lanes of each quad: lane j
+// of a quad ends with word j of quad lanes 0, 1, 2, 3 (in that order).  Two
+// exchange stages (lane bit 0 with word bit 0, then lane bit 1 with word bit
+// 1), each by a DPP quad permutation; every lane takes part.
+__device__ __forceinline__ void quad_transpose(u32x4_t& w) {
+  const int j = lane_id() & 3;
+  const bool b0 = j & 1, b1 = j & 2;
+#pragma unroll
+  for (int i = 0; i < 4; i += 2) {
+    const uint32_t send = b0 ? w[i] : w[i + 1];
+    const uint32_t recv = (uint32_t)__builtin_amdgcn_mov_dpp((int)send, 0xB1, 0xF, 0xF, false);
+    w[i] = b0 ? recv : w[i];
+    w[i + 1] = b0 ? w[i + 1] : recv;
+  }
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const uint32_t send = b1 ? w[i] : w[i + 2];
+    const uint32_t recv = (uint32_t)__builtin_amdgcn_mov_dpp((int)send, 0x4E, 0xF, 0xF, false);
+    w[i] = b1 ? recv : w[i];
+    w[i + 2] = b1 ? w[i + 2] : recv;
+  }
+}
+
+// Sum over the 32 lanes of a half wave (every lane gets it).
+__device__ __forceinline__ float half_wave_sum(float x) {
+  x = dpp_add<0xB1>(x);
+  x = dpp_add<0x4E>(x);
+  x = dpp_add<0x141>(x);
+  x = dpp_add<0x140>(x);
+  return x + lane_xor16(x);
+}
+
+__global__ __launch_bounds__(kPrepThreads, 1) void prep_mfma_kernel(
+    ConvSide<uint16_t> ks, ConvSide<uint16_t> vs, int F, int Hl, int Wl, int H, int tiles_r,
+    int tiles_c, int units, unsigned per, float eps, const uint16_t* __restrict__ qx,
+    uint16_t* __restrict__ qy, long qrows, int dq, unsigned qblocks) {
+  __shared__ __align__(16) uint32_t Xs[128 * kXPitch];  // staged halo tile (bf16 pairs)
+  __shared__ __align__(16) uint32_t Wt[128 * kWPitch];  // spatial taps as A operands
+  __shared__ float Rs[8 * 64];                           // K: partial sums of squares [group][pos]
+  __shared__ __align__(16) float Is[64];                 // K: inverse norms of the positions
+  __shared__ float Ft[5 * 128];                          // temporal taps [tau][channel]
+  constexpr int kIter = (kHR * kHC * 16 + kPrepThreads - 1) / kPrepThreads;
+  constexpr int kWaves = kPrepThreads / 64;
+  if (blockIdx.x >= 2 * kXcds * per) {
+    const unsigned qb = blockIdx.x - 2 * kXcds * per;
+    q_rows(qx, qy, qrows, F, Hl * Wl, H, dq, eps, (long)qb * kWaves + (threadIdx.x >> 6),
+           (long)qblocks * kWaves);
+    return;
+  }
+  const unsigned ntiles = (unsigned)tiles_r * tiles_c;
+  const unsigned jq = blockIdx.x / kXcds;  // position in the XCD's queue
+  const bool norm = jq < per;              // K first, then V
+  const unsigned item = (blockIdx.x % kXcds) * per + (norm ? jq : jq - per);
+  if (jq >= 2 * per || item >= (unsigned)units * ntiles) return;
+  const ConvSide<uint16_t> side = norm ? ks : vs;
+  const uint16_t* __restrict__ x = side.x;
+  const float* __restrict__ ws = side.ws;
+  const float* __restrict__ wt = side.wt;
+  uint16_t* __restrict__ y = side.y;
+  const int d = side.d;
+  const int unit = item / ntiles;
+  const int tile = item - unit * ntiles;
+  const int b = unit / H;
+  const int h = unit - b * H;
+  const int r0 = (tile / tiles_c) * kTR;
+  const int c0 = (tile % tiles_c) * kTC;
+  const int t = threadIdx.x;
+  const int lane = t & 63;
+  const int w = t >> 6;
+  const int U = Hl * Wl;
+
+  // this wave's compute role: channel group g (16 channels), output rows
+  // 4 hh .. 4 hh + 3 (lane (blk, n): row 4 hh + n), both column blocks
+  const int g = w & 7;
+  const int hh = w >> 3;
+  const bool gact = 16 * g < d;
+  const int blk = lane >> 2;
+  const int n = lane & 3;
+  const int ch = 16 * g + blk;  // this lane's channel (operands and accumulators)
+
+  // tap table: each active lane writes its own A operands (row n of T_a, per
+  // row a and k step, hi and lo); temporal taps to LDS as well
+  {
+    const float* wsc = ws + ((size_t)h * d + (gact ? ch : 0)) * 25;
+    if (gact) {
+#pragma unroll
+      for (int a = 0; a < 5; ++a)
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+          float v[4];
+#pragma unroll
+          for (int kk = 0; kk < 4; ++kk) {
+            const int dx = 4 * s + kk - n;
+            v[kk] = (dx >= 0 && dx <= 4) ? wsc[a * 5 + max(0, min(dx, 4))] : 0.0f;
+          }
+          const uint32_t h0 = pack_bf16(v[0], v[1]), h1 = pack_bf16(v[2], v[3]);
+          *reinterpret_cast<u32x2_t*>(Wt + wt_word(ch, a, s, 0, n)) = u32x2_t{h0, h1};
+          *reinterpret_cast<u32x2_t*>(Wt + wt_word(ch, a, s, 1, n)) =
+              u32x2_t{pack_bf16(v[0] - bf16_lo(h0), v[1] - bf16_hi(h0)),
+                      pack_bf16(v[2] - bf16_lo(h1), v[3] - bf16_hi(h1))};
+        }
+    }
+    if (n == 0) {  // zero for channels past d (their accumulators stay zero)
+      const float* wtc = wt + ((size_t)h * d + (gact ? ch : 0)) * 5;
+#pragma unroll
+      for (int i = 0; i < 5; ++i) Ft[i * 128 + ch] = gact ? wtc[i] : 0.0f;
+    }
+  }
+
+  // staging pieces: piece p = t + 1024 i -> quad lane k = p % 4 (halo column
+  // 4 q + k), channel group cg = (p / 4) % gpp, slot (p / 4) / gpp = 3 hr + q
+  const int gpp = d / 8;
+  const int npieces = kHR * kHC * gpp;
+  const int frame_bytes = U * H * d * (int)sizeof(uint16_t);
+  int poff[kIter];
+  int xsw[kIter];  // staged-tile word of the piece's first slot (channel 8 cg + 2 (p % 4)), or -1
+#pragma unroll
+  for (int i = 0; i < kIter; ++i) {
+    const int p = t + kPrepThreads * i;
+    const int k = p & 3;
+    const int r = p >> 2;
+    const int cg = r % gpp;
+    const int sl = r / gpp;
+    const int gi = r0 - 2 + sl / 3;
+    const int gj = c0 - 2 + 4 * (sl % 3) + k;
+    const bool ok = p < npieces && gi >= 0 && gi < Hl && gj >= 0 && gj < Wl;
+    poff[i] = ok ? (((gi * Wl + gj) * H + h) * d + cg * 8) * (int)sizeof(uint16_t) : frame_bytes;
+    // the second slot (channel + 1) is one channel pitch further: (c + 1) / 4 = c / 4 for even c
+    xsw[i] = p < npieces ? xs_word(8 * cg + 2 * k, sl / 3, sl % 3) : -1;
+  }
+  u32x4_t pre[kIter];
+  auto load_frame = [&](int tin) {
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(x + ((size_t)b * F + tin) * U * H * d, frame_bytes);
+#pragma unroll
+    for (int i = 0; i < kIter; ++i) pre[i] = buf_load16(rs, poff[i]);
+  };
+  auto store_frame = [&]() {
+#pragma unroll
+    for (int i = 0; i < kIter; ++i) {
+      u32x4_t v = pre[i];
+      quad_transpose(v);  // every lane (whole quads are in or out of range)
+      if (xsw[i] < 0) continue;
+      // v[k] = channels c, c + 1 (c = 8 cg + 2 (lane % 4)) at halo column 4 q + k
+      const u32x2_t lo = u32x2_t{(v[0] & 0xffffu) | (v[1] << 16), (v[2] & 0xffffu) | (v[3] << 16)};
+      const u32x2_t hi = u32x2_t{(v[0] >> 16) | (v[1] & 0xffff0000u),
+                                 (v[2] >> 16) | (v[3] & 0xffff0000u)};
+      *reinterpret_cast<u32x2_t*>(Xs + xsw[i]) = lo;
+      *reinterpret_cast<u32x2_t*>(Xs + xsw[i] + kXPitch) = hi;
+    }
+  };
+
+  f32x4_t ring[4][2];
+#pragma unroll
+  for (int sl = 0; sl < 4; ++sl) ring[sl][0] = ring[sl][1] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  f32x4_t pend[2];  // SiLU of the last finished output frame, stored one step later
+
+  const int orow = 4 * hh + n;  // this lane's output row in the tile
+  const int gi_out = r0 + orow;
+  const int ylane = (gi_out * Wl + c0) * d + ch;  // in-frame offset (the frame is < 2^31 bytes)
+  // the finished output frame t_out from pend: scale (K: by the inverse norms of
+  // its 8 positions, from invs) and store one channel per lane
+  auto finish = [&](int t_out) {
+    if (!gact || gi_out >= Hl) return;
+    f32x4_t sc[2] = {f32x4_t{1.0f, 1.0f, 1.0f, 1.0f}, f32x4_t{1.0f, 1.0f, 1.0f, 1.0f}};
+    if (norm) {
+      sc[0] = *reinterpret_cast<const f32x4_t*>(Is + orow * 8);
+      sc[1] = *reinterpret_cast<const f32x4_t*>(Is + orow * 8 + 4);
+    }
+    uint16_t* const yt = y + ((size_t)unit * F + t_out) * U * d + ylane;
+#pragma unroll
+    for (int xb = 0; xb < 2; ++xb)
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const int col = 4 * xb + m;
+        if (c0 + col < Wl)
+          yt[(size_t)col * d] = __builtin_bit_cast(uint16_t, (__bf16)(pend[xb][m] * sc[xb][m]));
+      }
+  };
+
+  auto step = [&](int tin, auto kc) {
+    constexpr int k = decltype(kc)::value;  // tin mod 4
+    constexpr int fin = (k + 2) % 4;        // slot of output tin - 2, then of tin + 2
+    __syncthreads();                        // staged tile tin and the inverse norms of tin - 3
+    f32x4_t acc[2] = {f32x4_t{0.0f, 0.0f, 0.0f, 0.0f}, f32x4_t{0.0f, 0.0f, 0.0f, 0.0f}};
+    if (gact && tin < F) {
+#pragma unroll
+      for (int a = 0; a < 5; ++a) {
+        const int hr = orow + a;
+        const u32x2_t x0 = *reinterpret_cast<const u32x2_t*>(Xs + xs_word(ch, hr, 0));
+        const u32x2_t x1 = *reinterpret_cast<const u32x2_t*>(Xs + xs_word(ch, hr, 1));
+        const u32x2_t x2 = *reinterpret_cast<const u32x2_t*>(Xs + xs_word(ch, hr, 2));
+        const u32x2_t h0 = *reinterpret_cast<const u32x2_t*>(Wt + wt_word(ch, a, 0, 0, n));
+        const u32x2_t l0 = *reinterpret_cast<const u32x2_t*>(Wt + wt_word(ch, a, 0, 1, n));
+        const u32x2_t h1 = *reinterpret_cast<const u32x2_t*>(Wt + wt_word(ch, a, 1, 0, n));
+        const u32x2_t l1 = *reinterpret_cast<const u32x2_t*>(Wt + wt_word(ch, a, 1, 1, n));
+        acc[0] = mfma4(h0, x0, acc[0]);
+        acc[1] = mfma4(h0, x1, acc[1]);
+        acc[0] = mfma4(l0, x0, acc[0]);
+        acc[1] = mfma4(l0, x1, acc[1]);
+        acc[0] = mfma4(h1, x1, acc[0]);
+        acc[1] = mfma4(h1, x2, acc[1]);
+        acc[0] = mfma4(l1, x1, acc[0]);
+        acc[1] = mfma4(l1, x2, acc[1]);
+        __builtin_amdgcn_sched_barrier(0);  // one row's operands live at a time
+      }
+    }
+    // output tin - 3 (finished last step) leaves while the products run
+    if (tin >= 3) finish(tin - 3);
+    // input frame tin feeds output frame tin + 2 - tau with w_t[tau]
+    float ft[5];
+#pragma unroll
+    for (int i = 0; i < 5; ++i) ft[i] = Ft[i * 128 + ch];
+    f32x4_t out[2];
+#pragma unroll
+    for (int xb = 0; xb < 2; ++xb) {
+      out[xb] = ring[fin][xb] + ft[4] * acc[xb];  // output tin - 2 is complete
+      ring[fin][xb] = ft[0] * acc[xb];            // output tin + 2 starts
+      ring[(k + 3) % 4][xb] += ft[3] * acc[xb];   // tin - 1
+      ring[k][xb] += ft[2] * acc[xb];             // tin
+      ring[(k + 1) % 4][xb] += ft[1] * acc[xb];   // tin + 1
+    }
+    const bool emit = tin >= 2;  // output tin - 2 exists
+    if (emit) {
+#pragma unroll
+      for (int xb = 0; xb < 2; ++xb)
+#pragma unroll
+        for (int m = 0; m < 4; ++m) pend[xb][m] = silu(out[xb][m]);
+      if (norm && gact) {
+        // sum of squares over the wave's 16 channels (lane bits 2 .. 5) of each
+        // of the lane's 8 positions, halving butterfly: the lane ends holding
+        // position column e = 4 bit5 + 2 bit4 + bit3 of its row
+        const bool h5 = lane & 32, h4 = lane & 16, h3 = lane & 8;
+        float a4[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float v0 = pend[0][i] * pend[0][i], v1 = pend[1][i] * pend[1][i];
+          a4[i] = (h5 ? v1 : v0) + lane_xor32(h5 ? v0 : v1);
+        }
+        float a2[2];
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+          a2[i] = (h4 ? a4[i + 2] : a4[i]) + lane_xor16(h4 ? a4[i] : a4[i + 2]);
+        const float keep = h3 ? a2[1] : a2[0];
+        const float send = h3 ? a2[0] : a2[1];
+        float s1 = keep + __int_as_float(__builtin_amdgcn_update_dpp(
+                              0, __float_as_int(send), 0x128, 0xF, 0xF, false));  // lane ^ 8
+        s1 += __shfl_xor(s1, 4);
+        if (!(lane & 4)) Rs[g * 64 + orow * 8 + (h5 ? 4 : 0) + (h4 ? 2 : 0) + (h3 ? 1 : 0)] = s1;
+      }
+    }
+    __syncthreads();  // every wave is done with the staged tile; partial sums complete
+    if (emit && norm && t < 64) {
+      float ss = 0.0f;
+      for (int gg = 0; gg < (d >> 4); ++gg) ss += Rs[gg * 64 + t];
+      Is[t] = 1.0f / fmaxf(sqrtf(ss), eps);
+    }
+    if (tin + 1 < F) store_frame();
+    if (tin + 2 < F) load_frame(tin + 2);  // in flight during the next frame's products
+  };
+
+  if (F > 0) {
+    load_frame(0);
+    store_frame();
+    if (F > 1) load_frame(1);
+  }
+  for (int tb = 0; tb < F + 2; tb += 4) {
+    step(tb, std::integral_constant<int, 0>{});
+    if (tb + 1 < F + 2) step(tb + 1, std::integral_constant<int, 1>{});
+    if (tb + 2 < F + 2) step(tb + 2, std::integral_constant<int, 2>{});
+    if (tb + 3 < F + 2) step(tb + 3, std::integral_constant<int, 3>{});
+  }
+  if (F > 0) {
+    __syncthreads();  // the inverse norms of the last output frame
+    finish(F - 1);
+  }
+}
+
 template <typename T>
 hipError_t launch_prep_typed(const PrepPlan& p, const void* q, const void* k, const void* v,
                              const float* wk_s, const float* wk_t, const float* wv_s,
@@ -386,9 +730,15 @@ hipError_t launch_prep_typed(const PrepPlan& p, const void* q, const void* k, co
     const ConvSide<T> ks{static_cast<const T*>(k), wk_s, wk_t, static_cast<T*>(ko), p.dk};
     const ConvSide<T> vs{static_cast<const T*>(v), wv_s, wv_t, static_cast<T*>(vo), p.dv};
     const unsigned qblocks = kQBlocks;
-    hipLaunchKernelGGL(prep_conv_kernel<T>, dim3(2 * kXcds * per + qblocks), dim3(kPrepThreads), 0,
-                       s, ks, vs, p.F, p.Hl, p.Wl, p.H, p.tiles_r, p.tiles_c, p.batch * p.H, per,
-                       p.eps, static_cast<const T*>(q), static_cast<T*>(qo), rows, p.dk, qblocks);
+    if constexpr (std::is_same<T, uint16_t>::value)
+      hipLaunchKernelGGL(prep_mfma_kernel, dim3(2 * kXcds * per + qblocks), dim3(kPrepThreads), 0,
+                         s, ks, vs, p.F, p.Hl, p.Wl, p.H, p.tiles_r, p.tiles_c, p.batch * p.H, per,
+                         p.eps, static_cast<const T*>(q), static_cast<T*>(qo), rows, p.dk, qblocks);
+    else
+      hipLaunchKernelGGL(prep_conv_kernel<T>, dim3(2 * kXcds * per + qblocks), dim3(kPrepThreads),
+                         0, s, ks, vs, p.F, p.Hl, p.Wl, p.H, p.tiles_r, p.tiles_c, p.batch * p.H,
+                         per, p.eps, static_cast<const T*>(q), static_cast<T*>(qo), rows, p.dk,
+                         qblocks);
   }
   return hipGetLastError();
 }
