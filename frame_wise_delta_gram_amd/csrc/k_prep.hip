@@ -407,17 +407,16 @@ __global__ __launch_bounds__(kPrepThreads, 1) void prep_conv_kernel(
 // slot index XORed with (c / 4) mod 8.  Both access patterns then touch 32
 // distinct banks per 16 lanes: the MFMA operand reads (4 channels x 4 rows:
 // channel pitch 24 mod 32 words, rows 3 slots apart, the XOR constant over the
-// 4 channels) and the staging writes (16 channels of one slot: the XOR spreads
-// them).  A staging piece is 8 channels of one halo position (16 bytes, as
-// laid out in memory); the four lanes of a quad load four consecutive
-// columns, and a 4 x 4 word transpose across the quad (DPP) leaves each lane
-// two channels x four columns, written as two 8-byte slots.
+// 4 channels) and the staging writes (16 channel pairs of one slot: the XOR
+// spreads them).  Staging: lane l loads channels 2 l, 2 l + 1 (4 bytes) of the
+// slot's four positions, so one wave instruction reads one position's row of
+// channels and the lane holds both slot rows after two byte permutes each.
 //
-// Output: each wave writes its finished fp32 values (before SiLU) to an
-// output tile [64 positions][128 channels] over the staged tile (channel
-// XORed with 16 on odd rows: two lanes per bank per write); after a barrier
-// each half wave reads one position's channels (16 bytes a lane), applies
-// SiLU, forms the L2 norm over its 32 lanes (K) and stores one contiguous row.
+// Output: each lane applies SiLU to its own 8 outputs; for K the sum of
+// squares over the wave's 16 channels of each position comes from a halving
+// butterfly across lane bits 5 .. 2, the 8 channel groups' partial sums meet in
+// LDS, and the scaled values are stored one frame step later, while the next
+// frame's products run (two barriers per frame step).
 constexpr int kXPitch = 88;   // words (bf16 pairs) per channel of the staged tile
 constexpr int kXSlots = 40;   // 8-byte slots per channel (36 used, the XOR reaches 39)
 static_assert(kXPitch >= 2 * kXSlots && kXPitch % 32 == 24, "staged tile pitch");
@@ -443,29 +442,6 @@ __device__ __forceinline__ int wt_word(int c, int a, int s, int hl, int m) {
   return kWPitch * c + 2 * (4 * (2 * (2 * a + s) + hl) + m);
 }
 
-// 4 x 4 transpose of 32-bit words across the four lanes of each quad: lane j
-// of a quad ends with word j of quad lanes 0, 1, 2, 3 (in that order).  Two
-// exchange stages (lane bit 0 with word bit 0, then lane bit 1 with word bit
-// 1), each by a DPP quad permutation; every lane takes part.
-__device__ __forceinline__ void quad_transpose(u32x4_t& w) {
-  const int j = lane_id() & 3;
-  const bool b0 = j & 1, b1 = j & 2;
-#pragma unroll
-  for (int i = 0; i < 4; i += 2) {
-    const uint32_t send = b0 ? w[i] : w[i + 1];
-    const uint32_t recv = (uint32_t)__builtin_amdgcn_mov_dpp((int)send, 0xB1, 0xF, 0xF, false);
-    w[i] = b0 ? recv : w[i];
-    w[i + 1] = b0 ? w[i + 1] : recv;
-  }
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const uint32_t send = b1 ? w[i] : w[i + 2];
-    const uint32_t recv = (uint32_t)__builtin_amdgcn_mov_dpp((int)send, 0x4E, 0xF, 0xF, false);
-    w[i] = b1 ? recv : w[i];
-    w[i + 2] = b1 ? w[i + 2] : recv;
-  }
-}
-
 // Sum over the 32 lanes of a half wave (every lane gets it).
 __device__ __forceinline__ float half_wave_sum(float x) {
   x = dpp_add<0xB1>(x);
@@ -484,7 +460,6 @@ __global__ __launch_bounds__(kPrepThreads, 1) void prep_mfma_kernel(
   __shared__ float Rs[8 * 64];                           // K: partial sums of squares [group][pos]
   __shared__ __align__(16) float Is[64];                 // K: inverse norms of the positions
   __shared__ float Ft[5 * 128];                          // temporal taps [tau][channel]
-  constexpr int kIter = (kHR * kHC * 16 + kPrepThreads - 1) / kPrepThreads;
   constexpr int kWaves = kPrepThreads / 64;
   if (blockIdx.x >= 2 * kXcds * per) {
     const unsigned qb = blockIdx.x - 2 * kXcds * per;
@@ -552,45 +527,51 @@ __global__ __launch_bounds__(kPrepThreads, 1) void prep_mfma_kernel(
     }
   }
 
-  // staging pieces: piece p = t + 1024 i -> quad lane k = p % 4 (halo column
-  // 4 q + k), channel group cg = (p / 4) % gpp, slot (p / 4) / gpp = 3 hr + q
-  const int gpp = d / 8;
-  const int npieces = kHR * kHC * gpp;
+  // staging: wave w takes the halo slots w, w + 16, w + 32 (those below 36;
+  // slot 3 hr + q = row hr, columns 4 q .. 4 q + 3), lane l the channel pair
+  // 2 l, 2 l + 1: one 4-byte load per column (a wave instruction reads one
+  // position's whole row of channels), so a lane ends holding its two channels
+  // at the slot's four columns, which two byte permutes per channel turn into
+  // the slot's two 8-byte rows.  Positions are wave-uniform: the scalar offset
+  // of a position outside the frame lies past the descriptor's range and reads
+  // as zero.
+  constexpr int kSlots = kHR * (kHC / 4);
+  constexpr int kSlotIter = (kSlots + kWaves - 1) / kWaves;
+  const int wu = __builtin_amdgcn_readfirstlane(w);
+  const bool pact = 2 * lane < d;
   const int frame_bytes = U * H * d * (int)sizeof(uint16_t);
-  int poff[kIter];
-  int xsw[kIter];  // staged-tile word of the piece's first slot (channel 8 cg + 2 (p % 4)), or -1
-#pragma unroll
-  for (int i = 0; i < kIter; ++i) {
-    const int p = t + kPrepThreads * i;
-    const int k = p & 3;
-    const int r = p >> 2;
-    const int cg = r % gpp;
-    const int sl = r / gpp;
-    const int gi = r0 - 2 + sl / 3;
-    const int gj = c0 - 2 + 4 * (sl % 3) + k;
-    const bool ok = p < npieces && gi >= 0 && gi < Hl && gj >= 0 && gj < Wl;
-    poff[i] = ok ? (((gi * Wl + gj) * H + h) * d + cg * 8) * (int)sizeof(uint16_t) : frame_bytes;
-    // the second slot (channel + 1) is one channel pitch further: (c + 1) / 4 = c / 4 for even c
-    xsw[i] = p < npieces ? xs_word(8 * cg + 2 * k, sl / 3, sl % 3) : -1;
-  }
-  u32x4_t pre[kIter];
+  uint32_t pre[kSlotIter][4];
   auto load_frame = [&](int tin) {
     const __amdgpu_buffer_rsrc_t rs = make_rsrc(x + ((size_t)b * F + tin) * U * H * d, frame_bytes);
 #pragma unroll
-    for (int i = 0; i < kIter; ++i) pre[i] = buf_load16(rs, poff[i]);
+    for (int j = 0; j < kSlotIter; ++j) {
+      const int sl = wu + kWaves * j;
+      if (sl >= kSlots) break;
+      const int gi = r0 - 2 + sl / 3;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int gj = c0 - 2 + 4 * (sl % 3) + k;
+        const bool ok = gi >= 0 && gi < Hl && gj >= 0 && gj < Wl;
+        const int soff = ok ? ((gi * Wl + gj) * H + h) * d * (int)sizeof(uint16_t) : frame_bytes;
+        pre[j][k] = __builtin_amdgcn_raw_buffer_load_b32(rs, 4 * lane, soff, 0);
+      }
+    }
   };
   auto store_frame = [&]() {
+    if (!pact) return;
 #pragma unroll
-    for (int i = 0; i < kIter; ++i) {
-      u32x4_t v = pre[i];
-      quad_transpose(v);  // every lane (whole quads are in or out of range)
-      if (xsw[i] < 0) continue;
-      // v[k] = channels c, c + 1 (c = 8 cg + 2 (lane % 4)) at halo column 4 q + k
-      const u32x2_t lo = u32x2_t{(v[0] & 0xffffu) | (v[1] << 16), (v[2] & 0xffffu) | (v[3] << 16)};
-      const u32x2_t hi = u32x2_t{(v[0] >> 16) | (v[1] & 0xffff0000u),
-                                 (v[2] >> 16) | (v[3] & 0xffff0000u)};
-      *reinterpret_cast<u32x2_t*>(Xs + xsw[i]) = lo;
-      *reinterpret_cast<u32x2_t*>(Xs + xsw[i] + kXPitch) = hi;
+    for (int j = 0; j < kSlotIter; ++j) {
+      const int sl = wu + kWaves * j;
+      if (sl >= kSlots) break;
+      const uint32_t* v = pre[j];  // v[k] = channels 2 l, 2 l + 1 at column 4 q + k
+      const u32x2_t lo = u32x2_t{__builtin_amdgcn_perm(v[1], v[0], 0x05040100u),
+                                 __builtin_amdgcn_perm(v[3], v[2], 0x05040100u)};
+      const u32x2_t hi = u32x2_t{__builtin_amdgcn_perm(v[1], v[0], 0x07060302u),
+                                 __builtin_amdgcn_perm(v[3], v[2], 0x07060302u)};
+      // channel 2 l + 1 sits one channel pitch after 2 l: (2 l + 1) / 4 = 2 l / 4
+      const int wd = xs_word(2 * lane, sl / 3, sl % 3);
+      *reinterpret_cast<u32x2_t*>(Xs + wd) = lo;
+      *reinterpret_cast<u32x2_t*>(Xs + wd + kXPitch) = hi;
     }
   };
 
