@@ -174,7 +174,7 @@ def short_kernel_name(full):
     import re
     m = re.search(r"vda::\(anonymous namespace\)::(\w+)", full)
     if m:
-        if m.group(1) == "prep_conv_kernel":
+        if m.group(1) in ("prep_conv_kernel", "prep_mfma_kernel"):
             return "prep"
         return KERNEL_NAMES.get(m.group(1), m.group(1))
     return "copy" if "add" in full.lower() else None
