@@ -627,7 +627,6 @@ __global__ __launch_bounds__(kPrepThreads, 1) void prep_mfma_kernel(
         acc[1] = mfma4(h1, x2, acc[1]);
         acc[0] = mfma4(l1, x1, acc[0]);
         acc[1] = mfma4(l1, x2, acc[1]);
-        __builtin_amdgcn_sched_barrier(0);  // one row's operands live at a time
       }
     }
     // output tin - 3 (finished last step) leaves while the products run
