@@ -15,10 +15,12 @@
 // (block P with S = G_PP^{-1}):
 //   G_PP -> -S,  G_Pi -> S G_Pi,  G_iP -> G_iP S,  G_ij -> G_ij - G_iP S G_Pj.
 // One workgroup (4 waves) per frame keeps the lower-triangle 32 x 32 blocks of
-// G = I + A_t in LDS (fp32, row stride 33).  Per pivot block: one wave sweeps
-// the block in its MFMA accumulators (below); each other wave forms one
-// Y_i = S G_Pi and the updates G_ji -= G_jP Y_i with 32x32x2 fp32 MFMA, Y_i
-// staying in registers as an MFMA operand.  At the end the blocks hold -M.
+// G = I + A_t in LDS (fp32, row stride 33).  Per pivot block P: the waves form
+// Y_i = S G_Pi for the other block columns and the updates G_ji -= G_jP Y_i
+// with 32x32x2 fp32 MFMA, Y_i staying in registers as an MFMA operand; the
+// next pivot block is swept (below, in one wave's MFMA accumulators) by the
+// wave that forms its update, while the others finish pivot P's updates.  At
+// the end the blocks hold -M.
 // 42 KiB of LDS per workgroup lets three workgroups share a CU.  fp32
 // throughout.
 #include "vda_device.h"
@@ -162,35 +164,51 @@ __global__ __launch_bounds__(256, 3) void solve_kernel(const float* __restrict__
     __syncthreads();
   }
 
+  // Pivot block 0 is swept first; every later pivot block is swept as soon as
+  // the previous pivot's update of it is formed (lookahead), by the wave that
+  // owns its column, while the other waves finish that pivot's updates.
+  if (w == 0) {  // G_00 -> -S
+    f32x16_t T = tile_from_lds(G(0, 0));
+    bool bad = false;
+    sweep_block(T, bad);
+    store_acc(G(0, 0), SG, T, 1.0f);
+    if (not_spd && bad && lane == 0) *not_spd = VDA_ERR_NOT_SPD;
+  }
+  __syncthreads();
   for (int p = 0; p < nb; ++p) {
-    if (w == 0) {  // G_PP -> -S
-      f32x16_t T = tile_from_lds(G(p, p));
-      bool bad = false;
-      sweep_block(T, bad);
-      store_acc(G(p, p), SG, T, 1.0f);
-      if (not_spd && bad && lane == 0) *not_spd = VDA_ERR_NOT_SPD;
-    }
-    __syncthreads();
-    const int i = w < p ? w : w + 1;  // this wave's non-pivot block
+    // waves 0 .. 2 own the non-pivot block columns i (in order); wave 3 forms
+    // Y for column n1 = p + 1 as well and updates that column below its
+    // diagonal, so the owner of column n1 only updates and sweeps block (n1, n1)
+    const int n1 = p + 1;
+    const bool spare = w == 3;
+    const int i = spare ? n1 : (w < p ? w : w + 1);
     const bool has = i < nb;
+    const bool next_owner = !spare && i == n1;
     f32x16_t Y;
     if (has) {
       // Yn = -Y_i = -S G_Pi = (G_PP) G_Pi with G_Pi = G(p, i) (i < p) or G(i, p)^T
       Y = i < p ? blk_mm32<false, false>(zero16(), G(p, p), SG, G(p, i), SG)
                 : blk_mm32<false, true>(zero16(), G(p, p), SG, G(i, p), SG);
-      // G_ji -= G_jP Y_i for the lower blocks (j >= i, j != p) of this column,
-      // G_jP still old: the MFMAs accumulate G_jP Yn onto G_ji itself
-      for (int j = i; j < nb; ++j) {
+      // G_ji -= G_jP Y_i for the lower blocks (j >= i, j != p) of this wave's
+      // share of column i, G_jP still old: the MFMAs accumulate G_jP Yn onto G_ji
+      const int jbeg = spare ? n1 + 1 : i;
+      const int jend = next_owner ? n1 + 1 : nb;
+      for (int j = jbeg; j < jend; ++j) {
         if (j == p) continue;
         float* C = G(j, i);
         const f32x16_t Cj = tile_from_lds(C);
-        const f32x16_t upd = j > p ? blk_mm32_breg<false>(Cj, G(j, p), SG, Y)
-                                   : blk_mm32_breg<true>(Cj, G(p, j), SG, Y);
+        f32x16_t upd = j > p ? blk_mm32_breg<false>(Cj, G(j, p), SG, Y)
+                             : blk_mm32_breg<true>(Cj, G(p, j), SG, Y);
+        if (next_owner) {  // block (n1, n1) is final for pivot n1: G_{n1 n1} -> -S
+          bool bad = false;
+          sweep_block(upd, bad);
+          if (not_spd && bad && lane == 0) *not_spd = VDA_ERR_NOT_SPD;
+        }
         store_acc(C, SG, upd, 1.0f);
       }
     }
     __syncthreads();  // every old G_jP has been read
-    if (has) {  // G_Pi -> Y_i = -Yn, stored as block (p, i) or, transposed, (i, p)
+    if (has && !spare) {  // G_Pi -> Y_i = -Yn, stored as block (p, i) or, transposed, (i, p)
       if (i < p)
         store_acc(G(p, i), SG, Y, -1.0f);
       else
