@@ -237,7 +237,10 @@ int vda_forward_decay(const vda_desc_t* desc, const void* q, const void* k, cons
  *   q, k out  [batch * heads][frames][height * width][d_k] dtype (unit = b * heads + h)
  *   v out     [batch * heads][frames][height * width][d_v] dtype
  * The outputs are exactly the q, k, v layouts of vda_forward (tokens =
- * height * width).  Outputs must not overlap inputs. */
+ * height * width).  Outputs must not overlap inputs.  Arithmetic is fp32;
+ * with bf16 features the spatial filter runs on the matrix cores with each tap
+ * split into bf16 hi + lo (the tap to about 2^-17 relative, every product
+ * exact, fp32 accumulation). */
 typedef struct vda_prep_desc {
   int32_t batch;  /* >= 0 */
   int32_t heads;  /* >= 0; batch x heads <= 65535 */
