@@ -468,7 +468,7 @@ __global__ __launch_bounds__(512, 4) void readout_c128_kernel(
           (void __attribute__((address_space(3)))*)(dst + j * 1024), 16, 0, 0);
   }
   if (t < 128) Ws[t] = wrms[t];
-  u32x4_t q0[4], q1[4], gr[4];
+  u32x4_t q0[4], q1[4], gr[4], g1[4];
   load16(q0, q, grp_row(0));
   load16(gr, gate, grp_row(0));
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the DMA into LDS has landed
@@ -531,13 +531,14 @@ __global__ __launch_bounds__(512, 4) void readout_c128_kernel(
     }
   };
 
-  // two groups per wave: q of the second is fetched before the first is processed
+  // two groups per wave: q and gate of the second are fetched before the first
+  // is processed
   if (grp_row(0) >= rows_total) return;
   load16(q1, q, grp_row(1));
+  load16(g1, gate, grp_row(1));
   process(q0, gr, grp_row(0));
   if (grp_row(1) >= rows_total) return;
-  load16(gr, gate, grp_row(1));
-  process(q1, gr, grp_row(1));
+  process(q1, g1, grp_row(1));
 }
 
 // fp32 features: 64 token rows per workgroup, S~ and the rows' queries in LDS.
