@@ -53,8 +53,9 @@ def algorithmic(cfg):
     "stats" is the latent frames' kernel, "stats_text" the text frame's (fp32
     MFMA), which at bf16 with d_k = d_v = 128 runs inside the "stats" kernel (its
     work is then counted there and "stats_text" is zero); with decay the gates
-    are read once by the composition and once by the readout, and the
-    composition also writes the reverse maps."""
+    are read once by the composition and once by the split kernel (bf16,
+    d_k = d_v = 128: one split image per frame) or the readout (other shapes),
+    and the composition also writes the reverse maps."""
     eb = 2 if cfg.dtype == "bf16" else 4
     th = cfg.units * cfg.frames * cfg.tokens        # token-heads
     tt = cfg.units * cfg.text_tokens
@@ -68,12 +69,13 @@ def algorithmic(cfg):
     a_frac = 1.0 if cfg.rule != 0 else nkb * (nkb + 1) / 2 / (nkb * nkb)
     stats_bytes = th * ((dk + dv) * eb + 4) + u * F * (a_frac * dk + dv) * dk * 4
     text_bytes = tt * ((dk + dv) * eb + 4) + u * (dk + dv) * dk * 4
-    split = cfg.dtype == "bf16" and dk == 128 and dv == 128 and cfg.alpha_mu is None
-    image = 2 * 128 * 136 * 2                        # one chunk's split S~ (bf16 hi + lo)
+    split = cfg.dtype == "bf16" and dk == 128 and dv == 128
+    image = 2 * 128 * 136 * 2                        # one segment's split S~ (bf16 hi + lo)
+    nimg = u * (F if cfg.alpha_mu is not None else n)  # segments: frames with decay, else chunks
     readout_bytes = (th * (dk + 2 * dv) * eb                           # q, gate read; out written
-                     + (u * n * image if split else u * n * 2 * st)     # the chunk's state(s)
-                     + dv * 4 + gates)
-    split_bytes = u * n * (2 * st + image) if split else 0             # P, R in; image out
+                     + (nimg * image if split else u * n * 2 * st + gates)  # S~ images, or states
+                     + dv * 4)
+    split_bytes = u * n * 2 * st + nimg * image + gates if split else 0  # P, R (gates) in; images
     solve_bytes = (a_frac + 1) * u * (F + 1) * mat                     # A in, M out
     compose_bytes = (u * (F + 1) * (mat + st) + gates                  # M, B (and gates) in
                      + u * n * (nmaps * mat + 2 * st)                   # chunk maps out

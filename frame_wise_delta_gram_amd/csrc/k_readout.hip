@@ -361,15 +361,25 @@ __device__ __forceinline__ int c128_row(int ch) {
   return 16 * (2 * s + (e >> 2)) + 4 * h + (e & 3);
 }
 
+// DECAY: one image per frame (segment = frame f of chunk c = f / C), S~_f =
+// P Diag(bridge of P) + R Diag(bridge of R) with the window's gate products.
+template <bool DECAY>
 __global__ __launch_bounds__(256) void split_states_kernel(const float* __restrict__ ST,
+                                                           const float* __restrict__ alpha,
                                                            uint16_t* __restrict__ Sp, int n,
-                                                           int radius) {
-  const int c = blockIdx.x;
+                                                           int radius, int F, int C, int anchors) {
+  __shared__ __align__(16) float Dbr[DECAY ? 256 : 1];  // bridge products (P: 0.., R: 128..)
+  const int seg = blockIdx.x;
   const int u = blockIdx.y;
+  const int c = DECAY ? seg / C : seg;
+  if (DECAY) {
+    bridge_products(Dbr, alpha, u, seg, c, F, C, radius, 128, anchors);
+    __syncthreads();
+  }
   const size_t SS = 128 * 128;
   const float* P = ST + ((size_t)(u * 2 + 0) * (n + 1) + max(c - radius, 0)) * SS;
   const float* R = ST + ((size_t)(u * 2 + 1) * (n + 1) + min(c + radius + 1, n)) * SS;
-  uint16_t* dst = Sp + ((size_t)u * n + c) * (kSplitBytes / 2);
+  uint16_t* dst = Sp + ((size_t)u * gridDim.x + seg) * (kSplitBytes / 2);
   for (int it = threadIdx.x; it < 128 * 17; it += kThreads) {
     const int ch = it / 17, k8 = it - 17 * (it / 17);
     u32x4_t hi = {0u, 0u, 0u, 0u}, lo = {0u, 0u, 0u, 0u};
@@ -378,10 +388,22 @@ __global__ __launch_bounds__(256) void split_states_kernel(const float* __restri
       const f32x4_t* rp = reinterpret_cast<const f32x4_t*>(R + (size_t)ch * 128 + 8 * k8);
       const f32x4_t p0 = pp[0], p1 = pp[1], r0 = rp[0], r1 = rp[1];
       float x[8];
+      if (DECAY) {
+        const f32x4_t df0 = *reinterpret_cast<const f32x4_t*>(Dbr + 8 * k8);
+        const f32x4_t df1 = *reinterpret_cast<const f32x4_t*>(Dbr + 8 * k8 + 4);
+        const f32x4_t dr0 = *reinterpret_cast<const f32x4_t*>(Dbr + 128 + 8 * k8);
+        const f32x4_t dr1 = *reinterpret_cast<const f32x4_t*>(Dbr + 128 + 8 * k8 + 4);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        x[e] = p0[e] + r0[e];
-        x[4 + e] = p1[e] + r1[e];
+        for (int e = 0; e < 4; ++e) {
+          x[e] = p0[e] * df0[e] + r0[e] * dr0[e];
+          x[4 + e] = p1[e] * df1[e] + r1[e] * dr1[e];
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          x[e] = p0[e] + r0[e];
+          x[4 + e] = p1[e] + r1[e];
+        }
       }
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -421,16 +443,19 @@ __global__ __launch_bounds__(512, 4) void readout_c128_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ gate,
     const float* __restrict__ wrms, uint16_t* __restrict__ out, const uint16_t* __restrict__ Sp,
     int F, int U, int C, int radius, int n, float eps, int units, int nblk, unsigned per,
-    int anchors) {
+    int anchors, int per_frame) {
   __shared__ __align__(16) uint16_t S[kSplitBytes / 2];  // hi rows 0..127, lo rows 128..255
   __shared__ __align__(16) float Ws[128];
+  // segments: chunks, or frames (per_frame: with decay each frame has its own S~)
+  const int nseg = per_frame ? F : n;
   const unsigned item = xcd_item(per);
-  if (item >= (unsigned)units * n * nblk) return;
+  if (item >= (unsigned)units * nseg * nblk) return;
   const int blk = item % nblk;
-  const int c = (item / nblk) % n;
-  const int u = item / (nblk * n);
-  const int f0 = c * C;
-  const int f1 = min(f0 + C, F);
+  const int seg = (item / nblk) % nseg;
+  const int u = item / (nblk * nseg);
+  const int c = per_frame ? seg / C : seg;
+  const int f0 = per_frame ? seg : c * C;
+  const int f1 = per_frame ? seg + 1 : min(f0 + C, F);
   const long rows_total = (long)(f1 - f0) * U;
   if ((long)blk * 128 >= rows_total) return;
   long zlo, zhi;
@@ -460,7 +485,7 @@ __global__ __launch_bounds__(512, 4) void readout_c128_kernel(
 
   // S~ image -> LDS by DMA, then the first group's q and gate
   {
-    const char* src = reinterpret_cast<const char*>(Sp + ((size_t)u * n + c) * (kSplitBytes / 2));
+    const char* src = reinterpret_cast<const char*>(Sp + ((size_t)u * nseg + seg) * (kSplitBytes / 2));
     char* dst = reinterpret_cast<char*>(S);
     for (int j = w; j < kSplitBytes / 1024; j += 8)
       __builtin_amdgcn_global_load_lds(
@@ -634,11 +659,15 @@ void launch_readout_bf16(const Plan& p, const void* q, const void* gate, const f
                      p.C, p.r, p.n, p.eps, p.units, nseg, nblk, per, p.anchors);
 }
 
-hipError_t launch_split(const Plan& p, const WsPtrs& w, bool decay, hipStream_t s) {
-  if (decay || !split_readout(p.dtype, p.dk, p.dv) || p.units == 0 || p.n == 0 || p.U == 0)
+hipError_t launch_split(const Plan& p, const WsPtrs& w, const float* alpha, hipStream_t s) {
+  if (!split_readout(p.dtype, p.dk, p.dv) || p.units == 0 || p.n == 0 || p.U == 0)
     return hipSuccess;
-  hipLaunchKernelGGL(split_states_kernel, dim3(p.n, p.units), dim3(kThreads), 0, s, w.ST, w.Sp,
-                     p.n, p.r);
+  if (alpha)
+    hipLaunchKernelGGL(split_states_kernel<true>, dim3(p.F, p.units), dim3(kThreads), 0, s, w.ST,
+                       alpha, decay_images(w), p.n, p.r, p.F, p.C, p.anchors);
+  else
+    hipLaunchKernelGGL(split_states_kernel<false>, dim3(p.n, p.units), dim3(kThreads), 0, s, w.ST,
+                       alpha, w.Sp, p.n, p.r, p.F, p.C, p.anchors);
   return hipGetLastError();
 }
 
@@ -651,17 +680,17 @@ hipError_t launch_readout(const Plan& p, const void* q, const void* gate, const 
   if (p.dtype == VDA_DTYPE_BF16) {
     const int nblk = (int)((max_rows + kRows - 1) / kRows);
     const bool d128 = p.dk == 128 && p.dv == 128;
-    if (alpha)
-      d128 ? launch_readout_bf16<128, 128, true>(p, q, gate, rms_weight, out, w, alpha, nseg, nblk, s)
-           : launch_readout_bf16<0, 0, true>(p, q, gate, rms_weight, out, w, alpha, nseg, nblk, s);
-    else if (d128) {  // Sp was written by launch_split after the scans
+    if (d128) {  // the split images were written by launch_split after the scans
       const int nb = (int)((max_rows + kRowsC - 1) / kRowsC);
-      const unsigned per = xcd_per((unsigned)p.units * p.n * nb);
+      const unsigned per = xcd_per((unsigned)p.units * nseg * nb);
       hipLaunchKernelGGL(readout_c128_kernel, dim3(kXcds * per), dim3(kThreadsR), 0, s,
                          static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(gate),
-                         rms_weight, static_cast<uint16_t*>(out), w.Sp, p.F, p.U, p.C, p.r, p.n,
-                         p.eps, p.units, nb, per, p.anchors);
-    } else
+                         rms_weight, static_cast<uint16_t*>(out), alpha ? decay_images(w) : w.Sp,
+                         p.F, p.U, p.C, p.r, p.n, p.eps, p.units, nb, per, p.anchors,
+                         alpha ? 1 : 0);
+    } else if (alpha)
+      launch_readout_bf16<0, 0, true>(p, q, gate, rms_weight, out, w, alpha, nseg, nblk, s);
+    else
       launch_readout_bf16<0, 0, false>(p, q, gate, rms_weight, out, w, alpha, nseg, nblk, s);
   } else {
     const int nblk = (int)((max_rows + kRowsF - 1) / kRowsF);

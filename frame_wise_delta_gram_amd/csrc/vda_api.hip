@@ -194,7 +194,7 @@ int run_states(const Plan& p, const void* k, const void* v, const float* beta, c
   if (upto >= 3 && (rec(2) != hipSuccess || launch_compose(p, w, alpha, s) != hipSuccess))
     return VDA_ERR_HIP;
   if (upto >= 4 && (rec(3) != hipSuccess || launch_scan(p, w, alpha != nullptr, s) != hipSuccess ||
-                    launch_split(p, w, alpha != nullptr, s) != hipSuccess))
+                    launch_split(p, w, alpha, s) != hipSuccess))
     return VDA_ERR_HIP;
   return VDA_OK;
 }

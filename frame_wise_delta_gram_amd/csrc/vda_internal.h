@@ -69,8 +69,14 @@ hipError_t launch_frame_injections(const Plan& p, const WsPtrs& w, float* J, hip
 hipError_t launch_compose(const Plan& p, const WsPtrs& w, const float* alpha,
                           hipStream_t s);  // Mc, McT, Jf, Jr (+ MrT with decay), seeds
 hipError_t launch_scan(const Plan& p, const WsPtrs& w, bool decay, hipStream_t s);
-// Sp from ST when the readout reads it (split_readout, no decay); else nothing
-hipError_t launch_split(const Plan& p, const WsPtrs& w, bool decay, hipStream_t s);
+// The readout's split images of S~ from ST when it reads them (split_readout):
+// one per chunk in Sp, or with decay (alpha) one per frame in decay_images(w);
+// else nothing
+hipError_t launch_split(const Plan& p, const WsPtrs& w, const float* alpha, hipStream_t s);
+// With decay the per-frame images (units x F x kSplitElems bf16) reuse the
+// statistics' A and B regions, which are adjacent and dead once the scans have
+// run: 2 x units x (F + 1) x 128 x 128 x 4 bytes >= units x F x kSplitElems x 2.
+inline uint16_t* decay_images(const WsPtrs& w) { return reinterpret_cast<uint16_t*>(w.A); }
 hipError_t launch_readout(const Plan& p, const void* q, const void* gate, const float* rms_weight,
                           void* out, const WsPtrs& w, const float* alpha, hipStream_t s);
 
