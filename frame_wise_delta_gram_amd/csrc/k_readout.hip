@@ -361,16 +361,22 @@ __device__ __forceinline__ int c128_row(int ch) {
   return 16 * (2 * s + (e >> 2)) + 4 * h + (e & 3);
 }
 
+// Work item (unit, segment) on a 1-D grid, segment fastest: the segments of a
+// unit that read the same two states run side by side on one XCD (its L2).
 // DECAY: one image per frame (segment = frame f of chunk c = f / C), S~_f =
 // P Diag(bridge of P) + R Diag(bridge of R) with the window's gate products.
 template <bool DECAY>
 __global__ __launch_bounds__(256) void split_states_kernel(const float* __restrict__ ST,
                                                            const float* __restrict__ alpha,
                                                            uint16_t* __restrict__ Sp, int n,
-                                                           int radius, int F, int C, int anchors) {
+                                                           int radius, int F, int C, int anchors,
+                                                           int units, unsigned per) {
   __shared__ __align__(16) float Dbr[DECAY ? 256 : 1];  // bridge products (P: 0.., R: 128..)
-  const int seg = blockIdx.x;
-  const int u = blockIdx.y;
+  const int nseg = DECAY ? F : n;
+  const unsigned item = xcd_item(per);
+  if (item >= (unsigned)units * nseg) return;
+  const int seg = item % nseg;
+  const int u = item / nseg;
   const int c = DECAY ? seg / C : seg;
   if (DECAY) {
     bridge_products(Dbr, alpha, u, seg, c, F, C, radius, 128, anchors);
@@ -379,7 +385,7 @@ __global__ __launch_bounds__(256) void split_states_kernel(const float* __restri
   const size_t SS = 128 * 128;
   const float* P = ST + ((size_t)(u * 2 + 0) * (n + 1) + max(c - radius, 0)) * SS;
   const float* R = ST + ((size_t)(u * 2 + 1) * (n + 1) + min(c + radius + 1, n)) * SS;
-  uint16_t* dst = Sp + ((size_t)u * gridDim.x + seg) * (kSplitBytes / 2);
+  uint16_t* dst = Sp + ((size_t)u * nseg + seg) * (kSplitBytes / 2);
   for (int it = threadIdx.x; it < 128 * 17; it += kThreads) {
     const int ch = it / 17, k8 = it - 17 * (it / 17);
     u32x4_t hi = {0u, 0u, 0u, 0u}, lo = {0u, 0u, 0u, 0u};
@@ -662,12 +668,13 @@ void launch_readout_bf16(const Plan& p, const void* q, const void* gate, const f
 hipError_t launch_split(const Plan& p, const WsPtrs& w, const float* alpha, hipStream_t s) {
   if (!split_readout(p.dtype, p.dk, p.dv) || p.units == 0 || p.n == 0 || p.U == 0)
     return hipSuccess;
+  const unsigned per = xcd_per((unsigned)p.units * (alpha ? p.F : p.n));
   if (alpha)
-    hipLaunchKernelGGL(split_states_kernel<true>, dim3(p.F, p.units), dim3(kThreads), 0, s, w.ST,
-                       alpha, decay_images(w), p.n, p.r, p.F, p.C, p.anchors);
+    hipLaunchKernelGGL(split_states_kernel<true>, dim3(kXcds * per), dim3(kThreads), 0, s, w.ST,
+                       alpha, decay_images(w), p.n, p.r, p.F, p.C, p.anchors, p.units, per);
   else
-    hipLaunchKernelGGL(split_states_kernel<false>, dim3(p.n, p.units), dim3(kThreads), 0, s, w.ST,
-                       alpha, w.Sp, p.n, p.r, p.F, p.C, p.anchors);
+    hipLaunchKernelGGL(split_states_kernel<false>, dim3(kXcds * per), dim3(kThreads), 0, s, w.ST,
+                       alpha, w.Sp, p.n, p.r, p.F, p.C, p.anchors, p.units, per);
   return hipGetLastError();
 }
 
