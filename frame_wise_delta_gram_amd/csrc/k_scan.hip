@@ -427,6 +427,38 @@ __device__ __forceinline__ void x_fill(__bf16* xh, __bf16* xl, const float* src,
   }
 }
 
+// The scan's transition operands, pre-split (bf16 features, d_k = 128).  A scan
+// step multiplies a 32-row block of the state by a chunk transition T (the
+// forward step by Mc, the reverse step by Mc^T), as the product T'[a][i] =
+// sum_k op[a][k] X[i][k] with op = Mc^T (forward) or Mc (reverse).  Wave w of
+// the scan owns rows a = 32 w .. + 31 of op and takes them as the A operand of
+// v_mfma_f32_32x32x16_bf16: in k step kk lane l needs
+// op[32 w + l % 32][16 kk + 8 (l / 32) .. + 7], hi and lo.  An image holds
+// exactly these 16-byte pieces in that order, piece ((w * 8 + kk) * 2 + h) * 64
+// + l (h = 0: hi, 1: lo), 64 KB per chunk, so each of the scan's loads reads 1 KB
+// contiguously straight into the operand registers and no scan step splits
+// anything.  Both images are written from split(Mc) in LDS (row stride SB):
+// the reverse pieces are row pieces of Mc, the forward pieces column pieces.
+constexpr int kImgPieces = 4096;  // 16-byte pieces per image
+
+__device__ __forceinline__ void op_images(const __bf16* Xh, const __bf16* Xl,
+                                          u32x4_t* __restrict__ imgF, u32x4_t* __restrict__ imgR) {
+  static_assert(kImgPieces % 512 == 0, "512-thread workgroups");
+#pragma unroll
+  for (int p = threadIdx.x; p < kImgPieces; p += 512) {
+    const int l = p & 63;
+    const uint16_t* X = reinterpret_cast<const uint16_t*>(((p >> 6) & 1) ? Xl : Xh);
+    const int a = 32 * (p >> 10) + (l & 31);
+    const int k0 = 16 * ((p >> 7) & 7) + 8 * (l >> 5);
+    imgR[p] = *reinterpret_cast<const u32x4_t*>(X + a * SB + k0);
+    u32x4_t f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      f[e] = (uint32_t)X[(k0 + 2 * e) * SB + a] | ((uint32_t)X[(k0 + 2 * e + 1) * SB + a] << 16);
+    imgF[p] = f;
+  }
+}
+
 // Forward transition chain and reverse injection of one chunk in one pass over
 // its frames (bf16 features, alpha = 1, frame-wise rule, d_k = d_v = 128).
 // Every M_t is symmetric, so the reverse injection
@@ -440,11 +472,12 @@ __device__ __forceinline__ void x_fill(__bf16* xh, __bf16* xl, const float* src,
 // Jr += B_t X_t^T (X_t as the A operand, B_t as B; the product helper returns
 // the tile in the layout of Jr's rows).  The next frame's transition and write
 // are in flight while the current one is multiplied.  Writes Mc = X_{f1-1},
-// its transpose McT and Jr.
+// Jr and the scan's two operand images of Mc (see op_images).
 __device__ __forceinline__ void compose_mc_jr(__bf16* Xh, __bf16* Xl, __bf16* Mh, __bf16* Ml,
                                               const float* __restrict__ Mw,
                                               const float* __restrict__ Bw, float* __restrict__ Mc,
-                                              float* __restrict__ McT, float* __restrict__ Jr,
+                                              u32x4_t* __restrict__ imgF,
+                                              u32x4_t* __restrict__ imgR, float* __restrict__ Jr,
                                               int u, int c, int F, int C, int n) {
   constexpr int dk = 128;
   const int w = threadIdx.x >> 6;
@@ -491,14 +524,11 @@ __device__ __forceinline__ void compose_mc_jr(__bf16* Xh, __bf16* Xl, __bf16* Mh
     split_mm_t_lds<2>(accj, Xh, Xl, jr, Mh, Ml, xr0, 8);  // Jr += B_t X_t^T
     __syncthreads();  // every wave has read B_t
   }
-  // Mc = X_{f1-1} (a one-frame chunk: M_{f0}, symmetric, so Mc^T = Mc as well)
+  // Mc = X_{f1-1} (a one-frame chunk: M_{f0})
   if (f1 - f0 == 1) {
     const f32x4_t* src = reinterpret_cast<const f32x4_t*>(Mp(f0));
-    for (int i = threadIdx.x; i < dk * dk / 4; i += blockDim.x) {
-      const f32x4_t v = src[i];
-      reinterpret_cast<f32x4_t*>(Mc + tile)[i] = v;
-      reinterpret_cast<f32x4_t*>(McT + tile)[i] = v;
-    }
+    for (int i = threadIdx.x; i < dk * dk / 4; i += blockDim.x)
+      reinterpret_cast<f32x4_t*>(Mc + tile)[i] = src[i];
   }
 #pragma unroll
   for (int x = 0; x < 2; ++x)
@@ -507,13 +537,12 @@ __device__ __forceinline__ void compose_mc_jr(__bf16* Xh, __bf16* Xl, __bf16* Mh
       const int row = xr0 + 32 * x + (lane & 31);
       const int col = jr + 8 * q + 4 * (lane >> 5);
       *reinterpret_cast<f32x4_t*>(Jr + tile + (size_t)row * dk + col) = out_quad(accj, x, q);
-      if (f1 - f0 > 1) {
-        const f32x4_t v = out_quad(accx, x, q);
-        *reinterpret_cast<f32x4_t*>(Mc + tile + (size_t)row * dk + col) = v;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) McT[tile + (size_t)(col + e) * dk + row] = v[e];
-      }
+      if (f1 - f0 > 1)
+        *reinterpret_cast<f32x4_t*>(Mc + tile + (size_t)row * dk + col) = out_quad(accx, x, q);
     }
+  // the split X in LDS is split(Mc) (the last step stored it, every wave has
+  // passed the loop's final barrier since)
+  op_images(Xh, Xl, imgF + ((size_t)u * n + c) * kImgPieces, imgR + ((size_t)u * n + c) * kImgPieces);
 }
 
 // compose (bf16): one workgroup of 8 waves per work item; wave w owns output
@@ -531,7 +560,9 @@ __device__ __forceinline__ void compose_mc_jr(__bf16* Xh, __bf16* Xl, __bf16* Mh
 // over the others (the transition index runs one frame ahead of the write's);
 // the seed and one-frame chunks are plain copies of B.
 // MCJR (frame-wise rule, no decay, d_k = d_v = 128): two items per chunk, the
-// forward transition chain with the reverse injection (compose_mc_jr) and Jf.
+// forward transition chain with the reverse injection (compose_mc_jr, which
+// also writes the scan's operand images of Mc into the McT and MrT regions)
+// and Jf.
 template <bool FULL, bool DECAY, bool BATCHED, bool MCJR = false>
 __global__ __launch_bounds__(512, 1) void compose_split_kernel(
     const float* __restrict__ Bw, const float* __restrict__ Mw, const float* __restrict__ alpha,
@@ -551,7 +582,8 @@ __global__ __launch_bounds__(512, 1) void compose_split_kernel(
   const int c = seed ? 0 : (item / nch) % n;
   const int u = seed ? item - chain_items : item / (nch * n);
   if (MCJR && chain == 0) {
-    compose_mc_jr(Xh, Xl, Mh, Ml, Mw, Bw, Mc, McT, Jr, u, c, F, C, n);
+    compose_mc_jr(Xh, Xl, Mh, Ml, Mw, Bw, Mc, reinterpret_cast<u32x4_t*>(McT),
+                  reinterpret_cast<u32x4_t*>(MrT), Jr, u, c, F, C, n);
     return;
   }
   const bool mchain = !seed && (chain == 0 || chain == 3);
@@ -746,7 +778,104 @@ __global__ __launch_bounds__(256) void scan_split_kernel(const float* __restrict
   if (s < n) step(s, ja, jb);
 }
 
+// scan (bf16, d_k = 128, d_v a multiple of 32) on the composition's operand
+// images: one workgroup per (32-row block of the state, unit, direction), row
+// blocks of one chain consecutive on one XCD as above.  Wave w owns state
+// columns 32 w .. + 31; its A operands for a chunk are 16 registers of 16 bytes
+// loaded from the image (1 KB contiguous per instruction), NS - 1 chunks ahead
+// in a ring of NS register sets, the injections likewise; the state block is
+// the B operand, split in LDS.  A step: 24 MFMAs, a barrier, the new state
+// (injection added) stored and split into LDS, a barrier.  The products and
+// their order are those of scan_split_kernel, so the states are bitwise the same.
+template <int NS>
+__global__ __launch_bounds__(256) void scan_img_kernel(const u32x4_t* __restrict__ imgF,
+                                                       const u32x4_t* __restrict__ imgR,
+                                                       const float* __restrict__ Jf,
+                                                       const float* __restrict__ Jr,
+                                                       float* __restrict__ ST, int dv, int n,
+                                                       int units, unsigned per) {
+  constexpr int dk = 128;
+  __shared__ __align__(16) __bf16 Xh[32 * SB];
+  __shared__ __align__(16) __bf16 Xl[32 * SB];
+  const int nrb = dv >> 5;
+  const unsigned item = xcd_item(per);
+  if (item >= (unsigned)units * 2 * nrb) return;
+  const int rb = item % nrb;
+  const int u = (item / nrb) % units;
+  const int dir = item / (nrb * units);  // 0: forward (P), 1: reverse (R)
+  const int lane = threadIdx.x & 63;
+  const int jr = 32 * (threadIdx.x >> 6);
+  const size_t SS = (size_t)dv * dk;
+  float* S = ST + (size_t)(u * 2 + dir) * (n + 1) * SS;
+  const int r0 = 32 * rb;
+  auto chunk = [&](int s) { return dir == 0 ? s : n - 1 - s; };
+  const float* Jb = (dir == 0 ? Jf : Jr) + (size_t)u * n * SS + (size_t)r0 * dk;
+  const u32x4_t* Ib = (dir == 0 ? imgF : imgR) + (size_t)u * n * kImgPieces +
+                      16 * (threadIdx.x & ~63) + lane;
+  auto load = [&](u32x4_t (&a)[16], f32x4_t (&j)[1][4], int s) {
+    const u32x4_t* src = Ib + (size_t)chunk(s) * kImgPieces;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) a[i] = src[64 * i];
+    rows_prefetch_t<1>(j, Jb + (size_t)chunk(s) * SS, 32, dk, 0, jr);
+  };
+
+  u32x4_t A[NS][16];
+  f32x4_t J[NS][1][4];
+#pragma unroll
+  for (int i = 0; i + 1 < NS; ++i) load(A[i], J[i], min(i, n - 1));
+  x_fill(Xh, Xl, S + (size_t)(dir == 0 ? 0 : n) * SS + (size_t)r0 * dk, 32, dk, 1.0f);
+  __syncthreads();
+
+  const int xb = (lane & 31) * SB + 8 * (lane >> 5);
+  for (int s0 = 0; s0 < n; s0 += NS) {
+#pragma unroll
+    for (int i = 0; i < NS; ++i) {
+      const int s = s0 + i;
+      if (s >= n) break;
+      // chunk s + NS - 1 (clamped: the last steps refetch the last chunk)
+      load(A[(i + NS - 1) % NS], J[(i + NS - 1) % NS], min(s + NS - 1, n - 1));
+      // every B operand is read before the MFMA chain, so the 24 dependent
+      // MFMAs issue back to back instead of each waiting for its LDS read
+      u32x4_t bh[8], bl[8];
+#pragma unroll
+      for (int kk = 0; kk < 8; ++kk) {
+        bh[kk] = *reinterpret_cast<const u32x4_t*>(Xh + xb + 16 * kk);
+        bl[kk] = *reinterpret_cast<const u32x4_t*>(Xl + xb + 16 * kk);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      f32x16_t acc = zero16();
+#pragma unroll
+      for (int kk = 0; kk < 8; ++kk) {
+        acc = mfma_bf16(A[i][2 * kk], bh[kk], acc);
+        acc = mfma_bf16(A[i][2 * kk + 1], bh[kk], acc);
+        acc = mfma_bf16(A[i][2 * kk], bl[kk], acc);
+      }
+      __syncthreads();  // every wave has read X
+      float* dstp = S + (size_t)(dir == 0 ? chunk(s) + 1 : chunk(s)) * SS + (size_t)r0 * dk;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int row = lane & 31;
+        const int col = jr + 8 * q + 4 * (lane >> 5);
+        const f32x4_t v = f32x4_t{acc[4 * q], acc[4 * q + 1], acc[4 * q + 2], acc[4 * q + 3]} +
+                          J[i][0][q];
+        *reinterpret_cast<f32x4_t*>(dstp + (size_t)row * dk + col) = v;
+        x_store_quad(Xh, Xl, row, col, v);
+      }
+      __syncthreads();
+    }
+  }
+}
+
 }  // namespace
+
+// bf16 products, frame-wise rule, no decay, d_k = d_v = 128: the composition
+// runs as compose_mc_jr items plus Jf items and leaves the scan's operand
+// images (op_images) in the McT (forward) and MrT (reverse) regions, which the
+// scan reads with scan_img_kernel
+static bool mcjr_path(const Plan& p, bool decay) {
+  return !p.fp32_products && p.rule == 0 && !decay && p.dk == 128 && p.dv == 128;
+}
+constexpr int kScanRing = 3;  // register sets of the image scan (loads kScanRing - 1 chunks ahead)
 
 template <bool FULL, bool DECAY, bool BATCHED = false, bool MCJR = false>
 void launch_compose_split(const Plan& p, const WsPtrs& w, const float* alpha, float seed_scale,
@@ -764,7 +893,7 @@ hipError_t launch_compose(const Plan& p, const WsPtrs& w, const float* alpha, hi
     if (p.rule != 0)  // the batched comparison rules (no decay)
       p.dk == 128 ? launch_compose_split<true, false, true>(p, w, nullptr, seed_scale, s)
                   : launch_compose_split<false, false, true>(p, w, nullptr, seed_scale, s);
-    else if (p.dk == 128 && p.dv == 128 && !alpha)
+    else if (mcjr_path(p, alpha != nullptr))
       launch_compose_split<true, false, false, true>(p, w, alpha, seed_scale, s);
     else if (p.dk == 128)
       alpha ? launch_compose_split<true, true>(p, w, alpha, seed_scale, s)
@@ -785,7 +914,12 @@ hipError_t launch_compose(const Plan& p, const WsPtrs& w, const float* alpha, hi
 hipError_t launch_scan(const Plan& p, const WsPtrs& w, bool decay, hipStream_t s) {
   const dim3 grid(pad32(p.dv) >> 5, p.units, 2);
   const float* rev = decay ? w.MrT : w.Mc;
-  if (!p.fp32_products) {
+  if (mcjr_path(p, decay)) {  // the composition left the operand images in McT and MrT
+    const unsigned per = xcd_per((unsigned)(p.dv >> 5) * p.units * 2);
+    hipLaunchKernelGGL(scan_img_kernel<kScanRing>, dim3(kXcds * per), dim3(kThreads), 0, s,
+                       reinterpret_cast<const u32x4_t*>(w.McT), reinterpret_cast<const u32x4_t*>(w.MrT),
+                       w.Jf, w.Jr, w.ST, p.dv, p.n, p.units, per);
+  } else if (!p.fp32_products) {
     const unsigned per = xcd_per((unsigned)(pad32(p.dv) >> 5) * p.units * 2);
     if (p.dk == 128 && p.dv % 32 == 0)
       hipLaunchKernelGGL(scan_split_kernel<true>, dim3(kXcds * per), dim3(kThreads), 0, s, rev,

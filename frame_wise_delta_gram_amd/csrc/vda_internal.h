@@ -14,12 +14,16 @@ namespace vda {
 //   B  [units][F + 1][d_v][d_k]
 //   M  [units][F + 1][d_k][d_k]   transitions (I + A)^{-1}
 //   Mc [units][n][d_k][d_k]       chunk transitions (forward order)
-//   McT [units][n][d_k][d_k]      the same, transposed (rows = columns of Mc)
+//   McT [units][n][d_k][d_k]      the same, transposed (rows = columns of Mc); with bf16
+//                                 products, the frame-wise rule, no decay and d_k = d_v = 128
+//                                 instead the forward scan's operand image of Mc (64 KB of
+//                                 pre-split bf16 pieces per chunk, same size)
 //   Jf [units][n][d_v][d_k]       chunk injections, forward
 //   Jr [units][n][d_v][d_k]       chunk injections, reverse
 //   ST [units][2][n + 1][d_v][d_k] boundary states: [0] = P (forward), [1] = R (reverse)
 //   MrT [units][n][d_k][d_k]      reverse chunk transitions, transposed (decay only;
-//                                 without decay the reverse transition is Mc^T)
+//                                 without decay the reverse transition is Mc^T); in the
+//                                 case named under McT the reverse scan's operand image
 //   Sp [units][n][69632 bytes]    bf16 features with d_k = d_v = 128: each chunk's gathered
 //                                 state S~ split into bf16 hi + lo in the readout's LDS image
 struct Plan {
