@@ -14,7 +14,9 @@ sample of the same workload on the host cores, (object "batched_rule") the
 same inputs under SANA-WM's batched comparison rule with the boundary-state
 norms of every rule, (object "decay") the same workload with channel-wise
 decay gates through vda_forward_decay, (object "prep") the feature map on the
-768p head share, and (object "configs") the tiny, small, medium and stress
+768p head share (k and v alone, with the query map left to the forward's
+readout; with its query pass; and vda_prep then vda_forward both ways), and
+(object "configs") the tiny, small, medium and stress
 workloads, each with its own roofline and oracle baseline (the small ones
 rotate through input copies that do not fit in the MALL together).  The text
 seed follows --seed-mode (default 1: the text written at beta / 2).
@@ -161,7 +163,8 @@ KERNELS = ("stats_text", "stats", "solve", "compose", "scan", "split", "readout"
 PREP_COMMAND = ("rocprofv3 {pmc} -d DIR/{sub} -o p --output-format csv -- python bench.py "
                 "--steps 1 --warmup 0 --cpu-seconds 0 --decay-steps 0 --batched-steps 0 "
                 "--prep-steps 5 --variant-steps 0 --other-configs=")
-PREP_KERNELS = ("prep",)  # one launch: the K and V sweeps, then the Q pass
+# one launch each: the K and V sweeps alone (q = NULL), or followed by the Q pass
+PREP_KERNELS = ("prep_kv", "prep")
 KERNEL_NAMES = {"stats_bf16_kernel": "stats", "stats_f32_kernel": "stats",
                 "stats_text_kernel": "stats_text",
                 "readout_bf16_kernel": "readout", "readout_f32_kernel": "readout",
@@ -169,7 +172,8 @@ KERNEL_NAMES = {"stats_bf16_kernel": "stats", "stats_f32_kernel": "stats",
                 "solve_kernel": "solve", "batched_factor_kernel": "solve",
                 "solve_chol_kernel": "solve",
                 "compose_split_kernel": "compose",
-                "compose_kernel": "compose", "scan_split_kernel": "scan", "scan_kernel": "scan"}
+                "compose_kernel": "compose", "scan_split_kernel": "scan", "scan_kernel": "scan",
+                "scan_img_kernel": "scan"}
 
 
 def short_kernel_name(full):
@@ -182,9 +186,10 @@ def short_kernel_name(full):
     return "copy" if "add" in full.lower() else None
 
 
-def sq_table(path, order):
+def sq_table(path, order, kind=None):
     """Markdown lines of the SQ_COUNTERS pass at `path` (empty when absent):
-    per kernel, occupancy, vector ALU activity and LDS figures per launch."""
+    per kernel, occupancy, vector ALU activity and LDS figures per launch
+    (kind(row) names a row's kernel; default: from its Kernel_Name)."""
     import collections
     import csv
     if not os.path.exists(path):
@@ -194,7 +199,7 @@ def sq_table(path, order):
     gui_rows = collections.Counter()
     with open(path) as fh:
         for r in csv.DictReader(fh):
-            k = short_kernel_name(r["Kernel_Name"])
+            k = kind(r) if kind else short_kernel_name(r["Kernel_Name"])
             if k is None or k == "copy":
                 continue
             i = int(r["Dispatch_Id"])
@@ -254,17 +259,31 @@ def summarize_prep(prep_dir):
     known = {"FETCH_SIZE": 2 * copy_bytes, "WRITE_SIZE": copy_bytes}
     eb = 2
     rows = cfg.batch * cfg.frames * cfg.tokens * cfg.heads
-    # q, k, v read and written once; the K and V filters (30 fp32 taps per channel)
-    alg = {"prep": 2 * eb * rows * (2 * cfg.d_k + cfg.d_v) + cfg.heads * (cfg.d_k + cfg.d_v) * 120}
-    flops = {"prep": 60 * rows * (cfg.d_k + cfg.d_v)}
+    # q (with the query pass), k, v read and written once; the K and V filters
+    # (30 fp32 taps per channel)
+    alg = {"prep": 2 * eb * rows * (2 * cfg.d_k + cfg.d_v) + cfg.heads * (cfg.d_k + cfg.d_v) * 120,
+           "prep_kv": 2 * eb * rows * (cfg.d_k + cfg.d_v) + cfg.heads * (cfg.d_k + cfg.d_v) * 120}
+    flops = {"prep": 60 * rows * (cfg.d_k + cfg.d_v), "prep_kv": 60 * rows * (cfg.d_k + cfg.d_v)}
+
+    def prep_kind(name, grid, kv_grid):
+        k = short_kernel_name(name)
+        return ("prep_kv" if grid <= kv_grid else "prep") if k == "prep" else k
+
+    def kv_grid_of(path, col):  # the K/V-only launches have the smallest prep grid
+        with open(path) as fh:
+            g = [int(r[col]) for r in csv.DictReader(fh)
+                 if short_kernel_name(r["Kernel_Name"]) == "prep"]
+        return min(g) if g else 0
+
     per = {}
     for ctr in ("FETCH_SIZE", "WRITE_SIZE"):
         path = os.path.join(prep_dir, ctr, "p_counter_collection.csv")
+        kvg = kv_grid_of(path, "Grid_Size")
         disp = collections.defaultdict(float)
         names = {}
         with open(path) as fh:
             for r in csv.DictReader(fh):
-                k = short_kernel_name(r["Kernel_Name"])
+                k = prep_kind(r["Kernel_Name"], int(r["Grid_Size"]), kvg)
                 if k is None or r["Counter_Name"] != ctr:
                     continue
                 disp[int(r["Dispatch_Id"])] += float(r["Counter_Value"])
@@ -278,11 +297,16 @@ def summarize_prep(prep_dir):
         per[ctr] = {k: sum(v) / len(v) for k, v in acc.items()}
     scale = {c: known[c] / (per[c]["copy"] * 1024.0) for c in per}
     durations = {}
-    with open(os.path.join(prep_dir, "trace", "p_kernel_stats.csv")) as fh:
+    tpath = os.path.join(prep_dir, "trace", "p_kernel_trace.csv")
+    kvg = kv_grid_of(tpath, "Grid_Size_X")
+    ns = collections.defaultdict(list)
+    with open(tpath) as fh:
         for r in csv.DictReader(fh):
-            k = short_kernel_name(r["Name"])
+            k = prep_kind(r["Kernel_Name"], int(r["Grid_Size_X"]), kvg)
             if k in PREP_KERNELS:
-                durations[k] = (int(r["Calls"]), float(r["AverageNs"]) / 1e3)
+                ns[k].append(int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+    for k, v in ns.items():
+        durations[k] = (len(v), sum(v) / len(v) / 1e3)
     cmds = [PREP_COMMAND.format(pmc="--kernel-trace --stats", sub="trace"),
             "timeout -s KILL 120 " + PREP_COMMAND.format(pmc="--pmc FETCH_SIZE", sub="FETCH_SIZE"),
             "timeout -s KILL 120 " + PREP_COMMAND.format(pmc="--pmc WRITE_SIZE", sub="WRITE_SIZE"),
@@ -307,7 +331,11 @@ def summarize_prep(prep_dir):
                      f"{(rb + wb) / alg[k]:.3f} |")
     lines += ["", f"Counter scale factors (torch.add calibration in the same runs): FETCH x "
               f"{scale['FETCH_SIZE']:.3f}, WRITE x {scale['WRITE_SIZE']:.3f}."]
-    lines += sq_table(os.path.join(prep_dir, "SQ", "p_counter_collection.csv"), PREP_KERNELS)
+    sq_path = os.path.join(prep_dir, "SQ", "p_counter_collection.csv")
+    if os.path.exists(sq_path):
+        sq_kvg = kv_grid_of(sq_path, "Grid_Size")
+        lines += sq_table(sq_path, PREP_KERNELS,
+                          lambda r: prep_kind(r["Kernel_Name"], int(r["Grid_Size"]), sq_kvg))
     os.makedirs(PROFILES, exist_ok=True)
     with open(os.path.join(PROFILES, f"prep_kernels_{cfg.name}.md"), "w") as fh:
         fh.write("\n".join(lines) + "\n")
@@ -901,19 +929,50 @@ def main():
 VALU_FP32_PEAK = 256 * 4 * 16 * 2 * 2.4e9  # unpacked fp32 FMA: CUs x SIMDs x lanes x 2 flop x clock
 
 
-def prep_algorithmic(cfg):
-    """Bytes (q, k, v read once, q', k', v' written once, filters) and fp32 flops
-    (30 multiply-adds per convolved element of k and v) of one vda_prep call."""
+def prep_algorithmic(cfg, query_pass=True):
+    """Bytes (q, k, v read once, q', k', v' written once, filters; without the
+    query pass k and v only) and fp32 flops (30 multiply-adds per convolved
+    element of k and v) of one vda_prep call."""
     eb = 2 if cfg.dtype == "bf16" else 4
     rows = cfg.batch * cfg.frames * cfg.tokens * cfg.heads
-    elems = rows * (2 * cfg.d_k + cfg.d_v)
+    elems = rows * ((2 if query_pass else 1) * cfg.d_k + cfg.d_v)
     filt = cfg.heads * (cfg.d_k + cfg.d_v) * 30 * 4
     return 2 * elems * eb + filt, 2 * 30 * rows * (cfg.d_k + cfg.d_v)
 
 
+def _time_calls(fn, steps, warmup, stream):
+    """Average ms of fn() over `steps` calls after `warmup`, by events on stream."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
+def _prep_line(cfg, ms, query_pass):
+    bytes_, flops = prep_algorithmic(cfg, query_pass)
+    return {"ms_per_call": ms, "token_heads_per_s": cfg.units * cfg.frames * cfg.tokens / (ms * 1e-3),
+            "roofline": {"bound": "alu", "achieved": flops / (ms * 1e-3) / 1e12,
+                         "peak": VALU_FP32_PEAK / 1e12, "unit": "TFLOP/s",
+                         "frac": flops / (ms * 1e-3) / VALU_FP32_PEAK,
+                         "hbm_GB/s": bytes_ / (ms * 1e-3) / 1e9,
+                         "hbm_frac": bytes_ / (ms * 1e-3) / HBM_PEAK,
+                         "algorithmic_bytes": bytes_, "flops": flops}}
+
+
 def bench_prep(cfg, steps, warmup):
-    """Whole-call time of vda_prep on ``cfg`` (inputs resident), with its ALU and
-    HBM fractions."""
+    """The feature map on ``cfg`` (inputs resident): vda_prep on k and v alone
+    (the query map left to the forward's readout) and with its query pass, each
+    with its ALU and HBM fractions; then the linear branch from projection
+    outputs both ways, vda_prep then vda_forward on the 768p share: the query
+    pass's q' in the unit layout, or the raw projection q normalised inside the
+    readout (q_heads = heads, q_l2_eps = the feature map's eps)."""
     import torch
     import frame_wise_delta_gram_amd as vda
     import workloads as W
@@ -925,28 +984,54 @@ def bench_prep(cfg, steps, warmup):
     qo = torch.empty((N, F, U, cfg.d_k), dtype=torch.bfloat16, device="cuda")
     ko = torch.empty_like(qo)
     vo = torch.empty((N, F, U, cfg.d_v), dtype=torch.bfloat16, device="cuda")
-    a = (desc, d["q"], d["k"], d["v"], d["wk_s"], d["wk_t"], d["wv_s"], d["wv_t"], qo, ko, vo)
     stream = torch.cuda.current_stream()
-    for _ in range(warmup):
-        vda.vda_prep(*a, stream=stream)
-    torch.cuda.synchronize()
-    log(f"[bench] {cfg.name}: timing {steps} steps")
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for _ in range(steps):
-        vda.vda_prep(*a, stream=stream)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / steps
-    bytes_, flops = prep_algorithmic(cfg)
-    return {"workload": cfg.name, "entry_point": "vda_prep", "steps": steps, "ms_per_call": ms,
-            "token_heads_per_s": N * F * U / (ms * 1e-3),
-            "roofline": {"bound": "alu", "achieved": flops / (ms * 1e-3) / 1e12,
-                         "peak": VALU_FP32_PEAK / 1e12, "unit": "TFLOP/s",
-                         "frac": flops / (ms * 1e-3) / VALU_FP32_PEAK,
-                         "hbm_GB/s": bytes_ / (ms * 1e-3) / 1e9,
-                         "hbm_frac": bytes_ / (ms * 1e-3) / HBM_PEAK,
-                         "algorithmic_bytes": bytes_, "flops": flops}}
+    w = (d["wk_s"], d["wk_t"], d["wv_s"], d["wv_t"])
+
+    def prep_qkv():
+        vda.vda_prep(desc, d["q"], d["k"], d["v"], *w, qo, ko, vo, stream=stream)
+
+    def prep_kv():
+        vda.vda_prep(desc, None, d["k"], d["v"], *w, None, ko, vo, stream=stream)
+
+    log(f"[bench] {cfg.name}: timing {steps} calls, k and v only, then with the query pass")
+    ms_kv = _time_calls(prep_kv, steps, warmup, stream)
+    ms_qkv = _time_calls(prep_qkv, steps, warmup, stream)
+    res = {"workload": cfg.name, "entry_point": "vda_prep", "steps": steps}
+    res.update(_prep_line(cfg, ms_kv, False))
+    res["scope"] = ("k and v (q = q_out = NULL; the query map runs in the forward's readout, "
+                    "q_heads / q_l2_eps)")
+    res["with_query_pass"] = _prep_line(cfg, ms_qkv, True)
+    fc = W.CONFIGS[4]
+    if (fc.units, fc.frames, fc.tokens, fc.d_k, fc.d_v) == (N, F, U, cfg.d_k, cfg.d_v):
+        log(f"[bench] {cfg.name}: vda_prep then vda_forward, both ways")
+        fi = W.device_inputs(fc)
+        del fi["q"], fi["k"], fi["v"]
+        fdesc = make_desc(fc)
+        qdesc = make_desc(fc)
+        qdesc.q_heads, qdesc.q_l2_eps = cfg.heads, cfg.eps
+        ws = torch.empty(vda.vda_workspace_bytes(fdesc), dtype=torch.uint8, device="cuda")
+        out = torch.empty((N, F, U, fc.d_v), dtype=torch.bfloat16, device="cuda")
+        q_proj = d["q"].view(cfg.batch, F, U, cfg.heads, cfg.d_k)
+        rest = (fi["beta"], fi["gate"], fi["text_k"], fi["text_v"], fi["text_beta"],
+                fi["rms_weight"], out, ws)
+
+        def pipe_unit_q():
+            prep_qkv()
+            vda.vda_forward(fdesc, qo, ko, vo, *rest, stream=stream)
+
+        def pipe_query_map():
+            prep_kv()
+            vda.vda_forward(qdesc, q_proj, ko, vo, *rest, stream=stream)
+
+        ms_a = _time_calls(pipe_unit_q, steps, warmup, stream)
+        ms_b = _time_calls(pipe_query_map, steps, warmup, stream)
+        res["prep_then_forward"] = {
+            "forward_workload": fc.name,
+            "query_pass_then_unit_layout_q_ms": ms_a,
+            "query_map_in_readout_ms": ms_b,
+            "speedup": ms_a / ms_b}
+        del fi, ws, out
+    return res
 
 
 if __name__ == "__main__":

@@ -44,6 +44,7 @@ class VdaDesc(ctypes.Structure):
         ("seed_mode", ctypes.c_int32), ("in_dtype", ctypes.c_int32), ("out_dtype", ctypes.c_int32),
         ("anchors", ctypes.c_int32), ("rule", ctypes.c_int32),
         ("fp32_products", ctypes.c_int32), ("solver", ctypes.c_int32),
+        ("q_heads", ctypes.c_int32), ("q_l2_eps", ctypes.c_float),
     ]
 
     @property
@@ -128,10 +129,10 @@ def vda_status_string(status: int) -> str:
 
 def make_desc(units, frames, tokens, text_tokens, d_k, d_v, chunk=5, radius=1, rms_eps=1e-6,
               seed_mode=0, dtype=VDA_DTYPE_BF16, anchors=0, rule=0, fp32_products=0,
-              solver=0) -> VdaDesc:
+              solver=0, q_heads=0, q_l2_eps=0.0) -> VdaDesc:
     return VdaDesc(units, frames, tokens, text_tokens, d_k, d_v, chunk, radius, rms_eps,
                    seed_mode, dtype, dtype, int(anchors), int(rule), int(fp32_products),
-                   int(solver))
+                   int(solver), int(q_heads), float(q_l2_eps))
 
 
 def vda_workspace_bytes(desc: VdaDesc) -> int:
@@ -294,7 +295,8 @@ def vda_prep_check_desc(desc: VdaPrepDesc) -> int:
 
 
 def vda_prep(desc, q, k, v, wk_s, wk_t, wv_s, wv_t, q_out, k_out, v_out, stream=None):
-    """C vda_prep: the feature map from projection outputs to prepared features."""
+    """C vda_prep: the feature map from projection outputs to prepared features
+    (q and q_out both None: K' and V' only, the query map left to the readout)."""
     st = load_library().vda_prep(
         ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(wk_s), _ptr(wk_t), _ptr(wv_s),
         _ptr(wv_t), _ptr(q_out), _ptr(k_out), _ptr(v_out), _stream(stream))
@@ -303,7 +305,8 @@ def vda_prep(desc, q, k, v, wk_s, wk_t, wv_s, wv_t, q_out, k_out, v_out, stream=
 
 # ----------------------------------------------------------------------------- torch helpers
 def desc_from_tensors(q, k, v, text_k, chunk=5, radius=1, eps=1e-6, seed_mode=0,
-                      anchors=False, rule=0, fp32_products=0, solver=0) -> VdaDesc:
+                      anchors=False, rule=0, fp32_products=0, solver=0, q_heads=0,
+                      q_l2_eps=0.0) -> VdaDesc:
     """Descriptor from tensor shapes: q/k [units, F, U, d_k], v [units, F, U, d_v],
     text_k [units, T, d_k]."""
     import torch
@@ -319,7 +322,7 @@ def desc_from_tensors(q, k, v, text_k, chunk=5, radius=1, eps=1e-6, seed_mode=0,
     else:
         raise TypeError("features must be bfloat16 or float32, got %s" % k.dtype)
     return make_desc(units, F, U, T, dk, dv, chunk, radius, eps, seed_mode, dt, anchors, rule,
-                     fp32_products, solver)
+                     fp32_products, solver, q_heads, q_l2_eps)
 
 
 def _check_tensor(name, x, dtype, shape, device=None):
@@ -342,7 +345,7 @@ def _check_tensor(name, x, dtype, shape, device=None):
 
 def forward(q, k, v, beta, gate, text_k, text_v, text_beta, rms_weight, chunk=5, radius=1,
             eps=1e-6, seed_mode=0, out=None, workspace=None, stream=None, alpha=None,
-            anchors=False, rule=0, fp32_products=0, solver=0):
+            anchors=False, rule=0, fp32_products=0, solver=0, q_heads=0, q_l2_eps=0.0):
     """VDA forward on torch GPU tensors; allocates `out` and the workspace when absent.
 
     Shapes: q, k [units, F, U, d_k]; v, gate [units, F, U, d_v]; beta [units, F, U]
@@ -352,7 +355,10 @@ def forward(q, k, v, beta, gate, text_k, text_v, text_beta, rms_weight, chunk=5,
     boundary anchors (frames 0 and F - 1 out of the linear states, their rows
     zero); rule: 0 the frame-wise delta rule, 1 / 2 the batched comparison rules
     (no decay); fp32_products: composition and scan on fp32 MFMA for bf16
-    features; solver: 0 symmetric Gauss-Jordan, 1 blocked Cholesky.  A caller-supplied `out` must be [units, F, U, d_v] in the
+    features; solver: 0 symmetric Gauss-Jordan, 1 blocked Cholesky; q_heads = H > 1:
+    q in the projection layout [units / H, F, U, H, d_k] (heads interleaved per
+    token); q_l2_eps > 0: each query row L2-normalised inside the readout (the
+    feature map's query map).  A caller-supplied `out` must be [units, F, U, d_v] in the
     features' dtype, a caller-supplied workspace a contiguous uint8 tensor on the
     features' GPU.  Every tensor is checked (dtype, shape, device, contiguity)
     before anything is enqueued: a mismatch raises TypeError or ValueError.
@@ -366,13 +372,17 @@ def forward(q, k, v, beta, gate, text_k, text_v, text_beta, rms_weight, chunk=5,
     if (text_k is None) != (text_v is None) or (text_k is None) != (text_beta is None):
         raise ValueError("text_k, text_v and text_beta are given together or all None")
     desc = desc_from_tensors(q, k, v, text_k, chunk, radius, eps, seed_mode, anchors, rule,
-                             fp32_products, solver)
+                             fp32_products, solver, q_heads, q_l2_eps)
     units, F, U, dk = k.shape
     dv = v.shape[-1]
     T = desc.text_tokens
     fdt = k.dtype
     dev = k.device
-    checks = [("k", k, fdt, (units, F, U, dk)), ("q", q, fdt, (units, F, U, dk)),
+    H = int(q_heads) if int(q_heads) > 1 else 1
+    if units % H:
+        raise ValueError("q_heads = %d does not divide units = %d" % (H, units))
+    qshape = (units, F, U, dk) if H == 1 else (units // H, F, U, H, dk)
+    checks = [("k", k, fdt, (units, F, U, dk)), ("q", q, fdt, qshape),
               ("v", v, fdt, (units, F, U, dv)), ("gate", gate, fdt, (units, F, U, dv)),
               ("beta", beta, torch.float32, (units, F, U))]
     if text_k is not None:

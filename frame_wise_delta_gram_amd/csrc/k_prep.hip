@@ -709,7 +709,7 @@ hipError_t launch_prep_typed(const PrepPlan& p, const void* q, const void* k, co
     const unsigned per = xcd_per((unsigned)(p.batch * p.H) * p.tiles_r * p.tiles_c);
     const ConvSide<T> ks{static_cast<const T*>(k), wk_s, wk_t, static_cast<T*>(ko), p.dk};
     const ConvSide<T> vs{static_cast<const T*>(v), wv_s, wv_t, static_cast<T*>(vo), p.dv};
-    const unsigned qblocks = kQBlocks;
+    const unsigned qblocks = q ? kQBlocks : 0;  // no query pass without q
     if constexpr (std::is_same<T, uint16_t>::value)
       hipLaunchKernelGGL(prep_mfma_kernel, dim3(2 * kXcds * per + qblocks), dim3(kPrepThreads), 0,
                          s, ks, vs, p.F, p.Hl, p.Wl, p.H, p.tiles_r, p.tiles_c, p.batch * p.H, per,

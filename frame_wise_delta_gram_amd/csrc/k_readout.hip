@@ -112,7 +112,7 @@ __global__ __launch_bounds__(512, 4) void readout_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ gate,
     const float* __restrict__ wrms, uint16_t* __restrict__ out, const float* __restrict__ ST,
     const float* __restrict__ alpha, int dk_rt, int dv_rt, int F, int U, int C, int radius, int n,
-    float eps, int units, int nseg, int nblk, unsigned per, int anchors) {
+    float eps, int units, int nseg, int nblk, unsigned per, int anchors, int qh, float rqeps) {
   const int dk = DK > 0 ? DK : dk_rt;
   const int dv = DV > 0 ? DV : dv_rt;
   __shared__ __align__(16) uint16_t Shi[128 * 136];
@@ -121,12 +121,14 @@ __global__ __launch_bounds__(512, 4) void readout_bf16_kernel(
   __shared__ __align__(16) float Dbr[DECAY ? 256 : 1];  // bridge products (P: 0.., R: 128..)
 
   // work item = (unit, segment, row block), row block fastest: the blocks of
-  // one segment (which all read the same two states) share an XCD
+  // one segment (which all read the same two states) share an XCD; with q in
+  // the projection layout unit u reads head u % qh of entry u / qh
   const unsigned item = xcd_item(per);
   if (item >= (unsigned)units * nseg * nblk) return;
   const int blk = item % nblk;
   const int seg = (item / nblk) % nseg;
   const int u = item / (nblk * nseg);
+  const int hq = u % qh;
   const int c = DECAY ? seg / C : seg;
   const int f0 = DECAY ? seg : c * C;
   const int f1 = DECAY ? seg + 1 : min(f0 + C, F);
@@ -234,8 +236,10 @@ __global__ __launch_bounds__(512, 4) void readout_bf16_kernel(
   // One 16-row group: 4 k-steps of q (fetched one group ahead) and 4 channel
   // groups of gate (fetched when the group starts: first used after its MFMAs).
   auto grow_of = [&](long rg) { return chunk_row0 + (size_t)min(rg + jl, rows_total - 1); };
+  // the segment's first query row (row stride qh x d_k)
+  const uint16_t* qbase = q + ((((size_t)(u / qh) * F + f0) * U) * qh + hq) * dk;
   auto load_q = [&](u32x4_t (&qr)[4], long rg) {
-    const uint16_t* qp = q + grow_of(rg) * dk;
+    const uint16_t* qp = qbase + (size_t)min(rg + jl, rows_total - 1) * qh * dk;
 #pragma unroll
     for (int s = 0; s < 4; ++s)
       qr[s] = *reinterpret_cast<const u32x4_t*>(qp + min(32 * s + 8 * h, dk - 8));
@@ -252,11 +256,15 @@ __global__ __launch_bounds__(512, 4) void readout_bf16_kernel(
     f32x4_t acc[8];
 #pragma unroll
     for (int T = 0; T < 8; ++T) acc[T] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    float qq = 0.0f;  // the token's ||q||^2 (query map only)
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       if (s >= NKS) continue;
       u32x4_t b0 = qr[s];
       if (kpad && 32 * s + 8 * h >= dk) b0 = z4;
+      if (rqeps > 0.0f)
+#pragma unroll
+        for (int d = 0; d < 4; ++d) qq = dot2_bf16(b0[d], b0[d], qq);
 #pragma unroll
       for (int T = 0; T < 8; ++T) {
         if (T >= NT) continue;
@@ -275,7 +283,14 @@ __global__ __launch_bounds__(512, 4) void readout_bf16_kernel(
       for (int r = 0; r < 4; ++r) ss = fmaf(acc[T][r], acc[T][r], ss);
     ss += __shfl_xor(ss, 16);
     ss += __shfl_xor(ss, 32);
-    const float inv = rsqrtf(ss * inv_dv + eps);
+    // RMSNorm of o' = rn o, rn = 1 / max(||q||, q_l2_eps) with the query map, else 1
+    float rn = 1.0f;
+    if (rqeps > 0.0f) {
+      qq += __shfl_xor(qq, 16);
+      qq += __shfl_xor(qq, 32);
+      rn = fminf(rsqrtf(qq), rqeps);
+    }
+    const float inv = rn * rsqrtf(ss * (rn * rn) * inv_dv + eps);
     const long myrow = rg + jl;
     const bool live = myrow >= zlo && myrow < zhi;
     if (myrow < rows_total) {
@@ -445,20 +460,28 @@ __device__ __forceinline__ void c128_exchange(u32x4_t (&X)[4], bool b3) {
 constexpr int kGroupsC = 2;                       // 16-row groups per wave
 constexpr int kRowsC = 8 * 16 * kGroupsC;         // token rows per workgroup
 
+// QN: the query map (each query row L2-normalised in the epilogue, rqeps =
+// 1 / q_l2_eps); without it the kernel is the plain readout
+template <bool QN>
 __global__ __launch_bounds__(512, 4) void readout_c128_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ gate,
     const float* __restrict__ wrms, uint16_t* __restrict__ out, const uint16_t* __restrict__ Sp,
     int F, int U, int C, int radius, int n, float eps, int units, int nblk, unsigned per,
-    int anchors, int per_frame) {
+    int anchors, int per_frame, int qh, float rqeps) {
   __shared__ __align__(16) uint16_t S[kSplitBytes / 2];  // hi rows 0..127, lo rows 128..255
   __shared__ __align__(16) float Ws[128];
   // segments: chunks, or frames (per_frame: with decay each frame has its own S~)
   const int nseg = per_frame ? F : n;
   const unsigned item = xcd_item(per);
   if (item >= (unsigned)units * nseg * nblk) return;
+  // work item (unit, segment, block), block fastest: the blocks of one segment
+  // read the same image and share an XCD (its L2).  With q in the projection
+  // layout (qh > 1) unit u reads head u % qh of entry u / qh; this order
+  // measured faster than running the heads of one token block side by side
   const int blk = item % nblk;
   const int seg = (item / nblk) % nseg;
   const int u = item / (nblk * nseg);
+  const int hq = u % qh;
   const int c = per_frame ? seg / C : seg;
   const int f0 = per_frame ? seg : c * C;
   const int f1 = per_frame ? seg + 1 : min(f0 + C, F);
@@ -476,15 +499,19 @@ __global__ __launch_bounds__(512, 4) void readout_c128_kernel(
   const size_t chunk_row0 = ((size_t)u * F + f0) * U;
   const uint16_t* Shi = S;
   const uint16_t* Slo = S + 128 * kSRow;
+  // the segment's first row of gate / out, and of q (row stride qh x 128)
+  const uint16_t* gbase = gate + chunk_row0 * 128;
+  const uint16_t* qbase = q + ((((size_t)(u / qh) * F + f0) * U) * qh + hq) * 128;
+  const size_t qstride = (size_t)qh * 128;
   // lane's row (within a 16-row group) and 16-byte chunk in load / store instruction i
   auto row_in = [&](int i) { return 8 * (i >> 1) + (lane & 7); };
   auto chunk_in = [&](int i) { return 8 * (i & 1) + (lane >> 3); };
-  auto load16 = [&](u32x4_t (&X)[4], const uint16_t* base, long rg) {
+  auto load16 = [&](u32x4_t (&X)[4], const uint16_t* base, size_t stride, long rg) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const long r = min(rg + row_in(i), rows_total - 1);  // clamped: never stored
-      X[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(
-          base + (chunk_row0 + (size_t)r) * 128 + 8 * chunk_in(i)));
+      X[i] = __builtin_nontemporal_load(
+          reinterpret_cast<const u32x4_t*>(base + (size_t)r * stride + 8 * chunk_in(i)));
     }
   };
   auto grp_row = [&](int it) { return ((long)it * nblk + blk) * 128 + (long)w * 16; };
@@ -500,13 +527,26 @@ __global__ __launch_bounds__(512, 4) void readout_c128_kernel(
   }
   if (t < 128) Ws[t] = wrms[t];
   u32x4_t q0[4], q1[4], gr[4], g1[4];
-  load16(q0, q, grp_row(0));
-  load16(gr, gate, grp_row(0));
+  load16(q0, qbase, qstride, grp_row(0));
+  load16(gr, gbase, 128, grp_row(0));
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the DMA into LDS has landed
   __syncthreads();
 
   auto process = [&](u32x4_t (&qr)[4], u32x4_t (&g)[4], long rg) {
     c128_exchange(qr, b3);
+    // with the query map: rn = 1 / max(||q||, q_l2_eps) of this lane's token
+    // (its 128 channels: 32 per lane of the four lane groups)
+    float rn = 1.0f;
+    if (QN) {
+      float qq = 0.0f;
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+#pragma unroll
+        for (int d = 0; d < 4; ++d) qq = dot2_bf16(qr[s][d], qr[s][d], qq);
+      qq += __shfl_xor(qq, 16);
+      qq += __shfl_xor(qq, 32);
+      rn = fminf(rsqrtf(qq), rqeps);
+    }
     f32x4_t acc[8];
 #pragma unroll
     for (int T = 0; T < 8; ++T) acc[T] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
@@ -530,7 +570,8 @@ __global__ __launch_bounds__(512, 4) void readout_c128_kernel(
       for (int r = 0; r < 4; ++r) ss = fmaf(acc[T][r], acc[T][r], ss);
     ss += __shfl_xor(ss, 16);
     ss += __shfl_xor(ss, 32);
-    const float inv = rsqrtf(ss * (1.0f / 128.0f) + eps);
+    // RMSNorm of o' = rn o (rn = 1 without the query map)
+    const float inv = rn * rsqrtf(ss * (rn * rn) * (1.0f / 128.0f) + eps);
     const long myrow = rg + jl;
     const bool live = myrow >= zlo && myrow < zhi;
     u32x4_t ov[4];
@@ -565,8 +606,8 @@ __global__ __launch_bounds__(512, 4) void readout_c128_kernel(
   // two groups per wave: q and gate of the second are fetched before the first
   // is processed
   if (grp_row(0) >= rows_total) return;
-  load16(q1, q, grp_row(1));
-  load16(g1, gate, grp_row(1));
+  load16(q1, qbase, qstride, grp_row(1));
+  load16(g1, gbase, 128, grp_row(1));
   process(q0, gr, grp_row(0));
   if (grp_row(1) >= rows_total) return;
   process(q1, g1, grp_row(1));
@@ -581,15 +622,19 @@ constexpr int kRowsF = 64;
 __global__ __launch_bounds__(256) void readout_f32_kernel(
     const float* __restrict__ q, const float* __restrict__ gate, const float* __restrict__ wrms,
     float* __restrict__ out, const float* __restrict__ ST, const float* __restrict__ alpha, int dk,
-    int dv, int F, int U, int C, int radius, int n, float eps, int nseg, int nblk, int anchors) {
+    int dv, int F, int U, int C, int radius, int n, float eps, int nseg, int nblk, int anchors,
+    int qh, float rqeps) {
   __shared__ float Ss[128 * SG];
   __shared__ float Qs[kRowsF * SG];
   __shared__ float Dbr[256];
   const bool decay = alpha != nullptr;
+  // work item (unit, segment, row block); with q in the projection layout unit
+  // u reads head u % qh of entry u / qh
   const unsigned item = blockIdx.x;
   const int blk = item % nblk;
   const int seg = (item / nblk) % nseg;
   const int u = item / (nblk * nseg);
+  const int hq = u % qh;
   const int c = decay ? seg / C : seg;
   const int f0 = decay ? seg : c * C;
   const int f1 = decay ? seg + 1 : min(f0 + C, F);
@@ -614,11 +659,12 @@ __global__ __launch_bounds__(256) void readout_f32_kernel(
     Ss[i * SG + j] = decay ? P[idx] * Dbr[j] + R[idx] * Dbr[128 + j] : P[idx] + R[idx];
   }
   const size_t chunk_row0 = ((size_t)u * F + f0) * U;
+  const float* qbase = q + ((((size_t)(u / qh) * F + f0) * U) * qh + hq) * dk;
   for (int idx = t; idx < kRowsF * dk; idx += 256) {
     const int i = idx / dk;
     const int j = idx - i * dk;
     const long row = row0 + i;
-    Qs[i * SG + j] = row < rows_total ? q[(chunk_row0 + row) * dk + j] : 0.0f;
+    Qs[i * SG + j] = row < rows_total ? qbase[(size_t)row * qh * dk + j] : 0.0f;
   }
   __syncthreads();
   const int lr = t >> 2;
@@ -637,7 +683,16 @@ __global__ __launch_bounds__(256) void readout_f32_kernel(
   }
   ss += __shfl_xor(ss, 1);
   ss += __shfl_xor(ss, 2);
-  const float inv = 1.0f / sqrtf(ss / (float)dv + eps);
+  // RMSNorm of o' = rn o, rn = 1 / max(||q||, q_l2_eps) with the query map, else 1
+  float rn = 1.0f;
+  if (rqeps > 0.0f) {
+    float qq = 0.0f;
+    for (int kx = part; kx < dk; kx += 4) qq = fmaf(Qs[lr * SG + kx], Qs[lr * SG + kx], qq);
+    qq += __shfl_xor(qq, 1);
+    qq += __shfl_xor(qq, 2);
+    rn = fminf(1.0f / sqrtf(qq), rqeps);
+  }
+  const float inv = rn / sqrtf(ss * (rn * rn) / (float)dv + eps);
   if (myrow < rows_total) {
     const size_t grow = chunk_row0 + (size_t)myrow;
     const bool live = myrow >= zlo && myrow < zhi;
@@ -654,6 +709,9 @@ __global__ __launch_bounds__(256) void readout_f32_kernel(
 
 }  // namespace
 
+// 1 / q_l2_eps with the query map (q_l2_eps >= FLT_MIN, so finite), else 0
+static float query_map_rcp(const Plan& p) { return p.qeps > 0.0f ? 1.0f / p.qeps : 0.0f; }
+
 template <int DK, int DV, bool DECAY>
 void launch_readout_bf16(const Plan& p, const void* q, const void* gate, const float* rms_weight,
                          void* out, const WsPtrs& w, const float* alpha, int nseg, int nblk,
@@ -662,7 +720,8 @@ void launch_readout_bf16(const Plan& p, const void* q, const void* gate, const f
   hipLaunchKernelGGL((readout_bf16_kernel<DK, DV, DECAY>), dim3(kXcds * per), dim3(kThreadsR), 0,
                      s, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(gate),
                      rms_weight, static_cast<uint16_t*>(out), w.ST, alpha, p.dk, p.dv, p.F, p.U,
-                     p.C, p.r, p.n, p.eps, p.units, nseg, nblk, per, p.anchors);
+                     p.C, p.r, p.n, p.eps, p.units, nseg, nblk, per, p.anchors, p.qh,
+                     query_map_rcp(p));
 }
 
 hipError_t launch_split(const Plan& p, const WsPtrs& w, const float* alpha, hipStream_t s) {
@@ -690,11 +749,12 @@ hipError_t launch_readout(const Plan& p, const void* q, const void* gate, const 
     if (d128) {  // the split images were written by launch_split after the scans
       const int nb = (int)((max_rows + kRowsC - 1) / kRowsC);
       const unsigned per = xcd_per((unsigned)p.units * nseg * nb);
-      hipLaunchKernelGGL(readout_c128_kernel, dim3(kXcds * per), dim3(kThreadsR), 0, s,
+      hipLaunchKernelGGL(p.qeps > 0.0f ? readout_c128_kernel<true> : readout_c128_kernel<false>,
+                         dim3(kXcds * per), dim3(kThreadsR), 0, s,
                          static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(gate),
                          rms_weight, static_cast<uint16_t*>(out), alpha ? decay_images(w) : w.Sp,
                          p.F, p.U, p.C, p.r, p.n, p.eps, p.units, nb, per, p.anchors,
-                         alpha ? 1 : 0);
+                         alpha ? 1 : 0, p.qh, query_map_rcp(p));
     } else if (alpha)
       launch_readout_bf16<0, 0, true>(p, q, gate, rms_weight, out, w, alpha, nseg, nblk, s);
     else
@@ -705,7 +765,7 @@ hipError_t launch_readout(const Plan& p, const void* q, const void* gate, const 
     hipLaunchKernelGGL(readout_f32_kernel, dim3(items), dim3(kThreads), 0, s,
                        static_cast<const float*>(q), static_cast<const float*>(gate), rms_weight,
                        static_cast<float*>(out), w.ST, alpha, p.dk, p.dv, p.F, p.U, p.C, p.r, p.n,
-                       p.eps, nseg, nblk, p.anchors);
+                       p.eps, nseg, nblk, p.anchors, p.qh, query_map_rcp(p));
   }
   return hipGetLastError();
 }

@@ -41,6 +41,11 @@ int make_plan(const vda_desc_t* d, Plan* p) {
   if (d->fp32_products != 0 && d->fp32_products != 1) return VDA_ERR_INVALID_ARG;
   if (d->solver != 0 && d->solver != 1) return VDA_ERR_INVALID_ARG;
   if (d->solver == 1 && d->rule != 0) return VDA_ERR_INVALID_ARG;  // a factor of I + A_t only
+  if (d->q_heads < 0 || d->q_heads > kMaxGridYZ) return VDA_ERR_INVALID_ARG;
+  if (d->q_heads > 1 && d->units % d->q_heads != 0) return VDA_ERR_INVALID_ARG;
+  // 0, or a normal float (its reciprocal is finite)
+  if (!isfinite(d->q_l2_eps) || (d->q_l2_eps != 0.0f && !(d->q_l2_eps >= 1.17549435e-38f)))
+    return VDA_ERR_INVALID_ARG;
   if (d->units > kMaxGridYZ) return VDA_ERR_INVALID_ARG;
   const int64_t n = d->frames > 0 ? (d->frames + (int64_t)d->chunk - 1) / d->chunk : 0;
   if (n > kMaxGridYZ) return VDA_ERR_INVALID_ARG;
@@ -91,6 +96,8 @@ int make_plan(const vda_desc_t* d, Plan* p) {
   p->fp32_products = d->fp32_products != 0 || d->in_dtype == VDA_DTYPE_F32;
   p->solver = d->solver;
   p->dtype = d->in_dtype;
+  p->qh = d->q_heads > 1 ? d->q_heads : 1;
+  p->qeps = d->q_l2_eps;
 
   const size_t U_ = (size_t)p->units, Fp1 = (size_t)p->F + 1, N = (size_t)p->n;
   const size_t kk = (size_t)p->dk * p->dk * 4, vk = (size_t)p->dv * p->dk * 4;
@@ -583,11 +590,12 @@ int vda_prep(const vda_prep_desc_t* desc, const void* q, const void* k, const vo
   if (st != VDA_OK) return st;
   const int64_t rows = (int64_t)p.batch * p.H * p.F * p.U;
   if (rows == 0) return VDA_OK;
-  if (!q || !k || !v || !q_out || !k_out || !v_out || !wk_s || !wk_t || !wv_s || !wv_t)
-    return VDA_ERR_INVALID_ARG;
+  // q and q_out both NULL: K' and V' only (the query map runs in the readout)
+  if ((q == nullptr) != (q_out == nullptr)) return VDA_ERR_INVALID_ARG;
+  if (!k || !v || !k_out || !v_out || !wk_s || !wk_t || !wv_s || !wv_t) return VDA_ERR_INVALID_ARG;
   for (const void* ptr : {q, k, v, static_cast<const void*>(q_out), static_cast<const void*>(k_out),
                           static_cast<const void*>(v_out)})
-    if (!vda::aligned(ptr, 16)) return VDA_ERR_MISALIGNED;
+    if (ptr && !vda::aligned(ptr, 16)) return VDA_ERR_MISALIGNED;
   for (const float* ptr : {wk_s, wk_t, wv_s, wv_t})
     if (!vda::aligned(ptr, 4)) return VDA_ERR_MISALIGNED;
   return vda::hip_status(vda::launch_prep(p, q, k, v, wk_s, wk_t, wv_s, wv_t, q_out, k_out, v_out,

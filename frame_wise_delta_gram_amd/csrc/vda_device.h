@@ -80,6 +80,13 @@ __device__ __forceinline__ uint32_t pack_bf16(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, r);
 }
 
+// c + a.lo b.lo + a.hi b.hi for two packed bf16 pairs (v_dot2c_f32_bf16; the
+// bf16 products are exact in fp32)
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                         __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+
 // Make this wave's earlier LDS writes visible to its other lanes (LDS
 // operations of one wave execute in order; this stops the compiler from
 // moving memory accesses across the point).

@@ -34,6 +34,8 @@ struct Plan {
   int rule;       // 0: frame-wise delta rule; 1, 2: batched comparison rules
   bool fp32_products;  // composition and scan on fp32 MFMA (always for fp32 features)
   int solver;     // 0: symmetric Gauss-Jordan sweep; 1: blocked Cholesky
+  int qh;         // heads interleaved in q (1: the unit layout)
+  float qeps;     // > 0: the readout L2-normalises each query row with this floor
   bool decay_ok;  // the decay path's launch grids fit too
   bool full_stats;  // store both triangles of every A_t (else the lower 32 x 32 blocks
                    // of latent frames only: all the frame-wise solve reads)

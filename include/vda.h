@@ -28,6 +28,12 @@
  *   5. the readout ([VDN] Eq. (1a), App. A.3 Eq. (A.4) with alpha = 1, Eq. (1c)):
  *      a query of chunk c reads S~ = P[max(c - radius, 0)] + R[min(c + radius + 1, n)],
  *      o = S~ q, y = w * o / sqrt(mean(o^2) + eps), out = sigmoid(g) * y.
+ *      With desc->q_l2_eps > 0 the query is first normalised to unit L2 norm,
+ *      q' = q / max(||q||_2, q_l2_eps) (the feature map's query map, [VDN]
+ *      Sec. 2.3); o is linear in q and the RMSNorm undoes any scale but its
+ *      eps, so the readout forms o = S~ q from the raw query and takes
+ *      y = w * o / sqrt(mean(o^2) + eps * max(||q||^2, q_l2_eps^2)), which
+ *      equals the normalised query's result up to rounding.
  *
  * With channel-wise decay (vda_forward_decay; [VDN] Sec. 3.1 Eq. (2), App. A.1
  * Eq. (A.1) and App. A.3 Eq. (A.4)), frame t carries gates alpha_t in [0, 1]^d_k:
@@ -58,7 +64,10 @@
  * run without decay (the decay entry points reject rule != 0).
  *
  * Layouts (row-major, last index fastest, all tensors contiguous):
- *   q     [units][frames][tokens][d_k]   in_dtype
+ *   q     [units][frames][tokens][d_k]   in_dtype (desc->q_heads <= 1), or with
+ *         q_heads = H > 1 [units / H][frames][tokens][H][d_k]: the QKV projection's
+ *         layout, heads interleaved per token (vda_prep's input order with
+ *         tokens = height x width), unit u = b x H + h reading head h of entry b
  *   k     [units][frames][tokens][d_k]   in_dtype (prepared features)
  *   v     [units][frames][tokens][d_v]   in_dtype
  *   beta  [units][frames][tokens]        float32, >= 0 (write strengths)
@@ -140,6 +149,12 @@ typedef struct vda_desc {
                           (block sweep, the default); 1 = blocked Cholesky factorisation
                           I + A_t = L L^T, then M_t = L^-T L^-1 (same result to rounding);
                           rules 1, 2 take 0 only */
+  int32_t q_heads;     /* 0 or 1: q in the unit layout; H > 1 (dividing units, <= 65535):
+                          q in the projection layout with H heads per token (above) */
+  float q_l2_eps;      /* 0: q read as given; > 0 (finite): each query row normalised to
+                          unit L2 norm with this floor inside the readout (above), so
+                          the feature map's query pass can be skipped (vda_prep with
+                          q = q_out = NULL) */
 } vda_desc_t;
 
 /* Bytes of device workspace vda_forward and the debug taps need for `desc`
@@ -237,7 +252,11 @@ int vda_forward_decay(const vda_desc_t* desc, const void* q, const void* k, cons
  *   q, k out  [batch * heads][frames][height * width][d_k] dtype (unit = b * heads + h)
  *   v out     [batch * heads][frames][height * width][d_v] dtype
  * The outputs are exactly the q, k, v layouts of vda_forward (tokens =
- * height * width).  Outputs must not overlap inputs.  Arithmetic is fp32;
+ * height * width).  Outputs must not overlap inputs.  q and q_out may both be
+ * NULL: then only K' and V' are formed (the query map is left to vda_forward,
+ * which takes the raw projection q with q_heads = heads and q_l2_eps = eps and
+ * normalises each query inside its readout, saving the query pass's read and
+ * write of q; one NULL without the other is VDA_ERR_INVALID_ARG).  Arithmetic is fp32;
  * with bf16 features the spatial filter runs on the matrix cores with each tap
  * split into bf16 hi + lo (the tap to about 2^-17 relative, every product
  * exact, fp32 accumulation). */

@@ -74,6 +74,8 @@ int main(void) {
     d.rule = DRAW(kFlagOk, kFlagEdge);
     d.fp32_products = DRAW(kFlagOk, kFlagEdge);
     d.solver = DRAW(kFlagOk, kFlagEdge);
+    d.q_heads = (next_u32() & 3u) ? 0 : DRAW(kChunkOk, kSmallEdge);
+    d.q_l2_eps = (next_u32() & 3u) ? 0.0f : pick_eps();
     const int st = vda_check_desc(&d);
     const size_t ws = vda_workspace_bytes(&d);
     if (st != VDA_OK && ws != 0) {

@@ -84,6 +84,8 @@ def test_prep_argument_errors(lib):
     d = prep_desc()
     P = [4096 * (i + 1) for i in range(10)]
     assert lib.vda_prep(ctypes.byref(d), None, *P[1:], None) == vda.VDA_ERR_INVALID_ARG
+    # q and q_out are left out together or not at all
+    assert lib.vda_prep(ctypes.byref(d), *P[:7], None, *P[8:], None) == vda.VDA_ERR_INVALID_ARG
     assert lib.vda_prep(ctypes.byref(d), *P[:9], None, None) == vda.VDA_ERR_INVALID_ARG
     assert lib.vda_prep(ctypes.byref(d), P[0] + 8, *P[1:], None) == vda.VDA_ERR_MISALIGNED
     assert lib.vda_prep(ctypes.byref(d), *P[:3], P[3] + 2, *P[4:], None) == \
@@ -176,6 +178,18 @@ def test_workspace_formula(lib):
     (dict(dtype=7), vda.VDA_ERR_BAD_DTYPE),
     (dict(units=0, frames=0, tokens=0), vda.VDA_OK),
     (dict(d_k=16, d_v=128), vda.VDA_OK),
+    # the query map: q_heads divides units (0 and 1 mean the unit layout), q_l2_eps
+    # is 0 or a finite normal float
+    (dict(q_heads=2), vda.VDA_OK),
+    (dict(q_heads=1, q_l2_eps=1e-6), vda.VDA_OK),
+    (dict(q_heads=3), vda.VDA_ERR_INVALID_ARG),
+    (dict(q_heads=-1), vda.VDA_ERR_INVALID_ARG),
+    (dict(q_heads=70000), vda.VDA_ERR_INVALID_ARG),
+    (dict(q_l2_eps=-1e-6), vda.VDA_ERR_INVALID_ARG),
+    (dict(q_l2_eps=float("nan")), vda.VDA_ERR_INVALID_ARG),
+    (dict(q_l2_eps=float("inf")), vda.VDA_ERR_INVALID_ARG),
+    (dict(q_l2_eps=1e-40), vda.VDA_ERR_INVALID_ARG),
+    (dict(q_l2_eps=1.1754944e-38), vda.VDA_OK),
 ])
 def test_descriptor_checks(lib, kw, status):
     assert vda.vda_check_desc(desc(**kw)) == status

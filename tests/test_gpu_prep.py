@@ -214,3 +214,35 @@ def test_prep_random_shapes(name, cfg):
         say(f"  {label}' max row-rel err {err:.3e}")
         assert g.shape == r.shape and np.all(np.isfinite(g))
         assert err <= TOL[cfg.dtype], label
+
+
+@pytest.mark.parametrize("name", ["small-bf16", "partial-tiles-bf16", "dk128-f32"])
+def test_prep_without_query_pass(name):
+    """q = q_out = NULL (the query map left to the forward's readout): k' and v'
+    are bitwise those of the full call, and nothing is written for q."""
+    require_gpu()
+    import torch
+    import frame_wise_delta_gram_amd as vda
+    cfg = SHAPES[name]
+    say(f"[prep] {name} without the query pass")
+    h = W.host_prep_inputs(cfg)
+    dt = vda.VDA_DTYPE_BF16 if cfg.dtype == "bf16" else vda.VDA_DTYPE_F32
+    desc = vda.make_prep_desc(cfg.batch, cfg.heads, cfg.frames, cfg.height, cfg.width,
+                              cfg.d_k, cfg.d_v, cfg.eps, dt)
+    d = {name: (W.host_to_tensor(x, cfg.dtype if name in ("q", "k", "v") else "f32", "cuda")
+                if isinstance(x, np.ndarray) else x) for name, x in h.items()}
+    tdt = d["q"].dtype
+    N, F, Uq = cfg.units, cfg.frames, cfg.tokens
+    outs = []
+    for with_q in (True, False):
+        qo = torch.full((N, F, Uq, cfg.d_k), 7.0, dtype=tdt, device="cuda")
+        ko = torch.empty_like(qo)
+        vo = torch.empty((N, F, Uq, cfg.d_v), dtype=tdt, device="cuda")
+        vda.vda_prep(desc, d["q"] if with_q else None, d["k"], d["v"], d["wk_s"], d["wk_t"],
+                     d["wv_s"], d["wv_t"], qo if with_q else None, ko, vo)
+        torch.cuda.synchronize()
+        outs.append((qo, ko, vo))
+    bits = (lambda t: t.view(torch.int16)) if tdt == torch.bfloat16 else (lambda t: t)
+    assert torch.equal(bits(outs[0][1]), bits(outs[1][1]))
+    assert torch.equal(bits(outs[0][2]), bits(outs[1][2]))
+    assert torch.all(outs[1][0] == 7.0)
