@@ -584,7 +584,7 @@ __global__ __launch_bounds__(kPrepThreads, 1) void prep_mfma_kernel(
   const int gi_out = r0 + orow;
   const int ylane = (gi_out * Wl + c0) * d + ch;  // in-frame offset (the frame is < 2^31 bytes)
   // the finished output frame t_out from pend: scale (K: by the inverse norms of
-  // its 8 positions, from invs) and store one channel per lane
+  // its 8 positions, from invs) and store it, a channel pair per 4-byte store
   auto finish = [&](int t_out) {
     if (!gact || gi_out >= Hl) return;
     f32x4_t sc[2] = {f32x4_t{1.0f, 1.0f, 1.0f, 1.0f}, f32x4_t{1.0f, 1.0f, 1.0f, 1.0f}};
@@ -592,15 +592,27 @@ __global__ __launch_bounds__(kPrepThreads, 1) void prep_mfma_kernel(
       sc[0] = *reinterpret_cast<const f32x4_t*>(Is + orow * 8);
       sc[1] = *reinterpret_cast<const f32x4_t*>(Is + orow * 8 + 4);
     }
-    uint16_t* const yt = y + ((size_t)unit * F + t_out) * U * d + ylane;
+    // lanes l and l ^ 4 hold channels 2 j and 2 j + 1 of the same row: the even
+    // one stores both channels of columns 0 .. 3, the odd one of columns 4 .. 7,
+    // one 4-byte store per column (DPP row rotations by 4 and 12 reach l ^ 4)
+    const bool odd = (lane >> 2) & 1;
+    float v[8];
 #pragma unroll
     for (int xb = 0; xb < 2; ++xb)
 #pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        const int col = 4 * xb + m;
-        if (c0 + col < Wl)
-          yt[(size_t)col * d] = __builtin_bit_cast(uint16_t, (__bf16)(pend[xb][m] * sc[xb][m]));
-      }
+      for (int m = 0; m < 4; ++m) v[4 * xb + m] = pend[xb][m] * sc[xb][m];
+    uint32_t* const yt = reinterpret_cast<uint32_t*>(y + ((size_t)unit * F + t_out) * U * d +
+                                                      ylane - (odd ? 1 : 0));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int send = __float_as_int(odd ? v[i] : v[4 + i]);
+      const int r4 = __builtin_amdgcn_update_dpp(0, send, 0x124, 0xF, 0xF, false);   // row_ror:4
+      const int r12 = __builtin_amdgcn_update_dpp(0, send, 0x12C, 0xF, 0xF, false);  // row_ror:12
+      const float got = __int_as_float(odd ? r4 : r12);
+      const int col = (odd ? 4 : 0) + i;
+      const uint32_t wv = odd ? pack_bf16(got, v[4 + i]) : pack_bf16(v[i], got);
+      if (c0 + col < Wl) yt[(size_t)col * (d >> 1)] = wv;
+    }
   };
 
   auto step = [&](int tin, auto kc) {
