@@ -47,6 +47,12 @@ EDGE = {
                        dtype="f32"),
     "eps-zero-f32": C(cfg_id=313, units=1, frames=10, tokens=16, d_k=16, d_v=16, text_tokens=8,
                       dtype="f32", rms_eps=0.0),
+    # d_k = d_v = 128 (the scans on the composition's pre-split operand images): a one-frame
+    # last chunk, and every chunk one frame
+    "d128-one-frame-last-chunk": C(cfg_id=316, units=2, frames=11, tokens=40, d_k=128, d_v=128,
+                                   text_tokens=5, dtype="bf16"),
+    "d128-chunk1": C(cfg_id=317, units=2, frames=6, tokens=24, d_k=128, d_v=128, text_tokens=3,
+                     dtype="bf16", chunk=1, radius=1),
 }
 
 
