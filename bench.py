@@ -57,14 +57,19 @@ def algorithmic(cfg):
     work is then counted there and "stats_text" is zero); with decay the gates
     are read once by the composition and once by the split kernel (bf16,
     d_k = d_v = 128: one split image per frame) or the readout (other shapes),
-    and the composition also writes the reverse maps."""
+    and the composition also writes the reverse maps; at bf16 with
+    d_k = d_v = 128 without decay under the frame-wise rule the composition
+    writes Mc and the scans' two operand images of it (one transition's size
+    each) in place of Mc^T."""
     eb = 2 if cfg.dtype == "bf16" else 4
     th = cfg.units * cfg.frames * cfg.tokens        # token-heads
     tt = cfg.units * cfg.text_tokens
     dk, dv, n, u, F = cfg.d_k, cfg.d_v, cfg.n_chunks, cfg.units, cfg.frames
     mat, st = dk * dk * 4, dv * dk * 4               # one transition, one state (fp32)
     gates = u * F * dk * 4 if cfg.alpha_mu is not None else 0
-    nmaps = 3 if cfg.alpha_mu is not None else 2     # Mc, Mc^T (+ Mr^T)
+    images = (cfg.dtype == "bf16" and dk == 128 and dv == 128 and cfg.alpha_mu is None
+              and cfg.rule == 0)
+    nmaps = 3 if cfg.alpha_mu is not None or images else 2  # Mc, Mc^T (+ Mr^T), or Mc + images
     # A is symmetric: under the frame-wise rule the kernel writes its blocks on
     # and below the diagonal (all the solve reads); the batched rules read all of A
     nkb = -(-dk // 32)
