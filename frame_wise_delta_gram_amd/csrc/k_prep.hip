@@ -472,244 +472,252 @@ __global__ __launch_bounds__(kPrepThreads, 1) void prep_mfma_kernel(
   const bool norm = jq < per;              // K first, then V
   const unsigned item = (blockIdx.x % kXcds) * per + (norm ? jq : jq - per);
   if (jq >= 2 * per || item >= (unsigned)units * ntiles) return;
-  const ConvSide<uint16_t> side = norm ? ks : vs;
-  const uint16_t* __restrict__ x = side.x;
-  const float* __restrict__ ws = side.ws;
-  const float* __restrict__ wt = side.wt;
-  uint16_t* __restrict__ y = side.y;
-  const int d = side.d;
-  const int unit = item / ntiles;
-  const int tile = item - unit * ntiles;
-  const int b = unit / H;
-  const int h = unit - b * H;
-  const int r0 = (tile / tiles_c) * kTR;
-  const int c0 = (tile % tiles_c) * kTC;
-  const int t = threadIdx.x;
-  const int lane = t & 63;
-  const int w = t >> 6;
-  const int U = Hl * Wl;
+  // K (NORM: L2-normalised) and V sweeps as two compiled bodies
+  auto sweep = [&](auto nc) {
+    constexpr bool NORM = decltype(nc)::value;
+    const ConvSide<uint16_t> side = NORM ? ks : vs;
+    const uint16_t* __restrict__ x = side.x;
+    const float* __restrict__ ws = side.ws;
+    const float* __restrict__ wt = side.wt;
+    uint16_t* __restrict__ y = side.y;
+    const int d = side.d;
+    const int unit = item / ntiles;
+    const int tile = item - unit * ntiles;
+    const int b = unit / H;
+    const int h = unit - b * H;
+    const int r0 = (tile / tiles_c) * kTR;
+    const int c0 = (tile % tiles_c) * kTC;
+    const int t = threadIdx.x;
+    const int lane = t & 63;
+    const int w = t >> 6;
+    const int U = Hl * Wl;
 
-  // this wave's compute role: channel group g (16 channels), output rows
-  // 4 hh .. 4 hh + 3 (lane (blk, n): row 4 hh + n), both column blocks
-  const int g = w & 7;
-  const int hh = w >> 3;
-  const bool gact = 16 * g < d;
-  const int blk = lane >> 2;
-  const int n = lane & 3;
-  const int ch = 16 * g + blk;  // this lane's channel (operands and accumulators)
+    // this wave's compute role: channel group g (16 channels), output rows
+    // 4 hh .. 4 hh + 3 (lane (blk, n): row 4 hh + n), both column blocks
+    const int g = w & 7;
+    const int hh = w >> 3;
+    const bool gact = 16 * g < d;
+    const int blk = lane >> 2;
+    const int n = lane & 3;
+    const int ch = 16 * g + blk;  // this lane's channel (operands and accumulators)
 
-  // tap table: each active lane writes its own A operands (row n of T_a, per
-  // row a and k step, hi and lo); temporal taps to LDS as well
-  {
-    const float* wsc = ws + ((size_t)h * d + (gact ? ch : 0)) * 25;
-    if (gact) {
-#pragma unroll
-      for (int a = 0; a < 5; ++a)
-#pragma unroll
-        for (int s = 0; s < 2; ++s) {
-          float v[4];
-#pragma unroll
-          for (int kk = 0; kk < 4; ++kk) {
-            const int dx = 4 * s + kk - n;
-            v[kk] = (dx >= 0 && dx <= 4) ? wsc[a * 5 + max(0, min(dx, 4))] : 0.0f;
+    // tap table: each active lane writes its own A operands (row n of T_a, per
+    // row a and k step, hi and lo); temporal taps to LDS as well
+    {
+      const float* wsc = ws + ((size_t)h * d + (gact ? ch : 0)) * 25;
+      if (gact) {
+  #pragma unroll
+        for (int a = 0; a < 5; ++a)
+  #pragma unroll
+          for (int s = 0; s < 2; ++s) {
+            float v[4];
+  #pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+              const int dx = 4 * s + kk - n;
+              v[kk] = (dx >= 0 && dx <= 4) ? wsc[a * 5 + max(0, min(dx, 4))] : 0.0f;
+            }
+            const uint32_t h0 = pack_bf16(v[0], v[1]), h1 = pack_bf16(v[2], v[3]);
+            *reinterpret_cast<u32x2_t*>(Wt + wt_word(ch, a, s, 0, n)) = u32x2_t{h0, h1};
+            *reinterpret_cast<u32x2_t*>(Wt + wt_word(ch, a, s, 1, n)) =
+                u32x2_t{pack_bf16(v[0] - bf16_lo(h0), v[1] - bf16_hi(h0)),
+                        pack_bf16(v[2] - bf16_lo(h1), v[3] - bf16_hi(h1))};
           }
-          const uint32_t h0 = pack_bf16(v[0], v[1]), h1 = pack_bf16(v[2], v[3]);
-          *reinterpret_cast<u32x2_t*>(Wt + wt_word(ch, a, s, 0, n)) = u32x2_t{h0, h1};
-          *reinterpret_cast<u32x2_t*>(Wt + wt_word(ch, a, s, 1, n)) =
-              u32x2_t{pack_bf16(v[0] - bf16_lo(h0), v[1] - bf16_hi(h0)),
-                      pack_bf16(v[2] - bf16_lo(h1), v[3] - bf16_hi(h1))};
+      }
+      if (n == 0) {  // zero for channels past d (their accumulators stay zero)
+        const float* wtc = wt + ((size_t)h * d + (gact ? ch : 0)) * 5;
+  #pragma unroll
+        for (int i = 0; i < 5; ++i) Ft[i * 128 + ch] = gact ? wtc[i] : 0.0f;
+      }
+    }
+
+    // staging: wave w takes the halo slots w, w + 16, w + 32 (those below 36;
+    // slot 3 hr + q = row hr, columns 4 q .. 4 q + 3), lane l the channel pair
+    // 2 l, 2 l + 1: one 4-byte load per column (a wave instruction reads one
+    // position's whole row of channels), so a lane ends holding its two channels
+    // at the slot's four columns, which two byte permutes per channel turn into
+    // the slot's two 8-byte rows.  Positions are wave-uniform: the scalar offset
+    // of a position outside the frame lies past the descriptor's range and reads
+    // as zero.
+    constexpr int kSlots = kHR * (kHC / 4);
+    constexpr int kSlotIter = (kSlots + kWaves - 1) / kWaves;
+    const int wu = __builtin_amdgcn_readfirstlane(w);
+    const bool pact = 2 * lane < d;
+    const int frame_bytes = U * H * d * (int)sizeof(uint16_t);
+    uint32_t pre[kSlotIter][4];
+    auto load_frame = [&](int tin) {
+      const __amdgpu_buffer_rsrc_t rs = make_rsrc(x + ((size_t)b * F + tin) * U * H * d, frame_bytes);
+  #pragma unroll
+      for (int j = 0; j < kSlotIter; ++j) {
+        const int sl = wu + kWaves * j;
+        if (sl >= kSlots) break;
+        const int gi = r0 - 2 + sl / 3;
+  #pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const int gj = c0 - 2 + 4 * (sl % 3) + k;
+          const bool ok = gi >= 0 && gi < Hl && gj >= 0 && gj < Wl;
+          const int soff = ok ? ((gi * Wl + gj) * H + h) * d * (int)sizeof(uint16_t) : frame_bytes;
+          pre[j][k] = __builtin_amdgcn_raw_buffer_load_b32(rs, 4 * lane, soff, 0);
         }
-    }
-    if (n == 0) {  // zero for channels past d (their accumulators stay zero)
-      const float* wtc = wt + ((size_t)h * d + (gact ? ch : 0)) * 5;
-#pragma unroll
-      for (int i = 0; i < 5; ++i) Ft[i * 128 + ch] = gact ? wtc[i] : 0.0f;
-    }
-  }
-
-  // staging: wave w takes the halo slots w, w + 16, w + 32 (those below 36;
-  // slot 3 hr + q = row hr, columns 4 q .. 4 q + 3), lane l the channel pair
-  // 2 l, 2 l + 1: one 4-byte load per column (a wave instruction reads one
-  // position's whole row of channels), so a lane ends holding its two channels
-  // at the slot's four columns, which two byte permutes per channel turn into
-  // the slot's two 8-byte rows.  Positions are wave-uniform: the scalar offset
-  // of a position outside the frame lies past the descriptor's range and reads
-  // as zero.
-  constexpr int kSlots = kHR * (kHC / 4);
-  constexpr int kSlotIter = (kSlots + kWaves - 1) / kWaves;
-  const int wu = __builtin_amdgcn_readfirstlane(w);
-  const bool pact = 2 * lane < d;
-  const int frame_bytes = U * H * d * (int)sizeof(uint16_t);
-  uint32_t pre[kSlotIter][4];
-  auto load_frame = [&](int tin) {
-    const __amdgpu_buffer_rsrc_t rs = make_rsrc(x + ((size_t)b * F + tin) * U * H * d, frame_bytes);
-#pragma unroll
-    for (int j = 0; j < kSlotIter; ++j) {
-      const int sl = wu + kWaves * j;
-      if (sl >= kSlots) break;
-      const int gi = r0 - 2 + sl / 3;
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const int gj = c0 - 2 + 4 * (sl % 3) + k;
-        const bool ok = gi >= 0 && gi < Hl && gj >= 0 && gj < Wl;
-        const int soff = ok ? ((gi * Wl + gj) * H + h) * d * (int)sizeof(uint16_t) : frame_bytes;
-        pre[j][k] = __builtin_amdgcn_raw_buffer_load_b32(rs, 4 * lane, soff, 0);
       }
-    }
-  };
-  auto store_frame = [&]() {
-    if (!pact) return;
-#pragma unroll
-    for (int j = 0; j < kSlotIter; ++j) {
-      const int sl = wu + kWaves * j;
-      if (sl >= kSlots) break;
-      const uint32_t* v = pre[j];  // v[k] = channels 2 l, 2 l + 1 at column 4 q + k
-      const u32x2_t lo = u32x2_t{__builtin_amdgcn_perm(v[1], v[0], 0x05040100u),
-                                 __builtin_amdgcn_perm(v[3], v[2], 0x05040100u)};
-      const u32x2_t hi = u32x2_t{__builtin_amdgcn_perm(v[1], v[0], 0x07060302u),
-                                 __builtin_amdgcn_perm(v[3], v[2], 0x07060302u)};
-      // channel 2 l + 1 sits one channel pitch after 2 l: (2 l + 1) / 4 = 2 l / 4
-      const int wd = xs_word(2 * lane, sl / 3, sl % 3);
-      *reinterpret_cast<u32x2_t*>(Xs + wd) = lo;
-      *reinterpret_cast<u32x2_t*>(Xs + wd + kXPitch) = hi;
-    }
-  };
-
-  f32x4_t ring[4][2];
-#pragma unroll
-  for (int sl = 0; sl < 4; ++sl) ring[sl][0] = ring[sl][1] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-  f32x4_t pend[2];  // SiLU of the last finished output frame, stored one step later
-
-  const int orow = 4 * hh + n;  // this lane's output row in the tile
-  const int gi_out = r0 + orow;
-  const int ylane = (gi_out * Wl + c0) * d + ch;  // in-frame offset (the frame is < 2^31 bytes)
-  // the finished output frame t_out from pend: scale (K: by the inverse norms of
-  // its 8 positions, from invs) and store it, a channel pair per 4-byte store
-  auto finish = [&](int t_out) {
-    if (!gact || gi_out >= Hl) return;
-    f32x4_t sc[2] = {f32x4_t{1.0f, 1.0f, 1.0f, 1.0f}, f32x4_t{1.0f, 1.0f, 1.0f, 1.0f}};
-    if (norm) {
-      sc[0] = *reinterpret_cast<const f32x4_t*>(Is + orow * 8);
-      sc[1] = *reinterpret_cast<const f32x4_t*>(Is + orow * 8 + 4);
-    }
-    // lanes l and l ^ 4 hold channels 2 j and 2 j + 1 of the same row: the even
-    // one stores both channels of columns 0 .. 3, the odd one of columns 4 .. 7,
-    // one 4-byte store per column (DPP row rotations by 4 and 12 reach l ^ 4)
-    const bool odd = (lane >> 2) & 1;
-    float v[8];
-#pragma unroll
-    for (int xb = 0; xb < 2; ++xb)
-#pragma unroll
-      for (int m = 0; m < 4; ++m) v[4 * xb + m] = pend[xb][m] * sc[xb][m];
-    uint32_t* const yt = reinterpret_cast<uint32_t*>(y + ((size_t)unit * F + t_out) * U * d +
-                                                      ylane - (odd ? 1 : 0));
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int send = __float_as_int(odd ? v[i] : v[4 + i]);
-      const int r4 = __builtin_amdgcn_update_dpp(0, send, 0x124, 0xF, 0xF, false);   // row_ror:4
-      const int r12 = __builtin_amdgcn_update_dpp(0, send, 0x12C, 0xF, 0xF, false);  // row_ror:12
-      const float got = __int_as_float(odd ? r4 : r12);
-      const int col = (odd ? 4 : 0) + i;
-      const uint32_t wv = odd ? pack_bf16(got, v[4 + i]) : pack_bf16(v[i], got);
-      if (c0 + col < Wl) yt[(size_t)col * (d >> 1)] = wv;
-    }
-  };
-
-  auto step = [&](int tin, auto kc) {
-    constexpr int k = decltype(kc)::value;  // tin mod 4
-    constexpr int fin = (k + 2) % 4;        // slot of output tin - 2, then of tin + 2
-    __syncthreads();                        // staged tile tin and the inverse norms of tin - 3
-    f32x4_t acc[2] = {f32x4_t{0.0f, 0.0f, 0.0f, 0.0f}, f32x4_t{0.0f, 0.0f, 0.0f, 0.0f}};
-    if (gact && tin < F) {
-#pragma unroll
-      for (int a = 0; a < 5; ++a) {
-        const int hr = orow + a;
-        const u32x2_t x0 = *reinterpret_cast<const u32x2_t*>(Xs + xs_word(ch, hr, 0));
-        const u32x2_t x1 = *reinterpret_cast<const u32x2_t*>(Xs + xs_word(ch, hr, 1));
-        const u32x2_t x2 = *reinterpret_cast<const u32x2_t*>(Xs + xs_word(ch, hr, 2));
-        const u32x2_t h0 = *reinterpret_cast<const u32x2_t*>(Wt + wt_word(ch, a, 0, 0, n));
-        const u32x2_t l0 = *reinterpret_cast<const u32x2_t*>(Wt + wt_word(ch, a, 0, 1, n));
-        const u32x2_t h1 = *reinterpret_cast<const u32x2_t*>(Wt + wt_word(ch, a, 1, 0, n));
-        const u32x2_t l1 = *reinterpret_cast<const u32x2_t*>(Wt + wt_word(ch, a, 1, 1, n));
-        acc[0] = mfma4(h0, x0, acc[0]);
-        acc[1] = mfma4(h0, x1, acc[1]);
-        acc[0] = mfma4(l0, x0, acc[0]);
-        acc[1] = mfma4(l0, x1, acc[1]);
-        acc[0] = mfma4(h1, x1, acc[0]);
-        acc[1] = mfma4(h1, x2, acc[1]);
-        acc[0] = mfma4(l1, x1, acc[0]);
-        acc[1] = mfma4(l1, x2, acc[1]);
+    };
+    auto store_frame = [&]() {
+      if (!pact) return;
+  #pragma unroll
+      for (int j = 0; j < kSlotIter; ++j) {
+        const int sl = wu + kWaves * j;
+        if (sl >= kSlots) break;
+        const uint32_t* v = pre[j];  // v[k] = channels 2 l, 2 l + 1 at column 4 q + k
+        const u32x2_t lo = u32x2_t{__builtin_amdgcn_perm(v[1], v[0], 0x05040100u),
+                                   __builtin_amdgcn_perm(v[3], v[2], 0x05040100u)};
+        const u32x2_t hi = u32x2_t{__builtin_amdgcn_perm(v[1], v[0], 0x07060302u),
+                                   __builtin_amdgcn_perm(v[3], v[2], 0x07060302u)};
+        // channel 2 l + 1 sits one channel pitch after 2 l: (2 l + 1) / 4 = 2 l / 4
+        const int wd = xs_word(2 * lane, sl / 3, sl % 3);
+        *reinterpret_cast<u32x2_t*>(Xs + wd) = lo;
+        *reinterpret_cast<u32x2_t*>(Xs + wd + kXPitch) = hi;
       }
-    }
-    // output tin - 3 (finished last step) leaves while the products run
-    if (tin >= 3) finish(tin - 3);
-    // input frame tin feeds output frame tin + 2 - tau with w_t[tau]
-    float ft[5];
-#pragma unroll
-    for (int i = 0; i < 5; ++i) ft[i] = Ft[i * 128 + ch];
-    f32x4_t out[2];
-#pragma unroll
-    for (int xb = 0; xb < 2; ++xb) {
-      out[xb] = ring[fin][xb] + ft[4] * acc[xb];  // output tin - 2 is complete
-      ring[fin][xb] = ft[0] * acc[xb];            // output tin + 2 starts
-      ring[(k + 3) % 4][xb] += ft[3] * acc[xb];   // tin - 1
-      ring[k][xb] += ft[2] * acc[xb];             // tin
-      ring[(k + 1) % 4][xb] += ft[1] * acc[xb];   // tin + 1
-    }
-    const bool emit = tin >= 2;  // output tin - 2 exists
-    if (emit) {
-#pragma unroll
+    };
+
+    f32x4_t ring[4][2];
+  #pragma unroll
+    for (int sl = 0; sl < 4; ++sl) ring[sl][0] = ring[sl][1] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    f32x4_t pend[2];  // SiLU of the last finished output frame, stored one step later
+
+    const int orow = 4 * hh + n;  // this lane's output row in the tile
+    const int gi_out = r0 + orow;
+    const int ylane = (gi_out * Wl + c0) * d + ch;  // in-frame offset (the frame is < 2^31 bytes)
+    // the finished output frame t_out from pend: scale (K: by the inverse norms of
+    // its 8 positions, from invs) and store it, a channel pair per 4-byte store
+    auto finish = [&](int t_out) {
+      if (!gact || gi_out >= Hl) return;
+      f32x4_t sc[2] = {f32x4_t{1.0f, 1.0f, 1.0f, 1.0f}, f32x4_t{1.0f, 1.0f, 1.0f, 1.0f}};
+      if (NORM) {
+        sc[0] = *reinterpret_cast<const f32x4_t*>(Is + orow * 8);
+        sc[1] = *reinterpret_cast<const f32x4_t*>(Is + orow * 8 + 4);
+      }
+      // lanes l and l ^ 4 hold channels 2 j and 2 j + 1 of the same row: the even
+      // one stores both channels of columns 0 .. 3, the odd one of columns 4 .. 7,
+      // one 4-byte store per column (DPP row rotations by 4 and 12 reach l ^ 4)
+      const bool odd = (lane >> 2) & 1;
+      float v[8];
+  #pragma unroll
       for (int xb = 0; xb < 2; ++xb)
-#pragma unroll
-        for (int m = 0; m < 4; ++m) pend[xb][m] = silu(out[xb][m]);
-      if (norm && gact) {
-        // sum of squares over the wave's 16 channels (lane bits 2 .. 5) of each
-        // of the lane's 8 positions, halving butterfly: the lane ends holding
-        // position column e = 4 bit5 + 2 bit4 + bit3 of its row
-        const bool h5 = lane & 32, h4 = lane & 16, h3 = lane & 8;
-        float a4[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float v0 = pend[0][i] * pend[0][i], v1 = pend[1][i] * pend[1][i];
-          a4[i] = (h5 ? v1 : v0) + lane_xor32(h5 ? v0 : v1);
-        }
-        float a2[2];
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-          a2[i] = (h4 ? a4[i + 2] : a4[i]) + lane_xor16(h4 ? a4[i] : a4[i + 2]);
-        const float keep = h3 ? a2[1] : a2[0];
-        const float send = h3 ? a2[0] : a2[1];
-        float s1 = keep + __int_as_float(__builtin_amdgcn_update_dpp(
-                              0, __float_as_int(send), 0x128, 0xF, 0xF, false));  // lane ^ 8
-        s1 += __shfl_xor(s1, 4);
-        if (!(lane & 4)) Rs[g * 64 + orow * 8 + (h5 ? 4 : 0) + (h4 ? 2 : 0) + (h3 ? 1 : 0)] = s1;
+  #pragma unroll
+        for (int m = 0; m < 4; ++m) v[4 * xb + m] = pend[xb][m] * sc[xb][m];
+      uint32_t* const yt = reinterpret_cast<uint32_t*>(y + ((size_t)unit * F + t_out) * U * d +
+                                                        ylane - (odd ? 1 : 0));
+  #pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int send = __float_as_int(odd ? v[i] : v[4 + i]);
+        const int r4 = __builtin_amdgcn_update_dpp(0, send, 0x124, 0xF, 0xF, false);   // row_ror:4
+        const int r12 = __builtin_amdgcn_update_dpp(0, send, 0x12C, 0xF, 0xF, false);  // row_ror:12
+        const float got = __int_as_float(odd ? r4 : r12);
+        const int col = (odd ? 4 : 0) + i;
+        const uint32_t wv = odd ? pack_bf16(got, v[4 + i]) : pack_bf16(v[i], got);
+        if (c0 + col < Wl) yt[(size_t)col * (d >> 1)] = wv;
       }
-    }
-    __syncthreads();  // every wave is done with the staged tile; partial sums complete
-    if (emit && norm && t < 64) {
-      float ss = 0.0f;
-      for (int gg = 0; gg < (d >> 4); ++gg) ss += Rs[gg * 64 + t];
-      Is[t] = 1.0f / fmaxf(sqrtf(ss), eps);
-    }
-    if (tin + 1 < F) store_frame();
-    if (tin + 2 < F) load_frame(tin + 2);  // in flight during the next frame's products
-  };
+    };
 
-  if (F > 0) {
-    load_frame(0);
-    store_frame();
-    if (F > 1) load_frame(1);
-  }
-  for (int tb = 0; tb < F + 2; tb += 4) {
-    step(tb, std::integral_constant<int, 0>{});
-    if (tb + 1 < F + 2) step(tb + 1, std::integral_constant<int, 1>{});
-    if (tb + 2 < F + 2) step(tb + 2, std::integral_constant<int, 2>{});
-    if (tb + 3 < F + 2) step(tb + 3, std::integral_constant<int, 3>{});
-  }
-  if (F > 0) {
-    __syncthreads();  // the inverse norms of the last output frame
-    finish(F - 1);
-  }
+    auto step = [&](int tin, auto kc) {
+      constexpr int k = decltype(kc)::value;  // tin mod 4
+      constexpr int fin = (k + 2) % 4;        // slot of output tin - 2, then of tin + 2
+      __syncthreads();                        // staged tile tin and the inverse norms of tin - 3
+      f32x4_t acc[2] = {f32x4_t{0.0f, 0.0f, 0.0f, 0.0f}, f32x4_t{0.0f, 0.0f, 0.0f, 0.0f}};
+      if (gact && tin < F) {
+  #pragma unroll
+        for (int a = 0; a < 5; ++a) {
+          const int hr = orow + a;
+          const u32x2_t x0 = *reinterpret_cast<const u32x2_t*>(Xs + xs_word(ch, hr, 0));
+          const u32x2_t x1 = *reinterpret_cast<const u32x2_t*>(Xs + xs_word(ch, hr, 1));
+          const u32x2_t x2 = *reinterpret_cast<const u32x2_t*>(Xs + xs_word(ch, hr, 2));
+          const u32x2_t h0 = *reinterpret_cast<const u32x2_t*>(Wt + wt_word(ch, a, 0, 0, n));
+          const u32x2_t l0 = *reinterpret_cast<const u32x2_t*>(Wt + wt_word(ch, a, 0, 1, n));
+          const u32x2_t h1 = *reinterpret_cast<const u32x2_t*>(Wt + wt_word(ch, a, 1, 0, n));
+          const u32x2_t l1 = *reinterpret_cast<const u32x2_t*>(Wt + wt_word(ch, a, 1, 1, n));
+          acc[0] = mfma4(h0, x0, acc[0]);
+          acc[1] = mfma4(h0, x1, acc[1]);
+          acc[0] = mfma4(l0, x0, acc[0]);
+          acc[1] = mfma4(l0, x1, acc[1]);
+          acc[0] = mfma4(h1, x1, acc[0]);
+          acc[1] = mfma4(h1, x2, acc[1]);
+          acc[0] = mfma4(l1, x1, acc[0]);
+          acc[1] = mfma4(l1, x2, acc[1]);
+        }
+      }
+      // output tin - 3 (finished last step) leaves while the products run
+      if (tin >= 3) finish(tin - 3);
+      // input frame tin feeds output frame tin + 2 - tau with w_t[tau]
+      float ft[5];
+  #pragma unroll
+      for (int i = 0; i < 5; ++i) ft[i] = Ft[i * 128 + ch];
+      f32x4_t out[2];
+  #pragma unroll
+      for (int xb = 0; xb < 2; ++xb) {
+        out[xb] = ring[fin][xb] + ft[4] * acc[xb];  // output tin - 2 is complete
+        ring[fin][xb] = ft[0] * acc[xb];            // output tin + 2 starts
+        ring[(k + 3) % 4][xb] += ft[3] * acc[xb];   // tin - 1
+        ring[k][xb] += ft[2] * acc[xb];             // tin
+        ring[(k + 1) % 4][xb] += ft[1] * acc[xb];   // tin + 1
+      }
+      const bool emit = tin >= 2;  // output tin - 2 exists
+      if (emit) {
+  #pragma unroll
+        for (int xb = 0; xb < 2; ++xb)
+  #pragma unroll
+          for (int m = 0; m < 4; ++m) pend[xb][m] = silu(out[xb][m]);
+        if (NORM && gact) {
+          // sum of squares over the wave's 16 channels (lane bits 2 .. 5) of each
+          // of the lane's 8 positions, halving butterfly: the lane ends holding
+          // position column e = 4 bit5 + 2 bit4 + bit3 of its row
+          const bool h5 = lane & 32, h4 = lane & 16, h3 = lane & 8;
+          float a4[4];
+  #pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float v0 = pend[0][i] * pend[0][i], v1 = pend[1][i] * pend[1][i];
+            a4[i] = (h5 ? v1 : v0) + lane_xor32(h5 ? v0 : v1);
+          }
+          float a2[2];
+  #pragma unroll
+          for (int i = 0; i < 2; ++i)
+            a2[i] = (h4 ? a4[i + 2] : a4[i]) + lane_xor16(h4 ? a4[i] : a4[i + 2]);
+          const float keep = h3 ? a2[1] : a2[0];
+          const float send = h3 ? a2[0] : a2[1];
+          float s1 = keep + __int_as_float(__builtin_amdgcn_update_dpp(
+                                0, __float_as_int(send), 0x128, 0xF, 0xF, false));  // lane ^ 8
+          s1 += __shfl_xor(s1, 4);
+          if (!(lane & 4)) Rs[g * 64 + orow * 8 + (h5 ? 4 : 0) + (h4 ? 2 : 0) + (h3 ? 1 : 0)] = s1;
+        }
+      }
+      __syncthreads();  // every wave is done with the staged tile; partial sums complete
+      if (emit && NORM && t < 64) {
+        float ss = 0.0f;
+        for (int gg = 0; gg < (d >> 4); ++gg) ss += Rs[gg * 64 + t];
+        Is[t] = 1.0f / fmaxf(sqrtf(ss), eps);
+      }
+      if (tin + 1 < F) store_frame();
+      if (tin + 2 < F) load_frame(tin + 2);  // in flight during the next frame's products
+    };
+
+    if (F > 0) {
+      load_frame(0);
+      store_frame();
+      if (F > 1) load_frame(1);
+    }
+    for (int tb = 0; tb < F + 2; tb += 4) {
+      step(tb, std::integral_constant<int, 0>{});
+      if (tb + 1 < F + 2) step(tb + 1, std::integral_constant<int, 1>{});
+      if (tb + 2 < F + 2) step(tb + 2, std::integral_constant<int, 2>{});
+      if (tb + 3 < F + 2) step(tb + 3, std::integral_constant<int, 3>{});
+    }
+    if (F > 0) {
+      __syncthreads();  // the inverse norms of the last output frame
+      finish(F - 1);
+    }
+  };
+  if (norm)
+    sweep(std::true_type{});
+  else
+    sweep(std::false_type{});
 }
 
 template <typename T>
