@@ -609,11 +609,12 @@ __global__ __launch_bounds__(kPrepThreads, 1) void prep_mfma_kernel(
   #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int send = __float_as_int(odd ? v[i] : v[4 + i]);
-        const int r4 = __builtin_amdgcn_update_dpp(0, send, 0x124, 0xF, 0xF, false);   // row_ror:4
-        const int r12 = __builtin_amdgcn_update_dpp(0, send, 0x12C, 0xF, 0xF, false);  // row_ror:12
-        const float got = __int_as_float(odd ? r4 : r12);
+        // even 4-lane banks (odd = 0) take lane + 4 (row_ror:12), odd banks lane - 4
+        // (row_ror:4); each DPP writes only its banks and leaves the others as they were
+        const int t12 = __builtin_amdgcn_update_dpp(send, send, 0x12C, 0xF, 0x5, false);
+        const float got = __int_as_float(__builtin_amdgcn_update_dpp(t12, send, 0x124, 0xF, 0xA, false));
         const int col = (odd ? 4 : 0) + i;
-        const uint32_t wv = odd ? pack_bf16(got, v[4 + i]) : pack_bf16(v[i], got);
+        const uint32_t wv = pack_bf16(odd ? got : v[i], odd ? v[4 + i] : got);
         if (c0 + col < Wl) yt[(size_t)col * (d >> 1)] = wv;
       }
     };
