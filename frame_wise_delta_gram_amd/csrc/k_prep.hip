@@ -469,12 +469,37 @@ __global__ __launch_bounds__(kPrepThreads, 1) void prep_mfma_kernel(
   }
   const unsigned ntiles = (unsigned)tiles_r * tiles_c;
   const unsigned jq = blockIdx.x / kXcds;  // position in the XCD's queue
-  const bool norm = jq < per;              // K first, then V
-  const unsigned item = (blockIdx.x % kXcds) * per + (norm ? jq : jq - per);
+  bool norm = jq < per;                    // K first, then V
+  unsigned item = (blockIdx.x % kXcds) * per + (norm ? jq : jq - per);
   if (jq >= 2 * per || item >= (unsigned)units * ntiles) return;
+  // With a last tile column at most 4 wide (half tiles: one column block of
+  // outputs) the XCD's queue runs its full tiles first (K, then V) and its half
+  // tiles last (K, then V), so the cheaper half sweeps fill the last round.
+  // Item g is a half tile when g % tiles_c == tiles_c - 1 (the last tile of
+  // each tile row; the rows of all units follow each other).
+  if (Wl % kTC != 0 && Wl % kTC <= 4 && tiles_c > 1) {
+    const unsigned tc = tiles_c;
+    const unsigned a = (blockIdx.x % kXcds) * per;
+    const unsigned bnd = min(a + per, (unsigned)units * ntiles);
+    // the XCD's valid queue positions [0, m) (K) and [per, per + m) (V), compacted
+    const unsigned jc = jq < per ? jq : jq - per + (bnd - a);
+    auto nfull = [&](unsigned g) { return g - g / tc; };  // full items in [0, g)
+    const unsigned f0 = nfull(a), nF = nfull(bnd) - f0;
+    const unsigned r0q = a / tc, nR = bnd / tc - r0q;   // half items: g = r tc + tc - 1
+    auto full_at = [&](unsigned f) { return (f / (tc - 1)) * tc + f % (tc - 1); };
+    if (jc < 2 * nF) {
+      norm = jc < nF;
+      item = full_at(f0 + (norm ? jc : jc - nF));
+    } else {
+      const unsigned r = jc - 2 * nF;
+      norm = r < nR;
+      item = (r0q + (norm ? r : r - nR)) * tc + tc - 1;
+    }
+  }
   // K (NORM: L2-normalised) and V sweeps as two compiled bodies
-  auto sweep = [&](auto nc) {
+  auto sweep = [&](auto nc, auto hc) {
     constexpr bool NORM = decltype(nc)::value;
+    constexpr bool half = decltype(hc)::value;
     const ConvSide<uint16_t> side = NORM ? ks : vs;
     const uint16_t* __restrict__ x = side.x;
     const float* __restrict__ ws = side.ws;
@@ -550,6 +575,7 @@ __global__ __launch_bounds__(kPrepThreads, 1) void prep_mfma_kernel(
       for (int j = 0; j < kSlotIter; ++j) {
         const int sl = wu + kWaves * j;
         if (sl >= kSlots) break;
+        if (half && sl % 3 == 2) continue;
         const int gi = r0 - 2 + sl / 3;
   #pragma unroll
         for (int k = 0; k < 4; ++k) {
@@ -566,6 +592,7 @@ __global__ __launch_bounds__(kPrepThreads, 1) void prep_mfma_kernel(
       for (int j = 0; j < kSlotIter; ++j) {
         const int sl = wu + kWaves * j;
         if (sl >= kSlots) break;
+        if (half && sl % 3 == 2) continue;
         const uint32_t* v = pre[j];  // v[k] = channels 2 l, 2 l + 1 at column 4 q + k
         const u32x2_t lo = u32x2_t{__builtin_amdgcn_perm(v[1], v[0], 0x05040100u),
                                    __builtin_amdgcn_perm(v[3], v[2], 0x05040100u)};
@@ -581,7 +608,9 @@ __global__ __launch_bounds__(kPrepThreads, 1) void prep_mfma_kernel(
     f32x4_t ring[4][2];
   #pragma unroll
     for (int sl = 0; sl < 4; ++sl) ring[sl][0] = ring[sl][1] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
-    f32x4_t pend[2];  // SiLU of the last finished output frame, stored one step later
+    // SiLU of the last finished output frame, stored one step later (block 1 stays
+    // zero in a half tile)
+    f32x4_t pend[2] = {f32x4_t{0.0f, 0.0f, 0.0f, 0.0f}, f32x4_t{0.0f, 0.0f, 0.0f, 0.0f}};
 
     const int orow = 4 * hh + n;  // this lane's output row in the tile
     const int gi_out = r0 + orow;
@@ -624,7 +653,22 @@ __global__ __launch_bounds__(kPrepThreads, 1) void prep_mfma_kernel(
       constexpr int fin = (k + 2) % 4;        // slot of output tin - 2, then of tin + 2
       __syncthreads();                        // staged tile tin and the inverse norms of tin - 3
       f32x4_t acc[2] = {f32x4_t{0.0f, 0.0f, 0.0f, 0.0f}, f32x4_t{0.0f, 0.0f, 0.0f, 0.0f}};
-      if (gact && tin < F) {
+      if (half && gact && tin < F) {
+  #pragma unroll
+        for (int a = 0; a < 5; ++a) {
+          const int hr = orow + a;
+          const u32x2_t x0 = *reinterpret_cast<const u32x2_t*>(Xs + xs_word(ch, hr, 0));
+          const u32x2_t x1 = *reinterpret_cast<const u32x2_t*>(Xs + xs_word(ch, hr, 1));
+          const u32x2_t h0 = *reinterpret_cast<const u32x2_t*>(Wt + wt_word(ch, a, 0, 0, n));
+          const u32x2_t l0 = *reinterpret_cast<const u32x2_t*>(Wt + wt_word(ch, a, 0, 1, n));
+          const u32x2_t h1 = *reinterpret_cast<const u32x2_t*>(Wt + wt_word(ch, a, 1, 0, n));
+          const u32x2_t l1 = *reinterpret_cast<const u32x2_t*>(Wt + wt_word(ch, a, 1, 1, n));
+          acc[0] = mfma4(h0, x0, acc[0]);
+          acc[0] = mfma4(l0, x0, acc[0]);
+          acc[0] = mfma4(h1, x1, acc[0]);
+          acc[0] = mfma4(l1, x1, acc[0]);
+        }
+      } else if (!half && gact && tin < F) {
   #pragma unroll
         for (int a = 0; a < 5; ++a) {
           const int hr = orow + a;
@@ -652,8 +696,10 @@ __global__ __launch_bounds__(kPrepThreads, 1) void prep_mfma_kernel(
   #pragma unroll
       for (int i = 0; i < 5; ++i) ft[i] = Ft[i * 128 + ch];
       f32x4_t out[2];
+      out[1] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
   #pragma unroll
       for (int xb = 0; xb < 2; ++xb) {
+        if (xb == 1 && half) break;
         out[xb] = ring[fin][xb] + ft[4] * acc[xb];  // output tin - 2 is complete
         ring[fin][xb] = ft[0] * acc[xb];            // output tin + 2 starts
         ring[(k + 3) % 4][xb] += ft[3] * acc[xb];   // tin - 1
@@ -663,9 +709,11 @@ __global__ __launch_bounds__(kPrepThreads, 1) void prep_mfma_kernel(
       const bool emit = tin >= 2;  // output tin - 2 exists
       if (emit) {
   #pragma unroll
-        for (int xb = 0; xb < 2; ++xb)
+        for (int xb = 0; xb < 2; ++xb) {
+          if (xb == 1 && half) break;
   #pragma unroll
           for (int m = 0; m < 4; ++m) pend[xb][m] = silu(out[xb][m]);
+        }
         if (NORM && gact) {
           // sum of squares over the wave's 16 channels (lane bits 2 .. 5) of each
           // of the lane's 8 positions, halving butterfly: the lane ends holding
@@ -715,10 +763,21 @@ __global__ __launch_bounds__(kPrepThreads, 1) void prep_mfma_kernel(
       finish(F - 1);
     }
   };
-  if (norm)
-    sweep(std::true_type{});
-  else
-    sweep(std::false_type{});
+  // a half tile (at most 4 columns left in the frame): only output column block
+  // 0 exists, so halo column slot 2, column block 1's products and its temporal
+  // filter and SiLU are left out (a body of its own)
+  const bool half = (int)((item % ntiles) % tiles_c) * kTC + 4 >= Wl;
+  if (norm) {
+    if (half)
+      sweep(std::true_type{}, std::true_type{});
+    else
+      sweep(std::true_type{}, std::false_type{});
+  } else {
+    if (half)
+      sweep(std::false_type{}, std::true_type{});
+    else
+      sweep(std::false_type{}, std::false_type{});
+  }
 }
 
 template <typename T>

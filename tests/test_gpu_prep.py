@@ -28,6 +28,9 @@ SHAPES = {
     "two-frames-f32": P(714, "two-frames-f32", 1, 1, 2, 10, 6, 16, 16, "f32"),
     "dk16-dv128-bf16": P(715, "dk16-dv128-bf16", 2, 2, 6, 8, 16, 16, 128, "bf16"),
     "dk128-f32": P(716, "dk128-f32", 1, 2, 7, 9, 17, 128, 64, "f32"),
+    # last tile column 3 wide (a half tile: one output column block) over 6 units,
+    # so that the launch's queues reorder full and half tiles across XCD ranges
+    "half-tiles-bf16": P(717, "half-tiles-bf16", 2, 3, 5, 9, 19, 64, 32, "bf16"),
 }
 
 TOL = {"f32": 1e-4, "bf16": 2e-2}
